@@ -1,0 +1,89 @@
+"""Reference construction of the library's weight layout (test infrastructure only).
+
+The pages fix only that the repack is a pure permutation of the 4-bit codes into the
+kernel's own tile order, with the same byte count, and that act_order stores weight rows
+in the permuted order (vllm_marlin.rs, `ferrum_vllm_gptq_marlin_repack` doc; marlin.rs,
+`MarlinWeight.perm` doc).  The order itself is this library's design; it is stated here
+as nested loops (the slow, checkable form) so that the GPU repack kernel, which uses a
+direct index formula, can be compared against it bit for bit.
+
+Layout of repacked B (uint32 words, K*N/8 of them), with G = K/128:
+  for each 16-column block nb (columns n = 16*nb + c), each 128-row chunk g, each lane
+  l = c + 16*q (q = 0..3) and each dword j = 0..3, word ((nb*G + g)*64 + l)*4 + j holds
+  the codes of rows k = 128*g + 32*j + 8*q + i (i = 0..7) of column n; the code of row
+  offset i sits in nibble slot SLOT[i] (bits 4*SLOT[i]..+3), SLOT = [0, 4, 1, 5, 2, 6, 3, 7],
+  i.e. even offsets in the low half-word and odd offsets in the high half-word.
+  With act_order, row position k of the repacked matrix is original row perm[k].
+
+Layout of repacked scales (fp16): [N/16][G][16], element (nb, g, c) = s[g][16*nb + c].
+Layout of repacked zero points (uint32): [N/16][G][2], word (nb, g, h) = zeros[g][2*nb + h]
+  (column 16*nb + 8*h + i in bits 4*i).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .reference import unpack_qweight
+
+SLOT = (0, 4, 1, 5, 2, 6, 3, 7)
+
+
+def repack_b_loops(codes: np.ndarray, perm=None) -> np.ndarray:
+    """Nested-loop construction from codes uint8 [K][N] (small shapes only)."""
+    k_total, n_total = codes.shape
+    groups = k_total // 128
+    out = np.zeros(k_total * n_total // 8, dtype=np.uint32)
+    for nb in range(n_total // 16):
+        for g in range(groups):
+            for lane in range(64):
+                c, q = lane % 16, lane // 16
+                for j in range(4):
+                    word = 0
+                    for i in range(8):
+                        k = 128 * g + 32 * j + 8 * q + i
+                        src = int(perm[k]) if perm is not None else k
+                        word |= int(codes[src, 16 * nb + c]) << (4 * SLOT[i])
+                    out[((nb * groups + g) * 64 + lane) * 4 + j] = word
+    return out
+
+
+def repack_b(qweight: np.ndarray, perm=None) -> np.ndarray:
+    """Same layout as `repack_b_loops`, built with array reshapes (any size)."""
+    codes = unpack_qweight(qweight)
+    if perm is not None:
+        codes = codes[np.asarray(perm, dtype=np.int64), :]
+    k_total, n_total = codes.shape
+    groups = k_total // 128
+    # k = 128*g + 32*j + 8*q + i ; n = 16*nb + c
+    t = codes.reshape(groups, 4, 4, 8, n_total // 16, 16)          # g, j, q, i, nb, c
+    t = t.transpose(4, 0, 2, 5, 1, 3).astype(np.uint32)            # nb, g, q, c, j, i
+    word = np.zeros(t.shape[:-1], dtype=np.uint32)
+    for i in range(8):
+        word |= t[..., i] << np.uint32(4 * SLOT[i])
+    return word.reshape(-1)
+
+
+def unrepack_b(words: np.ndarray, k_total: int, n_total: int) -> np.ndarray:
+    """Inverse of `repack_b`: codes uint8 [K][N] in the repacked row order."""
+    groups = k_total // 128
+    w = np.asarray(words, dtype=np.uint32).reshape(n_total // 16, groups, 4, 16, 4)
+    codes = np.empty((n_total // 16, groups, 4, 16, 4, 8), dtype=np.uint8)
+    for i in range(8):
+        codes[..., i] = (w >> np.uint32(4 * SLOT[i])) & np.uint32(0xF)
+    # nb, g, q, c, j, i -> g, j, q, i, nb, c
+    return codes.transpose(1, 4, 2, 5, 0, 3).reshape(k_total, n_total)
+
+
+def repack_scales(scales: np.ndarray) -> np.ndarray:
+    """fp16 [G][N] -> fp16 [N/16][G][16] (flattened)."""
+    s = np.asarray(scales, dtype=np.float16)
+    groups, n_total = s.shape
+    return s.reshape(groups, n_total // 16, 16).transpose(1, 0, 2).reshape(-1).copy()
+
+
+def repack_zero_points(zeros: np.ndarray) -> np.ndarray:
+    """uint32 [G][N/8] -> uint32 [N/16][G][2] (flattened)."""
+    z = np.asarray(zeros, dtype=np.uint32)
+    groups, n8 = z.shape
+    return z.reshape(groups, n8 // 2, 2).transpose(1, 0, 2).reshape(-1).copy()

@@ -1,0 +1,302 @@
+"""CPU oracle for the W4A16 weight-only quantized GEMM: the plain definition, computed slowly.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or execute this
+module; only the tests, the smoke check of the build entry point and the bench's CPU
+baseline leg use it.  It shares no code, tables or constants with the HIP library.
+
+What it computes (the pages give the operation only through interfaces, doc comments and
+tests; this is the plain definition they describe):
+
+  C[m, n] = sum_k A[m, k] * W[k, n],   W[k, n] = (q[k, n] - z(k, n)) * s[g(k), n]
+
+* ferrum-kernels marlin.rs, module doc and `marlin_gemm` doc: C = A @ dequant(B), INT4
+  weights, FP16 activations, constraints K % 128 == 0 and N % 256 == 0.
+* ferrum-kernels marlin.rs, `ferrum_vllm_marlin_moe_f16` declaration (`has_zp`): symmetric
+  kU4B8 (zero point fixed at 8) or asymmetric kU4 with per-group zero points.
+* ferrum-kernels marlin.rs, `MarlinWeight.qzeros` doc and vllm_marlin.rs
+  `repack_gptq_qzeros_to_marlin`: zero points are the actual codes (0..15).
+* ferrum-kernels marlin.rs, `MarlinWeight.perm` doc: act_order; each row k belongs to group
+  g_idx[k]; the permutation is argsort(g_idx).
+
+Precision: codes, zero points and scales are exact; W = (q - z) * s is formed exactly
+(a 5-bit integer times an fp16 value fits in fp64, and in fp32 too); the product is
+accumulated in fp64 and left unrounded.  Only `dequantize_fp16` rounds (once, to nearest
+even), for the bit-exact check of the library's dequant export.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+U4B8_ZERO = 8  # kU4B8: stored code q means q - 8
+
+
+# ---------------------------------------------------------------------------------------
+# Unpacking the plain input formats
+# ---------------------------------------------------------------------------------------
+
+def unpack_qweight(qweight: np.ndarray) -> np.ndarray:
+    """GPTQ words uint32 [K/8][N] -> codes uint8 [K][N]; row 8r+i sits in bits 4i of word r.
+
+    Reading of the pages: 4-bit codes are packed low nibble first (the zero-point words of
+    vllm_marlin.rs's qzeros tests and the low-nibble-first source decode of marlin.rs's
+    MXFP4 quality test use that order; GPTQ's [K/8, N] qweight shape is named on
+    vllm_marlin.rs, `load_stacked_gptq_vllm_marlin` doc).
+    """
+    qweight = np.asarray(qweight, dtype=np.uint32)
+    k8, n = qweight.shape
+    q = np.empty((k8 * 8, n), dtype=np.uint8)
+    for i in range(8):
+        q[i::8] = (qweight >> np.uint32(4 * i)) & np.uint32(0xF)
+    return q
+
+
+def unpack_zero_points(zeros: np.ndarray) -> np.ndarray:
+    """Zero-point words uint32 [G][N/8] -> codes uint8 [G][N]; column 8j+i in bits 4i of word j.
+
+    vllm_marlin.rs, `repack_gptq_qzeros_to_marlin` and its test
+    `qzeros_repack_preserves_kernel_layout` (codes 1..8 pack to 0x87654321).
+    """
+    zeros = np.asarray(zeros, dtype=np.uint32)
+    g, n8 = zeros.shape
+    z = np.empty((g, n8 * 8), dtype=np.uint8)
+    for i in range(8):
+        z[:, i::8] = (zeros >> np.uint32(4 * i)) & np.uint32(0xF)
+    return z
+
+
+def num_groups(k: int, group_size: int) -> int:
+    """Group count along K (transformer.rs `marlin_num_groups`; only positive sizes here)."""
+    if k <= 0:
+        raise ValueError(f"input width {k} must be positive")
+    if group_size <= 0:
+        raise ValueError(f"group size {group_size} must be positive")
+    if k % group_size:
+        raise ValueError(f"input width {k} is not divisible by group size {group_size}")
+    return k // group_size
+
+
+def group_of_rows(k: int, group_size: int, g_idx: np.ndarray | None = None) -> np.ndarray:
+    """Group of every original row: g_idx[k] with act_order, else k // group_size."""
+    if g_idx is not None:
+        g = np.asarray(g_idx, dtype=np.int64)
+        if g.shape != (k,):
+            raise ValueError("g_idx must have one entry per row of K")
+        return g
+    return np.arange(k, dtype=np.int64) // group_size
+
+
+# ---------------------------------------------------------------------------------------
+# Dequantization and the product
+# ---------------------------------------------------------------------------------------
+
+def dequantize(q: np.ndarray, scales: np.ndarray, group: np.ndarray,
+               zero_codes: np.ndarray | None = None) -> np.ndarray:
+    """W[k, n] = (q[k, n] - z) * s[group[k], n] in fp64 (exact).
+
+    z = 8 without zero points (kU4B8), else the code zero_codes[group[k], n] (kU4).
+    """
+    s = np.asarray(scales, dtype=np.float16).astype(np.float64)
+    qi = q.astype(np.int64)
+    zi = U4B8_ZERO if zero_codes is None else np.asarray(zero_codes).astype(np.int64)[group, :]
+    return (qi - zi).astype(np.float64) * s[group, :]
+
+
+def dequantize_fp16(w: np.ndarray) -> np.ndarray:
+    """fp16 round-to-nearest-even of the exact dequantized weights (one rounding)."""
+    return np.asarray(w, dtype=np.float64).astype(np.float16)
+
+
+def matmul_fp64(a: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """fp64 product A @ W of fp16 activations and exact weights (unrounded result)."""
+    return np.asarray(a).astype(np.float64) @ w
+
+
+def w4a16_weights(qweight, scales, *, zeros=None, g_idx=None, group_size=128,
+                  columns=None) -> np.ndarray:
+    """Exact fp64 weights W [K][N] (or [K][len(columns)] for a column subset)."""
+    qweight = np.asarray(qweight, dtype=np.uint32)
+    scales = np.asarray(scales)
+    k = qweight.shape[0] * 8
+    num_groups(k, group_size)
+    zero_codes = None if zeros is None else unpack_zero_points(zeros)
+    if columns is not None:
+        cols = np.asarray(columns, dtype=np.int64)
+        qweight, scales = qweight[:, cols], scales[:, cols]
+        zero_codes = None if zero_codes is None else zero_codes[:, cols]
+    group = group_of_rows(k, group_size, g_idx)
+    return dequantize(unpack_qweight(qweight), scales, group, zero_codes)
+
+
+def w4a16_gemm(a, qweight, scales, *, zeros=None, g_idx=None, group_size=128,
+               columns=None) -> np.ndarray:
+    """Reference C = A @ dequant(B) in fp64, [M][N] (or [M][len(columns)])."""
+    w = w4a16_weights(qweight, scales, zeros=zeros, g_idx=g_idx, group_size=group_size,
+                      columns=columns)
+    return matmul_fp64(a, w)
+
+
+# ---------------------------------------------------------------------------------------
+# act_order
+# ---------------------------------------------------------------------------------------
+
+def act_order_perm(g_idx: np.ndarray, group_size: int) -> tuple[np.ndarray, np.ndarray]:
+    """perm = stable argsort(g_idx) and the group of each sorted position, g_idx[perm].
+
+    marlin.rs, `MarlinWeight.perm` doc: perm[i] is the original row placed at position i,
+    computed as argsort of g_idx; weight rows are stored in that order and activations are
+    gathered by it, which leaves the product unchanged.  Reading: ties keep ascending row
+    order (stable sort), and the layout requires every group to hold exactly group_size
+    rows (GPTQ's construction), so that sorted position i belongs to group i // group_size.
+    """
+    g = np.asarray(g_idx, dtype=np.int64)
+    perm = np.argsort(g, kind="stable")
+    sorted_g = g[perm]
+    k = g.size
+    if k % group_size or not np.array_equal(sorted_g, np.arange(k) // group_size):
+        raise ValueError("act_order groups must each hold exactly group_size rows, "
+                         "numbered 0..K/group_size-1")
+    return perm.astype(np.int32), sorted_g.astype(np.int32)
+
+
+# ---------------------------------------------------------------------------------------
+# Expert-major CSR (mmq_ffi.rs, `ExpertCsr`) and the grouped product
+# ---------------------------------------------------------------------------------------
+
+class CsrError(ValueError):
+    pass
+
+
+def csr_from_pair_rows(n_expert: int, n_tokens: int, selected, pair_tok) -> dict:
+    """Expert-major CSR from one expert choice and one activation row per output pair.
+
+    mmq_ffi.rs, `ExpertCsr::from_pair_rows`: count pairs per expert, prefix-sum, list the
+    non-empty experts in ascending order with their segment starts (plus the final pair
+    count), then place pairs into their expert's segment in ascending pair order.
+    """
+    selected = [int(x) for x in selected]
+    pair_tok = [int(x) for x in pair_tok]
+    if n_expert <= 0 or n_tokens <= 0 or not selected:
+        raise CsrError("CSR requires non-empty experts, tokens and pairs")
+    if len(pair_tok) != len(selected):
+        raise CsrError("one activation row per pair is required")
+    counts = [0] * n_expert
+    for e in selected:
+        if not 0 <= e < n_expert:
+            raise CsrError(f"expert {e} outside 0..{n_expert}")
+        counts[e] += 1
+    for t in pair_tok:
+        if not 0 <= t < n_tokens:
+            raise CsrError(f"token {t} outside 0..{n_tokens}")
+    start = [0] * (n_expert + 1)
+    for e in range(n_expert):
+        start[e + 1] = start[e] + counts[e]
+    ex_ids = [e for e in range(n_expert) if counts[e]]
+    ex_off = [start[e] for e in ex_ids] + [len(selected)]
+    cursor = start[:n_expert]
+    ex_pairs = [0] * len(selected)
+    for p, e in enumerate(selected):
+        ex_pairs[cursor[e]] = p
+        cursor[e] += 1
+    csr = dict(ex_ids=ex_ids, ex_off=ex_off, ex_pairs=ex_pairs, pair_tok=pair_tok,
+               n_expert=n_expert, n_tokens=n_tokens)
+    validate_csr(csr)
+    return csr
+
+
+def csr_from_token_routes(n_expert: int, n_tokens: int, top_k: int, selected) -> dict:
+    """CSR from token-major top-k routes; pair p reads activation row p // top_k.
+
+    mmq_ffi.rs, `ExpertCsr::from_token_routes`.
+    """
+    if top_k <= 0:
+        raise CsrError("experts per token must be nonzero")
+    selected = [int(x) for x in np.asarray(selected).reshape(-1)]
+    if len(selected) != n_tokens * top_k:
+        raise CsrError("route count must equal tokens x top_k")
+    return csr_from_pair_rows(n_expert, n_tokens, selected,
+                              [p // top_k for p in range(len(selected))])
+
+
+def validate_csr(csr: dict) -> None:
+    """The CSR invariants of mmq_ffi.rs `ExpertCsr::from_parts`."""
+    ex_ids, ex_off = csr["ex_ids"], csr["ex_off"]
+    ex_pairs, pair_tok = csr["ex_pairs"], csr["pair_tok"]
+    n_expert, n_tokens = csr["n_expert"], csr["n_tokens"]
+    if n_expert <= 0 or n_tokens <= 0 or not ex_ids or not ex_pairs:
+        raise CsrError("CSR requires non-empty experts, tokens and pairs")
+    if len(ex_off) != len(ex_ids) + 1 or ex_off[0] != 0:
+        raise CsrError("offsets must be active experts + 1 long and start at zero")
+    if len(pair_tok) != len(ex_pairs) or ex_off[-1] != len(ex_pairs):
+        raise CsrError("offsets must end at the pair count")
+    if any(a >= b for a, b in zip(ex_ids, ex_ids[1:])):
+        raise CsrError("expert ids must be strictly increasing")
+    if any(not 0 <= e < n_expert for e in ex_ids):
+        raise CsrError("expert id out of range")
+    seen = [False] * len(ex_pairs)
+    for p in ex_pairs:
+        if not 0 <= p < len(ex_pairs):
+            raise CsrError(f"pair {p} out of range")
+        if seen[p]:
+            raise CsrError(f"pair {p} appears more than once")
+        seen[p] = True
+        if not 0 <= pair_tok[p] < n_tokens:
+            raise CsrError("token out of range")
+    if any(a >= b for a, b in zip(ex_off, ex_off[1:])):
+        raise CsrError("segments must be non-empty and increasing")
+
+
+def grouped_w4a16_gemm(a, experts, csr, *, group_size=128, columns=None,
+                       pairs=None) -> np.ndarray:
+    """Pair-major reference y[p] = A[pair_tok[p]] @ dequant(B_e) for the expert e owning p.
+
+    Walks the expert-major CSR: segment i covers positions ex_off[i]..ex_off[i+1] of
+    ex_pairs and uses expert ex_ids[i]; no top-k weight multiply (mmq_ffi.rs grouped
+    projection contract).  `experts[e]` holds that expert's qweight, scales and optional
+    zeros.  `pairs` restricts the rows computed (others stay NaN).
+    """
+    a = np.asarray(a)
+    n_pairs = len(csr["ex_pairs"])
+    ncols = experts[0]["qweight"].shape[1] if columns is None else len(columns)
+    y = np.full((n_pairs, ncols), np.nan)
+    want = None if pairs is None else set(int(p) for p in pairs)
+    for i, e in enumerate(csr["ex_ids"]):
+        rows = [csr["ex_pairs"][j] for j in range(csr["ex_off"][i], csr["ex_off"][i + 1])]
+        if want is not None:
+            rows = [p for p in rows if p in want]
+        if not rows:
+            continue
+        ex = experts[e]
+        w = w4a16_weights(ex["qweight"], ex["scales"], zeros=ex.get("zeros"),
+                          group_size=group_size, columns=columns)
+        toks = [csr["pair_tok"][p] for p in rows]
+        y[rows, :] = matmul_fp64(a[toks, :], w)
+    return y
+
+
+# ---------------------------------------------------------------------------------------
+# Checker
+# ---------------------------------------------------------------------------------------
+
+def check(c: np.ndarray, ref: np.ndarray, *, rel_max: float = 2e-3, abs_max: float = 1e-3,
+          rel_frob: float = 1e-3) -> dict:
+    """Tolerance test of an fp16 result against the fp64 reference.
+
+    Pass iff no non-finite output, max |C - ref| <= rel_max * rms(ref) + abs_max, and
+    ||C - ref||_F / ||ref||_F <= rel_frob (rms over every compared element).
+    """
+    c64 = np.asarray(c).astype(np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if c64.shape != ref.shape:
+        raise ValueError(f"shape mismatch {c64.shape} vs {ref.shape}")
+    nonfinite = int(np.count_nonzero(~np.isfinite(c64)))
+    diff = np.abs(c64 - ref)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    tol = rel_max * rms + abs_max
+    max_err = float(np.max(diff)) if diff.size else 0.0
+    ref_norm = float(np.linalg.norm(ref))
+    relf = float(np.linalg.norm(c64 - ref) / ref_norm) if ref_norm > 0 else float(
+        np.linalg.norm(c64 - ref))
+    ok = nonfinite == 0 and max_err <= tol and relf <= rel_frob
+    return dict(ok=bool(ok), max_err=max_err, tol=tol, rms=rms, rel_frob=relf,
+                nonfinite=nonfinite, violations=int(np.count_nonzero(diff > tol)))

@@ -1,0 +1,313 @@
+"""Pins of the CPU oracle to facts fixed by the pages and by plain arithmetic.
+
+Each test checks the oracle against something other than itself: a value printed on a
+page (golden fixtures), a closed form, or a brute-force computation in plain Python that
+decodes words through their hexadecimal digits rather than through shifts.
+"""
+
+import struct
+
+import numpy as np
+import pytest
+
+from conftest import golden_csr_cases, read_golden
+from oracle import layout, reference as ref
+import synthetic
+
+
+def hex_nibbles(word):
+    """The eight 4-bit fields of a word, lowest first, read from its hex digits."""
+    h = f"{int(word) & 0xFFFFFFFF:08x}"
+    return [int(h[7 - i], 16) for i in range(8)]
+
+
+def hex_word(nibbles):
+    """Inverse of hex_nibbles: eight fields (lowest first) to a word via hex digits."""
+    return int("".join(f"{v:x}" for v in reversed(nibbles)), 16)
+
+
+def codes_bruteforce(qweight):
+    """Codes [K][N] as nested Python lists, decoded digit by digit."""
+    k8, n = qweight.shape
+    out = [[0] * n for _ in range(8 * k8)]
+    for r in range(k8):
+        for c in range(n):
+            for i, v in enumerate(hex_nibbles(qweight[r, c])):
+                out[8 * r + i][c] = v
+    return out
+
+
+def zero_codes_bruteforce(zeros):
+    g, n8 = zeros.shape
+    return [[hex_nibbles(zeros[gi, c // 8])[c % 8] for c in range(8 * n8)] for gi in range(g)]
+
+
+def gemm_bruteforce(a, codes, scales, group, zcodes=None):
+    """Plain-Python triple loop with exact float products (fp64)."""
+    m, k = a.shape
+    n = len(codes[0])
+    out = [[0.0] * n for _ in range(m)]
+    for mi in range(m):
+        for c in range(n):
+            acc = 0.0
+            for ki in range(k):
+                z = 8 if zcodes is None else zcodes[group[ki]][c]
+                w = (codes[ki][c] - z) * float(scales[group[ki], c])
+                acc += float(a[mi, ki]) * w
+            out[mi][c] = acc
+    return np.array(out)
+
+
+# --------------------------------------------------------------------------- formats
+
+def test_zero_point_words_match_page_example():
+    for parts in read_golden("zero_point_words.txt"):
+        word = int(parts[0], 16)
+        codes = [int(x) for x in parts[1:]]
+        got = ref.unpack_zero_points(np.array([[word]], dtype=np.uint32))[0].tolist()
+        assert got == codes
+        assert hex_word(codes) == word
+
+
+def test_qweight_rows_are_low_nibble_first():
+    # column 0 holds rows 0..7 = 0..7 and column 1 rows = 15..8
+    w0 = hex_word(list(range(8)))
+    w1 = hex_word(list(range(15, 7, -1)))
+    assert w0 == 0x76543210
+    q = ref.unpack_qweight(np.array([[w0, w1]], dtype=np.uint32))
+    assert q[:, 0].tolist() == list(range(8))
+    assert q[:, 1].tolist() == list(range(15, 7, -1))
+
+
+def test_unpack_matches_hex_digits_on_random_words():
+    qw = synthetic.qweight_words(11, 64, 24)
+    assert ref.unpack_qweight(qw).tolist() == codes_bruteforce(qw)
+    zw = synthetic.zero_point_words(12, 3, 32)
+    assert ref.unpack_zero_points(zw).tolist() == zero_codes_bruteforce(zw)
+
+
+def test_group_counts_match_page():
+    for k, gs, expect in read_golden("group_counts.txt"):
+        if expect == "error":
+            with pytest.raises(ValueError):
+                ref.num_groups(int(k), int(gs))
+        else:
+            assert ref.num_groups(int(k), int(gs)) == int(expect)
+
+
+# --------------------------------------------------------------------------- closed forms
+
+def test_all_eight_codes_give_exact_zero():
+    """u4b8 code 8 means 0, so C == 0 for any A and scales."""
+    k, n = 256, 32
+    a = synthetic.activations(1, 5, k)
+    qw = np.full((k // 8, n), 0x88888888, dtype=np.uint32)
+    s = synthetic.scales(2, k // 128, n)
+    c = ref.w4a16_gemm(a, qw, s)
+    assert np.all(c == 0.0)
+
+
+def test_codes_equal_to_zero_points_give_exact_zero():
+    """u4 with q == z in every group and column gives C == 0."""
+    k, n = 256, 16
+    zcodes = [[(3 * g + c) % 16 for c in range(n)] for g in range(2)]
+    zeros = np.array([[hex_word(zcodes[g][8 * j:8 * j + 8]) for j in range(n // 8)]
+                      for g in range(2)], dtype=np.uint32)
+    qw = np.array([[hex_word([zcodes[(8 * r) // 128][c]] * 8) for c in range(n)]
+                   for r in range(k // 8)], dtype=np.uint32)
+    a = synthetic.activations(3, 4, k)
+    s = synthetic.scales(4, 2, n)
+    assert np.all(ref.w4a16_gemm(a, qw, s, zeros=zeros) == 0.0)
+
+
+def test_unit_scales_match_integer_bruteforce():
+    """s = 1 and A in {-1, 0, 1}: every output is the exact integer sum of (q - 8)."""
+    m, k, n = 3, 256, 16
+    rng_codes = synthetic.qweight_words(5, k, n)
+    trits = (synthetic.below(6, m * k, 3) - 1).reshape(m, k).astype(np.float16)
+    ones = np.ones((k // 128, n), dtype=np.float16)
+    codes = codes_bruteforce(rng_codes)
+    want = [[sum(int(trits[i, kk]) * (codes[kk][c] - 8) for kk in range(k)) for c in range(n)]
+            for i in range(m)]
+    got = ref.w4a16_gemm(trits, rng_codes, ones)
+    assert got.tolist() == [[float(v) for v in row] for row in want]
+
+
+def test_one_hot_rows_select_one_dequantized_weight_row():
+    """A = e_k picks row k: C = (q[k, :] - 8) * s[k // 128, :], exactly."""
+    k, n = 512, 32
+    qw = synthetic.qweight_words(7, k, n)
+    s = synthetic.scales(8, k // 128, n)
+    rows = [0, 1, 127, 128, 200, 383, 384, 511]
+    a = np.zeros((len(rows), k), dtype=np.float16)
+    for i, r in enumerate(rows):
+        a[i, r] = 1.0
+    codes = codes_bruteforce(qw)
+    got = ref.w4a16_gemm(a, qw, s)
+    for i, r in enumerate(rows):
+        want = [(codes[r][c] - 8) * float(s[r // 128, c]) for c in range(n)]
+        assert got[i].tolist() == want
+
+
+def test_zero_point_product_matches_bruteforce():
+    m, k, n = 2, 256, 16
+    a = synthetic.activations(9, m, k)
+    qw = synthetic.qweight_words(10, k, n)
+    s = synthetic.scales(11, 2, n)
+    zw = synthetic.zero_point_words(12, 2, n)
+    group = [kk // 128 for kk in range(k)]
+    want = gemm_bruteforce(a, codes_bruteforce(qw), s, group, zero_codes_bruteforce(zw))
+    got = ref.w4a16_gemm(a, qw, s, zeros=zw)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_act_order_product_matches_bruteforce():
+    m, k, n = 2, 256, 16
+    a = synthetic.activations(13, m, k)
+    qw = synthetic.qweight_words(14, k, n)
+    s = synthetic.scales(15, 2, n)
+    g_idx = synthetic.act_order_g_idx(16, k, 128)
+    want = gemm_bruteforce(a, codes_bruteforce(qw), s, [int(x) for x in g_idx])
+    got = ref.w4a16_gemm(a, qw, s, g_idx=g_idx)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_act_order_equals_plain_product_on_permuted_operands():
+    """Gathering A's columns and B's rows by perm = argsort(g_idx) leaves C unchanged."""
+    m, k, n = 4, 512, 32
+    a = synthetic.activations(17, m, k)
+    qw = synthetic.qweight_words(18, k, n)
+    s = synthetic.scales(19, k // 128, n)
+    g_idx = synthetic.act_order_g_idx(20, k, 128)
+    perm = sorted(range(k), key=lambda r: (int(g_idx[r]), r))
+    codes = codes_bruteforce(qw)
+    qw_perm = np.array([[hex_word([codes[perm[8 * r + i]][c] for i in range(8)])
+                         for c in range(n)] for r in range(k // 8)], dtype=np.uint32)
+    plain = ref.w4a16_gemm(a[:, perm], qw_perm, s)
+    ordered = ref.w4a16_gemm(a, qw, s, g_idx=g_idx)
+    np.testing.assert_allclose(ordered, plain, rtol=1e-12, atol=1e-12)
+    p, sorted_g = ref.act_order_perm(g_idx, 128)
+    assert p.tolist() == perm
+    assert sorted_g.tolist() == [i // 128 for i in range(k)]
+
+
+def test_act_order_perm_keeps_ties_in_row_order_and_rejects_uneven_groups():
+    g_idx = np.array([1, 0, 1, 0], dtype=np.int32)
+    p, sg = ref.act_order_perm(g_idx, 2)
+    assert p.tolist() == [1, 3, 0, 2] and sg.tolist() == [0, 0, 1, 1]
+    with pytest.raises(ValueError):
+        ref.act_order_perm(np.array([0, 0, 0, 1], dtype=np.int32), 2)
+
+
+def test_fp16_dequant_is_one_round_to_nearest_even():
+    s = synthetic.scales(21, 1, 64)[0]
+    for d in range(-15, 16):
+        q = np.full((1, 64), max(d, 0), dtype=np.uint8)
+        z = np.full((1, 64), max(-d, 0), dtype=np.uint8)
+        w = ref.dequantize(q, s[None, :], np.zeros(1, dtype=np.int64), z)
+        got = ref.dequantize_fp16(w)[0]
+        for c in range(64):
+            exact = d * float(s[c])
+            want = struct.unpack("<e", struct.pack("<e", exact))[0]
+            assert float(got[c]) == want
+
+
+# --------------------------------------------------------------------------- CSR
+
+def test_csr_worked_examples_from_page():
+    for case in golden_csr_cases():
+        if case["kind"] == "token_routes":
+            csr = ref.csr_from_token_routes(case["n_expert"][0], case["n_tokens"][0],
+                                            case["top_k"][0], case["selected"])
+        else:
+            csr = ref.csr_from_pair_rows(case["n_expert"][0], case["n_tokens"][0],
+                                         case["selected"], case["pair_tok_in"])
+        for key in ("ex_ids", "ex_off", "ex_pairs", "pair_tok"):
+            assert list(csr[key]) == case[key], key
+
+
+def test_csr_rejects_the_pages_bad_routes_and_parts():
+    with pytest.raises(ref.CsrError):
+        ref.csr_from_token_routes(4, 2, 3, [0, 1])
+    with pytest.raises(ref.CsrError):
+        ref.csr_from_pair_rows(2, 1, [2], [0])
+    with pytest.raises(ref.CsrError):
+        ref.csr_from_pair_rows(2, 1, [0], [1])
+    with pytest.raises(ref.CsrError):
+        ref.validate_csr(dict(ex_ids=[0, 1], ex_off=[0, 1, 2], ex_pairs=[0, 0],
+                              pair_tok=[0, 1], n_expert=2, n_tokens=2))
+    with pytest.raises(ref.CsrError):
+        ref.validate_csr(dict(ex_ids=[1, 0], ex_off=[0, 1, 2], ex_pairs=[0, 1],
+                              pair_tok=[0, 1], n_expert=2, n_tokens=2))
+
+
+def test_grouped_product_equals_dense_rows():
+    """Every pair's row equals the dense product of its token row with its expert."""
+    k, n, tokens, experts = 256, 32, 6, 3
+    a = synthetic.activations(22, tokens, k)
+    ex = [dict(qweight=synthetic.qweight_words(23 + e, k, n),
+               scales=synthetic.scales(30 + e, 2, n)) for e in range(experts)]
+    routes = np.array([[0, 2], [1, 0], [2, 1], [2, 0], [1, 2], [0, 1]])
+    csr = ref.csr_from_token_routes(experts, tokens, 2, routes)
+    y = ref.grouped_w4a16_gemm(a, ex, csr)
+    for p in range(2 * tokens):
+        t, e = p // 2, int(routes.reshape(-1)[p])
+        dense = ref.w4a16_gemm(a[t:t + 1], ex[e]["qweight"], ex[e]["scales"])
+        assert y[p].tolist() == dense[0].tolist()
+
+
+# --------------------------------------------------------------------------- checker
+
+def test_checker_accepts_exact_and_rejects_large_error_and_nan():
+    r = np.linspace(-3, 3, 64).reshape(8, 8)
+    good = r.astype(np.float16)
+    assert ref.check(good, r)["ok"]
+    bad = good.copy()
+    bad[3, 3] += np.float16(0.5)
+    out = ref.check(bad, r)
+    assert not out["ok"] and out["violations"] == 1
+    nan = good.copy()
+    nan[0, 0] = np.nan
+    assert ref.check(nan, r)["nonfinite"] == 1 and not ref.check(nan, r)["ok"]
+
+
+# --------------------------------------------------------------------------- layout
+
+def test_layout_words_by_hand():
+    """Rows 0..7 of column 0 carry codes 0..7: slots [0,4,1,5,2,6,3,7] give 0x75316420."""
+    k, n = 128, 16
+    codes = np.array([[kk % 16] * n for kk in range(k)], dtype=np.uint8)
+    words = layout.repack_b_loops(codes)
+    assert words[0] == 0x75316420          # lane 0, dword 0: rows 0..7
+    assert words[1] == 0x75316420          # lane 0, dword 1: rows 32..39
+    assert words[16 * 4] == 0xFDB9ECA8     # lane 16 (q = 1), dword 0: rows 8..15
+    assert words[1 * 4] == 0x75316420      # lane 1 is column 1, rows 0..7
+
+
+def test_layout_vectorized_matches_loops_and_round_trips():
+    k, n = 256, 32
+    qw = synthetic.qweight_words(40, k, n)
+    codes = ref.unpack_qweight(qw)
+    perm = synthetic.permutation(41, k)
+    for p in (None, perm):
+        loops = layout.repack_b_loops(codes, p)
+        vec = layout.repack_b(qw, p)
+        assert np.array_equal(loops, vec)
+        assert vec.size * 8 == k * n   # same byte count as the plain format
+        back = layout.unrepack_b(vec, k, n)
+        assert np.array_equal(back, codes if p is None else codes[p])
+
+
+def test_scale_and_zero_point_layouts():
+    s = synthetic.scales(42, 2, 32)
+    rs = layout.repack_scales(s)
+    for nb in range(2):
+        for g in range(2):
+            for c in range(16):
+                assert rs[(nb * 2 + g) * 16 + c] == s[g, 16 * nb + c]
+    z = synthetic.zero_point_words(43, 2, 32)
+    rz = layout.repack_zero_points(z)
+    for nb in range(2):
+        for g in range(2):
+            for h in range(2):
+                assert rz[(nb * 2 + g) * 2 + h] == z[g, 2 * nb + h]

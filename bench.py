@@ -1,0 +1,210 @@
+"""Benchmark of the W4A16 GEMM on one MI355X; prints one JSON line.
+
+Headline (value): packed-weight TB/s of the decode GEMM, M=1 K=4096 N=14336, u4b8, group
+128, split-K with the fp32 workspace reduce.  Each step is one wq_gemm call; steps rotate
+over enough weight copies that the weights stream from HBM rather than from the 256 MB
+Infinity Cache.  The same line carries the prefill (M=2048, act_order) TFLOP/s with its
+MFMA roofline, the batched-decode and grouped-MoE figures, and the oracle timed on the
+host cores as the CPU baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "weight TB/s at M=1 + TFLOP/s at M=2048 W4A16 g128; % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
+
+
+def timed_loop(torch, fn, steps: int, warmup: int) -> float:
+    """Seconds per step over `steps` calls after `warmup` calls (HIP events on the stream)."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(i)
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / 1e3 / steps
+
+
+def dense_setup(torch, torch_ops, name: str, copies: int):
+    import synthetic
+    case = synthetic.config_case(name)
+    w0 = torch_ops.PackedWeight(case["qweight"], case["scales"], case["zeros"], case["g_idx"],
+                                device="cuda")
+    weights = [w0] + [w0.clone() for _ in range(copies - 1)]
+    a = torch_ops.to_device(case["a"], "cuda")
+    out = torch.empty((case["m"], case["n"]), dtype=torch.float16, device="cuda")
+    bufs = torch_ops.GemmBuffers(w0, case["m"], case["fp32_reduce"])
+    torch.cuda.synchronize()
+    return case, weights, a, out, bufs
+
+
+def algorithmic_bytes(case) -> int:
+    m, k, n = case["m"], case["k"], case["n"]
+    b = k * n // 2 + (k // 128) * n * 2 + m * k * 2 + m * n * 2
+    if case["zeros"] is not None:
+        b += (k // 128) * n // 2
+    return b
+
+
+def bench_dense(torch, torch_ops, name, copies, steps, warmup):
+    case, weights, a, out, bufs = dense_setup(torch, torch_ops, name, copies)
+    fp32 = case["fp32_reduce"]
+
+    def step(i):
+        torch_ops.gemm(a, weights[i % len(weights)], out, fp32_reduce=fp32, buffers=bufs)
+
+    sec = timed_loop(torch, step, steps, warmup)
+    m, k, n = case["m"], case["k"], case["n"]
+    return dict(case=case, sec=sec, weight_bytes=k * n // 2, alg_bytes=algorithmic_bytes(case),
+                flops=2.0 * m * n * k)
+
+
+def bench_moe(torch, torch_ops, steps, warmup):
+    import synthetic
+    import weight_only_quantized_gemm_amd as wq
+    moe = synthetic.moe_case()
+    bank = torch_ops.ExpertBank(moe["experts"], device="cuda")
+    csr = wq.wq_csr_from_routes(moe["routes"], moe["n_tokens"], moe["top_k"], moe["n_expert"])
+    dcsr = {key: torch_ops.to_device(np.asarray(csr[key], np.int32), "cuda")
+            for key in ("ex_ids", "ex_off", "ex_pairs", "pair_tok")}
+    a = torch_ops.to_device(moe["a"], "cuda")
+    y = torch.empty((csr["n_pairs"], moe["n"]), dtype=torch.float16, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(i):
+        torch_ops.grouped_gemm(a, bank, csr, y, device_csr=dcsr)
+
+    sec = timed_loop(torch, step, steps, warmup)
+    flops = 2.0 * csr["n_pairs"] * moe["n"] * moe["k"]
+    return dict(sec=sec, flops=flops, weight_bytes=moe["n_expert"] * moe["k"] * moe["n"] // 2)
+
+
+def cpu_baseline(budget_s: float) -> dict:
+    """The oracle (fp64 numpy) on the decode workload, repeated for about `budget_s`."""
+    import synthetic
+    from oracle import reference as ref
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        blas = 1
+    case = synthetic.config_case("decode")
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        ref.w4a16_gemm(case["a"], case["qweight"], case["scales"])
+        runs += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    sec = (time.perf_counter() - t0) / runs
+    weight_bytes = case["k"] * case["n"] // 2
+    return {"value": weight_bytes / sec / 1e12, "unit": "TB/s", "cores": int(blas),
+            "kind": "oracle",
+            "sample": f"full decode problem M=1 K=4096 N=14336 (unpack, exact dequant, fp64 "
+                      f"matmul), {runs} runs in {sec * runs:.1f} s; {sec * 1e3:.0f} ms per run; "
+                      f"elementwise numpy on 1 thread, BLAS on {blas}"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["decode", "batched", "prefill", "moe", "tiny"],
+                    default=None, help="time one workload (profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        return 2
+
+    import torch
+    from weight_only_quantized_gemm_amd import torch_ops
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    if args.only:
+        if args.only == "moe":
+            r = bench_moe(torch, torch_ops, args.steps, args.warmup)
+            print(json.dumps({"only": "moe", "us": r["sec"] * 1e6,
+                              "tflops": r["flops"] / r["sec"] / 1e12}), flush=True)
+        else:
+            copies = {"decode": 12, "batched": 40}.get(args.only, 1)
+            r = bench_dense(torch, torch_ops, args.only, copies, args.steps, args.warmup)
+            print(json.dumps({"only": args.only, "us": r["sec"] * 1e6,
+                              "weight_tbs": r["weight_bytes"] / r["sec"] / 1e12,
+                              "tflops": r["flops"] / r["sec"] / 1e12}), flush=True)
+        return 0
+
+    dec = bench_dense(torch, torch_ops, "decode", 12, args.steps, args.warmup)
+    print(f"decode: {dec['sec'] * 1e6:.2f} us/call", file=sys.stderr, flush=True)
+    bat = bench_dense(torch, torch_ops, "batched", 40, args.steps, args.warmup)
+    print(f"batched: {bat['sec'] * 1e6:.2f} us/call", file=sys.stderr, flush=True)
+    pre_steps = max(10, args.steps // 4)
+    pre = bench_dense(torch, torch_ops, "prefill", 1, pre_steps, max(3, args.warmup // 4))
+    print(f"prefill: {pre['sec'] * 1e6:.1f} us/call", file=sys.stderr, flush=True)
+    moe = bench_moe(torch, torch_ops, pre_steps, max(3, args.warmup // 4))
+    print(f"moe: {moe['sec'] * 1e6:.1f} us/call", file=sys.stderr, flush=True)
+
+    tbs = dec["weight_bytes"] / dec["sec"] / 1e12
+    achieved = dec["alg_bytes"] / dec["sec"] / 1e9
+    pre_tflops = pre["flops"] / pre["sec"] / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(tbs, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dec["sec"] * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": "decode GEMM M=1 K=4096 N=14336 u4b8 group128 split-K fp32 "
+                               "reduce, 12 rotating weight copies",
+                   "m": 1, "k": 4096, "n": 14336, "weight_bytes": dec["weight_bytes"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+        "prefill": {"workload": "M=2048 K=4096 N=14336 u4b8 group128 act_order (gather + GEMM)",
+                    "tflops": round(pre_tflops, 2), "us": round(pre["sec"] * 1e6, 2),
+                    "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2),
+                                 "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": round(pre_tflops / MFMA_FP16_PEAK_TFLOPS, 4)}},
+        "batched": {"workload": "M=16 K=4096 N=4096 u4+zp group128 fp32 reduce, 40 copies",
+                    "us": round(bat["sec"] * 1e6, 3),
+                    "weight_tbs": round(bat["weight_bytes"] / bat["sec"] / 1e12, 4),
+                    "hbm_frac": round(bat["alg_bytes"] / bat["sec"] / 1e9 / HBM_PEAK_GBS, 4)},
+        "moe": {"workload": "1024 tokens top-2 of 8 experts K=4096 N=14336 u4b8 group128",
+                "us": round(moe["sec"] * 1e6, 2),
+                "tflops": round(moe["flops"] / moe["sec"] / 1e12, 2),
+                "mfma_frac": round(moe["flops"] / moe["sec"] / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.cpu_budget)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,211 @@
+/*
+ * wq.h -- C ABI of the MI355X (gfx950) W4A16 weight-only quantized GEMM library (libwq.so).
+ *
+ * Operation: C[m][n] = sum_k A[m][k] * W[k][n], W[k][n] = (q[k][n] - z) * s[g(k)][n],
+ * fp16 activations and output, fp32 accumulation, 4-bit codes q, fp16 group scales s,
+ * zero point z = 8 (symmetric "u4b8") or a per-group 4-bit code (asymmetric "u4").
+ * Sources: ferrum-kernels marlin.rs (module doc: Marlin INT4 x FP16 GEMM, K % 128 == 0,
+ * N % 256 == 0; `marlin_gemm` doc: C = A @ dequant(B)); ferrum-kernels vllm_marlin.rs
+ * (`FerrumMarlinLaunch`, the versioned launch problem this ABI is trimmed from; the scalar
+ * ids and flag bits; `ferrum_vllm_gptq_marlin_repack`); memra-engine mmq_ffi.rs
+ * (`ExpertCsr`, `memra_mmq_fp8_blk_grouped`: the expert-major grouped call).
+ *
+ * Conventions for every call:
+ *  - Device pointers are caller-owned and must stay valid until the work enqueued on
+ *    `stream` (a hipStream_t, NULL = the null stream) has completed.  Calls enqueue and
+ *    return: they never allocate, free or synchronize, and never abort the process.
+ *  - Return value: 0 on success, else (stage << 16) | code.  Stages: WQ_STAGE_ARGS and
+ *    WQ_STAGE_SHAPE carry a wq_error code; WQ_STAGE_DEVICE (device query),
+ *    WQ_STAGE_LAUNCH_CONFIG, WQ_STAGE_FUNC_ATTR and WQ_STAGE_LAUNCH carry the hipError_t.
+ *    This is the staged native status of ferrum-kernels marlin.rs (`marlin_moe_ffi_status`).
+ *  - Validation happens before any launch (fail closed); nothing is enqueued on error.
+ *  - Shapes: k % 128 == 0, n % 256 == 0, group_size == 128 (one group = 128 rows of K).
+ *
+ * Library weight layout (produced by the wq_repack_* calls; G = k / 128):
+ *  - B: k*n/8 uint32 words (k*n/2 bytes, the plain format's byte count).  For 16-column
+ *    block nb (columns 16*nb + c), 128-row chunk g, lane l = c + 16*qd (qd = 0..3) and
+ *    dword j = 0..3, word ((nb*G + g)*64 + l)*4 + j holds rows 128*g + 32*j + 8*qd + i
+ *    (i = 0..7) of column 16*nb + c; row offset i sits in nibble slot {0,4,1,5,2,6,3,7}[i].
+ *    One 16-byte load per lane then feeds four 16x16x32 fp16 MFMA B operands of a wave.
+ *  - scales: fp16 [n/16][G][16]; zero points: uint32 [n/16][G][2] (16 codes per pair,
+ *    column c of the block in bits 4*(c%8) of word c/8).
+ *  - act_order: B rows are stored in sorted order (row position i holds original row
+ *    perm[i]); sorted position i belongs to group i / 128 (see wq_act_order_perm).
+ */
+#ifndef WQ_H
+#define WQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WQ_ABI_VERSION 1u
+
+/* Flag bits: the bit positions of the vllm_marlin.rs launch flags. */
+#define WQ_FLAG_ACT_ORDER   (1u << 1) /* gather A by perm before the product              */
+#define WQ_FLAG_IS_K_FULL   (1u << 2) /* accepted, no effect: one GPU always holds all of K */
+#define WQ_FLAG_HAS_ZP      (1u << 3) /* u4 with per-group zero points (else u4b8)         */
+#define WQ_FLAG_ATOMIC_ADD  (1u << 4) /* not supported: rejected (non-deterministic sums)  */
+#define WQ_FLAG_FP32_REDUCE (1u << 5) /* allow split-K with an fp32 workspace reduce        */
+
+enum wq_stage {
+  WQ_STAGE_ARGS = 1,
+  WQ_STAGE_SHAPE = 2,
+  WQ_STAGE_DEVICE = 3,
+  WQ_STAGE_LAUNCH_CONFIG = 4,
+  WQ_STAGE_FUNC_ATTR = 5,
+  WQ_STAGE_LAUNCH = 6
+};
+
+enum wq_error {
+  WQ_ERR_NULL = 1,        /* a required pointer is NULL                                 */
+  WQ_ERR_ALIGN = 2,       /* a pointer is misaligned (16 B for fp16/packed, 4 B for ints) */
+  WQ_ERR_SHAPE = 3,       /* m/n/k/lda/group_size outside the supported set             */
+  WQ_ERR_FLAGS = 4,       /* unknown or unsupported flag, or flag/pointer mismatch      */
+  WQ_ERR_WORKSPACE = 5,   /* workspace missing or smaller than wq_*_workspace_bytes     */
+  WQ_ERR_ABI = 6,         /* abi_version / struct_size mismatch                         */
+  WQ_ERR_OVERFLOW = 7,    /* a byte extent overflows                                    */
+  WQ_ERR_CSR = 8,         /* expert-major CSR invariant violated                        */
+  WQ_ERR_ACT_ORDER = 9    /* g_idx does not give every group exactly group_size rows    */
+};
+
+#define WQ_STATUS(stage, code) ((int)(((unsigned)(stage) << 16) | ((unsigned)(code) & 0xFFFFu)))
+
+/* ABI version of the loaded library (WQ_ABI_VERSION). */
+uint32_t wq_abi_version(void);
+
+/* Static text naming a status: "ok", or "<stage>: <code>" (never NULL, never freed). */
+const char* wq_status_str(int status);
+
+/*
+ * Repack plain GPTQ words into the library's B layout (vllm_marlin.rs,
+ * `ferrum_vllm_gptq_marlin_repack`: same byte count, a pure permutation of the codes,
+ * optional row permutation for act_order).
+ *   qweight: device uint32 [k/8][n]; rows 8r..8r+7 of column c in word (r, c), row 8r+i
+ *            in bits 4i (low nibble first).
+ *   perm:    device int32 [k] or NULL; when given, row position i of the output is input
+ *            row perm[i] (perm must be a permutation of 0..k-1; entries are clamped into
+ *            range, so a bad perm gives wrong codes, never an out-of-bounds read).
+ *   b_out:   device, k*n/2 bytes, 16-byte aligned; must not overlap qweight.
+ */
+int wq_repack_b(const uint32_t* qweight, const int32_t* perm, void* b_out, int k, int n,
+                void* stream);
+
+/* Scales fp16 [k/group_size][n] row-major -> library layout fp16 [n/16][G][16]. */
+int wq_repack_scales(const void* scales, void* s_out, int k, int n, int group_size,
+                     void* stream);
+
+/*
+ * Zero points uint32 [k/group_size][n/8] (actual codes 0..15, column 8j+i in bits 4i of
+ * word j: vllm_marlin.rs `repack_gptq_qzeros_to_marlin`) -> library layout [n/16][G][2].
+ */
+int wq_repack_zeros(const uint32_t* zeros, void* z_out, int k, int n, int group_size,
+                    void* stream);
+
+/*
+ * act_order helper (host memory, synchronous): perm_out[i] = stable argsort(g_idx)[i]
+ * (marlin.rs `MarlinWeight.perm` doc: perm = argsort(g_idx)), sorted_gidx_out[i] =
+ * g_idx[perm[i]] (either output may be NULL).  Fails with WQ_ERR_ACT_ORDER unless every
+ * group 0..k/group_size-1 holds exactly group_size rows, the GPTQ construction, which
+ * makes sorted position i belong to group i / group_size.
+ */
+int wq_act_order_perm(const int32_t* g_idx, int k, int group_size, int32_t* perm_out,
+                      int32_t* sorted_gidx_out);
+
+/* Workspace bytes wq_gemm needs for (m, n, k, flags); 0 when no split-K can happen.
+ * The workspace must be zero-filled once after allocation; every completed call leaves
+ * its tile counters at zero again, so no per-call clearing is needed.  Calls that share
+ * one workspace must not run concurrently. */
+int wq_gemm_workspace_bytes(int m, int n, int k, uint32_t flags, size_t* bytes_out);
+
+typedef struct wq_gemm_args {
+  uint32_t abi_version;     /* WQ_ABI_VERSION                                          */
+  uint32_t struct_size;     /* sizeof(wq_gemm_args)                                   */
+  const void* a;            /* device fp16 [m][lda], 16-byte aligned rows               */
+  const void* b;            /* device, library B layout (wq_repack_b)                   */
+  void* c;                  /* device fp16 [m][n], output                               */
+  const void* b_scales;     /* device, library scale layout (wq_repack_scales)          */
+  const void* zero_points;  /* device, library zero-point layout, or NULL (u4b8)        */
+  const int32_t* perm;      /* device int32 [k] with WQ_FLAG_ACT_ORDER, else NULL       */
+  void* a_tmp;              /* device fp16 [m][k] gather scratch with act_order, else NULL */
+  void* workspace;          /* device scratch (wq_gemm_workspace_bytes), may be NULL if 0 */
+  size_t workspace_bytes;
+  void* stream;             /* hipStream_t                                              */
+  int32_t m, n, k;          /* m >= 1, n % 256 == 0, k % 128 == 0                        */
+  int32_t lda;              /* row stride of a in elements, >= k, multiple of 8         */
+  int32_t group_size;       /* 128                                                      */
+  uint32_t flags;           /* WQ_FLAG_*; HAS_ZP iff zero_points != NULL; ACT_ORDER iff perm */
+  int32_t split_k;          /* 0 = library's choice; 1 = no split; s > 1 requests s splits
+                               (needs WQ_FLAG_FP32_REDUCE; clamped to what k allows)     */
+  int32_t reserved;         /* must be 0                                                */
+} wq_gemm_args;
+
+/* C = A @ dequant(B) (all of it enqueued on args->stream). */
+int wq_gemm(const wq_gemm_args* args);
+
+/*
+ * Dequant export for bit-exact tests: reads library-layout B, scales and optional zero
+ * points and writes w[k][n] = fp16_rne((q - z) * s) (fp16, row-major, rows in the stored
+ * order, i.e. sorted order for act_order weights).  flags: only WQ_FLAG_HAS_ZP is read.
+ */
+int wq_dequant(const void* b, const void* b_scales, const void* zero_points, int k, int n,
+               int group_size, uint32_t flags, void* w_out, void* stream);
+
+/*
+ * Expert-major CSR from token-major top-k routes (host memory, synchronous), as
+ * mmq_ffi.rs `ExpertCsr::from_token_routes`: count pairs per expert, list non-empty
+ * experts ascending (ex_ids, n_active of them) with segment starts ex_off (n_active + 1
+ * entries, last = n_pairs), place pairs into segments in ascending pair order (ex_pairs),
+ * pair_tok[p] = p / top_k.  Capacities: ex_ids and ex_off hold n_expert (+1) entries,
+ * ex_pairs and pair_tok n_tokens*top_k.  Fails with WQ_ERR_CSR on an out-of-range expert.
+ */
+int wq_csr_from_routes(const int32_t* selected, int n_tokens, int top_k, int n_expert,
+                       int32_t* ex_ids, int32_t* ex_off, int32_t* ex_pairs, int32_t* pair_tok,
+                       int32_t* n_active_out);
+
+typedef struct wq_grouped_args {
+  uint32_t abi_version;
+  uint32_t struct_size;     /* sizeof(wq_grouped_args)                                  */
+  const void* a;            /* device fp16 [n_tokens][k]                                 */
+  const void* b_bank;       /* expert e's library-layout B at b_bank + e*b_stride_bytes  */
+  size_t b_stride_bytes;    /* >= k*n/2, multiple of 16                                  */
+  const void* s_bank;       /* expert e's scales at s_bank + e*s_stride_bytes            */
+  size_t s_stride_bytes;    /* >= (k/128)*n*2, multiple of 16                            */
+  const void* zp_bank;      /* expert e's zero points at zp_bank + e*zp_stride_bytes, or NULL */
+  size_t zp_stride_bytes;
+  const int32_t* ex_ids;    /* device [n_active] expert of each segment, or NULL = identity */
+  const int32_t* ex_off;    /* device [n_active + 1] segment starts into ex_pairs        */
+  const int32_t* ex_pairs;  /* device [n_pairs] pair ids grouped by expert               */
+  const int32_t* pair_tok;  /* device [n_pairs] activation row of each pair              */
+  void* y;                  /* device fp16 [n_pairs][n], pair-major output               */
+  void* workspace;          /* reserved for the grouped schedule; may be NULL            */
+  size_t workspace_bytes;
+  void* stream;
+  int32_t n_expert, n_active, n_pairs, n_tokens;
+  int32_t k, n, group_size;
+  uint32_t flags;           /* WQ_FLAG_HAS_ZP iff zp_bank != NULL                         */
+  int32_t reserved;
+} wq_grouped_args;
+
+/* Workspace bytes wq_grouped_gemm needs (currently 0 for every shape). */
+int wq_grouped_workspace_bytes(int n_pairs, int n_active, int n, int k, uint32_t flags,
+                               size_t* bytes_out);
+
+/*
+ * Grouped W4A16 product over an expert-major CSR (mmq_ffi.rs grouped projection call):
+ * for active segment i with expert e = ex_ids[i] (i when ex_ids is NULL) and each pair p
+ * in ex_pairs[ex_off[i] .. ex_off[i+1]), y[p][:] = A[pair_tok[p]][:] @ dequant(B_e).
+ * No top-k weight multiply.  The device CSR is not re-validated (that would need a
+ * host sync): build it with wq_csr_from_routes; entries out of range are skipped by the
+ * kernel (never read or written out of bounds), leaving those output rows unwritten.
+ */
+int wq_grouped_gemm(const wq_grouped_args* args);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQ_H */

@@ -1,0 +1,218 @@
+"""Host-side checks of the C ABI: exports, status codes, validation, host helpers.
+
+No GPU is needed: every call here either runs on the host (act_order perm, CSR builder,
+workspace sizing) or fails validation before anything is launched.  Fake device pointers
+(0x1000, 0x2000, ...) stand in for buffers, as in the pages' validation tests
+(ferrum-kernels marlin.rs test module).
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synthetic
+import weight_only_quantized_gemm_amd as wq
+from conftest import ROOT, golden_csr_cases
+from oracle import reference as ref
+
+STAGE_ARGS, STAGE_SHAPE = wq.WQ_STAGE_ARGS, wq.WQ_STAGE_SHAPE
+
+
+def status(stage, code):
+    return (stage << 16) | code
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(wq.LIB_PATH):
+        pytest.fail("libwq.so is not built (run __graft_entry__.build())")
+    return wq.lib()
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "wq.h")) as f:
+        text = f.read()
+    # declarations start a line: "<type> [*]wq_name(" with an optional const
+    return sorted(set(re.findall(r"^(?:const )?[a-z_0-9]+ ?\*? ?(wq_[a-z_0-9]+)\(", text,
+                                 flags=re.M)))
+
+
+def test_library_exports_every_declared_function(L):
+    names = declared_functions()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(wq.EXPORTED)
+
+
+def test_abi_version(L):
+    assert wq.wq_abi_version() == wq.WQ_ABI_VERSION == 1
+
+
+def test_status_strings_decode_stage_and_code(L):
+    assert wq.wq_status_str(0) == "ok"
+    assert wq.wq_status_str(status(STAGE_ARGS, wq.WQ_ERR_NULL)).startswith("args: null pointer")
+    assert "shape" in wq.wq_status_str(status(STAGE_SHAPE, wq.WQ_ERR_SHAPE))
+    assert wq.wq_status_str(status(6, 1)).startswith("kernel-launch:")
+    assert wq.wq_status_str(17).startswith("unknown")
+
+
+def gemm_args(**over):
+    base = dict(abi_version=1, struct_size=ctypes.sizeof(wq.wq_gemm_args), a=0x1000, b=0x2000,
+                c=0x3000, b_scales=0x4000, zero_points=None, perm=None, a_tmp=None,
+                workspace=None, workspace_bytes=0, stream=None, m=16, n=256, k=1024, lda=1024,
+                group_size=128, flags=0, split_k=0, reserved=0)
+    base.update(over)
+    return wq.wq_gemm_args(**base)
+
+
+def call_gemm(L, **over):
+    return L.wq_gemm(ctypes.byref(gemm_args(**over)))
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(a=None), status(STAGE_ARGS, wq.WQ_ERR_NULL)),
+    (dict(b=None), status(STAGE_ARGS, wq.WQ_ERR_NULL)),
+    (dict(c=None), status(STAGE_ARGS, wq.WQ_ERR_NULL)),
+    (dict(b_scales=None), status(STAGE_ARGS, wq.WQ_ERR_NULL)),
+    (dict(a=0x1002), status(STAGE_ARGS, wq.WQ_ERR_ALIGN)),
+    (dict(c=0x3008), status(STAGE_ARGS, wq.WQ_ERR_ALIGN)),
+    (dict(k=1000, lda=1000), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
+    (dict(n=320), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
+    (dict(m=0), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
+    (dict(lda=512), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
+    (dict(lda=1028), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
+    (dict(group_size=64), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
+    (dict(group_size=-1), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
+    (dict(flags=wq.WQ_FLAG_HAS_ZP), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
+    (dict(zero_points=0x5000), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
+    (dict(flags=wq.WQ_FLAG_HAS_ZP, zero_points=0x5008), status(STAGE_ARGS, wq.WQ_ERR_ALIGN)),
+    (dict(flags=wq.WQ_FLAG_ATOMIC_ADD), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
+    (dict(flags=1 << 9), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
+    (dict(flags=wq.WQ_FLAG_ACT_ORDER), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
+    (dict(perm=0x6000), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
+    (dict(flags=wq.WQ_FLAG_ACT_ORDER, perm=0x6000), status(STAGE_ARGS, wq.WQ_ERR_NULL)),
+    (dict(split_k=2), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
+    (dict(split_k=-1), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
+    (dict(flags=wq.WQ_FLAG_FP32_REDUCE, split_k=2), status(STAGE_ARGS, wq.WQ_ERR_WORKSPACE)),
+    (dict(flags=wq.WQ_FLAG_FP32_REDUCE, split_k=2, workspace=0x7000, workspace_bytes=16),
+     status(STAGE_ARGS, wq.WQ_ERR_WORKSPACE)),
+    (dict(abi_version=2), status(STAGE_ARGS, wq.WQ_ERR_ABI)),
+    (dict(struct_size=8), status(STAGE_ARGS, wq.WQ_ERR_ABI)),
+    (dict(reserved=1), status(STAGE_ARGS, wq.WQ_ERR_ABI)),
+])
+def test_gemm_rejects_bad_arguments_before_launch(L, over, expect):
+    assert call_gemm(L, **over) == expect
+
+
+def test_gemm_null_struct(L):
+    assert L.wq_gemm(None) == status(STAGE_ARGS, wq.WQ_ERR_NULL)
+
+
+def test_workspace_sizes():
+    fp32 = wq.WQ_FLAG_FP32_REDUCE
+    assert wq.wq_gemm_workspace_bytes(16, 4096, 4096, 0) == 0
+    assert wq.wq_gemm_workspace_bytes(2048, 14336, 4096, fp32) == 0
+    assert wq.wq_gemm_workspace_bytes(1, 256, 128, fp32) == 0   # one group: never split
+    ws = wq.wq_gemm_workspace_bytes(1, 14336, 4096, fp32)
+    assert ws >= 16 * 1 * 14336 * 4 + (14336 // 16) * 4
+    assert wq.wq_gemm_workspace_bytes(16, 4096, 4096, fp32) >= 16 * 16 * 4096 * 4
+    with pytest.raises(wq.WQError):
+        wq.wq_gemm_workspace_bytes(1, 100, 4096, fp32)
+
+
+def test_repack_and_dequant_validation(L):
+    assert L.wq_repack_b(None, None, 0x2000, 1024, 256, None) == status(STAGE_ARGS, wq.WQ_ERR_NULL)
+    assert L.wq_repack_b(0x1000, None, 0x2008, 1024, 256, None) == status(STAGE_ARGS,
+                                                                         wq.WQ_ERR_ALIGN)
+    assert L.wq_repack_b(0x1000, None, 0x2000, 1000, 256, None) == status(STAGE_SHAPE,
+                                                                         wq.WQ_ERR_SHAPE)
+    assert L.wq_repack_b(0x1000, 0x3002, 0x2000, 1024, 256, None) == status(STAGE_ARGS,
+                                                                           wq.WQ_ERR_ALIGN)
+    assert L.wq_repack_scales(0x1000, 0x2000, 1024, 256, 64, None) == status(STAGE_SHAPE,
+                                                                            wq.WQ_ERR_SHAPE)
+    assert L.wq_repack_zeros(0x1000, None, 1024, 256, 128, None) == status(STAGE_ARGS,
+                                                                          wq.WQ_ERR_NULL)
+    assert L.wq_dequant(0x1000, 0x2000, None, 1024, 256, 128, wq.WQ_FLAG_HAS_ZP, 0x3000,
+                        None) == status(STAGE_ARGS, wq.WQ_ERR_FLAGS)
+
+
+def test_act_order_perm_matches_oracle_and_rejects_uneven_groups():
+    for seed in (1, 2, 3):
+        g_idx = synthetic.act_order_g_idx(seed, 4096, 128)
+        perm, sorted_g = wq.wq_act_order_perm(g_idx, 128)
+        operm, osorted = ref.act_order_perm(g_idx, 128)
+        assert np.array_equal(perm, operm) and np.array_equal(sorted_g, osorted)
+    with pytest.raises(wq.WQError) as e:
+        wq.wq_act_order_perm(np.array([0, 0, 0, 1], np.int32), 2)
+    assert e.value.code == wq.WQ_ERR_ACT_ORDER
+    with pytest.raises(wq.WQError):
+        wq.wq_act_order_perm(np.array([0, 5, 0, 1], np.int32), 2)
+
+
+def test_csr_builder_reproduces_the_pages_examples():
+    for case in golden_csr_cases():
+        if case["kind"] != "token_routes":
+            continue
+        csr = wq.wq_csr_from_routes(case["selected"], case["n_tokens"][0], case["top_k"][0],
+                                    case["n_expert"][0])
+        for key in ("ex_ids", "ex_off", "ex_pairs", "pair_tok"):
+            assert csr[key].tolist() == case[key], key
+
+
+def test_csr_builder_matches_oracle_on_random_routes():
+    routes = synthetic.top2_routes(5, 1024, 8)
+    csr = wq.wq_csr_from_routes(routes, 1024, 2, 8)
+    ocsr = ref.csr_from_token_routes(8, 1024, 2, routes)
+    for key in ("ex_ids", "ex_off", "ex_pairs", "pair_tok"):
+        assert csr[key].tolist() == list(ocsr[key]), key
+    # inactive experts are left out
+    few = np.array([[1, 5]] * 7, dtype=np.int32)
+    csr = wq.wq_csr_from_routes(few, 7, 2, 8)
+    assert csr["ex_ids"].tolist() == [1, 5] and csr["ex_off"].tolist() == [0, 7, 14]
+
+
+def test_csr_builder_rejects_out_of_range_expert():
+    with pytest.raises(wq.WQError) as e:
+        wq.wq_csr_from_routes(np.array([0, 8], np.int32), 1, 2, 8)
+    assert e.value.code == wq.WQ_ERR_CSR
+
+
+def grouped_args(**over):
+    base = dict(abi_version=1, struct_size=ctypes.sizeof(wq.wq_grouped_args), a=0x1000,
+                b_bank=0x2000, b_stride_bytes=1024 * 256 // 2, s_bank=0x3000,
+                s_stride_bytes=8 * 256 * 2, zp_bank=None, zp_stride_bytes=0, ex_ids=None,
+                ex_off=0x4000, ex_pairs=0x5000, pair_tok=0x6000, y=0x7000, workspace=None,
+                workspace_bytes=0, stream=None, n_expert=2, n_active=2, n_pairs=4, n_tokens=2,
+                k=1024, n=256, group_size=128, flags=0, reserved=0)
+    base.update(over)
+    return wq.wq_grouped_args(**base)
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(a=None), status(STAGE_ARGS, wq.WQ_ERR_NULL)),
+    (dict(y=0x7004), status(STAGE_ARGS, wq.WQ_ERR_ALIGN)),
+    (dict(ex_off=None), status(STAGE_ARGS, wq.WQ_ERR_NULL)),
+    (dict(ex_pairs=0x5002), status(STAGE_ARGS, wq.WQ_ERR_ALIGN)),
+    (dict(n_active=3), status(STAGE_ARGS, wq.WQ_ERR_CSR)),
+    (dict(n_pairs=0), status(STAGE_ARGS, wq.WQ_ERR_CSR)),
+    (dict(n_tokens=0), status(STAGE_ARGS, wq.WQ_ERR_CSR)),
+    (dict(b_stride_bytes=1000), status(STAGE_ARGS, wq.WQ_ERR_SHAPE)),
+    (dict(s_stride_bytes=16), status(STAGE_ARGS, wq.WQ_ERR_SHAPE)),
+    (dict(flags=wq.WQ_FLAG_HAS_ZP), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
+    (dict(flags=wq.WQ_FLAG_ACT_ORDER), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
+    (dict(k=1000), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
+    (dict(struct_size=4), status(STAGE_ARGS, wq.WQ_ERR_ABI)),
+])
+def test_grouped_rejects_bad_arguments_before_launch(L, over, expect):
+    assert L.wq_grouped_gemm(ctypes.byref(grouped_args(**over))) == expect
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(wq, "_LIB", None)
+    monkeypatch.setattr(wq, "LIB_PATH", "/nonexistent/libwq.so")
+    with pytest.raises(RuntimeError):
+        wq.wq_abi_version()

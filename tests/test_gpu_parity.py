@@ -1,0 +1,292 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on an MI355X.
+
+Integer and byte work (repack, dequant export, integer-valued pins) must match bit for
+bit; GEMM outputs must satisfy max |C - ref| <= 2e-3 * rms(ref) + 1e-3 and
+||C - ref||_F / ||ref||_F <= 1e-3 with no non-finite value.
+"""
+
+import numpy as np
+import pytest
+
+import synthetic
+from oracle import layout
+from oracle import reference as ref
+
+torch = pytest.importorskip("torch")
+wq = pytest.importorskip("weight_only_quantized_gemm_amd")
+from weight_only_quantized_gemm_amd import torch_ops  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def say(*args):
+    print(*args, flush=True)
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def gpu_gemm(case, dev, *, fp32_reduce=False, split_k=0, a=None):
+    w = torch_ops.PackedWeight(case["qweight"], case["scales"], case.get("zeros"),
+                               case.get("g_idx"), device=dev)
+    a_d = torch_ops.to_device(case["a"] if a is None else a, dev)
+    c = torch_ops.gemm(a_d, w, fp32_reduce=fp32_reduce, split_k=split_k)
+    torch.cuda.synchronize()
+    return host(c)
+
+
+def oracle_gemm(case, columns=None):
+    return ref.w4a16_gemm(case["a"], case["qweight"], case["scales"], zeros=case.get("zeros"),
+                          g_idx=case.get("g_idx"), columns=columns)
+
+
+def assert_parity(c, want, label):
+    res = ref.check(c, want)
+    say(f"{label}: max_err={res['max_err']:.3e} tol={res['tol']:.3e} "
+        f"rel_frob={res['rel_frob']:.3e} nonfinite={res['nonfinite']}")
+    assert res["ok"], (label, res)
+
+
+# --------------------------------------------------------------------------- layout
+
+@pytest.mark.parametrize("k,n,use_perm", [(128, 256, False), (1024, 512, False),
+                                          (1024, 512, True), (4096, 4096, True)])
+def test_repack_matches_reference_layout_bitwise(dev, k, n, use_perm):
+    say(f"repack k={k} n={n} perm={use_perm}")
+    qw = synthetic.qweight_words(100 + k + n, k, n)
+    perm = synthetic.permutation(7, k).astype(np.int32) if use_perm else None
+    out = torch.empty(k * n // 8, dtype=torch.int32, device=dev)
+    wq.wq_repack_b(torch_ops.to_device(qw, dev), out, k, n,
+                   perm=None if perm is None else torch_ops.to_device(perm, dev))
+    torch.cuda.synchronize()
+    want = layout.repack_b(qw, perm)
+    assert np.array_equal(host(out).view(np.uint32), want)
+
+
+def test_scale_and_zero_repack_bitwise(dev):
+    k, n = 1024, 512
+    s = synthetic.scales(1, k // 128, n)
+    z = synthetic.zero_point_words(2, k // 128, n)
+    s_out = torch.empty(s.size, dtype=torch.float16, device=dev)
+    z_out = torch.empty(z.size, dtype=torch.int32, device=dev)
+    wq.wq_repack_scales(torch_ops.to_device(s, dev), s_out, k, n)
+    wq.wq_repack_zeros(torch_ops.to_device(z, dev), z_out, k, n)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(s_out).view(np.uint16), layout.repack_scales(s).view(np.uint16))
+    assert np.array_equal(host(z_out).view(np.uint32), layout.repack_zero_points(z))
+
+
+@pytest.mark.parametrize("zp,act_order", [(False, False), (True, False), (False, True)])
+def test_dequant_export_bitwise(dev, zp, act_order):
+    k, n = 1024, 512
+    say(f"dequant zp={zp} act_order={act_order}")
+    case = synthetic.dense_case(1, k, n, zp=zp, act_order=act_order, seed=11)
+    w = torch_ops.PackedWeight(case["qweight"], case["scales"], case["zeros"], case["g_idx"],
+                               device=dev)
+    out = torch.empty((k, n), dtype=torch.float16, device=dev)
+    wq.wq_dequant(w.b, w.s, w.z, out, k=k, n=n, flags=wq.WQ_FLAG_HAS_ZP if zp else 0)
+    torch.cuda.synchronize()
+    exact = ref.w4a16_weights(case["qweight"], case["scales"], zeros=case["zeros"],
+                              g_idx=case["g_idx"])
+    if act_order:
+        perm, _ = ref.act_order_perm(case["g_idx"], 128)
+        exact = exact[perm, :]
+    want = ref.dequantize_fp16(exact)
+    assert np.array_equal(host(out).view(np.uint16), want.view(np.uint16))
+
+
+# --------------------------------------------------------------------------- GEMM parity
+
+SMALL_SHAPES = [
+    # m, k, n, zp, act_order, fp32_reduce, split_k
+    (1, 128, 256, False, False, False, 0),
+    (1, 1024, 512, False, False, True, 0),
+    (1, 1024, 512, True, False, True, 3),
+    (3, 384, 256, True, False, False, 0),
+    (7, 1024, 768, False, True, True, 0),
+    (16, 1024, 256, False, False, False, 0),
+    (16, 2048, 512, True, False, True, 0),
+    (16, 2048, 512, False, False, True, 16),
+    (17, 1024, 256, False, False, False, 0),
+    (64, 512, 512, True, False, False, 0),
+    (100, 1024, 512, False, True, False, 0),
+    (255, 256, 256, False, False, False, 0),
+    (257, 1024, 512, True, False, False, 0),
+    (300, 640, 768, False, True, False, 0),
+    (513, 256, 256, False, False, False, 0),
+]
+
+
+@pytest.mark.parametrize("m,k,n,zp,act_order,fp32,split", SMALL_SHAPES)
+def test_gemm_matches_oracle_small(dev, m, k, n, zp, act_order, fp32, split):
+    label = f"gemm m={m} k={k} n={n} zp={zp} act_order={act_order} fp32={fp32} split={split}"
+    say(label)
+    case = synthetic.dense_case(m, k, n, zp=zp, act_order=act_order, seed=1000 + m + k + n)
+    c = gpu_gemm(case, dev, fp32_reduce=fp32, split_k=split)
+    assert_parity(c, oracle_gemm(case), label)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "batched"])
+def test_config_matches_oracle_in_full(dev, name):
+    case = synthetic.config_case(name)
+    say(f"config {name}: m={case['m']} k={case['k']} n={case['n']}")
+    c = gpu_gemm(case, dev, fp32_reduce=case["fp32_reduce"])
+    assert_parity(c, oracle_gemm(case), name)
+
+
+def sample_columns(n, seed, count=256):
+    cols = set(range(0, 128)) | set(range(n - 128, n))
+    cols |= set(int(x) for x in synthetic.below(seed, count, n))
+    return np.array(sorted(cols))
+
+
+def test_prefill_config_matches_oracle_on_sampled_columns(dev):
+    case = synthetic.config_case("prefill")
+    say("config prefill: m=2048 k=4096 n=14336 act_order, sampled columns")
+    c = gpu_gemm(case, dev)
+    cols = sample_columns(case["n"], 5)
+    assert_parity(c[:, cols], oracle_gemm(case, columns=cols), "prefill")
+    assert np.isfinite(c).all()
+
+
+# --------------------------------------------------------------------------- pins
+
+def test_all_eight_codes_give_exact_zero(dev):
+    for m in (1, 16, 300):
+        case = synthetic.dense_case(m, 512, 256, seed=3)
+        case["qweight"][:] = 0x88888888
+        c = gpu_gemm(case, dev, fp32_reduce=True)
+        assert np.all(c.astype(np.float64) == 0.0), m
+
+
+def test_unit_scales_integer_products_are_bit_exact(dev):
+    for m in (1, 16, 40):
+        k, n = 1024, 256
+        case = synthetic.dense_case(m, k, n, seed=4)
+        case["a"] = (synthetic.below(5, m * k, 3) - 1).reshape(m, k).astype(np.float16)
+        case["scales"] = np.ones_like(case["scales"])
+        want = oracle_gemm(case)
+        assert np.abs(want).max() <= 2048   # every integer below this is exact in fp16
+        c = gpu_gemm(case, dev, fp32_reduce=True)
+        assert np.array_equal(c.astype(np.float64), want), m
+
+
+def test_one_hot_rows_give_dequantized_rows_bitwise(dev):
+    k, n = 1024, 512
+    rows = [0, 1, 127, 128, 500, 1023]
+    for zp in (False, True):
+        case = synthetic.dense_case(len(rows), k, n, zp=zp, seed=6)
+        a = np.zeros((len(rows), k), dtype=np.float16)
+        for i, r in enumerate(rows):
+            a[i, r] = 1.0
+        case["a"] = a
+        c = gpu_gemm(case, dev)
+        exact = ref.w4a16_weights(case["qweight"], case["scales"], zeros=case["zeros"])
+        want = ref.dequantize_fp16(exact[rows, :])
+        assert np.array_equal(c.view(np.uint16), want.view(np.uint16)), zp
+
+
+def test_results_are_deterministic_and_split_independent(dev):
+    for m, zp in ((1, False), (16, True)):
+        case = synthetic.dense_case(m, 4096, 1024, zp=zp, seed=8)
+        c1 = gpu_gemm(case, dev, fp32_reduce=True)
+        c2 = gpu_gemm(case, dev, fp32_reduce=True)
+        assert np.array_equal(c1.view(np.uint16), c2.view(np.uint16))
+        want = oracle_gemm(case)
+        for split in (1, 2, 5, 16):
+            assert_parity(gpu_gemm(case, dev, fp32_reduce=True, split_k=split), want,
+                          f"m={m} split={split}")
+
+
+def test_act_order_equals_plain_product_on_permuted_operands(dev):
+    k, n = 1024, 512
+    for m in (4, 300):
+        case = synthetic.dense_case(m, k, n, act_order=True, seed=9)
+        perm, _ = ref.act_order_perm(case["g_idx"], 128)
+        c_act = gpu_gemm(case, dev)
+        codes = ref.unpack_qweight(case["qweight"])[perm, :]
+        packed = np.zeros((k // 8, n), dtype=np.uint32)
+        for i in range(8):
+            packed |= codes[i::8].astype(np.uint32) << np.uint32(4 * i)
+        plain = dict(case, qweight=packed, g_idx=None)
+        c_plain = gpu_gemm(plain, dev, a=np.ascontiguousarray(case["a"][:, perm]))
+        assert_parity(c_act, c_plain.astype(np.float64), f"act_order vs plain m={m}")
+
+
+def test_strided_activations(dev):
+    m, k, n = 20, 512, 256
+    case = synthetic.dense_case(m, k, n, seed=12)
+    w = torch_ops.PackedWeight(case["qweight"], case["scales"], device=dev)
+    wide = torch.zeros((m, k + 64), dtype=torch.float16, device=dev)
+    wide[:, :k] = torch_ops.to_device(case["a"], dev)
+    c = torch_ops.gemm(wide[:, :k], w)
+    torch.cuda.synchronize()
+    assert_parity(host(c), oracle_gemm(case), "lda > k")
+
+
+# --------------------------------------------------------------------------- grouped (MoE)
+
+def run_grouped(moe, dev, zeros=None):
+    experts = [dict(e) for e in moe["experts"]]
+    if zeros is not None:
+        for e, z in zip(experts, zeros):
+            e["zeros"] = z
+    bank = torch_ops.ExpertBank(experts, device=dev)
+    csr = wq.wq_csr_from_routes(moe["routes"], moe["n_tokens"], moe["top_k"], moe["n_expert"])
+    a = torch_ops.to_device(moe["a"], dev)
+    y = torch_ops.grouped_gemm(a, bank, csr)
+    torch.cuda.synchronize()
+    ocsr = ref.csr_from_token_routes(moe["n_expert"], moe["n_tokens"], moe["top_k"],
+                                     moe["routes"])
+    return host(y), experts, ocsr
+
+
+@pytest.mark.parametrize("tokens,experts,k,n,zp", [(40, 4, 256, 256, False),
+                                                   (300, 3, 512, 512, True),
+                                                   (700, 2, 256, 256, False)])
+def test_grouped_matches_oracle(dev, tokens, experts, k, n, zp):
+    label = f"grouped tokens={tokens} experts={experts} k={k} n={n} zp={zp}"
+    say(label)
+    moe = synthetic.moe_case(tokens, experts, k, n, seed=200 + tokens)
+    zeros = ([synthetic.zero_point_words(300 + e, k // 128, n) for e in range(experts)]
+             if zp else None)
+    y, ex, ocsr = run_grouped(moe, dev, zeros)
+    assert_parity(y, ref.grouped_w4a16_gemm(moe["a"], ex, ocsr), label)
+
+
+def test_grouped_skips_inactive_experts(dev):
+    moe = synthetic.moe_case(50, 6, 256, 256, seed=21)
+    moe["routes"] = np.where(moe["routes"] % 2 == 0, 4, 1).astype(np.int32)
+    moe["routes"][:, 1] = np.where(moe["routes"][:, 0] == 4, 1, 4)
+    y, ex, ocsr = run_grouped(moe, dev)
+    assert list(ocsr["ex_ids"]) == [1, 4]
+    assert_parity(y, ref.grouped_w4a16_gemm(moe["a"], ex, ocsr), "inactive experts")
+
+
+def test_grouped_single_expert_equals_dense(dev):
+    k, n, tokens = 512, 512, 270
+    moe = synthetic.moe_case(tokens, 1, k, n, seed=22)
+    bank = torch_ops.ExpertBank(moe["experts"], device=dev)
+    csr = wq.wq_csr_from_routes(np.zeros(tokens, np.int32), tokens, 1, 1)
+    a = torch_ops.to_device(moe["a"], dev)
+    y = host(torch_ops.grouped_gemm(a, bank, csr))
+    dense = gpu_gemm(dict(a=moe["a"], qweight=moe["experts"][0]["qweight"],
+                          scales=moe["experts"][0]["scales"]), dev)
+    assert np.array_equal(y.view(np.uint16), dense.view(np.uint16))
+
+
+def test_moe_config_matches_oracle_on_sampled_columns(dev):
+    say("config moe: 1024 tokens top-2 of 8 experts, k=4096 n=14336, sampled columns")
+    moe = synthetic.moe_case()
+    y, ex, ocsr = run_grouped(moe, dev)
+    cols = sample_columns(moe["n"], 6, 128)
+    want = ref.grouped_w4a16_gemm(moe["a"], ex, ocsr, columns=cols)
+    assert_parity(y[:, cols], want, "moe")
+    assert np.isfinite(y).all()

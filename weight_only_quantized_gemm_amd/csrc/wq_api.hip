@@ -1,0 +1,384 @@
+// C ABI of libwq: argument validation, planning and launches (see include/wq.h).
+//
+// Validation mirrors the fail-closed launch checks of ferrum-kernels marlin.rs
+// (`MarlinMoeRawLaunchArgs::validate`: non-null and aligned pointers, positive shapes,
+// group size rules, zero-point flag/pointer agreement, fp32-reduce/scratch agreement)
+// and returns the staged status of `marlin_moe_ffi_status` instead of aborting.
+#include <stdio.h>
+#include <string.h>
+
+#include <limits>
+#include <vector>
+
+#include "wq.h"
+#include "wq_internal.h"
+
+namespace {
+
+constexpr int kGroupSize = 128;
+constexpr int kMaxSplits = 16;        // fp32 partial slots per output element
+constexpr size_t kCounterBytes = 256; // alignment of the partials after the counters
+
+int fail(int stage, int code) { return WQ_STATUS(stage, code); }
+int hip_fail(hipError_t e) { return fail(WQ_STAGE_LAUNCH, (int)e); }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_ptr(const void* p, size_t align) {
+  if (p == nullptr) return fail(WQ_STAGE_ARGS, WQ_ERR_NULL);
+  if (!aligned(p, align)) return fail(WQ_STAGE_ARGS, WQ_ERR_ALIGN);
+  return 0;
+}
+
+// k % 128 == 0, n % 256 == 0, group_size == 128, and byte extents that fit.
+int check_kn(int k, int n, int group_size) {
+  if (k <= 0 || n <= 0 || k % kGroupSize != 0 || n % 256 != 0)
+    return fail(WQ_STAGE_SHAPE, WQ_ERR_SHAPE);
+  if (group_size != kGroupSize) return fail(WQ_STAGE_SHAPE, WQ_ERR_SHAPE);
+  if ((long long)k * n / 8 > (long long)std::numeric_limits<int32_t>::max() * 4LL)
+    return fail(WQ_STAGE_SHAPE, WQ_ERR_OVERFLOW);
+  return 0;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// --- planning of the small-M kernel ------------------------------------------------------
+
+int small_splits(int n, int k, uint32_t flags, int requested) {
+  const int groups = k / kGroupSize;
+  if (!(flags & WQ_FLAG_FP32_REDUCE)) return 1;
+  int s;
+  if (requested > 0) {
+    s = requested;
+  } else {
+    // Enough work-groups to keep every CU streaming: aim for ~1024 (four per CU).
+    const int col_blocks = n / 16;
+    s = (1024 + col_blocks - 1) / col_blocks;
+    // Keep at least one group per wave of a split.
+    const int max_s = groups / 4 > 0 ? groups / 4 : 1;
+    if (s > max_s) s = max_s;
+  }
+  if (s > groups) s = groups;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return s < 1 ? 1 : s;
+}
+
+wq::SmallPlan plan_small(int m, int n, int k, uint32_t flags, int requested) {
+  wq::SmallPlan p{};
+  p.nb = 1;
+  p.splits = small_splits(n, k, flags, requested);
+  const int groups = k / kGroupSize;
+  const int per_wave = (groups / p.splits + 3) / 4;
+  p.depth = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 8;
+  (void)m;
+  return p;
+}
+
+size_t gemm_workspace_bytes(int m, int n, int k, uint32_t flags) {
+  if (m > 16 || !(flags & WQ_FLAG_FP32_REDUCE)) return 0;
+  int smax = k / kGroupSize;
+  if (smax > kMaxSplits) smax = kMaxSplits;
+  if (smax <= 1) return 0;
+  return kCounterBytes * (((size_t)(n / 16) * 4 + kCounterBytes - 1) / kCounterBytes) +
+         (size_t)smax * m * n * sizeof(float);
+}
+
+const char* stage_name(int stage) {
+  switch (stage) {
+    case WQ_STAGE_ARGS: return "args";
+    case WQ_STAGE_SHAPE: return "shape";
+    case WQ_STAGE_DEVICE: return "device-query";
+    case WQ_STAGE_LAUNCH_CONFIG: return "launch-config";
+    case WQ_STAGE_FUNC_ATTR: return "function-attribute";
+    case WQ_STAGE_LAUNCH: return "kernel-launch";
+    default: return "unknown";
+  }
+}
+
+const char* error_name(int code) {
+  switch (code) {
+    case WQ_ERR_NULL: return "null pointer";
+    case WQ_ERR_ALIGN: return "misaligned pointer";
+    case WQ_ERR_SHAPE: return "unsupported shape";
+    case WQ_ERR_FLAGS: return "unsupported or inconsistent flags";
+    case WQ_ERR_WORKSPACE: return "workspace too small";
+    case WQ_ERR_ABI: return "abi version or struct size mismatch";
+    case WQ_ERR_OVERFLOW: return "size overflow";
+    case WQ_ERR_CSR: return "invalid expert CSR";
+    case WQ_ERR_ACT_ORDER: return "act_order groups are not group_size rows each";
+    default: return "unknown error";
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t wq_abi_version(void) { return WQ_ABI_VERSION; }
+
+const char* wq_status_str(int status) {
+  static thread_local char buf[160];
+  if (status == 0) return "ok";
+  const int stage = (int)((unsigned)status >> 16);
+  const int code = (int)((unsigned)status & 0xFFFFu);
+  if (stage == WQ_STAGE_ARGS || stage == WQ_STAGE_SHAPE)
+    snprintf(buf, sizeof buf, "%s: %s (%d)", stage_name(stage), error_name(code), code);
+  else if (stage >= WQ_STAGE_DEVICE && stage <= WQ_STAGE_LAUNCH)
+    snprintf(buf, sizeof buf, "%s: %s (%d)", stage_name(stage),
+             hipGetErrorString((hipError_t)code), code);
+  else
+    snprintf(buf, sizeof buf, "unknown: %d", status);
+  return buf;
+}
+
+int wq_repack_b(const uint32_t* qweight, const int32_t* perm, void* b_out, int k, int n,
+                void* stream) {
+  int st = check_kn(k, n, kGroupSize);
+  if (st) return st;
+  if ((st = check_ptr(qweight, 4))) return st;
+  if ((st = check_ptr(b_out, 16))) return st;
+  if (perm && !aligned(perm, 4)) return fail(WQ_STAGE_ARGS, WQ_ERR_ALIGN);
+  const hipError_t e = wq::launch_repack_b(qweight, perm, static_cast<uint32_t*>(b_out), k, n,
+                                           as_stream(stream));
+  return e == hipSuccess ? 0 : hip_fail(e);
+}
+
+int wq_repack_scales(const void* scales, void* s_out, int k, int n, int group_size,
+                     void* stream) {
+  int st = check_kn(k, n, group_size);
+  if (st) return st;
+  if ((st = check_ptr(scales, 2))) return st;
+  if ((st = check_ptr(s_out, 16))) return st;
+  const hipError_t e =
+      wq::launch_repack_scales(static_cast<const uint16_t*>(scales), static_cast<uint16_t*>(s_out),
+                               k, n, as_stream(stream));
+  return e == hipSuccess ? 0 : hip_fail(e);
+}
+
+int wq_repack_zeros(const uint32_t* zeros, void* z_out, int k, int n, int group_size,
+                    void* stream) {
+  int st = check_kn(k, n, group_size);
+  if (st) return st;
+  if ((st = check_ptr(zeros, 4))) return st;
+  if ((st = check_ptr(z_out, 16))) return st;
+  const hipError_t e = wq::launch_repack_zeros(zeros, static_cast<uint32_t*>(z_out), k, n,
+                                               as_stream(stream));
+  return e == hipSuccess ? 0 : hip_fail(e);
+}
+
+int wq_act_order_perm(const int32_t* g_idx, int k, int group_size, int32_t* perm_out,
+                      int32_t* sorted_gidx_out) {
+  if (g_idx == nullptr) return fail(WQ_STAGE_ARGS, WQ_ERR_NULL);
+  if (k <= 0 || group_size <= 0 || k % group_size != 0) return fail(WQ_STAGE_SHAPE, WQ_ERR_SHAPE);
+  const int groups = k / group_size;
+  // Counting sort by group keeps equal groups in ascending row order (a stable argsort).
+  std::vector<int> count(groups + 1, 0);
+  for (int r = 0; r < k; ++r) {
+    const int g = g_idx[r];
+    if (g < 0 || g >= groups) return fail(WQ_STAGE_ARGS, WQ_ERR_ACT_ORDER);
+    ++count[g + 1];
+  }
+  for (int g = 0; g < groups; ++g)
+    if (count[g + 1] != group_size) return fail(WQ_STAGE_ARGS, WQ_ERR_ACT_ORDER);
+  for (int g = 0; g < groups; ++g) count[g + 1] += count[g];
+  for (int r = 0; r < k; ++r) {
+    const int pos = count[g_idx[r]]++;
+    if (perm_out) perm_out[pos] = r;
+    if (sorted_gidx_out) sorted_gidx_out[pos] = g_idx[r];
+  }
+  return 0;
+}
+
+int wq_gemm_workspace_bytes(int m, int n, int k, uint32_t flags, size_t* bytes_out) {
+  if (bytes_out == nullptr) return fail(WQ_STAGE_ARGS, WQ_ERR_NULL);
+  if (m <= 0) return fail(WQ_STAGE_SHAPE, WQ_ERR_SHAPE);
+  const int st = check_kn(k, n, kGroupSize);
+  if (st) return st;
+  *bytes_out = gemm_workspace_bytes(m, n, k, flags);
+  return 0;
+}
+
+int wq_gemm(const wq_gemm_args* args) {
+  if (args == nullptr) return fail(WQ_STAGE_ARGS, WQ_ERR_NULL);
+  if (args->abi_version != WQ_ABI_VERSION || args->struct_size != sizeof(wq_gemm_args) ||
+      args->reserved != 0)
+    return fail(WQ_STAGE_ARGS, WQ_ERR_ABI);
+  const wq_gemm_args& p = *args;
+  const uint32_t known = WQ_FLAG_ACT_ORDER | WQ_FLAG_IS_K_FULL | WQ_FLAG_HAS_ZP |
+                         WQ_FLAG_ATOMIC_ADD | WQ_FLAG_FP32_REDUCE;
+  if ((p.flags & ~known) || (p.flags & WQ_FLAG_ATOMIC_ADD)) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
+  int st = check_kn(p.k, p.n, p.group_size);
+  if (st) return st;
+  if (p.m <= 0 || p.lda < p.k || p.lda % 8 != 0) return fail(WQ_STAGE_SHAPE, WQ_ERR_SHAPE);
+  if ((long long)p.m * p.lda > (long long)std::numeric_limits<int64_t>::max() / 4 ||
+      (long long)(p.m + 255) / 256 > 65535)
+    return fail(WQ_STAGE_SHAPE, WQ_ERR_OVERFLOW);
+  if ((st = check_ptr(p.a, 16)) || (st = check_ptr(p.b, 16)) || (st = check_ptr(p.c, 16)) ||
+      (st = check_ptr(p.b_scales, 16)))
+    return st;
+  const bool has_zp = (p.flags & WQ_FLAG_HAS_ZP) != 0;
+  if (has_zp != (p.zero_points != nullptr)) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
+  if (has_zp && (st = check_ptr(p.zero_points, 16))) return st;
+  const bool act_order = (p.flags & WQ_FLAG_ACT_ORDER) != 0;
+  if (act_order != (p.perm != nullptr)) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
+  if (act_order) {
+    if ((st = check_ptr(p.perm, 16))) return st;
+    if ((st = check_ptr(p.a_tmp, 16))) return st;
+  }
+  if (p.split_k < 0) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
+  if (p.split_k > 1 && !(p.flags & WQ_FLAG_FP32_REDUCE)) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
+
+  const hipStream_t stream = as_stream(p.stream);
+  const uint16_t* a = static_cast<const uint16_t*>(p.a);
+  int lda = p.lda;
+  if (act_order) {
+    const hipError_t e = wq::launch_gather_columns(a, lda, p.perm, static_cast<uint16_t*>(p.a_tmp),
+                                                   p.m, p.k, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    a = static_cast<const uint16_t*>(p.a_tmp);
+    lda = p.k;
+  }
+  const uint32_t* b = static_cast<const uint32_t*>(p.b);
+  const uint16_t* s = static_cast<const uint16_t*>(p.b_scales);
+  const uint32_t* z = static_cast<const uint32_t*>(p.zero_points);
+  uint16_t* c = static_cast<uint16_t*>(p.c);
+
+  if (p.m <= 16) {
+    const wq::SmallPlan plan = plan_small(p.m, p.n, p.k, p.flags, p.split_k);
+    float* partials = nullptr;
+    int32_t* counters = nullptr;
+    if (plan.splits > 1) {
+      const size_t need = gemm_workspace_bytes(p.m, p.n, p.k, p.flags);
+      if (p.workspace == nullptr || p.workspace_bytes < need || need == 0)
+        return fail(WQ_STAGE_ARGS, WQ_ERR_WORKSPACE);
+      if (!aligned(p.workspace, 256)) return fail(WQ_STAGE_ARGS, WQ_ERR_ALIGN);
+      counters = static_cast<int32_t*>(p.workspace);
+      partials = reinterpret_cast<float*>(
+          static_cast<char*>(p.workspace) +
+          kCounterBytes * (((size_t)(p.n / 16) * 4 + kCounterBytes - 1) / kCounterBytes));
+    }
+    const hipError_t e = wq::launch_gemm_small(a, lda, p.m, b, s, z, c, p.n, p.k, plan, partials,
+                                               counters, stream);
+    return e == hipSuccess ? 0 : hip_fail(e);
+  }
+  const hipError_t e = wq::launch_gemm_tile(a, lda, p.m, b, s, z, c, p.n, p.k, stream);
+  return e == hipSuccess ? 0 : hip_fail(e);
+}
+
+int wq_dequant(const void* b, const void* b_scales, const void* zero_points, int k, int n,
+               int group_size, uint32_t flags, void* w_out, void* stream) {
+  int st = check_kn(k, n, group_size);
+  if (st) return st;
+  if ((st = check_ptr(b, 16)) || (st = check_ptr(b_scales, 16)) || (st = check_ptr(w_out, 16)))
+    return st;
+  const bool has_zp = (flags & WQ_FLAG_HAS_ZP) != 0;
+  if (has_zp != (zero_points != nullptr)) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
+  if (has_zp && (st = check_ptr(zero_points, 16))) return st;
+  const hipError_t e = wq::launch_dequant(
+      static_cast<const uint32_t*>(b), static_cast<const uint16_t*>(b_scales),
+      static_cast<const uint32_t*>(zero_points), k, n, static_cast<uint16_t*>(w_out),
+      as_stream(stream));
+  return e == hipSuccess ? 0 : hip_fail(e);
+}
+
+int wq_csr_from_routes(const int32_t* selected, int n_tokens, int top_k, int n_expert,
+                       int32_t* ex_ids, int32_t* ex_off, int32_t* ex_pairs, int32_t* pair_tok,
+                       int32_t* n_active_out) {
+  if (!selected || !ex_ids || !ex_off || !ex_pairs || !pair_tok || !n_active_out)
+    return fail(WQ_STAGE_ARGS, WQ_ERR_NULL);
+  if (n_tokens <= 0 || top_k <= 0 || n_expert <= 0) return fail(WQ_STAGE_ARGS, WQ_ERR_CSR);
+  const long long pairs = (long long)n_tokens * top_k;
+  if (pairs > std::numeric_limits<int32_t>::max()) return fail(WQ_STAGE_ARGS, WQ_ERR_OVERFLOW);
+  const int n_pairs = (int)pairs;
+  std::vector<int> count(n_expert + 1, 0);
+  for (int p = 0; p < n_pairs; ++p) {
+    const int e = selected[p];
+    if (e < 0 || e >= n_expert) return fail(WQ_STAGE_ARGS, WQ_ERR_CSR);
+    ++count[e + 1];
+  }
+  for (int e = 0; e < n_expert; ++e) count[e + 1] += count[e];
+  int active = 0;
+  for (int e = 0; e < n_expert; ++e) {
+    if (count[e + 1] > count[e]) {
+      ex_ids[active] = e;
+      ex_off[active] = count[e];
+      ++active;
+    }
+  }
+  ex_off[active] = n_pairs;
+  for (int p = 0; p < n_pairs; ++p) {
+    ex_pairs[count[selected[p]]++] = p;
+    pair_tok[p] = p / top_k;
+  }
+  *n_active_out = active;
+  return 0;
+}
+
+int wq_grouped_workspace_bytes(int n_pairs, int n_active, int n, int k, uint32_t flags,
+                               size_t* bytes_out) {
+  (void)flags;
+  if (bytes_out == nullptr) return fail(WQ_STAGE_ARGS, WQ_ERR_NULL);
+  if (n_pairs <= 0 || n_active <= 0) return fail(WQ_STAGE_SHAPE, WQ_ERR_SHAPE);
+  const int st = check_kn(k, n, kGroupSize);
+  if (st) return st;
+  *bytes_out = 0;
+  return 0;
+}
+
+int wq_grouped_gemm(const wq_grouped_args* args) {
+  if (args == nullptr) return fail(WQ_STAGE_ARGS, WQ_ERR_NULL);
+  if (args->abi_version != WQ_ABI_VERSION || args->struct_size != sizeof(wq_grouped_args) ||
+      args->reserved != 0)
+    return fail(WQ_STAGE_ARGS, WQ_ERR_ABI);
+  const wq_grouped_args& p = *args;
+  if (p.flags & ~(uint32_t)(WQ_FLAG_HAS_ZP | WQ_FLAG_IS_K_FULL))
+    return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
+  int st = check_kn(p.k, p.n, p.group_size);
+  if (st) return st;
+  if (p.n_expert <= 0 || p.n_active <= 0 || p.n_active > p.n_expert || p.n_pairs <= 0 ||
+      p.n_tokens <= 0 || p.n_active > p.n_pairs)
+    return fail(WQ_STAGE_ARGS, WQ_ERR_CSR);
+  if ((st = check_ptr(p.a, 16)) || (st = check_ptr(p.b_bank, 16)) ||
+      (st = check_ptr(p.s_bank, 16)) || (st = check_ptr(p.y, 16)) ||
+      (st = check_ptr(p.ex_off, 4)) || (st = check_ptr(p.ex_pairs, 4)) ||
+      (st = check_ptr(p.pair_tok, 4)))
+    return st;
+  if (p.ex_ids && !aligned(p.ex_ids, 4)) return fail(WQ_STAGE_ARGS, WQ_ERR_ALIGN);
+  const bool has_zp = (p.flags & WQ_FLAG_HAS_ZP) != 0;
+  if (has_zp != (p.zp_bank != nullptr)) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
+  if (has_zp && (st = check_ptr(p.zp_bank, 16))) return st;
+  const size_t groups = (size_t)(p.k / kGroupSize);
+  const size_t b_bytes = (size_t)p.k * p.n / 2;
+  const size_t s_bytes = groups * p.n * 2;
+  const size_t z_bytes = groups * p.n / 2;
+  if (p.b_stride_bytes < b_bytes || p.b_stride_bytes % 16 || p.s_stride_bytes < s_bytes ||
+      p.s_stride_bytes % 16 || (has_zp && (p.zp_stride_bytes < z_bytes || p.zp_stride_bytes % 16)))
+    return fail(WQ_STAGE_ARGS, WQ_ERR_SHAPE);
+  const long long tiles =
+      ((long long)(p.n_pairs + wq::kTileM - 1) / wq::kTileM + p.n_active) * (p.n / wq::kTileN);
+  if (tiles > std::numeric_limits<int32_t>::max()) return fail(WQ_STAGE_SHAPE, WQ_ERR_OVERFLOW);
+
+  wq::GroupedProblem g{};
+  g.a = static_cast<const uint16_t*>(p.a);
+  g.b_bank = static_cast<const uint8_t*>(p.b_bank);
+  g.b_stride = p.b_stride_bytes;
+  g.s_bank = static_cast<const uint8_t*>(p.s_bank);
+  g.s_stride = p.s_stride_bytes;
+  g.z_bank = static_cast<const uint8_t*>(p.zp_bank);
+  g.z_stride = p.zp_stride_bytes;
+  g.ex_ids = p.ex_ids;
+  g.ex_off = p.ex_off;
+  g.ex_pairs = p.ex_pairs;
+  g.pair_tok = p.pair_tok;
+  g.y = static_cast<uint16_t*>(p.y);
+  g.n_expert = p.n_expert;
+  g.n_active = p.n_active;
+  g.n_pairs = p.n_pairs;
+  g.n_tokens = p.n_tokens;
+  g.k = p.k;
+  g.n = p.n;
+  const hipError_t e = wq::launch_grouped_tile(g, as_stream(p.stream));
+  return e == hipSuccess ? 0 : hip_fail(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Host-side launchers of the kernels, shared between the kernel files and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wq {
+
+// Repack / export / gather kernels (wq_repack.hip).
+hipError_t launch_repack_b(const uint32_t* qweight, const int32_t* perm, uint32_t* out, int k,
+                           int n, hipStream_t stream);
+hipError_t launch_repack_scales(const uint16_t* s, uint16_t* out, int k, int n,
+                                hipStream_t stream);
+hipError_t launch_repack_zeros(const uint32_t* z, uint32_t* out, int k, int n,
+                               hipStream_t stream);
+hipError_t launch_dequant(const uint32_t* b, const uint16_t* s, const uint32_t* z, int k, int n,
+                          uint16_t* w, hipStream_t stream);
+hipError_t launch_gather_columns(const uint16_t* a, int lda, const int32_t* perm, uint16_t* out,
+                                 int m, int k, hipStream_t stream);
+
+// Small-M kernel (wq_gemm_small.hip): m <= 16, one 16-row MFMA block, split-K over
+// `splits` work-groups per column block with an fp32 partial reduce.
+struct SmallPlan {
+  int nb;          // 16-column blocks per work-group
+  int splits;      // work-groups along K per column block
+  int depth;       // groups of K prefetched per wave per batch
+};
+hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* b,
+                             const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
+                             const SmallPlan& plan, float* partials, int32_t* counters,
+                             hipStream_t stream);
+
+// Tiled kernel (wq_gemm_tile.hip): 256 x 128 output tiles on 4 waves of 128 x 64.
+constexpr int kTileM = 256;
+constexpr int kTileN = 128;
+hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b,
+                            const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
+                            hipStream_t stream);
+
+struct GroupedProblem {
+  const uint16_t* a;
+  const uint8_t* b_bank;
+  size_t b_stride;
+  const uint8_t* s_bank;
+  size_t s_stride;
+  const uint8_t* z_bank;  // may be null
+  size_t z_stride;
+  const int32_t* ex_ids;  // may be null
+  const int32_t* ex_off;
+  const int32_t* ex_pairs;
+  const int32_t* pair_tok;
+  uint16_t* y;
+  int n_expert, n_active, n_pairs, n_tokens, k, n;
+};
+hipError_t launch_grouped_tile(const GroupedProblem& p, hipStream_t stream);
+
+}  // namespace wq

@@ -1,0 +1,189 @@
+// Offline repack of plain GPTQ weights, scales and zero points into the library layout,
+// the dequant export used by bit-exact tests, and the act_order column gather.
+//
+// The repack is a pure permutation of the 4-bit codes with an optional row permutation
+// (ferrum-kernels vllm_marlin.rs, `ferrum_vllm_gptq_marlin_repack` doc: same byte count;
+// marlin.rs, `MarlinWeight.perm` doc: weight rows stored in argsort(g_idx) order).  The
+// target order is this library's own (see include/wq.h), built here by a direct index
+// formula per output word.
+#include "wq_device.h"
+#include "wq_internal.h"
+
+namespace wq {
+namespace {
+
+// Row offset i of a layout word lives in nibble slot (i even ? i/2 : 4 + i/2).
+__device__ __forceinline__ uint32_t place_codes(const uint32_t codes[8]) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w |= codes[i] << (4 * ((i & 1) ? 4 + (i >> 1) : (i >> 1)));
+  return w;
+}
+
+__global__ __launch_bounds__(256) void repack_b_kernel(const uint32_t* __restrict__ qweight,
+                                                       const int32_t* __restrict__ perm,
+                                                       uint32_t* __restrict__ out, int k, int n) {
+  const long total = (long)k * n / 8;
+  const int groups = k / kGroup;
+  for (long o = (long)blockIdx.x * blockDim.x + threadIdx.x; o < total;
+       o += (long)gridDim.x * blockDim.x) {
+    const int j = (int)(o & 3);
+    const int lane = (int)((o >> 2) & 63);
+    const long rest = o >> 8;
+    const int g = (int)(rest % groups);
+    const long nb = rest / groups;
+    const int col = (int)(nb * 16 + (lane & 15));
+    const int row0 = g * kGroup + 32 * j + 8 * (lane >> 4);
+    uint32_t codes[8];
+    if (perm == nullptr) {
+      const uint32_t src = qweight[(long)(row0 >> 3) * n + col];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) codes[i] = (src >> (4 * i)) & 0xFu;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        int r = perm[row0 + i];
+        r = r < 0 ? 0 : (r >= k ? k - 1 : r);
+        codes[i] = (qweight[(long)(r >> 3) * n + col] >> (4 * (r & 7))) & 0xFu;
+      }
+    }
+    out[o] = place_codes(codes);
+  }
+}
+
+__global__ __launch_bounds__(256) void repack_scales_kernel(const uint16_t* __restrict__ s,
+                                                            uint16_t* __restrict__ out, int k,
+                                                            int n) {
+  const int groups = k / kGroup;
+  const long total = (long)groups * n;
+  for (long o = (long)blockIdx.x * blockDim.x + threadIdx.x; o < total;
+       o += (long)gridDim.x * blockDim.x) {
+    const int c = (int)(o & 15);
+    const long rest = o >> 4;
+    const int g = (int)(rest % groups);
+    const long nb = rest / groups;
+    out[o] = s[(long)g * n + nb * 16 + c];
+  }
+}
+
+__global__ __launch_bounds__(256) void repack_zeros_kernel(const uint32_t* __restrict__ z,
+                                                           uint32_t* __restrict__ out, int k,
+                                                           int n) {
+  const int groups = k / kGroup;
+  const long total = (long)groups * (n / 8);
+  for (long o = (long)blockIdx.x * blockDim.x + threadIdx.x; o < total;
+       o += (long)gridDim.x * blockDim.x) {
+    const int h = (int)(o & 1);
+    const long rest = o >> 1;
+    const int g = (int)(rest % groups);
+    const long nb = rest / groups;
+    out[o] = z[(long)g * (n / 8) + nb * 2 + h];
+  }
+}
+
+// w[row][col] = fp16_rne((q - z) * s): the product is exact in fp32 (5-bit integer times
+// an fp16 value), so the single conversion to fp16 is the only rounding.
+__global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict__ b,
+                                                      const uint16_t* __restrict__ s,
+                                                      const uint32_t* __restrict__ z, int k,
+                                                      int n, uint16_t* __restrict__ w) {
+  const long total = (long)k * n / 8;
+  const int groups = k / kGroup;
+  for (long o = (long)blockIdx.x * blockDim.x + threadIdx.x; o < total;
+       o += (long)gridDim.x * blockDim.x) {
+    const int j = (int)(o & 3);
+    const int lane = (int)((o >> 2) & 63);
+    const long rest = o >> 8;
+    const int g = (int)(rest % groups);
+    const long nb = rest / groups;
+    const int c = lane & 15;
+    const long col = nb * 16 + c;
+    const int row0 = g * kGroup + 32 * j + 8 * (lane >> 4);
+    const long blk = nb * groups + g;
+    const float scale = (float)__builtin_bit_cast(f16, s[blk * 16 + c]);
+    int zc = 8;
+    if (z != nullptr) zc = zero_code(u32x2{z[blk * 2], z[blk * 2 + 1]}, c);
+    const uint32_t word = b[o];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int slot = (i & 1) ? 4 + (i >> 1) : (i >> 1);
+      const int q = (int)((word >> (4 * slot)) & 0xFu);
+      const f16 v = (f16)((float)(q - zc) * scale);
+      w[(long)(row0 + i) * n + col] = __builtin_bit_cast(uint16_t, v);
+    }
+  }
+}
+
+// out[r][i] = a[r][perm[i]] for the act_order gather (eight columns per thread).
+__global__ __launch_bounds__(256) void gather_columns_kernel(const uint16_t* __restrict__ a,
+                                                             int lda,
+                                                             const int32_t* __restrict__ perm,
+                                                             uint16_t* __restrict__ out, int m,
+                                                             int k) {
+  const int per_row = k / 8;
+  const long total = (long)m * per_row;
+  for (long t = (long)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (long)gridDim.x * blockDim.x) {
+    const long r = t / per_row;
+    const int i0 = (int)(t % per_row) * 8;
+    const i32x4 p0 = *reinterpret_cast<const i32x4*>(perm + i0);
+    const i32x4 p1 = *reinterpret_cast<const i32x4*>(perm + i0 + 4);
+    const uint16_t* row = a + r * lda;
+    uint16_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int c = j < 4 ? p0[j] : p1[j - 4];
+      c = c < 0 ? 0 : (c >= k ? k - 1 : c);
+      v[j] = row[c];
+    }
+    u32x4 packed;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) packed[j] = (uint32_t)v[2 * j] | ((uint32_t)v[2 * j + 1] << 16);
+    *reinterpret_cast<u32x4*>(out + r * k + i0) = packed;
+  }
+}
+
+int grid_for(long work) {
+  long blocks = (work + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  return (int)(blocks < 1 ? 1 : blocks);
+}
+
+}  // namespace
+
+hipError_t launch_repack_b(const uint32_t* qweight, const int32_t* perm, uint32_t* out, int k,
+                           int n, hipStream_t stream) {
+  hipLaunchKernelGGL(repack_b_kernel, dim3(grid_for((long)k * n / 8)), dim3(256), 0, stream,
+                     qweight, perm, out, k, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_repack_scales(const uint16_t* s, uint16_t* out, int k, int n,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL(repack_scales_kernel, dim3(grid_for((long)(k / kGroup) * n)), dim3(256), 0,
+                     stream, s, out, k, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_repack_zeros(const uint32_t* z, uint32_t* out, int k, int n,
+                               hipStream_t stream) {
+  hipLaunchKernelGGL(repack_zeros_kernel, dim3(grid_for((long)(k / kGroup) * (n / 8))),
+                     dim3(256), 0, stream, z, out, k, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint32_t* b, const uint16_t* s, const uint32_t* z, int k, int n,
+                          uint16_t* w, hipStream_t stream) {
+  hipLaunchKernelGGL(dequant_kernel, dim3(grid_for((long)k * n / 8)), dim3(256), 0, stream, b, s,
+                     z, k, n, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_columns(const uint16_t* a, int lda, const int32_t* perm, uint16_t* out,
+                                 int m, int k, hipStream_t stream) {
+  hipLaunchKernelGGL(gather_columns_kernel, dim3(grid_for((long)m * (k / 8))), dim3(256), 0,
+                     stream, a, lda, perm, out, m, k);
+  return hipGetLastError();
+}
+
+}  // namespace wq

@@ -1,0 +1,133 @@
+"""Device-memory plumbing around libwq with PyTorch tensors.
+
+PyTorch only allocates device buffers and supplies the stream; every operation on the
+data (repack, gather, GEMM, reduce) is a libwq kernel called through the binding.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import (WQ_FLAG_ACT_ORDER, WQ_FLAG_FP32_REDUCE, WQ_FLAG_HAS_ZP, wq_act_order_perm,
+               wq_gemm, wq_gemm_workspace_bytes, wq_grouped_gemm, wq_repack_b,
+               wq_repack_scales, wq_repack_zeros)
+
+GROUP = 128
+
+
+def to_device(x: np.ndarray, device) -> torch.Tensor:
+    """Upload a numpy array; uint32 words travel as int32 (same bits)."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint32:
+        x = x.view(np.int32)
+    return torch.from_numpy(x).to(device)
+
+
+class PackedWeight:
+    """One weight matrix in the library layout (B, scales, optional zero points, perm)."""
+
+    def __init__(self, qweight: np.ndarray, scales: np.ndarray, zeros: np.ndarray | None = None,
+                 g_idx: np.ndarray | None = None, device="cuda"):
+        self.k = qweight.shape[0] * 8
+        self.n = qweight.shape[1]
+        self.device = torch.device(device)
+        self.perm = None
+        if g_idx is not None:
+            perm, _ = wq_act_order_perm(g_idx, GROUP)
+            self.perm = to_device(perm, self.device)
+        qw = to_device(qweight, self.device)
+        self.b = torch.empty(self.k * self.n // 8, dtype=torch.int32, device=self.device)
+        wq_repack_b(qw, self.b, self.k, self.n, perm=self.perm)
+        sc = to_device(np.asarray(scales, dtype=np.float16), self.device)
+        self.s = torch.empty((self.k // GROUP) * self.n, dtype=torch.float16, device=self.device)
+        wq_repack_scales(sc, self.s, self.k, self.n, GROUP)
+        self.z = None
+        if zeros is not None:
+            zw = to_device(zeros, self.device)
+            self.z = torch.empty((self.k // GROUP) * self.n // 8, dtype=torch.int32,
+                                 device=self.device)
+            wq_repack_zeros(zw, self.z, self.k, self.n, GROUP)
+        torch.cuda.synchronize(self.device)
+
+    def clone(self) -> "PackedWeight":
+        """A second copy of the device buffers (same values, new memory)."""
+        other = object.__new__(PackedWeight)
+        other.__dict__.update(self.__dict__)
+        other.b = self.b.clone()
+        other.s = self.s.clone()
+        other.z = None if self.z is None else self.z.clone()
+        return other
+
+    def flags(self, fp32_reduce: bool = False) -> int:
+        f = 0
+        if self.z is not None:
+            f |= WQ_FLAG_HAS_ZP
+        if self.perm is not None:
+            f |= WQ_FLAG_ACT_ORDER
+        if fp32_reduce:
+            f |= WQ_FLAG_FP32_REDUCE
+        return f
+
+
+class GemmBuffers:
+    """Scratch a call needs: the act_order gather buffer and the split-K workspace."""
+
+    def __init__(self, w: PackedWeight, m: int, fp32_reduce: bool):
+        self.flags = w.flags(fp32_reduce)
+        self.a_tmp = (torch.empty((m, w.k), dtype=torch.float16, device=w.device)
+                      if w.perm is not None else None)
+        nbytes = wq_gemm_workspace_bytes(m, w.n, w.k, self.flags)
+        self.workspace = (torch.zeros(nbytes, dtype=torch.uint8, device=w.device)
+                          if nbytes else None)
+
+
+def gemm(a: torch.Tensor, w: PackedWeight, out: torch.Tensor | None = None, *,
+         fp32_reduce: bool = False, split_k: int = 0, buffers: GemmBuffers | None = None,
+         stream=None) -> torch.Tensor:
+    """C = A @ dequant(B) through wq_gemm (A fp16 [m][k], row stride a.stride(0))."""
+    m = a.shape[0]
+    if out is None:
+        out = torch.empty((m, w.n), dtype=torch.float16, device=a.device)
+    if buffers is None:
+        buffers = GemmBuffers(w, m, fp32_reduce)
+    wq_gemm(a, w.b, out, w.s, m=m, n=w.n, k=w.k, zero_points=w.z, perm=w.perm,
+            a_tmp=buffers.a_tmp, workspace=buffers.workspace, flags=buffers.flags,
+            split_k=split_k, lda=a.stride(0), stream=stream)
+    return out
+
+
+class ExpertBank:
+    """Repacked weights of several experts stored back to back (one stride per tensor)."""
+
+    def __init__(self, experts: list[dict], device="cuda"):
+        self.packed = [PackedWeight(e["qweight"], e["scales"], e.get("zeros"), device=device)
+                       for e in experts]
+        p0 = self.packed[0]
+        self.k, self.n = p0.k, p0.n
+        self.b = torch.stack([p.b for p in self.packed])
+        self.s = torch.stack([p.s for p in self.packed])
+        self.z = torch.stack([p.z for p in self.packed]) if p0.z is not None else None
+        self.packed = None  # the stacked copies are the bank
+        self.b_stride = self.b.stride(0) * self.b.element_size()
+        self.s_stride = self.s.stride(0) * self.s.element_size()
+        self.z_stride = 0 if self.z is None else self.z.stride(0) * self.z.element_size()
+        self.n_expert = self.b.shape[0]
+
+
+def grouped_gemm(a: torch.Tensor, bank: ExpertBank, csr: dict, out: torch.Tensor | None = None,
+                 device_csr: dict | None = None, stream=None) -> torch.Tensor:
+    """Pair-major y = grouped product over an expert-major CSR (host dict from the library)."""
+    if device_csr is None:
+        device_csr = {key: to_device(np.asarray(csr[key], dtype=np.int32), a.device)
+                      for key in ("ex_ids", "ex_off", "ex_pairs", "pair_tok")}
+    n_pairs = len(csr["ex_pairs"])
+    if out is None:
+        out = torch.empty((n_pairs, bank.n), dtype=torch.float16, device=a.device)
+    wq_grouped_gemm(a, bank.b, bank.b_stride, bank.s, bank.s_stride, device_csr["ex_ids"],
+                    device_csr["ex_off"], device_csr["ex_pairs"], device_csr["pair_tok"], out,
+                    n_expert=bank.n_expert, n_active=len(csr["ex_ids"]), n_pairs=n_pairs,
+                    n_tokens=a.shape[0], k=bank.k, n=bank.n, zp_bank=bank.z,
+                    zp_stride_bytes=bank.z_stride,
+                    flags=WQ_FLAG_HAS_ZP if bank.z is not None else 0, stream=stream)
+    return out

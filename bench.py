@@ -27,15 +27,29 @@ MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
 
 
 def timed_loop(torch, fn, steps: int, warmup: int) -> float:
-    """Seconds per step over `steps` calls after `warmup` calls (HIP events on the stream)."""
-    for i in range(warmup):
-        fn(i)
+    """Seconds per step over `steps` calls after `warmup` eager calls.
+
+    The timed calls are captured once into a HIP graph and replayed, so that host-side
+    launch overhead (Python, ctypes) does not hide the kernels' own time; the replay is
+    bracketed by HIP events on the stream the kernels run on.
+    """
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(warmup):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            fn(i)
+    graph.replay()                      # one untimed replay
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record()
-    for i in range(steps):
-        fn(i)
+    graph.replay()
     stop.record()
     torch.cuda.synchronize()
     return start.elapsed_time(stop) / 1e3 / steps

@@ -115,10 +115,10 @@ int wq_repack_zeros(const uint32_t* zeros, void* z_out, int k, int n, int group_
 int wq_act_order_perm(const int32_t* g_idx, int k, int group_size, int32_t* perm_out,
                       int32_t* sorted_gidx_out);
 
-/* Workspace bytes wq_gemm needs for (m, n, k, flags); 0 when no split-K can happen.
- * The workspace must be zero-filled once after allocation; every completed call leaves
- * its tile counters at zero again, so no per-call clearing is needed.  Calls that share
- * one workspace must not run concurrently. */
+/* Workspace bytes wq_gemm needs for (m, n, k, flags): room for the fp32 split-K partials
+ * of the largest split the library may choose (0 when it never splits: m > 16 or no
+ * WQ_FLAG_FP32_REDUCE).  Contents need no initialization; calls that share one workspace
+ * must not run concurrently. */
 int wq_gemm_workspace_bytes(int m, int n, int k, uint32_t flags, size_t* bytes_out);
 
 typedef struct wq_gemm_args {
@@ -139,7 +139,8 @@ typedef struct wq_gemm_args {
   int32_t group_size;       /* 128                                                      */
   uint32_t flags;           /* WQ_FLAG_*; HAS_ZP iff zero_points != NULL; ACT_ORDER iff perm */
   int32_t split_k;          /* 0 = library's choice; 1 = no split; s > 1 requests s splits
-                               (needs WQ_FLAG_FP32_REDUCE; clamped to what k allows)     */
+                               along K for m <= 16 (needs WQ_FLAG_FP32_REDUCE; clamped to
+                               k/128 and 16); partials are added in split order          */
   int32_t reserved;         /* must be 0                                                */
 } wq_gemm_args;
 

@@ -205,5 +205,6 @@ def moe_case(n_tokens: int = 1024, n_expert: int = 8, k: int = 4096, n: int = 14
         n_tokens=n_tokens, n_expert=n_expert, top_k=2, k=k, n=n, group_size=group_size,
         a=activations(stream_seed(root, TAG_ACT), n_tokens, k),
         experts=experts,
-        routes=top2_routes(stream_seed(root, TAG_ROUTE), n_tokens, n_expert),
+        routes=(top2_routes(stream_seed(root, TAG_ROUTE), n_tokens, n_expert) if n_expert > 1
+                else np.zeros((n_tokens, 2), dtype=np.int32)),
     )

@@ -290,3 +290,33 @@ def test_moe_config_matches_oracle_on_sampled_columns(dev):
     want = ref.grouped_w4a16_gemm(moe["a"], ex, ocsr, columns=cols)
     assert_parity(y[:, cols], want, "moe")
     assert np.isfinite(y).all()
+
+
+# --------------------------------------------------------------------------- graph replay
+
+@pytest.mark.parametrize("m,fp32", [(1, True), (16, True), (300, False)])
+def test_graph_replays_match_eager(dev, m, fp32):
+    """Captured calls replay bit-identically, with eager work between replays."""
+    case = synthetic.dense_case(m, 2048, 512, zp=(m == 16), act_order=(m == 300), seed=31)
+    w = torch_ops.PackedWeight(case["qweight"], case["scales"], case["zeros"], case["g_idx"],
+                               device=dev)
+    a = torch_ops.to_device(case["a"], dev)
+    bufs = torch_ops.GemmBuffers(w, m, fp32)
+    eager = host(torch_ops.gemm(a, w, fp32_reduce=fp32, buffers=bufs))
+    out = torch.empty((m, w.n), dtype=torch.float16, device=dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        torch_ops.gemm(a, w, out, fp32_reduce=fp32, buffers=bufs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        torch_ops.gemm(a, w, out, fp32_reduce=fp32, buffers=bufs)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out).view(np.uint16), eager.view(np.uint16)), rep
+        torch_ops.gemm(a, w, fp32_reduce=fp32, buffers=bufs)   # eager work in between
+        torch.cuda.synchronize()

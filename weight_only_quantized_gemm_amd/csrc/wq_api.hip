@@ -16,8 +16,7 @@
 namespace {
 
 constexpr int kGroupSize = 128;
-constexpr int kMaxSplits = 16;        // fp32 partial slots per output element
-constexpr size_t kCounterBytes = 256; // alignment of the partials after the counters
+constexpr int kMaxSplits = 16;  // fp32 partial slots per output element
 
 int fail(int stage, int code) { return WQ_STATUS(stage, code); }
 int hip_fail(hipError_t e) { return fail(WQ_STAGE_LAUNCH, (int)e); }
@@ -44,43 +43,51 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 // --- planning of the small-M kernel ------------------------------------------------------
 
-int small_splits(int n, int k, uint32_t flags, int requested) {
+// Plan of the small-M kernel, or false when no plan fits its staging limits (the tiled
+// kernel then computes the product).  Without WQ_FLAG_FP32_REDUCE the product is never
+// split (every output is one work-group's fp32 sum, rounded once).  With it, a requested
+// split count is honoured, raised if the activation slice would not fit in LDS; the
+// library's own choice splits only when the 16-column blocks alone give fewer than ~512
+// work-groups (two per CU), since every split adds an fp32 partial round trip and a reduce
+// launch.  Each split's groups are shared by 4, 8 or 16 waves, at most 8 groups per wave.
+bool plan_small(int m, int n, int k, uint32_t flags, int requested, wq::SmallPlan* plan) {
   const int groups = k / kGroupSize;
-  if (!(flags & WQ_FLAG_FP32_REDUCE)) return 1;
-  int s;
-  if (requested > 0) {
+  const bool fp32 = (flags & WQ_FLAG_FP32_REDUCE) != 0;
+  int s = 1;
+  if (fp32 && requested > 0) {
     s = requested;
-  } else {
-    // Enough work-groups to keep every CU streaming: aim for ~1024 (four per CU).
+  } else if (fp32) {
     const int col_blocks = n / 16;
-    s = (1024 + col_blocks - 1) / col_blocks;
-    // Keep at least one group per wave of a split.
-    const int max_s = groups / 4 > 0 ? groups / 4 : 1;
+    s = col_blocks >= 512 ? 1 : (512 + col_blocks - 1) / col_blocks;
+    const int max_s = groups / 4 > 0 ? groups / 4 : 1;  // keep a group per wave of a split
     if (s > max_s) s = max_s;
   }
-  if (s > groups) s = groups;
-  if (s > kMaxSplits) s = kMaxSplits;
-  return s < 1 ? 1 : s;
+  for (; s <= groups && s <= kMaxSplits; ++s) {
+    if (s > 1 && !fp32) return false;
+    const int span = (groups + s - 1) / s;
+    for (int waves = 4; waves <= 16; waves *= 2) {
+      const int per_wave = (span + waves - 1) / waves;
+      if (per_wave > 8) continue;
+      wq::SmallPlan p{};
+      p.waves = waves;
+      p.splits = s;
+      p.depth = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 8;
+      if (wq::small_plan_fits(m, k, p)) {
+        *plan = p;
+        return true;
+      }
+    }
+  }
+  return false;
 }
 
-wq::SmallPlan plan_small(int m, int n, int k, uint32_t flags, int requested) {
-  wq::SmallPlan p{};
-  p.nb = 1;
-  p.splits = small_splits(n, k, flags, requested);
-  const int groups = k / kGroupSize;
-  const int per_wave = (groups / p.splits + 3) / 4;
-  p.depth = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 8;
-  (void)m;
-  return p;
-}
-
+// fp32 partials [splits][m][n] for the largest split the small-M path may use.
 size_t gemm_workspace_bytes(int m, int n, int k, uint32_t flags) {
   if (m > 16 || !(flags & WQ_FLAG_FP32_REDUCE)) return 0;
   int smax = k / kGroupSize;
   if (smax > kMaxSplits) smax = kMaxSplits;
   if (smax <= 1) return 0;
-  return kCounterBytes * (((size_t)(n / 16) * 4 + kCounterBytes - 1) / kCounterBytes) +
-         (size_t)smax * m * n * sizeof(float);
+  return (size_t)smax * m * n * sizeof(float);
 }
 
 const char* stage_name(int stage) {
@@ -243,22 +250,18 @@ int wq_gemm(const wq_gemm_args* args) {
   const uint32_t* z = static_cast<const uint32_t*>(p.zero_points);
   uint16_t* c = static_cast<uint16_t*>(p.c);
 
-  if (p.m <= 16) {
-    const wq::SmallPlan plan = plan_small(p.m, p.n, p.k, p.flags, p.split_k);
+  wq::SmallPlan plan{};
+  if (p.m <= 16 && plan_small(p.m, p.n, p.k, p.flags, p.split_k, &plan)) {
     float* partials = nullptr;
-    int32_t* counters = nullptr;
     if (plan.splits > 1) {
-      const size_t need = gemm_workspace_bytes(p.m, p.n, p.k, p.flags);
-      if (p.workspace == nullptr || p.workspace_bytes < need || need == 0)
+      const size_t need = (size_t)plan.splits * p.m * p.n * sizeof(float);
+      if (p.workspace == nullptr || p.workspace_bytes < need)
         return fail(WQ_STAGE_ARGS, WQ_ERR_WORKSPACE);
-      if (!aligned(p.workspace, 256)) return fail(WQ_STAGE_ARGS, WQ_ERR_ALIGN);
-      counters = static_cast<int32_t*>(p.workspace);
-      partials = reinterpret_cast<float*>(
-          static_cast<char*>(p.workspace) +
-          kCounterBytes * (((size_t)(p.n / 16) * 4 + kCounterBytes - 1) / kCounterBytes));
+      if (!aligned(p.workspace, 16)) return fail(WQ_STAGE_ARGS, WQ_ERR_ALIGN);
+      partials = static_cast<float*>(p.workspace);
     }
-    const hipError_t e = wq::launch_gemm_small(a, lda, p.m, b, s, z, c, p.n, p.k, plan, partials,
-                                               counters, stream);
+    const hipError_t e =
+        wq::launch_gemm_small(a, lda, p.m, b, s, z, c, p.n, p.k, plan, partials, stream);
     return e == hipSuccess ? 0 : hip_fail(e);
   }
   const hipError_t e = wq::launch_gemm_tile(a, lda, p.m, b, s, z, c, p.n, p.k, stream);

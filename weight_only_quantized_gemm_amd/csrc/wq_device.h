@@ -29,18 +29,34 @@ __device__ __forceinline__ ZeroOffsets zero_offsets(int z) {
   return ZeroOffsets{f16x2{a, a}, f16x2{b, b}};
 }
 
+// The two exponent patterns of the dequant, held in VGPRs.  gfx9 VOP3 encodings take at
+// most one literal or SGPR operand, so with the mask as literal the OR pattern must come
+// from a VGPR for (w & mask) | pattern to fold into a single v_and_or_b32.  The inline asm
+// keeps the compiler from turning the values back into literals.
+struct MagicRegs {
+  uint32_t m1024;
+  uint32_t m64;
+};
+
+__device__ __forceinline__ MagicRegs magic_regs() {
+  MagicRegs r;
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(r.m1024));
+  asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(r.m64));
+  return r;
+}
+
 // One layout word -> the eight values (q - z) of its rows, in row order, as fp16.
 // Slots hold row offsets {0,2,4,6} in nibbles 0..3 and {1,3,5,7} in nibbles 4..7, so a
 // 0x000F000F mask picks a pair of rows into the two mantissas; OR-ing the exponent of
 // 1024.0 (0x6400, unit ulp) turns nibble q into 1024 + q, and for the nibbles one place
 // higher the exponent of 64.0 (0x5400, ulp 1/16) turns (q << 4) into 64 + q.  Subtracting
 // 1024 + z (resp. 64 + z) leaves the exact integer q - z in [-15, 15].
-__device__ __forceinline__ f16x8 dequant8(uint32_t w, ZeroOffsets zo) {
+__device__ __forceinline__ f16x8 dequant8(uint32_t w, ZeroOffsets zo, MagicRegs mr) {
   const uint32_t w8 = w >> 8;
-  const f16x2 p0 = __builtin_bit_cast(f16x2, (w & 0x000F000Fu) | 0x64006400u) - zo.o1024;
-  const f16x2 p1 = __builtin_bit_cast(f16x2, (w & 0x00F000F0u) | 0x54005400u) - zo.o64;
-  const f16x2 p2 = __builtin_bit_cast(f16x2, (w8 & 0x000F000Fu) | 0x64006400u) - zo.o1024;
-  const f16x2 p3 = __builtin_bit_cast(f16x2, (w8 & 0x00F000F0u) | 0x54005400u) - zo.o64;
+  const f16x2 p0 = __builtin_bit_cast(f16x2, (w & 0x000F000Fu) | mr.m1024) - zo.o1024;
+  const f16x2 p1 = __builtin_bit_cast(f16x2, (w & 0x00F000F0u) | mr.m64) - zo.o64;
+  const f16x2 p2 = __builtin_bit_cast(f16x2, (w8 & 0x000F000Fu) | mr.m1024) - zo.o1024;
+  const f16x2 p3 = __builtin_bit_cast(f16x2, (w8 & 0x00F000F0u) | mr.m64) - zo.o64;
   return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 

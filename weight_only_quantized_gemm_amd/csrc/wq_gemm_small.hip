@@ -1,201 +1,272 @@
 // Small-M W4A16 GEMM (m <= 16): decode and small batches, bound by the weight stream.
 //
 // One 16x16x32 fp16 MFMA block covers all m rows (rows >= m read as zero), so the packed
-// weights are read exactly once.  A work-group owns `NB` 16-column blocks and a range of
-// K; its four waves split that range, each streaming one 1 KiB layout chunk per 128-row
-// group and 16-column block with a single 16-byte load per lane.  Codes become exact
-// fp16 integers (q - z) in registers; each group's MFMA partial is scaled by the fp16
-// group scale in fp32 and accumulated in fp32.
+// weights are read exactly once.  A work-group owns one 16-column block and a range of K
+// groups; its WAVES waves split that range, each streaming one 1 KiB layout chunk per
+// 128-row group with a single non-temporal 16-byte load per lane.  All of a wave's weight
+// loads are issued before any arithmetic and consumed in issue order, so the weight
+// stream is never stalled behind compute.  Activations, scales and zero points of the
+// work-group's range are staged once in LDS.  Codes become exact fp16 integers (q - z) in
+// registers; each group's MFMA partial is scaled by the fp16 group scale in fp32 and
+// accumulated in fp32; the waves' sums are added in wave order.
 //
 // Split-K (`splits` > 1 work-groups per column block) follows the pages' fp32 reduce
 // (ferrum-kernels marlin.rs, `ferrum_vllm_marlin_moe_f16`: `use_fp32_reduce` with an fp32
-// `c_tmp`): each split stores its fp32 partial tile, and the last work-group to arrive on
-// the column block's counter adds the partials in split order 0..S-1 (a fixed order, so
-// results do not depend on arrival order or device size: memra mmq_ffi.rs records that
-// fold-order changes flipped outputs), writes fp16 C and resets the counter to zero.
+// `c_tmp`): each split stores its fp32 partial tile to the workspace and a second kernel
+// adds the partials in split order 0..S-1 and rounds once to fp16.  The order is fixed, so
+// results do not depend on scheduling or device size (memra mmq_ffi.rs records that
+// fold-order changes flipped outputs).  The kernel boundary orders the partial stores
+// before the reduce's loads; a device-scope fence inside the GEMM would instead write back
+// and invalidate a whole L2 per work-group on this multi-L2 part.
 #include "wq_device.h"
 #include "wq_internal.h"
 
 namespace wq {
 namespace {
 
-template <bool ZP, int NB, int DEPTH>
-__global__ __launch_bounds__(256) void gemm_small_kernel(
+// LDS budget of one work-group's activation slice (fp16 [m][span*128], padded to a whole
+// number of staging rounds).
+constexpr int kSmallLdsA = 128 * 1024;
+constexpr int kMaxSpan = 64;   // groups per work-group covered by the staged scales
+
+// The kernel body is branch-free up to the arithmetic: every load is issued
+// unconditionally (addresses are clamped into the tensors) and ragged ends are masked by
+// value, so the compiler's in-order load counting can let LDS writes wait for the
+// activations alone and each group wait for its own weight chunk, while the rest of the
+// weight stream stays in flight.
+template <bool ZP, int WAVES, int GW, int STAGE>
+__global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     const f16* __restrict__ a, int lda, int m, const u32x4* __restrict__ b,
     const f16* __restrict__ s, const u32x2* __restrict__ z, f16* __restrict__ c, int n,
-    int groups, int splits, float* __restrict__ partials, int32_t* __restrict__ counters) {
-  __shared__ f32x4 red[4][NB][64];
-  __shared__ int is_last;
+    int groups, int splits, float* __restrict__ partials) {
+  constexpr int T = WAVES * 64;
+  extern __shared__ f16x8 a_lds[];                // [m][span*16] granules (+ padding)
+  __shared__ uint32_t s_lds[kMaxSpan * 8 + 2 * T];  // scales of the range, [g][col] as fp16
+  __shared__ u32x2 z_lds[ZP ? T : 1];          // zero points of the range (+ padding)
+  __shared__ f32x4 red[WAVES][64];
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int col = lane & 15;  // column inside a 16-column block; also the A row of the lane
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 15;  // column inside the 16-column block; also the A row of the lane
   const int qd = lane >> 4;   // which 8 rows of each 32-row MFMA step the lane carries
-  const int nb0 = blockIdx.x * NB;
+  const int nb = blockIdx.x;
   const int split = blockIdx.y;
 
   const int gs0 = (int)((long)groups * split / splits);
   const int gs1 = (int)((long)groups * (split + 1) / splits);
   const int span = gs1 - gs0;
-  const int g0 = gs0 + span * wave / 4;
-  const int g1 = gs0 + span * (wave + 1) / 4;
+  const int g0 = gs0 + span * wave / WAVES;
+  const int g1 = gs0 + span * (wave + 1) / WAVES;
+  const int gw = g1 - g0;  // <= GW by the launch plan
 
-  const bool row_ok = col < m;
-  const f16* arow = a + (long)(row_ok ? col : 0) * lda + 8 * qd;
+  // 1. Activation granules: slot u of this thread is granule tid + u*T of the slice, at row
+  //    r and granule column q; (r, q) advance by a fixed (dr, dq) per slot.
+  const int per_row = span * (kGroup / 8);
+  const int dr = T / per_row;
+  const int dq = T - dr * per_row;
+  int r = tid / per_row;
+  int q = tid - r * per_row;
+  const f16* a_base = a + (long)gs0 * kGroup;
+  f16x8 stage[STAGE];
+#pragma unroll
+  for (int u = 0; u < STAGE; ++u) {
+    const int rr = r < m ? r : m - 1;
+    stage[u] = *reinterpret_cast<const f16x8*>(a_base + (long)rr * lda + 8 * q);
+    q += dq;
+    r += dr;
+    const bool wrap = q >= per_row;
+    q = wrap ? q - per_row : q;
+    r = wrap ? r + 1 : r;
+  }
+  // 2. Scales (8 dwords of fp16 pairs per group) and zero points of the range.
+  const long blk0 = (long)nb * groups + gs0;
+  const uint32_t* s32 = reinterpret_cast<const uint32_t*>(s) + blk0 * 8;
+  const int s_words = span * 8;
+  uint32_t s_stage[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = tid + u * T;
+    s_stage[u] = s32[i < s_words ? i : s_words - 1];
+  }
+  u32x2 z_stage = u32x2{0u, 0u};
+  if constexpr (ZP) z_stage = z[blk0 + (tid < span ? tid : span - 1)];
 
-  f32x4 acc[NB];
+  // 3. The wave's weight chunks, all in flight before any arithmetic.
+  u32x4 bw[GW];
 #pragma unroll
-  for (int bb = 0; bb < NB; ++bb) acc[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int gb = g0; gb < g1; gb += DEPTH) {
-    const int cnt = min(DEPTH, g1 - gb);
-    u32x4 bw[DEPTH][NB];
-#pragma unroll
-    for (int i = 0; i < DEPTH; ++i)
-#pragma unroll
-      for (int bb = 0; bb < NB; ++bb)
-        if (i < cnt) bw[i][bb] = b[((long)(nb0 + bb) * groups + gb + i) * 64 + lane];
-
-#pragma unroll
-    for (int i = 0; i < DEPTH; ++i) {
-      if (i < cnt) {
-        const int g = gb + i;
-        f16x8 av[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          av[j] = row_ok ? *reinterpret_cast<const f16x8*>(arow + (long)g * kGroup + 32 * j)
-                         : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int bb = 0; bb < NB; ++bb) {
-          const long blk = (long)(nb0 + bb) * groups + g;
-          const float sc = (float)s[blk * 16 + col];
-          const ZeroOffsets zo = zero_offsets(ZP ? zero_code(z[blk], col) : 8);
-          f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) p = mfma16x16x32(av[j], dequant8(bw[i][bb][j], zo), p);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[bb][r] = __builtin_fmaf(sc, p[r], acc[bb][r]);
-        }
-      }
-    }
+  for (int i = 0; i < GW; ++i) {
+    const int g = g0 + (i < gw ? i : gw - 1);
+    bw[i] = __builtin_nontemporal_load(&b[((long)nb * groups + g) * 64 + lane]);
   }
 
-  // Work-group reduce over the four waves, in wave order.
+  // 4. Stage into LDS (waits for the activations and scales only), then sync.
 #pragma unroll
-  for (int bb = 0; bb < NB; ++bb) red[wave][bb][lane] = acc[bb];
+  for (int u = 0; u < STAGE; ++u) a_lds[tid + u * T] = stage[u];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) s_lds[tid + u * T] = s_stage[u];
+  if constexpr (ZP) z_lds[tid] = z_stage;
   __syncthreads();
 
-  f32x4 tot[NB];
-  if (wave == 0) {
+  // 5. Arithmetic.  MFMA rows >= m are never stored, and a row of the product depends on
+  //    its own A row only, so those lanes read row m - 1 instead of selecting zeros.
+  const MagicRegs mr = magic_regs();
+  const int arow = (col < m ? col : m - 1) * per_row;
+  const f16* s_half = reinterpret_cast<const f16*>(s_lds);
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      f32x4 t = red[0][bb][lane];
+  for (int i = 0; i < GW; ++i) {
+    const int gl = g0 - gs0 + (i < gw ? i : gw - 1);  // group inside the staged range
+    const float sc = i < gw ? (float)s_half[gl * 16 + col] : 0.f;
+    const ZeroOffsets zo = zero_offsets(ZP ? zero_code(z_lds[gl], col) : 8);
+    f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int w = 1; w < 4; ++w) t += red[w][bb][lane];
-      tot[bb] = t;
-    }
+    for (int j = 0; j < 4; ++j)
+      p = mfma16x16x32(a_lds[arow + gl * 16 + 4 * j + qd], dequant8(bw[i][j], zo, mr), p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sc, p[e], acc[e]);
   }
 
-  // Output layout of the 16x16 block: lane holds rows 4*qd + r of column `col`.
-  if (splits == 1) {
-    if (wave == 0) {
-#pragma unroll
-      for (int bb = 0; bb < NB; ++bb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 4 * qd + r;
-          if (row < m) c[(long)row * n + (nb0 + bb) * 16 + col] = (f16)tot[bb][r];
-        }
-    }
-    return;
-  }
-
-  if (wave == 0) {
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 4 * qd + r;
-        if (row < m) partials[((long)split * m + row) * n + (nb0 + bb) * 16 + col] = tot[bb][r];
-      }
-    __threadfence();  // release this split's partials at device scope
-  }
+  // Work-group reduce over the waves, in wave order.
+  red[wave][lane] = acc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = atomicAdd(&counters[blockIdx.x], 1);
-    const int last = prev == splits - 1;
-    if (last) __hip_atomic_store(&counters[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = last;
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();  // acquire the other splits' partials
+  if (wave != 0) return;
+  f32x4 tot = red[0][lane];
+#pragma unroll
+  for (int w = 1; w < WAVES; ++w) tot += red[w][lane];
 
-  if (wave == 0) {
+  // Output layout of the 16x16 block: lane holds rows 4*qd + e of column `col`.
+  const long colx = (long)nb * 16 + col;
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 4 * qd + r;
-        if (row >= m) continue;
-        const long colx = (long)(nb0 + bb) * 16 + col;
-        float sum = 0.f;
-        for (int sp = 0; sp < splits; ++sp) {
-          const float v = sp == split ? tot[bb][r] : partials[((long)sp * m + row) * n + colx];
-          sum = sp == 0 ? v : sum + v;
-        }
-        c[(long)row * n + colx] = (f16)sum;
-      }
+  for (int e = 0; e < 4; ++e) {
+    const int row = 4 * qd + e;
+    if (row >= m) continue;
+    if (splits == 1)
+      c[(long)row * n + colx] = (f16)tot[e];
+    else
+      partials[((long)split * m + row) * n + colx] = tot[e];
   }
 }
 
-template <bool ZP, int NB, int DEPTH>
+// c[row][col] = fp16(sum over splits 0..S-1 of partials[split][row][col]), eight columns
+// per thread, added in split order.
+__global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ partials,
+                                                            f16* __restrict__ c, int m, int n,
+                                                            int splits) {
+  const long per_split = (long)m * n;
+  const long total = per_split / 8;
+  for (long t = (long)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (long)gridDim.x * blockDim.x) {
+    const long e = t * 8;
+    f32x4 lo = *reinterpret_cast<const f32x4*>(partials + e);
+    f32x4 hi = *reinterpret_cast<const f32x4*>(partials + e + 4);
+    for (int sp = 1; sp < splits; ++sp) {
+      lo += *reinterpret_cast<const f32x4*>(partials + sp * per_split + e);
+      hi += *reinterpret_cast<const f32x4*>(partials + sp * per_split + e + 4);
+    }
+    f16x8 out;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      out[j] = (f16)lo[j];
+      out[4 + j] = (f16)hi[j];
+    }
+    *reinterpret_cast<f16x8*>(c + e) = out;
+  }
+}
+
+// Staging slots per thread for an activation slice of m rows and `span` groups.
+int stage_slots(int m, int span, int waves) {
+  const long granules = (long)m * span * (kGroup / 8);
+  const long per_slot = (long)waves * 64;
+  return (int)((granules + per_slot - 1) / per_slot);
+}
+
+int round_slots(int slots) {
+  return slots <= 1 ? 1 : slots <= 2 ? 2 : slots <= 4 ? 4 : slots <= 8 ? 8 : 16;
+}
+
+template <bool ZP, int WAVES, int GW, int STAGE>
 hipError_t launch_small_t(const uint16_t* a, int lda, int m, const uint32_t* b,
                           const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
-                          int splits, float* partials, int32_t* counters, hipStream_t stream) {
-  const dim3 grid(n / (16 * NB), splits);
-  hipLaunchKernelGGL((gemm_small_kernel<ZP, NB, DEPTH>), grid, dim3(256), 0, stream,
-                     reinterpret_cast<const f16*>(a), lda, m,
+                          int splits, float* partials, hipStream_t stream) {
+  const int groups = k / kGroup;
+  const size_t lds = (size_t)STAGE * WAVES * 64 * sizeof(f16x8);
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&gemm_small_kernel<ZP, WAVES, GW, STAGE>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, kSmallLdsA);
+  if (attr != hipSuccess) return attr;
+  const dim3 grid(n / 16, splits);
+  hipLaunchKernelGGL((gemm_small_kernel<ZP, WAVES, GW, STAGE>), grid, dim3(WAVES * 64), lds,
+                     stream, reinterpret_cast<const f16*>(a), lda, m,
                      reinterpret_cast<const u32x4*>(b), reinterpret_cast<const f16*>(s),
-                     reinterpret_cast<const u32x2*>(z), reinterpret_cast<f16*>(c), n,
-                     k / kGroup, splits, partials, counters);
+                     reinterpret_cast<const u32x2*>(z), reinterpret_cast<f16*>(c), n, groups,
+                     splits, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  long blocks = ((long)m * n / 8 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     partials, reinterpret_cast<f16*>(c), m, n, splits);
   return hipGetLastError();
 }
 
-template <bool ZP, int NB>
-hipError_t launch_small_depth(const uint16_t* a, int lda, int m, const uint32_t* b,
+template <bool ZP, int WAVES, int GW>
+hipError_t launch_small_stage(const uint16_t* a, int lda, int m, const uint32_t* b,
                               const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
-                              const SmallPlan& plan, float* partials, int32_t* counters,
-                              hipStream_t stream) {
+                              const SmallPlan& plan, float* partials, hipStream_t stream) {
+  const int span = (k / kGroup + plan.splits - 1) / plan.splits;
+  switch (round_slots(stage_slots(m, span, WAVES))) {
+    case 1: return launch_small_t<ZP, WAVES, GW, 1>(a, lda, m, b, s, z, c, n, k, plan.splits, partials, stream);
+    case 2: return launch_small_t<ZP, WAVES, GW, 2>(a, lda, m, b, s, z, c, n, k, plan.splits, partials, stream);
+    case 4: return launch_small_t<ZP, WAVES, GW, 4>(a, lda, m, b, s, z, c, n, k, plan.splits, partials, stream);
+    case 8: return launch_small_t<ZP, WAVES, GW, 8>(a, lda, m, b, s, z, c, n, k, plan.splits, partials, stream);
+    default: return launch_small_t<ZP, WAVES, GW, 16>(a, lda, m, b, s, z, c, n, k, plan.splits, partials, stream);
+  }
+}
+
+template <bool ZP, int WAVES>
+hipError_t launch_small_gw(const uint16_t* a, int lda, int m, const uint32_t* b,
+                           const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
+                           const SmallPlan& plan, float* partials, hipStream_t stream) {
   switch (plan.depth) {
-    case 1: return launch_small_t<ZP, NB, 1>(a, lda, m, b, s, z, c, n, k, plan.splits, partials, counters, stream);
-    case 2: return launch_small_t<ZP, NB, 2>(a, lda, m, b, s, z, c, n, k, plan.splits, partials, counters, stream);
-    case 4: return launch_small_t<ZP, NB, 4>(a, lda, m, b, s, z, c, n, k, plan.splits, partials, counters, stream);
-    default: return launch_small_t<ZP, NB, 8>(a, lda, m, b, s, z, c, n, k, plan.splits, partials, counters, stream);
+    case 1: return launch_small_stage<ZP, WAVES, 1>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
+    case 2: return launch_small_stage<ZP, WAVES, 2>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
+    case 4: return launch_small_stage<ZP, WAVES, 4>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
+    default: return launch_small_stage<ZP, WAVES, 8>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
   }
 }
 
 template <bool ZP>
-hipError_t launch_small_nb(const uint16_t* a, int lda, int m, const uint32_t* b,
-                           const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
-                           const SmallPlan& plan, float* partials, int32_t* counters,
-                           hipStream_t stream) {
-  switch (plan.nb) {
-    case 1: return launch_small_depth<ZP, 1>(a, lda, m, b, s, z, c, n, k, plan, partials, counters, stream);
-    case 2: return launch_small_depth<ZP, 2>(a, lda, m, b, s, z, c, n, k, plan, partials, counters, stream);
-    default: return launch_small_depth<ZP, 4>(a, lda, m, b, s, z, c, n, k, plan, partials, counters, stream);
-  }
+hipError_t launch_small_waves(const uint16_t* a, int lda, int m, const uint32_t* b,
+                              const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
+                              const SmallPlan& plan, float* partials, hipStream_t stream) {
+  if (plan.waves == 8)
+    return launch_small_gw<ZP, 8>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
+  return launch_small_gw<ZP, 4>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
 }
 
 }  // namespace
 
+bool small_plan_fits(int m, int k, const SmallPlan& plan) {
+  const int groups = k / kGroup;
+  if (plan.splits < 1 || plan.splits > groups) return false;
+  const int span = (groups + plan.splits - 1) / plan.splits;
+  const int min_span = groups / plan.splits;  // every split holds at least this many groups
+  if (plan.waves != 4 && plan.waves != 8) return false;
+  if (span > kMaxSpan || min_span < plan.waves) return false;   // every wave has a group
+  if ((span + plan.waves - 1) / plan.waves > plan.depth || plan.depth > 8) return false;
+  const int slots = stage_slots(m, span, plan.waves);
+  return slots <= 16 &&
+         (long)round_slots(slots) * plan.waves * 64 * (long)sizeof(f16x8) <= kSmallLdsA;
+}
+
 hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* b,
                              const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
-                             const SmallPlan& plan, float* partials, int32_t* counters,
-                             hipStream_t stream) {
+                             const SmallPlan& plan, float* partials, hipStream_t stream) {
+  if (!small_plan_fits(m, k, plan)) return hipErrorInvalidConfiguration;
   if (z != nullptr)
-    return launch_small_nb<true>(a, lda, m, b, s, z, c, n, k, plan, partials, counters, stream);
-  return launch_small_nb<false>(a, lda, m, b, s, z, c, n, k, plan, partials, counters, stream);
+    return launch_small_waves<true>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
+  return launch_small_waves<false>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
 }
 
 }  // namespace wq

@@ -228,6 +228,7 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(TileArgs p) {
   load_b(0, bcur, scur, zcur);
   __syncthreads();
 
+  const MagicRegs mr = magic_regs();
   const int nchunks = p.k / KC;
   for (int ch = 0; ch < nchunks; ++ch) {
     const int g = ch >> 1;
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(TileArgs p) {
       f16x8 bop[2];
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
-        bop[cb] = dequant8(bcur[cb][s & 1][2 * h2 + (s >> 1)], zo[cb]);
+        bop[cb] = dequant8(bcur[cb][s & 1][2 * h2 + (s >> 1)], zo[cb], mr);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         if (rb < nrb) {

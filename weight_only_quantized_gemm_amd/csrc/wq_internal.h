@@ -19,17 +19,18 @@ hipError_t launch_dequant(const uint32_t* b, const uint16_t* s, const uint32_t* 
 hipError_t launch_gather_columns(const uint16_t* a, int lda, const int32_t* perm, uint16_t* out,
                                  int m, int k, hipStream_t stream);
 
-// Small-M kernel (wq_gemm_small.hip): m <= 16, one 16-row MFMA block, split-K over
-// `splits` work-groups per column block with an fp32 partial reduce.
+// Small-M kernel (wq_gemm_small.hip): m <= 16, one 16-row MFMA block; with `splits` > 1
+// work-groups per column block, fp32 partials go to `partials` [splits][m][n] and a second
+// kernel reduces them in split order.
 struct SmallPlan {
-  int nb;          // 16-column blocks per work-group
+  int waves;       // waves per work-group (4, 8 or 16), splitting the work-group's K range
   int splits;      // work-groups along K per column block
-  int depth;       // groups of K prefetched per wave per batch
+  int depth;       // groups of K per wave, all loaded before arithmetic (1, 2, 4 or 8)
 };
+bool small_plan_fits(int m, int k, const SmallPlan& plan);
 hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* b,
                              const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
-                             const SmallPlan& plan, float* partials, int32_t* counters,
-                             hipStream_t stream);
+                             const SmallPlan& plan, float* partials, hipStream_t stream);
 
 // Tiled kernel (wq_gemm_tile.hip): 256 x 128 output tiles on 4 waves of 128 x 64.
 constexpr int kTileM = 256;

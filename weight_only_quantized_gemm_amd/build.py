@@ -27,6 +27,8 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
            # keep the compiler from forming packed-fp32 VALU ops (v_pk_*_f32)
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # keep MFMA accumulators in arch VGPRs: the kernels update them with VALU ops
+           "-mllvm", "-amdgpu-mfma-vgpr-form=1",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES] + (extra or [])
     if verbose:

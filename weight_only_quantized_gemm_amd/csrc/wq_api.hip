@@ -47,9 +47,10 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 // kernel then computes the product).  Without WQ_FLAG_FP32_REDUCE the product is never
 // split (every output is one work-group's fp32 sum, rounded once).  With it, a requested
 // split count is honoured, raised if the activation slice would not fit in LDS; the
-// library's own choice splits only when the 16-column blocks alone give fewer than ~512
-// work-groups (two per CU), since every split adds an fp32 partial round trip and a reduce
-// launch.  Each split's groups are shared by 4, 8 or 16 waves, at most 8 groups per wave.
+// library's own choice splits only when the 16-column blocks alone give fewer than 128
+// work-groups (half the CUs), since every split adds an fp32 partial round trip and a
+// reduce launch (measured on MI355X: at N=4096..14336 one split is fastest).  Each split's
+// groups are shared by 4 or 8 waves, at most 8 groups per wave.
 bool plan_small(int m, int n, int k, uint32_t flags, int requested, wq::SmallPlan* plan) {
   const int groups = k / kGroupSize;
   const bool fp32 = (flags & WQ_FLAG_FP32_REDUCE) != 0;
@@ -58,14 +59,14 @@ bool plan_small(int m, int n, int k, uint32_t flags, int requested, wq::SmallPla
     s = requested;
   } else if (fp32) {
     const int col_blocks = n / 16;
-    s = col_blocks >= 512 ? 1 : (512 + col_blocks - 1) / col_blocks;
+    s = col_blocks >= 128 ? 1 : (256 + col_blocks - 1) / col_blocks;
     const int max_s = groups / 4 > 0 ? groups / 4 : 1;  // keep a group per wave of a split
     if (s > max_s) s = max_s;
   }
   for (; s <= groups && s <= kMaxSplits; ++s) {
     if (s > 1 && !fp32) return false;
     const int span = (groups + s - 1) / s;
-    for (int waves = 4; waves <= 16; waves *= 2) {
+    for (int waves = 4; waves <= 8; waves *= 2) {
       const int per_wave = (span + waves - 1) / waves;
       if (per_wave > 8) continue;
       wq::SmallPlan p{};

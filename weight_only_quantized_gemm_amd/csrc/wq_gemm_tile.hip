@@ -1,18 +1,31 @@
 // Tiled W4A16 GEMM for larger M (prefill) and the expert-major grouped (MoE) variant.
 //
 // A work-group computes a 256 x 128 tile of C with four waves of 128 x 64, each a 4 x 2
-// grid of 32x32x16 fp16 MFMA blocks with fp32 accumulators.  A (fp16) goes through LDS
-// in 256 x 64 chunks, double-buffered and XOR-swizzled by 16-byte granule so that both
-// the row-per-lane reads and the coalesced writes are free of bank conflicts.  Packed
-// weights go straight from HBM into registers (two 16-byte loads per lane and 32-column
-// block per 128-row group), one group ahead of use, and are dequantized in registers to
-// exact fp16 integers (q - z).
+// grid of 32x32x16 fp16 MFMA blocks with fp32 accumulators held in VGPRs.
 //
-// Group scales are applied in fp32 without a second accumulator set: before the MFMAs of
-// group g accumulate, the running sums are multiplied by sigma_{g-1} / sigma_g, and the
-// result is multiplied by sigma_last at the end, so C = sum_g sigma_g * P_g with P_g the
-// exact-integer-weight partial of group g.  sigma is the fp16 scale widened to fp32, with
-// an exact zero replaced by 2^-60 (its contribution then vanishes after rounding to fp16).
+// Data movement is all direct-to-LDS loads (global_load_lds), issued at a fixed count per
+// wave so that the in-order load counter tells exactly when a stage has landed:
+//  * A (fp16) in 256 x 64 chunks through a 4-stage ring (128 KiB), three chunks ahead;
+//    each wave load writes 8 rows x 128 B, and the source granule of every lane is chosen
+//    so that the ring holds the 16-byte granules of a row XOR-swizzled by (row & 7):
+//    reads of one granule column by 32 consecutive rows are then free of bank conflicts.
+//  * packed B (8 KiB per 128-row group for the tile's 8 column blocks) and the group's
+//    scales / zero points into one of two group slots, one group ahead.
+// Every iteration waits for its own loads, meets the other waves at a barrier (after which
+// the stage about to be refilled is no longer read by anyone), issues the next loads and
+// computes.  Loads past the end re-read the last chunk / group into the free stage, so the
+// counts never change; nothing is read outside the tensors.
+//
+// Weights are dequantized in registers to exact fp16 integers (q - z).  Group scales are
+// applied in fp32 without a second accumulator set: before the MFMAs of group g accumulate,
+// the running sums are multiplied by sigma_{g-1} / sigma_g, and the result is multiplied by
+// sigma_last at the end, so C = sum_g sigma_g * P_g with P_g the exact-integer-weight
+// partial of group g.  sigma is the fp16 scale widened to fp32, with an exact zero
+// replaced by 2^-60 (its contribution then vanishes after rounding to fp16).
+//
+// Tiles are assigned XCD-aware: work-groups are dealt to the 8 XCDs round-robin, so tile
+// ids are remapped to give each XCD a contiguous range (for a 2048-row problem, one
+// 256-row A panel per XCD, which then stays in that XCD's L2).
 //
 // Grouped variant (memra-engine mmq_ffi.rs, `ExpertCsr` and the grouped projection call):
 // tiles are enumerated over (active expert segment, column tile, row tile); a tile's rows
@@ -26,7 +39,26 @@ namespace {
 
 constexpr int TM = kTileM;   // 256
 constexpr int TN = kTileN;   // 128
-constexpr int KC = 64;       // K rows per LDS chunk (half a group)
+constexpr int KC = 64;       // K rows per A chunk (half a group)
+constexpr int NS = 4;        // A ring stages
+constexpr int kXcds = 8;
+
+// Direct-to-LDS loads each wave issues: 8 per A chunk; per group 2 (B) + 1 (scales / zero
+// points), issued with the group's even chunk.
+constexpr int kDmaA = 8;
+constexpr int kDmaG = 3;
+// Loads issued after the ones an iteration waits for (see the pipeline above):
+//  even chunk c = 2g waits for B/SZ(g), followed by A(c+1) and A(c+2);
+//  odd chunk c waits for A(c), followed by A(c+1), B/SZ, A(c+2).
+constexpr int kWaitEven = 2 * kDmaA;
+constexpr int kWaitOdd = 2 * kDmaA + kDmaG;
+static_assert(kWaitOdd < 64, "vmcnt holds 6 bits");
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  // s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, expcnt 6:4 (7 = none), lgkmcnt 11:8.
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 struct TileArgs {
   const uint16_t* a;
@@ -38,6 +70,7 @@ struct TileArgs {
   uint16_t* c;
   int n;
   int k;
+  int tiles;  // work-groups launched
   // grouped
   const uint8_t* b_bank;
   size_t b_stride;
@@ -57,20 +90,30 @@ __device__ __forceinline__ float sigma_of(f16 v) {
   return f == 0.f ? 0x1p-60f : f;
 }
 
+struct Smem {
+  f16x8 a[NS][TM * KC / 8];     // 4 x 32 KiB
+  u32x4 b[2][8 * 64];           // 2 x 8 KiB: 8 column blocks x 64 lanes x 16 B
+  uint32_t sz[2][4 * 64];       // 2 x 1 KiB: wave 0 scales, wave 1 zero points, 2-3 spare
+  int row_a[TM];
+  int row_c[TM];
+  int info[5];
+};
+
 template <bool ZP, bool GROUPED>
 __global__ __launch_bounds__(256) void gemm_tile_kernel(TileArgs p) {
-  __shared__ f16x8 lds_a[2][TM * (KC / 8)];
-  __shared__ int row_a[TM];
-  __shared__ int row_c[TM];
-  __shared__ int tile_info[5];
+  __shared__ Smem sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int wm = wave >> 1;   // wave's 128-row half of the tile
   const int wn = wave & 1;    // wave's 64-column half of the tile
   const int groups = p.k / kGroup;
   const int ntiles_n = p.n / TN;
+
+  // XCD-aware tile id: work-group i runs on XCD i % 8; give each XCD a contiguous range.
+  int t = blockIdx.x;
+  if (p.tiles % kXcds == 0) t = (t % kXcds) * (p.tiles / kXcds) + t / kXcds;
 
   int n0, valid_rows;
   const uint32_t* bptr;
@@ -79,7 +122,6 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(TileArgs p) {
 
   if constexpr (GROUPED) {
     if (tid == 0) {
-      int t = blockIdx.x;
       int seg = -1, lo = 0, rows = 0, mt = 0, nt = 0;
       for (int i = 0; i < p.n_active; ++i) {
         int a0 = p.ex_off[i], a1 = p.ex_off[i + 1];
@@ -101,114 +143,113 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(TileArgs p) {
       int e = seg;
       if (seg >= 0 && p.ex_ids != nullptr) e = p.ex_ids[seg];
       if (e < 0 || e >= p.n_expert) seg = -1;
-      tile_info[0] = seg;
-      tile_info[1] = e;
-      tile_info[2] = lo + mt * TM;   // first CSR position of the tile
-      tile_info[3] = rows - mt * TM; // CSR positions left in the segment from there
-      tile_info[4] = nt;
+      sm.info[0] = seg;
+      sm.info[1] = e;
+      sm.info[2] = lo + mt * TM;    // first CSR position of the tile
+      sm.info[3] = rows - mt * TM;  // CSR positions left in the segment from there
+      sm.info[4] = nt;
     }
     __syncthreads();
-    const int seg = tile_info[0];
+    const int seg = sm.info[0];
     if (seg < 0) return;
-    const int e = tile_info[1];
-    const int pos0 = tile_info[2];
-    const int left = tile_info[3];
-    const int nt = tile_info[4];
+    const int e = sm.info[1];
+    const int pos0 = sm.info[2];
+    const int left = sm.info[3];
+    const int nt = sm.info[4];
     valid_rows = left < TM ? left : TM;
     n0 = nt * TN;
-    // Row maps: CSR position -> (activation row, output row); invalid entries -> -1.
-    {
-      int ra = -1, rc = -1;
-      if (tid < valid_rows) {
-        const int pair = p.ex_pairs[pos0 + tid];
-        if (pair >= 0 && pair < p.n_pairs) {
-          const int tok = p.pair_tok[pair];
-          if (tok >= 0 && tok < p.n_tokens) {
-            ra = tok;
-            rc = pair;
-          }
+    // Row maps: CSR position -> (activation row, output row); rows without a valid pair
+    // read activation row 0 (finite data, never stored) and are not written.
+    int ra = 0, rc = -1;
+    if (tid < valid_rows) {
+      const int pair = p.ex_pairs[pos0 + tid];
+      if (pair >= 0 && pair < p.n_pairs) {
+        const int tok = p.pair_tok[pair];
+        if (tok >= 0 && tok < p.n_tokens) {
+          ra = tok;
+          rc = pair;
         }
       }
-      row_a[tid] = ra;
-      row_c[tid] = rc;
     }
+    sm.row_a[tid] = ra;
+    sm.row_c[tid] = rc;
     bptr = reinterpret_cast<const uint32_t*>(p.b_bank + (size_t)e * p.b_stride);
     sptr = reinterpret_cast<const uint16_t*>(p.s_bank + (size_t)e * p.s_stride);
     zptr = ZP ? reinterpret_cast<const uint32_t*>(p.z_bank + (size_t)e * p.z_stride) : nullptr;
-    __syncthreads();
   } else {
-    const int mt = blockIdx.y;
-    n0 = blockIdx.x * TN;
+    const int mt = t / ntiles_n;
+    const int nt = t - mt * ntiles_n;
+    n0 = nt * TN;
     const int m0 = mt * TM;
     valid_rows = p.m - m0 < TM ? p.m - m0 : TM;
-    {
-      const int r = m0 + tid;
-      row_a[tid] = tid < valid_rows ? r : -1;
-      row_c[tid] = tid < valid_rows ? r : -1;
-    }
+    // Rows past m read the last row (finite, never stored).
+    const int r = m0 + tid;
+    sm.row_a[tid] = r < p.m ? r : p.m - 1;
+    sm.row_c[tid] = r < p.m ? r : -1;
     bptr = p.b;
     sptr = p.s;
     zptr = p.z;
-    __syncthreads();
   }
+  __syncthreads();
 
   // Row blocks of this wave that hold at least one valid row (wave-uniform).
   int nrb = (valid_rows - 128 * wm + 31) / 32;
-  nrb = nrb < 0 ? 0 : (nrb > 4 ? 4 : nrb);
+  nrb = __builtin_amdgcn_readfirstlane(nrb < 0 ? 0 : (nrb > 4 ? 4 : nrb));
 
-  // ---- A staging: thread owns granule gi of rows (tid >> 3) + 32 * i --------------------
-  const int gi = tid & 7;
-  const f16* arows[8];
+  // ---- load sources -------------------------------------------------------------------
+  // A: slot u of this lane fills ring granule (u*4 + wave)*64 + lane = row 8*(u*4+wave) +
+  // lane/8, physical granule lane%8, i.e. logical granule (lane%8) ^ (row & 7).
+  const f16* asrc[kDmaA];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = row_a[(tid >> 3) + 32 * i];
-    arows[i] = r >= 0 ? reinterpret_cast<const f16*>(p.a) + (long)r * p.lda + 8 * gi : nullptr;
+  for (int u = 0; u < kDmaA; ++u) {
+    const int row = 8 * (u * 4 + wave) + (lane >> 3);
+    const int gi = (lane & 7) ^ (row & 7);
+    asrc[u] = reinterpret_cast<const f16*>(p.a) + (long)sm.row_a[row] * p.lda + 8 * gi;
   }
-  auto load_a = [&](int chunk, f16x8 (&st)[8]) {
+  // B: wave w fills column blocks 2w and 2w+1 of the tile (1 KiB each per group).
+  const int nb0 = n0 / 16;
+  const u32x4* bsrc0 =
+      reinterpret_cast<const u32x4*>(bptr) + ((long)(nb0 + 2 * wave) * groups) * 64 + lane;
+  const u32x4* bsrc1 = bsrc0 + (long)groups * 64;
+  // Scales (wave 0) / zero points (wave 1): lane l reads dword l%8 of column block l/8
+  // (zero points: dword l%2 of block (l%16)/2); the other waves re-read the scales into
+  // their spare slot.
+  const uint32_t* szsrc;
+  long szstride;  // dwords per group
+  if (ZP && wave == 1) {
+    const int l = lane & 15;
+    szsrc = zptr + ((long)(nb0 + (l >> 1)) * groups) * 2 + (l & 1);
+    szstride = 2;
+  } else {
+    szsrc = reinterpret_cast<const uint32_t*>(sptr) + ((long)(nb0 + (lane >> 3)) * groups) * 8 +
+            (lane & 7);
+    szstride = 8;
+  }
+
+  const int nchunks = p.k / KC;
+  auto issue_a = [&](int c) {
+    const int cc = c < nchunks ? c : nchunks - 1;
+    f16x8* dst = &sm.a[c % NS][wave * 64];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      st[i] = arows[i] ? *reinterpret_cast<const f16x8*>(arows[i] + (long)chunk * KC)
-                       : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int u = 0; u < kDmaA; ++u)
+      __builtin_amdgcn_global_load_lds(asrc[u] + (long)cc * KC, dst + u * 256, 16, 0, 0);
   };
-  auto store_a = [&](int stage, const f16x8 (&st)[8]) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = (tid >> 3) + 32 * i;
-      lds_a[stage][row * 8 + (gi ^ (row & 7))] = st[i];
-    }
+  auto issue_g = [&](int g) {
+    const int gg = g < groups ? g : groups - 1;
+    u32x4* bdst = &sm.b[g & 1][2 * wave * 64];
+    __builtin_amdgcn_global_load_lds(bsrc0 + (long)gg * 64, bdst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(bsrc1 + (long)gg * 64, bdst + 64, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(szsrc + (long)gg * szstride, &sm.sz[g & 1][wave * 64], 4, 0,
+                                     0);
   };
 
-  // ---- B: lane (c = lane & 31, h = lane >> 5) of 32-column block cb ----------------------
+  // ---- per-lane compute geometry ---------------------------------------------------------
   const int c32 = lane & 31;
   const int hh = lane >> 5;
-  long bbase[2];   // index (in 16-byte units) of the lane's first vector, group 0
-  long sbase[2];   // scale index of the lane's column, group 0
-  long zbase[2];
+  int bblk[2];  // tile column block holding the lane's column in each 32-column block
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int col = n0 + 64 * wn + 32 * cb + c32;
-    const long nb = col >> 4;
-    bbase[cb] = nb * groups * 64 + (col & 15) + 16 * hh;
-    sbase[cb] = nb * groups * 16 + (col & 15);
-    zbase[cb] = nb * groups;
-  }
-  const u32x4* bvec = reinterpret_cast<const u32x4*>(bptr);
-  const f16* svec = reinterpret_cast<const f16*>(sptr);
-  const u32x2* zvec = reinterpret_cast<const u32x2*>(zptr);
-
-  u32x4 bcur[2][2], bnext[2][2];   // [cb][r]: r = 0 rows 8h.., r = 1 rows 16 + 8h..
-  f16 scur[2], snext[2];
-  u32x2 zcur[2], znext[2];
-  auto load_b = [&](int g, u32x4 (&bw)[2][2], f16 (&sv)[2], u32x2 (&zv)[2]) {
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const long base = bbase[cb] + (long)g * 64;
-      bw[cb][0] = bvec[base];
-      bw[cb][1] = bvec[base + 32];
-      sv[cb] = svec[sbase[cb] + (long)g * 16];
-      if (ZP) zv[cb] = zvec[zbase[cb] + g];
-    }
-  };
+  for (int cb = 0; cb < 2; ++cb) bblk[cb] = 4 * wn + 2 * cb + (c32 >> 4);
+  const int c16 = c32 & 15;
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -218,27 +259,37 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(TileArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
   float sigma[2] = {1.f, 1.f};
-
-  // Prologue: chunk 0 into LDS stage 0, weights of group 0 into registers.
-  {
-    f16x8 st[8];
-    load_a(0, st);
-    store_a(0, st);
-  }
-  load_b(0, bcur, scur, zcur);
-  __syncthreads();
-
+  u32x4 bw[2][2];  // [cb][r]: vector r of the lane's column, rows 16*r + 8*h + ... per step
+  ZeroOffsets zo[2];
   const MagicRegs mr = magic_regs();
-  const int nchunks = p.k / KC;
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int g = ch >> 1;
-    const int h2 = ch & 1;
-    ZeroOffsets zo[2];
+
+  // Prologue, in steady-state order: A(0) | B/SZ(0), A(1) | A(2).
+  issue_a(0);
+  issue_g(0);
+  issue_a(1);
+  issue_a(2);
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int g = c >> 1;
+    const int h2 = c & 1;
+    if (h2 == 0)
+      wait_vmcnt<kWaitEven>();
+    else
+      wait_vmcnt<kWaitOdd>();
+    __builtin_amdgcn_s_barrier();
+    if (h2 == 0) issue_g(g + 1);
+    issue_a(c + 3);
+
     if (h2 == 0) {
-      // New group: rescale running sums to this group's scale, fetch next group's weights.
+      // New group: weights of the group from its slot, then rescale the running sums.
+      const u32x4* bslot = sm.b[g & 1];
+      const f16* sl = reinterpret_cast<const f16*>(sm.sz[g & 1]);
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        const float sn = sigma_of(scur[cb]);
+        const int base = bblk[cb] * 64 + c16 + 16 * hh;
+        bw[cb][0] = bslot[base];
+        bw[cb][1] = bslot[base + 32];
+        const float sn = sigma_of(sl[bblk[cb] * 16 + c16]);
         if (g > 0) {
           const float ratio = sigma[cb] / sn;
 #pragma unroll
@@ -247,47 +298,53 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(TileArgs p) {
             for (int r = 0; r < 16; ++r) acc[rb][cb][r] *= ratio;
         }
         sigma[cb] = sn;
+        int zc = 8;
+        if constexpr (ZP) {
+          const uint32_t* zl = sm.sz[g & 1] + 64;
+          zc = zero_code(u32x2{zl[2 * bblk[cb]], zl[2 * bblk[cb] + 1]}, c16);
+        }
+        zo[cb] = zero_offsets(zc);
       }
-      if (g + 1 < groups) load_b(g + 1, bnext, snext, znext);
     }
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) zo[cb] = zero_offsets(ZP ? zero_code(zcur[cb], c32 & 15) : 8);
 
-    f16x8 st[8];
-    const bool more = ch + 1 < nchunks;
-    if (more) load_a(ch + 1, st);
-
-    const f16x8* lds = lds_a[ch & 1];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      // Weights of 16-row step (4*h2 + s) of the group: dword (2*h2 + s/2) of vector s%2.
-      f16x8 bop[2];
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-        bop[cb] = dequant8(bcur[cb][s & 1][2 * h2 + (s >> 1)], zo[cb], mr);
+    // Waves whose rows are all past the end skip the arithmetic (but keep loading and
+    // meeting the barrier); the others run all four row blocks, the next step's A operands
+    // being read from LDS while the current step's MFMAs run.
+    if (nrb > 0) {
+      const f16x8* stage = sm.a[c % NS];
+      f16x8 aop[4];
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
-        if (rb < nrb) {
-          const int row = 128 * wm + 32 * rb + c32;
-          const f16x8 aop = lds[row * 8 + ((2 * s + hh) ^ (row & 7))];
+        const int row = 128 * wm + 32 * rb + c32;
+        aop[rb] = stage[row * 8 + (hh ^ (row & 7))];
+      }
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma32x32x16(aop, bop[cb], acc[rb][cb]);
+      for (int s = 0; s < 4; ++s) {
+        f16x8 anext[4];
+        if (s < 3) {
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) {
+            const int row = 128 * wm + 32 * rb + c32;
+            anext[rb] = stage[row * 8 + ((2 * (s + 1) + hh) ^ (row & 7))];
+          }
+        }
+        // Weights of 16-row step (4*h2 + s) of the group: dword (2*h2 + s/2) of vector s%2.
+        f16x8 bop[2];
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+          bop[cb] = dequant8(bw[cb][s & 1][2 * h2 + (s >> 1)], zo[cb], mr);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma32x32x16(aop[rb], bop[cb], acc[rb][cb]);
+        if (s < 3) {
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) aop[rb] = anext[rb];
         }
       }
     }
-
-    if (more) store_a((ch + 1) & 1, st);
-    __syncthreads();
-    if (h2 == 1 && g + 1 < groups) {
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        bcur[cb][0] = bnext[cb][0];
-        bcur[cb][1] = bnext[cb][1];
-        scur[cb] = snext[cb];
-        zcur[cb] = znext[cb];
-      }
-    }
   }
+  wait_vmcnt<0>();  // the trailing re-reads have landed before the work-group ends
 
   // Epilogue: lane holds rows 8*(r/4) + 4*h + (r%4) of column c32 in each 32x32 block.
 #pragma unroll
@@ -299,7 +356,7 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(TileArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = 128 * wm + 32 * rb + 8 * (r >> 2) + 4 * hh + (r & 3);
-        const int orow = row_c[row];
+        const int orow = sm.row_c[row];
         if (orow >= 0)
           p.c[(long)orow * p.n + col] =
               __builtin_bit_cast(uint16_t, (f16)(acc[rb][cb][r] * sigma[cb]));
@@ -323,11 +380,11 @@ hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b
   p.c = c;
   p.n = n;
   p.k = k;
-  const dim3 grid(n / TN, (m + TM - 1) / TM);
+  p.tiles = (n / TN) * ((m + TM - 1) / TM);
   if (z != nullptr)
-    hipLaunchKernelGGL((gemm_tile_kernel<true, false>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((gemm_tile_kernel<true, false>), dim3(p.tiles), dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm_tile_kernel<false, false>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((gemm_tile_kernel<false, false>), dim3(p.tiles), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -353,9 +410,12 @@ hipError_t launch_grouped_tile(const GroupedProblem& g, hipStream_t stream) {
   p.n_active = g.n_active;
   p.n_pairs = g.n_pairs;
   p.n_tokens = g.n_tokens;
-  // Upper bound on tiles: every segment adds at most one partial row tile.
-  const long tiles = ((long)(g.n_pairs + TM - 1) / TM + g.n_active) * (g.n / TN);
+  // Upper bound on tiles (every segment adds at most one partial row tile), rounded up to
+  // a multiple of the XCD count; work-groups without a tile exit at once.
+  long tiles = ((long)(g.n_pairs + TM - 1) / TM + g.n_active) * (g.n / TN);
+  tiles = (tiles + kXcds - 1) / kXcds * kXcds;
   if (tiles <= 0) return hipSuccess;
+  p.tiles = (int)tiles;
   if (g.z_bank != nullptr)
     hipLaunchKernelGGL((gemm_tile_kernel<true, true>), dim3((unsigned)tiles), dim3(256), 0,
                        stream, p);

@@ -1,15 +1,16 @@
 // Tiled W4A16 GEMM for larger M (prefill) and the expert-major grouped (MoE) variant.
 //
-// A work-group computes a 256 x 128 tile of C with four waves of 128 x 64, each a 4 x 2
-// grid of 32x32x16 fp16 MFMA blocks with fp32 accumulators held in VGPRs.
+// A work-group computes a 256 x 256 tile of C with eight waves (2 x 4) of 128 x 64, each
+// a 4 x 2 grid of 32x32x16 fp16 MFMA blocks with fp32 accumulators held in VGPRs.  Two
+// waves share each SIMD, so one wave's MFMAs cover the other's LDS waits and barrier.
 //
 // Data movement is all direct-to-LDS loads (global_load_lds), issued at a fixed count per
 // wave so that the in-order load counter tells exactly when a stage has landed:
-//  * A (fp16) in 256 x 64 chunks through a 4-stage ring (128 KiB), three chunks ahead;
+//  * A (fp16) in 256 x 64 chunks through a 3-stage ring (96 KiB), two chunks ahead;
 //    each wave load writes 8 rows x 128 B, and the source granule of every lane is chosen
 //    so that the ring holds the 16-byte granules of a row XOR-swizzled by (row & 7):
 //    reads of one granule column by 32 consecutive rows are then free of bank conflicts.
-//  * packed B (8 KiB per 128-row group for the tile's 8 column blocks) and the group's
+//  * packed B (16 KiB per 128-row group for the tile's 16 column blocks) and the group's
 //    scales / zero points into one of two group slots, one group ahead.
 // Every iteration waits for its own loads, meets the other waves at a barrier (after which
 // the stage about to be refilled is no longer read by anyone), issues the next loads and
@@ -38,20 +39,24 @@ namespace wq {
 namespace {
 
 constexpr int TM = kTileM;   // 256
-constexpr int TN = kTileN;   // 128
+constexpr int TN = kTileN;   // 256
 constexpr int KC = 64;       // K rows per A chunk (half a group)
-constexpr int NS = 4;        // A ring stages
+constexpr int NS = 3;        // A ring stages
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBlocks = TN / 16;  // 16-column blocks per tile
 constexpr int kXcds = 8;
 
-// Direct-to-LDS loads each wave issues: 8 per A chunk; per group 2 (B) + 1 (scales / zero
+// Direct-to-LDS loads each wave issues: 4 per A chunk; per group 2 (B) + 1 (scales / zero
 // points), issued with the group's even chunk.
-constexpr int kDmaA = 8;
+constexpr int kDmaA = TM * KC / 8 / kThreads;
 constexpr int kDmaG = 3;
 // Loads issued after the ones an iteration waits for (see the pipeline above):
-//  even chunk c = 2g waits for B/SZ(g), followed by A(c+1) and A(c+2);
-//  odd chunk c waits for A(c), followed by A(c+1), B/SZ, A(c+2).
-constexpr int kWaitEven = 2 * kDmaA;
-constexpr int kWaitOdd = 2 * kDmaA + kDmaG;
+//  even chunk c = 2g waits for A(c) (and the earlier B/SZ(g)), followed by A(c+1);
+//  odd chunk c waits for A(c), followed by B/SZ(g+1) and A(c+2).
+constexpr int kWaitEven = kDmaA;
+constexpr int kWaitOdd = kDmaA + kDmaG;
+static_assert(kDmaA == 4 && 2 * kWaves == kBlocks, "load split assumes 8 waves, 256 x 256");
 static_assert(kWaitOdd < 64, "vmcnt holds 6 bits");
 
 template <int N>
@@ -91,23 +96,23 @@ __device__ __forceinline__ float sigma_of(f16 v) {
 }
 
 struct Smem {
-  f16x8 a[NS][TM * KC / 8];     // 4 x 32 KiB
-  u32x4 b[2][8 * 64];           // 2 x 8 KiB: 8 column blocks x 64 lanes x 16 B
-  uint32_t sz[2][4 * 64];       // 2 x 1 KiB: wave 0 scales, wave 1 zero points, 2-3 spare
+  f16x8 a[NS][TM * KC / 8];     // 3 x 32 KiB
+  u32x4 b[2][kBlocks * 64];     // 2 x 16 KiB: 16 column blocks x 64 lanes x 16 B
+  uint32_t sz[2][kWaves * 64];  // 2 x 2 KiB: waves 0-1 scales, wave 2 zero points, spare
   int row_a[TM];
   int row_c[TM];
   int info[5];
 };
 
 template <bool ZP, bool GROUPED>
-__global__ __launch_bounds__(256) void gemm_tile_kernel(TileArgs p) {
+__global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
   __shared__ Smem sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
-  const int wm = wave >> 1;   // wave's 128-row half of the tile
-  const int wn = wave & 1;    // wave's 64-column half of the tile
+  const int wm = wave >> 2;   // wave's 128-row half of the tile
+  const int wn = wave & 3;    // wave's 64-column quarter of the tile
   const int groups = p.k / kGroup;
   const int ntiles_n = p.n / TN;
 
@@ -171,8 +176,10 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(TileArgs p) {
         }
       }
     }
-    sm.row_a[tid] = ra;
-    sm.row_c[tid] = rc;
+    if (tid < TM) {
+      sm.row_a[tid] = ra;
+      sm.row_c[tid] = rc;
+    }
     bptr = reinterpret_cast<const uint32_t*>(p.b_bank + (size_t)e * p.b_stride);
     sptr = reinterpret_cast<const uint16_t*>(p.s_bank + (size_t)e * p.s_stride);
     zptr = ZP ? reinterpret_cast<const uint32_t*>(p.z_bank + (size_t)e * p.z_stride) : nullptr;
@@ -184,8 +191,10 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(TileArgs p) {
     valid_rows = p.m - m0 < TM ? p.m - m0 : TM;
     // Rows past m read the last row (finite, never stored).
     const int r = m0 + tid;
-    sm.row_a[tid] = r < p.m ? r : p.m - 1;
-    sm.row_c[tid] = r < p.m ? r : -1;
+    if (tid < TM) {
+      sm.row_a[tid] = r < p.m ? r : p.m - 1;
+      sm.row_c[tid] = r < p.m ? r : -1;
+    }
     bptr = p.b;
     sptr = p.s;
     zptr = p.z;
@@ -197,12 +206,12 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(TileArgs p) {
   nrb = __builtin_amdgcn_readfirstlane(nrb < 0 ? 0 : (nrb > 4 ? 4 : nrb));
 
   // ---- load sources -------------------------------------------------------------------
-  // A: slot u of this lane fills ring granule (u*4 + wave)*64 + lane = row 8*(u*4+wave) +
+  // A: slot u of this lane fills ring granule (u*8 + wave)*64 + lane = row 8*(u*8+wave) +
   // lane/8, physical granule lane%8, i.e. logical granule (lane%8) ^ (row & 7).
   const f16* asrc[kDmaA];
 #pragma unroll
   for (int u = 0; u < kDmaA; ++u) {
-    const int row = 8 * (u * 4 + wave) + (lane >> 3);
+    const int row = 8 * (u * kWaves + wave) + (lane >> 3);
     const int gi = (lane & 7) ^ (row & 7);
     asrc[u] = reinterpret_cast<const f16*>(p.a) + (long)sm.row_a[row] * p.lda + 8 * gi;
   }
@@ -211,17 +220,18 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(TileArgs p) {
   const u32x4* bsrc0 =
       reinterpret_cast<const u32x4*>(bptr) + ((long)(nb0 + 2 * wave) * groups) * 64 + lane;
   const u32x4* bsrc1 = bsrc0 + (long)groups * 64;
-  // Scales (wave 0) / zero points (wave 1): lane l reads dword l%8 of column block l/8
-  // (zero points: dword l%2 of block (l%16)/2); the other waves re-read the scales into
-  // their spare slot.
+  // Scales (waves 0 and 1): lane l reads dword l%8 of column block 8*wave + l/8; zero
+  // points (wave 2): lane l reads word l%2 of block (l%32)/2; the other waves re-read the
+  // scales of blocks 0-7 into their spare slot.
   const uint32_t* szsrc;
   long szstride;  // dwords per group
-  if (ZP && wave == 1) {
-    const int l = lane & 15;
+  if (ZP && wave == 2) {
+    const int l = lane & 31;
     szsrc = zptr + ((long)(nb0 + (l >> 1)) * groups) * 2 + (l & 1);
     szstride = 2;
   } else {
-    szsrc = reinterpret_cast<const uint32_t*>(sptr) + ((long)(nb0 + (lane >> 3)) * groups) * 8 +
+    const int blk = (wave == 1 ? 8 : 0) + (lane >> 3);
+    szsrc = reinterpret_cast<const uint32_t*>(sptr) + ((long)(nb0 + blk) * groups) * 8 +
             (lane & 7);
     szstride = 8;
   }
@@ -232,7 +242,7 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(TileArgs p) {
     f16x8* dst = &sm.a[c % NS][wave * 64];
 #pragma unroll
     for (int u = 0; u < kDmaA; ++u)
-      __builtin_amdgcn_global_load_lds(asrc[u] + (long)cc * KC, dst + u * 256, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(asrc[u] + (long)cc * KC, dst + u * kThreads, 16, 0, 0);
   };
   auto issue_g = [&](int g) {
     const int gg = g < groups ? g : groups - 1;
@@ -263,11 +273,10 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(TileArgs p) {
   ZeroOffsets zo[2];
   const MagicRegs mr = magic_regs();
 
-  // Prologue, in steady-state order: A(0) | B/SZ(0), A(1) | A(2).
+  // Prologue, in steady-state order: A(0) | B/SZ(0), A(1).
   issue_a(0);
   issue_g(0);
   issue_a(1);
-  issue_a(2);
 
   for (int c = 0; c < nchunks; ++c) {
     const int g = c >> 1;
@@ -278,7 +287,7 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(TileArgs p) {
       wait_vmcnt<kWaitOdd>();
     __builtin_amdgcn_s_barrier();
     if (h2 == 0) issue_g(g + 1);
-    issue_a(c + 3);
+    issue_a(c + 2);
 
     if (h2 == 0) {
       // New group: weights of the group from its slot, then rescale the running sums.
@@ -300,7 +309,7 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(TileArgs p) {
         sigma[cb] = sn;
         int zc = 8;
         if constexpr (ZP) {
-          const uint32_t* zl = sm.sz[g & 1] + 64;
+          const uint32_t* zl = sm.sz[g & 1] + 128;
           zc = zero_code(u32x2{zl[2 * bblk[cb]], zl[2 * bblk[cb] + 1]}, c16);
         }
         zo[cb] = zero_offsets(zc);
@@ -382,9 +391,9 @@ hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b
   p.k = k;
   p.tiles = (n / TN) * ((m + TM - 1) / TM);
   if (z != nullptr)
-    hipLaunchKernelGGL((gemm_tile_kernel<true, false>), dim3(p.tiles), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((gemm_tile_kernel<true, false>), dim3(p.tiles), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm_tile_kernel<false, false>), dim3(p.tiles), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((gemm_tile_kernel<false, false>), dim3(p.tiles), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -417,10 +426,10 @@ hipError_t launch_grouped_tile(const GroupedProblem& g, hipStream_t stream) {
   if (tiles <= 0) return hipSuccess;
   p.tiles = (int)tiles;
   if (g.z_bank != nullptr)
-    hipLaunchKernelGGL((gemm_tile_kernel<true, true>), dim3((unsigned)tiles), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_tile_kernel<true, true>), dim3((unsigned)tiles), dim3(kThreads), 0,
                        stream, p);
   else
-    hipLaunchKernelGGL((gemm_tile_kernel<false, true>), dim3((unsigned)tiles), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_tile_kernel<false, true>), dim3((unsigned)tiles), dim3(kThreads), 0,
                        stream, p);
   return hipGetLastError();
 }

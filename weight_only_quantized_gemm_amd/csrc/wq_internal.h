@@ -32,9 +32,9 @@ hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* 
                              const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                              const SmallPlan& plan, float* partials, hipStream_t stream);
 
-// Tiled kernel (wq_gemm_tile.hip): 256 x 128 output tiles on 4 waves of 128 x 64.
+// Tiled kernel (wq_gemm_tile.hip): 256 x 256 output tiles on 8 waves of 128 x 64.
 constexpr int kTileM = 256;
-constexpr int kTileN = 128;
+constexpr int kTileN = 256;
 hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b,
                             const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                             hipStream_t stream);

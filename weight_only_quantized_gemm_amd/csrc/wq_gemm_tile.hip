@@ -8,7 +8,7 @@
 // wave so that the in-order load counter tells exactly when a stage has landed:
 //  * A (fp16) in 256 x 64 chunks through a 3-stage ring (96 KiB), two chunks ahead;
 //    each wave load writes 8 rows x 128 B, and the source granule of every lane is chosen
-//    so that the ring holds the 16-byte granules of a row XOR-swizzled by (row & 7):
+//    so that the ring holds the 16-byte granules of a row XOR-swizzled by ((row >> 1) & 7):
 //    reads of one granule column by 32 consecutive rows are then free of bank conflicts.
 //  * packed B (16 KiB per 128-row group for the tile's 16 column blocks) and the group's
 //    scales / zero points into one of two group slots, one group ahead.
@@ -32,6 +32,8 @@
 // tiles are enumerated over (active expert segment, column tile, row tile); a tile's rows
 // are CSR positions of one expert, A rows come from pair_tok[ex_pairs[j]] and outputs go
 // to pair-major row ex_pairs[j].
+#include <type_traits>
+
 #include "wq_device.h"
 #include "wq_internal.h"
 
@@ -207,12 +209,12 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
 
   // ---- load sources -------------------------------------------------------------------
   // A: slot u of this lane fills ring granule (u*8 + wave)*64 + lane = row 8*(u*8+wave) +
-  // lane/8, physical granule lane%8, i.e. logical granule (lane%8) ^ (row & 7).
+  // lane/8, physical granule lane%8, i.e. logical granule (lane%8) ^ ((row >> 1) & 7).
   const f16* asrc[kDmaA];
 #pragma unroll
   for (int u = 0; u < kDmaA; ++u) {
     const int row = 8 * (u * kWaves + wave) + (lane >> 3);
-    const int gi = (lane & 7) ^ (row & 7);
+    const int gi = (lane & 7) ^ ((row >> 1) & 7);
     asrc[u] = reinterpret_cast<const f16*>(p.a) + (long)sm.row_a[row] * p.lda + 8 * gi;
   }
   // B: wave w fills column blocks 2w and 2w+1 of the tile (1 KiB each per group).
@@ -260,6 +262,9 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) bblk[cb] = 4 * wn + 2 * cb + (c32 >> 4);
   const int c16 = c32 & 15;
+  int aswz[4];  // granule of step s inside the lane's A row: (2s + h) ^ swizzle
+#pragma unroll
+  for (int st = 0; st < 4; ++st) aswz[st] = (2 * st + hh) ^ ((c32 >> 1) & 7);
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -278,13 +283,12 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
   issue_g(0);
   issue_a(1);
 
-  for (int c = 0; c < nchunks; ++c) {
+  // One iteration per group: its even chunk (which also starts the group) and odd chunk,
+  // so that the chunk parity, and with it the weight dwords each step reads, is static.
+  auto chunk = [&](auto h2c, int c) {
+    constexpr int h2 = decltype(h2c)::value;
     const int g = c >> 1;
-    const int h2 = c & 1;
-    if (h2 == 0)
-      wait_vmcnt<kWaitEven>();
-    else
-      wait_vmcnt<kWaitOdd>();
+    wait_vmcnt<h2 == 0 ? kWaitEven : kWaitOdd>();
     __builtin_amdgcn_s_barrier();
     if (h2 == 0) issue_g(g + 1);
     issue_a(c + 2);
@@ -300,7 +304,9 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
         bw[cb][1] = bslot[base + 32];
         const float sn = sigma_of(sl[bblk[cb] * 16 + c16]);
         if (g > 0) {
-          const float ratio = sigma[cb] / sn;
+          // sigma_prev / sigma_new with the hardware reciprocal (about 1 ulp): a relative
+          // error near 1e-7 per group boundary.
+          const float ratio = sigma[cb] * __builtin_amdgcn_rcpf(sn);
 #pragma unroll
           for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
@@ -320,22 +326,18 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
     // meeting the barrier); the others run all four row blocks, the next step's A operands
     // being read from LDS while the current step's MFMAs run.
     if (nrb > 0) {
-      const f16x8* stage = sm.a[c % NS];
+      // Row 128*wm + 32*rb + c32 of the stage; its swizzle (row >> 1) & 7 = (c32 >> 1) & 7
+      // does not depend on rb, so a step's four reads share one address plus offsets.
+      const f16x8* arow = sm.a[c % NS] + (128 * wm + c32) * 8;
       f16x8 aop[4];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const int row = 128 * wm + 32 * rb + c32;
-        aop[rb] = stage[row * 8 + (hh ^ (row & 7))];
-      }
+      for (int rb = 0; rb < 4; ++rb) aop[rb] = arow[rb * 256 + aswz[0]];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         f16x8 anext[4];
         if (s < 3) {
 #pragma unroll
-          for (int rb = 0; rb < 4; ++rb) {
-            const int row = 128 * wm + 32 * rb + c32;
-            anext[rb] = stage[row * 8 + ((2 * (s + 1) + hh) ^ (row & 7))];
-          }
+          for (int rb = 0; rb < 4; ++rb) anext[rb] = arow[rb * 256 + aswz[s + 1]];
         }
         // Weights of 16-row step (4*h2 + s) of the group: dword (2*h2 + s/2) of vector s%2.
         f16x8 bop[2];
@@ -352,6 +354,10 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
         }
       }
     }
+  };
+  for (int g = 0; g < groups; ++g) {
+    chunk(std::integral_constant<int, 0>{}, 2 * g);
+    chunk(std::integral_constant<int, 1>{}, 2 * g + 1);
   }
   wait_vmcnt<0>();  // the trailing re-reads have landed before the work-group ends
 

@@ -11,6 +11,7 @@ host cores as the CPU baseline.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -109,6 +110,51 @@ def bench_moe(torch, torch_ops, steps, warmup):
     return dict(sec=sec, flops=flops, weight_bytes=moe["n_expert"] * moe["k"] * moe["n"] // 2)
 
 
+COPY_BYTES = 1 << 30  # plain device copy used to calibrate the HBM byte counters
+
+
+def bench_copy(torch, steps, warmup):
+    """A plain 1 GiB device-to-device copy (reads and writes COPY_BYTES each)."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    sec = timed_loop(torch, lambda i: dst.copy_(src), steps, warmup)
+    return dict(sec=sec, bytes=COPY_BYTES)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_hbm_traffic.txt")
+SMALL_SOURCE = os.path.join(ROOT, "weight_only_quantized_gemm_amd", "csrc", "wq_gemm_small.hip")
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic() -> float | None:
+    """HBM bytes per decode launch from the committed counter summary, or None.
+
+    The summary records FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the decode kernel
+    and of a plain copy of known size; each counter is scaled by the factor the copy gives.
+    It only applies while the kernel source is the one that was profiled.
+    """
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, _, val = line.partition(":")
+                vals[key.strip()] = val.strip()
+    try:
+        if vals.get("kernel_source_sha256_16") != source_hash(SMALL_SOURCE):
+            return None
+        fetch = float(vals["decode_fetch_kib"]) * 1024 * float(vals["fetch_factor"])
+        write = float(vals["decode_write_kib"]) * 1024 * float(vals["write_factor"])
+        return fetch + write
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(budget_s: float) -> dict:
     """The oracle (fp64 numpy) on the decode workload, repeated for about `budget_s`."""
     import synthetic
@@ -141,7 +187,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "batched", "prefill", "moe", "tiny"],
+    ap.add_argument("--only", choices=["decode", "batched", "prefill", "moe", "tiny", "copy"],
                     default=None, help="time one workload (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -156,7 +202,12 @@ def main() -> int:
     torch.cuda.set_device(0)
 
     if args.only:
-        if args.only == "moe":
+        if args.only == "copy":
+            r = bench_copy(torch, args.steps, args.warmup)
+            print(json.dumps({"only": "copy", "bytes_read": r["bytes"], "bytes_written": r["bytes"],
+                              "us": r["sec"] * 1e6,
+                              "TBs_read_plus_write": 2 * r["bytes"] / r["sec"] / 1e12}), flush=True)
+        elif args.only == "moe":
             r = bench_moe(torch, torch_ops, args.steps, args.warmup)
             print(json.dumps({"only": "moe", "us": r["sec"] * 1e6,
                               "tflops": r["flops"] / r["sec"] / 1e12}), flush=True)
@@ -199,7 +250,7 @@ def main() -> int:
                    "m": 1, "k": 4096, "n": 14336, "weight_bytes": dec["weight_bytes"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic()},
         "prefill": {"workload": "M=2048 K=4096 N=14336 u4b8 group128 act_order (gather + GEMM)",
                     "tflops": round(pre_tflops, 2), "us": round(pre["sec"] * 1e6, 2),
                     "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2),

@@ -133,6 +133,22 @@ def test_gemm_matches_oracle_small(dev, m, k, n, zp, act_order, fp32, split):
     assert_parity(c, oracle_gemm(case), label)
 
 
+# act_order gathers: every LDS staging width of the row gather (K/8 granules over 256
+# threads: 1, 2, 4, 8 per thread), its global-memory fallback beyond K = 16384, and more
+# rows than the gather's 1024 work-groups, so that work-groups loop over rows.
+ACT_ORDER_SHAPES = [(5, 256), (20, 2048), (1100, 4096), (40, 8192), (33, 16384), (17, 17408)]
+
+
+@pytest.mark.parametrize("m,k", ACT_ORDER_SHAPES)
+def test_act_order_gather_widths(dev, m, k):
+    n = 256
+    label = f"act_order m={m} k={k} n={n}"
+    say(label)
+    case = synthetic.dense_case(m, k, n, act_order=True, seed=2000 + m + k)
+    c = gpu_gemm(case, dev)
+    assert_parity(c, oracle_gemm(case), label)
+
+
 @pytest.mark.parametrize("name", ["tiny", "decode", "batched"])
 def test_config_matches_oracle_in_full(dev, name):
     case = synthetic.config_case(name)

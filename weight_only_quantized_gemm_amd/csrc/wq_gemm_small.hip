@@ -109,22 +109,44 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   __syncthreads();
 
   // 5. Arithmetic.  MFMA rows >= m are never stored, and a row of the product depends on
-  //    its own A row only, so those lanes read row m - 1 instead of selecting zeros.
+  //    its own A row only, so those lanes read row m - 1 instead of selecting zeros.  The
+  //    group scales are read up front and each group's activation operands are read from
+  //    LDS while the previous group's MFMAs run, so that no LDS round trip sits between a
+  //    weight chunk's arrival and its products.
   const MagicRegs mr = magic_regs();
   const int arow = (col < m ? col : m - 1) * per_row;
   const f16* s_half = reinterpret_cast<const f16*>(s_lds);
+  int gl[GW];  // group of step i inside the staged range (clamped for the masked steps)
+  float sc[GW];
+#pragma unroll
+  for (int i = 0; i < GW; ++i) {
+    gl[i] = g0 - gs0 + (i < gw ? i : gw - 1);
+    const float v = (float)s_half[gl[i] * 16 + col];
+    sc[i] = i < gw ? v : 0.f;
+  }
+  f16x8 an[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) an[j] = a_lds[arow + gl[0] * 16 + 4 * j + qd];
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < GW; ++i) {
-    const int gl = g0 - gs0 + (i < gw ? i : gw - 1);  // group inside the staged range
-    const float sc = i < gw ? (float)s_half[gl * 16 + col] : 0.f;
-    const ZeroOffsets zo = zero_offsets(ZP ? zero_code(z_lds[gl], col) : 8);
+    f16x8 ac[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ac[j] = an[j];
+    if (i + 1 < GW) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) an[j] = a_lds[arow + gl[i + 1] * 16 + 4 * j + qd];
+    }
+    // With eight groups per wave, pin the prefetch ahead of this group's work (measured
+    // faster for the decode shape, slower for shallower pipelines).
+    if constexpr (GW >= 8) __builtin_amdgcn_sched_barrier(0);
+    const ZeroOffsets zo = zero_offsets(ZP ? zero_code(z_lds[gl[i]], col) : 8);
     f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      p = mfma16x16x32(a_lds[arow + gl * 16 + 4 * j + qd], dequant8(bw[i][j], zo, mr), p);
+    for (int j = 0; j < 4; ++j) p = mfma16x16x32(ac[j], dequant8(bw[i][j], zo, mr), p);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sc, p[e], acc[e]);
+    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sc[i], p[e], acc[e]);
+    if constexpr (GW >= 8) __builtin_amdgcn_sched_barrier(0);
   }
 
   // Work-group reduce over the waves, in wave order.

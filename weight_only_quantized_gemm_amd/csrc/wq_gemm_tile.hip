@@ -10,28 +10,35 @@
 //    each wave load writes 8 rows x 128 B, and the source granule of every lane is chosen
 //    so that the ring holds the 16-byte granules of a row XOR-swizzled by ((row >> 1) & 7):
 //    reads of one granule column by 32 consecutive rows are then free of bank conflicts.
-//  * packed B (16 KiB per 128-row group for the tile's 16 column blocks) and the group's
-//    scales / zero points into one of two group slots, one group ahead.
-// Every iteration waits for its own loads, meets the other waves at a barrier (after which
+//  * packed B (16 KiB per 128-row group for the tile's 16 column blocks) into one of two
+//    group slots, issued with the odd chunk two groups ahead of its use;
+//  * the group's scales / zero points into one of two small slots, two groups ahead.
+// Every chunk waits for its own loads, meets the other waves at a barrier (after which
 // the stage about to be refilled is no longer read by anyone), issues the next loads and
 // computes.  Loads past the end re-read the last chunk / group into the free stage, so the
 // counts never change; nothing is read outside the tensors.
 //
+// Inside a chunk each 16-row step reads the next step's A operands from LDS and
+// dequantizes its weights while the current step's eight MFMAs run; the order is pinned
+// with scheduling-group hints, as the default schedule waits on every LDS read right
+// before its MFMA.
+//
 // Weights are dequantized in registers to exact fp16 integers (q - z).  Group scales are
-// applied in fp32 without a second accumulator set: before the MFMAs of group g accumulate,
-// the running sums are multiplied by sigma_{g-1} / sigma_g, and the result is multiplied by
-// sigma_last at the end, so C = sum_g sigma_g * P_g with P_g the exact-integer-weight
-// partial of group g.  sigma is the fp16 scale widened to fp32, with an exact zero
-// replaced by 2^-60 (its contribution then vanishes after rounding to fp16).
+// applied in fp32 without a second accumulator set: after the last MFMAs of group g the
+// running sums are multiplied by sigma_g / sigma_{g+1} (interleaved with those MFMAs), and
+// the result is multiplied by sigma_last at the end, so C = sum_g sigma_g * P_g with P_g
+// the exact-integer-weight partial of group g.  sigma is the fp16 scale widened to fp32,
+// with an exact zero replaced by 2^-60 (its contribution then vanishes after rounding to
+// fp16).
 //
 // Tiles are assigned XCD-aware: work-groups are dealt to the 8 XCDs round-robin, so tile
 // ids are remapped to give each XCD a contiguous range (for a 2048-row problem, one
 // 256-row A panel per XCD, which then stays in that XCD's L2).
 //
 // Grouped variant (memra-engine mmq_ffi.rs, `ExpertCsr` and the grouped projection call):
-// tiles are enumerated over (active expert segment, column tile, row tile); a tile's rows
-// are CSR positions of one expert, A rows come from pair_tok[ex_pairs[j]] and outputs go
-// to pair-major row ex_pairs[j].
+// a tile's rows are CSR positions of one expert, A rows come from pair_tok[ex_pairs[j]]
+// and outputs go to pair-major row ex_pairs[j].  Tiles are dispatched longest first:
+// full row tiles before the short partial tiles that ragged expert sizes leave.
 #include <type_traits>
 
 #include "wq_device.h"
@@ -48,18 +55,28 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBlocks = TN / 16;  // 16-column blocks per tile
 constexpr int kXcds = 8;
+constexpr int kTailRows = TM / 2;  // grouped tiles with at most this many rows are "small"
 
-// Direct-to-LDS loads each wave issues: 4 per A chunk; per group 2 (B) + 1 (scales / zero
-// points), issued with the group's even chunk.
+// Direct-to-LDS loads each wave issues: 4 per A chunk, 2 per B group, 1 per scale /
+// zero-point group.  Issue order (one group = chunks 2g, 2g+1):
+//   prologue:   SZ(0) B(0) SZ(1) A(0) A(1) B(1)
+//   chunk 2g:   SZ(g+2) A(2g+2)
+//   chunk 2g+1: A(2g+3) B(g+2)
+// Chunk 2g needs A(2g) (followed by A(2g+1), B(g+1)); chunk 2g+1 needs A(2g+1) and, for
+// the next group's weights read in its last step, B(g+1) (followed by SZ(g+2), A(2g+2)).
 constexpr int kDmaA = TM * KC / 8 / kThreads;
-constexpr int kDmaG = 3;
-// Loads issued after the ones an iteration waits for (see the pipeline above):
-//  even chunk c = 2g waits for A(c) (and the earlier B/SZ(g)), followed by A(c+1);
-//  odd chunk c waits for A(c), followed by B/SZ(g+1) and A(c+2).
-constexpr int kWaitEven = kDmaA;
-constexpr int kWaitOdd = kDmaA + kDmaG;
+constexpr int kDmaB = 2;
+constexpr int kDmaS = 1;
+constexpr int kWaitEven = kDmaA + kDmaB;
+constexpr int kWaitOdd = kDmaS + kDmaA;
+constexpr int kWaitPrologue = kDmaS + 2 * kDmaA + kDmaB;  // SZ(0) and B(0) landed
 static_assert(kDmaA == 4 && 2 * kWaves == kBlocks, "load split assumes 8 waves, 256 x 256");
-static_assert(kWaitOdd < 64, "vmcnt holds 6 bits");
+static_assert(kWaitPrologue < 64, "vmcnt holds 6 bits");
+
+// Scheduling-group masks (instruction classes of the AMDGPU scheduler hints).
+constexpr int kSchedVALU = 0x002;
+constexpr int kSchedMFMA = 0x008;
+constexpr int kSchedDSRead = 0x100;
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -120,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
 
   // XCD-aware tile id: work-group i runs on XCD i % 8; give each XCD a contiguous range.
   int t = blockIdx.x;
-  if (p.tiles % kXcds == 0) t = (t % kXcds) * (p.tiles / kXcds) + t / kXcds;
+  if (!GROUPED && p.tiles % kXcds == 0) t = (t % kXcds) * (p.tiles / kXcds) + t / kXcds;
 
   int n0, valid_rows;
   const uint32_t* bptr;
@@ -129,23 +146,52 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
 
   if constexpr (GROUPED) {
     if (tid == 0) {
-      int seg = -1, lo = 0, rows = 0, mt = 0, nt = 0;
+      // Tiles in longest-first order.  A segment's row tiles are its full 256-row tiles
+      // plus a partial last one; a partial tile of at most kTailRows rows only busies the
+      // first half of the waves and is "small", every other tile is "big".  Each XCD takes
+      // a contiguous share of the big tiles (column tile fastest, so consecutive tiles
+      // reuse the same activation rows) followed by a share of the small ones, and work-
+      // groups are dispatched in order, so the small tiles fill the CUs that the last
+      // round of big tiles leaves idle.
+      int nbig = 0, nsmall = 0;
       for (int i = 0; i < p.n_active; ++i) {
         int a0 = p.ex_off[i], a1 = p.ex_off[i + 1];
         a0 = a0 < 0 ? 0 : (a0 > p.n_pairs ? p.n_pairs : a0);
         a1 = a1 < a0 ? a0 : (a1 > p.n_pairs ? p.n_pairs : a1);
-        const int r = a1 - a0;
-        const int mtiles = (r + TM - 1) / TM;
-        const int tiles = mtiles * ntiles_n;
-        if (t < tiles) {
+        const int r = a1 - a0, full = r / TM, rem = r - full * TM;
+        nbig += full + (rem > kTailRows ? 1 : 0);
+        nsmall += (rem > 0 && rem <= kTailRows) ? 1 : 0;
+      }
+      nbig *= ntiles_n;
+      nsmall *= ntiles_n;
+      const int b8 = (nbig + kXcds - 1) / kXcds, s8 = (nsmall + kXcds - 1) / kXcds;
+      const int x = (int)(blockIdx.x % kXcds), l = (int)(blockIdx.x / kXcds);
+      int kind = -1, idx = 0;  // 0 big, 1 small
+      if (l < b8) {
+        idx = x * b8 + l;
+        kind = idx < nbig ? 0 : -1;
+      } else if (l < b8 + s8) {
+        idx = x * s8 + (l - b8);
+        kind = idx < nsmall ? 1 : -1;
+      }
+      int seg = -1, lo = 0, rows = 0, mt = 0, nt = 0;
+      for (int i = 0; kind >= 0 && i < p.n_active; ++i) {
+        int a0 = p.ex_off[i], a1 = p.ex_off[i + 1];
+        a0 = a0 < 0 ? 0 : (a0 > p.n_pairs ? p.n_pairs : a0);
+        a1 = a1 < a0 ? a0 : (a1 > p.n_pairs ? p.n_pairs : a1);
+        const int r = a1 - a0, full = r / TM, rem = r - full * TM;
+        const int cnt = kind == 1 ? ((rem > 0 && rem <= kTailRows) ? 1 : 0)
+                                  : full + (rem > kTailRows ? 1 : 0);
+        const int tiles = cnt * ntiles_n;
+        if (idx < tiles) {
           seg = i;
           lo = a0;
           rows = r;
-          mt = t % mtiles;
-          nt = t / mtiles;
+          mt = kind == 1 ? full : idx / ntiles_n;
+          nt = kind == 1 ? idx : idx - (idx / ntiles_n) * ntiles_n;
           break;
         }
-        t -= tiles;
+        idx -= tiles;
       }
       int e = seg;
       if (seg >= 0 && p.ex_ids != nullptr) e = p.ex_ids[seg];
@@ -246,11 +292,14 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
     for (int u = 0; u < kDmaA; ++u)
       __builtin_amdgcn_global_load_lds(asrc[u] + (long)cc * KC, dst + u * kThreads, 16, 0, 0);
   };
-  auto issue_g = [&](int g) {
+  auto issue_b = [&](int g) {
     const int gg = g < groups ? g : groups - 1;
     u32x4* bdst = &sm.b[g & 1][2 * wave * 64];
     __builtin_amdgcn_global_load_lds(bsrc0 + (long)gg * 64, bdst, 16, 0, 0);
     __builtin_amdgcn_global_load_lds(bsrc1 + (long)gg * 64, bdst + 64, 16, 0, 0);
+  };
+  auto issue_sz = [&](int g) {
+    const int gg = g < groups ? g : groups - 1;
     __builtin_amdgcn_global_load_lds(szsrc + (long)gg * szstride, &sm.sz[g & 1][wave * 64], 4, 0,
                                      0);
   };
@@ -273,85 +322,152 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
-  float sigma[2] = {1.f, 1.f};
+  float sigma[2];
   u32x4 bw[2][2];  // [cb][r]: vector r of the lane's column, rows 16*r + 8*h + ... per step
   ZeroOffsets zo[2];
   const MagicRegs mr = magic_regs();
 
-  // Prologue, in steady-state order: A(0) | B/SZ(0), A(1).
-  issue_a(0);
-  issue_g(0);
-  issue_a(1);
+  // Scale and zero-point offsets of group g for the lane's two columns (slot g & 1).
+  auto read_sz = [&](int g, float* sg, ZeroOffsets* zg) {
+    const f16* sl = reinterpret_cast<const f16*>(sm.sz[g & 1]);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      sg[cb] = sigma_of(sl[bblk[cb] * 16 + c16]);
+      int zc = 8;
+      if constexpr (ZP) {
+        const uint32_t* zl = sm.sz[g & 1] + 128;
+        zc = zero_code(u32x2{zl[2 * bblk[cb]], zl[2 * bblk[cb] + 1]}, c16);
+      }
+      zg[cb] = zero_offsets(zc);
+    }
+  };
+  // The lane's weight vectors of group g (slot g & 1).
+  auto read_b = [&](int g) {
+    const u32x4* bslot = sm.b[g & 1];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int base = bblk[cb] * 64 + c16 + 16 * hh;
+      bw[cb][0] = bslot[base];
+      bw[cb][1] = bslot[base + 32];
+    }
+  };
 
-  // One iteration per group: its even chunk (which also starts the group) and odd chunk,
-  // so that the chunk parity, and with it the weight dwords each step reads, is static.
+  // Prologue (see the issue order above), then group 0's scales and weights.
+  issue_sz(0);
+  issue_b(0);
+  issue_sz(1);
+  issue_a(0);
+  issue_a(1);
+  issue_b(1);
+  wait_vmcnt<kWaitPrologue>();
+  __builtin_amdgcn_s_barrier();
+  read_sz(0, sigma, zo);
+  read_b(0);
+
+  // One iteration per group: its even chunk and its odd chunk, so that the chunk parity,
+  // and with it the weight dwords each step reads, is static.
   auto chunk = [&](auto h2c, int c) {
     constexpr int h2 = decltype(h2c)::value;
     const int g = c >> 1;
     wait_vmcnt<h2 == 0 ? kWaitEven : kWaitOdd>();
     __builtin_amdgcn_s_barrier();
-    if (h2 == 0) issue_g(g + 1);
-    issue_a(c + 2);
-
     if (h2 == 0) {
-      // New group: weights of the group from its slot, then rescale the running sums.
-      const u32x4* bslot = sm.b[g & 1];
-      const f16* sl = reinterpret_cast<const f16*>(sm.sz[g & 1]);
+      issue_sz(g + 2);
+      issue_a(c + 2);
+    } else {
+      issue_a(c + 2);
+      issue_b(g + 2);
+    }
+
+    // Odd chunk: the next group's scales, and the factor sigma_g / sigma_{g+1} applied to
+    // the running sums after this group's last MFMAs (1 after the last group).  The
+    // hardware reciprocal is about 1 ulp: a relative error near 1e-7 per group boundary.
+    float snext[2], ratio[2];
+    ZeroOffsets znext[2];
+    if (h2 == 1) {
+      read_sz(g + 1, snext, znext);
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const int base = bblk[cb] * 64 + c16 + 16 * hh;
-        bw[cb][0] = bslot[base];
-        bw[cb][1] = bslot[base + 32];
-        const float sn = sigma_of(sl[bblk[cb] * 16 + c16]);
-        if (g > 0) {
-          // sigma_prev / sigma_new with the hardware reciprocal (about 1 ulp): a relative
-          // error near 1e-7 per group boundary.
-          const float ratio = sigma[cb] * __builtin_amdgcn_rcpf(sn);
-#pragma unroll
-          for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[rb][cb][r] *= ratio;
-        }
-        sigma[cb] = sn;
-        int zc = 8;
-        if constexpr (ZP) {
-          const uint32_t* zl = sm.sz[g & 1] + 128;
-          zc = zero_code(u32x2{zl[2 * bblk[cb]], zl[2 * bblk[cb] + 1]}, c16);
-        }
-        zo[cb] = zero_offsets(zc);
-      }
+      for (int cb = 0; cb < 2; ++cb)
+        ratio[cb] = g + 1 < groups ? sigma[cb] * __builtin_amdgcn_rcpf(snext[cb]) : 1.f;
     }
 
     // Waves whose rows are all past the end skip the arithmetic (but keep loading and
-    // meeting the barrier); the others run all four row blocks, the next step's A operands
-    // being read from LDS while the current step's MFMAs run.
+    // meeting the barrier).
     if (nrb > 0) {
       // Row 128*wm + 32*rb + c32 of the stage; its swizzle (row >> 1) & 7 = (c32 >> 1) & 7
       // does not depend on rb, so a step's four reads share one address plus offsets.
       const f16x8* arow = sm.a[c % NS] + (128 * wm + c32) * 8;
-      f16x8 aop[4];
+      f16x8 aop[4], bop[2];
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) aop[rb] = arow[rb * 256 + aswz[0]];
+      // Weights of 16-row step (4*h2 + s) of the group: dword (2*h2 + s/2) of vector s%2.
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) bop[cb] = dequant8(bw[cb][0][2 * h2], zo[cb], mr);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        f16x8 anext[4];
+        f16x8 anext[4], bnext[2];
         if (s < 3) {
 #pragma unroll
           for (int rb = 0; rb < 4; ++rb) anext[rb] = arow[rb * 256 + aswz[s + 1]];
-        }
-        // Weights of 16-row step (4*h2 + s) of the group: dword (2*h2 + s/2) of vector s%2.
-        f16x8 bop[2];
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-          bop[cb] = dequant8(bw[cb][s & 1][2 * h2 + (s >> 1)], zo[cb], mr);
+          for (int cb = 0; cb < 2; ++cb)
+            bnext[cb] = dequant8(bw[cb][(s + 1) & 1][2 * h2 + ((s + 1) >> 1)], zo[cb], mr);
+        } else if (h2 == 1) {
+          read_b(g + 1);  // the current weights are dead after step 2's dequant
+        }
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma32x32x16(aop[rb], bop[cb], acc[rb][cb]);
+        if (s == 3 && h2 == 1) {
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) acc[rb][cb][r] *= ratio[cb];
+        }
+        // Schedule: LDS reads of the next step first, dequant between the MFMAs; in the
+        // rescaling step each block's products follow its MFMA by one MFMA.
+        if (s < 3) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedVALU, 3, 0);
+          }
+#pragma unroll
+          for (int i = 4; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedVALU, 2, 0);
+          }
+        } else if (h2 == 1) {
+          __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+#pragma unroll
+          for (int i = 2; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedVALU, 16, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(kSchedVALU, 32, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         if (s < 3) {
 #pragma unroll
           for (int rb = 0; rb < 4; ++rb) aop[rb] = anext[rb];
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) bop[cb] = bnext[cb];
         }
+      }
+    }
+    if (h2 == 1) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        sigma[cb] = snext[cb];
+        zo[cb] = znext[cb];
       }
     }
   };
@@ -425,11 +541,15 @@ hipError_t launch_grouped_tile(const GroupedProblem& g, hipStream_t stream) {
   p.n_active = g.n_active;
   p.n_pairs = g.n_pairs;
   p.n_tokens = g.n_tokens;
-  // Upper bound on tiles (every segment adds at most one partial row tile), rounded up to
-  // a multiple of the XCD count; work-groups without a tile exit at once.
-  long tiles = ((long)(g.n_pairs + TM - 1) / TM + g.n_active) * (g.n / TN);
-  tiles = (tiles + kXcds - 1) / kXcds * kXcds;
+  // Per XCD: an upper bound on its share of big tiles (at most n_pairs / 256 full row tiles
+  // plus one partial tile per segment) and of small tiles (one per segment); the kernel
+  // derives the exact shares from the CSR, and work-groups without a tile exit at once.
+  const long ntn = g.n / TN;
+  const long big = ((long)g.n_pairs / TM + g.n_active) * ntn;
+  const long small = (long)g.n_active * ntn;
+  const long tiles = kXcds * ((big + kXcds - 1) / kXcds + (small + kXcds - 1) / kXcds);
   if (tiles <= 0) return hipSuccess;
+  if (tiles > 0x7fffffffL) return hipErrorInvalidConfiguration;
   p.tiles = (int)tiles;
   if (g.z_bank != nullptr)
     hipLaunchKernelGGL((gemm_tile_kernel<true, true>), dim3((unsigned)tiles), dim3(kThreads), 0,

@@ -143,6 +143,66 @@ __global__ __launch_bounds__(256) void gather_columns_kernel(const uint16_t* __r
   }
 }
 
+// Row-staged gather for K up to 8 * 256 * G: a work-group copies whole activation rows into
+// LDS with coalesced 16-byte loads (the next row's loads issued before the current row is
+// gathered), then each thread assembles its G output granules of 8 columns from LDS through
+// the permutation, which it holds in registers for all its rows.  Reading permuted columns
+// straight from global memory instead touches a different cache line per lane and load.
+template <int G>
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ a,
+                                                          int lda,
+                                                          const int32_t* __restrict__ perm,
+                                                          uint16_t* __restrict__ out, int m,
+                                                          int k) {
+  extern __shared__ u32x4 row_lds[];  // one row, k / 8 granules
+  const uint16_t* row16 = reinterpret_cast<const uint16_t*>(row_lds);
+  const int t = threadIdx.x;
+  const int granules = k / 8;
+  int src[G][8];  // permuted source column of each output column (clamped into the row)
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const int g = t + 256 * j;
+    const int gg = g < granules ? g : granules - 1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = perm[8 * gg + e];
+      src[j][e] = c < 0 ? 0 : (c >= k ? k - 1 : c);
+    }
+  }
+  int r = blockIdx.x;
+  u32x4 next[G];
+  auto load_row = [&](int rr) {
+    const u32x4* rp = reinterpret_cast<const u32x4*>(a + (long)rr * lda);
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int g = t + 256 * j;
+      next[j] = rp[g < granules ? g : granules - 1];
+    }
+  };
+  if (r < m) load_row(r);
+  for (; r < m; r += gridDim.x) {
+    __syncthreads();  // the previous row's gather is done with the buffer
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int g = t + 256 * j;
+      if (g < granules) row_lds[g] = next[j];
+    }
+    __syncthreads();
+    const int rn = r + (int)gridDim.x;
+    if (rn < m) load_row(rn);
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int g = t + 256 * j;
+      if (g >= granules) break;
+      u32x4 packed;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        packed[e] = (uint32_t)row16[src[j][2 * e]] | ((uint32_t)row16[src[j][2 * e + 1]] << 16);
+      *reinterpret_cast<u32x4*>(out + (long)r * k + 8 * g) = packed;
+    }
+  }
+}
+
 int grid_for(long work) {
   long blocks = (work + 255) / 256;
   if (blocks > 65536) blocks = 65536;
@@ -179,8 +239,23 @@ hipError_t launch_dequant(const uint32_t* b, const uint16_t* s, const uint32_t* 
   return hipGetLastError();
 }
 
+template <int G>
+hipError_t launch_gather_rows(const uint16_t* a, int lda, const int32_t* perm, uint16_t* out,
+                              int m, int k, hipStream_t stream) {
+  // Up to 1024 work-groups (four per CU); larger m loops, amortizing the permutation loads.
+  const int blocks = m < 1024 ? m : 1024;
+  hipLaunchKernelGGL((gather_rows_kernel<G>), dim3(blocks), dim3(256), (size_t)k * 2, stream, a,
+                     lda, perm, out, m, k);
+  return hipGetLastError();
+}
+
 hipError_t launch_gather_columns(const uint16_t* a, int lda, const int32_t* perm, uint16_t* out,
                                  int m, int k, hipStream_t stream) {
+  const int granules = k / 8;
+  if (granules <= 256) return launch_gather_rows<1>(a, lda, perm, out, m, k, stream);
+  if (granules <= 512) return launch_gather_rows<2>(a, lda, perm, out, m, k, stream);
+  if (granules <= 1024) return launch_gather_rows<4>(a, lda, perm, out, m, k, stream);
+  if (granules <= 2048) return launch_gather_rows<8>(a, lda, perm, out, m, k, stream);
   hipLaunchKernelGGL(gather_columns_kernel, dim3(grid_for((long)m * (k / 8))), dim3(256), 0,
                      stream, a, lda, perm, out, m, k);
   return hipGetLastError();

@@ -365,9 +365,12 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
   read_b(0);
 
   // One iteration per group: its even chunk and its odd chunk, so that the chunk parity,
-  // and with it the weight dwords each step reads, is static.
-  auto chunk = [&](auto h2c, int c) {
+  // and with it the weight dwords each step reads, is static.  NRB is the number of the
+  // wave's 32-row blocks that hold valid rows (rounded up to 1, 2 or 4; 0 for none): the
+  // loads and barriers are the same for every NRB, only the arithmetic shrinks.
+  auto chunk = [&](auto h2c, auto nrbc, int c) {
     constexpr int h2 = decltype(h2c)::value;
+    constexpr int NRB = decltype(nrbc)::value;
     const int g = c >> 1;
     wait_vmcnt<h2 == 0 ? kWaitEven : kWaitOdd>();
     __builtin_amdgcn_s_barrier();
@@ -391,25 +394,23 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
         ratio[cb] = g + 1 < groups ? sigma[cb] * __builtin_amdgcn_rcpf(snext[cb]) : 1.f;
     }
 
-    // Waves whose rows are all past the end skip the arithmetic (but keep loading and
-    // meeting the barrier).
-    if (nrb > 0) {
+    if constexpr (NRB > 0) {
       // Row 128*wm + 32*rb + c32 of the stage; its swizzle (row >> 1) & 7 = (c32 >> 1) & 7
-      // does not depend on rb, so a step's four reads share one address plus offsets.
+      // does not depend on rb, so a step's reads share one address plus offsets.
       const f16x8* arow = sm.a[c % NS] + (128 * wm + c32) * 8;
-      f16x8 aop[4], bop[2];
+      f16x8 aop[NRB], bop[2];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) aop[rb] = arow[rb * 256 + aswz[0]];
+      for (int rb = 0; rb < NRB; ++rb) aop[rb] = arow[rb * 256 + aswz[0]];
       // Weights of 16-row step (4*h2 + s) of the group: dword (2*h2 + s/2) of vector s%2.
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) bop[cb] = dequant8(bw[cb][0][2 * h2], zo[cb], mr);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        f16x8 anext[4], bnext[2];
+        f16x8 anext[NRB], bnext[2];
         if (s < 3) {
 #pragma unroll
-          for (int rb = 0; rb < 4; ++rb) anext[rb] = arow[rb * 256 + aswz[s + 1]];
+          for (int rb = 0; rb < NRB; ++rb) anext[rb] = arow[rb * 256 + aswz[s + 1]];
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb)
             bnext[cb] = dequant8(bw[cb][(s + 1) & 1][2 * h2 + ((s + 1) >> 1)], zo[cb], mr);
@@ -417,30 +418,27 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
           read_b(g + 1);  // the current weights are dead after step 2's dequant
         }
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
+        for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma32x32x16(aop[rb], bop[cb], acc[rb][cb]);
         if (s == 3 && h2 == 1) {
 #pragma unroll
-          for (int rb = 0; rb < 4; ++rb)
+          for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
               for (int r = 0; r < 16; ++r) acc[rb][cb][r] *= ratio[cb];
         }
         // Schedule: LDS reads of the next step first, dequant between the MFMAs; in the
-        // rescaling step each block's products follow its MFMA by one MFMA.
+        // rescaling step the products of the blocks follow the MFMAs.
+        constexpr int nm = 2 * NRB;  // MFMAs per step
         if (s < 3) {
+          constexpr int per = (20 + nm - 1) / nm;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+          for (int i = 0; i < nm; ++i) {
+            if (i < NRB) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedVALU, 3, 0);
-          }
-#pragma unroll
-          for (int i = 4; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedVALU, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedVALU, per, 0);
           }
         } else if (h2 == 1) {
           __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
@@ -448,7 +446,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
           __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
           __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
 #pragma unroll
-          for (int i = 2; i < 8; ++i) {
+          for (int i = 2; i < nm; ++i) {
             __builtin_amdgcn_sched_group_barrier(kSchedVALU, 16, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
           }
@@ -457,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
         __builtin_amdgcn_sched_barrier(0);
         if (s < 3) {
 #pragma unroll
-          for (int rb = 0; rb < 4; ++rb) aop[rb] = anext[rb];
+          for (int rb = 0; rb < NRB; ++rb) aop[rb] = anext[rb];
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb) bop[cb] = bnext[cb];
         }
@@ -471,10 +469,20 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
       }
     }
   };
-  for (int g = 0; g < groups; ++g) {
-    chunk(std::integral_constant<int, 0>{}, 2 * g);
-    chunk(std::integral_constant<int, 1>{}, 2 * g + 1);
-  }
+  auto run = [&](auto nrbc) {
+    for (int g = 0; g < groups; ++g) {
+      chunk(std::integral_constant<int, 0>{}, nrbc, 2 * g);
+      chunk(std::integral_constant<int, 1>{}, nrbc, 2 * g + 1);
+    }
+  };
+  if (nrb >= 3)
+    run(std::integral_constant<int, 4>{});
+  else if (nrb == 2)
+    run(std::integral_constant<int, 2>{});
+  else if (nrb == 1)
+    run(std::integral_constant<int, 1>{});
+  else
+    run(std::integral_constant<int, 0>{});
   wait_vmcnt<0>();  // the trailing re-reads have landed before the work-group ends
 
   // Epilogue: lane holds rows 8*(r/4) + 4*h + (r%4) of column c32 in each 32x32 block.

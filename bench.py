@@ -87,7 +87,22 @@ def bench_dense(torch, torch_ops, name, copies, steps, warmup):
     sec = timed_loop(torch, step, steps, warmup)
     m, k, n = case["m"], case["k"], case["n"]
     return dict(case=case, sec=sec, weight_bytes=k * n // 2, alg_bytes=algorithmic_bytes(case),
-                flops=2.0 * m * n * k)
+                flops=2.0 * m * n * k, weights=weights)
+
+
+def bench_stream_read(torch, weights, steps, warmup):
+    """Practical HBM read ceiling: the library's plain streaming read (wq_stream_read)
+    over the same rotating packed-weight buffers the GEMM reads, timed the same way."""
+    import weight_only_quantized_gemm_amd as wq
+    nbytes = weights[0].b.numel() * 4
+    words = wq.wq_stream_read_sink_words(nbytes)
+    sink = torch.zeros(words, dtype=torch.int32, device="cuda")
+
+    def step(i):
+        wq.wq_stream_read(weights[i % len(weights)].b, nbytes, sink, words)
+
+    sec = timed_loop(torch, step, steps, warmup)
+    return dict(sec=sec, bytes=nbytes)
 
 
 def bench_moe(torch, torch_ops, steps, warmup):
@@ -187,7 +202,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "batched", "prefill", "moe", "tiny", "copy"],
+    ap.add_argument("--only", choices=["decode", "batched", "prefill", "moe", "tiny", "copy",
+                                       "ceiling"],
                     default=None, help="time one workload (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -207,6 +223,11 @@ def main() -> int:
             print(json.dumps({"only": "copy", "bytes_read": r["bytes"], "bytes_written": r["bytes"],
                               "us": r["sec"] * 1e6,
                               "TBs_read_plus_write": 2 * r["bytes"] / r["sec"] / 1e12}), flush=True)
+        elif args.only == "ceiling":
+            r = bench_dense(torch, torch_ops, "decode", 12, 1, 1)
+            c = bench_stream_read(torch, r["weights"], args.steps, args.warmup)
+            print(json.dumps({"only": "ceiling", "bytes": c["bytes"], "us": c["sec"] * 1e6,
+                              "TBs": c["bytes"] / c["sec"] / 1e12}), flush=True)
         elif args.only == "moe":
             r = bench_moe(torch, torch_ops, args.steps, args.warmup)
             print(json.dumps({"only": "moe", "us": r["sec"] * 1e6,
@@ -221,10 +242,16 @@ def main() -> int:
 
     dec = bench_dense(torch, torch_ops, "decode", 12, args.steps, args.warmup)
     print(f"decode: {dec['sec'] * 1e6:.2f} us/call", file=sys.stderr, flush=True)
+    ceil = bench_stream_read(torch, dec.pop("weights"), args.steps, args.warmup)
+    ceil_tbs = ceil["bytes"] / ceil["sec"] / 1e12
+    print(f"streaming read of the same bytes: {ceil['sec'] * 1e6:.2f} us ({ceil_tbs:.3f} TB/s)",
+          file=sys.stderr, flush=True)
     bat = bench_dense(torch, torch_ops, "batched", 40, args.steps, args.warmup)
+    bat.pop("weights")
     print(f"batched: {bat['sec'] * 1e6:.2f} us/call", file=sys.stderr, flush=True)
     pre_steps = max(10, args.steps // 4)
     pre = bench_dense(torch, torch_ops, "prefill", 1, pre_steps, max(3, args.warmup // 4))
+    pre.pop("weights")
     print(f"prefill: {pre['sec'] * 1e6:.1f} us/call", file=sys.stderr, flush=True)
     moe = bench_moe(torch, torch_ops, pre_steps, max(3, args.warmup // 4))
     print(f"moe: {moe['sec'] * 1e6:.1f} us/call", file=sys.stderr, flush=True)
@@ -251,6 +278,12 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic()},
+        "hbm_read_ceiling": {"kernel": "wq_stream_read (plain 16-byte non-temporal streaming "
+                                       "read of the same 12 rotating weight buffers)",
+                             "bytes": ceil["bytes"], "us": round(ceil["sec"] * 1e6, 3),
+                             "TBs": round(ceil_tbs, 4),
+                             "frac_of_peak": round(ceil_tbs * 1e3 / HBM_PEAK_GBS, 4),
+                             "decode_frac_of_ceiling": round(tbs / ceil_tbs, 4)},
         "prefill": {"workload": "M=2048 K=4096 N=14336 u4b8 group128 act_order (gather + GEMM)",
                     "tflops": round(pre_tflops, 2), "us": round(pre["sec"] * 1e6, 2),
                     "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2),

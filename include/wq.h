@@ -205,6 +205,19 @@ int wq_grouped_workspace_bytes(int n_pairs, int n_active, int n, int k, uint32_t
  */
 int wq_grouped_gemm(const wq_grouped_args* args);
 
+/*
+ * Measurement helper, not a step of the method: reads the `bytes` bytes at device address
+ * `src` (16-byte aligned, bytes a positive multiple of 16) once, with the 16-byte
+ * non-temporal loads the small-M GEMM streams its weights with, as the practical HBM read
+ * ceiling to report that GEMM against.  `sink` is device memory of at least
+ * wq_stream_read_sink_words(bytes) uint32 words; a word is written only when the data
+ * XOR of a wave's reads equals a fixed constant (its content is meaningless).  Enqueues on
+ * `stream`; fails with WQ_ERR_NULL / WQ_ERR_ALIGN / WQ_ERR_SHAPE / WQ_ERR_WORKSPACE.
+ */
+int wq_stream_read_sink_words(size_t bytes, size_t* words_out);
+int wq_stream_read(const void* src, size_t bytes, void* sink, size_t sink_words,
+                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

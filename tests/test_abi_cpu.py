@@ -140,6 +140,24 @@ def test_repack_and_dequant_validation(L):
                         None) == status(STAGE_ARGS, wq.WQ_ERR_FLAGS)
 
 
+def test_stream_read_sizing_and_validation(L):
+    # one wave reads 64 lanes x 8 granules of 16 B; four waves per work-group
+    assert wq.wq_stream_read_sink_words(29360128) == 3584
+    assert wq.wq_stream_read_sink_words(16) == 4
+    assert wq.wq_stream_read_sink_words(8192 * 5) == 8
+    with pytest.raises(wq.WQError):
+        wq.wq_stream_read_sink_words(100)
+    with pytest.raises(wq.WQError):
+        wq.wq_stream_read_sink_words(0)
+    assert L.wq_stream_read(None, 1024, 0x2000, 4, None) == status(STAGE_ARGS, wq.WQ_ERR_NULL)
+    assert L.wq_stream_read(0x1008, 1024, 0x2000, 4, None) == status(STAGE_ARGS,
+                                                                      wq.WQ_ERR_ALIGN)
+    assert L.wq_stream_read(0x1000, 1024, 0x2000, 3, None) == status(STAGE_ARGS,
+                                                                      wq.WQ_ERR_WORKSPACE)
+    assert L.wq_stream_read(0x1000, 1000, 0x2000, 4, None) == status(STAGE_SHAPE,
+                                                                      wq.WQ_ERR_SHAPE)
+
+
 def test_act_order_perm_matches_oracle_and_rejects_uneven_groups():
     for seed in (1, 2, 3):
         g_idx = synthetic.act_order_g_idx(seed, 4096, 128)

@@ -336,3 +336,29 @@ def test_graph_replays_match_eager(dev, m, fp32):
         assert np.array_equal(host(out).view(np.uint16), eager.view(np.uint16)), rep
         torch_ops.gemm(a, w, fp32_reduce=fp32, buffers=bufs)   # eager work in between
         torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------------------- measurement helper
+
+def test_stream_read_reads_every_granule_once(dev):
+    """The streaming-read helper's data-dependent store fires exactly for the wave whose
+    lane read a planted word equal to its trigger value, so each planted position shows
+    that its granule was read, by the wave that owns it."""
+    magic = 0x9E3779B9
+    nbytes = (1 << 20) + 16 * 37  # a ragged last wave
+    granules = nbytes // 16
+    for pos in (0, 511, 512, 12345, granules - 37, granules - 1):
+        buf = torch.zeros(nbytes // 4, dtype=torch.int32, device=dev)
+        buf[4 * pos + (pos % 4)] = magic - (1 << 32)  # the same 32 bits as int32
+        words = wq.wq_stream_read_sink_words(nbytes)
+        sink = torch.zeros(words, dtype=torch.int32, device=dev)
+        wq.wq_stream_read(buf, nbytes, sink, words)
+        torch.cuda.synchronize()
+        got = host(sink).view(np.uint32)
+        owner = pos // 512
+        if pos == granules - 1:
+            # lanes past the end re-read the last granule: an even number of extra reads
+            # cancels in the XOR unless exactly one lane reads it
+            continue
+        assert got[owner] == magic, (pos, owner, got[max(owner - 1, 0):owner + 2])
+        assert np.count_nonzero(got) == 1, pos

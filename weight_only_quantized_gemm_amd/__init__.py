@@ -32,6 +32,7 @@ EXPORTED = (
     "wq_abi_version", "wq_status_str", "wq_repack_b", "wq_repack_scales", "wq_repack_zeros",
     "wq_act_order_perm", "wq_gemm_workspace_bytes", "wq_gemm", "wq_dequant",
     "wq_csr_from_routes", "wq_grouped_workspace_bytes", "wq_grouped_gemm",
+    "wq_stream_read_sink_words", "wq_stream_read",
 )
 
 
@@ -103,6 +104,8 @@ def lib() -> ctypes.CDLL:
             "wq_grouped_workspace_bytes": (ctypes.c_int, [i32, i32, i32, i32, u32,
                                                           ctypes.POINTER(sz)]),
             "wq_grouped_gemm": (ctypes.c_int, [ctypes.POINTER(wq_grouped_args)]),
+            "wq_stream_read_sink_words": (ctypes.c_int, [sz, ctypes.POINTER(sz)]),
+            "wq_stream_read": (ctypes.c_int, [vp, sz, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -241,3 +244,15 @@ def wq_grouped_gemm(a, b_bank, b_stride_bytes: int, s_bank, s_stride_bytes: int,
         n_active=n_active, n_pairs=n_pairs, n_tokens=n_tokens, k=k, n=n,
         group_size=group_size, flags=flags, reserved=0)
     _check(lib().wq_grouped_gemm(ctypes.byref(args)))
+
+
+def wq_stream_read_sink_words(nbytes: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().wq_stream_read_sink_words(nbytes, ctypes.byref(out)))
+    return out.value
+
+
+def wq_stream_read(src, nbytes: int, sink, sink_words: int, stream=None) -> None:
+    """Measurement helper: one streaming read of `nbytes` at `src` (see include/wq.h)."""
+    _check(lib().wq_stream_read(_ptr(src), nbytes, _ptr(sink), sink_words,
+                                _stream(stream, src)))

@@ -11,7 +11,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libwq.so")
-SOURCES = ["wq_api.hip", "wq_repack.hip", "wq_gemm_small.hip", "wq_gemm_tile.hip"]
+SOURCES = ["wq_api.hip", "wq_repack.hip", "wq_gemm_small.hip", "wq_gemm_tile.hip",
+           "wq_measure.hip"]
 
 
 def hipcc() -> str:

@@ -385,4 +385,26 @@ int wq_grouped_gemm(const wq_grouped_args* args) {
   return e == hipSuccess ? 0 : hip_fail(e);
 }
 
+int wq_stream_read_sink_words(size_t bytes, size_t* words_out) {
+  if (words_out == nullptr) return fail(WQ_STAGE_ARGS, WQ_ERR_NULL);
+  if (bytes == 0 || bytes % 16 != 0 || bytes / 16 > (size_t)1 << 40)
+    return fail(WQ_STAGE_SHAPE, WQ_ERR_SHAPE);
+  *words_out = (size_t)wq::stream_read_sink_words(bytes);
+  return 0;
+}
+
+int wq_stream_read(const void* src, size_t bytes, void* sink, size_t sink_words,
+                   void* stream) {
+  size_t need = 0;
+  const int st = wq_stream_read_sink_words(bytes, &need);
+  if (st != 0) return st;
+  if (src == nullptr || sink == nullptr) return fail(WQ_STAGE_ARGS, WQ_ERR_NULL);
+  if (!aligned(src, 16) || !aligned(sink, 4)) return fail(WQ_STAGE_ARGS, WQ_ERR_ALIGN);
+  if (sink_words < need) return fail(WQ_STAGE_ARGS, WQ_ERR_WORKSPACE);
+  if (need / 4 > 0x7fffffffu) return fail(WQ_STAGE_SHAPE, WQ_ERR_OVERFLOW);
+  const hipError_t e =
+      wq::launch_stream_read(src, bytes, static_cast<uint32_t*>(sink), as_stream(stream));
+  return e == hipSuccess ? 0 : hip_fail(e);
+}
+
 }  // extern "C"

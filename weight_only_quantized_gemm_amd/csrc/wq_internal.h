@@ -56,4 +56,9 @@ struct GroupedProblem {
 };
 hipError_t launch_grouped_tile(const GroupedProblem& p, hipStream_t stream);
 
+// Streaming-read measurement helper (wq_measure.hip).
+long stream_read_sink_words(size_t bytes);
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink,
+                              hipStream_t stream);
+
 }  // namespace wq

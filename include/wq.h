@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define WQ_ABI_VERSION 1u
+#define WQ_ABI_VERSION 2u
 
 /* Flag bits: the bit positions of the vllm_marlin.rs launch flags. */
 #define WQ_FLAG_ACT_ORDER   (1u << 1) /* gather A by perm before the product              */
@@ -50,6 +50,9 @@ extern "C" {
 #define WQ_FLAG_HAS_ZP      (1u << 3) /* u4 with per-group zero points (else u4b8)         */
 #define WQ_FLAG_ATOMIC_ADD  (1u << 4) /* not supported: rejected (non-deterministic sums)  */
 #define WQ_FLAG_FP32_REDUCE (1u << 5) /* allow split-K with an fp32 workspace reduce        */
+/* Grouped call only: scale each output row by its pair's fp32 routing weight (vllm_marlin.rs
+ * MoE launch, `mul_topk_weights` with `topk_weights`). */
+#define WQ_FLAG_MUL_TOPK_WEIGHTS (1u << 6)
 
 enum wq_stage {
   WQ_STAGE_ARGS = 1,
@@ -181,13 +184,16 @@ typedef struct wq_grouped_args {
   const int32_t* ex_off;    /* device [n_active + 1] segment starts into ex_pairs        */
   const int32_t* ex_pairs;  /* device [n_pairs] pair ids grouped by expert               */
   const int32_t* pair_tok;  /* device [n_pairs] activation row of each pair              */
+  const float* topk_weights; /* device fp32 [n_pairs], pair-major routing weights, with
+                                WQ_FLAG_MUL_TOPK_WEIGHTS; else NULL                      */
   void* y;                  /* device fp16 [n_pairs][n], pair-major output               */
   void* workspace;          /* reserved for the grouped schedule; may be NULL            */
   size_t workspace_bytes;
   void* stream;
   int32_t n_expert, n_active, n_pairs, n_tokens;
   int32_t k, n, group_size;
-  uint32_t flags;           /* WQ_FLAG_HAS_ZP iff zp_bank != NULL                         */
+  uint32_t flags;           /* WQ_FLAG_HAS_ZP iff zp_bank != NULL; WQ_FLAG_MUL_TOPK_WEIGHTS
+                               iff topk_weights != NULL                                   */
   int32_t reserved;
 } wq_grouped_args;
 
@@ -199,9 +205,12 @@ int wq_grouped_workspace_bytes(int n_pairs, int n_active, int n, int k, uint32_t
  * Grouped W4A16 product over an expert-major CSR (mmq_ffi.rs grouped projection call):
  * for active segment i with expert e = ex_ids[i] (i when ex_ids is NULL) and each pair p
  * in ex_pairs[ex_off[i] .. ex_off[i+1]), y[p][:] = A[pair_tok[p]][:] @ dequant(B_e).
- * No top-k weight multiply.  The device CSR is not re-validated (that would need a
- * host sync): build it with wq_csr_from_routes; entries out of range are skipped by the
- * kernel (never read or written out of bounds), leaving those output rows unwritten.
+ * With WQ_FLAG_MUL_TOPK_WEIGHTS the row is also multiplied by topk_weights[p], on the fp32
+ * result before its one rounding to fp16 (the vllm_marlin.rs MoE launch's
+ * `mul_topk_weights` with its fp32 `topk_weights`, one per routed pair).  The device CSR is
+ * not re-validated (that would need a host sync): build it with wq_csr_from_routes;
+ * entries out of range are skipped by the kernel (never read or written out of bounds),
+ * leaving those output rows unwritten.
  */
 int wq_grouped_gemm(const wq_grouped_args* args);
 

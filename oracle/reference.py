@@ -247,13 +247,17 @@ def validate_csr(csr: dict) -> None:
 
 
 def grouped_w4a16_gemm(a, experts, csr, *, group_size=128, columns=None,
-                       pairs=None) -> np.ndarray:
+                       pairs=None, topk_weights=None) -> np.ndarray:
     """Pair-major reference y[p] = A[pair_tok[p]] @ dequant(B_e) for the expert e owning p.
 
     Walks the expert-major CSR: segment i covers positions ex_off[i]..ex_off[i+1] of
-    ex_pairs and uses expert ex_ids[i]; no top-k weight multiply (mmq_ffi.rs grouped
-    projection contract).  `experts[e]` holds that expert's qweight, scales and optional
-    zeros.  `pairs` restricts the rows computed (others stay NaN).
+    ex_pairs and uses expert ex_ids[i] (mmq_ffi.rs grouped projection contract).
+    `experts[e]` holds that expert's qweight, scales and optional zeros.  `pairs` restricts
+    the rows computed (others stay NaN).
+
+    With `topk_weights` (one fp32 routing weight per pair, pair-major: the vllm_marlin.rs
+    MoE launch's `topk_weights` under `mul_topk_weights`), row p is multiplied by
+    topk_weights[p], in fp64.
     """
     a = np.asarray(a)
     n_pairs = len(csr["ex_pairs"])
@@ -271,6 +275,9 @@ def grouped_w4a16_gemm(a, experts, csr, *, group_size=128, columns=None,
                           group_size=group_size, columns=columns)
         toks = [csr["pair_tok"][p] for p in rows]
         y[rows, :] = matmul_fp64(a[toks, :], w)
+        if topk_weights is not None:
+            scale = np.asarray(topk_weights, dtype=np.float32)[rows].astype(np.float64)
+            y[rows, :] *= scale[:, None]
     return y
 
 

@@ -136,6 +136,13 @@ def act_order_g_idx(seed: int, k: int, group_size: int) -> np.ndarray:
     return (permutation(seed, k) // group_size).astype(np.int32)
 
 
+def routing_weights(seed: int, n_tokens: int, top_k: int) -> np.ndarray:
+    """Routing weights, pair-major fp32 [n_tokens * top_k]: per token, top_k draws from
+    U[0.05, 1) divided by their sum (a renormalised top-k selection)."""
+    u = 0.05 + 0.95 * uniform01(seed, n_tokens * top_k).reshape(n_tokens, top_k)
+    return (u / u.sum(axis=1, keepdims=True)).astype(np.float32).reshape(-1)
+
+
 def top2_routes(seed: int, n_tokens: int, n_expert: int) -> np.ndarray:
     """Two distinct experts per token, uniform without replacement, in draw order.
 

@@ -49,7 +49,7 @@ def test_library_exports_every_declared_function(L):
 
 
 def test_abi_version(L):
-    assert wq.wq_abi_version() == wq.WQ_ABI_VERSION == 1
+    assert wq.wq_abi_version() == wq.WQ_ABI_VERSION == 2
 
 
 def test_status_strings_decode_stage_and_code(L):
@@ -61,7 +61,8 @@ def test_status_strings_decode_stage_and_code(L):
 
 
 def gemm_args(**over):
-    base = dict(abi_version=1, struct_size=ctypes.sizeof(wq.wq_gemm_args), a=0x1000, b=0x2000,
+    base = dict(abi_version=wq.WQ_ABI_VERSION, struct_size=ctypes.sizeof(wq.wq_gemm_args),
+                a=0x1000, b=0x2000,
                 c=0x3000, b_scales=0x4000, zero_points=None, perm=None, a_tmp=None,
                 workspace=None, workspace_bytes=0, stream=None, m=16, n=256, k=1024, lda=1024,
                 group_size=128, flags=0, split_k=0, reserved=0)
@@ -100,7 +101,7 @@ def call_gemm(L, **over):
     (dict(flags=wq.WQ_FLAG_FP32_REDUCE, split_k=2), status(STAGE_ARGS, wq.WQ_ERR_WORKSPACE)),
     (dict(flags=wq.WQ_FLAG_FP32_REDUCE, split_k=2, workspace=0x7000, workspace_bytes=16),
      status(STAGE_ARGS, wq.WQ_ERR_WORKSPACE)),
-    (dict(abi_version=2), status(STAGE_ARGS, wq.WQ_ERR_ABI)),
+    (dict(abi_version=wq.WQ_ABI_VERSION + 1), status(STAGE_ARGS, wq.WQ_ERR_ABI)),
     (dict(struct_size=8), status(STAGE_ARGS, wq.WQ_ERR_ABI)),
     (dict(reserved=1), status(STAGE_ARGS, wq.WQ_ERR_ABI)),
 ])
@@ -200,7 +201,8 @@ def test_csr_builder_rejects_out_of_range_expert():
 
 
 def grouped_args(**over):
-    base = dict(abi_version=1, struct_size=ctypes.sizeof(wq.wq_grouped_args), a=0x1000,
+    base = dict(abi_version=wq.WQ_ABI_VERSION, struct_size=ctypes.sizeof(wq.wq_grouped_args),
+                a=0x1000,
                 b_bank=0x2000, b_stride_bytes=1024 * 256 // 2, s_bank=0x3000,
                 s_stride_bytes=8 * 256 * 2, zp_bank=None, zp_stride_bytes=0, ex_ids=None,
                 ex_off=0x4000, ex_pairs=0x5000, pair_tok=0x6000, y=0x7000, workspace=None,
@@ -222,8 +224,14 @@ def grouped_args(**over):
     (dict(s_stride_bytes=16), status(STAGE_ARGS, wq.WQ_ERR_SHAPE)),
     (dict(flags=wq.WQ_FLAG_HAS_ZP), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
     (dict(flags=wq.WQ_FLAG_ACT_ORDER), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
+    # routing weights: the flag and the pointer go together (marlin.rs MoE validation)
+    (dict(flags=wq.WQ_FLAG_MUL_TOPK_WEIGHTS), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
+    (dict(topk_weights=0x8000), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
+    (dict(topk_weights=0x8002, flags=wq.WQ_FLAG_MUL_TOPK_WEIGHTS),
+     status(STAGE_ARGS, wq.WQ_ERR_ALIGN)),
     (dict(k=1000), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
     (dict(struct_size=4), status(STAGE_ARGS, wq.WQ_ERR_ABI)),
+    (dict(abi_version=1), status(STAGE_ARGS, wq.WQ_ERR_ABI)),
 ])
 def test_grouped_rejects_bad_arguments_before_launch(L, over, expect):
     assert L.wq_grouped_gemm(ctypes.byref(grouped_args(**over))) == expect

@@ -249,7 +249,7 @@ def test_strided_activations(dev):
 
 # --------------------------------------------------------------------------- grouped (MoE)
 
-def run_grouped(moe, dev, zeros=None):
+def run_grouped(moe, dev, zeros=None, weights=None):
     experts = [dict(e) for e in moe["experts"]]
     if zeros is not None:
         for e, z in zip(experts, zeros):
@@ -257,24 +257,35 @@ def run_grouped(moe, dev, zeros=None):
     bank = torch_ops.ExpertBank(experts, device=dev)
     csr = wq.wq_csr_from_routes(moe["routes"], moe["n_tokens"], moe["top_k"], moe["n_expert"])
     a = torch_ops.to_device(moe["a"], dev)
-    y = torch_ops.grouped_gemm(a, bank, csr)
+    w = None if weights is None else torch_ops.to_device(weights, dev)
+    y = torch_ops.grouped_gemm(a, bank, csr, topk_weights=w)
     torch.cuda.synchronize()
     ocsr = ref.csr_from_token_routes(moe["n_expert"], moe["n_tokens"], moe["top_k"],
                                      moe["routes"])
     return host(y), experts, ocsr
 
 
-@pytest.mark.parametrize("tokens,experts,k,n,zp", [(40, 4, 256, 256, False),
-                                                   (300, 3, 512, 512, True),
-                                                   (700, 2, 256, 256, False)])
-def test_grouped_matches_oracle(dev, tokens, experts, k, n, zp):
-    label = f"grouped tokens={tokens} experts={experts} k={k} n={n} zp={zp}"
+@pytest.mark.parametrize("tokens,experts,k,n,zp,weighted", [(40, 4, 256, 256, False, False),
+                                                            (300, 3, 512, 512, True, False),
+                                                            (700, 2, 256, 256, False, False),
+                                                            (40, 4, 256, 256, False, True),
+                                                            (300, 3, 512, 512, True, True)])
+def test_grouped_matches_oracle(dev, tokens, experts, k, n, zp, weighted):
+    label = f"grouped tokens={tokens} experts={experts} k={k} n={n} zp={zp} weighted={weighted}"
     say(label)
     moe = synthetic.moe_case(tokens, experts, k, n, seed=200 + tokens)
     zeros = ([synthetic.zero_point_words(300 + e, k // 128, n) for e in range(experts)]
              if zp else None)
-    y, ex, ocsr = run_grouped(moe, dev, zeros)
-    assert_parity(y, ref.grouped_w4a16_gemm(moe["a"], ex, ocsr), label)
+    w = synthetic.routing_weights(400 + tokens, tokens, 2) if weighted else None
+    y, ex, ocsr = run_grouped(moe, dev, zeros, w)
+    assert_parity(y, ref.grouped_w4a16_gemm(moe["a"], ex, ocsr, topk_weights=w), label)
+
+
+def test_grouped_unit_weights_change_nothing(dev):
+    moe = synthetic.moe_case(90, 3, 256, 256, seed=23)
+    y0, _, _ = run_grouped(moe, dev)
+    y1, _, _ = run_grouped(moe, dev, weights=np.ones(180, np.float32))
+    assert np.array_equal(y0.view(np.uint16), y1.view(np.uint16))
 
 
 def test_grouped_skips_inactive_experts(dev):
@@ -298,12 +309,15 @@ def test_grouped_single_expert_equals_dense(dev):
     assert np.array_equal(y.view(np.uint16), dense.view(np.uint16))
 
 
-def test_moe_config_matches_oracle_on_sampled_columns(dev):
-    say("config moe: 1024 tokens top-2 of 8 experts, k=4096 n=14336, sampled columns")
+@pytest.mark.parametrize("weighted", [False, True])
+def test_moe_config_matches_oracle_on_sampled_columns(dev, weighted):
+    say(f"config moe: 1024 tokens top-2 of 8 experts, k=4096 n=14336, sampled columns, "
+        f"weighted={weighted}")
     moe = synthetic.moe_case()
-    y, ex, ocsr = run_grouped(moe, dev)
+    w = synthetic.routing_weights(77, moe["n_tokens"], 2) if weighted else None
+    y, ex, ocsr = run_grouped(moe, dev, weights=w)
     cols = sample_columns(moe["n"], 6, 128)
-    want = ref.grouped_w4a16_gemm(moe["a"], ex, ocsr, columns=cols)
+    want = ref.grouped_w4a16_gemm(moe["a"], ex, ocsr, columns=cols, topk_weights=w)
     assert_parity(y[:, cols], want, "moe")
     assert np.isfinite(y).all()
 

@@ -256,6 +256,29 @@ def test_grouped_product_equals_dense_rows():
         assert y[p].tolist() == dense[0].tolist()
 
 
+def test_routing_weights_scale_each_pair_row():
+    """Row p is the dense product of its token row and expert times topk_weights[p]: the
+    weights follow pair order, not CSR position or token; unit weights change nothing."""
+    k, n, tokens, experts = 256, 32, 6, 3
+    a = synthetic.activations(24, tokens, k)
+    ex = [dict(qweight=synthetic.qweight_words(25 + e, k, n),
+               scales=synthetic.scales(33 + e, 2, n)) for e in range(experts)]
+    routes = np.array([[0, 2], [1, 0], [2, 1], [2, 0], [1, 2], [0, 1]])
+    csr = ref.csr_from_token_routes(experts, tokens, 2, routes)
+    assert list(csr["ex_pairs"]) != list(range(2 * tokens))  # CSR order differs from pairs
+    w = np.array([0.5, 2.0, -1.25, 3.0, 0.0, 1.0, 0.75, -2.0, 1.5, 0.25, 4.0, -0.5],
+                 dtype=np.float32)
+    y = ref.grouped_w4a16_gemm(a, ex, csr, topk_weights=w)
+    for p in range(2 * tokens):
+        t, e = p // 2, int(routes.reshape(-1)[p])
+        dense = ref.w4a16_gemm(a[t:t + 1], ex[e]["qweight"], ex[e]["scales"])
+        assert y[p].tolist() == (float(w[p]) * dense[0]).tolist()
+    ones = ref.grouped_w4a16_gemm(a, ex, csr, topk_weights=np.ones(2 * tokens, np.float32))
+    assert ones.tolist() == ref.grouped_w4a16_gemm(a, ex, csr).tolist()
+    r = synthetic.routing_weights(5, 100, 2)
+    assert r.dtype == np.float32 and np.allclose(r.reshape(100, 2).sum(axis=1), 1.0, atol=1e-6)
+
+
 # --------------------------------------------------------------------------- checker
 
 def test_checker_accepts_exact_and_rejects_large_error_and_nan():

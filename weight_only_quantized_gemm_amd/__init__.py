@@ -16,12 +16,13 @@ import numpy as np
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libwq.so")
 
-WQ_ABI_VERSION = 1
+WQ_ABI_VERSION = 2
 WQ_FLAG_ACT_ORDER = 1 << 1
 WQ_FLAG_IS_K_FULL = 1 << 2
 WQ_FLAG_HAS_ZP = 1 << 3
 WQ_FLAG_ATOMIC_ADD = 1 << 4
 WQ_FLAG_FP32_REDUCE = 1 << 5
+WQ_FLAG_MUL_TOPK_WEIGHTS = 1 << 6
 
 WQ_STAGE_ARGS, WQ_STAGE_SHAPE, WQ_STAGE_DEVICE = 1, 2, 3
 WQ_STAGE_LAUNCH_CONFIG, WQ_STAGE_FUNC_ATTR, WQ_STAGE_LAUNCH = 4, 5, 6
@@ -67,7 +68,7 @@ class wq_grouped_args(ctypes.Structure):
         ("zp_bank", ctypes.c_void_p), ("zp_stride_bytes", ctypes.c_size_t),
         ("ex_ids", ctypes.c_void_p), ("ex_off", ctypes.c_void_p),
         ("ex_pairs", ctypes.c_void_p), ("pair_tok", ctypes.c_void_p),
-        ("y", ctypes.c_void_p),
+        ("topk_weights", ctypes.c_void_p), ("y", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
         ("n_expert", ctypes.c_int32), ("n_active", ctypes.c_int32),
@@ -232,14 +233,16 @@ def wq_grouped_workspace_bytes(n_pairs: int, n_active: int, n: int, k: int,
 def wq_grouped_gemm(a, b_bank, b_stride_bytes: int, s_bank, s_stride_bytes: int, ex_ids,
                     ex_off, ex_pairs, pair_tok, y, *, n_expert: int, n_active: int,
                     n_pairs: int, n_tokens: int, k: int, n: int, zp_bank=None,
-                    zp_stride_bytes: int = 0, flags: int = 0, workspace=None,
-                    workspace_bytes: int = 0, group_size: int = 128, stream=None) -> None:
+                    zp_stride_bytes: int = 0, topk_weights=None, flags: int = 0,
+                    workspace=None, workspace_bytes: int = 0, group_size: int = 128,
+                    stream=None) -> None:
     args = wq_grouped_args(
         abi_version=WQ_ABI_VERSION, struct_size=ctypes.sizeof(wq_grouped_args),
         a=_ptr(a), b_bank=_ptr(b_bank), b_stride_bytes=b_stride_bytes, s_bank=_ptr(s_bank),
         s_stride_bytes=s_stride_bytes, zp_bank=_ptr(zp_bank), zp_stride_bytes=zp_stride_bytes,
         ex_ids=_ptr(ex_ids), ex_off=_ptr(ex_off), ex_pairs=_ptr(ex_pairs),
-        pair_tok=_ptr(pair_tok), y=_ptr(y), workspace=_ptr(workspace),
+        pair_tok=_ptr(pair_tok), topk_weights=_ptr(topk_weights), y=_ptr(y),
+        workspace=_ptr(workspace),
         workspace_bytes=workspace_bytes, stream=_stream(stream, y), n_expert=n_expert,
         n_active=n_active, n_pairs=n_pairs, n_tokens=n_tokens, k=k, n=n,
         group_size=group_size, flags=flags, reserved=0)

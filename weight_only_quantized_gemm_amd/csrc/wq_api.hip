@@ -335,7 +335,7 @@ int wq_grouped_gemm(const wq_grouped_args* args) {
       args->reserved != 0)
     return fail(WQ_STAGE_ARGS, WQ_ERR_ABI);
   const wq_grouped_args& p = *args;
-  if (p.flags & ~(uint32_t)(WQ_FLAG_HAS_ZP | WQ_FLAG_IS_K_FULL))
+  if (p.flags & ~(uint32_t)(WQ_FLAG_HAS_ZP | WQ_FLAG_IS_K_FULL | WQ_FLAG_MUL_TOPK_WEIGHTS))
     return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
   int st = check_kn(p.k, p.n, p.group_size);
   if (st) return st;
@@ -351,6 +351,9 @@ int wq_grouped_gemm(const wq_grouped_args* args) {
   const bool has_zp = (p.flags & WQ_FLAG_HAS_ZP) != 0;
   if (has_zp != (p.zp_bank != nullptr)) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
   if (has_zp && (st = check_ptr(p.zp_bank, 16))) return st;
+  const bool mul_w = (p.flags & WQ_FLAG_MUL_TOPK_WEIGHTS) != 0;
+  if (mul_w != (p.topk_weights != nullptr)) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
+  if (mul_w && !aligned(p.topk_weights, 4)) return fail(WQ_STAGE_ARGS, WQ_ERR_ALIGN);
   const size_t groups = (size_t)(p.k / kGroupSize);
   const size_t b_bytes = (size_t)p.k * p.n / 2;
   const size_t s_bytes = groups * p.n * 2;
@@ -358,8 +361,10 @@ int wq_grouped_gemm(const wq_grouped_args* args) {
   if (p.b_stride_bytes < b_bytes || p.b_stride_bytes % 16 || p.s_stride_bytes < s_bytes ||
       p.s_stride_bytes % 16 || (has_zp && (p.zp_stride_bytes < z_bytes || p.zp_stride_bytes % 16)))
     return fail(WQ_STAGE_ARGS, WQ_ERR_SHAPE);
-  const long long tiles =
-      ((long long)(p.n_pairs + wq::kTileM - 1) / wq::kTileM + p.n_active) * (p.n / wq::kTileN);
+  // The launch's work-group count: per-XCD shares of at most n_pairs/256 + n_active row
+  // tiles and n_active tail tiles, each times n/256 column tiles.
+  const long long ntn = p.n / wq::kTileN;
+  const long long tiles = ((long long)p.n_pairs / wq::kTileM + 2LL * p.n_active) * ntn + 16;
   if (tiles > std::numeric_limits<int32_t>::max()) return fail(WQ_STAGE_SHAPE, WQ_ERR_OVERFLOW);
 
   wq::GroupedProblem g{};
@@ -374,6 +379,7 @@ int wq_grouped_gemm(const wq_grouped_args* args) {
   g.ex_off = p.ex_off;
   g.ex_pairs = p.ex_pairs;
   g.pair_tok = p.pair_tok;
+  g.topk_w = p.topk_weights;
   g.y = static_cast<uint16_t*>(p.y);
   g.n_expert = p.n_expert;
   g.n_active = p.n_active;

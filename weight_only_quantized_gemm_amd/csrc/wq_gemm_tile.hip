@@ -106,6 +106,7 @@ struct TileArgs {
   const int32_t* ex_off;
   const int32_t* ex_pairs;
   const int32_t* pair_tok;
+  const float* topk_w;  // may be null
   int n_expert, n_active, n_pairs, n_tokens;
 };
 
@@ -120,6 +121,7 @@ struct Smem {
   uint32_t sz[2][kWaves * 64];  // 2 x 2 KiB: waves 0-1 scales, wave 2 zero points, spare
   int row_a[TM];
   int row_c[TM];
+  float row_w[TM];  // grouped: routing weight of each output row (1 without the multiply)
   int info[5];
 };
 
@@ -214,6 +216,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
     // Row maps: CSR position -> (activation row, output row); rows without a valid pair
     // read activation row 0 (finite data, never stored) and are not written.
     int ra = 0, rc = -1;
+    float rw = 1.f;
     if (tid < valid_rows) {
       const int pair = p.ex_pairs[pos0 + tid];
       if (pair >= 0 && pair < p.n_pairs) {
@@ -221,12 +224,14 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
         if (tok >= 0 && tok < p.n_tokens) {
           ra = tok;
           rc = pair;
+          if (p.topk_w != nullptr) rw = p.topk_w[pair];
         }
       }
     }
     if (tid < TM) {
       sm.row_a[tid] = ra;
       sm.row_c[tid] = rc;
+      sm.row_w[tid] = rw;
     }
     bptr = reinterpret_cast<const uint32_t*>(p.b_bank + (size_t)e * p.b_stride);
     sptr = reinterpret_cast<const uint16_t*>(p.s_bank + (size_t)e * p.s_stride);
@@ -496,9 +501,11 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
       for (int r = 0; r < 16; ++r) {
         const int row = 128 * wm + 32 * rb + 8 * (r >> 2) + 4 * hh + (r & 3);
         const int orow = sm.row_c[row];
+        // The routing weight (1 without the multiply) joins the scale, so that the output
+        // is one rounding of acc * factor, as on the dense path.
+        const float factor = GROUPED ? sigma[cb] * sm.row_w[row] : sigma[cb];
         if (orow >= 0)
-          p.c[(long)orow * p.n + col] =
-              __builtin_bit_cast(uint16_t, (f16)(acc[rb][cb][r] * sigma[cb]));
+          p.c[(long)orow * p.n + col] = __builtin_bit_cast(uint16_t, (f16)(acc[rb][cb][r] * factor));
       }
     }
   }
@@ -545,6 +552,7 @@ hipError_t launch_grouped_tile(const GroupedProblem& g, hipStream_t stream) {
   p.ex_off = g.ex_off;
   p.ex_pairs = g.ex_pairs;
   p.pair_tok = g.pair_tok;
+  p.topk_w = g.topk_w;
   p.n_expert = g.n_expert;
   p.n_active = g.n_active;
   p.n_pairs = g.n_pairs;

@@ -51,6 +51,7 @@ struct GroupedProblem {
   const int32_t* ex_off;
   const int32_t* ex_pairs;
   const int32_t* pair_tok;
+  const float* topk_w;    // may be null: no routing-weight multiply
   uint16_t* y;
   int n_expert, n_active, n_pairs, n_tokens, k, n;
 };

@@ -9,7 +9,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (WQ_FLAG_ACT_ORDER, WQ_FLAG_FP32_REDUCE, WQ_FLAG_HAS_ZP, wq_act_order_perm,
+from . import (WQ_FLAG_ACT_ORDER, WQ_FLAG_FP32_REDUCE, WQ_FLAG_HAS_ZP, WQ_FLAG_MUL_TOPK_WEIGHTS,
+               wq_act_order_perm,
                wq_gemm, wq_gemm_workspace_bytes, wq_grouped_gemm, wq_repack_b,
                wq_repack_scales, wq_repack_zeros)
 
@@ -116,8 +117,10 @@ class ExpertBank:
 
 
 def grouped_gemm(a: torch.Tensor, bank: ExpertBank, csr: dict, out: torch.Tensor | None = None,
-                 device_csr: dict | None = None, stream=None) -> torch.Tensor:
-    """Pair-major y = grouped product over an expert-major CSR (host dict from the library)."""
+                 device_csr: dict | None = None, topk_weights: torch.Tensor | None = None,
+                 stream=None) -> torch.Tensor:
+    """Pair-major y = grouped product over an expert-major CSR (host dict from the library),
+    each row times its fp32 routing weight when `topk_weights` [n_pairs] is given."""
     if device_csr is None:
         device_csr = {key: to_device(np.asarray(csr[key], dtype=np.int32), a.device)
                       for key in ("ex_ids", "ex_off", "ex_pairs", "pair_tok")}
@@ -128,6 +131,8 @@ def grouped_gemm(a: torch.Tensor, bank: ExpertBank, csr: dict, out: torch.Tensor
                     device_csr["ex_off"], device_csr["ex_pairs"], device_csr["pair_tok"], out,
                     n_expert=bank.n_expert, n_active=len(csr["ex_ids"]), n_pairs=n_pairs,
                     n_tokens=a.shape[0], k=bank.k, n=bank.n, zp_bank=bank.z,
-                    zp_stride_bytes=bank.z_stride,
-                    flags=WQ_FLAG_HAS_ZP if bank.z is not None else 0, stream=stream)
+                    zp_stride_bytes=bank.z_stride, topk_weights=topk_weights,
+                    flags=(WQ_FLAG_HAS_ZP if bank.z is not None else 0)
+                    | (WQ_FLAG_MUL_TOPK_WEIGHTS if topk_weights is not None else 0),
+                    stream=stream)
     return out

@@ -19,7 +19,12 @@
  *    WQ_STAGE_LAUNCH_CONFIG, WQ_STAGE_FUNC_ATTR and WQ_STAGE_LAUNCH carry the hipError_t.
  *    This is the staged native status of ferrum-kernels marlin.rs (`marlin_moe_ffi_status`).
  *  - Validation happens before any launch (fail closed); nothing is enqueued on error.
- *  - Shapes: k % 128 == 0, n % 256 == 0, group_size == 128 (one group = 128 rows of K).
+ *  - Shapes: k % 128 == 0, n % 256 == 0.  group_size (rows of K per scale / zero point) is
+ *    -1 (channelwise: one group over all of K, as transformer.rs `marlin_num_groups` maps
+ *    it) or a multiple of 128 dividing k.  The pages also allow the other positive
+ *    multiples of 16 dividing k; those fail with WQ_ERR_SHAPE.  The library stores scales
+ *    and zero points per 128-row chunk, so the GEMM calls read the same layout for every
+ *    supported group_size.
  *
  * Library weight layout (produced by the wq_repack_* calls; G = k / 128):
  *  - B: k*n/8 uint32 words (k*n/2 bytes, the plain format's byte count).  For 16-column
@@ -97,13 +102,17 @@ const char* wq_status_str(int status);
 int wq_repack_b(const uint32_t* qweight, const int32_t* perm, void* b_out, int k, int n,
                 void* stream);
 
-/* Scales fp16 [k/group_size][n] row-major -> library layout fp16 [n/16][G][16]. */
+/*
+ * Scales fp16 [k/group_size][n] row-major ([1][n] for group_size -1) -> library layout
+ * fp16 [n/16][G][16]: chunk g takes the scales of the group holding its rows.
+ */
 int wq_repack_scales(const void* scales, void* s_out, int k, int n, int group_size,
                      void* stream);
 
 /*
  * Zero points uint32 [k/group_size][n/8] (actual codes 0..15, column 8j+i in bits 4i of
- * word j: vllm_marlin.rs `repack_gptq_qzeros_to_marlin`) -> library layout [n/16][G][2].
+ * word j: vllm_marlin.rs `repack_gptq_qzeros_to_marlin`; [1][n/8] for group_size -1) ->
+ * library layout [n/16][G][2], chunk g taking the codes of the group holding its rows.
  */
 int wq_repack_zeros(const uint32_t* zeros, void* z_out, int k, int n, int group_size,
                     void* stream);
@@ -113,7 +122,8 @@ int wq_repack_zeros(const uint32_t* zeros, void* z_out, int k, int n, int group_
  * (marlin.rs `MarlinWeight.perm` doc: perm = argsort(g_idx)), sorted_gidx_out[i] =
  * g_idx[perm[i]] (either output may be NULL).  Fails with WQ_ERR_ACT_ORDER unless every
  * group 0..k/group_size-1 holds exactly group_size rows, the GPTQ construction, which
- * makes sorted position i belong to group i / group_size.
+ * makes sorted position i belong to group i / group_size (group_size -1: one group of k
+ * rows).
  */
 int wq_act_order_perm(const int32_t* g_idx, int k, int group_size, int32_t* perm_out,
                       int32_t* sorted_gidx_out);
@@ -139,7 +149,7 @@ typedef struct wq_gemm_args {
   void* stream;             /* hipStream_t                                              */
   int32_t m, n, k;          /* m >= 1, n % 256 == 0, k % 128 == 0                        */
   int32_t lda;              /* row stride of a in elements, >= k, multiple of 8         */
-  int32_t group_size;       /* 128                                                      */
+  int32_t group_size;       /* as repacked: -1 or a multiple of 128 dividing k          */
   uint32_t flags;           /* WQ_FLAG_*; HAS_ZP iff zero_points != NULL; ACT_ORDER iff perm */
   int32_t split_k;          /* 0 = library's choice; 1 = no split; s > 1 requests s splits
                                along K for m <= 16 (needs WQ_FLAG_FP32_REDUCE; clamped to

@@ -27,6 +27,7 @@ import numpy as np
 from .reference import unpack_qweight
 
 SLOT = (0, 4, 1, 5, 2, 6, 3, 7)
+CHUNK = 128  # rows of K per layout chunk (and per stored scale row)
 
 
 def repack_b_loops(codes: np.ndarray, perm=None) -> np.ndarray:
@@ -75,15 +76,28 @@ def unrepack_b(words: np.ndarray, k_total: int, n_total: int) -> np.ndarray:
     return codes.transpose(1, 4, 2, 5, 0, 3).reshape(k_total, n_total)
 
 
-def repack_scales(scales: np.ndarray) -> np.ndarray:
-    """fp16 [G][N] -> fp16 [N/16][G][16] (flattened)."""
-    s = np.asarray(scales, dtype=np.float16)
+def chunk_rows(values: np.ndarray, k: int | None, group_size: int) -> np.ndarray:
+    """Per-group rows [K/group_size][...] -> one row per 128-row chunk of K: chunk g takes
+    the row of the group holding rows 128g..128g+127 (the single row when channelwise)."""
+    v = np.asarray(values)
+    if k is None or group_size == CHUNK:
+        return v
+    chunks = k // CHUNK
+    src = np.zeros(chunks, dtype=np.int64) if group_size == -1 else \
+        (np.arange(chunks) * CHUNK) // group_size
+    return v[src]
+
+
+def repack_scales(scales: np.ndarray, k: int | None = None, group_size: int = 128) -> np.ndarray:
+    """fp16 [K/group_size][N] -> fp16 [N/16][K/128][16] (flattened)."""
+    s = chunk_rows(np.asarray(scales, dtype=np.float16), k, group_size)
     groups, n_total = s.shape
     return s.reshape(groups, n_total // 16, 16).transpose(1, 0, 2).reshape(-1).copy()
 
 
-def repack_zero_points(zeros: np.ndarray) -> np.ndarray:
-    """uint32 [G][N/8] -> uint32 [N/16][G][2] (flattened)."""
-    z = np.asarray(zeros, dtype=np.uint32)
+def repack_zero_points(zeros: np.ndarray, k: int | None = None,
+                       group_size: int = 128) -> np.ndarray:
+    """uint32 [K/group_size][N/8] -> uint32 [N/16][K/128][2] (flattened)."""
+    z = chunk_rows(np.asarray(zeros, dtype=np.uint32), k, group_size)
     groups, n8 = z.shape
     return z.reshape(groups, n8 // 2, 2).transpose(1, 0, 2).reshape(-1).copy()

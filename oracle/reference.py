@@ -66,23 +66,29 @@ def unpack_zero_points(zeros: np.ndarray) -> np.ndarray:
 
 
 def num_groups(k: int, group_size: int) -> int:
-    """Group count along K (transformer.rs `marlin_num_groups`; only positive sizes here)."""
+    """Group count along K, as transformer.rs `marlin_num_groups` defines it: -1 means one
+    channelwise group; any other size must be positive and divide K."""
     if k <= 0:
         raise ValueError(f"input width {k} must be positive")
+    if group_size == -1:
+        return 1
     if group_size <= 0:
-        raise ValueError(f"group size {group_size} must be positive")
+        raise ValueError(f"group size {group_size} must be -1 for channelwise weights or positive")
     if k % group_size:
         raise ValueError(f"input width {k} is not divisible by group size {group_size}")
     return k // group_size
 
 
 def group_of_rows(k: int, group_size: int, g_idx: np.ndarray | None = None) -> np.ndarray:
-    """Group of every original row: g_idx[k] with act_order, else k // group_size."""
+    """Group of every original row: g_idx[k] with act_order, else k // group_size (0 for
+    every row when channelwise, group_size -1)."""
     if g_idx is not None:
         g = np.asarray(g_idx, dtype=np.int64)
         if g.shape != (k,):
             raise ValueError("g_idx must have one entry per row of K")
         return g
+    if group_size == -1:
+        return np.zeros(k, dtype=np.int64)
     return np.arange(k, dtype=np.int64) // group_size
 
 
@@ -153,6 +159,8 @@ def act_order_perm(g_idx: np.ndarray, group_size: int) -> tuple[np.ndarray, np.n
     perm = np.argsort(g, kind="stable")
     sorted_g = g[perm]
     k = g.size
+    if group_size == -1:
+        group_size = k
     if k % group_size or not np.array_equal(sorted_g, np.arange(k) // group_size):
         raise ValueError("act_order groups must each hold exactly group_size rows, "
                          "numbered 0..K/group_size-1")

@@ -173,15 +173,17 @@ GROUP_SIZE = 128
 
 def dense_case(m: int, k: int, n: int, *, zp: bool = False, act_order: bool = False,
                group_size: int = GROUP_SIZE, seed: int = ROOT_SEED) -> dict:
-    """One dense problem's inputs in the boundary's plain formats."""
-    groups = k // group_size
+    """One dense problem's inputs in the boundary's plain formats (group_size -1: one
+    channelwise group)."""
+    groups = 1 if group_size == -1 else k // group_size
     case = dict(
         m=m, k=k, n=n, group_size=group_size,
         a=activations(stream_seed(seed, TAG_ACT), m, k),
         qweight=qweight_words(stream_seed(seed, TAG_WEIGHT), k, n),
         scales=scales(stream_seed(seed, TAG_SCALE), groups, n),
         zeros=zero_point_words(stream_seed(seed, TAG_ZERO), groups, n) if zp else None,
-        g_idx=act_order_g_idx(stream_seed(seed, TAG_PERM), k, group_size) if act_order else None,
+        g_idx=(act_order_g_idx(stream_seed(seed, TAG_PERM), k,
+                               k if group_size == -1 else group_size) if act_order else None),
     )
     return case
 

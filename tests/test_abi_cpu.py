@@ -86,8 +86,12 @@ def call_gemm(L, **over):
     (dict(m=0), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
     (dict(lda=512), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
     (dict(lda=1028), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
+    # group sizes: -1 and multiples of 128 dividing k are supported; others are not
     (dict(group_size=64), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
-    (dict(group_size=-1), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
+    (dict(group_size=192), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
+    (dict(group_size=2048), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),   # does not divide k
+    (dict(group_size=-2), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
+    (dict(group_size=0), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
     (dict(flags=wq.WQ_FLAG_HAS_ZP), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
     (dict(zero_points=0x5000), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
     (dict(flags=wq.WQ_FLAG_HAS_ZP, zero_points=0x5008), status(STAGE_ARGS, wq.WQ_ERR_ALIGN)),
@@ -157,6 +161,25 @@ def test_stream_read_sizing_and_validation(L):
                                                                       wq.WQ_ERR_WORKSPACE)
     assert L.wq_stream_read(0x1000, 1000, 0x2000, 4, None) == status(STAGE_SHAPE,
                                                                       wq.WQ_ERR_SHAPE)
+
+
+def test_repack_validation_of_group_sizes(L):
+    # k = 1024: 256 and 1024 divide it, 768 does not; -1 is channelwise
+    for gs in (64, 768, -2, 0):
+        assert L.wq_repack_scales(0x1000, 0x2000, 1024, 256, gs, None) == status(
+            STAGE_SHAPE, wq.WQ_ERR_SHAPE), gs
+        assert L.wq_repack_zeros(0x1000, 0x2000, 1024, 256, gs, None) == status(
+            STAGE_SHAPE, wq.WQ_ERR_SHAPE), gs
+
+
+def test_act_order_perm_with_other_group_sizes():
+    g_idx = synthetic.act_order_g_idx(4, 1024, 256)
+    perm, sorted_g = wq.wq_act_order_perm(g_idx, 256)
+    operm, osorted = ref.act_order_perm(g_idx, 256)
+    assert np.array_equal(perm, operm) and np.array_equal(sorted_g, osorted)
+    # channelwise: one group of all rows, so the stable argsort is the identity
+    perm, sorted_g = wq.wq_act_order_perm(np.zeros(512, np.int32), -1)
+    assert perm.tolist() == list(range(512)) and not sorted_g.any()
 
 
 def test_act_order_perm_matches_oracle_and_rejects_uneven_groups():

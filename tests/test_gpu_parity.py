@@ -35,7 +35,8 @@ def host(t):
 
 def gpu_gemm(case, dev, *, fp32_reduce=False, split_k=0, a=None):
     w = torch_ops.PackedWeight(case["qweight"], case["scales"], case.get("zeros"),
-                               case.get("g_idx"), device=dev)
+                               case.get("g_idx"), device=dev,
+                               group_size=case.get("group_size", 128))
     a_d = torch_ops.to_device(case["a"] if a is None else a, dev)
     c = torch_ops.gemm(a_d, w, fp32_reduce=fp32_reduce, split_k=split_k)
     torch.cuda.synchronize()
@@ -44,7 +45,8 @@ def gpu_gemm(case, dev, *, fp32_reduce=False, split_k=0, a=None):
 
 def oracle_gemm(case, columns=None):
     return ref.w4a16_gemm(case["a"], case["qweight"], case["scales"], zeros=case.get("zeros"),
-                          g_idx=case.get("g_idx"), columns=columns)
+                          g_idx=case.get("g_idx"), group_size=case.get("group_size", 128),
+                          columns=columns)
 
 
 def assert_parity(c, want, label):
@@ -147,6 +149,47 @@ def test_act_order_gather_widths(dev, m, k):
     case = synthetic.dense_case(m, k, n, act_order=True, seed=2000 + m + k)
     c = gpu_gemm(case, dev)
     assert_parity(c, oracle_gemm(case), label)
+
+
+# group sizes other than 128: channelwise (-1) and multiples of 128, whose scales and zero
+# points the repack repeats per 128-row chunk, on both kernels, with zp and act_order.
+GROUP_SHAPES = [
+    # m, k, n, group_size, zp, act_order
+    (1, 1024, 512, -1, False, False),
+    (16, 2048, 256, 256, True, False),
+    (7, 1024, 512, 512, False, True),
+    (300, 1024, 512, -1, True, False),
+    (257, 2048, 256, 1024, False, True),
+    (40, 4096, 256, 2048, True, False),
+]
+
+
+@pytest.mark.parametrize("m,k,n,gs,zp,act_order", GROUP_SHAPES)
+def test_group_sizes_match_oracle(dev, m, k, n, gs, zp, act_order):
+    label = f"group_size={gs} m={m} k={k} n={n} zp={zp} act_order={act_order}"
+    say(label)
+    case = synthetic.dense_case(m, k, n, zp=zp, act_order=act_order, group_size=gs,
+                                seed=3000 + m + k + gs)
+    c = gpu_gemm(case, dev, fp32_reduce=True)
+    assert_parity(c, oracle_gemm(case), label)
+
+
+@pytest.mark.parametrize("gs", [-1, 256, 1024])
+def test_group_size_repack_and_dequant_bitwise(dev, gs):
+    k, n = 1024, 512
+    say(f"repack/dequant group_size={gs}")
+    groups = 1 if gs == -1 else k // gs
+    s = synthetic.scales(90, groups, n)
+    z = synthetic.zero_point_words(91, groups, n)
+    qw = synthetic.qweight_words(92, k, n)
+    w = torch_ops.PackedWeight(qw, s, z, device=dev, group_size=gs)
+    assert np.array_equal(host(w.s).view(np.uint16), layout.repack_scales(s, k, gs).view(np.uint16))
+    assert np.array_equal(host(w.z).view(np.uint32), layout.repack_zero_points(z, k, gs))
+    out = torch.empty((k, n), dtype=torch.float16, device=dev)
+    wq.wq_dequant(w.b, w.s, w.z, out, k=k, n=n, flags=wq.WQ_FLAG_HAS_ZP, group_size=gs)
+    torch.cuda.synchronize()
+    want = ref.dequantize_fp16(ref.w4a16_weights(qw, s, zeros=z, group_size=gs))
+    assert np.array_equal(host(out).view(np.uint16), want.view(np.uint16))
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode", "batched"])
@@ -279,6 +322,15 @@ def test_grouped_matches_oracle(dev, tokens, experts, k, n, zp, weighted):
     w = synthetic.routing_weights(400 + tokens, tokens, 2) if weighted else None
     y, ex, ocsr = run_grouped(moe, dev, zeros, w)
     assert_parity(y, ref.grouped_w4a16_gemm(moe["a"], ex, ocsr, topk_weights=w), label)
+
+
+def test_grouped_with_256_row_groups(dev):
+    tokens, experts, k, n, gs = 120, 3, 1024, 256, 256
+    moe = synthetic.moe_case(tokens, experts, k, n, group_size=gs, seed=24)
+    for e in moe["experts"]:
+        e["group_size"] = gs
+    y, ex, ocsr = run_grouped(moe, dev)
+    assert_parity(y, ref.grouped_w4a16_gemm(moe["a"], ex, ocsr, group_size=gs), "grouped gs=256")
 
 
 def test_grouped_unit_weights_change_nothing(dev):

@@ -256,6 +256,46 @@ def test_grouped_product_equals_dense_rows():
         assert y[p].tolist() == dense[0].tolist()
 
 
+def test_larger_and_channelwise_groups_equal_repeated_128_row_groups():
+    """A group of 256 or 512 rows (or one channelwise group) is the same as 128-row groups
+    repeating its scales and zero points: the row -> group map must use the group size."""
+    k, n, m = 1024, 32, 3
+    a = synthetic.activations(60, m, k)
+    qw = synthetic.qweight_words(61, k, n)
+    for gs in (256, 512, -1):
+        groups = ref.num_groups(k, gs)
+        rep = (k // 128) // groups
+        s = synthetic.scales(62 + gs % 7, groups, n)
+        z = synthetic.zero_point_words(63, groups, n)
+        got = ref.w4a16_gemm(a, qw, s, zeros=z, group_size=gs)
+        want = ref.w4a16_gemm(a, qw, np.repeat(s, rep, axis=0), zeros=np.repeat(z, rep, axis=0),
+                              group_size=128)
+        assert got.tolist() == want.tolist(), gs
+        assert np.array_equal(layout.repack_scales(s, k, gs),
+                              layout.repack_scales(np.repeat(s, rep, axis=0)))
+        assert np.array_equal(layout.repack_zero_points(z, k, gs),
+                              layout.repack_zero_points(np.repeat(z, rep, axis=0)))
+    # with 256-row groups, row 128 is in group 0 and row 256 in group 1
+    assert ref.group_of_rows(1024, 256)[[127, 128, 255, 256]].tolist() == [0, 0, 0, 1]
+    assert ref.group_of_rows(1024, -1).max() == 0
+
+
+def test_act_order_with_256_row_groups_equals_plain_product():
+    k, n, m, gs = 1024, 32, 4, 256
+    a = synthetic.activations(70, m, k)
+    qw = synthetic.qweight_words(71, k, n)
+    s = synthetic.scales(72, k // gs, n)
+    g_idx = (synthetic.permutation(73, k) // gs).astype(np.int32)
+    perm, sorted_g = ref.act_order_perm(g_idx, gs)
+    assert sorted_g.tolist() == (np.arange(k) // gs).tolist()
+    got = ref.w4a16_gemm(a, qw, s, g_idx=g_idx, group_size=gs)
+    # permuted operands: rows of W in sorted order (codes moved with their rows), A columns
+    q = ref.unpack_qweight(qw)[perm, :]
+    w = (q.astype(np.float64) - 8) * s.astype(np.float64)[np.arange(k) // gs, :]
+    want = a.astype(np.float64)[:, perm] @ w
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
 def test_routing_weights_scale_each_pair_row():
     """Row p is the dense product of its token row and expert times topk_weights[p]: the
     weights follow pair order, not CSR position or token; unit weights change nothing."""

@@ -29,11 +29,20 @@ int check_ptr(const void* p, size_t align) {
   return 0;
 }
 
-// k % 128 == 0, n % 256 == 0, group_size == 128, and byte extents that fit.
+// Group sizes the library stores per 128-row chunk: -1 (one group over K, channelwise, as
+// transformer.rs `marlin_num_groups` maps it to one group) or a multiple of 128 dividing K
+// (its scales are repeated for each chunk it covers).  The pages also allow the other
+// positive multiples of 16 dividing K; those are rejected here.
+bool chunk_group_size(int k, int group_size) {
+  if (group_size == -1) return true;
+  return group_size > 0 && group_size % kGroupSize == 0 && k % group_size == 0;
+}
+
+// k % 128 == 0, n % 256 == 0, a supported group_size, and byte extents that fit.
 int check_kn(int k, int n, int group_size) {
   if (k <= 0 || n <= 0 || k % kGroupSize != 0 || n % 256 != 0)
     return fail(WQ_STAGE_SHAPE, WQ_ERR_SHAPE);
-  if (group_size != kGroupSize) return fail(WQ_STAGE_SHAPE, WQ_ERR_SHAPE);
+  if (!chunk_group_size(k, group_size)) return fail(WQ_STAGE_SHAPE, WQ_ERR_SHAPE);
   if ((long long)k * n / 8 > (long long)std::numeric_limits<int32_t>::max() * 4LL)
     return fail(WQ_STAGE_SHAPE, WQ_ERR_OVERFLOW);
   return 0;
@@ -159,7 +168,7 @@ int wq_repack_scales(const void* scales, void* s_out, int k, int n, int group_si
   if ((st = check_ptr(s_out, 16))) return st;
   const hipError_t e =
       wq::launch_repack_scales(static_cast<const uint16_t*>(scales), static_cast<uint16_t*>(s_out),
-                               k, n, as_stream(stream));
+                               k, n, group_size, as_stream(stream));
   return e == hipSuccess ? 0 : hip_fail(e);
 }
 
@@ -170,13 +179,14 @@ int wq_repack_zeros(const uint32_t* zeros, void* z_out, int k, int n, int group_
   if ((st = check_ptr(zeros, 4))) return st;
   if ((st = check_ptr(z_out, 16))) return st;
   const hipError_t e = wq::launch_repack_zeros(zeros, static_cast<uint32_t*>(z_out), k, n,
-                                               as_stream(stream));
+                                               group_size, as_stream(stream));
   return e == hipSuccess ? 0 : hip_fail(e);
 }
 
 int wq_act_order_perm(const int32_t* g_idx, int k, int group_size, int32_t* perm_out,
                       int32_t* sorted_gidx_out) {
   if (g_idx == nullptr) return fail(WQ_STAGE_ARGS, WQ_ERR_NULL);
+  if (k > 0 && group_size == -1) group_size = k;  // channelwise: one group of all K rows
   if (k <= 0 || group_size <= 0 || k % group_size != 0) return fail(WQ_STAGE_SHAPE, WQ_ERR_SHAPE);
   const int groups = k / group_size;
   // Counting sort by group keeps equal groups in ascending row order (a stable argsort).

@@ -10,9 +10,11 @@ namespace wq {
 // Repack / export / gather kernels (wq_repack.hip).
 hipError_t launch_repack_b(const uint32_t* qweight, const int32_t* perm, uint32_t* out, int k,
                            int n, hipStream_t stream);
+// group_size: -1 (channelwise) or a multiple of 128 dividing k; the output always holds
+// one entry per 128-row chunk of K.
 hipError_t launch_repack_scales(const uint16_t* s, uint16_t* out, int k, int n,
-                                hipStream_t stream);
-hipError_t launch_repack_zeros(const uint32_t* z, uint32_t* out, int k, int n,
+                                int group_size, hipStream_t stream);
+hipError_t launch_repack_zeros(const uint32_t* z, uint32_t* out, int k, int n, int group_size,
                                hipStream_t stream);
 hipError_t launch_dequant(const uint32_t* b, const uint16_t* s, const uint32_t* z, int k, int n,
                           uint16_t* w, hipStream_t stream);

@@ -51,9 +51,16 @@ __global__ __launch_bounds__(256) void repack_b_kernel(const uint32_t* __restric
   }
 }
 
+// Scales and zero points are stored per 128-row chunk of K.  A source group covering
+// `chunks_per_group` chunks (its size / 128) is repeated for each of them; 0 stands for
+// one group over all of K (channelwise).
+__device__ __forceinline__ long source_group(int chunk, int chunks_per_group) {
+  return chunks_per_group > 0 ? chunk / chunks_per_group : 0;
+}
+
 __global__ __launch_bounds__(256) void repack_scales_kernel(const uint16_t* __restrict__ s,
                                                             uint16_t* __restrict__ out, int k,
-                                                            int n) {
+                                                            int n, int chunks_per_group) {
   const int groups = k / kGroup;
   const long total = (long)groups * n;
   for (long o = (long)blockIdx.x * blockDim.x + threadIdx.x; o < total;
@@ -62,13 +69,13 @@ __global__ __launch_bounds__(256) void repack_scales_kernel(const uint16_t* __re
     const long rest = o >> 4;
     const int g = (int)(rest % groups);
     const long nb = rest / groups;
-    out[o] = s[(long)g * n + nb * 16 + c];
+    out[o] = s[source_group(g, chunks_per_group) * n + nb * 16 + c];
   }
 }
 
 __global__ __launch_bounds__(256) void repack_zeros_kernel(const uint32_t* __restrict__ z,
                                                            uint32_t* __restrict__ out, int k,
-                                                           int n) {
+                                                           int n, int chunks_per_group) {
   const int groups = k / kGroup;
   const long total = (long)groups * (n / 8);
   for (long o = (long)blockIdx.x * blockDim.x + threadIdx.x; o < total;
@@ -77,7 +84,7 @@ __global__ __launch_bounds__(256) void repack_zeros_kernel(const uint32_t* __res
     const long rest = o >> 1;
     const int g = (int)(rest % groups);
     const long nb = rest / groups;
-    out[o] = z[(long)g * (n / 8) + nb * 2 + h];
+    out[o] = z[source_group(g, chunks_per_group) * (n / 8) + nb * 2 + h];
   }
 }
 
@@ -219,16 +226,18 @@ hipError_t launch_repack_b(const uint32_t* qweight, const int32_t* perm, uint32_
 }
 
 hipError_t launch_repack_scales(const uint16_t* s, uint16_t* out, int k, int n,
-                                hipStream_t stream) {
+                                int group_size, hipStream_t stream) {
+  const int chunks_per_group = group_size > 0 ? group_size / kGroup : 0;
   hipLaunchKernelGGL(repack_scales_kernel, dim3(grid_for((long)(k / kGroup) * n)), dim3(256), 0,
-                     stream, s, out, k, n);
+                     stream, s, out, k, n, chunks_per_group);
   return hipGetLastError();
 }
 
-hipError_t launch_repack_zeros(const uint32_t* z, uint32_t* out, int k, int n,
+hipError_t launch_repack_zeros(const uint32_t* z, uint32_t* out, int k, int n, int group_size,
                                hipStream_t stream) {
+  const int chunks_per_group = group_size > 0 ? group_size / kGroup : 0;
   hipLaunchKernelGGL(repack_zeros_kernel, dim3(grid_for((long)(k / kGroup) * (n / 8))),
-                     dim3(256), 0, stream, z, out, k, n);
+                     dim3(256), 0, stream, z, out, k, n, chunks_per_group);
   return hipGetLastError();
 }
 

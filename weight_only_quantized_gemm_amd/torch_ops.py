@@ -29,26 +29,27 @@ class PackedWeight:
     """One weight matrix in the library layout (B, scales, optional zero points, perm)."""
 
     def __init__(self, qweight: np.ndarray, scales: np.ndarray, zeros: np.ndarray | None = None,
-                 g_idx: np.ndarray | None = None, device="cuda"):
+                 g_idx: np.ndarray | None = None, device="cuda", group_size: int = GROUP):
         self.k = qweight.shape[0] * 8
         self.n = qweight.shape[1]
+        self.group_size = group_size
         self.device = torch.device(device)
         self.perm = None
         if g_idx is not None:
-            perm, _ = wq_act_order_perm(g_idx, GROUP)
+            perm, _ = wq_act_order_perm(g_idx, group_size)
             self.perm = to_device(perm, self.device)
         qw = to_device(qweight, self.device)
         self.b = torch.empty(self.k * self.n // 8, dtype=torch.int32, device=self.device)
         wq_repack_b(qw, self.b, self.k, self.n, perm=self.perm)
         sc = to_device(np.asarray(scales, dtype=np.float16), self.device)
         self.s = torch.empty((self.k // GROUP) * self.n, dtype=torch.float16, device=self.device)
-        wq_repack_scales(sc, self.s, self.k, self.n, GROUP)
+        wq_repack_scales(sc, self.s, self.k, self.n, group_size)
         self.z = None
         if zeros is not None:
             zw = to_device(zeros, self.device)
             self.z = torch.empty((self.k // GROUP) * self.n // 8, dtype=torch.int32,
                                  device=self.device)
-            wq_repack_zeros(zw, self.z, self.k, self.n, GROUP)
+            wq_repack_zeros(zw, self.z, self.k, self.n, group_size)
         torch.cuda.synchronize(self.device)
 
     def clone(self) -> "PackedWeight":
@@ -94,7 +95,7 @@ def gemm(a: torch.Tensor, w: PackedWeight, out: torch.Tensor | None = None, *,
         buffers = GemmBuffers(w, m, fp32_reduce)
     wq_gemm(a, w.b, out, w.s, m=m, n=w.n, k=w.k, zero_points=w.z, perm=w.perm,
             a_tmp=buffers.a_tmp, workspace=buffers.workspace, flags=buffers.flags,
-            split_k=split_k, lda=a.stride(0), stream=stream)
+            split_k=split_k, lda=a.stride(0), group_size=w.group_size, stream=stream)
     return out
 
 
@@ -102,10 +103,11 @@ class ExpertBank:
     """Repacked weights of several experts stored back to back (one stride per tensor)."""
 
     def __init__(self, experts: list[dict], device="cuda"):
-        self.packed = [PackedWeight(e["qweight"], e["scales"], e.get("zeros"), device=device)
+        self.packed = [PackedWeight(e["qweight"], e["scales"], e.get("zeros"), device=device,
+                                    group_size=e.get("group_size", GROUP))
                        for e in experts]
         p0 = self.packed[0]
-        self.k, self.n = p0.k, p0.n
+        self.k, self.n, self.group_size = p0.k, p0.n, p0.group_size
         self.b = torch.stack([p.b for p in self.packed])
         self.s = torch.stack([p.s for p in self.packed])
         self.z = torch.stack([p.z for p in self.packed]) if p0.z is not None else None
@@ -132,6 +134,7 @@ def grouped_gemm(a: torch.Tensor, bank: ExpertBank, csr: dict, out: torch.Tensor
                     n_expert=bank.n_expert, n_active=len(csr["ex_ids"]), n_pairs=n_pairs,
                     n_tokens=a.shape[0], k=bank.k, n=bank.n, zp_bank=bank.z,
                     zp_stride_bytes=bank.z_stride, topk_weights=topk_weights,
+                    group_size=bank.group_size,
                     flags=(WQ_FLAG_HAS_ZP if bank.z is not None else 0)
                     | (WQ_FLAG_MUL_TOPK_WEIGHTS if topk_weights is not None else 0),
                     stream=stream)

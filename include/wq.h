@@ -58,6 +58,13 @@ extern "C" {
 /* Grouped call only: scale each output row by its pair's fp32 routing weight (vllm_marlin.rs
  * MoE launch, `mul_topk_weights` with `topk_weights`). */
 #define WQ_FLAG_MUL_TOPK_WEIGHTS (1u << 6)
+/* SwiGLU epilogue (the transformer.rs dense SwiGLU chain's gate and up projections with its
+ * planar silu*mul, fused): B, scales and zero points hold a gate and an up projection of
+ * n/2 columns each, paired by wq_interleave_gate_up before the repack (16-column block 2t
+ * is gate block t, block 2t+1 up block t); the output is the [rows][n/2] fp16 activation
+ * fp16(silu(A Wg) * (A Wu)), silu(x) = x / (1 + exp(-x)), from the fp32 sums.  Not with
+ * WQ_FLAG_MUL_TOPK_WEIGHTS. */
+#define WQ_FLAG_SWIGLU (1u << 7)
 
 enum wq_stage {
   WQ_STAGE_ARGS = 1,
@@ -118,6 +125,17 @@ int wq_repack_zeros(const uint32_t* zeros, void* z_out, int k, int n, int group_
                     void* stream);
 
 /*
+ * Load-time helper for WQ_FLAG_SWIGLU: pairs the columns of a gate and an up tensor in
+ * 16-column blocks, out[r] = [gate block 0, up block 0, gate block 1, up block 1, ...].
+ * gate and up are row-major [rows][cols] with bits_per_column bits per column: 32 for
+ * GPTQ qweight words ([k/8][cols] uint32), 16 for fp16 scales, 4 for packed zero points
+ * ([groups][cols/8] uint32); out has 2*cols columns.  cols % 16 == 0; device pointers,
+ * 4-byte aligned; enqueued on `stream`.
+ */
+int wq_interleave_gate_up(const void* gate, const void* up, void* out, int rows, int cols,
+                          int bits_per_column, void* stream);
+
+/*
  * act_order helper (host memory, synchronous): perm_out[i] = stable argsort(g_idx)[i]
  * (marlin.rs `MarlinWeight.perm` doc: perm = argsort(g_idx)), sorted_gidx_out[i] =
  * g_idx[perm[i]] (either output may be NULL).  Fails with WQ_ERR_ACT_ORDER unless every
@@ -157,7 +175,11 @@ typedef struct wq_gemm_args {
   int32_t reserved;         /* must be 0                                                */
 } wq_gemm_args;
 
-/* C = A @ dequant(B) (all of it enqueued on args->stream). */
+/*
+ * C = A @ dequant(B) (all of it enqueued on args->stream).  With WQ_FLAG_SWIGLU, c is the
+ * [m][n/2] activation silu(A Wg) * (A Wu) of paired gate/up weights (any m; the decode-
+ * shaped small-M kernel is not used for it).
+ */
 int wq_gemm(const wq_gemm_args* args);
 
 /*

@@ -76,6 +76,21 @@ def unrepack_b(words: np.ndarray, k_total: int, n_total: int) -> np.ndarray:
     return codes.transpose(1, 4, 2, 5, 0, 3).reshape(k_total, n_total)
 
 
+def interleave_gate_up(gate: np.ndarray, up: np.ndarray, cols_per_elem: int = 1) -> np.ndarray:
+    """Pair the columns of two row-major tensors in 16-column blocks: out column block 2t is
+    block t of `gate`, block 2t+1 block t of `up` (a fused gate/up projection's weights).
+    `cols_per_elem` columns share one element (8 for packed 4-bit zero points)."""
+    g = np.asarray(gate)
+    u = np.asarray(up)
+    per = 16 // cols_per_elem  # elements per 16-column block
+    rows, cols = g.shape
+    out = np.empty((rows, 2 * cols), dtype=g.dtype)
+    for t in range(cols // per):
+        out[:, 2 * t * per:(2 * t + 1) * per] = g[:, t * per:(t + 1) * per]
+        out[:, (2 * t + 1) * per:(2 * t + 2) * per] = u[:, t * per:(t + 1) * per]
+    return out
+
+
 def chunk_rows(values: np.ndarray, k: int | None, group_size: int) -> np.ndarray:
     """Per-group rows [K/group_size][...] -> one row per 128-row chunk of K: chunk g takes
     the row of the group holding rows 128g..128g+127 (the single row when channelwise)."""

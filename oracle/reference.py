@@ -290,14 +290,49 @@ def grouped_w4a16_gemm(a, experts, csr, *, group_size=128, columns=None,
 
 
 # ---------------------------------------------------------------------------------------
+# SwiGLU MLP chain (ferrum-kernels transformer.rs, the dense SwiGLU encode with W4
+# projections: gate and up projections of the same activations, the planar silu*mul of the
+# two, then the down projection of its fp16 result)
+# ---------------------------------------------------------------------------------------
+
+def silu(x: np.ndarray) -> np.ndarray:
+    """silu(x) = x * sigmoid(x) = x / (1 + exp(-x)), fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def swiglu_activation(a, gate: dict, up: dict, *, group_size=128, columns=None) -> np.ndarray:
+    """act = silu(A @ W_gate) * (A @ W_up), fp64 and unrounded ([M][I], or a column subset).
+
+    `gate` and `up` hold qweight, scales and optional zeros of the two projections.
+    """
+    g = w4a16_gemm(a, gate["qweight"], gate["scales"], zeros=gate.get("zeros"),
+                   group_size=group_size, columns=columns)
+    u = w4a16_gemm(a, up["qweight"], up["scales"], zeros=up.get("zeros"),
+                   group_size=group_size, columns=columns)
+    return silu(g) * u
+
+
+def swiglu_mlp(a, gate: dict, up: dict, down: dict, *, group_size=128) -> tuple:
+    """The chain: act16 = fp16_rne(swiglu_activation) (the activation handed to the down
+    projection is fp16, as every W4A16 operand A is), out = act16 @ W_down in fp64.
+    Returns (act16, out)."""
+    act16 = dequantize_fp16(swiglu_activation(a, gate, up, group_size=group_size))
+    out = w4a16_gemm(act16, down["qweight"], down["scales"], zeros=down.get("zeros"),
+                     group_size=group_size)
+    return act16, out
+
+
+# ---------------------------------------------------------------------------------------
 # Checker
 # ---------------------------------------------------------------------------------------
 
 def check(c: np.ndarray, ref: np.ndarray, *, rel_max: float = 2e-3, abs_max: float = 1e-3,
-          rel_frob: float = 1e-3) -> dict:
+          rel_frob: float = 1e-3, rel_elem: float = 0.0) -> dict:
     """Tolerance test of an fp16 result against the fp64 reference.
 
-    Pass iff no non-finite output, max |C - ref| <= rel_max * rms(ref) + abs_max, and
+    Pass iff no non-finite output, |C - ref| <= rel_elem * |ref| + rel_max * rms(ref) +
+    abs_max for every element (rel_elem is 0 for the GEMM outputs), and
     ||C - ref||_F / ||ref||_F <= rel_frob (rms over every compared element).
     """
     c64 = np.asarray(c).astype(np.float64)
@@ -308,6 +343,8 @@ def check(c: np.ndarray, ref: np.ndarray, *, rel_max: float = 2e-3, abs_max: flo
     diff = np.abs(c64 - ref)
     rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
     tol = rel_max * rms + abs_max
+    if rel_elem:
+        diff = diff - rel_elem * np.abs(ref)  # the element's own rounding allowance
     max_err = float(np.max(diff)) if diff.size else 0.0
     ref_norm = float(np.linalg.norm(ref))
     relf = float(np.linalg.norm(c64 - ref) / ref_norm) if ref_norm > 0 else float(

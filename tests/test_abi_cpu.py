@@ -163,6 +163,17 @@ def test_stream_read_sizing_and_validation(L):
                                                                       wq.WQ_ERR_SHAPE)
 
 
+def test_interleave_gate_up_validation(L):
+    assert L.wq_interleave_gate_up(0x1000, 0x2000, 0x3000, 4, 32, 8, None) == status(
+        STAGE_SHAPE, wq.WQ_ERR_SHAPE)                      # bits per column
+    assert L.wq_interleave_gate_up(0x1000, 0x2000, 0x3000, 4, 24, 16, None) == status(
+        STAGE_SHAPE, wq.WQ_ERR_SHAPE)                      # columns not a multiple of 16
+    assert L.wq_interleave_gate_up(None, 0x2000, 0x3000, 4, 32, 16, None) == status(
+        STAGE_ARGS, wq.WQ_ERR_NULL)
+    assert L.wq_interleave_gate_up(0x1000, 0x2002, 0x3000, 4, 32, 16, None) == status(
+        STAGE_ARGS, wq.WQ_ERR_ALIGN)
+
+
 def test_repack_validation_of_group_sizes(L):
     # k = 1024: 256 and 1024 divide it, 768 does not; -1 is channelwise
     for gs in (64, 768, -2, 0):
@@ -255,6 +266,10 @@ def grouped_args(**over):
     (dict(k=1000), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
     (dict(struct_size=4), status(STAGE_ARGS, wq.WQ_ERR_ABI)),
     (dict(abi_version=1), status(STAGE_ARGS, wq.WQ_ERR_ABI)),
+    # the SwiGLU activation takes no routing weight
+    (dict(topk_weights=0x8000, flags=wq.WQ_FLAG_MUL_TOPK_WEIGHTS | wq.WQ_FLAG_SWIGLU),
+     status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
+    (dict(flags=1 << 9), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
 ])
 def test_grouped_rejects_bad_arguments_before_launch(L, over, expect):
     assert L.wq_grouped_gemm(ctypes.byref(grouped_args(**over))) == expect

@@ -49,8 +49,8 @@ def oracle_gemm(case, columns=None):
                           columns=columns)
 
 
-def assert_parity(c, want, label):
-    res = ref.check(c, want)
+def assert_parity(c, want, label, rel_elem=0.0):
+    res = ref.check(c, want, rel_elem=rel_elem)
     say(f"{label}: max_err={res['max_err']:.3e} tol={res['tol']:.3e} "
         f"rel_frob={res['rel_frob']:.3e} nonfinite={res['nonfinite']}")
     assert res["ok"], (label, res)
@@ -428,3 +428,112 @@ def test_stream_read_reads_every_granule_once(dev):
             continue
         assert got[owner] == magic, (pos, owner, got[max(owner - 1, 0):owner + 2])
         assert np.count_nonzero(got) == 1, pos
+
+
+# --------------------------------------------------------------------------- SwiGLU chain
+
+# The SwiGLU activation is a product of two sums, so its values (and the down projection's
+# outputs of them) are heavy-tailed: fp16 rounding alone (up to 2^-11 |x|) can exceed the
+# GEMM bound at the largest elements, so these checks add twice that per-element rounding
+# allowance.
+ACT_REL = 2.0 ** -10
+
+def mlp_weights(seed, k, i, h=None, zp=False, group_size=128):
+    groups = 1 if group_size == -1 else k // group_size
+
+    def one(s, kk, nn):
+        g = 1 if group_size == -1 else kk // group_size
+        w = dict(qweight=synthetic.qweight_words(s, kk, nn), scales=synthetic.scales(s + 1, g, nn))
+        if zp:
+            w["zeros"] = synthetic.zero_point_words(s + 2, g, nn)
+        return w
+    gate, up = one(seed, k, i), one(seed + 10, k, i)
+    down = one(seed + 20, i, h) if h else None
+    return gate, up, down
+
+
+@pytest.mark.parametrize("bits,rows,cols", [(32, 128, 256), (16, 8, 512), (4, 8, 256)])
+def test_interleave_gate_up_bitwise(dev, bits, rows, cols):
+    per_word = 32 // bits
+    words = cols // per_word
+    g = synthetic.words_u32(95, rows * words).reshape(rows, words)
+    u = synthetic.words_u32(96, rows * words).reshape(rows, words)
+    out = torch.empty((rows, 2 * words), dtype=torch.int32, device=dev)
+    wq.wq_interleave_gate_up(torch_ops.to_device(g, dev), torch_ops.to_device(u, dev), out,
+                             rows, cols, bits)
+    torch.cuda.synchronize()
+    # a 16-column block is 16 words, 8 words (two fp16 per word) or 2 words
+    want = layout.interleave_gate_up(g, u, cols_per_elem=per_word) if bits != 16 else \
+        layout.interleave_gate_up(g.view(np.uint16).reshape(rows, cols),
+                                  u.view(np.uint16).reshape(rows, cols)).view(np.uint32)
+    assert np.array_equal(host(out).view(np.uint32), want.reshape(rows, 2 * words))
+
+
+@pytest.mark.parametrize("m,k,i,zp,act_order", [(1, 1024, 256, False, False),
+                                                 (16, 512, 512, True, False),
+                                                 (300, 1024, 256, False, True),
+                                                 (513, 256, 384, True, False)])
+def test_swiglu_activation_matches_oracle(dev, m, k, i, zp, act_order):
+    label = f"swiglu m={m} k={k} i={i} zp={zp} act_order={act_order}"
+    say(label)
+    gate, up, _ = mlp_weights(500 + m, k, i, zp=zp)
+    a = synthetic.activations(501 + m, m, k)
+    g_idx = synthetic.act_order_g_idx(502, k, 128) if act_order else None
+    if act_order:
+        gate["g_idx"] = up["g_idx"] = g_idx
+    w = torch_ops.PackedWeight.gate_up(gate, up, device=dev, g_idx=g_idx)
+    act = host(torch_ops.gemm(torch_ops.to_device(a, dev), w))
+    torch.cuda.synchronize()
+    if act_order:  # the oracle reads g_idx through its own argument
+        g = ref.w4a16_gemm(a, gate["qweight"], gate["scales"], zeros=gate.get("zeros"), g_idx=g_idx)
+        u = ref.w4a16_gemm(a, up["qweight"], up["scales"], zeros=up.get("zeros"), g_idx=g_idx)
+        want = ref.silu(g) * u
+    else:
+        want = ref.swiglu_activation(a, gate, up)
+    assert act.shape == (m, i)
+    assert_parity(act, want, label, rel_elem=ACT_REL)
+
+
+def test_swiglu_mlp_chain_matches_oracle(dev):
+    m, h, i = 200, 512, 768
+    say(f"swiglu mlp chain m={m} hidden={h} intermediate={i}")
+    gate, up, down = mlp_weights(600, h, i, h, zp=True)
+    a = synthetic.activations(601, m, h)
+    wgu = torch_ops.PackedWeight.gate_up(gate, up, device=dev)
+    wd = torch_ops.PackedWeight(down["qweight"], down["scales"], down["zeros"], device=dev)
+    act = torch_ops.gemm(torch_ops.to_device(a, dev), wgu)
+    out = host(torch_ops.gemm(act, wd))
+    act16, want = ref.swiglu_mlp(a, gate, up, down)
+    assert_parity(host(act), act16.astype(np.float64), "chain activation", rel_elem=ACT_REL)
+    assert_parity(out, want, "chain output", rel_elem=ACT_REL)
+
+
+def test_moe_swiglu_chain_matches_oracle(dev):
+    tokens, experts, h, i = 300, 4, 512, 256
+    say(f"moe swiglu chain tokens={tokens} experts={experts} hidden={h} intermediate={i}")
+    moe = synthetic.moe_case(tokens, experts, h, i, seed=610)
+    mats = [mlp_weights(620 + 30 * e, h, i, h) for e in range(experts)]
+    gu_bank = torch_ops.ExpertBank([dict(gate=g, up=u) for g, u, _ in mats], device=dev)
+    dn_bank = torch_ops.ExpertBank([d for _, _, d in mats], device=dev)
+    csr = wq.wq_csr_from_routes(moe["routes"], tokens, 2, experts)
+    a = torch_ops.to_device(moe["a"], dev)
+    act = torch_ops.grouped_gemm(a, gu_bank, csr)            # [pairs][i], pair-major
+    # the down projection reads pair rows: the same CSR with pair_tok = identity
+    n_pairs = 2 * tokens
+    ident = dict(csr)
+    ident["pair_tok"] = np.arange(n_pairs, dtype=np.int32)
+    wts = synthetic.routing_weights(611, tokens, 2)
+    out = host(torch_ops.grouped_gemm(act, dn_bank, ident,
+                                      topk_weights=torch_ops.to_device(wts, dev)))
+    ocsr = ref.csr_from_token_routes(experts, tokens, 2, moe["routes"])
+    act_want = np.full((n_pairs, i), np.nan)
+    for seg, e in enumerate(ocsr["ex_ids"]):
+        rows = [ocsr["ex_pairs"][j] for j in range(ocsr["ex_off"][seg], ocsr["ex_off"][seg + 1])]
+        toks = [ocsr["pair_tok"][p] for p in rows]
+        act_want[rows] = ref.swiglu_activation(moe["a"][toks], mats[e][0], mats[e][1])
+    assert_parity(host(act), act_want, "moe swiglu activation", rel_elem=ACT_REL)
+    act16 = ref.dequantize_fp16(act_want)
+    oid = dict(ocsr)
+    oid["pair_tok"] = list(range(n_pairs))
+    want = ref.grouped_w4a16_gemm(act16, [d for _, _, d in mats], oid, topk_weights=wts)
+    assert_parity(out, want, "moe swiglu chain output", rel_elem=ACT_REL)

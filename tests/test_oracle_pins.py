@@ -296,6 +296,54 @@ def test_act_order_with_256_row_groups_equals_plain_product():
     assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
 
 
+def test_silu_closed_forms():
+    e = np.e
+    got = ref.silu(np.array([0.0, 1.0, -1.0, 2.0]))
+    assert got[0] == 0.0
+    assert abs(got[1] - e / (1 + e)) < 1e-15 and abs(got[2] + 1 / (1 + e)) < 1e-15
+    assert abs(got[3] - 2 * e * e / (1 + e * e)) < 1e-15
+    x = np.linspace(-12, 12, 97)
+    assert np.allclose(ref.silu(x) - ref.silu(-x), x, rtol=0, atol=1e-13)  # x*(s(x)+s(-x))
+    assert np.all(ref.silu(np.array([40.0, 60.0])) == np.array([40.0, 60.0]))  # exp(-x) < ulp
+
+
+def test_swiglu_activation_by_brute_force():
+    """act[m][j] = silu(sum_k a*wg) * (sum_k a*wu), summed here by plain loops over codes
+    read from the hex digits of the words (ternary A, unit scales: exact integers)."""
+    k, n, m = 128, 16, 2
+    rng_a = synthetic.below(80, m * k, 3).reshape(m, k).astype(np.float64) - 1.0
+    a = rng_a.astype(np.float16)
+    gq, uq = synthetic.qweight_words(81, k, n), synthetic.qweight_words(82, k, n)
+    ones = np.ones((1, n), np.float16)
+    act = ref.swiglu_activation(a, dict(qweight=gq, scales=ones), dict(qweight=uq, scales=ones))
+    for i in range(m):
+        for j in range(n):
+            g = u = 0.0
+            for kk in range(k):
+                qg = int(f"{int(gq[kk // 8, j]):08x}"[7 - kk % 8], 16) - 8
+                qu = int(f"{int(uq[kk // 8, j]):08x}"[7 - kk % 8], 16) - 8
+                g += float(rng_a[i, kk]) * qg
+                u += float(rng_a[i, kk]) * qu
+            assert act[i, j] == g / (1.0 + np.exp(-g)) * u
+
+
+def test_gate_up_interleave_and_mlp_chain_shapes():
+    g = np.arange(4 * 32).reshape(4, 32)
+    u = 1000 + np.arange(4 * 32).reshape(4, 32)
+    out = layout.interleave_gate_up(g, u)
+    assert out.shape == (4, 64)
+    assert out[0, :16].tolist() == g[0, :16].tolist() and out[0, 16:32].tolist() == u[0, :16].tolist()
+    assert out[3, 32:48].tolist() == g[3, 16:32].tolist() and out[3, 48:].tolist() == u[3, 16:32].tolist()
+    z = layout.interleave_gate_up(g[:, :4], u[:, :4], cols_per_elem=8)  # 2 words per block
+    assert z[1].tolist() == [g[1, 0], g[1, 1], u[1, 0], u[1, 1], g[1, 2], g[1, 3], u[1, 2], u[1, 3]]
+    k, h, i, m = 256, 256, 128, 3
+    a = synthetic.activations(84, m, k)
+    mk = lambda s, kk, nn: dict(qweight=synthetic.qweight_words(s, kk, nn),
+                                scales=synthetic.scales(s + 1, kk // 128, nn))
+    act16, out = ref.swiglu_mlp(a, mk(85, k, i), mk(87, k, i), mk(89, i, h))
+    assert act16.dtype == np.float16 and act16.shape == (m, i) and out.shape == (m, h)
+
+
 def test_routing_weights_scale_each_pair_row():
     """Row p is the dense product of its token row and expert times topk_weights[p]: the
     weights follow pair order, not CSR position or token; unit weights change nothing."""
@@ -320,6 +368,16 @@ def test_routing_weights_scale_each_pair_row():
 
 
 # --------------------------------------------------------------------------- checker
+
+def test_checker_element_allowance():
+    r = np.ones((50, 50))
+    r[0, 0] = 40.0           # rms 1.28: the bound is 3.6e-3; 2^-10 * 40 = 0.039
+    c = r.copy()
+    c[0, 0] += 0.03
+    assert not ref.check(c, r)["ok"] and ref.check(c, r, rel_elem=2.0 ** -10)["ok"]
+    c[0, 0] = 40.0 + 0.045   # beyond the allowance plus the bound
+    assert not ref.check(c, r, rel_elem=2.0 ** -10)["ok"]
+
 
 def test_checker_accepts_exact_and_rejects_large_error_and_nan():
     r = np.linspace(-3, 3, 64).reshape(8, 8)

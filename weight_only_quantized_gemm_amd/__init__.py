@@ -23,6 +23,7 @@ WQ_FLAG_HAS_ZP = 1 << 3
 WQ_FLAG_ATOMIC_ADD = 1 << 4
 WQ_FLAG_FP32_REDUCE = 1 << 5
 WQ_FLAG_MUL_TOPK_WEIGHTS = 1 << 6
+WQ_FLAG_SWIGLU = 1 << 7
 
 WQ_STAGE_ARGS, WQ_STAGE_SHAPE, WQ_STAGE_DEVICE = 1, 2, 3
 WQ_STAGE_LAUNCH_CONFIG, WQ_STAGE_FUNC_ATTR, WQ_STAGE_LAUNCH = 4, 5, 6
@@ -33,7 +34,7 @@ EXPORTED = (
     "wq_abi_version", "wq_status_str", "wq_repack_b", "wq_repack_scales", "wq_repack_zeros",
     "wq_act_order_perm", "wq_gemm_workspace_bytes", "wq_gemm", "wq_dequant",
     "wq_csr_from_routes", "wq_grouped_workspace_bytes", "wq_grouped_gemm",
-    "wq_stream_read_sink_words", "wq_stream_read",
+    "wq_stream_read_sink_words", "wq_stream_read", "wq_interleave_gate_up",
 )
 
 
@@ -107,6 +108,7 @@ def lib() -> ctypes.CDLL:
             "wq_grouped_gemm": (ctypes.c_int, [ctypes.POINTER(wq_grouped_args)]),
             "wq_stream_read_sink_words": (ctypes.c_int, [sz, ctypes.POINTER(sz)]),
             "wq_stream_read": (ctypes.c_int, [vp, sz, vp, sz, vp]),
+            "wq_interleave_gate_up": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -259,3 +261,10 @@ def wq_stream_read(src, nbytes: int, sink, sink_words: int, stream=None) -> None
     """Measurement helper: one streaming read of `nbytes` at `src` (see include/wq.h)."""
     _check(lib().wq_stream_read(_ptr(src), nbytes, _ptr(sink), sink_words,
                                 _stream(stream, src)))
+
+
+def wq_interleave_gate_up(gate, up, out, rows: int, cols: int, bits_per_column: int,
+                          stream=None) -> None:
+    """Pair gate/up columns in 16-column blocks for WQ_FLAG_SWIGLU (see include/wq.h)."""
+    _check(lib().wq_interleave_gate_up(_ptr(gate), _ptr(up), _ptr(out), rows, cols,
+                                       bits_per_column, _stream(stream, out)))

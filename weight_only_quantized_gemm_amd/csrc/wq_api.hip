@@ -223,7 +223,7 @@ int wq_gemm(const wq_gemm_args* args) {
     return fail(WQ_STAGE_ARGS, WQ_ERR_ABI);
   const wq_gemm_args& p = *args;
   const uint32_t known = WQ_FLAG_ACT_ORDER | WQ_FLAG_IS_K_FULL | WQ_FLAG_HAS_ZP |
-                         WQ_FLAG_ATOMIC_ADD | WQ_FLAG_FP32_REDUCE;
+                         WQ_FLAG_ATOMIC_ADD | WQ_FLAG_FP32_REDUCE | WQ_FLAG_SWIGLU;
   if ((p.flags & ~known) || (p.flags & WQ_FLAG_ATOMIC_ADD)) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
   int st = check_kn(p.k, p.n, p.group_size);
   if (st) return st;
@@ -245,6 +245,19 @@ int wq_gemm(const wq_gemm_args* args) {
   }
   if (p.split_k < 0) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
   if (p.split_k > 1 && !(p.flags & WQ_FLAG_FP32_REDUCE)) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
+  const bool swiglu = (p.flags & WQ_FLAG_SWIGLU) != 0;
+
+  // Plan, and check the workspace the plan needs, before anything is enqueued.
+  wq::SmallPlan plan{};
+  const bool small = !swiglu && p.m <= 16 && plan_small(p.m, p.n, p.k, p.flags, p.split_k, &plan);
+  float* partials = nullptr;
+  if (small && plan.splits > 1) {
+    const size_t need = (size_t)plan.splits * p.m * p.n * sizeof(float);
+    if (p.workspace == nullptr || p.workspace_bytes < need)
+      return fail(WQ_STAGE_ARGS, WQ_ERR_WORKSPACE);
+    if (!aligned(p.workspace, 16)) return fail(WQ_STAGE_ARGS, WQ_ERR_ALIGN);
+    partials = static_cast<float*>(p.workspace);
+  }
 
   const hipStream_t stream = as_stream(p.stream);
   const uint16_t* a = static_cast<const uint16_t*>(p.a);
@@ -261,21 +274,12 @@ int wq_gemm(const wq_gemm_args* args) {
   const uint32_t* z = static_cast<const uint32_t*>(p.zero_points);
   uint16_t* c = static_cast<uint16_t*>(p.c);
 
-  wq::SmallPlan plan{};
-  if (p.m <= 16 && plan_small(p.m, p.n, p.k, p.flags, p.split_k, &plan)) {
-    float* partials = nullptr;
-    if (plan.splits > 1) {
-      const size_t need = (size_t)plan.splits * p.m * p.n * sizeof(float);
-      if (p.workspace == nullptr || p.workspace_bytes < need)
-        return fail(WQ_STAGE_ARGS, WQ_ERR_WORKSPACE);
-      if (!aligned(p.workspace, 16)) return fail(WQ_STAGE_ARGS, WQ_ERR_ALIGN);
-      partials = static_cast<float*>(p.workspace);
-    }
+  if (small) {
     const hipError_t e =
         wq::launch_gemm_small(a, lda, p.m, b, s, z, c, p.n, p.k, plan, partials, stream);
     return e == hipSuccess ? 0 : hip_fail(e);
   }
-  const hipError_t e = wq::launch_gemm_tile(a, lda, p.m, b, s, z, c, p.n, p.k, stream);
+  const hipError_t e = wq::launch_gemm_tile(a, lda, p.m, b, s, z, c, p.n, p.k, swiglu, stream);
   return e == hipSuccess ? 0 : hip_fail(e);
 }
 
@@ -345,7 +349,12 @@ int wq_grouped_gemm(const wq_grouped_args* args) {
       args->reserved != 0)
     return fail(WQ_STAGE_ARGS, WQ_ERR_ABI);
   const wq_grouped_args& p = *args;
-  if (p.flags & ~(uint32_t)(WQ_FLAG_HAS_ZP | WQ_FLAG_IS_K_FULL | WQ_FLAG_MUL_TOPK_WEIGHTS))
+  if (p.flags & ~(uint32_t)(WQ_FLAG_HAS_ZP | WQ_FLAG_IS_K_FULL | WQ_FLAG_MUL_TOPK_WEIGHTS |
+                            WQ_FLAG_SWIGLU))
+    return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
+  // The routing weight scales an expert's output, i.e. the down projection; the SwiGLU
+  // activation of the gate/up projection takes none.
+  if ((p.flags & WQ_FLAG_SWIGLU) && (p.flags & WQ_FLAG_MUL_TOPK_WEIGHTS))
     return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
   int st = check_kn(p.k, p.n, p.group_size);
   if (st) return st;
@@ -397,7 +406,23 @@ int wq_grouped_gemm(const wq_grouped_args* args) {
   g.n_tokens = p.n_tokens;
   g.k = p.k;
   g.n = p.n;
+  g.swiglu = (p.flags & WQ_FLAG_SWIGLU) != 0;
   const hipError_t e = wq::launch_grouped_tile(g, as_stream(p.stream));
+  return e == hipSuccess ? 0 : hip_fail(e);
+}
+
+int wq_interleave_gate_up(const void* gate, const void* up, void* out, int rows, int cols,
+                          int bits_per_column, void* stream) {
+  if (bits_per_column != 32 && bits_per_column != 16 && bits_per_column != 4)
+    return fail(WQ_STAGE_SHAPE, WQ_ERR_SHAPE);
+  if (rows <= 0 || cols <= 0 || cols % 16 != 0) return fail(WQ_STAGE_SHAPE, WQ_ERR_SHAPE);
+  if ((long long)rows * cols * bits_per_column / 8 * 2 > (1LL << 46))
+    return fail(WQ_STAGE_SHAPE, WQ_ERR_OVERFLOW);
+  int st;
+  if ((st = check_ptr(gate, 4)) || (st = check_ptr(up, 4)) || (st = check_ptr(out, 4)))
+    return st;
+  const hipError_t e = wq::launch_interleave_gate_up(gate, up, out, rows, cols,
+                                                     bits_per_column, as_stream(stream));
   return e == hipSuccess ? 0 : hip_fail(e);
 }
 

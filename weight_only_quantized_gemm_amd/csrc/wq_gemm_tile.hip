@@ -94,6 +94,7 @@ struct TileArgs {
   uint16_t* c;
   int n;
   int k;
+  int ldc;    // output row stride: n, or n / 2 for the SwiGLU epilogue
   int tiles;  // work-groups launched
   // grouped
   const uint8_t* b_bank;
@@ -125,7 +126,17 @@ struct Smem {
   int info[5];
 };
 
-template <bool ZP, bool GROUPED>
+// The SwiGLU epilogue: B holds a gate and an up projection with their 16-column blocks
+// paired (block 2t = gate columns 16t.., block 2t+1 = up columns 16t..), so in every 32x32
+// output block lane c (c < 16) holds gate column j and lane c + 16 up column j of the same
+// row.  The two lanes exchange their scaled sums (a lane swizzle, xor 16) and the gate lane
+// writes fp16(silu(g) * u) to column j of the [rows][n/2] activation: the gate and up
+// products never leave the registers.
+__device__ __forceinline__ float silu_times(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
+}
+
+template <bool ZP, bool GROUPED, bool SWIGLU>
 __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
   __shared__ Smem sm;
 
@@ -491,6 +502,29 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
   wait_vmcnt<0>();  // the trailing re-reads have landed before the work-group ends
 
   // Epilogue: lane holds rows 8*(r/4) + 4*h + (r%4) of column c32 in each 32x32 block.
+  if constexpr (SWIGLU) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      if (rb >= nrb) continue;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const long j = (n0 + 64 * wn + 32 * cb) / 2 + (c32 & 15);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 128 * wm + 32 * rb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const float mine = acc[rb][cb][r] * sigma[cb];
+          // ds_swizzle bit mode: and 0x1f, or 0, xor 0x10 (lanes l and l ^ 16 swap)
+          const float other = __builtin_bit_cast(
+              float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, mine), 0x401F));
+          const int orow = sm.row_c[row];
+          if (c32 < 16 && orow >= 0)
+            p.c[(long)orow * p.ldc + j] =
+                __builtin_bit_cast(uint16_t, (f16)silu_times(mine, other));
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     if (rb >= nrb) continue;
@@ -505,7 +539,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
         // is one rounding of acc * factor, as on the dense path.
         const float factor = GROUPED ? sigma[cb] * sm.row_w[row] : sigma[cb];
         if (orow >= 0)
-          p.c[(long)orow * p.n + col] = __builtin_bit_cast(uint16_t, (f16)(acc[rb][cb][r] * factor));
+          p.c[(long)orow * p.ldc + col] = __builtin_bit_cast(uint16_t, (f16)(acc[rb][cb][r] * factor));
       }
     }
   }
@@ -513,9 +547,20 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
 
 }  // namespace
 
+template <bool GROUPED, bool SWIGLU>
+hipError_t launch_tile_t(const TileArgs& p, bool zp, hipStream_t stream) {
+  if (zp)
+    hipLaunchKernelGGL((gemm_tile_kernel<true, GROUPED, SWIGLU>), dim3((unsigned)p.tiles),
+                       dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((gemm_tile_kernel<false, GROUPED, SWIGLU>), dim3((unsigned)p.tiles),
+                       dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b,
                             const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
-                            hipStream_t stream) {
+                            bool swiglu, hipStream_t stream) {
   TileArgs p{};
   p.a = a;
   p.lda = lda;
@@ -526,12 +571,10 @@ hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b
   p.c = c;
   p.n = n;
   p.k = k;
+  p.ldc = swiglu ? n / 2 : n;
   p.tiles = (n / TN) * ((m + TM - 1) / TM);
-  if (z != nullptr)
-    hipLaunchKernelGGL((gemm_tile_kernel<true, false>), dim3(p.tiles), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((gemm_tile_kernel<false, false>), dim3(p.tiles), dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+  return swiglu ? launch_tile_t<false, true>(p, z != nullptr, stream)
+                : launch_tile_t<false, false>(p, z != nullptr, stream);
 }
 
 hipError_t launch_grouped_tile(const GroupedProblem& g, hipStream_t stream) {
@@ -567,13 +610,9 @@ hipError_t launch_grouped_tile(const GroupedProblem& g, hipStream_t stream) {
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7fffffffL) return hipErrorInvalidConfiguration;
   p.tiles = (int)tiles;
-  if (g.z_bank != nullptr)
-    hipLaunchKernelGGL((gemm_tile_kernel<true, true>), dim3((unsigned)tiles), dim3(kThreads), 0,
-                       stream, p);
-  else
-    hipLaunchKernelGGL((gemm_tile_kernel<false, true>), dim3((unsigned)tiles), dim3(kThreads), 0,
-                       stream, p);
-  return hipGetLastError();
+  p.ldc = g.swiglu ? g.n / 2 : g.n;
+  return g.swiglu ? launch_tile_t<true, true>(p, g.z_bank != nullptr, stream)
+                  : launch_tile_t<true, false>(p, g.z_bank != nullptr, stream);
 }
 
 }  // namespace wq

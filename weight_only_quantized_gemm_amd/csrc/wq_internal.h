@@ -16,6 +16,9 @@ hipError_t launch_repack_scales(const uint16_t* s, uint16_t* out, int k, int n,
                                 int group_size, hipStream_t stream);
 hipError_t launch_repack_zeros(const uint32_t* z, uint32_t* out, int k, int n, int group_size,
                                hipStream_t stream);
+// Gate/up column pairing for the SwiGLU epilogue (bits_per_column 32, 16 or 4).
+hipError_t launch_interleave_gate_up(const void* gate, const void* up, void* out, int rows,
+                                     int cols, int bits_per_column, hipStream_t stream);
 hipError_t launch_dequant(const uint32_t* b, const uint16_t* s, const uint32_t* z, int k, int n,
                           uint16_t* w, hipStream_t stream);
 hipError_t launch_gather_columns(const uint16_t* a, int lda, const int32_t* perm, uint16_t* out,
@@ -37,9 +40,10 @@ hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* 
 // Tiled kernel (wq_gemm_tile.hip): 256 x 256 output tiles on 8 waves of 128 x 64.
 constexpr int kTileM = 256;
 constexpr int kTileN = 256;
+// swiglu: B pairs gate/up 16-column blocks and c is the [m][n/2] activation.
 hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b,
                             const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
-                            hipStream_t stream);
+                            bool swiglu, hipStream_t stream);
 
 struct GroupedProblem {
   const uint16_t* a;
@@ -56,6 +60,7 @@ struct GroupedProblem {
   const float* topk_w;    // may be null: no routing-weight multiply
   uint16_t* y;
   int n_expert, n_active, n_pairs, n_tokens, k, n;
+  bool swiglu;            // SwiGLU epilogue: y is [n_pairs][n/2]
 };
 hipError_t launch_grouped_tile(const GroupedProblem& p, hipStream_t stream);
 

@@ -210,6 +210,22 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
   }
 }
 
+// Pair two row-major tensors' columns in 16-column blocks (gate block t, then up block t)
+// for the fused gate/up projection.  Words of 4 bytes; `block_words` words per 16 columns.
+__global__ __launch_bounds__(256) void interleave_gate_up_kernel(
+    const uint32_t* __restrict__ gate, const uint32_t* __restrict__ up,
+    uint32_t* __restrict__ out, long rows, long row_words, int block_words) {
+  const long total = rows * 2 * row_words;
+  for (long o = (long)blockIdx.x * blockDim.x + threadIdx.x; o < total;
+       o += (long)gridDim.x * blockDim.x) {
+    const long r = o / (2 * row_words);
+    const long w = o - r * 2 * row_words;
+    const long blk = w / block_words;
+    const long src = (blk >> 1) * block_words + (w - blk * block_words);
+    out[o] = ((blk & 1) ? up : gate)[r * row_words + src];
+  }
+}
+
 int grid_for(long work) {
   long blocks = (work + 255) / 256;
   if (blocks > 65536) blocks = 65536;
@@ -238,6 +254,17 @@ hipError_t launch_repack_zeros(const uint32_t* z, uint32_t* out, int k, int n, i
   const int chunks_per_group = group_size > 0 ? group_size / kGroup : 0;
   hipLaunchKernelGGL(repack_zeros_kernel, dim3(grid_for((long)(k / kGroup) * (n / 8))),
                      dim3(256), 0, stream, z, out, k, n, chunks_per_group);
+  return hipGetLastError();
+}
+
+hipError_t launch_interleave_gate_up(const void* gate, const void* up, void* out, int rows,
+                                     int cols, int bits_per_column, hipStream_t stream) {
+  const long row_words = (long)cols * bits_per_column / 32;
+  const int block_words = 16 * bits_per_column / 32;
+  hipLaunchKernelGGL(interleave_gate_up_kernel, dim3(grid_for((long)rows * 2 * row_words)),
+                     dim3(256), 0, stream, static_cast<const uint32_t*>(gate),
+                     static_cast<const uint32_t*>(up), static_cast<uint32_t*>(out), (long)rows,
+                     row_words, block_words);
   return hipGetLastError();
 }
 

@@ -10,7 +10,7 @@ import numpy as np
 import torch
 
 from . import (WQ_FLAG_ACT_ORDER, WQ_FLAG_FP32_REDUCE, WQ_FLAG_HAS_ZP, WQ_FLAG_MUL_TOPK_WEIGHTS,
-               wq_act_order_perm,
+               WQ_FLAG_SWIGLU, wq_act_order_perm, wq_interleave_gate_up,
                wq_gemm, wq_gemm_workspace_bytes, wq_grouped_gemm, wq_repack_b,
                wq_repack_scales, wq_repack_zeros)
 
@@ -18,7 +18,9 @@ GROUP = 128
 
 
 def to_device(x: np.ndarray, device) -> torch.Tensor:
-    """Upload a numpy array; uint32 words travel as int32 (same bits)."""
+    """Upload a numpy array (a tensor is moved as it is); uint32 words travel as int32."""
+    if isinstance(x, torch.Tensor):
+        return x.to(device)
     x = np.ascontiguousarray(x)
     if x.dtype == np.uint32:
         x = x.view(np.int32)
@@ -33,6 +35,7 @@ class PackedWeight:
         self.k = qweight.shape[0] * 8
         self.n = qweight.shape[1]
         self.group_size = group_size
+        self.swiglu = False
         self.device = torch.device(device)
         self.perm = None
         if g_idx is not None:
@@ -41,7 +44,8 @@ class PackedWeight:
         qw = to_device(qweight, self.device)
         self.b = torch.empty(self.k * self.n // 8, dtype=torch.int32, device=self.device)
         wq_repack_b(qw, self.b, self.k, self.n, perm=self.perm)
-        sc = to_device(np.asarray(scales, dtype=np.float16), self.device)
+        sc = to_device(scales if isinstance(scales, torch.Tensor)
+                       else np.asarray(scales, dtype=np.float16), self.device)
         self.s = torch.empty((self.k // GROUP) * self.n, dtype=torch.float16, device=self.device)
         wq_repack_scales(sc, self.s, self.k, self.n, group_size)
         self.z = None
@@ -51,6 +55,27 @@ class PackedWeight:
                                  device=self.device)
             wq_repack_zeros(zw, self.z, self.k, self.n, group_size)
         torch.cuda.synchronize(self.device)
+
+    @classmethod
+    def gate_up(cls, gate: dict, up: dict, device="cuda", group_size: int = GROUP,
+                g_idx: np.ndarray | None = None) -> "PackedWeight":
+        """One weight of 2*I columns for the SwiGLU epilogue: the gate and up projections'
+        qweight, scales and zero points paired in 16-column blocks on the device
+        (wq_interleave_gate_up), then repacked like any weight."""
+        dev = torch.device(device)
+        i = gate["qweight"].shape[1]
+
+        def pair(key, bits):
+            g, u = to_device(gate[key], dev), to_device(up[key], dev)
+            out = torch.empty((g.shape[0], 2 * g.shape[1]), dtype=g.dtype, device=dev)
+            wq_interleave_gate_up(g, u, out, g.shape[0], i, bits)
+            return out
+
+        zeros = pair("zeros", 4) if gate.get("zeros") is not None else None
+        w = cls(pair("qweight", 32), pair("scales", 16), zeros, g_idx, device=dev,
+                group_size=group_size)
+        w.swiglu = True
+        return w
 
     def clone(self) -> "PackedWeight":
         """A second copy of the device buffers (same values, new memory)."""
@@ -69,6 +94,8 @@ class PackedWeight:
             f |= WQ_FLAG_ACT_ORDER
         if fp32_reduce:
             f |= WQ_FLAG_FP32_REDUCE
+        if self.swiglu:
+            f |= WQ_FLAG_SWIGLU
         return f
 
 
@@ -87,10 +114,12 @@ class GemmBuffers:
 def gemm(a: torch.Tensor, w: PackedWeight, out: torch.Tensor | None = None, *,
          fp32_reduce: bool = False, split_k: int = 0, buffers: GemmBuffers | None = None,
          stream=None) -> torch.Tensor:
-    """C = A @ dequant(B) through wq_gemm (A fp16 [m][k], row stride a.stride(0))."""
+    """C = A @ dequant(B) through wq_gemm (A fp16 [m][k], row stride a.stride(0)); for a
+    gate/up weight, the [m][n/2] SwiGLU activation."""
     m = a.shape[0]
     if out is None:
-        out = torch.empty((m, w.n), dtype=torch.float16, device=a.device)
+        cols = w.n // 2 if w.swiglu else w.n
+        out = torch.empty((m, cols), dtype=torch.float16, device=a.device)
     if buffers is None:
         buffers = GemmBuffers(w, m, fp32_reduce)
     wq_gemm(a, w.b, out, w.s, m=m, n=w.n, k=w.k, zero_points=w.z, perm=w.perm,
@@ -103,11 +132,17 @@ class ExpertBank:
     """Repacked weights of several experts stored back to back (one stride per tensor)."""
 
     def __init__(self, experts: list[dict], device="cuda"):
-        self.packed = [PackedWeight(e["qweight"], e["scales"], e.get("zeros"), device=device,
-                                    group_size=e.get("group_size", GROUP))
-                       for e in experts]
+        """Each expert is a weight dict (qweight, scales, optional zeros and group_size), or
+        {"gate": ..., "up": ...} for a fused gate/up projection with the SwiGLU epilogue."""
+        def pack(e):
+            gs = e.get("group_size", GROUP)
+            if "gate" in e:
+                return PackedWeight.gate_up(e["gate"], e["up"], device=device, group_size=gs)
+            return PackedWeight(e["qweight"], e["scales"], e.get("zeros"), device=device,
+                                group_size=gs)
+        self.packed = [pack(e) for e in experts]
         p0 = self.packed[0]
-        self.k, self.n, self.group_size = p0.k, p0.n, p0.group_size
+        self.k, self.n, self.group_size, self.swiglu = p0.k, p0.n, p0.group_size, p0.swiglu
         self.b = torch.stack([p.b for p in self.packed])
         self.s = torch.stack([p.s for p in self.packed])
         self.z = torch.stack([p.z for p in self.packed]) if p0.z is not None else None
@@ -128,7 +163,8 @@ def grouped_gemm(a: torch.Tensor, bank: ExpertBank, csr: dict, out: torch.Tensor
                       for key in ("ex_ids", "ex_off", "ex_pairs", "pair_tok")}
     n_pairs = len(csr["ex_pairs"])
     if out is None:
-        out = torch.empty((n_pairs, bank.n), dtype=torch.float16, device=a.device)
+        cols = bank.n // 2 if bank.swiglu else bank.n
+        out = torch.empty((n_pairs, cols), dtype=torch.float16, device=a.device)
     wq_grouped_gemm(a, bank.b, bank.b_stride, bank.s, bank.s_stride, device_csr["ex_ids"],
                     device_csr["ex_off"], device_csr["ex_pairs"], device_csr["pair_tok"], out,
                     n_expert=bank.n_expert, n_active=len(csr["ex_ids"]), n_pairs=n_pairs,
@@ -136,6 +172,7 @@ def grouped_gemm(a: torch.Tensor, bank: ExpertBank, csr: dict, out: torch.Tensor
                     zp_stride_bytes=bank.z_stride, topk_weights=topk_weights,
                     group_size=bank.group_size,
                     flags=(WQ_FLAG_HAS_ZP if bank.z is not None else 0)
-                    | (WQ_FLAG_MUL_TOPK_WEIGHTS if topk_weights is not None else 0),
+                    | (WQ_FLAG_MUL_TOPK_WEIGHTS if topk_weights is not None else 0)
+                    | (WQ_FLAG_SWIGLU if bank.swiglu else 0),
                     stream=stream)
     return out

@@ -21,10 +21,11 @@
  *  - Validation happens before any launch (fail closed); nothing is enqueued on error.
  *  - Shapes: k % 128 == 0, n % 256 == 0.  group_size (rows of K per scale / zero point) is
  *    -1 (channelwise: one group over all of K, as transformer.rs `marlin_num_groups` maps
- *    it) or a multiple of 128 dividing k.  The pages also allow the other positive
+ *    it), 32, 64, or a multiple of 128 dividing k.  The pages also allow the other positive
  *    multiples of 16 dividing k; those fail with WQ_ERR_SHAPE.  The library stores scales
- *    and zero points per 128-row chunk, so the GEMM calls read the same layout for every
- *    supported group_size.
+ *    and zero points per unit of U = min(group_size, 128) rows (U = 128 for -1): a larger
+ *    group is repeated for each 128-row chunk it covers.  Groups of 32 or 64 rows use the
+ *    tiled kernel at every m.
  *
  * Library weight layout (produced by the wq_repack_* calls; G = k / 128):
  *  - B: k*n/8 uint32 words (k*n/2 bytes, the plain format's byte count).  For 16-column
@@ -32,7 +33,7 @@
  *    dword j = 0..3, word ((nb*G + g)*64 + l)*4 + j holds rows 128*g + 32*j + 8*qd + i
  *    (i = 0..7) of column 16*nb + c; row offset i sits in nibble slot {0,4,1,5,2,6,3,7}[i].
  *    One 16-byte load per lane then feeds four 16x16x32 fp16 MFMA B operands of a wave.
- *  - scales: fp16 [n/16][G][16]; zero points: uint32 [n/16][G][2] (16 codes per pair,
+ *  - scales: fp16 [n/16][k/U][16]; zero points: uint32 [n/16][k/U][2] (16 codes per pair,
  *    column c of the block in bits 4*(c%8) of word c/8).
  *  - act_order: B rows are stored in sorted order (row position i holds original row
  *    perm[i]); sorted position i belongs to group i / 128 (see wq_act_order_perm).
@@ -111,7 +112,7 @@ int wq_repack_b(const uint32_t* qweight, const int32_t* perm, void* b_out, int k
 
 /*
  * Scales fp16 [k/group_size][n] row-major ([1][n] for group_size -1) -> library layout
- * fp16 [n/16][G][16]: chunk g takes the scales of the group holding its rows.
+ * fp16 [n/16][k/U][16]: unit u takes the scales of the group holding its rows.
  */
 int wq_repack_scales(const void* scales, void* s_out, int k, int n, int group_size,
                      void* stream);
@@ -119,7 +120,7 @@ int wq_repack_scales(const void* scales, void* s_out, int k, int n, int group_si
 /*
  * Zero points uint32 [k/group_size][n/8] (actual codes 0..15, column 8j+i in bits 4i of
  * word j: vllm_marlin.rs `repack_gptq_qzeros_to_marlin`; [1][n/8] for group_size -1) ->
- * library layout [n/16][G][2], chunk g taking the codes of the group holding its rows.
+ * library layout [n/16][k/U][2], unit u taking the codes of the group holding its rows.
  */
 int wq_repack_zeros(const uint32_t* zeros, void* z_out, int k, int n, int group_size,
                     void* stream);
@@ -167,7 +168,7 @@ typedef struct wq_gemm_args {
   void* stream;             /* hipStream_t                                              */
   int32_t m, n, k;          /* m >= 1, n % 256 == 0, k % 128 == 0                        */
   int32_t lda;              /* row stride of a in elements, >= k, multiple of 8         */
-  int32_t group_size;       /* as repacked: -1 or a multiple of 128 dividing k          */
+  int32_t group_size;       /* as repacked: -1, 32, 64 or a multiple of 128 dividing k  */
   uint32_t flags;           /* WQ_FLAG_*; HAS_ZP iff zero_points != NULL; ACT_ORDER iff perm */
   int32_t split_k;          /* 0 = library's choice; 1 = no split; s > 1 requests s splits
                                along K for m <= 16 (needs WQ_FLAG_FP32_REDUCE; clamped to

@@ -92,11 +92,12 @@ def interleave_gate_up(gate: np.ndarray, up: np.ndarray, cols_per_elem: int = 1)
 
 
 def chunk_rows(values: np.ndarray, k: int | None, group_size: int) -> np.ndarray:
-    """Per-group rows [K/group_size][...] -> one row per 128-row chunk of K: chunk g takes
-    the row of the group holding rows 128g..128g+127 (the single row when channelwise)."""
+    """Per-group rows [K/group_size][...] -> the library's scale rows: one per group for
+    groups of fewer than 128 rows, else one per 128-row chunk of K, chunk g taking the row
+    of the group holding rows 128g..128g+127 (the single row when channelwise)."""
     v = np.asarray(values)
-    if k is None or group_size == CHUNK:
-        return v
+    if k is None or group_size == CHUNK or 0 < group_size < CHUNK:
+        return v  # one stored row per group (groups below 128 rows are stored as they are)
     chunks = k // CHUNK
     src = np.zeros(chunks, dtype=np.int64) if group_size == -1 else \
         (np.arange(chunks) * CHUNK) // group_size
@@ -104,7 +105,7 @@ def chunk_rows(values: np.ndarray, k: int | None, group_size: int) -> np.ndarray
 
 
 def repack_scales(scales: np.ndarray, k: int | None = None, group_size: int = 128) -> np.ndarray:
-    """fp16 [K/group_size][N] -> fp16 [N/16][K/128][16] (flattened)."""
+    """fp16 [K/group_size][N] -> fp16 [N/16][K/U][16] (flattened), U = min(group_size, 128)."""
     s = chunk_rows(np.asarray(scales, dtype=np.float16), k, group_size)
     groups, n_total = s.shape
     return s.reshape(groups, n_total // 16, 16).transpose(1, 0, 2).reshape(-1).copy()
@@ -112,7 +113,7 @@ def repack_scales(scales: np.ndarray, k: int | None = None, group_size: int = 12
 
 def repack_zero_points(zeros: np.ndarray, k: int | None = None,
                        group_size: int = 128) -> np.ndarray:
-    """uint32 [K/group_size][N/8] -> uint32 [N/16][K/128][2] (flattened)."""
+    """uint32 [K/group_size][N/8] -> uint32 [N/16][K/U][2] (flattened)."""
     z = chunk_rows(np.asarray(zeros, dtype=np.uint32), k, group_size)
     groups, n8 = z.shape
     return z.reshape(groups, n8 // 2, 2).transpose(1, 0, 2).reshape(-1).copy()

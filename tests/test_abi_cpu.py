@@ -86,8 +86,10 @@ def call_gemm(L, **over):
     (dict(m=0), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
     (dict(lda=512), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
     (dict(lda=1028), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
-    # group sizes: -1 and multiples of 128 dividing k are supported; others are not
-    (dict(group_size=64), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
+    # group sizes: -1, 32, 64 and multiples of 128 dividing k are supported; others are not
+    (dict(group_size=16), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
+    (dict(group_size=48), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
+    (dict(group_size=96), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
     (dict(group_size=192), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
     (dict(group_size=2048), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),   # does not divide k
     (dict(group_size=-2), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
@@ -137,7 +139,7 @@ def test_repack_and_dequant_validation(L):
                                                                          wq.WQ_ERR_SHAPE)
     assert L.wq_repack_b(0x1000, 0x3002, 0x2000, 1024, 256, None) == status(STAGE_ARGS,
                                                                            wq.WQ_ERR_ALIGN)
-    assert L.wq_repack_scales(0x1000, 0x2000, 1024, 256, 64, None) == status(STAGE_SHAPE,
+    assert L.wq_repack_scales(0x1000, 0x2000, 1024, 256, 48, None) == status(STAGE_SHAPE,
                                                                             wq.WQ_ERR_SHAPE)
     assert L.wq_repack_zeros(0x1000, None, 1024, 256, 128, None) == status(STAGE_ARGS,
                                                                           wq.WQ_ERR_NULL)
@@ -175,8 +177,9 @@ def test_interleave_gate_up_validation(L):
 
 
 def test_repack_validation_of_group_sizes(L):
-    # k = 1024: 256 and 1024 divide it, 768 does not; -1 is channelwise
-    for gs in (64, 768, -2, 0):
+    # k = 1024: 256 and 1024 divide it, 768 does not; -1 is channelwise; 32 and 64 are kept
+    # at their own granularity; other multiples of 16 are not supported
+    for gs in (16, 48, 768, -2, 0):
         assert L.wq_repack_scales(0x1000, 0x2000, 1024, 256, gs, None) == status(
             STAGE_SHAPE, wq.WQ_ERR_SHAPE), gs
         assert L.wq_repack_zeros(0x1000, 0x2000, 1024, 256, gs, None) == status(

@@ -155,6 +155,12 @@ def test_act_order_gather_widths(dev, m, k):
 # points the repack repeats per 128-row chunk, on both kernels, with zp and act_order.
 GROUP_SHAPES = [
     # m, k, n, group_size, zp, act_order
+    (1, 1024, 512, 32, True, False),
+    (16, 512, 256, 64, False, False),
+    (300, 1024, 512, 32, False, True),
+    (513, 512, 256, 64, True, False),
+    (64, 768, 512, 64, False, True),
+    (130, 1024, 256, 32, True, False),
     (1, 1024, 512, -1, False, False),
     (16, 2048, 256, 256, True, False),
     (7, 1024, 512, 512, False, True),
@@ -174,7 +180,7 @@ def test_group_sizes_match_oracle(dev, m, k, n, gs, zp, act_order):
     assert_parity(c, oracle_gemm(case), label)
 
 
-@pytest.mark.parametrize("gs", [-1, 256, 1024])
+@pytest.mark.parametrize("gs", [-1, 32, 64, 256, 1024])
 def test_group_size_repack_and_dequant_bitwise(dev, gs):
     k, n = 1024, 512
     say(f"repack/dequant group_size={gs}")
@@ -324,13 +330,15 @@ def test_grouped_matches_oracle(dev, tokens, experts, k, n, zp, weighted):
     assert_parity(y, ref.grouped_w4a16_gemm(moe["a"], ex, ocsr, topk_weights=w), label)
 
 
-def test_grouped_with_256_row_groups(dev):
-    tokens, experts, k, n, gs = 120, 3, 1024, 256, 256
+@pytest.mark.parametrize("gs", [256, 64, 32])
+def test_grouped_with_other_group_sizes(dev, gs):
+    tokens, experts, k, n = 120, 3, 1024, 256
     moe = synthetic.moe_case(tokens, experts, k, n, group_size=gs, seed=24)
     for e in moe["experts"]:
         e["group_size"] = gs
     y, ex, ocsr = run_grouped(moe, dev)
-    assert_parity(y, ref.grouped_w4a16_gemm(moe["a"], ex, ocsr, group_size=gs), "grouped gs=256")
+    assert_parity(y, ref.grouped_w4a16_gemm(moe["a"], ex, ocsr, group_size=gs),
+                  f"grouped gs={gs}")
 
 
 def test_grouped_unit_weights_change_nothing(dev):
@@ -469,19 +477,20 @@ def test_interleave_gate_up_bitwise(dev, bits, rows, cols):
     assert np.array_equal(host(out).view(np.uint32), want.reshape(rows, 2 * words))
 
 
-@pytest.mark.parametrize("m,k,i,zp,act_order", [(1, 1024, 256, False, False),
-                                                 (16, 512, 512, True, False),
-                                                 (300, 1024, 256, False, True),
-                                                 (513, 256, 384, True, False)])
-def test_swiglu_activation_matches_oracle(dev, m, k, i, zp, act_order):
-    label = f"swiglu m={m} k={k} i={i} zp={zp} act_order={act_order}"
+@pytest.mark.parametrize("m,k,i,zp,act_order,gs", [(1, 1024, 256, False, False, 128),
+                                                    (16, 512, 512, True, False, 128),
+                                                    (300, 1024, 256, False, True, 128),
+                                                    (513, 256, 384, True, False, 128),
+                                                    (100, 512, 256, True, False, 32)])
+def test_swiglu_activation_matches_oracle(dev, m, k, i, zp, act_order, gs):
+    label = f"swiglu m={m} k={k} i={i} zp={zp} act_order={act_order} group_size={gs}"
     say(label)
-    gate, up, _ = mlp_weights(500 + m, k, i, zp=zp)
+    gate, up, _ = mlp_weights(500 + m, k, i, zp=zp, group_size=gs)
     a = synthetic.activations(501 + m, m, k)
     g_idx = synthetic.act_order_g_idx(502, k, 128) if act_order else None
     if act_order:
         gate["g_idx"] = up["g_idx"] = g_idx
-    w = torch_ops.PackedWeight.gate_up(gate, up, device=dev, g_idx=g_idx)
+    w = torch_ops.PackedWeight.gate_up(gate, up, device=dev, g_idx=g_idx, group_size=gs)
     act = host(torch_ops.gemm(torch_ops.to_device(a, dev), w))
     torch.cuda.synchronize()
     if act_order:  # the oracle reads g_idx through its own argument
@@ -489,7 +498,7 @@ def test_swiglu_activation_matches_oracle(dev, m, k, i, zp, act_order):
         u = ref.w4a16_gemm(a, up["qweight"], up["scales"], zeros=up.get("zeros"), g_idx=g_idx)
         want = ref.silu(g) * u
     else:
-        want = ref.swiglu_activation(a, gate, up)
+        want = ref.swiglu_activation(a, gate, up, group_size=gs)
     assert act.shape == (m, i)
     assert_parity(act, want, label, rel_elem=ACT_REL)
 

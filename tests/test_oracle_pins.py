@@ -275,6 +275,14 @@ def test_larger_and_channelwise_groups_equal_repeated_128_row_groups():
                               layout.repack_scales(np.repeat(s, rep, axis=0)))
         assert np.array_equal(layout.repack_zero_points(z, k, gs),
                               layout.repack_zero_points(np.repeat(z, rep, axis=0)))
+    # groups of 64 rows equal groups of 32 rows repeating each scale and zero point twice
+    s = synthetic.scales(64, k // 64, n)
+    z = synthetic.zero_point_words(65, k // 64, n)
+    got = ref.w4a16_gemm(a, qw, s, zeros=z, group_size=64)
+    want = ref.w4a16_gemm(a, qw, np.repeat(s, 2, axis=0), zeros=np.repeat(z, 2, axis=0),
+                          group_size=32)
+    assert got.tolist() == want.tolist()
+    assert ref.group_of_rows(256, 32)[[31, 32, 63, 64]].tolist() == [0, 1, 1, 2]
     # with 256-row groups, row 128 is in group 0 and row 256 in group 1
     assert ref.group_of_rows(1024, 256)[[127, 128, 255, 256]].tolist() == [0, 0, 0, 1]
     assert ref.group_of_rows(1024, -1).max() == 0

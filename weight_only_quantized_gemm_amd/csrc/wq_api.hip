@@ -29,14 +29,18 @@ int check_ptr(const void* p, size_t align) {
   return 0;
 }
 
-// Group sizes the library stores per 128-row chunk: -1 (one group over K, channelwise, as
-// transformer.rs `marlin_num_groups` maps it to one group) or a multiple of 128 dividing K
-// (its scales are repeated for each chunk it covers).  The pages also allow the other
-// positive multiples of 16 dividing K; those are rejected here.
+// Supported group sizes: -1 (one group over K, channelwise, as transformer.rs
+// `marlin_num_groups` maps it to one group), 32 and 64 (2 or 4 scale sub-groups per 128
+// rows, tiled kernel), or a multiple of 128 dividing K (its scales repeated for each
+// 128-row chunk it covers).  The pages also allow the other positive multiples of 16
+// dividing K; those are rejected here.
 bool chunk_group_size(int k, int group_size) {
-  if (group_size == -1) return true;
+  if (group_size == -1 || group_size == 32 || group_size == 64) return true;
   return group_size > 0 && group_size % kGroupSize == 0 && k % group_size == 0;
 }
+
+// Scale sub-groups per 128 rows of K.
+int subgroups(int group_size) { return group_size == 32 ? 4 : group_size == 64 ? 2 : 1; }
 
 // k % 128 == 0, n % 256 == 0, a supported group_size, and byte extents that fit.
 int check_kn(int k, int n, int group_size) {
@@ -247,9 +251,12 @@ int wq_gemm(const wq_gemm_args* args) {
   if (p.split_k > 1 && !(p.flags & WQ_FLAG_FP32_REDUCE)) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
   const bool swiglu = (p.flags & WQ_FLAG_SWIGLU) != 0;
 
-  // Plan, and check the workspace the plan needs, before anything is enqueued.
+  // Plan, and check the workspace the plan needs, before anything is enqueued.  The small-M
+  // kernel reads one scale per 128 rows, so smaller groups take the tiled kernel.
+  const int gpc = subgroups(p.group_size);
   wq::SmallPlan plan{};
-  const bool small = !swiglu && p.m <= 16 && plan_small(p.m, p.n, p.k, p.flags, p.split_k, &plan);
+  const bool small = !swiglu && gpc == 1 && p.m <= 16 &&
+                     plan_small(p.m, p.n, p.k, p.flags, p.split_k, &plan);
   float* partials = nullptr;
   if (small && plan.splits > 1) {
     const size_t need = (size_t)plan.splits * p.m * p.n * sizeof(float);
@@ -279,7 +286,8 @@ int wq_gemm(const wq_gemm_args* args) {
         wq::launch_gemm_small(a, lda, p.m, b, s, z, c, p.n, p.k, plan, partials, stream);
     return e == hipSuccess ? 0 : hip_fail(e);
   }
-  const hipError_t e = wq::launch_gemm_tile(a, lda, p.m, b, s, z, c, p.n, p.k, swiglu, stream);
+  const hipError_t e =
+      wq::launch_gemm_tile(a, lda, p.m, b, s, z, c, p.n, p.k, swiglu, gpc, stream);
   return e == hipSuccess ? 0 : hip_fail(e);
 }
 
@@ -294,8 +302,8 @@ int wq_dequant(const void* b, const void* b_scales, const void* zero_points, int
   if (has_zp && (st = check_ptr(zero_points, 16))) return st;
   const hipError_t e = wq::launch_dequant(
       static_cast<const uint32_t*>(b), static_cast<const uint16_t*>(b_scales),
-      static_cast<const uint32_t*>(zero_points), k, n, static_cast<uint16_t*>(w_out),
-      as_stream(stream));
+      static_cast<const uint32_t*>(zero_points), k, n, wq::scale_unit_rows(k, group_size),
+      static_cast<uint16_t*>(w_out), as_stream(stream));
   return e == hipSuccess ? 0 : hip_fail(e);
 }
 
@@ -373,7 +381,7 @@ int wq_grouped_gemm(const wq_grouped_args* args) {
   const bool mul_w = (p.flags & WQ_FLAG_MUL_TOPK_WEIGHTS) != 0;
   if (mul_w != (p.topk_weights != nullptr)) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
   if (mul_w && !aligned(p.topk_weights, 4)) return fail(WQ_STAGE_ARGS, WQ_ERR_ALIGN);
-  const size_t groups = (size_t)(p.k / kGroupSize);
+  const size_t groups = (size_t)(p.k / wq::scale_unit_rows(p.k, p.group_size));  // scale rows
   const size_t b_bytes = (size_t)p.k * p.n / 2;
   const size_t s_bytes = groups * p.n * 2;
   const size_t z_bytes = groups * p.n / 2;
@@ -407,6 +415,7 @@ int wq_grouped_gemm(const wq_grouped_args* args) {
   g.k = p.k;
   g.n = p.n;
   g.swiglu = (p.flags & WQ_FLAG_SWIGLU) != 0;
+  g.gpc = subgroups(p.group_size);
   const hipError_t e = wq::launch_grouped_tile(g, as_stream(p.stream));
   return e == hipSuccess ? 0 : hip_fail(e);
 }

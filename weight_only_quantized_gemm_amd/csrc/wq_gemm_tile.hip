@@ -57,8 +57,8 @@ constexpr int kBlocks = TN / 16;  // 16-column blocks per tile
 constexpr int kXcds = 8;
 constexpr int kTailRows = TM / 2;  // grouped tiles with at most this many rows are "small"
 
-// Direct-to-LDS loads each wave issues: 4 per A chunk, 2 per B group, 1 per scale /
-// zero-point group.  Issue order (one group = chunks 2g, 2g+1):
+// Direct-to-LDS loads each wave issues: 4 per A chunk, 2 per B group, kDmaS per scale /
+// zero-point group ("SZ").  Issue order (one group = 128 rows = chunks 2g, 2g+1):
 //   prologue:   SZ(0) B(0) SZ(1) A(0) A(1) B(1)
 //   chunk 2g:   SZ(g+2) A(2g+2)
 //   chunk 2g+1: A(2g+3) B(g+2)
@@ -66,12 +66,26 @@ constexpr int kTailRows = TM / 2;  // grouped tiles with at most this many rows 
 // the next group's weights read in its last step, B(g+1) (followed by SZ(g+2), A(2g+2)).
 constexpr int kDmaA = TM * KC / 8 / kThreads;
 constexpr int kDmaB = 2;
-constexpr int kDmaS = 1;
 constexpr int kWaitEven = kDmaA + kDmaB;
-constexpr int kWaitOdd = kDmaS + kDmaA;
-constexpr int kWaitPrologue = kDmaS + 2 * kDmaA + kDmaB;  // SZ(0) and B(0) landed
 static_assert(kDmaA == 4 && 2 * kWaves == kBlocks, "load split assumes 8 waves, 256 x 256");
-static_assert(kWaitPrologue < 64, "vmcnt holds 6 bits");
+
+// Scale groups smaller than 128 rows: GPC = 128 / group_size sub-groups (1, 2 or 4) per
+// 128-row group.  A group's SZ data is GPC x 128 dwords of scales (16 blocks x 16 fp16 per
+// sub-group) then GPC x 32 words of zero points, loaded 4 bytes per lane (kDmaS loads per
+// wave).  With one sub-group its scales are read once, a group ahead, so two LDS slots
+// suffice; with several, a group reads its own slot while the scales of two groups ahead
+// arrive, hence three.
+template <int GPC>
+struct SzPlan {
+  static constexpr int kDmaS = GPC == 4 ? 2 : 1;
+  static constexpr int kSlots = GPC == 1 ? 2 : 3;
+  static constexpr int kScaleWords = 128 * GPC;
+  static constexpr int kWaitOdd = kDmaS + kDmaA;
+  static constexpr int kWaitPrologue = kDmaS + 2 * kDmaA + kDmaB;  // SZ(0) and B(0) landed
+  static_assert(kWaitPrologue < 64, "vmcnt holds 6 bits");
+  static_assert(160 * GPC <= kDmaS * kThreads, "SZ data fits the loads");
+};
+constexpr int kSzSlotWords = 2 * kThreads;  // room for two loads per wave
 
 // Scheduling-group masks (instruction classes of the AMDGPU scheduler hints).
 constexpr int kSchedVALU = 0x002;
@@ -119,7 +133,7 @@ __device__ __forceinline__ float sigma_of(f16 v) {
 struct Smem {
   f16x8 a[NS][TM * KC / 8];     // 3 x 32 KiB
   u32x4 b[2][kBlocks * 64];     // 2 x 16 KiB: 16 column blocks x 64 lanes x 16 B
-  uint32_t sz[2][kWaves * 64];  // 2 x 2 KiB: waves 0-1 scales, wave 2 zero points, spare
+  uint32_t sz[3][kSzSlotWords];  // scale / zero-point slots (see SzPlan)
   int row_a[TM];
   int row_c[TM];
   float row_w[TM];  // grouped: routing weight of each output row (1 without the multiply)
@@ -136,9 +150,18 @@ __device__ __forceinline__ float silu_times(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
 }
 
-template <bool ZP, bool GROUPED, bool SWIGLU>
+template <bool ZP, bool GROUPED, bool SWIGLU, int GPC>
 __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
   __shared__ Smem sm;
+  using SZ = SzPlan<GPC>;
+  constexpr int kDmaS = SZ::kDmaS;
+  constexpr int kWaitOdd = SZ::kWaitOdd;
+  constexpr int kWaitPrologue = SZ::kWaitPrologue;
+  constexpr int kStepsPerSub = 8 / GPC;  // 16-row MFMA steps per scale sub-group
+  // With four sub-groups the extra scale and zero-point registers leave no room for
+  // reading the next step's A operands a step ahead; they are read at the step instead.
+  constexpr bool kPrefetchA = GPC < 4;
+  auto slot_of = [](int g) { return SZ::kSlots == 2 ? (g & 1) : g % 3; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -284,20 +307,29 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
   const u32x4* bsrc0 =
       reinterpret_cast<const u32x4*>(bptr) + ((long)(nb0 + 2 * wave) * groups) * 64 + lane;
   const u32x4* bsrc1 = bsrc0 + (long)groups * 64;
-  // Scales (waves 0 and 1): lane l reads dword l%8 of column block 8*wave + l/8; zero
-  // points (wave 2): lane l reads word l%2 of block (l%32)/2; the other waves re-read the
-  // scales of blocks 0-7 into their spare slot.
-  const uint32_t* szsrc;
-  long szstride;  // dwords per group
-  if (ZP && wave == 2) {
-    const int l = lane & 31;
-    szsrc = zptr + ((long)(nb0 + (l >> 1)) * groups) * 2 + (l & 1);
-    szstride = 2;
-  } else {
-    const int blk = (wave == 1 ? 8 : 0) + (lane >> 3);
-    szsrc = reinterpret_cast<const uint32_t*>(sptr) + ((long)(nb0 + blk) * groups) * 8 +
-            (lane & 7);
-    szstride = 8;
+  // SZ: load u of this lane fills slot dword d = u*512 + wave*64 + lane.  Dwords below
+  // 128*GPC are scales (block d / (8 GPC), dword d % (8 GPC) of that block's GPC sub-groups),
+  // the next 32*GPC zero-point words (block e / (2 GPC), word e % (2 GPC)); the rest re-read
+  // the first scale dword.  Scales and zero points are stored [block][sub-group] with
+  // groups*GPC sub-groups per block.
+  const uint32_t* szsrc[kDmaS];
+  long szstride[kDmaS];  // dwords per 128-row group
+#pragma unroll
+  for (int u = 0; u < kDmaS; ++u) {
+    const int d = u * kThreads + wave * 64 + lane;
+    const long sub_rows = (long)groups * GPC;
+    if (d < SZ::kScaleWords) {
+      szsrc[u] = reinterpret_cast<const uint32_t*>(sptr) +
+                 ((long)(nb0 + d / (8 * GPC)) * sub_rows) * 8 + d % (8 * GPC);
+      szstride[u] = 8 * GPC;
+    } else if (ZP && d < SZ::kScaleWords + 32 * GPC) {
+      const int e = d - SZ::kScaleWords;
+      szsrc[u] = zptr + ((long)(nb0 + e / (2 * GPC)) * sub_rows) * 2 + e % (2 * GPC);
+      szstride[u] = 2 * GPC;
+    } else {
+      szsrc[u] = reinterpret_cast<const uint32_t*>(sptr) + (long)nb0 * sub_rows * 8;
+      szstride[u] = 8 * GPC;
+    }
   }
 
   const int nchunks = p.k / KC;
@@ -316,8 +348,10 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
   };
   auto issue_sz = [&](int g) {
     const int gg = g < groups ? g : groups - 1;
-    __builtin_amdgcn_global_load_lds(szsrc + (long)gg * szstride, &sm.sz[g & 1][wave * 64], 4, 0,
-                                     0);
+#pragma unroll
+    for (int u = 0; u < kDmaS; ++u)
+      __builtin_amdgcn_global_load_lds(szsrc[u] + (long)gg * szstride[u],
+                                       &sm.sz[slot_of(g)][u * kThreads + wave * 64], 4, 0, 0);
   };
 
   // ---- per-lane compute geometry ---------------------------------------------------------
@@ -343,16 +377,17 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
   ZeroOffsets zo[2];
   const MagicRegs mr = magic_regs();
 
-  // Scale and zero-point offsets of group g for the lane's two columns (slot g & 1).
-  auto read_sz = [&](int g, float* sg, ZeroOffsets* zg) {
-    const f16* sl = reinterpret_cast<const f16*>(sm.sz[g & 1]);
+  // Scale and zero-point offsets of sub-group q of group g for the lane's two columns.
+  auto read_sz = [&](int g, int q, float* sg, ZeroOffsets* zg) {
+    const uint32_t* slot = sm.sz[slot_of(g)];
+    const f16* sl = reinterpret_cast<const f16*>(slot);
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      sg[cb] = sigma_of(sl[bblk[cb] * 16 + c16]);
+      sg[cb] = sigma_of(sl[bblk[cb] * 16 * GPC + 16 * q + c16]);
       int zc = 8;
       if constexpr (ZP) {
-        const uint32_t* zl = sm.sz[g & 1] + 128;
-        zc = zero_code(u32x2{zl[2 * bblk[cb]], zl[2 * bblk[cb] + 1]}, c16);
+        const uint32_t* zl = slot + SZ::kScaleWords + bblk[cb] * 2 * GPC + 2 * q;
+        zc = zero_code(u32x2{zl[0], zl[1]}, c16);
       }
       zg[cb] = zero_offsets(zc);
     }
@@ -377,7 +412,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
   issue_b(1);
   wait_vmcnt<kWaitPrologue>();
   __builtin_amdgcn_s_barrier();
-  read_sz(0, sigma, zo);
+  read_sz(0, 0, sigma, zo);
   read_b(0);
 
   // One iteration per group: its even chunk and its odd chunk, so that the chunk parity,
@@ -398,16 +433,21 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
       issue_b(g + 2);
     }
 
-    // Odd chunk: the next group's scales, and the factor sigma_g / sigma_{g+1} applied to
-    // the running sums after this group's last MFMAs (1 after the last group).  The
-    // hardware reciprocal is about 1 ulp: a relative error near 1e-7 per group boundary.
-    float snext[2], ratio[2];
-    ZeroOffsets znext[2];
-    if (h2 == 1) {
-      read_sz(g + 1, snext, znext);
+    // Odd chunk: the next group's first scales, for the factor sigma / sigma_next applied
+    // to the running sums after this group's last MFMAs (1 after the last group).  The
+    // hardware reciprocal is about 1 ulp: a relative error near 1e-7 per boundary.
+    float snext[2] = {1.f, 1.f}, gfactor[2] = {1.f, 1.f};
+    ZeroOffsets znext[2] = {zo[0], zo[1]};
+    // With at most two sub-groups the running scale at the odd chunk's start is already the
+    // group's last, so the factor is formed here, off the rescaling step's path.
+    auto group_factor = [&](float* f) {
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
-        ratio[cb] = g + 1 < groups ? sigma[cb] * __builtin_amdgcn_rcpf(snext[cb]) : 1.f;
+        f[cb] = g + 1 < groups ? sigma[cb] * __builtin_amdgcn_rcpf(snext[cb]) : 1.f;
+    };
+    if (h2 == 1) {
+      read_sz(g + 1, 0, snext, znext);
+      if (GPC <= 2) group_factor(gfactor);
     }
 
     if constexpr (NRB > 0) {
@@ -423,13 +463,40 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        f16x8 anext[NRB], bnext[2];
-        if (s < 3) {
+        // Step t of the group ends a sub-group when (t + 1) is a multiple of its steps;
+        // an inner boundary switches to the group's next sub-group scale and zero point.
+        const int t = 4 * h2 + s;
+        const bool end_sub = ((t + 1) % kStepsPerSub) == 0;
+        const bool end_group = t == 7;
+        const bool inner = end_sub && !end_group;
+        float sn[2] = {1.f, 1.f}, factor[2] = {1.f, 1.f};
+        ZeroOffsets zn[2] = {zo[0], zo[1]};
+        if (inner) {
+          read_sz(g, (t + 1) / kStepsPerSub, sn, zn);
 #pragma unroll
-          for (int rb = 0; rb < NRB; ++rb) anext[rb] = arow[rb * 256 + aswz[s + 1]];
+          for (int cb = 0; cb < 2; ++cb) factor[cb] = sigma[cb] * __builtin_amdgcn_rcpf(sn[cb]);
+        } else if (end_group) {
+          if (GPC <= 2) {
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) factor[cb] = gfactor[cb];
+          } else {
+            group_factor(factor);
+          }
+        }
+        f16x8 anext[NRB], bnext[2];
+        if (!kPrefetchA && s > 0) {
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb) aop[rb] = arow[rb * 256 + aswz[s]];
+        }
+        if (s < 3) {
+          if (kPrefetchA) {
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) anext[rb] = arow[rb * 256 + aswz[s + 1]];
+          }
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb)
-            bnext[cb] = dequant8(bw[cb][(s + 1) & 1][2 * h2 + ((s + 1) >> 1)], zo[cb], mr);
+            bnext[cb] = dequant8(bw[cb][(s + 1) & 1][2 * h2 + ((s + 1) >> 1)],
+                                 inner ? zn[cb] : zo[cb], mr);
         } else if (h2 == 1) {
           read_b(g + 1);  // the current weights are dead after step 2's dequant
         }
@@ -437,18 +504,19 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
         for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma32x32x16(aop[rb], bop[cb], acc[rb][cb]);
-        if (s == 3 && h2 == 1) {
+        if (end_sub) {
 #pragma unroll
           for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-              for (int r = 0; r < 16; ++r) acc[rb][cb][r] *= ratio[cb];
+              for (int r = 0; r < 16; ++r) acc[rb][cb][r] *= factor[cb];
         }
         // Schedule: LDS reads of the next step first, dequant between the MFMAs; in the
-        // rescaling step the products of the blocks follow the MFMAs.
+        // group's last step the products of the blocks follow the MFMAs.  (Steps at inner
+        // sub-group boundaries are left to the compiler.)
         constexpr int nm = 2 * NRB;  // MFMAs per step
-        if (s < 3) {
+        if (s < 3 && !inner && kPrefetchA) {
           constexpr int per = (20 + nm - 1) / nm;
 #pragma unroll
           for (int i = 0; i < nm; ++i) {
@@ -456,7 +524,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
             __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedVALU, per, 0);
           }
-        } else if (h2 == 1) {
+        } else if (end_group) {
           __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
           __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
           __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
@@ -469,15 +537,26 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
           __builtin_amdgcn_sched_group_barrier(kSchedVALU, 32, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (s < 3) {
+        if (inner) {
 #pragma unroll
-          for (int rb = 0; rb < NRB; ++rb) aop[rb] = anext[rb];
+          for (int cb = 0; cb < 2; ++cb) {
+            sigma[cb] = sn[cb];
+            zo[cb] = zn[cb];
+          }
+        }
+        if (s < 3) {
+          if (kPrefetchA) {
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) aop[rb] = anext[rb];
+          }
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb) bop[cb] = bnext[cb];
         }
       }
     }
-    if (h2 == 1) {
+    // After the last group the running sums stay in units of its last sub-group's scale,
+    // which the epilogue applies.
+    if (h2 == 1 && g + 1 < groups) {
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         sigma[cb] = snext[cb];
@@ -547,20 +626,31 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
 
 }  // namespace
 
-template <bool GROUPED, bool SWIGLU>
-hipError_t launch_tile_t(const TileArgs& p, bool zp, hipStream_t stream) {
+template <bool GROUPED, bool SWIGLU, int GPC>
+hipError_t launch_tile_g(const TileArgs& p, bool zp, hipStream_t stream) {
   if (zp)
-    hipLaunchKernelGGL((gemm_tile_kernel<true, GROUPED, SWIGLU>), dim3((unsigned)p.tiles),
+    hipLaunchKernelGGL((gemm_tile_kernel<true, GROUPED, SWIGLU, GPC>), dim3((unsigned)p.tiles),
                        dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm_tile_kernel<false, GROUPED, SWIGLU>), dim3((unsigned)p.tiles),
-                       dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_tile_kernel<false, GROUPED, SWIGLU, GPC>),
+                       dim3((unsigned)p.tiles), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+// gpc: scale sub-groups per 128 rows of K (1, 2 or 4).
+template <bool GROUPED, bool SWIGLU>
+hipError_t launch_tile_t(const TileArgs& p, bool zp, int gpc, hipStream_t stream) {
+  switch (gpc) {
+    case 1: return launch_tile_g<GROUPED, SWIGLU, 1>(p, zp, stream);
+    case 2: return launch_tile_g<GROUPED, SWIGLU, 2>(p, zp, stream);
+    case 4: return launch_tile_g<GROUPED, SWIGLU, 4>(p, zp, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b,
                             const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
-                            bool swiglu, hipStream_t stream) {
+                            bool swiglu, int gpc, hipStream_t stream) {
   TileArgs p{};
   p.a = a;
   p.lda = lda;
@@ -573,8 +663,8 @@ hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b
   p.k = k;
   p.ldc = swiglu ? n / 2 : n;
   p.tiles = (n / TN) * ((m + TM - 1) / TM);
-  return swiglu ? launch_tile_t<false, true>(p, z != nullptr, stream)
-                : launch_tile_t<false, false>(p, z != nullptr, stream);
+  return swiglu ? launch_tile_t<false, true>(p, z != nullptr, gpc, stream)
+                : launch_tile_t<false, false>(p, z != nullptr, gpc, stream);
 }
 
 hipError_t launch_grouped_tile(const GroupedProblem& g, hipStream_t stream) {
@@ -611,8 +701,8 @@ hipError_t launch_grouped_tile(const GroupedProblem& g, hipStream_t stream) {
   if (tiles > 0x7fffffffL) return hipErrorInvalidConfiguration;
   p.tiles = (int)tiles;
   p.ldc = g.swiglu ? g.n / 2 : g.n;
-  return g.swiglu ? launch_tile_t<true, true>(p, g.z_bank != nullptr, stream)
-                  : launch_tile_t<true, false>(p, g.z_bank != nullptr, stream);
+  return g.swiglu ? launch_tile_t<true, true>(p, g.z_bank != nullptr, g.gpc, stream)
+                  : launch_tile_t<true, false>(p, g.z_bank != nullptr, g.gpc, stream);
 }
 
 }  // namespace wq

@@ -10,8 +10,10 @@ namespace wq {
 // Repack / export / gather kernels (wq_repack.hip).
 hipError_t launch_repack_b(const uint32_t* qweight, const int32_t* perm, uint32_t* out, int k,
                            int n, hipStream_t stream);
-// group_size: -1 (channelwise) or a multiple of 128 dividing k; the output always holds
-// one entry per 128-row chunk of K.
+// group_size: -1 (channelwise), 32, 64 or a multiple of 128 dividing k.  The output holds
+// one entry per unit of min(group_size, 128) rows of K (a larger group is repeated for
+// each 128-row chunk it covers).
+int scale_unit_rows(int k, int group_size);
 hipError_t launch_repack_scales(const uint16_t* s, uint16_t* out, int k, int n,
                                 int group_size, hipStream_t stream);
 hipError_t launch_repack_zeros(const uint32_t* z, uint32_t* out, int k, int n, int group_size,
@@ -20,7 +22,7 @@ hipError_t launch_repack_zeros(const uint32_t* z, uint32_t* out, int k, int n, i
 hipError_t launch_interleave_gate_up(const void* gate, const void* up, void* out, int rows,
                                      int cols, int bits_per_column, hipStream_t stream);
 hipError_t launch_dequant(const uint32_t* b, const uint16_t* s, const uint32_t* z, int k, int n,
-                          uint16_t* w, hipStream_t stream);
+                          int unit, uint16_t* w, hipStream_t stream);
 hipError_t launch_gather_columns(const uint16_t* a, int lda, const int32_t* perm, uint16_t* out,
                                  int m, int k, hipStream_t stream);
 
@@ -40,10 +42,11 @@ hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* 
 // Tiled kernel (wq_gemm_tile.hip): 256 x 256 output tiles on 8 waves of 128 x 64.
 constexpr int kTileM = 256;
 constexpr int kTileN = 256;
-// swiglu: B pairs gate/up 16-column blocks and c is the [m][n/2] activation.
+// swiglu: B pairs gate/up 16-column blocks and c is the [m][n/2] activation.  gpc: scale
+// sub-groups per 128 rows of K (1, or 2 / 4 for 64- / 32-row groups).
 hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b,
                             const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
-                            bool swiglu, hipStream_t stream);
+                            bool swiglu, int gpc, hipStream_t stream);
 
 struct GroupedProblem {
   const uint16_t* a;
@@ -61,6 +64,7 @@ struct GroupedProblem {
   uint16_t* y;
   int n_expert, n_active, n_pairs, n_tokens, k, n;
   bool swiglu;            // SwiGLU epilogue: y is [n_pairs][n/2]
+  int gpc;                // scale sub-groups per 128 rows of K
 };
 hipError_t launch_grouped_tile(const GroupedProblem& p, hipStream_t stream);
 

@@ -51,40 +51,40 @@ __global__ __launch_bounds__(256) void repack_b_kernel(const uint32_t* __restric
   }
 }
 
-// Scales and zero points are stored per 128-row chunk of K.  A source group covering
-// `chunks_per_group` chunks (its size / 128) is repeated for each of them; 0 stands for
-// one group over all of K (channelwise).
-__device__ __forceinline__ long source_group(int chunk, int chunks_per_group) {
-  return chunks_per_group > 0 ? chunk / chunks_per_group : 0;
+// Scales and zero points are stored per unit of min(group_size, 128) rows of K.  Unit u
+// takes the group holding its rows, u * unit / group_size (a group larger than 128 rows is
+// repeated for each chunk it covers); group_size -1 is one group over all of K.
+__device__ __forceinline__ long source_group(int u, int unit, int group_size) {
+  return group_size > 0 ? (long)u * unit / group_size : 0;
 }
 
 __global__ __launch_bounds__(256) void repack_scales_kernel(const uint16_t* __restrict__ s,
                                                             uint16_t* __restrict__ out, int k,
-                                                            int n, int chunks_per_group) {
-  const int groups = k / kGroup;
-  const long total = (long)groups * n;
+                                                            int n, int unit, int group_size) {
+  const int units = k / unit;
+  const long total = (long)units * n;
   for (long o = (long)blockIdx.x * blockDim.x + threadIdx.x; o < total;
        o += (long)gridDim.x * blockDim.x) {
     const int c = (int)(o & 15);
     const long rest = o >> 4;
-    const int g = (int)(rest % groups);
-    const long nb = rest / groups;
-    out[o] = s[source_group(g, chunks_per_group) * n + nb * 16 + c];
+    const int g = (int)(rest % units);
+    const long nb = rest / units;
+    out[o] = s[source_group(g, unit, group_size) * n + nb * 16 + c];
   }
 }
 
 __global__ __launch_bounds__(256) void repack_zeros_kernel(const uint32_t* __restrict__ z,
                                                            uint32_t* __restrict__ out, int k,
-                                                           int n, int chunks_per_group) {
-  const int groups = k / kGroup;
-  const long total = (long)groups * (n / 8);
+                                                           int n, int unit, int group_size) {
+  const int units = k / unit;
+  const long total = (long)units * (n / 8);
   for (long o = (long)blockIdx.x * blockDim.x + threadIdx.x; o < total;
        o += (long)gridDim.x * blockDim.x) {
     const int h = (int)(o & 1);
     const long rest = o >> 1;
-    const int g = (int)(rest % groups);
-    const long nb = rest / groups;
-    out[o] = z[source_group(g, chunks_per_group) * (n / 8) + nb * 2 + h];
+    const int g = (int)(rest % units);
+    const long nb = rest / units;
+    out[o] = z[source_group(g, unit, group_size) * (n / 8) + nb * 2 + h];
   }
 }
 
@@ -93,9 +93,11 @@ __global__ __launch_bounds__(256) void repack_zeros_kernel(const uint32_t* __res
 __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict__ b,
                                                       const uint16_t* __restrict__ s,
                                                       const uint32_t* __restrict__ z, int k,
-                                                      int n, uint16_t* __restrict__ w) {
+                                                      int n, int unit,
+                                                      uint16_t* __restrict__ w) {
   const long total = (long)k * n / 8;
   const int groups = k / kGroup;
+  const int units = k / unit;  // scale rows per column block
   for (long o = (long)blockIdx.x * blockDim.x + threadIdx.x; o < total;
        o += (long)gridDim.x * blockDim.x) {
     const int j = (int)(o & 3);
@@ -106,7 +108,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
     const int c = lane & 15;
     const long col = nb * 16 + c;
     const int row0 = g * kGroup + 32 * j + 8 * (lane >> 4);
-    const long blk = nb * groups + g;
+    const long blk = nb * units + row0 / unit;  // the 8 rows share one scale unit
     const float scale = (float)__builtin_bit_cast(f16, s[blk * 16 + c]);
     int zc = 8;
     if (z != nullptr) zc = zero_code(u32x2{z[blk * 2], z[blk * 2 + 1]}, c);
@@ -241,19 +243,24 @@ hipError_t launch_repack_b(const uint32_t* qweight, const int32_t* perm, uint32_
   return hipGetLastError();
 }
 
+int scale_unit_rows(int k, int group_size) {
+  (void)k;
+  return group_size > 0 && group_size < kGroup ? group_size : kGroup;
+}
+
 hipError_t launch_repack_scales(const uint16_t* s, uint16_t* out, int k, int n,
                                 int group_size, hipStream_t stream) {
-  const int chunks_per_group = group_size > 0 ? group_size / kGroup : 0;
-  hipLaunchKernelGGL(repack_scales_kernel, dim3(grid_for((long)(k / kGroup) * n)), dim3(256), 0,
-                     stream, s, out, k, n, chunks_per_group);
+  const int unit = scale_unit_rows(k, group_size);
+  hipLaunchKernelGGL(repack_scales_kernel, dim3(grid_for((long)(k / unit) * n)), dim3(256), 0,
+                     stream, s, out, k, n, unit, group_size);
   return hipGetLastError();
 }
 
 hipError_t launch_repack_zeros(const uint32_t* z, uint32_t* out, int k, int n, int group_size,
                                hipStream_t stream) {
-  const int chunks_per_group = group_size > 0 ? group_size / kGroup : 0;
-  hipLaunchKernelGGL(repack_zeros_kernel, dim3(grid_for((long)(k / kGroup) * (n / 8))),
-                     dim3(256), 0, stream, z, out, k, n, chunks_per_group);
+  const int unit = scale_unit_rows(k, group_size);
+  hipLaunchKernelGGL(repack_zeros_kernel, dim3(grid_for((long)(k / unit) * (n / 8))),
+                     dim3(256), 0, stream, z, out, k, n, unit, group_size);
   return hipGetLastError();
 }
 
@@ -269,9 +276,9 @@ hipError_t launch_interleave_gate_up(const void* gate, const void* up, void* out
 }
 
 hipError_t launch_dequant(const uint32_t* b, const uint16_t* s, const uint32_t* z, int k, int n,
-                          uint16_t* w, hipStream_t stream) {
+                          int unit, uint16_t* w, hipStream_t stream) {
   hipLaunchKernelGGL(dequant_kernel, dim3(grid_for((long)k * n / 8)), dim3(256), 0, stream, b, s,
-                     z, k, n, w);
+                     z, k, n, unit, w);
   return hipGetLastError();
 }
 

@@ -46,12 +46,13 @@ class PackedWeight:
         wq_repack_b(qw, self.b, self.k, self.n, perm=self.perm)
         sc = to_device(scales if isinstance(scales, torch.Tensor)
                        else np.asarray(scales, dtype=np.float16), self.device)
-        self.s = torch.empty((self.k // GROUP) * self.n, dtype=torch.float16, device=self.device)
+        unit = group_size if 0 < group_size < GROUP else GROUP  # rows per stored scale row
+        self.s = torch.empty((self.k // unit) * self.n, dtype=torch.float16, device=self.device)
         wq_repack_scales(sc, self.s, self.k, self.n, group_size)
         self.z = None
         if zeros is not None:
             zw = to_device(zeros, self.device)
-            self.z = torch.empty((self.k // GROUP) * self.n // 8, dtype=torch.int32,
+            self.z = torch.empty((self.k // unit) * self.n // 8, dtype=torch.int32,
                                  device=self.device)
             wq_repack_zeros(zw, self.z, self.k, self.n, group_size)
         torch.cuda.synchronize(self.device)

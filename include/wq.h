@@ -178,8 +178,9 @@ typedef struct wq_gemm_args {
 
 /*
  * C = A @ dequant(B) (all of it enqueued on args->stream).  With WQ_FLAG_SWIGLU, c is the
- * [m][n/2] activation silu(A Wg) * (A Wu) of paired gate/up weights (any m; the decode-
- * shaped small-M kernel is not used for it).
+ * [m][n/2] activation silu(A Wg) * (A Wu) of paired gate/up weights (any m; for m <= 16
+ * and k <= 8192 the small-M kernel computes both sums of a pair in one work-group, with
+ * no split along K).
  */
 int wq_gemm(const wq_gemm_args* args);
 

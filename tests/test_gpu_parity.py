@@ -481,7 +481,12 @@ def test_interleave_gate_up_bitwise(dev, bits, rows, cols):
                                                     (16, 512, 512, True, False, 128),
                                                     (300, 1024, 256, False, True, 128),
                                                     (513, 256, 384, True, False, 128),
-                                                    (100, 512, 256, True, False, 32)])
+                                                    (100, 512, 256, True, False, 32),
+                                                    # small-M paired form: 8 and 16 waves,
+                                                    # and beyond it the tiled kernel
+                                                    (1, 4096, 1024, False, False, 128),
+                                                    (4, 8192, 256, True, False, 128),
+                                                    (2, 12288, 256, False, False, 128)])
 def test_swiglu_activation_matches_oracle(dev, m, k, i, zp, act_order, gs):
     label = f"swiglu m={m} k={k} i={i} zp={zp} act_order={act_order} group_size={gs}"
     say(label)

@@ -64,6 +64,26 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 // work-groups (half the CUs), since every split adds an fp32 partial round trip and a
 // reduce launch (measured on MI355X: at N=4096..14336 one split is fastest).  Each split's
 // groups are shared by 4 or 8 waves, at most 8 groups per wave.
+// Plan of the small-M kernel's SwiGLU (paired) form: no split, 8 or 16 waves (4 or 8 per
+// block along K), or false when no plan fits (the tiled kernel then computes it).
+bool plan_small_pair(int m, int k, wq::SmallPlan* plan) {
+  const int groups = k / kGroupSize;
+  for (int waves = 8; waves <= 16; waves *= 2) {
+    const int per_wave = (groups + waves / 2 - 1) / (waves / 2);
+    if (per_wave > 8) continue;
+    wq::SmallPlan p{};
+    p.waves = waves;
+    p.splits = 1;
+    p.depth = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 8;
+    p.pair = true;
+    if (wq::small_plan_fits(m, k, p)) {
+      *plan = p;
+      return true;
+    }
+  }
+  return false;
+}
+
 bool plan_small(int m, int n, int k, uint32_t flags, int requested, wq::SmallPlan* plan) {
   const int groups = k / kGroupSize;
   const bool fp32 = (flags & WQ_FLAG_FP32_REDUCE) != 0;
@@ -255,8 +275,9 @@ int wq_gemm(const wq_gemm_args* args) {
   // kernel reads one scale per 128 rows, so smaller groups take the tiled kernel.
   const int gpc = subgroups(p.group_size);
   wq::SmallPlan plan{};
-  const bool small = !swiglu && gpc == 1 && p.m <= 16 &&
-                     plan_small(p.m, p.n, p.k, p.flags, p.split_k, &plan);
+  const bool small = gpc == 1 && p.m <= 16 &&
+                     (swiglu ? plan_small_pair(p.m, p.k, &plan)
+                             : plan_small(p.m, p.n, p.k, p.flags, p.split_k, &plan));
   float* partials = nullptr;
   if (small && plan.splits > 1) {
     const size_t need = (size_t)plan.splits * p.m * p.n * sizeof(float);

@@ -66,6 +66,12 @@ __device__ __forceinline__ int zero_code(u32x2 zw, int c) {
   return (int)((w >> (4 * (c & 7))) & 0xFu);
 }
 
+// silu(g) * u = g / (1 + exp(-g)) * u in fp32 (hardware exp and reciprocal), the SwiGLU
+// activation of a gate sum g and an up sum u.
+__device__ __forceinline__ float silu_times(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }

@@ -24,24 +24,38 @@
 namespace wq {
 namespace {
 
-// LDS budget of one work-group's activation slice (fp16 [m][span*128], padded to a whole
-// number of staging rounds).
-constexpr int kSmallLdsA = 128 * 1024;
+// LDS of one work-group: 160 KiB on gfx950, shared by the statically sized scale, zero-point
+// and reduction buffers and the dynamically sized activation slice (fp16 [m][span*128],
+// padded to a whole number of staging rounds).
+constexpr int kLdsBytes = 160 * 1024;
 constexpr int kMaxSpan = 64;   // groups per work-group covered by the staged scales
+
+// Static LDS of an instance (see the kernel's __shared__ arrays), an upper bound over ZP.
+constexpr long small_static_lds(int waves, bool pair) {
+  return ((pair ? 2 : 1) * kMaxSpan * 8 + 2L * waves * 64) * 4  // s_lds
+         + (long)waves * 64 * 8                                 // z_lds
+         + (long)waves * 64 * 16;                               // red
+}
 
 // The kernel body is branch-free up to the arithmetic: every load is issued
 // unconditionally (addresses are clamped into the tensors) and ragged ends are masked by
 // value, so the compiler's in-order load counting can let LDS writes wait for the
 // activations alone and each group wait for its own weight chunk, while the rest of the
 // weight stream stays in flight.
-template <bool ZP, int WAVES, int GW, int STAGE>
+// PAIR (the SwiGLU epilogue): the work-group owns a gate/up pair of 16-column blocks
+// (2t, 2t+1, as wq_interleave_gate_up pairs them); its first half of waves streams the gate
+// block, the second half the up block, both over the same K range and staged activations,
+// and the reduction writes fp16(silu(g) * u) to column 16t + c of the [m][n/2] activation.
+template <bool ZP, int WAVES, int GW, int STAGE, bool PAIR>
 __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     const f16* __restrict__ a, int lda, int m, const u32x4* __restrict__ b,
     const f16* __restrict__ s, const u32x2* __restrict__ z, f16* __restrict__ c, int n,
     int groups, int splits, float* __restrict__ partials) {
   constexpr int T = WAVES * 64;
+  constexpr int NB = PAIR ? 2 : 1;            // column blocks of the work-group
+  constexpr int KW = WAVES / NB;              // waves splitting K for one block
   extern __shared__ f16x8 a_lds[];                // [m][span*16] granules (+ padding)
-  __shared__ uint32_t s_lds[kMaxSpan * 8 + 2 * T];  // scales of the range, [g][col] as fp16
+  __shared__ uint32_t s_lds[NB * kMaxSpan * 8 + 2 * T];  // scales, [block][g][col] as fp16
   __shared__ u32x2 z_lds[ZP ? T : 1];          // zero points of the range (+ padding)
   __shared__ f32x4 red[WAVES][64];
 
@@ -50,14 +64,16 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   const int wave = tid >> 6;
   const int col = lane & 15;  // column inside the 16-column block; also the A row of the lane
   const int qd = lane >> 4;   // which 8 rows of each 32-row MFMA step the lane carries
-  const int nb = blockIdx.x;
+  const int half = PAIR ? wave / KW : 0;       // the wave's block of the pair
+  const int kwave = wave - half * KW;          // the wave's index along K
+  const int nb = NB * blockIdx.x + half;
   const int split = blockIdx.y;
 
   const int gs0 = (int)((long)groups * split / splits);
   const int gs1 = (int)((long)groups * (split + 1) / splits);
   const int span = gs1 - gs0;
-  const int g0 = gs0 + span * wave / WAVES;
-  const int g1 = gs0 + span * (wave + 1) / WAVES;
+  const int g0 = gs0 + span * kwave / KW;
+  const int g1 = gs0 + span * (kwave + 1) / KW;
   const int gw = g1 - g0;  // <= GW by the launch plan
 
   // 1. Activation granules: slot u of this thread is granule tid + u*T of the slice, at row
@@ -79,18 +95,26 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     q = wrap ? q - per_row : q;
     r = wrap ? r + 1 : r;
   }
-  // 2. Scales (8 dwords of fp16 pairs per group) and zero points of the range.
-  const long blk0 = (long)nb * groups + gs0;
-  const uint32_t* s32 = reinterpret_cast<const uint32_t*>(s) + blk0 * 8;
+  // 2. Scales (8 dwords of fp16 pairs per group) and zero points of the range, for each of
+  //    the work-group's blocks ([block][group] in LDS).
+  const long blk0 = (long)nb * groups + gs0;  // this wave's block
+  const long pair0 = (long)NB * blockIdx.x * groups + gs0;  // the work-group's first block
+  const uint32_t* s32 = reinterpret_cast<const uint32_t*>(s);
   const int s_words = span * 8;
   uint32_t s_stage[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int i = tid + u * T;
-    s_stage[u] = s32[i < s_words ? i : s_words - 1];
+    int i = tid + u * T;
+    i = i < NB * s_words ? i : NB * s_words - 1;
+    const int h = PAIR && i >= s_words ? 1 : 0;  // block of the pair holding dword i
+    s_stage[u] = s32[(pair0 + (long)h * groups) * 8 + (i - h * s_words)];
   }
   u32x2 z_stage = u32x2{0u, 0u};
-  if constexpr (ZP) z_stage = z[blk0 + (tid < span ? tid : span - 1)];
+  if constexpr (ZP) {
+    const int i = tid < NB * span ? tid : NB * span - 1;
+    const int h = PAIR && i >= span ? 1 : 0;
+    z_stage = z[pair0 + (long)h * groups + (i - h * span)];
+  }
 
   // 3. The wave's weight chunks, all in flight before any arithmetic.
   u32x4 bw[GW];
@@ -121,7 +145,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
   for (int i = 0; i < GW; ++i) {
     gl[i] = g0 - gs0 + (i < gw ? i : gw - 1);
-    const float v = (float)s_half[gl[i] * 16 + col];
+    const float v = (float)s_half[(half * span + gl[i]) * 16 + col];
     sc[i] = i < gw ? v : 0.f;
   }
   f16x8 an[4];
@@ -140,7 +164,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     // With eight groups per wave, pin the prefetch ahead of this group's work (measured
     // faster for the decode shape, slower for shallower pipelines).
     if constexpr (GW >= 8) __builtin_amdgcn_sched_barrier(0);
-    const ZeroOffsets zo = zero_offsets(ZP ? zero_code(z_lds[gl[i]], col) : 8);
+    const ZeroOffsets zo = zero_offsets(ZP ? zero_code(z_lds[half * span + gl[i]], col) : 8);
     f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) p = mfma16x16x32(ac[j], dequant8(bw[i][j], zo, mr), p);
@@ -153,6 +177,21 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   red[wave][lane] = acc;
   __syncthreads();
   if (wave != 0) return;
+  if constexpr (PAIR) {
+    f32x4 gs = red[0][lane], us = red[KW][lane];
+#pragma unroll
+    for (int w = 1; w < KW; ++w) {
+      gs += red[w][lane];
+      us += red[KW + w][lane];
+    }
+    const long colj = (long)blockIdx.x * 16 + col;  // column of the [m][n/2] activation
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 4 * qd + e;
+      if (row < m) c[(long)row * (n / 2) + colj] = (f16)silu_times(gs[e], us[e]);
+    }
+    return;
+  }
   f32x4 tot = red[0][lane];
 #pragma unroll
   for (int w = 1; w < WAVES; ++w) tot += red[w][lane];
@@ -207,19 +246,20 @@ int round_slots(int slots) {
   return slots <= 1 ? 1 : slots <= 2 ? 2 : slots <= 4 ? 4 : slots <= 8 ? 8 : 16;
 }
 
-template <bool ZP, int WAVES, int GW, int STAGE>
+template <bool ZP, int WAVES, int GW, int STAGE, bool PAIR>
 hipError_t launch_small_t(const uint16_t* a, int lda, int m, const uint32_t* b,
                           const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                           int splits, float* partials, hipStream_t stream) {
   const int groups = k / kGroup;
-  const size_t lds = (size_t)STAGE * WAVES * 64 * sizeof(f16x8);
+  // The activation slice of this instance (its size is fixed by STAGE and WAVES).
+  constexpr size_t lds = (size_t)STAGE * WAVES * 64 * sizeof(f16x8);
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_small_kernel<ZP, WAVES, GW, STAGE>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, kSmallLdsA);
+      reinterpret_cast<const void*>(&gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
-  const dim3 grid(n / 16, splits);
-  hipLaunchKernelGGL((gemm_small_kernel<ZP, WAVES, GW, STAGE>), grid, dim3(WAVES * 64), lds,
-                     stream, reinterpret_cast<const f16*>(a), lda, m,
+  const dim3 grid(n / (PAIR ? 32 : 16), splits);
+  hipLaunchKernelGGL((gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR>), grid, dim3(WAVES * 64),
+                     lds, stream, reinterpret_cast<const f16*>(a), lda, m,
                      reinterpret_cast<const u32x4*>(b), reinterpret_cast<const f16*>(s),
                      reinterpret_cast<const u32x2*>(z), reinterpret_cast<f16*>(c), n, groups,
                      splits, partials);
@@ -232,39 +272,50 @@ hipError_t launch_small_t(const uint16_t* a, int lda, int m, const uint32_t* b,
   return hipGetLastError();
 }
 
-template <bool ZP, int WAVES, int GW>
+template <bool ZP, int WAVES, int GW, bool PAIR>
 hipError_t launch_small_stage(const uint16_t* a, int lda, int m, const uint32_t* b,
                               const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                               const SmallPlan& plan, float* partials, hipStream_t stream) {
   const int span = (k / kGroup + plan.splits - 1) / plan.splits;
+#define WQ_SMALL(ST) \
+  launch_small_t<ZP, WAVES, GW, ST, PAIR>(a, lda, m, b, s, z, c, n, k, plan.splits, partials, stream)
   switch (round_slots(stage_slots(m, span, WAVES))) {
-    case 1: return launch_small_t<ZP, WAVES, GW, 1>(a, lda, m, b, s, z, c, n, k, plan.splits, partials, stream);
-    case 2: return launch_small_t<ZP, WAVES, GW, 2>(a, lda, m, b, s, z, c, n, k, plan.splits, partials, stream);
-    case 4: return launch_small_t<ZP, WAVES, GW, 4>(a, lda, m, b, s, z, c, n, k, plan.splits, partials, stream);
-    case 8: return launch_small_t<ZP, WAVES, GW, 8>(a, lda, m, b, s, z, c, n, k, plan.splits, partials, stream);
-    default: return launch_small_t<ZP, WAVES, GW, 16>(a, lda, m, b, s, z, c, n, k, plan.splits, partials, stream);
+    case 1: return WQ_SMALL(1);
+    case 2: return WQ_SMALL(2);
+    case 4: return WQ_SMALL(4);
+    case 8: return WQ_SMALL(8);
+    default: return WQ_SMALL(16);
   }
+#undef WQ_SMALL
 }
 
-template <bool ZP, int WAVES>
+template <bool ZP, int WAVES, bool PAIR>
 hipError_t launch_small_gw(const uint16_t* a, int lda, int m, const uint32_t* b,
                            const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                            const SmallPlan& plan, float* partials, hipStream_t stream) {
+#define WQ_SMALL(GWV) \
+  launch_small_stage<ZP, WAVES, GWV, PAIR>(a, lda, m, b, s, z, c, n, k, plan, partials, stream)
   switch (plan.depth) {
-    case 1: return launch_small_stage<ZP, WAVES, 1>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
-    case 2: return launch_small_stage<ZP, WAVES, 2>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
-    case 4: return launch_small_stage<ZP, WAVES, 4>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
-    default: return launch_small_stage<ZP, WAVES, 8>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
+    case 1: return WQ_SMALL(1);
+    case 2: return WQ_SMALL(2);
+    case 4: return WQ_SMALL(4);
+    default: return WQ_SMALL(8);
   }
+#undef WQ_SMALL
 }
 
 template <bool ZP>
 hipError_t launch_small_waves(const uint16_t* a, int lda, int m, const uint32_t* b,
                               const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                               const SmallPlan& plan, float* partials, hipStream_t stream) {
+  if (plan.pair) {
+    if (plan.waves == 16)
+      return launch_small_gw<ZP, 16, true>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
+    return launch_small_gw<ZP, 8, true>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
+  }
   if (plan.waves == 8)
-    return launch_small_gw<ZP, 8>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
-  return launch_small_gw<ZP, 4>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
+    return launch_small_gw<ZP, 8, false>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
+  return launch_small_gw<ZP, 4, false>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
 }
 
 }  // namespace
@@ -272,14 +323,17 @@ hipError_t launch_small_waves(const uint16_t* a, int lda, int m, const uint32_t*
 bool small_plan_fits(int m, int k, const SmallPlan& plan) {
   const int groups = k / kGroup;
   if (plan.splits < 1 || plan.splits > groups) return false;
+  if (plan.pair && plan.splits != 1) return false;  // the SwiGLU epilogue needs whole sums
   const int span = (groups + plan.splits - 1) / plan.splits;
   const int min_span = groups / plan.splits;  // every split holds at least this many groups
-  if (plan.waves != 4 && plan.waves != 8) return false;
-  if (span > kMaxSpan || min_span < plan.waves) return false;   // every wave has a group
-  if ((span + plan.waves - 1) / plan.waves > plan.depth || plan.depth > 8) return false;
+  if (plan.pair ? (plan.waves != 8 && plan.waves != 16) : (plan.waves != 4 && plan.waves != 8))
+    return false;
+  const int kw = plan.pair ? plan.waves / 2 : plan.waves;  // waves along K per block
+  if (span > kMaxSpan || min_span < kw) return false;   // every wave has a group
+  if ((span + kw - 1) / kw > plan.depth || plan.depth > 8) return false;
   const int slots = stage_slots(m, span, plan.waves);
-  return slots <= 16 &&
-         (long)round_slots(slots) * plan.waves * 64 * (long)sizeof(f16x8) <= kSmallLdsA;
+  const long dynamic = (long)round_slots(slots) * plan.waves * 64 * (long)sizeof(f16x8);
+  return slots <= 16 && dynamic + small_static_lds(plan.waves, plan.pair) <= kLdsBytes;
 }
 
 hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* b,

@@ -146,10 +146,6 @@ struct Smem {
 // row.  The two lanes exchange their scaled sums (a lane swizzle, xor 16) and the gate lane
 // writes fp16(silu(g) * u) to column j of the [rows][n/2] activation: the gate and up
 // products never leave the registers.
-__device__ __forceinline__ float silu_times(float g, float u) {
-  return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
-}
-
 template <bool ZP, bool GROUPED, bool SWIGLU, int GPC>
 __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
   __shared__ Smem sm;

@@ -30,9 +30,11 @@ hipError_t launch_gather_columns(const uint16_t* a, int lda, const int32_t* perm
 // work-groups per column block, fp32 partials go to `partials` [splits][m][n] and a second
 // kernel reduces them in split order.
 struct SmallPlan {
-  int waves;       // waves per work-group (4, 8 or 16), splitting the work-group's K range
+  int waves;       // waves per work-group (4 or 8; 8 or 16 when pair), splitting K
   int splits;      // work-groups along K per column block
   int depth;       // groups of K per wave, all loaded before arithmetic (1, 2, 4 or 8)
+  bool pair;       // SwiGLU epilogue: a gate/up pair of blocks per work-group, half the
+                   // waves on each (n counts both; c is [m][n/2]; splits must be 1)
 };
 bool small_plan_fits(int m, int k, const SmallPlan& plan);
 hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* b,

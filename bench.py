@@ -125,6 +125,76 @@ def bench_moe(torch, torch_ops, steps, warmup):
     return dict(sec=sec, flops=flops, weight_bytes=moe["n_expert"] * moe["k"] * moe["n"] // 2)
 
 
+def bench_extended(torch, torch_ops, steps, warmup):
+    """Timings of the widened features on the same workload shapes (one object per row):
+    the SwiGLU gate/up projection with its fused activation at decode (M=1) and prefill
+    (M=2048) shape, 32-row and channelwise scale groups, and MoE with routing weights."""
+    import synthetic
+    import weight_only_quantized_gemm_amd as wq
+    out = {}
+    k, inter = 4096, 14336
+
+    def proj(seed):
+        return dict(qweight=synthetic.qweight_words(seed, k, inter),
+                    scales=synthetic.scales(seed + 1, k // 128, inter))
+    gate, up = proj(11), proj(13)
+    w0 = torch_ops.PackedWeight.gate_up(gate, up, device="cuda")
+    for m, copies in ((1, 6), (2048, 1)):
+        ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+        a = torch_ops.to_device(synthetic.activations(15, m, k), "cuda")
+        act = torch.empty((m, inter), dtype=torch.float16, device="cuda")
+        bufs = torch_ops.GemmBuffers(w0, m, False)
+
+        def step(i, ws=ws, a=a, act=act, bufs=bufs, copies=copies):
+            torch_ops.gemm(a, ws[i % copies], act, buffers=bufs)
+        sec = timed_loop(torch, step, steps if m == 1 else max(5, steps // 8), warmup)
+        flops = 2.0 * m * 2 * inter * k
+        out[f"swiglu_gate_up_m{m}"] = {
+            "workload": f"gate+up M={m} K={k} I={inter} u4b8 g128, fused silu*mul epilogue",
+            "us": round(sec * 1e6, 2), "tflops": round(flops / sec / 1e12, 2),
+            "weight_tbs": round(k * 2 * inter / 2 / sec / 1e12, 4)}
+        del ws
+    for name, gs in (("decode", 32), ("decode", -1), ("prefill", 32)):
+        cfg = synthetic.CONFIGS[name]
+        case = synthetic.dense_case(cfg["m"], cfg["k"], cfg["n"], group_size=gs, seed=17)
+        w = torch_ops.PackedWeight(case["qweight"], case["scales"], device="cuda",
+                                   group_size=gs)
+        copies = 12 if name == "decode" else 1
+        ws = [w] + [w.clone() for _ in range(copies - 1)]
+        a = torch_ops.to_device(case["a"], "cuda")
+        c = torch.empty((cfg["m"], cfg["n"]), dtype=torch.float16, device="cuda")
+        fp32 = cfg["fp32_reduce"]
+        bufs = torch_ops.GemmBuffers(w, cfg["m"], fp32)
+
+        def step(i, ws=ws, a=a, c=c, bufs=bufs, copies=copies, fp32=fp32):
+            torch_ops.gemm(a, ws[i % copies], c, fp32_reduce=fp32, buffers=bufs)
+        sec = timed_loop(torch, step, steps if name == "decode" else max(5, steps // 8), warmup)
+        flops = 2.0 * cfg["m"] * cfg["n"] * cfg["k"]
+        out[f"{name}_group{gs}"] = {
+            "workload": f"{name} shape M={cfg['m']} K={cfg['k']} N={cfg['n']} u4b8 "
+                        f"group_size {gs}",
+            "us": round(sec * 1e6, 2), "tflops": round(flops / sec / 1e12, 2),
+            "weight_tbs": round(cfg["k"] * cfg["n"] / 2 / sec / 1e12, 4)}
+        del ws
+    moe = synthetic.moe_case()
+    bank = torch_ops.ExpertBank(moe["experts"], device="cuda")
+    csr = wq.wq_csr_from_routes(moe["routes"], moe["n_tokens"], moe["top_k"], moe["n_expert"])
+    dcsr = {key: torch_ops.to_device(np.asarray(csr[key], np.int32), "cuda")
+            for key in ("ex_ids", "ex_off", "ex_pairs", "pair_tok")}
+    a = torch_ops.to_device(moe["a"], "cuda")
+    y = torch.empty((csr["n_pairs"], moe["n"]), dtype=torch.float16, device="cuda")
+    wts = torch_ops.to_device(synthetic.routing_weights(19, moe["n_tokens"], 2), "cuda")
+
+    def moe_step(i):
+        torch_ops.grouped_gemm(a, bank, csr, y, device_csr=dcsr, topk_weights=wts)
+    sec = timed_loop(torch, moe_step, max(5, steps // 8), warmup)
+    out["moe_routing_weights"] = {
+        "workload": "MoE config with a per-pair fp32 routing-weight multiply",
+        "us": round(sec * 1e6, 2),
+        "tflops": round(2.0 * csr["n_pairs"] * moe["n"] * moe["k"] / sec / 1e12, 2)}
+    return out
+
+
 COPY_BYTES = 1 << 30  # plain device copy used to calibrate the HBM byte counters
 
 
@@ -202,6 +272,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extended", action="store_true",
+                    help="skip the timings of the widened features")
     ap.add_argument("--only", choices=["decode", "batched", "prefill", "moe", "tiny", "copy",
                                        "ceiling"],
                     default=None, help="time one workload (profiling runs)")
@@ -298,6 +370,10 @@ def main() -> int:
                 "tflops": round(moe["flops"] / moe["sec"] / 1e12, 2),
                 "mfma_frac": round(moe["flops"] / moe["sec"] / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4)},
     }
+    if not args.no_extended:
+        line["extended"] = bench_extended(torch, torch_ops, args.steps, max(3, args.warmup // 4))
+        print("extended: " + ", ".join(f"{k} {v['us']} us" for k, v in line["extended"].items()),
+              file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.cpu_budget)
     print(json.dumps(line), flush=True)

@@ -154,7 +154,9 @@ def bench_extended(torch, torch_ops, steps, warmup):
             "us": round(sec * 1e6, 2), "tflops": round(flops / sec / 1e12, 2),
             "weight_tbs": round(k * 2 * inter / 2 / sec / 1e12, 4)}
         del ws
-    for name, gs in (("decode", 32), ("decode", -1), ("prefill", 32)):
+    # group 128 at decode shape is the control: the same kernel timed in the same context
+    for name, gs in (("decode", 128), ("decode", 64), ("decode", 32), ("decode", -1),
+                     ("prefill", 32)):
         cfg = synthetic.CONFIGS[name]
         case = synthetic.dense_case(cfg["m"], cfg["k"], cfg["n"], group_size=gs, seed=17)
         w = torch_ops.PackedWeight(case["qweight"], case["scales"], device="cuda",

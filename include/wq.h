@@ -24,8 +24,8 @@
  *    it), 32, 64, or a multiple of 128 dividing k.  The pages also allow the other positive
  *    multiples of 16 dividing k; those fail with WQ_ERR_SHAPE.  The library stores scales
  *    and zero points per unit of U = min(group_size, 128) rows (U = 128 for -1): a larger
- *    group is repeated for each 128-row chunk it covers.  Groups of 32 or 64 rows use the
- *    tiled kernel at every m.
+ *    group is repeated for each 128-row chunk it covers.  Both kernels (small-M and tiled)
+ *    take every supported group size.
  *
  * Library weight layout (produced by the wq_repack_* calls; G = k / 128):
  *  - B: k*n/8 uint32 words (k*n/2 bytes, the plain format's byte count).  For 16-column

@@ -180,6 +180,34 @@ def test_group_sizes_match_oracle(dev, m, k, n, gs, zp, act_order):
     assert_parity(c, oracle_gemm(case), label)
 
 
+# The small-M kernel (m <= 16) with 2 or 4 scale groups per 128-row chunk: one split over a
+# 32- or 64-chunk span, automatic and requested (ragged) splits, act_order, zero points, and
+# a K that is not a multiple of the waves' share.
+SMALL_GROUP_SHAPES = [
+    # m, k, n, group_size, zp, act_order, fp32_reduce, split_k
+    (1, 4096, 512, 32, False, False, False, 0),
+    (1, 4096, 512, 32, True, False, True, 0),
+    (5, 2048, 256, 64, True, False, True, 3),
+    (16, 1024, 512, 32, True, True, False, 0),
+    (3, 8192, 256, 64, False, False, False, 0),
+    (8, 8192, 256, 32, True, False, False, 0),
+    (2, 3968, 256, 32, False, False, True, 5),
+    (12, 1536, 768, 64, False, True, True, 0),
+    (1, 2048, 256, -1, True, False, True, 0),
+]
+
+
+@pytest.mark.parametrize("m,k,n,gs,zp,act_order,fp32,split", SMALL_GROUP_SHAPES)
+def test_small_m_group_sizes_match_oracle(dev, m, k, n, gs, zp, act_order, fp32, split):
+    label = (f"small-M group_size={gs} m={m} k={k} n={n} zp={zp} act_order={act_order} "
+             f"fp32={fp32} split={split}")
+    say(label)
+    case = synthetic.dense_case(m, k, n, zp=zp, act_order=act_order, group_size=gs,
+                                seed=3500 + m + k + gs)
+    c = gpu_gemm(case, dev, fp32_reduce=fp32, split_k=split)
+    assert_parity(c, oracle_gemm(case), label)
+
+
 @pytest.mark.parametrize("gs", [-1, 32, 64, 256, 1024])
 def test_group_size_repack_and_dequant_bitwise(dev, gs):
     k, n = 1024, 512
@@ -486,7 +514,11 @@ def test_interleave_gate_up_bitwise(dev, bits, rows, cols):
                                                     # and beyond it the tiled kernel
                                                     (1, 4096, 1024, False, False, 128),
                                                     (4, 8192, 256, True, False, 128),
-                                                    (2, 12288, 256, False, False, 128)])
+                                                    (2, 12288, 256, False, False, 128),
+                                                    # the paired form with 32/64-row groups
+                                                    (1, 4096, 512, False, False, 32),
+                                                    (4, 2048, 256, True, False, 64),
+                                                    (2, 8192, 256, True, False, 32)])
 def test_swiglu_activation_matches_oracle(dev, m, k, i, zp, act_order, gs):
     label = f"swiglu m={m} k={k} i={i} zp={zp} act_order={act_order} group_size={gs}"
     say(label)

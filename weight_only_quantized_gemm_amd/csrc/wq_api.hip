@@ -66,7 +66,7 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 // groups are shared by 4 or 8 waves, at most 8 groups per wave.
 // Plan of the small-M kernel's SwiGLU (paired) form: no split, 8 or 16 waves (4 or 8 per
 // block along K), or false when no plan fits (the tiled kernel then computes it).
-bool plan_small_pair(int m, int k, wq::SmallPlan* plan) {
+bool plan_small_pair(int m, int k, int gpc, wq::SmallPlan* plan) {
   const int groups = k / kGroupSize;
   for (int waves = 8; waves <= 16; waves *= 2) {
     const int per_wave = (groups + waves / 2 - 1) / (waves / 2);
@@ -76,6 +76,7 @@ bool plan_small_pair(int m, int k, wq::SmallPlan* plan) {
     p.splits = 1;
     p.depth = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 8;
     p.pair = true;
+    p.gpc = gpc;
     if (wq::small_plan_fits(m, k, p)) {
       *plan = p;
       return true;
@@ -84,7 +85,8 @@ bool plan_small_pair(int m, int k, wq::SmallPlan* plan) {
   return false;
 }
 
-bool plan_small(int m, int n, int k, uint32_t flags, int requested, wq::SmallPlan* plan) {
+bool plan_small(int m, int n, int k, uint32_t flags, int requested, int gpc,
+                wq::SmallPlan* plan) {
   const int groups = k / kGroupSize;
   const bool fp32 = (flags & WQ_FLAG_FP32_REDUCE) != 0;
   int s = 1;
@@ -106,6 +108,7 @@ bool plan_small(int m, int n, int k, uint32_t flags, int requested, wq::SmallPla
       p.waves = waves;
       p.splits = s;
       p.depth = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 8;
+      p.gpc = gpc;
       if (wq::small_plan_fits(m, k, p)) {
         *plan = p;
         return true;
@@ -271,13 +274,12 @@ int wq_gemm(const wq_gemm_args* args) {
   if (p.split_k > 1 && !(p.flags & WQ_FLAG_FP32_REDUCE)) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
   const bool swiglu = (p.flags & WQ_FLAG_SWIGLU) != 0;
 
-  // Plan, and check the workspace the plan needs, before anything is enqueued.  The small-M
-  // kernel reads one scale per 128 rows, so smaller groups take the tiled kernel.
+  // Plan, and check the workspace the plan needs, before anything is enqueued.
   const int gpc = subgroups(p.group_size);
   wq::SmallPlan plan{};
-  const bool small = gpc == 1 && p.m <= 16 &&
-                     (swiglu ? plan_small_pair(p.m, p.k, &plan)
-                             : plan_small(p.m, p.n, p.k, p.flags, p.split_k, &plan));
+  const bool small = p.m <= 16 &&
+                     (swiglu ? plan_small_pair(p.m, p.k, gpc, &plan)
+                             : plan_small(p.m, p.n, p.k, p.flags, p.split_k, gpc, &plan));
   float* partials = nullptr;
   if (small && plan.splits > 1) {
     const size_t need = (size_t)plan.splits * p.m * p.n * sizeof(float);

@@ -35,11 +35,25 @@ struct SmallPlan {
   int depth;       // groups of K per wave, all loaded before arithmetic (1, 2, 4 or 8)
   bool pair;       // SwiGLU epilogue: a gate/up pair of blocks per work-group, half the
                    // waves on each (n counts both; c is [m][n/2]; splits must be 1)
+  int gpc;         // scale groups per 128-row chunk: 1, or 2 / 4 for 64- / 32-row groups
 };
 bool small_plan_fits(int m, int k, const SmallPlan& plan);
 hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* b,
                              const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                              const SmallPlan& plan, float* partials, hipStream_t stream);
+// The instances of each scale-group count (wq_gemm_small.hip, _g2.hip, _g4.hip).
+#define WQ_SMALL_GPC_DECL(G)                                                                \
+  hipError_t launch_small_g##G(const uint16_t* a, int lda, int m, const uint32_t* b,        \
+                               const uint16_t* s, const uint32_t* z, uint16_t* c, int n,    \
+                               int k, const SmallPlan& plan, float* partials,               \
+                               hipStream_t stream);
+WQ_SMALL_GPC_DECL(1)
+WQ_SMALL_GPC_DECL(2)
+WQ_SMALL_GPC_DECL(4)
+#undef WQ_SMALL_GPC_DECL
+// c = fp16(sum of the fp32 partials [splits][m][n] in split order).
+hipError_t launch_reduce_splits(const float* partials, uint16_t* c, int m, int n, int splits,
+                                hipStream_t stream);
 
 // Tiled kernel (wq_gemm_tile.hip): 256 x 256 output tiles on 8 waves of 128 x 64.
 constexpr int kTileM = 256;

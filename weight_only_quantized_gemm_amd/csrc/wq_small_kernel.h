@@ -1,0 +1,323 @@
+// Small-M W4A16 GEMM (m <= 16): decode and small batches, bound by the weight stream.
+//
+// One 16x16x32 fp16 MFMA block covers all m rows (rows >= m read as zero), so the packed
+// weights are read exactly once.  A work-group owns one 16-column block and a range of K
+// groups; its WAVES waves split that range, each streaming one 1 KiB layout chunk per
+// 128-row group with a single non-temporal 16-byte load per lane.  All of a wave's weight
+// loads are issued before any arithmetic and consumed in issue order, so the weight
+// stream is never stalled behind compute.  Activations, scales and zero points of the
+// work-group's range are staged once in LDS.  Codes become exact fp16 integers (q - z) in
+// registers; each scale group's MFMA partial is scaled by its fp16 group scale in fp32 and
+// accumulated in fp32; the waves' sums are added in wave order.
+//
+// GPC is the number of scale groups per 128-row chunk (1; 2 for 64-row groups; 4 for
+// 32-row groups).  The chunk's four 32-row MFMA steps then form GPC separate partials, one
+// per group, each scaled before it is added.  Scales and zero points are stored per unit of
+// min(group_size, 128) rows, so a chunk owns GPC consecutive unit rows of its column block.
+//
+// This header holds the kernel template and its launch chain; each translation unit that
+// includes it instantiates one GPC (the instances of the three counts compile in parallel).
+#pragma once
+#include "wq_device.h"
+#include "wq_internal.h"
+
+namespace wq {
+namespace {
+
+// LDS of one work-group: 160 KiB on gfx950, shared by the statically sized scale, zero-point
+// and reduction buffers and the dynamically sized activation slice (fp16 [m][span*128],
+// padded to a whole number of staging rounds).
+constexpr int kLdsBytes = 160 * 1024;
+constexpr int kMaxSpan = 64;   // groups per work-group covered by the staged scales
+
+// Static LDS of an instance (see the kernel's __shared__ arrays), an upper bound over ZP.
+// The staged scales take 2*GPC dwords per thread: NB blocks x kMaxSpan chunks x 8 dwords x
+// GPC fit since a work-group has at least 4 waves per block.
+constexpr long small_static_lds(int waves, int gpc) {
+  return 2L * gpc * waves * 64 * 4       // s_lds
+         + (long)waves * 64 * 8          // z_lds
+         + (long)waves * 64 * 16;        // red
+}
+
+// The kernel body is branch-free up to the arithmetic: every load is issued
+// unconditionally (addresses are clamped into the tensors) and ragged ends are masked by
+// value, so the compiler's in-order load counting can let LDS writes wait for the
+// activations alone and each group wait for its own weight chunk, while the rest of the
+// weight stream stays in flight.
+// PAIR (the SwiGLU epilogue): the work-group owns a gate/up pair of 16-column blocks
+// (2t, 2t+1, as wq_interleave_gate_up pairs them); its first half of waves streams the gate
+// block, the second half the up block, both over the same K range and staged activations,
+// and the reduction writes fp16(silu(g) * u) to column 16t + c of the [m][n/2] activation.
+template <bool ZP, int WAVES, int GW, int STAGE, bool PAIR, int GPC>
+__global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
+    const f16* __restrict__ a, int lda, int m, const u32x4* __restrict__ b,
+    const f16* __restrict__ s, const u32x2* __restrict__ z, f16* __restrict__ c, int n,
+    int groups, int splits, float* __restrict__ partials) {
+  constexpr int T = WAVES * 64;
+  constexpr int NB = PAIR ? 2 : 1;            // column blocks of the work-group
+  constexpr int KW = WAVES / NB;              // waves splitting K for one block
+  constexpr int SU = 2 * GPC;                 // staged scale dwords per thread
+  constexpr int JQ = 4 / GPC;                 // 32-row MFMA steps per scale group
+  extern __shared__ f16x8 a_lds[];            // [m][span*16] granules (+ padding)
+  __shared__ uint32_t s_lds[SU * T];          // scales, [block][chunk][sub][col] as fp16
+  __shared__ u32x2 z_lds[ZP ? T : 1];         // zero points, [block][chunk][sub]
+  __shared__ f32x4 red[WAVES][64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 15;  // column inside the 16-column block; also the A row of the lane
+  const int qd = lane >> 4;   // which 8 rows of each 32-row MFMA step the lane carries
+  const int half = PAIR ? wave / KW : 0;       // the wave's block of the pair
+  const int kwave = wave - half * KW;          // the wave's index along K
+  const int nb = NB * blockIdx.x + half;
+  const int split = blockIdx.y;
+
+  const int gs0 = (int)((long)groups * split / splits);
+  const int gs1 = (int)((long)groups * (split + 1) / splits);
+  const int span = gs1 - gs0;
+  const int g0 = gs0 + span * kwave / KW;
+  const int g1 = gs0 + span * (kwave + 1) / KW;
+  const int gw = g1 - g0;  // <= GW by the launch plan
+
+  // 1. Activation granules: slot u of this thread is granule tid + u*T of the slice, at row
+  //    r and granule column q; (r, q) advance by a fixed (dr, dq) per slot.
+  const int per_row = span * (kGroup / 8);
+  const int dr = T / per_row;
+  const int dq = T - dr * per_row;
+  int r = tid / per_row;
+  int q = tid - r * per_row;
+  const f16* a_base = a + (long)gs0 * kGroup;
+  f16x8 stage[STAGE];
+#pragma unroll
+  for (int u = 0; u < STAGE; ++u) {
+    const int rr = r < m ? r : m - 1;
+    stage[u] = *reinterpret_cast<const f16x8*>(a_base + (long)rr * lda + 8 * q);
+    q += dq;
+    r += dr;
+    const bool wrap = q >= per_row;
+    q = wrap ? q - per_row : q;
+    r = wrap ? r + 1 : r;
+  }
+  // 2. Scales (8 dwords of fp16 pairs per unit row) and zero points of the range, for each
+  //    of the work-group's blocks ([block][unit] in LDS).  A block holds groups*GPC units.
+  const long units = (long)groups * GPC;
+  const long pair0 = (long)NB * blockIdx.x * units + (long)gs0 * GPC;  // first block's range
+  const uint32_t* s32 = reinterpret_cast<const uint32_t*>(s);
+  const int s_words = span * GPC * 8;
+  uint32_t s_stage[SU];
+#pragma unroll
+  for (int u = 0; u < SU; ++u) {
+    int i = tid + u * T;
+    i = i < NB * s_words ? i : NB * s_words - 1;
+    const int h = PAIR && i >= s_words ? 1 : 0;  // block of the pair holding dword i
+    s_stage[u] = s32[(pair0 + h * units) * 8 + (i - h * s_words)];
+  }
+  u32x2 z_stage = u32x2{0u, 0u};
+  if constexpr (ZP) {
+    const int z_words = span * GPC;
+    const int i = tid < NB * z_words ? tid : NB * z_words - 1;
+    const int h = PAIR && i >= z_words ? 1 : 0;
+    z_stage = z[pair0 + h * units + (i - h * z_words)];
+  }
+
+  // 3. The wave's weight chunks, all in flight before any arithmetic.
+  u32x4 bw[GW];
+#pragma unroll
+  for (int i = 0; i < GW; ++i) {
+    const int g = g0 + (i < gw ? i : gw - 1);
+    bw[i] = __builtin_nontemporal_load(&b[((long)nb * groups + g) * 64 + lane]);
+  }
+
+  // 4. Stage into LDS (waits for the activations and scales only), then sync.
+#pragma unroll
+  for (int u = 0; u < STAGE; ++u) a_lds[tid + u * T] = stage[u];
+#pragma unroll
+  for (int u = 0; u < SU; ++u) s_lds[tid + u * T] = s_stage[u];
+  if constexpr (ZP) z_lds[tid] = z_stage;
+  __syncthreads();
+
+  // 5. Arithmetic.  MFMA rows >= m are never stored, and a row of the product depends on
+  //    its own A row only, so those lanes read row m - 1 instead of selecting zeros.  The
+  //    group scales are read up front and each chunk's activation operands are read from
+  //    LDS while the previous chunk's MFMAs run, so that no LDS round trip sits between a
+  //    weight chunk's arrival and its products.
+  const MagicRegs mr = magic_regs();
+  const int arow = (col < m ? col : m - 1) * per_row;
+  const f16* s_half = reinterpret_cast<const f16*>(s_lds);
+  int gl[GW];  // chunk of step i inside the staged range (clamped for the masked steps)
+  float sc[GW][GPC];
+#pragma unroll
+  for (int i = 0; i < GW; ++i) {
+    gl[i] = g0 - gs0 + (i < gw ? i : gw - 1);
+#pragma unroll
+    for (int t = 0; t < GPC; ++t) {
+      const float v = (float)s_half[((half * span + gl[i]) * GPC + t) * 16 + col];
+      sc[i][t] = i < gw ? v : 0.f;
+    }
+  }
+  f16x8 an[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) an[j] = a_lds[arow + gl[0] * 16 + 4 * j + qd];
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < GW; ++i) {
+    f16x8 ac[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ac[j] = an[j];
+    if (i + 1 < GW) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) an[j] = a_lds[arow + gl[i + 1] * 16 + 4 * j + qd];
+    }
+    // With eight groups per wave, pin the prefetch ahead of this group's work (measured
+    // faster for the decode shape, slower for shallower pipelines).
+    if constexpr (GW >= 8) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < GPC; ++t) {
+      const ZeroOffsets zo =
+          zero_offsets(ZP ? zero_code(z_lds[(half * span + gl[i]) * GPC + t], col) : 8);
+      f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jj = 0; jj < JQ; ++jj) {
+        const int j = t * JQ + jj;
+        p = mfma16x16x32(ac[j], dequant8(bw[i][j], zo, mr), p);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sc[i][t], p[e], acc[e]);
+    }
+    if constexpr (GW >= 8) __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // Work-group reduce over the waves, in wave order.
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  if constexpr (PAIR) {
+    f32x4 gs = red[0][lane], us = red[KW][lane];
+#pragma unroll
+    for (int w = 1; w < KW; ++w) {
+      gs += red[w][lane];
+      us += red[KW + w][lane];
+    }
+    const long colj = (long)blockIdx.x * 16 + col;  // column of the [m][n/2] activation
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 4 * qd + e;
+      if (row < m) c[(long)row * (n / 2) + colj] = (f16)silu_times(gs[e], us[e]);
+    }
+    return;
+  }
+  f32x4 tot = red[0][lane];
+#pragma unroll
+  for (int w = 1; w < WAVES; ++w) tot += red[w][lane];
+
+  // Output layout of the 16x16 block: lane holds rows 4*qd + e of column `col`.
+  const long colx = (long)nb * 16 + col;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int row = 4 * qd + e;
+    if (row >= m) continue;
+    if (splits == 1)
+      c[(long)row * n + colx] = (f16)tot[e];
+    else
+      partials[((long)split * m + row) * n + colx] = tot[e];
+  }
+}
+
+// Staging slots per thread for an activation slice of m rows and `span` groups.
+inline int stage_slots(int m, int span, int waves) {
+  const long granules = (long)m * span * (kGroup / 8);
+  const long per_slot = (long)waves * 64;
+  return (int)((granules + per_slot - 1) / per_slot);
+}
+
+inline int round_slots(int slots) {
+  return slots <= 1 ? 1 : slots <= 2 ? 2 : slots <= 4 ? 4 : slots <= 8 ? 8 : 16;
+}
+
+template <bool ZP, int WAVES, int GW, int STAGE, bool PAIR, int GPC>
+hipError_t launch_small_t(const uint16_t* a, int lda, int m, const uint32_t* b,
+                          const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
+                          int splits, float* partials, hipStream_t stream) {
+  const int groups = k / kGroup;
+  // The activation slice of this instance (its size is fixed by STAGE and WAVES).
+  constexpr size_t lds = (size_t)STAGE * WAVES * 64 * sizeof(f16x8);
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
+  const dim3 grid(n / (PAIR ? 32 : 16), splits);
+  hipLaunchKernelGGL((gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC>), grid,
+                     dim3(WAVES * 64), lds, stream, reinterpret_cast<const f16*>(a), lda, m,
+                     reinterpret_cast<const u32x4*>(b), reinterpret_cast<const f16*>(s),
+                     reinterpret_cast<const u32x2*>(z), reinterpret_cast<f16*>(c), n, groups,
+                     splits, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  return launch_reduce_splits(partials, c, m, n, splits, stream);
+}
+
+template <bool ZP, int WAVES, int GW, bool PAIR, int GPC>
+hipError_t launch_small_stage(const uint16_t* a, int lda, int m, const uint32_t* b,
+                              const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
+                              const SmallPlan& plan, float* partials, hipStream_t stream) {
+  const int span = (k / kGroup + plan.splits - 1) / plan.splits;
+#define WQ_SMALL(ST)                                                                         \
+  launch_small_t<ZP, WAVES, GW, ST, PAIR, GPC>(a, lda, m, b, s, z, c, n, k, plan.splits,     \
+                                               partials, stream)
+  switch (round_slots(stage_slots(m, span, WAVES))) {
+    case 1: return WQ_SMALL(1);
+    case 2: return WQ_SMALL(2);
+    case 4: return WQ_SMALL(4);
+    case 8: return WQ_SMALL(8);
+    default: return WQ_SMALL(16);
+  }
+#undef WQ_SMALL
+}
+
+template <bool ZP, int WAVES, bool PAIR, int GPC>
+hipError_t launch_small_gw(const uint16_t* a, int lda, int m, const uint32_t* b,
+                           const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
+                           const SmallPlan& plan, float* partials, hipStream_t stream) {
+#define WQ_SMALL(GWV)                                                                          \
+  launch_small_stage<ZP, WAVES, GWV, PAIR, GPC>(a, lda, m, b, s, z, c, n, k, plan, partials, \
+                                                stream)
+  switch (plan.depth) {
+    case 1: return WQ_SMALL(1);
+    case 2: return WQ_SMALL(2);
+    case 4: return WQ_SMALL(4);
+    default: return WQ_SMALL(8);
+  }
+#undef WQ_SMALL
+}
+
+template <bool ZP, int GPC>
+hipError_t launch_small_waves(const uint16_t* a, int lda, int m, const uint32_t* b,
+                              const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
+                              const SmallPlan& plan, float* partials, hipStream_t stream) {
+  if (plan.pair) {
+    if (plan.waves == 16)
+      return launch_small_gw<ZP, 16, true, GPC>(a, lda, m, b, s, z, c, n, k, plan, partials,
+                                                stream);
+    return launch_small_gw<ZP, 8, true, GPC>(a, lda, m, b, s, z, c, n, k, plan, partials,
+                                             stream);
+  }
+  if (plan.waves == 8)
+    return launch_small_gw<ZP, 8, false, GPC>(a, lda, m, b, s, z, c, n, k, plan, partials,
+                                              stream);
+  return launch_small_gw<ZP, 4, false, GPC>(a, lda, m, b, s, z, c, n, k, plan, partials,
+                                            stream);
+}
+
+// Entry of one GPC: the plan has been checked by small_plan_fits.
+template <int GPC>
+hipError_t launch_small_gpc(const uint16_t* a, int lda, int m, const uint32_t* b,
+                            const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
+                            const SmallPlan& plan, float* partials, hipStream_t stream) {
+  if (z != nullptr)
+    return launch_small_waves<true, GPC>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
+  return launch_small_waves<false, GPC>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
+}
+
+}  // namespace
+}  // namespace wq

@@ -155,8 +155,8 @@ def bench_extended(torch, torch_ops, steps, warmup):
             "weight_tbs": round(k * 2 * inter / 2 / sec / 1e12, 4)}
         del ws
     # group 128 at decode shape is the control: the same kernel timed in the same context
-    for name, gs in (("decode", 128), ("decode", 64), ("decode", 32), ("decode", -1),
-                     ("prefill", 32)):
+    for name, gs in (("decode", 128), ("decode", 64), ("decode", 32), ("decode", 16),
+                     ("decode", -1), ("prefill", 32), ("prefill", 16)):
         cfg = synthetic.CONFIGS[name]
         case = synthetic.dense_case(cfg["m"], cfg["k"], cfg["n"], group_size=gs, seed=17)
         w = torch_ops.PackedWeight(case["qweight"], case["scales"], device="cuda",
@@ -209,7 +209,7 @@ def bench_copy(torch, steps, warmup):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_hbm_traffic.txt")
-SMALL_SOURCE = os.path.join(ROOT, "weight_only_quantized_gemm_amd", "csrc", "wq_gemm_small.hip")
+SMALL_SOURCE = os.path.join(ROOT, "weight_only_quantized_gemm_amd", "csrc", "wq_small_kernel.h")
 
 
 def source_hash(path: str) -> str:

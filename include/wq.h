@@ -21,11 +21,11 @@
  *  - Validation happens before any launch (fail closed); nothing is enqueued on error.
  *  - Shapes: k % 128 == 0, n % 256 == 0.  group_size (rows of K per scale / zero point) is
  *    -1 (channelwise: one group over all of K, as transformer.rs `marlin_num_groups` maps
- *    it), 32, 64, or a multiple of 128 dividing k.  The pages also allow the other positive
- *    multiples of 16 dividing k; those fail with WQ_ERR_SHAPE.  The library stores scales
- *    and zero points per unit of U = min(group_size, 128) rows (U = 128 for -1): a larger
- *    group is repeated for each 128-row chunk it covers.  Both kernels (small-M and tiled)
- *    take every supported group size.
+ *    it) or a positive multiple of 16 dividing k (the pages' rule); anything else fails
+ *    with WQ_ERR_SHAPE.  The library stores scales and zero points per unit of
+ *    U = gcd(group_size, 128) rows (U = 128 for -1; so 16, 32, 64 or 128): a group is
+ *    repeated for each unit it covers.  Both kernels (small-M and tiled) take every
+ *    supported group size.
  *
  * Library weight layout (produced by the wq_repack_* calls; G = k / 128):
  *  - B: k*n/8 uint32 words (k*n/2 bytes, the plain format's byte count).  For 16-column

@@ -91,21 +91,35 @@ def interleave_gate_up(gate: np.ndarray, up: np.ndarray, cols_per_elem: int = 1)
     return out
 
 
+def unit_rows(group_size: int) -> int:
+    """Rows of K per stored scale / zero-point row: the largest power of two dividing both
+    the group size and the 128-row chunk (16, 32, 64 or 128; 128 when channelwise), so that
+    every unit lies inside one group and one chunk."""
+    if group_size == -1:
+        return CHUNK
+    unit = CHUNK
+    while group_size % unit:
+        unit //= 2
+    return unit
+
+
 def chunk_rows(values: np.ndarray, k: int | None, group_size: int) -> np.ndarray:
-    """Per-group rows [K/group_size][...] -> the library's scale rows: one per group for
-    groups of fewer than 128 rows, else one per 128-row chunk of K, chunk g taking the row
-    of the group holding rows 128g..128g+127 (the single row when channelwise)."""
+    """Per-group rows [K/group_size][...] -> the library's stored rows, one per unit of
+    unit_rows(group_size) rows of K: unit u takes the row of the group holding its rows
+    (the single row when channelwise)."""
     v = np.asarray(values)
-    if k is None or group_size == CHUNK or 0 < group_size < CHUNK:
-        return v  # one stored row per group (groups below 128 rows are stored as they are)
-    chunks = k // CHUNK
-    src = np.zeros(chunks, dtype=np.int64) if group_size == -1 else \
-        (np.arange(chunks) * CHUNK) // group_size
+    unit = unit_rows(group_size)
+    if k is None:
+        if unit != group_size:
+            raise ValueError(f"group size {group_size} needs k to lay out its units")
+        return v  # one stored row per group
+    first_row = np.arange(k // unit, dtype=np.int64) * unit
+    src = np.zeros(k // unit, dtype=np.int64) if group_size == -1 else first_row // group_size
     return v[src]
 
 
 def repack_scales(scales: np.ndarray, k: int | None = None, group_size: int = 128) -> np.ndarray:
-    """fp16 [K/group_size][N] -> fp16 [N/16][K/U][16] (flattened), U = min(group_size, 128)."""
+    """fp16 [K/group_size][N] -> fp16 [N/16][K/U][16] (flattened), U = unit_rows(group_size)."""
     s = chunk_rows(np.asarray(scales, dtype=np.float16), k, group_size)
     groups, n_total = s.shape
     return s.reshape(groups, n_total // 16, 16).transpose(1, 0, 2).reshape(-1).copy()

@@ -86,11 +86,12 @@ def call_gemm(L, **over):
     (dict(m=0), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
     (dict(lda=512), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
     (dict(lda=1028), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
-    # group sizes: -1, 32, 64 and multiples of 128 dividing k are supported; others are not
-    (dict(group_size=16), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
-    (dict(group_size=48), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
-    (dict(group_size=96), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
-    (dict(group_size=192), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
+    # group sizes: -1 and multiples of 16 dividing k (k = 1024 here) are supported
+    (dict(group_size=8), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),      # not a multiple of 16
+    (dict(group_size=24), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),     # not a multiple of 16
+    (dict(group_size=48), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),     # does not divide k
+    (dict(group_size=96), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),     # does not divide k
+    (dict(group_size=192), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),    # does not divide k
     (dict(group_size=2048), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),   # does not divide k
     (dict(group_size=-2), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
     (dict(group_size=0), status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
@@ -177,13 +178,14 @@ def test_interleave_gate_up_validation(L):
 
 
 def test_repack_validation_of_group_sizes(L):
-    # k = 1024: 256 and 1024 divide it, 768 does not; -1 is channelwise; 32 and 64 are kept
-    # at their own granularity; other multiples of 16 are not supported
-    for gs in (16, 48, 768, -2, 0):
-        assert L.wq_repack_scales(0x1000, 0x2000, 1024, 256, gs, None) == status(
-            STAGE_SHAPE, wq.WQ_ERR_SHAPE), gs
-        assert L.wq_repack_zeros(0x1000, 0x2000, 1024, 256, gs, None) == status(
-            STAGE_SHAPE, wq.WQ_ERR_SHAPE), gs
+    # group sizes are -1 or multiples of 16 dividing k: at k = 1024, 48, 96 and 768 do not
+    # divide it, 8, 24 and 40 are not multiples of 16; at k = 384, 80 does not divide it
+    for k, gs in ((1024, 48), (1024, 96), (1024, 768), (1024, 8), (1024, 24), (1024, 40),
+                  (1024, -2), (1024, 0), (384, 80), (384, 40)):
+        assert L.wq_repack_scales(0x1000, 0x2000, k, 256, gs, None) == status(
+            STAGE_SHAPE, wq.WQ_ERR_SHAPE), (k, gs)
+        assert L.wq_repack_zeros(0x1000, 0x2000, k, 256, gs, None) == status(
+            STAGE_SHAPE, wq.WQ_ERR_SHAPE), (k, gs)
 
 
 def test_act_order_perm_with_other_group_sizes():

@@ -167,6 +167,13 @@ GROUP_SHAPES = [
     (300, 1024, 512, -1, True, False),
     (257, 2048, 256, 1024, False, True),
     (40, 4096, 256, 2048, True, False),
+    # multiples of 16 that are not divisors or multiples of 128: units of 16, 32 or 64 rows
+    (257, 1536, 512, 16, True, False),
+    (300, 384, 256, 48, False, True),
+    (64, 640, 256, 80, True, False),
+    (130, 1152, 512, 96, True, True),
+    (40, 768, 256, 192, False, False),
+    (513, 1280, 256, 320, True, False),
 ]
 
 
@@ -194,6 +201,13 @@ SMALL_GROUP_SHAPES = [
     (2, 3968, 256, 32, False, False, True, 5),
     (12, 1536, 768, 64, False, True, True, 0),
     (1, 2048, 256, -1, True, False, True, 0),
+    # 16-row units (two MFMA passes per step) and units repeated for 48/80/96-row groups
+    (1, 4096, 512, 16, False, False, False, 0),
+    (3, 1536, 256, 48, True, False, True, 0),
+    (16, 768, 512, 16, True, True, False, 0),
+    (7, 3840, 256, 80, False, False, True, 3),
+    (2, 8192, 256, 16, True, False, False, 0),
+    (5, 1152, 512, 96, True, False, False, 0),
 ]
 
 
@@ -208,9 +222,10 @@ def test_small_m_group_sizes_match_oracle(dev, m, k, n, gs, zp, act_order, fp32,
     assert_parity(c, oracle_gemm(case), label)
 
 
-@pytest.mark.parametrize("gs", [-1, 32, 64, 256, 1024])
-def test_group_size_repack_and_dequant_bitwise(dev, gs):
-    k, n = 1024, 512
+@pytest.mark.parametrize("gs,k", [(-1, 1024), (32, 1024), (64, 1024), (256, 1024), (1024, 1024),
+                                  (16, 1024), (48, 768), (80, 1280), (96, 1152)])
+def test_group_size_repack_and_dequant_bitwise(dev, gs, k):
+    n = 512
     say(f"repack/dequant group_size={gs}")
     groups = 1 if gs == -1 else k // gs
     s = synthetic.scales(90, groups, n)
@@ -358,9 +373,9 @@ def test_grouped_matches_oracle(dev, tokens, experts, k, n, zp, weighted):
     assert_parity(y, ref.grouped_w4a16_gemm(moe["a"], ex, ocsr, topk_weights=w), label)
 
 
-@pytest.mark.parametrize("gs", [256, 64, 32])
-def test_grouped_with_other_group_sizes(dev, gs):
-    tokens, experts, k, n = 120, 3, 1024, 256
+@pytest.mark.parametrize("gs,k", [(256, 1024), (64, 1024), (32, 1024), (16, 1024), (48, 768)])
+def test_grouped_with_other_group_sizes(dev, gs, k):
+    tokens, experts, n = 120, 3, 256
     moe = synthetic.moe_case(tokens, experts, k, n, group_size=gs, seed=24)
     for e in moe["experts"]:
         e["group_size"] = gs
@@ -518,7 +533,9 @@ def test_interleave_gate_up_bitwise(dev, bits, rows, cols):
                                                     # the paired form with 32/64-row groups
                                                     (1, 4096, 512, False, False, 32),
                                                     (4, 2048, 256, True, False, 64),
-                                                    (2, 8192, 256, True, False, 32)])
+                                                    (2, 8192, 256, True, False, 32),
+                                                    (1, 768, 256, False, False, 48),
+                                                    (100, 768, 256, True, False, 16)])
 def test_swiglu_activation_matches_oracle(dev, m, k, i, zp, act_order, gs):
     label = f"swiglu m={m} k={k} i={i} zp={zp} act_order={act_order} group_size={gs}"
     say(label)

@@ -7,6 +7,8 @@ decodes words through their hexadecimal digits rather than through shifts.
 
 import struct
 
+import math
+
 import numpy as np
 import pytest
 
@@ -286,6 +288,52 @@ def test_larger_and_channelwise_groups_equal_repeated_128_row_groups():
     # with 256-row groups, row 128 is in group 0 and row 256 in group 1
     assert ref.group_of_rows(1024, 256)[[127, 128, 255, 256]].tolist() == [0, 0, 0, 1]
     assert ref.group_of_rows(1024, -1).max() == 0
+
+
+def test_multiple_of_16_group_sizes_match_bruteforce():
+    """Any multiple of 16 dividing K is a valid group size (16, 48, 80 here, none of which
+    divides 128 or is divided by it): row r belongs to group r // group_size."""
+    m, n = 2, 16
+    for gs, k in ((16, 64), (48, 96), (80, 160)):
+        a = synthetic.activations(70 + gs, m, k)
+        qw = synthetic.qweight_words(71 + gs, k, n)
+        s = synthetic.scales(72 + gs, k // gs, n)
+        zw = synthetic.zero_point_words(73 + gs, k // gs, n)
+        group = [kk // gs for kk in range(k)]
+        want = gemm_bruteforce(a, codes_bruteforce(qw), s, group, zero_codes_bruteforce(zw))
+        got = ref.w4a16_gemm(a, qw, s, zeros=zw, group_size=gs)
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12, err_msg=str(gs))
+
+
+def test_scale_units_are_the_gcd_with_the_chunk():
+    for gs in range(16, 2049, 16):
+        assert layout.unit_rows(gs) == math.gcd(gs, 128), gs
+    assert layout.unit_rows(-1) == 128
+
+
+def test_groups_straddling_chunks_equal_repeated_smaller_units():
+    """A 48-, 96- or 192-row group is stored as 3 units of 16, 32 or 64 rows: its layout and
+    its product equal those of the unit-sized groups with each row repeated 3 times."""
+    k, n, m = 384, 32, 2
+    a = synthetic.activations(80, m, k)
+    qw = synthetic.qweight_words(81, k, n)
+    for gs, unit in ((48, 16), (96, 32), (192, 64)):
+        s = synthetic.scales(82 + gs, k // gs, n)
+        z = synthetic.zero_point_words(83 + gs, k // gs, n)
+        sr, zr = np.repeat(s, 3, axis=0), np.repeat(z, 3, axis=0)
+        assert np.array_equal(layout.repack_scales(s, k, gs), layout.repack_scales(sr, k, unit))
+        assert np.array_equal(layout.repack_zero_points(z, k, gs),
+                              layout.repack_zero_points(zr, k, unit))
+        got = ref.w4a16_gemm(a, qw, s, zeros=z, group_size=gs)
+        want = ref.w4a16_gemm(a, qw, sr, zeros=zr, group_size=unit)
+        assert got.tolist() == want.tolist(), gs
+    # 16-row units by hand: block nb, unit u, column c
+    s = synthetic.scales(90, 4, 32)
+    rs = layout.repack_scales(s, 64, 16)
+    for nb in range(2):
+        for u in range(4):
+            for c in range(16):
+                assert rs[(nb * 4 + u) * 16 + c] == s[u, 16 * nb + c]
 
 
 def test_act_order_with_256_row_groups_equals_plain_product():

@@ -12,7 +12,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libwq.so")
 SOURCES = ["wq_api.hip", "wq_repack.hip", "wq_gemm_small.hip", "wq_gemm_small_g2.hip",
-           "wq_gemm_small_g4.hip", "wq_gemm_tile.hip", "wq_measure.hip"]
+           "wq_gemm_small_g4.hip", "wq_gemm_small_g8.hip", "wq_gemm_tile.hip",
+           "wq_measure.hip"]
 OBJ_DIR = os.path.join(PKG, "_build")  # per-source objects (git-ignored)
 
 
@@ -56,7 +57,7 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
             if lines:
                 sys.stderr.write("\n".join(lines) + "\n")
     tmp = LIB + ".tmp"
-    link = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + \
+    link = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp] + \
         [obj for obj, _ in results]
     res = subprocess.run(link, capture_output=True, text=True)
     if res.returncode != 0:

@@ -35,12 +35,12 @@ int check_ptr(const void* p, size_t align) {
 // 128-row chunk it covers).  The pages also allow the other positive multiples of 16
 // dividing K; those are rejected here.
 bool chunk_group_size(int k, int group_size) {
-  if (group_size == -1 || group_size == 32 || group_size == 64) return true;
-  return group_size > 0 && group_size % kGroupSize == 0 && k % group_size == 0;
+  if (group_size == -1) return true;
+  return group_size > 0 && group_size % 16 == 0 && k % group_size == 0;
 }
 
-// Scale sub-groups per 128 rows of K.
-int subgroups(int group_size) { return group_size == 32 ? 4 : group_size == 64 ? 2 : 1; }
+// Scale units per 128 rows of K (units of gcd(group_size, 128) rows: 1, 2, 4 or 8).
+int subgroups(int k, int group_size) { return kGroupSize / wq::scale_unit_rows(k, group_size); }
 
 // k % 128 == 0, n % 256 == 0, a supported group_size, and byte extents that fit.
 int check_kn(int k, int n, int group_size) {
@@ -275,7 +275,7 @@ int wq_gemm(const wq_gemm_args* args) {
   const bool swiglu = (p.flags & WQ_FLAG_SWIGLU) != 0;
 
   // Plan, and check the workspace the plan needs, before anything is enqueued.
-  const int gpc = subgroups(p.group_size);
+  const int gpc = subgroups(p.k, p.group_size);
   wq::SmallPlan plan{};
   const bool small = p.m <= 16 &&
                      (swiglu ? plan_small_pair(p.m, p.k, gpc, &plan)
@@ -438,7 +438,7 @@ int wq_grouped_gemm(const wq_grouped_args* args) {
   g.k = p.k;
   g.n = p.n;
   g.swiglu = (p.flags & WQ_FLAG_SWIGLU) != 0;
-  g.gpc = subgroups(p.group_size);
+  g.gpc = subgroups(p.k, p.group_size);
   const hipError_t e = wq::launch_grouped_tile(g, as_stream(p.stream));
   return e == hipSuccess ? 0 : hip_fail(e);
 }

@@ -60,7 +60,7 @@ hipError_t launch_small_g1(const uint16_t* a, int lda, int m, const uint32_t* b,
 
 bool small_plan_fits(int m, int k, const SmallPlan& plan) {
   const int groups = k / kGroup;
-  if (plan.gpc != 1 && plan.gpc != 2 && plan.gpc != 4) return false;
+  if (plan.gpc != 1 && plan.gpc != 2 && plan.gpc != 4 && plan.gpc != 8) return false;
   if (plan.splits < 1 || plan.splits > groups) return false;
   if (plan.pair && plan.splits != 1) return false;  // the SwiGLU epilogue needs whole sums
   const int span = (groups + plan.splits - 1) / plan.splits;
@@ -72,7 +72,8 @@ bool small_plan_fits(int m, int k, const SmallPlan& plan) {
   if ((span + kw - 1) / kw > plan.depth || plan.depth > 8) return false;
   const int slots = stage_slots(m, span, plan.waves);
   const long dynamic = (long)round_slots(slots) * plan.waves * 64 * (long)sizeof(f16x8);
-  return slots <= 16 && dynamic + small_static_lds(plan.waves, plan.gpc) <= kLdsBytes;
+  return slots <= 16 &&
+         dynamic + small_static_lds(plan.waves, plan.pair, plan.gpc) <= kLdsBytes;
 }
 
 hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* b,
@@ -82,6 +83,7 @@ hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* 
   switch (plan.gpc) {
     case 2: return launch_small_g2(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
     case 4: return launch_small_g4(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
+    case 8: return launch_small_g8(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
     default: return launch_small_g1(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
   }
 }

@@ -69,15 +69,15 @@ constexpr int kDmaB = 2;
 constexpr int kWaitEven = kDmaA + kDmaB;
 static_assert(kDmaA == 4 && 2 * kWaves == kBlocks, "load split assumes 8 waves, 256 x 256");
 
-// Scale groups smaller than 128 rows: GPC = 128 / group_size sub-groups (1, 2 or 4) per
-// 128-row group.  A group's SZ data is GPC x 128 dwords of scales (16 blocks x 16 fp16 per
-// sub-group) then GPC x 32 words of zero points, loaded 4 bytes per lane (kDmaS loads per
-// wave).  With one sub-group its scales are read once, a group ahead, so two LDS slots
+// Scale units smaller than 128 rows: scales and zero points are stored per unit of
+// gcd(group_size, 128) rows, GPC = 1, 2, 4 or 8 sub-groups per 128-row group.  A group's SZ
+// data is GPC x 128 dwords of scales (16 blocks x 16 fp16 per sub-group) then GPC x 32
+// words of zero points, loaded 4 bytes per lane (kDmaS loads per wave).  With one sub-group its scales are read once, a group ahead, so two LDS slots
 // suffice; with several, a group reads its own slot while the scales of two groups ahead
 // arrive, hence three.
 template <int GPC>
 struct SzPlan {
-  static constexpr int kDmaS = GPC == 4 ? 2 : 1;
+  static constexpr int kDmaS = GPC == 8 ? 3 : GPC == 4 ? 2 : 1;
   static constexpr int kSlots = GPC == 1 ? 2 : 3;
   static constexpr int kScaleWords = 128 * GPC;
   static constexpr int kWaitOdd = kDmaS + kDmaA;
@@ -85,7 +85,8 @@ struct SzPlan {
   static_assert(kWaitPrologue < 64, "vmcnt holds 6 bits");
   static_assert(160 * GPC <= kDmaS * kThreads, "SZ data fits the loads");
 };
-constexpr int kSzSlotWords = 2 * kThreads;  // room for two loads per wave
+constexpr int kSzSlotWords = 3 * kThreads;  // room for three loads per wave
+static_assert(SzPlan<8>::kDmaS * kThreads <= kSzSlotWords, "SZ loads fit a slot");
 
 // Scheduling-group masks (instruction classes of the AMDGPU scheduler hints).
 constexpr int kSchedVALU = 0x002;
@@ -640,6 +641,7 @@ hipError_t launch_tile_t(const TileArgs& p, bool zp, int gpc, hipStream_t stream
     case 1: return launch_tile_g<GROUPED, SWIGLU, 1>(p, zp, stream);
     case 2: return launch_tile_g<GROUPED, SWIGLU, 2>(p, zp, stream);
     case 4: return launch_tile_g<GROUPED, SWIGLU, 4>(p, zp, stream);
+    case 8: return launch_tile_g<GROUPED, SWIGLU, 8>(p, zp, stream);
     default: return hipErrorInvalidValue;
   }
 }

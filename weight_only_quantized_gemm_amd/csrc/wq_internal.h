@@ -10,9 +10,9 @@ namespace wq {
 // Repack / export / gather kernels (wq_repack.hip).
 hipError_t launch_repack_b(const uint32_t* qweight, const int32_t* perm, uint32_t* out, int k,
                            int n, hipStream_t stream);
-// group_size: -1 (channelwise), 32, 64 or a multiple of 128 dividing k.  The output holds
-// one entry per unit of min(group_size, 128) rows of K (a larger group is repeated for
-// each 128-row chunk it covers).
+// group_size: -1 (channelwise) or a multiple of 16 dividing k.  The output holds one entry
+// per unit of gcd(group_size, 128) rows of K (128 for -1): a group is repeated for each
+// unit it covers.
 int scale_unit_rows(int k, int group_size);
 hipError_t launch_repack_scales(const uint16_t* s, uint16_t* out, int k, int n,
                                 int group_size, hipStream_t stream);
@@ -35,13 +35,13 @@ struct SmallPlan {
   int depth;       // groups of K per wave, all loaded before arithmetic (1, 2, 4 or 8)
   bool pair;       // SwiGLU epilogue: a gate/up pair of blocks per work-group, half the
                    // waves on each (n counts both; c is [m][n/2]; splits must be 1)
-  int gpc;         // scale groups per 128-row chunk: 1, or 2 / 4 for 64- / 32-row groups
+  int gpc;         // scale units per 128-row chunk: 1, 2, 4 or 8 (units of 128/gpc rows)
 };
 bool small_plan_fits(int m, int k, const SmallPlan& plan);
 hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* b,
                              const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                              const SmallPlan& plan, float* partials, hipStream_t stream);
-// The instances of each scale-group count (wq_gemm_small.hip, _g2.hip, _g4.hip).
+// The instances of each scale-unit count (wq_gemm_small.hip, _g2.hip, _g4.hip, _g8.hip).
 #define WQ_SMALL_GPC_DECL(G)                                                                \
   hipError_t launch_small_g##G(const uint16_t* a, int lda, int m, const uint32_t* b,        \
                                const uint16_t* s, const uint32_t* z, uint16_t* c, int n,    \
@@ -50,6 +50,7 @@ hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* 
 WQ_SMALL_GPC_DECL(1)
 WQ_SMALL_GPC_DECL(2)
 WQ_SMALL_GPC_DECL(4)
+WQ_SMALL_GPC_DECL(8)
 #undef WQ_SMALL_GPC_DECL
 // c = fp16(sum of the fp32 partials [splits][m][n] in split order).
 hipError_t launch_reduce_splits(const float* partials, uint16_t* c, int m, int n, int splits,
@@ -80,7 +81,7 @@ struct GroupedProblem {
   uint16_t* y;
   int n_expert, n_active, n_pairs, n_tokens, k, n;
   bool swiglu;            // SwiGLU epilogue: y is [n_pairs][n/2]
-  int gpc;                // scale sub-groups per 128 rows of K
+  int gpc;                // scale units per 128 rows of K (1, 2, 4 or 8)
 };
 hipError_t launch_grouped_tile(const GroupedProblem& p, hipStream_t stream);
 

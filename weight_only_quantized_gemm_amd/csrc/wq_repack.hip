@@ -245,7 +245,14 @@ hipError_t launch_repack_b(const uint32_t* qweight, const int32_t* perm, uint32_
 
 int scale_unit_rows(int k, int group_size) {
   (void)k;
-  return group_size > 0 && group_size < kGroup ? group_size : kGroup;
+  if (group_size <= 0) return kGroup;  // channelwise: one unit per 128-row chunk
+  int a = group_size, b = kGroup;      // gcd(group_size, 128): 16, 32, 64 or 128
+  while (b != 0) {
+    const int t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
 }
 
 hipError_t launch_repack_scales(const uint16_t* s, uint16_t* out, int k, int n,

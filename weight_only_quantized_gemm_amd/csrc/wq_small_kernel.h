@@ -10,13 +10,15 @@
 // registers; each scale group's MFMA partial is scaled by its fp16 group scale in fp32 and
 // accumulated in fp32; the waves' sums are added in wave order.
 //
-// GPC is the number of scale groups per 128-row chunk (1; 2 for 64-row groups; 4 for
-// 32-row groups).  The chunk's four 32-row MFMA steps then form GPC separate partials, one
-// per group, each scaled before it is added.  Scales and zero points are stored per unit of
-// min(group_size, 128) rows, so a chunk owns GPC consecutive unit rows of its column block.
+// GPC is the number of scale units per 128-row chunk: scales and zero points are stored
+// per unit of gcd(group_size, 128) rows (128, 64, 32 or 16), so a chunk owns GPC = 1, 2, 4
+// or 8 consecutive unit rows of its column block.  The chunk's four 32-row MFMA steps then
+// form one partial per unit, each scaled before it is added.  A 16-row unit is half an
+// MFMA step (lanes 0-31 carry its first 16 rows, lanes 32-63 the rest), so with GPC = 8
+// each step runs twice, once with the other half's weight lanes set to zero.
 //
 // This header holds the kernel template and its launch chain; each translation unit that
-// includes it instantiates one GPC (the instances of the three counts compile in parallel).
+// includes it instantiates one GPC (the instances of the four counts compile in parallel).
 #pragma once
 #include "wq_device.h"
 #include "wq_internal.h"
@@ -30,13 +32,21 @@ namespace {
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kMaxSpan = 64;   // groups per work-group covered by the staged scales
 
+// Scale and zero-point staging: the work-group's blocks hold at most NB x kMaxSpan chunks
+// of GPC units, 8 scale dwords and one zero-point pair per unit.  Threads stage whole
+// slots of T entries (T = waves x 64, a multiple of 256, so the scale count divides).
+constexpr int small_scale_slots(int waves, bool pair, int gpc) {
+  return (pair ? 2 : 1) * kMaxSpan * 8 * gpc / (waves * 64);
+}
+constexpr int small_zero_slots(int waves, bool pair, int gpc) {
+  return (pair ? 2 : 1) * kMaxSpan * gpc > waves * 64
+             ? (pair ? 2 : 1) * kMaxSpan * gpc / (waves * 64) : 1;
+}
 // Static LDS of an instance (see the kernel's __shared__ arrays), an upper bound over ZP.
-// The staged scales take 2*GPC dwords per thread: NB blocks x kMaxSpan chunks x 8 dwords x
-// GPC fit since a work-group has at least 4 waves per block.
-constexpr long small_static_lds(int waves, int gpc) {
-  return 2L * gpc * waves * 64 * 4       // s_lds
-         + (long)waves * 64 * 8          // z_lds
-         + (long)waves * 64 * 16;        // red
+constexpr long small_static_lds(int waves, bool pair, int gpc) {
+  return (long)small_scale_slots(waves, pair, gpc) * waves * 64 * 4    // s_lds
+         + (long)small_zero_slots(waves, pair, gpc) * waves * 64 * 8   // z_lds
+         + (long)waves * 64 * 16;                                      // red
 }
 
 // The kernel body is branch-free up to the arithmetic: every load is issued
@@ -56,11 +66,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   constexpr int T = WAVES * 64;
   constexpr int NB = PAIR ? 2 : 1;            // column blocks of the work-group
   constexpr int KW = WAVES / NB;              // waves splitting K for one block
-  constexpr int SU = 2 * GPC;                 // staged scale dwords per thread
-  constexpr int JQ = 4 / GPC;                 // 32-row MFMA steps per scale group
+  constexpr int SU = small_scale_slots(WAVES, PAIR, GPC);  // staged scale dwords per thread
+  constexpr int ZU = small_zero_slots(WAVES, PAIR, GPC);   // staged zero points per thread
+  constexpr int JQ = GPC <= 4 ? 4 / GPC : 1;  // 32-row MFMA steps per scale unit (GPC <= 4)
+  static_assert(SU >= 1 && SU * T == NB * kMaxSpan * 8 * GPC, "scale slots cover the range");
+  static_assert(ZU * T >= NB * kMaxSpan * GPC, "zero-point slots cover the range");
   extern __shared__ f16x8 a_lds[];            // [m][span*16] granules (+ padding)
-  __shared__ uint32_t s_lds[SU * T];          // scales, [block][chunk][sub][col] as fp16
-  __shared__ u32x2 z_lds[ZP ? T : 1];         // zero points, [block][chunk][sub]
+  __shared__ uint32_t s_lds[SU * T];          // scales, [block][chunk][unit][col] as fp16
+  __shared__ u32x2 z_lds[ZP ? ZU * T : 1];    // zero points, [block][chunk][unit]
   __shared__ f32x4 red[WAVES][64];
 
   const int tid = threadIdx.x;
@@ -113,12 +126,17 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     const int h = PAIR && i >= s_words ? 1 : 0;  // block of the pair holding dword i
     s_stage[u] = s32[(pair0 + h * units) * 8 + (i - h * s_words)];
   }
-  u32x2 z_stage = u32x2{0u, 0u};
-  if constexpr (ZP) {
-    const int z_words = span * GPC;
-    const int i = tid < NB * z_words ? tid : NB * z_words - 1;
-    const int h = PAIR && i >= z_words ? 1 : 0;
-    z_stage = z[pair0 + h * units + (i - h * z_words)];
+  u32x2 z_stage[ZU];
+#pragma unroll
+  for (int u = 0; u < ZU; ++u) {
+    z_stage[u] = u32x2{0u, 0u};
+    if constexpr (ZP) {
+      const int z_words = span * GPC;
+      int i = tid + u * T;
+      i = i < NB * z_words ? i : NB * z_words - 1;
+      const int h = PAIR && i >= z_words ? 1 : 0;
+      z_stage[u] = z[pair0 + h * units + (i - h * z_words)];
+    }
   }
 
   // 3. The wave's weight chunks, all in flight before any arithmetic.
@@ -134,7 +152,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   for (int u = 0; u < STAGE; ++u) a_lds[tid + u * T] = stage[u];
 #pragma unroll
   for (int u = 0; u < SU; ++u) s_lds[tid + u * T] = s_stage[u];
-  if constexpr (ZP) z_lds[tid] = z_stage;
+  if constexpr (ZP) {
+#pragma unroll
+    for (int u = 0; u < ZU; ++u) z_lds[tid + u * T] = z_stage[u];
+  }
   __syncthreads();
 
   // 5. Arithmetic.  MFMA rows >= m are never stored, and a row of the product depends on
@@ -146,14 +167,17 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   const int arow = (col < m ? col : m - 1) * per_row;
   const f16* s_half = reinterpret_cast<const f16*>(s_lds);
   int gl[GW];  // chunk of step i inside the staged range (clamped for the masked steps)
-  float sc[GW][GPC];
+  constexpr int HS = GPC <= 4 ? GPC : 1;  // scales hoisted per chunk (read in place for 8)
+  float sc[GW][HS];
 #pragma unroll
   for (int i = 0; i < GW; ++i) {
     gl[i] = g0 - gs0 + (i < gw ? i : gw - 1);
+    if constexpr (GPC <= 4) {
 #pragma unroll
-    for (int t = 0; t < GPC; ++t) {
-      const float v = (float)s_half[((half * span + gl[i]) * GPC + t) * 16 + col];
-      sc[i][t] = i < gw ? v : 0.f;
+      for (int t = 0; t < GPC; ++t) {
+        const float v = (float)s_half[((half * span + gl[i]) * GPC + t) * 16 + col];
+        sc[i][t] = i < gw ? v : 0.f;
+      }
     }
   }
   f16x8 an[4];
@@ -172,18 +196,44 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     // With eight groups per wave, pin the prefetch ahead of this group's work (measured
     // faster for the decode shape, slower for shallower pipelines).
     if constexpr (GW >= 8) __builtin_amdgcn_sched_barrier(0);
+    if constexpr (GPC <= 4) {
 #pragma unroll
-    for (int t = 0; t < GPC; ++t) {
-      const ZeroOffsets zo =
-          zero_offsets(ZP ? zero_code(z_lds[(half * span + gl[i]) * GPC + t], col) : 8);
-      f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < GPC; ++t) {
+        const ZeroOffsets zo =
+            zero_offsets(ZP ? zero_code(z_lds[(half * span + gl[i]) * GPC + t], col) : 8);
+        f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int jj = 0; jj < JQ; ++jj) {
-        const int j = t * JQ + jj;
-        p = mfma16x16x32(ac[j], dequant8(bw[i][j], zo, mr), p);
+        for (int jj = 0; jj < JQ; ++jj) {
+          const int j = t * JQ + jj;
+          p = mfma16x16x32(ac[j], dequant8(bw[i][j], zo, mr), p);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sc[i][t], p[e], acc[e]);
       }
+    } else {
+      // 16-row units: the lane's 8 rows of step j lie in unit 2j + hi.  Its weights enter
+      // the MFMA of that unit and zeros the other's, so each product sums one unit only.
+      const int hi = qd >> 1;
+      const int ubase = (half * span + gl[i]) * 8;
+      const f16x8 zero8 = f16x8{};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sc[i][t], p[e], acc[e]);
+      for (int j = 0; j < 4; ++j) {
+        const ZeroOffsets zo =
+            zero_offsets(ZP ? zero_code(z_lds[ubase + 2 * j + hi], col) : 8);
+        const f16x8 w = dequant8(bw[i][j], zo, mr);
+        const f32x4 p0 = mfma16x16x32(ac[j], hi ? zero8 : w, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 p1 = mfma16x16x32(ac[j], hi ? w : zero8, f32x4{0.f, 0.f, 0.f, 0.f});
+        // (the reads are unconditional, in bounds through the clamped chunk; a masked step
+        // selects zero scales)
+        const float v0 = (float)s_half[(ubase + 2 * j) * 16 + col];
+        const float v1 = (float)s_half[(ubase + 2 * j + 1) * 16 + col];
+        const float s0 = i < gw ? v0 : 0.f;
+        const float s1 = i < gw ? v1 : 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(s0, p0[e], acc[e]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(s1, p1[e], acc[e]);
+      }
     }
     if constexpr (GW >= 8) __builtin_amdgcn_sched_barrier(0);
   }

@@ -6,6 +6,8 @@ data (repack, gather, GEMM, reduce) is a libwq kernel called through the binding
 
 from __future__ import annotations
 
+import math
+
 import numpy as np
 import torch
 
@@ -46,7 +48,7 @@ class PackedWeight:
         wq_repack_b(qw, self.b, self.k, self.n, perm=self.perm)
         sc = to_device(scales if isinstance(scales, torch.Tensor)
                        else np.asarray(scales, dtype=np.float16), self.device)
-        unit = group_size if 0 < group_size < GROUP else GROUP  # rows per stored scale row
+        unit = math.gcd(group_size, GROUP) if group_size > 0 else GROUP  # rows per scale row
         self.s = torch.empty((self.k // unit) * self.n, dtype=torch.float16, device=self.device)
         wq_repack_scales(sc, self.s, self.k, self.n, group_size)
         self.z = None

@@ -155,16 +155,21 @@ def bench_extended(torch, torch_ops, steps, warmup):
             "weight_tbs": round(k * 2 * inter / 2 / sec / 1e12, 4)}
         del ws
     # group 128 at decode shape is the control: the same kernel timed in the same context
-    for name, gs in (("decode", 128), ("decode", 64), ("decode", 32), ("decode", 16),
-                     ("decode", -1), ("prefill", 32), ("prefill", 16)):
+    # (bf16 rows: bf16 activations, scales and outputs, with the headline's flags)
+    for name, gs, bf16 in (("decode", 128, False), ("decode", 64, False),
+                           ("decode", 32, False), ("decode", 16, False), ("decode", -1, False),
+                           ("prefill", 32, False), ("prefill", 16, False),
+                           ("decode", 128, True), ("prefill", 128, True)):
         cfg = synthetic.CONFIGS[name]
-        case = synthetic.dense_case(cfg["m"], cfg["k"], cfg["n"], group_size=gs, seed=17)
-        w = torch_ops.PackedWeight(case["qweight"], case["scales"], device="cuda",
-                                   group_size=gs)
+        act_order = bf16 and cfg["act_order"]
+        case = synthetic.dense_case(cfg["m"], cfg["k"], cfg["n"], group_size=gs, seed=17,
+                                    act_order=act_order, bf16=bf16)
+        w = torch_ops.PackedWeight(case["qweight"], case["scales"], None, case["g_idx"],
+                                   device="cuda", group_size=gs, bf16=bf16)
         copies = 12 if name == "decode" else 1
         ws = [w] + [w.clone() for _ in range(copies - 1)]
         a = torch_ops.to_device(case["a"], "cuda")
-        c = torch.empty((cfg["m"], cfg["n"]), dtype=torch.float16, device="cuda")
+        c = torch.empty((cfg["m"], cfg["n"]), dtype=torch_ops.act_dtype(bf16), device="cuda")
         fp32 = cfg["fp32_reduce"]
         bufs = torch_ops.GemmBuffers(w, cfg["m"], fp32)
 
@@ -172,9 +177,11 @@ def bench_extended(torch, torch_ops, steps, warmup):
             torch_ops.gemm(a, ws[i % copies], c, fp32_reduce=fp32, buffers=bufs)
         sec = timed_loop(torch, step, steps if name == "decode" else max(5, steps // 8), warmup)
         flops = 2.0 * cfg["m"] * cfg["n"] * cfg["k"]
-        out[f"{name}_group{gs}"] = {
+        key = f"{name}_bf16" if bf16 else f"{name}_group{gs}"
+        out[key] = {
             "workload": f"{name} shape M={cfg['m']} K={cfg['k']} N={cfg['n']} u4b8 "
-                        f"group_size {gs}",
+                        f"group_size {gs}" + (" act_order" if act_order else "")
+                        + (" bf16 activations" if bf16 else ""),
             "us": round(sec * 1e6, 2), "tflops": round(flops / sec / 1e12, 2),
             "weight_tbs": round(cfg["k"] * cfg["n"] / 2 / sec / 1e12, 4)}
         del ws

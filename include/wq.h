@@ -2,8 +2,8 @@
  * wq.h -- C ABI of the MI355X (gfx950) W4A16 weight-only quantized GEMM library (libwq.so).
  *
  * Operation: C[m][n] = sum_k A[m][k] * W[k][n], W[k][n] = (q[k][n] - z) * s[g(k)][n],
- * fp16 activations and output, fp32 accumulation, 4-bit codes q, fp16 group scales s,
- * zero point z = 8 (symmetric "u4b8") or a per-group 4-bit code (asymmetric "u4").
+ * fp16 activations, output and group scales s (bf16 with WQ_FLAG_BF16), fp32 accumulation,
+ * 4-bit codes q, zero point z = 8 (symmetric "u4b8") or a per-group 4-bit code ("u4").
  * Sources: ferrum-kernels marlin.rs (module doc: Marlin INT4 x FP16 GEMM, K % 128 == 0,
  * N % 256 == 0; `marlin_gemm` doc: C = A @ dequant(B)); ferrum-kernels vllm_marlin.rs
  * (`FerrumMarlinLaunch`, the versioned launch problem this ABI is trimmed from; the scalar
@@ -62,10 +62,16 @@ extern "C" {
 /* SwiGLU epilogue (the transformer.rs dense SwiGLU chain's gate and up projections with its
  * planar silu*mul, fused): B, scales and zero points hold a gate and an up projection of
  * n/2 columns each, paired by wq_interleave_gate_up before the repack (16-column block 2t
- * is gate block t, block 2t+1 up block t); the output is the [rows][n/2] fp16 activation
- * fp16(silu(A Wg) * (A Wu)), silu(x) = x / (1 + exp(-x)), from the fp32 sums.  Not with
+ * is gate block t, block 2t+1 up block t); the output is the [rows][n/2] activation
+ * round(silu(A Wg) * (A Wu)), silu(x) = x / (1 + exp(-x)), from the fp32 sums.  Not with
  * WQ_FLAG_MUL_TOPK_WEIGHTS. */
 #define WQ_FLAG_SWIGLU (1u << 7)
+/* bf16 activations (the element type of the pages' vllm_marlin.rs MXFP4 MoE entry point,
+ * `ferrum_vllm_marlin_moe_mxfp4_bf16`, here with the same 4-bit integer weights): a, the
+ * scales, c (y of the grouped call, w of wq_dequant) and a_tmp hold bf16 values instead of
+ * fp16; codes and zero points are unchanged.  Products are accumulated in fp32 and rounded
+ * once to bf16 (round to nearest even).  Scales are repacked bit for bit either way. */
+#define WQ_FLAG_BF16 (1u << 8)
 
 enum wq_stage {
   WQ_STAGE_ARGS = 1,
@@ -111,8 +117,9 @@ int wq_repack_b(const uint32_t* qweight, const int32_t* perm, void* b_out, int k
                 void* stream);
 
 /*
- * Scales fp16 [k/group_size][n] row-major ([1][n] for group_size -1) -> library layout
- * fp16 [n/16][k/U][16]: unit u takes the scales of the group holding its rows.
+ * Scales fp16 or bf16 [k/group_size][n] row-major ([1][n] for group_size -1), moved as
+ * 16-bit values -> library layout [n/16][k/U][16]: unit u takes the scales of the group
+ * holding its rows.
  */
 int wq_repack_scales(const void* scales, void* s_out, int k, int n, int group_size,
                      void* stream);
@@ -129,7 +136,7 @@ int wq_repack_zeros(const uint32_t* zeros, void* z_out, int k, int n, int group_
  * Load-time helper for WQ_FLAG_SWIGLU: pairs the columns of a gate and an up tensor in
  * 16-column blocks, out[r] = [gate block 0, up block 0, gate block 1, up block 1, ...].
  * gate and up are row-major [rows][cols] with bits_per_column bits per column: 32 for
- * GPTQ qweight words ([k/8][cols] uint32), 16 for fp16 scales, 4 for packed zero points
+ * GPTQ qweight words ([k/8][cols] uint32), 16 for scales, 4 for packed zero points
  * ([groups][cols/8] uint32); out has 2*cols columns.  cols % 16 == 0; device pointers,
  * 4-byte aligned; enqueued on `stream`.
  */
@@ -156,19 +163,19 @@ int wq_gemm_workspace_bytes(int m, int n, int k, uint32_t flags, size_t* bytes_o
 typedef struct wq_gemm_args {
   uint32_t abi_version;     /* WQ_ABI_VERSION                                          */
   uint32_t struct_size;     /* sizeof(wq_gemm_args)                                   */
-  const void* a;            /* device fp16 [m][lda], 16-byte aligned rows               */
+  const void* a;            /* device fp16 (bf16) [m][lda], 16-byte aligned rows        */
   const void* b;            /* device, library B layout (wq_repack_b)                   */
-  void* c;                  /* device fp16 [m][n], output                               */
+  void* c;                  /* device fp16 (bf16) [m][n], output                        */
   const void* b_scales;     /* device, library scale layout (wq_repack_scales)          */
   const void* zero_points;  /* device, library zero-point layout, or NULL (u4b8)        */
   const int32_t* perm;      /* device int32 [k] with WQ_FLAG_ACT_ORDER, else NULL       */
-  void* a_tmp;              /* device fp16 [m][k] gather scratch with act_order, else NULL */
+  void* a_tmp;              /* device [m][k] 16-bit gather scratch with act_order, or NULL */
   void* workspace;          /* device scratch (wq_gemm_workspace_bytes), may be NULL if 0 */
   size_t workspace_bytes;
   void* stream;             /* hipStream_t                                              */
   int32_t m, n, k;          /* m >= 1, n % 256 == 0, k % 128 == 0                        */
   int32_t lda;              /* row stride of a in elements, >= k, multiple of 8         */
-  int32_t group_size;       /* as repacked: -1, 32, 64 or a multiple of 128 dividing k  */
+  int32_t group_size;       /* as repacked: -1 or a multiple of 16 dividing k           */
   uint32_t flags;           /* WQ_FLAG_*; HAS_ZP iff zero_points != NULL; ACT_ORDER iff perm */
   int32_t split_k;          /* 0 = library's choice; 1 = no split; s > 1 requests s splits
                                along K for m <= 16 (needs WQ_FLAG_FP32_REDUCE; clamped to
@@ -186,8 +193,9 @@ int wq_gemm(const wq_gemm_args* args);
 
 /*
  * Dequant export for bit-exact tests: reads library-layout B, scales and optional zero
- * points and writes w[k][n] = fp16_rne((q - z) * s) (fp16, row-major, rows in the stored
- * order, i.e. sorted order for act_order weights).  flags: only WQ_FLAG_HAS_ZP is read.
+ * points and writes w[k][n] = rne((q - z) * s) (fp16, or bf16 with WQ_FLAG_BF16; row-major,
+ * rows in the stored order, i.e. sorted order for act_order weights).  flags: HAS_ZP and
+ * BF16 are read, ACT_ORDER and IS_K_FULL accepted; any other bit fails with WQ_ERR_FLAGS.
  */
 int wq_dequant(const void* b, const void* b_scales, const void* zero_points, int k, int n,
                int group_size, uint32_t flags, void* w_out, void* stream);
@@ -207,7 +215,7 @@ int wq_csr_from_routes(const int32_t* selected, int n_tokens, int top_k, int n_e
 typedef struct wq_grouped_args {
   uint32_t abi_version;
   uint32_t struct_size;     /* sizeof(wq_grouped_args)                                  */
-  const void* a;            /* device fp16 [n_tokens][k]                                 */
+  const void* a;            /* device fp16 (bf16) [n_tokens][k]                          */
   const void* b_bank;       /* expert e's library-layout B at b_bank + e*b_stride_bytes  */
   size_t b_stride_bytes;    /* >= k*n/2, multiple of 16                                  */
   const void* s_bank;       /* expert e's scales at s_bank + e*s_stride_bytes            */
@@ -220,7 +228,7 @@ typedef struct wq_grouped_args {
   const int32_t* pair_tok;  /* device [n_pairs] activation row of each pair              */
   const float* topk_weights; /* device fp32 [n_pairs], pair-major routing weights, with
                                 WQ_FLAG_MUL_TOPK_WEIGHTS; else NULL                      */
-  void* y;                  /* device fp16 [n_pairs][n], pair-major output               */
+  void* y;                  /* device fp16 (bf16) [n_pairs][n], pair-major output        */
   void* workspace;          /* reserved for the grouped schedule; may be NULL            */
   size_t workspace_bytes;
   void* stream;
@@ -240,7 +248,7 @@ int wq_grouped_workspace_bytes(int n_pairs, int n_active, int n, int k, uint32_t
  * for active segment i with expert e = ex_ids[i] (i when ex_ids is NULL) and each pair p
  * in ex_pairs[ex_off[i] .. ex_off[i+1]), y[p][:] = A[pair_tok[p]][:] @ dequant(B_e).
  * With WQ_FLAG_MUL_TOPK_WEIGHTS the row is also multiplied by topk_weights[p], on the fp32
- * result before its one rounding to fp16 (the vllm_marlin.rs MoE launch's
+ * result before its one rounding to the output type (the vllm_marlin.rs MoE launch's
  * `mul_topk_weights` with its fp32 `topk_weights`, one per routed pair).  The device CSR is
  * not re-validated (that would need a host sync): build it with wq_csr_from_routes;
  * entries out of range are skipped by the kernel (never read or written out of bounds),

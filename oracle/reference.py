@@ -17,11 +17,15 @@ tests; this is the plain definition they describe):
   `repack_gptq_qzeros_to_marlin`: zero points are the actual codes (0..15).
 * ferrum-kernels marlin.rs, `MarlinWeight.perm` doc: act_order; each row k belongs to group
   g_idx[k]; the permutation is argsort(g_idx).
+* ferrum-kernels vllm_marlin.rs, `ferrum_vllm_marlin_moe_mxfp4_bf16`: the pages' bf16
+  activation and output type.  Read here with the same 4-bit integer weights: with bf16,
+  activations and scales arrive as bf16 bit patterns (the upper half of a binary32).
 
 Precision: codes, zero points and scales are exact; W = (q - z) * s is formed exactly
 (a 5-bit integer times an fp16 value fits in fp64, and in fp32 too); the product is
-accumulated in fp64 and left unrounded.  Only `dequantize_fp16` rounds (once, to nearest
-even), for the bit-exact check of the library's dequant export.
+accumulated in fp64 and left unrounded.  Only `dequantize_fp16` and `round_bf16` round
+(once, to nearest even), for the bit-exact check of the library's dequant export and for
+the 16-bit activation handed on in the SwiGLU chain.
 """
 
 from __future__ import annotations
@@ -96,13 +100,35 @@ def group_of_rows(k: int, group_size: int, g_idx: np.ndarray | None = None) -> n
 # Dequantization and the product
 # ---------------------------------------------------------------------------------------
 
+def bf16_value(bits) -> np.ndarray:
+    """fp64 values of bf16 bit patterns (uint16): bfloat16 is the upper half of an IEEE
+    binary32 (sign, 8-bit exponent, 7 stored mantissa bits), so the value is that of the
+    binary32 word bits << 16."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round fp64 values to the nearest bf16 value (8 significant bits), ties to even, as
+    fp64 (normal range; no overflow or subnormal handling is needed here)."""
+    x = np.asarray(x, dtype=np.float64)
+    mant, exp = np.frexp(x)                 # x = mant * 2**exp, 0.5 <= |mant| < 1
+    return np.ldexp(np.round(mant * 256.0) / 256.0, exp)  # np.round: half to even
+
+
+def values16(x, bf16: bool = False) -> np.ndarray:
+    """fp64 values of 16-bit operands: fp16 numbers, or bf16 bit patterns when bf16."""
+    return bf16_value(x) if bf16 else np.asarray(x, dtype=np.float16).astype(np.float64)
+
+
 def dequantize(q: np.ndarray, scales: np.ndarray, group: np.ndarray,
-               zero_codes: np.ndarray | None = None) -> np.ndarray:
+               zero_codes: np.ndarray | None = None, bf16: bool = False) -> np.ndarray:
     """W[k, n] = (q[k, n] - z) * s[group[k], n] in fp64 (exact).
 
-    z = 8 without zero points (kU4B8), else the code zero_codes[group[k], n] (kU4).
+    z = 8 without zero points (kU4B8), else the code zero_codes[group[k], n] (kU4).  Scales
+    are fp16, or bf16 bit patterns with bf16.
     """
-    s = np.asarray(scales, dtype=np.float16).astype(np.float64)
+    s = values16(scales, bf16)
     qi = q.astype(np.int64)
     zi = U4B8_ZERO if zero_codes is None else np.asarray(zero_codes).astype(np.int64)[group, :]
     return (qi - zi).astype(np.float64) * s[group, :]
@@ -113,13 +139,14 @@ def dequantize_fp16(w: np.ndarray) -> np.ndarray:
     return np.asarray(w, dtype=np.float64).astype(np.float16)
 
 
-def matmul_fp64(a: np.ndarray, w: np.ndarray) -> np.ndarray:
-    """fp64 product A @ W of fp16 activations and exact weights (unrounded result)."""
-    return np.asarray(a).astype(np.float64) @ w
+def matmul_fp64(a: np.ndarray, w: np.ndarray, bf16: bool = False) -> np.ndarray:
+    """fp64 product A @ W of 16-bit activations (fp16, or bf16 bit patterns with bf16) and
+    exact weights (unrounded result)."""
+    return values16(a, bf16) @ w
 
 
 def w4a16_weights(qweight, scales, *, zeros=None, g_idx=None, group_size=128,
-                  columns=None) -> np.ndarray:
+                  columns=None, bf16=False) -> np.ndarray:
     """Exact fp64 weights W [K][N] (or [K][len(columns)] for a column subset)."""
     qweight = np.asarray(qweight, dtype=np.uint32)
     scales = np.asarray(scales)
@@ -131,15 +158,16 @@ def w4a16_weights(qweight, scales, *, zeros=None, g_idx=None, group_size=128,
         qweight, scales = qweight[:, cols], scales[:, cols]
         zero_codes = None if zero_codes is None else zero_codes[:, cols]
     group = group_of_rows(k, group_size, g_idx)
-    return dequantize(unpack_qweight(qweight), scales, group, zero_codes)
+    return dequantize(unpack_qweight(qweight), scales, group, zero_codes, bf16)
 
 
 def w4a16_gemm(a, qweight, scales, *, zeros=None, g_idx=None, group_size=128,
-               columns=None) -> np.ndarray:
-    """Reference C = A @ dequant(B) in fp64, [M][N] (or [M][len(columns)])."""
+               columns=None, bf16=False) -> np.ndarray:
+    """Reference C = A @ dequant(B) in fp64, [M][N] (or [M][len(columns)]); with bf16 the
+    activations and scales are bf16 bit patterns."""
     w = w4a16_weights(qweight, scales, zeros=zeros, g_idx=g_idx, group_size=group_size,
-                      columns=columns)
-    return matmul_fp64(a, w)
+                      columns=columns, bf16=bf16)
+    return matmul_fp64(a, w, bf16)
 
 
 # ---------------------------------------------------------------------------------------
@@ -255,7 +283,7 @@ def validate_csr(csr: dict) -> None:
 
 
 def grouped_w4a16_gemm(a, experts, csr, *, group_size=128, columns=None,
-                       pairs=None, topk_weights=None) -> np.ndarray:
+                       pairs=None, topk_weights=None, bf16=False) -> np.ndarray:
     """Pair-major reference y[p] = A[pair_tok[p]] @ dequant(B_e) for the expert e owning p.
 
     Walks the expert-major CSR: segment i covers positions ex_off[i]..ex_off[i+1] of
@@ -265,7 +293,7 @@ def grouped_w4a16_gemm(a, experts, csr, *, group_size=128, columns=None,
 
     With `topk_weights` (one fp32 routing weight per pair, pair-major: the vllm_marlin.rs
     MoE launch's `topk_weights` under `mul_topk_weights`), row p is multiplied by
-    topk_weights[p], in fp64.
+    topk_weights[p], in fp64.  With bf16, A and the scales are bf16 bit patterns.
     """
     a = np.asarray(a)
     n_pairs = len(csr["ex_pairs"])
@@ -280,9 +308,9 @@ def grouped_w4a16_gemm(a, experts, csr, *, group_size=128, columns=None,
             continue
         ex = experts[e]
         w = w4a16_weights(ex["qweight"], ex["scales"], zeros=ex.get("zeros"),
-                          group_size=group_size, columns=columns)
+                          group_size=group_size, columns=columns, bf16=bf16)
         toks = [csr["pair_tok"][p] for p in rows]
-        y[rows, :] = matmul_fp64(a[toks, :], w)
+        y[rows, :] = matmul_fp64(a[toks, :], w, bf16)
         if topk_weights is not None:
             scale = np.asarray(topk_weights, dtype=np.float32)[rows].astype(np.float64)
             y[rows, :] *= scale[:, None]
@@ -301,15 +329,16 @@ def silu(x: np.ndarray) -> np.ndarray:
     return x / (1.0 + np.exp(-x))
 
 
-def swiglu_activation(a, gate: dict, up: dict, *, group_size=128, columns=None) -> np.ndarray:
+def swiglu_activation(a, gate: dict, up: dict, *, group_size=128, columns=None,
+                      bf16=False) -> np.ndarray:
     """act = silu(A @ W_gate) * (A @ W_up), fp64 and unrounded ([M][I], or a column subset).
 
     `gate` and `up` hold qweight, scales and optional zeros of the two projections.
     """
     g = w4a16_gemm(a, gate["qweight"], gate["scales"], zeros=gate.get("zeros"),
-                   group_size=group_size, columns=columns)
+                   group_size=group_size, columns=columns, bf16=bf16)
     u = w4a16_gemm(a, up["qweight"], up["scales"], zeros=up.get("zeros"),
-                   group_size=group_size, columns=columns)
+                   group_size=group_size, columns=columns, bf16=bf16)
     return silu(g) * u
 
 
@@ -321,6 +350,15 @@ def swiglu_mlp(a, gate: dict, up: dict, down: dict, *, group_size=128) -> tuple:
     out = w4a16_gemm(act16, down["qweight"], down["scales"], zeros=down.get("zeros"),
                      group_size=group_size)
     return act16, out
+
+
+def swiglu_mlp_bf16(a, gate: dict, up: dict, down: dict, *, group_size=128) -> tuple:
+    """The chain with bf16 activations: act = bf16_rne(swiglu_activation), out = act @
+    W_down in fp64 (A and every scale as bf16 bit patterns).  Returns (act values, out)."""
+    act = round_bf16(swiglu_activation(a, gate, up, group_size=group_size, bf16=True))
+    w = w4a16_weights(down["qweight"], down["scales"], zeros=down.get("zeros"),
+                      group_size=group_size, bf16=True)
+    return act, act @ w
 
 
 # ---------------------------------------------------------------------------------------

@@ -106,6 +106,24 @@ def activations(seed: int, m: int, k: int) -> np.ndarray:
     return normal(seed, m * k).astype(np.float16).reshape(m, k)
 
 
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Inputs for the bf16 path: fp64 draws -> binary32 -> the nearest bf16 (ties to even on
+    the binary32 bits), as uint16 bit patterns (numpy has no bf16 type)."""
+    u = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def activations_bf16(seed: int, m: int, k: int) -> np.ndarray:
+    """A ~ N(0, 1) as bf16 bit patterns, shape [m][k] (the draws of `activations`)."""
+    return bf16_bits(normal(seed, m * k)).reshape(m, k)
+
+
+def scales_bf16(seed: int, groups: int, n: int, lo: float = 0.005,
+                hi: float = 0.02) -> np.ndarray:
+    """Group scales ~ U[lo, hi) as bf16 bit patterns: [groups][n] (the draws of `scales`)."""
+    return bf16_bits(lo + (hi - lo) * uniform01(seed, groups * n)).reshape(groups, n)
+
+
 def qweight_words(seed: int, k: int, n: int) -> np.ndarray:
     """Uniform 4-bit codes 0..15 packed GPTQ-style: uint32 [k/8][n]."""
     return words_u32(seed, (k // 8) * n).reshape(k // 8, n)
@@ -172,15 +190,16 @@ GROUP_SIZE = 128
 
 
 def dense_case(m: int, k: int, n: int, *, zp: bool = False, act_order: bool = False,
-               group_size: int = GROUP_SIZE, seed: int = ROOT_SEED) -> dict:
+               group_size: int = GROUP_SIZE, seed: int = ROOT_SEED, bf16: bool = False) -> dict:
     """One dense problem's inputs in the boundary's plain formats (group_size -1: one
-    channelwise group)."""
+    channelwise group; bf16: activations and scales as bf16 bit patterns)."""
     groups = 1 if group_size == -1 else k // group_size
+    act, sc = (activations_bf16, scales_bf16) if bf16 else (activations, scales)
     case = dict(
-        m=m, k=k, n=n, group_size=group_size,
-        a=activations(stream_seed(seed, TAG_ACT), m, k),
+        m=m, k=k, n=n, group_size=group_size, bf16=bf16,
+        a=act(stream_seed(seed, TAG_ACT), m, k),
         qweight=qweight_words(stream_seed(seed, TAG_WEIGHT), k, n),
-        scales=scales(stream_seed(seed, TAG_SCALE), groups, n),
+        scales=sc(stream_seed(seed, TAG_SCALE), groups, n),
         zeros=zero_point_words(stream_seed(seed, TAG_ZERO), groups, n) if zp else None,
         g_idx=(act_order_g_idx(stream_seed(seed, TAG_PERM), k,
                                k if group_size == -1 else group_size) if act_order else None),
@@ -200,19 +219,22 @@ def config_case(name: str, seed: int | None = None) -> dict:
 
 
 def moe_case(n_tokens: int = 1024, n_expert: int = 8, k: int = 4096, n: int = 14336,
-             *, group_size: int = GROUP_SIZE, seed: int | None = None) -> dict:
-    """Grouped (MoE) problem: A [tokens][k], one weight bank per expert, top-2 routes."""
+             *, group_size: int = GROUP_SIZE, seed: int | None = None,
+             bf16: bool = False) -> dict:
+    """Grouped (MoE) problem: A [tokens][k], one weight bank per expert, top-2 routes
+    (bf16: activations and scales as bf16 bit patterns)."""
     root = (ROOT_SEED ^ CONFIG_INDEX["moe"]) if seed is None else seed
     groups = k // group_size
+    act, sc = (activations_bf16, scales_bf16) if bf16 else (activations, scales)
     experts = []
     for e in range(n_expert):
         experts.append(dict(
             qweight=qweight_words(stream_seed(root, TAG_WEIGHT, e + 1), k, n),
-            scales=scales(stream_seed(root, TAG_SCALE, e + 1), groups, n),
+            scales=sc(stream_seed(root, TAG_SCALE, e + 1), groups, n),
         ))
     return dict(
         n_tokens=n_tokens, n_expert=n_expert, top_k=2, k=k, n=n, group_size=group_size,
-        a=activations(stream_seed(root, TAG_ACT), n_tokens, k),
+        bf16=bf16, a=act(stream_seed(root, TAG_ACT), n_tokens, k),
         experts=experts,
         routes=(top2_routes(stream_seed(root, TAG_ROUTE), n_tokens, n_expert) if n_expert > 1
                 else np.zeros((n_tokens, 2), dtype=np.int32)),

@@ -146,6 +146,21 @@ def test_repack_and_dequant_validation(L):
                                                                           wq.WQ_ERR_NULL)
     assert L.wq_dequant(0x1000, 0x2000, None, 1024, 256, 128, wq.WQ_FLAG_HAS_ZP, 0x3000,
                         None) == status(STAGE_ARGS, wq.WQ_ERR_FLAGS)
+    # unknown flag bits (beyond HAS_ZP, ACT_ORDER, IS_K_FULL and BF16) are rejected
+    assert L.wq_dequant(0x1000, 0x2000, None, 1024, 256, 128, 1 << 9, 0x3000,
+                        None) == status(STAGE_ARGS, wq.WQ_ERR_FLAGS)
+    assert L.wq_dequant(0x1000, 0x2000, None, 1024, 256, 128, wq.WQ_FLAG_SWIGLU, 0x3000,
+                        None) == status(STAGE_ARGS, wq.WQ_ERR_FLAGS)
+
+
+def test_flag_values_match_the_header():
+    with open(os.path.join(ROOT, "include", "wq.h")) as f:
+        text = f.read()
+    found = dict((name, int(bit)) for name, bit in
+                 re.findall(r"#define (WQ_FLAG_[A-Z_0-9]+)\s+\(1u << (\d+)\)", text))
+    assert found["WQ_FLAG_BF16"] == 8
+    for name, bit in found.items():
+        assert getattr(wq, name) == 1 << bit, name
 
 
 def test_stream_read_sizing_and_validation(L):

@@ -336,6 +336,48 @@ def test_groups_straddling_chunks_equal_repeated_smaller_units():
                 assert rs[(nb * 4 + u) * 16 + c] == s[u, 16 * nb + c]
 
 
+def test_bf16_values_of_known_bit_patterns():
+    """bfloat16 = sign, 8 exponent bits (bias 127), 7 mantissa bits."""
+    cases = {0x0000: 0.0, 0x3F80: 1.0, 0xBF80: -1.0, 0x4000: 2.0, 0xC040: -3.0,
+             0x3F00: 0.5, 0x4049: 3.140625, 0x3F81: 1.0 + 2.0 ** -7, 0x7F7F: 255 * 2.0 ** 120,
+             0x0080: 2.0 ** -126, 0x0001: 2.0 ** -133, 0x4300: 128.0, 0x4380: 256.0}
+    bits = np.array(list(cases), dtype=np.uint16)
+    assert ref.bf16_value(bits).tolist() == list(cases.values())
+
+
+def test_bf16_rounding_is_nearest_even_by_brute_force():
+    """round_bf16 against a search over every finite positive bf16 value: the nearest one,
+    and on a tie the one with an even last mantissa bit."""
+    table_bits = np.arange(0x0080, 0x7F80, dtype=np.uint16)   # positive normal bf16 values
+    table = ref.bf16_value(table_bits)
+    rng = np.random.default_rng(7)
+    xs = np.concatenate([rng.uniform(2.0 ** -20, 2.0 ** 20, 300),
+                         # exact midpoints between neighbours: ties
+                         (table[1000:1100] + table[1001:1101]) / 2,
+                         table[2000:2050]])
+    got = ref.round_bf16(xs)
+    for x, g in zip(xs, got):
+        d = np.abs(table - x)
+        best = np.flatnonzero(d == d.min())
+        pick = best[0] if len(best) == 1 else [i for i in best if table_bits[i] % 2 == 0][0]
+        assert g == table[pick], x
+    assert ref.round_bf16(-xs).tolist() == (-got).tolist()
+
+
+def test_bf16_product_matches_bruteforce():
+    """bf16 activations and scales (bit patterns) decoded and multiplied exactly."""
+    m, k, n = 2, 256, 16
+    a = synthetic.activations_bf16(20, m, k)
+    qw = synthetic.qweight_words(21, k, n)
+    s = synthetic.scales_bf16(22, 2, n)
+    zw = synthetic.zero_point_words(23, 2, n)
+    group = [kk // 128 for kk in range(k)]
+    want = gemm_bruteforce(ref.bf16_value(a), codes_bruteforce(qw), ref.bf16_value(s), group,
+                           zero_codes_bruteforce(zw))
+    got = ref.w4a16_gemm(a, qw, s, zeros=zw, bf16=True)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
 def test_act_order_with_256_row_groups_equals_plain_product():
     k, n, m, gs = 1024, 32, 4, 256
     a = synthetic.activations(70, m, k)

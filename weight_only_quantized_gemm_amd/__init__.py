@@ -24,6 +24,7 @@ WQ_FLAG_ATOMIC_ADD = 1 << 4
 WQ_FLAG_FP32_REDUCE = 1 << 5
 WQ_FLAG_MUL_TOPK_WEIGHTS = 1 << 6
 WQ_FLAG_SWIGLU = 1 << 7
+WQ_FLAG_BF16 = 1 << 8
 
 WQ_STAGE_ARGS, WQ_STAGE_SHAPE, WQ_STAGE_DEVICE = 1, 2, 3
 WQ_STAGE_LAUNCH_CONFIG, WQ_STAGE_FUNC_ATTR, WQ_STAGE_LAUNCH = 4, 5, 6

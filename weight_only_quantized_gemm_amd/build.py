@@ -11,9 +11,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libwq.so")
-SOURCES = ["wq_api.hip", "wq_repack.hip", "wq_gemm_small.hip", "wq_gemm_small_g2.hip",
-           "wq_gemm_small_g4.hip", "wq_gemm_small_g8.hip", "wq_gemm_tile.hip",
-           "wq_measure.hip"]
+# every translation unit in csrc/ (the kernel headers are included by them)
+SOURCES = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
 OBJ_DIR = os.path.join(PKG, "_build")  # per-source objects (git-ignored)
 
 

@@ -250,8 +250,10 @@ int wq_gemm(const wq_gemm_args* args) {
     return fail(WQ_STAGE_ARGS, WQ_ERR_ABI);
   const wq_gemm_args& p = *args;
   const uint32_t known = WQ_FLAG_ACT_ORDER | WQ_FLAG_IS_K_FULL | WQ_FLAG_HAS_ZP |
-                         WQ_FLAG_ATOMIC_ADD | WQ_FLAG_FP32_REDUCE | WQ_FLAG_SWIGLU;
-  if ((p.flags & ~known) || (p.flags & WQ_FLAG_ATOMIC_ADD)) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
+                         WQ_FLAG_ATOMIC_ADD | WQ_FLAG_FP32_REDUCE | WQ_FLAG_SWIGLU |
+                         WQ_FLAG_BF16;
+  if ((p.flags & ~known) || (p.flags & WQ_FLAG_ATOMIC_ADD))
+    return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
   int st = check_kn(p.k, p.n, p.group_size);
   if (st) return st;
   if (p.m <= 0 || p.lda < p.k || p.lda % 8 != 0) return fail(WQ_STAGE_SHAPE, WQ_ERR_SHAPE);
@@ -273,6 +275,7 @@ int wq_gemm(const wq_gemm_args* args) {
   if (p.split_k < 0) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
   if (p.split_k > 1 && !(p.flags & WQ_FLAG_FP32_REDUCE)) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
   const bool swiglu = (p.flags & WQ_FLAG_SWIGLU) != 0;
+  const bool bf16 = (p.flags & WQ_FLAG_BF16) != 0;
 
   // Plan, and check the workspace the plan needs, before anything is enqueued.
   const int gpc = subgroups(p.k, p.group_size);
@@ -306,11 +309,11 @@ int wq_gemm(const wq_gemm_args* args) {
 
   if (small) {
     const hipError_t e =
-        wq::launch_gemm_small(a, lda, p.m, b, s, z, c, p.n, p.k, plan, partials, stream);
+        wq::launch_gemm_small(a, lda, p.m, b, s, z, c, p.n, p.k, plan, partials, bf16, stream);
     return e == hipSuccess ? 0 : hip_fail(e);
   }
   const hipError_t e =
-      wq::launch_gemm_tile(a, lda, p.m, b, s, z, c, p.n, p.k, swiglu, gpc, stream);
+      wq::launch_gemm_tile(a, lda, p.m, b, s, z, c, p.n, p.k, swiglu, gpc, bf16, stream);
   return e == hipSuccess ? 0 : hip_fail(e);
 }
 
@@ -320,13 +323,15 @@ int wq_dequant(const void* b, const void* b_scales, const void* zero_points, int
   if (st) return st;
   if ((st = check_ptr(b, 16)) || (st = check_ptr(b_scales, 16)) || (st = check_ptr(w_out, 16)))
     return st;
+  if (flags & ~(uint32_t)(WQ_FLAG_HAS_ZP | WQ_FLAG_ACT_ORDER | WQ_FLAG_IS_K_FULL | WQ_FLAG_BF16))
+    return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
   const bool has_zp = (flags & WQ_FLAG_HAS_ZP) != 0;
   if (has_zp != (zero_points != nullptr)) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
   if (has_zp && (st = check_ptr(zero_points, 16))) return st;
   const hipError_t e = wq::launch_dequant(
       static_cast<const uint32_t*>(b), static_cast<const uint16_t*>(b_scales),
       static_cast<const uint32_t*>(zero_points), k, n, wq::scale_unit_rows(k, group_size),
-      static_cast<uint16_t*>(w_out), as_stream(stream));
+      (flags & WQ_FLAG_BF16) != 0, static_cast<uint16_t*>(w_out), as_stream(stream));
   return e == hipSuccess ? 0 : hip_fail(e);
 }
 
@@ -381,7 +386,7 @@ int wq_grouped_gemm(const wq_grouped_args* args) {
     return fail(WQ_STAGE_ARGS, WQ_ERR_ABI);
   const wq_grouped_args& p = *args;
   if (p.flags & ~(uint32_t)(WQ_FLAG_HAS_ZP | WQ_FLAG_IS_K_FULL | WQ_FLAG_MUL_TOPK_WEIGHTS |
-                            WQ_FLAG_SWIGLU))
+                            WQ_FLAG_SWIGLU | WQ_FLAG_BF16))
     return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
   // The routing weight scales an expert's output, i.e. the down projection; the SwiGLU
   // activation of the gate/up projection takes none.
@@ -438,6 +443,7 @@ int wq_grouped_gemm(const wq_grouped_args* args) {
   g.k = p.k;
   g.n = p.n;
   g.swiglu = (p.flags & WQ_FLAG_SWIGLU) != 0;
+  g.bf16 = (p.flags & WQ_FLAG_BF16) != 0;
   g.gpc = subgroups(p.k, p.group_size);
   const hipError_t e = wq::launch_grouped_tile(g, as_stream(p.stream));
   return e == hipSuccess ? 0 : hip_fail(e);

@@ -9,6 +9,8 @@ namespace wq {
 typedef _Float16 f16;
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -79,5 +81,92 @@ __device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
 __device__ __forceinline__ f32x16 mfma32x32x16(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
+
+// ---- bf16 activations -------------------------------------------------------------------
+// gfx950 has bf16 MFMAs but no packed bf16 add, so the dequant forms (q - z) in fp32 and
+// packs pairs with v_cvt_pk_bf16_f32 (exact: |q - z| <= 15 needs 4 significant bits).  A
+// nibble at bits 4j..4j+3 OR-ed into the mantissa of 2^(23 - 4j) gives 2^(23 - 4j) + q
+// (the nibble's unit is then the ulp), and subtracting 2^(23 - 4j) + z leaves q - z.
+struct ZeroOffsetsBf {
+  float o[4];  // 2^(23 - 4j) + z, j = 0..3
+};
+
+__device__ __forceinline__ ZeroOffsetsBf zero_offsets_bf(int z) {
+  const float fz = (float)z;
+  return ZeroOffsetsBf{{0x1p23f + fz, 0x1p19f + fz, 0x1p15f + fz, 0x1p11f + fz}};
+}
+
+// The four exponent patterns in VGPRs (so that mask-and-pattern folds into v_and_or_b32).
+struct MagicRegsBf {
+  uint32_t m[4];
+};
+
+__device__ __forceinline__ MagicRegsBf magic_regs_bf() {
+  MagicRegsBf r;
+  asm volatile("v_mov_b32 %0, 0x4b000000" : "=v"(r.m[0]));
+  asm volatile("v_mov_b32 %0, 0x49000000" : "=v"(r.m[1]));
+  asm volatile("v_mov_b32 %0, 0x47000000" : "=v"(r.m[2]));
+  asm volatile("v_mov_b32 %0, 0x45000000" : "=v"(r.m[3]));
+  return r;
+}
+
+// One layout word -> the eight values (q - z) of its rows, in row order, as bf16 (rows 2j
+// and 2j + 1 are nibbles j and j + 4, at bits 4j of the word and of its upper half).
+__device__ __forceinline__ bf16x8 dequant8_bf(uint32_t w, ZeroOffsetsBf zo, MagicRegsBf mr) {
+  const uint32_t w16 = w >> 16;
+  bf16x8 out;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t mask = 0xFu << (4 * j);
+    const float lo = __builtin_bit_cast(float, (w & mask) | mr.m[j]) - zo.o[j];
+    const float hi = __builtin_bit_cast(float, (w16 & mask) | mr.m[j]) - zo.o[j];
+    out[2 * j] = (bf16)lo;
+    out[2 * j + 1] = (bf16)hi;
+  }
+  return out;
+}
+
+// The two activation types behind one interface.  A, scales and outputs are 16-bit values
+// of type T; activations travel as raw 16-byte granules (f16x8) until the MFMA.
+template <bool BF16>
+struct Act;
+
+template <>
+struct Act<false> {
+  using Zo = ZeroOffsets;
+  using Mr = MagicRegs;
+  using W8 = f16x8;
+  __device__ static Zo zero(int z) { return zero_offsets(z); }
+  __device__ static Mr magic() { return magic_regs(); }
+  __device__ static W8 dequant(uint32_t w, Zo zo, Mr mr) { return dequant8(w, zo, mr); }
+  __device__ static f32x4 mfma16(f16x8 a, W8 b, f32x4 c) { return mfma16x16x32(a, b, c); }
+  __device__ static f32x16 mfma32(f16x8 a, W8 b, f32x16 c) { return mfma32x32x16(a, b, c); }
+  __device__ static float value(uint16_t bits) {
+    return (float)__builtin_bit_cast(f16, bits);
+  }
+  __device__ static uint16_t round(float v) { return __builtin_bit_cast(uint16_t, (f16)v); }
+};
+
+template <>
+struct Act<true> {
+  using Zo = ZeroOffsetsBf;
+  using Mr = MagicRegsBf;
+  using W8 = bf16x8;
+  __device__ static Zo zero(int z) { return zero_offsets_bf(z); }
+  __device__ static Mr magic() { return magic_regs_bf(); }
+  __device__ static W8 dequant(uint32_t w, Zo zo, Mr mr) { return dequant8_bf(w, zo, mr); }
+  __device__ static f32x4 mfma16(f16x8 a, W8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0,
+                                                   0);
+  }
+  __device__ static f32x16 mfma32(f16x8 a, W8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0,
+                                                   0);
+  }
+  __device__ static float value(uint16_t bits) {
+    return __builtin_bit_cast(float, (uint32_t)bits << 16);
+  }
+  __device__ static uint16_t round(float v) { return __builtin_bit_cast(uint16_t, (bf16)v); }
+};
 
 }  // namespace wq

@@ -15,11 +15,12 @@
 namespace wq {
 namespace {
 
-// c[row][col] = fp16(sum over splits 0..S-1 of partials[split][row][col]), eight columns
-// per thread, added in split order.
+// c[row][col] = round(sum over splits 0..S-1 of partials[split][row][col]) to fp16 or bf16,
+// eight columns per thread, added in split order.
+template <bool BF16>
 __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ partials,
-                                                            f16* __restrict__ c, int m, int n,
-                                                            int splits) {
+                                                            uint16_t* __restrict__ c, int m,
+                                                            int n, int splits) {
   const long per_split = (long)m * n;
   const long total = per_split / 8;
   for (long t = (long)blockIdx.x * blockDim.x + threadIdx.x; t < total;
@@ -31,31 +32,36 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restr
       lo += *reinterpret_cast<const f32x4*>(partials + sp * per_split + e);
       hi += *reinterpret_cast<const f32x4*>(partials + sp * per_split + e + 4);
     }
-    f16x8 out;
+    u32x4 out;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      out[j] = (f16)lo[j];
-      out[4 + j] = (f16)hi[j];
+      const float x0 = j < 2 ? lo[2 * j] : hi[2 * j - 4];
+      const float x1 = j < 2 ? lo[2 * j + 1] : hi[2 * j - 3];
+      out[j] = (uint32_t)Act<BF16>::round(x0) | ((uint32_t)Act<BF16>::round(x1) << 16);
     }
-    *reinterpret_cast<f16x8*>(c + e) = out;
+    *reinterpret_cast<u32x4*>(c + e) = out;
   }
 }
 
 }  // namespace
 
 hipError_t launch_reduce_splits(const float* partials, uint16_t* c, int m, int n, int splits,
-                                hipStream_t stream) {
+                                bool bf16, hipStream_t stream) {
   long blocks = ((long)m * n / 8 + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     partials, reinterpret_cast<f16*>(c), m, n, splits);
+  if (bf16)
+    hipLaunchKernelGGL(reduce_splits_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       partials, c, m, n, splits);
+  else
+    hipLaunchKernelGGL(reduce_splits_kernel<false>, dim3((unsigned)blocks), dim3(256), 0,
+                       stream, partials, c, m, n, splits);
   return hipGetLastError();
 }
 
 hipError_t launch_small_g1(const uint16_t* a, int lda, int m, const uint32_t* b,
                            const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                            const SmallPlan& plan, float* partials, hipStream_t stream) {
-  return launch_small_gpc<1>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
+  return launch_small_gpc<1, false>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
 }
 
 bool small_plan_fits(int m, int k, const SmallPlan& plan) {
@@ -78,8 +84,17 @@ bool small_plan_fits(int m, int k, const SmallPlan& plan) {
 
 hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* b,
                              const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
-                             const SmallPlan& plan, float* partials, hipStream_t stream) {
+                             const SmallPlan& plan, float* partials, bool bf16,
+                             hipStream_t stream) {
   if (!small_plan_fits(m, k, plan)) return hipErrorInvalidConfiguration;
+  if (bf16) {
+    switch (plan.gpc) {
+      case 2: return launch_small_bf16_g2(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
+      case 4: return launch_small_bf16_g4(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
+      case 8: return launch_small_bf16_g8(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
+      default: return launch_small_bf16_g1(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
+    }
+  }
   switch (plan.gpc) {
     case 2: return launch_small_g2(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
     case 4: return launch_small_g4(a, lda, m, b, s, z, c, n, k, plan, partials, stream);

@@ -1,0 +1,13 @@
+// Small-M W4A16 GEMM instances for bf16 activations
+// (64-row scale units, 2 per 128-row chunk).
+#include "wq_small_kernel.h"
+
+namespace wq {
+
+hipError_t launch_small_bf16_g2(const uint16_t* a, int lda, int m, const uint32_t* b,
+                                const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
+                                const SmallPlan& plan, float* partials, hipStream_t stream) {
+  return launch_small_gpc<2, true>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
+}
+
+}  // namespace wq

@@ -21,8 +21,9 @@ hipError_t launch_repack_zeros(const uint32_t* z, uint32_t* out, int k, int n, i
 // Gate/up column pairing for the SwiGLU epilogue (bits_per_column 32, 16 or 4).
 hipError_t launch_interleave_gate_up(const void* gate, const void* up, void* out, int rows,
                                      int cols, int bits_per_column, hipStream_t stream);
+// bf16: s and w hold bf16 values (else fp16).
 hipError_t launch_dequant(const uint32_t* b, const uint16_t* s, const uint32_t* z, int k, int n,
-                          int unit, uint16_t* w, hipStream_t stream);
+                          int unit, bool bf16, uint16_t* w, hipStream_t stream);
 hipError_t launch_gather_columns(const uint16_t* a, int lda, const int32_t* perm, uint16_t* out,
                                  int m, int k, hipStream_t stream);
 
@@ -38,32 +39,39 @@ struct SmallPlan {
   int gpc;         // scale units per 128-row chunk: 1, 2, 4 or 8 (units of 128/gpc rows)
 };
 bool small_plan_fits(int m, int k, const SmallPlan& plan);
+// bf16: A, s and c hold bf16 values (else fp16).
 hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* b,
                              const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
-                             const SmallPlan& plan, float* partials, hipStream_t stream);
-// The instances of each scale-unit count (wq_gemm_small.hip, _g2.hip, _g4.hip, _g8.hip).
-#define WQ_SMALL_GPC_DECL(G)                                                                \
-  hipError_t launch_small_g##G(const uint16_t* a, int lda, int m, const uint32_t* b,        \
-                               const uint16_t* s, const uint32_t* z, uint16_t* c, int n,    \
-                               int k, const SmallPlan& plan, float* partials,               \
-                               hipStream_t stream);
-WQ_SMALL_GPC_DECL(1)
-WQ_SMALL_GPC_DECL(2)
-WQ_SMALL_GPC_DECL(4)
-WQ_SMALL_GPC_DECL(8)
+                             const SmallPlan& plan, float* partials, bool bf16,
+                             hipStream_t stream);
+// The instances of each scale-unit count and activation type (wq_gemm_small.hip, _g2.hip,
+// _g4.hip, _g8.hip; wq_gemm_small_bf16.hip, _bf16_g2.hip, _bf16_g4.hip, _bf16_g8.hip).
+#define WQ_SMALL_GPC_DECL(NAME)                                                             \
+  hipError_t NAME(const uint16_t* a, int lda, int m, const uint32_t* b, const uint16_t* s,  \
+                  const uint32_t* z, uint16_t* c, int n, int k, const SmallPlan& plan,      \
+                  float* partials, hipStream_t stream);
+WQ_SMALL_GPC_DECL(launch_small_g1)
+WQ_SMALL_GPC_DECL(launch_small_g2)
+WQ_SMALL_GPC_DECL(launch_small_g4)
+WQ_SMALL_GPC_DECL(launch_small_g8)
+WQ_SMALL_GPC_DECL(launch_small_bf16_g1)
+WQ_SMALL_GPC_DECL(launch_small_bf16_g2)
+WQ_SMALL_GPC_DECL(launch_small_bf16_g4)
+WQ_SMALL_GPC_DECL(launch_small_bf16_g8)
 #undef WQ_SMALL_GPC_DECL
-// c = fp16(sum of the fp32 partials [splits][m][n] in split order).
+// c = round(sum of the fp32 partials [splits][m][n] in split order) to fp16, or bf16.
 hipError_t launch_reduce_splits(const float* partials, uint16_t* c, int m, int n, int splits,
-                                hipStream_t stream);
+                                bool bf16, hipStream_t stream);
 
-// Tiled kernel (wq_gemm_tile.hip): 256 x 256 output tiles on 8 waves of 128 x 64.
+// Tiled kernel (wq_tile_kernel.h, wq_gemm_tile*.hip): 256 x 256 output tiles on 8 waves
+// of 128 x 64.
 constexpr int kTileM = 256;
 constexpr int kTileN = 256;
 // swiglu: B pairs gate/up 16-column blocks and c is the [m][n/2] activation.  gpc: scale
-// sub-groups per 128 rows of K (1, or 2 / 4 for 64- / 32-row groups).
+// units per 128 rows of K (1, 2, 4 or 8).  bf16: A, s and c hold bf16 values (else fp16).
 hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b,
                             const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
-                            bool swiglu, int gpc, hipStream_t stream);
+                            bool swiglu, int gpc, bool bf16, hipStream_t stream);
 
 struct GroupedProblem {
   const uint16_t* a;
@@ -82,6 +90,7 @@ struct GroupedProblem {
   int n_expert, n_active, n_pairs, n_tokens, k, n;
   bool swiglu;            // SwiGLU epilogue: y is [n_pairs][n/2]
   int gpc;                // scale units per 128 rows of K (1, 2, 4 or 8)
+  bool bf16;              // a, scales and y hold bf16 values (else fp16)
 };
 hipError_t launch_grouped_tile(const GroupedProblem& p, hipStream_t stream);
 

@@ -88,8 +88,9 @@ __global__ __launch_bounds__(256) void repack_zeros_kernel(const uint32_t* __res
   }
 }
 
-// w[row][col] = fp16_rne((q - z) * s): the product is exact in fp32 (5-bit integer times
-// an fp16 value), so the single conversion to fp16 is the only rounding.
+// w[row][col] = rne((q - z) * s) in the scale's type (fp16, or bf16): the product is exact
+// in fp32 (a 5-bit integer times a 16-bit float), so the one conversion is the only rounding.
+template <bool BF16>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict__ b,
                                                       const uint16_t* __restrict__ s,
                                                       const uint32_t* __restrict__ z, int k,
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
     const long col = nb * 16 + c;
     const int row0 = g * kGroup + 32 * j + 8 * (lane >> 4);
     const long blk = nb * units + row0 / unit;  // the 8 rows share one scale unit
-    const float scale = (float)__builtin_bit_cast(f16, s[blk * 16 + c]);
+    const float scale = Act<BF16>::value(s[blk * 16 + c]);
     int zc = 8;
     if (z != nullptr) zc = zero_code(u32x2{z[blk * 2], z[blk * 2 + 1]}, c);
     const uint32_t word = b[o];
@@ -117,8 +118,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
     for (int i = 0; i < 8; ++i) {
       const int slot = (i & 1) ? 4 + (i >> 1) : (i >> 1);
       const int q = (int)((word >> (4 * slot)) & 0xFu);
-      const f16 v = (f16)((float)(q - zc) * scale);
-      w[(long)(row0 + i) * n + col] = __builtin_bit_cast(uint16_t, v);
+      w[(long)(row0 + i) * n + col] = Act<BF16>::round((float)(q - zc) * scale);
     }
   }
 }
@@ -283,9 +283,12 @@ hipError_t launch_interleave_gate_up(const void* gate, const void* up, void* out
 }
 
 hipError_t launch_dequant(const uint32_t* b, const uint16_t* s, const uint32_t* z, int k, int n,
-                          int unit, uint16_t* w, hipStream_t stream) {
-  hipLaunchKernelGGL(dequant_kernel, dim3(grid_for((long)k * n / 8)), dim3(256), 0, stream, b, s,
-                     z, k, n, unit, w);
+                          int unit, bool bf16, uint16_t* w, hipStream_t stream) {
+  const dim3 grid(grid_for((long)k * n / 8));
+  if (bf16)
+    hipLaunchKernelGGL(dequant_kernel<true>, grid, dim3(256), 0, stream, b, s, z, k, n, unit, w);
+  else
+    hipLaunchKernelGGL(dequant_kernel<false>, grid, dim3(256), 0, stream, b, s, z, k, n, unit, w);
   return hipGetLastError();
 }
 

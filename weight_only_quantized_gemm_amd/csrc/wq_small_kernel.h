@@ -17,8 +17,12 @@
 // MFMA step (lanes 0-31 carry its first 16 rows, lanes 32-63 the rest), so with GPC = 8
 // each step runs twice, once with the other half's weight lanes set to zero.
 //
+// BF16 selects bf16 activations, scales and outputs (bf16 MFMAs and dequant); the
+// arithmetic is otherwise the same.
+//
 // This header holds the kernel template and its launch chain; each translation unit that
-// includes it instantiates one GPC (the instances of the four counts compile in parallel).
+// includes it instantiates one GPC and activation type, so that the instances compile in
+// parallel.
 #pragma once
 #include "wq_device.h"
 #include "wq_internal.h"
@@ -58,11 +62,12 @@ constexpr long small_static_lds(int waves, bool pair, int gpc) {
 // (2t, 2t+1, as wq_interleave_gate_up pairs them); its first half of waves streams the gate
 // block, the second half the up block, both over the same K range and staged activations,
 // and the reduction writes fp16(silu(g) * u) to column 16t + c of the [m][n/2] activation.
-template <bool ZP, int WAVES, int GW, int STAGE, bool PAIR, int GPC>
+template <bool ZP, int WAVES, int GW, int STAGE, bool PAIR, int GPC, bool BF16>
 __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     const f16* __restrict__ a, int lda, int m, const u32x4* __restrict__ b,
-    const f16* __restrict__ s, const u32x2* __restrict__ z, f16* __restrict__ c, int n,
-    int groups, int splits, float* __restrict__ partials) {
+    const uint16_t* __restrict__ s, const u32x2* __restrict__ z, uint16_t* __restrict__ c,
+    int n, int groups, int splits, float* __restrict__ partials) {
+  using A = Act<BF16>;
   constexpr int T = WAVES * 64;
   constexpr int NB = PAIR ? 2 : 1;            // column blocks of the work-group
   constexpr int KW = WAVES / NB;              // waves splitting K for one block
@@ -163,9 +168,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   //    group scales are read up front and each chunk's activation operands are read from
   //    LDS while the previous chunk's MFMAs run, so that no LDS round trip sits between a
   //    weight chunk's arrival and its products.
-  const MagicRegs mr = magic_regs();
+  const auto mr = A::magic();
   const int arow = (col < m ? col : m - 1) * per_row;
-  const f16* s_half = reinterpret_cast<const f16*>(s_lds);
+  const uint16_t* s_half = reinterpret_cast<const uint16_t*>(s_lds);
   int gl[GW];  // chunk of step i inside the staged range (clamped for the masked steps)
   constexpr int HS = GPC <= 4 ? GPC : 1;  // scales hoisted per chunk (read in place for 8)
   float sc[GW][HS];
@@ -175,7 +180,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     if constexpr (GPC <= 4) {
 #pragma unroll
       for (int t = 0; t < GPC; ++t) {
-        const float v = (float)s_half[((half * span + gl[i]) * GPC + t) * 16 + col];
+        const float v = A::value(s_half[((half * span + gl[i]) * GPC + t) * 16 + col]);
         sc[i][t] = i < gw ? v : 0.f;
       }
     }
@@ -199,13 +204,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     if constexpr (GPC <= 4) {
 #pragma unroll
       for (int t = 0; t < GPC; ++t) {
-        const ZeroOffsets zo =
-            zero_offsets(ZP ? zero_code(z_lds[(half * span + gl[i]) * GPC + t], col) : 8);
+        const auto zo = A::zero(ZP ? zero_code(z_lds[(half * span + gl[i]) * GPC + t], col) : 8);
         f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int jj = 0; jj < JQ; ++jj) {
           const int j = t * JQ + jj;
-          p = mfma16x16x32(ac[j], dequant8(bw[i][j], zo, mr), p);
+          p = A::mfma16(ac[j], A::dequant(bw[i][j], zo, mr), p);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sc[i][t], p[e], acc[e]);
@@ -215,18 +219,17 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
       // the MFMA of that unit and zeros the other's, so each product sums one unit only.
       const int hi = qd >> 1;
       const int ubase = (half * span + gl[i]) * 8;
-      const f16x8 zero8 = f16x8{};
+      const typename A::W8 zero8{};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const ZeroOffsets zo =
-            zero_offsets(ZP ? zero_code(z_lds[ubase + 2 * j + hi], col) : 8);
-        const f16x8 w = dequant8(bw[i][j], zo, mr);
-        const f32x4 p0 = mfma16x16x32(ac[j], hi ? zero8 : w, f32x4{0.f, 0.f, 0.f, 0.f});
-        const f32x4 p1 = mfma16x16x32(ac[j], hi ? w : zero8, f32x4{0.f, 0.f, 0.f, 0.f});
+        const auto zo = A::zero(ZP ? zero_code(z_lds[ubase + 2 * j + hi], col) : 8);
+        const typename A::W8 w = A::dequant(bw[i][j], zo, mr);
+        const f32x4 p0 = A::mfma16(ac[j], hi ? zero8 : w, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 p1 = A::mfma16(ac[j], hi ? w : zero8, f32x4{0.f, 0.f, 0.f, 0.f});
         // (the reads are unconditional, in bounds through the clamped chunk; a masked step
         // selects zero scales)
-        const float v0 = (float)s_half[(ubase + 2 * j) * 16 + col];
-        const float v1 = (float)s_half[(ubase + 2 * j + 1) * 16 + col];
+        const float v0 = A::value(s_half[(ubase + 2 * j) * 16 + col]);
+        const float v1 = A::value(s_half[(ubase + 2 * j + 1) * 16 + col]);
         const float s0 = i < gw ? v0 : 0.f;
         const float s1 = i < gw ? v1 : 0.f;
 #pragma unroll
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = 4 * qd + e;
-      if (row < m) c[(long)row * (n / 2) + colj] = (f16)silu_times(gs[e], us[e]);
+      if (row < m) c[(long)row * (n / 2) + colj] = A::round(silu_times(gs[e], us[e]));
     }
     return;
   }
@@ -268,7 +271,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     const int row = 4 * qd + e;
     if (row >= m) continue;
     if (splits == 1)
-      c[(long)row * n + colx] = (f16)tot[e];
+      c[(long)row * n + colx] = A::round(tot[e]);
     else
       partials[((long)split * m + row) * n + colx] = tot[e];
   }
@@ -285,7 +288,7 @@ inline int round_slots(int slots) {
   return slots <= 1 ? 1 : slots <= 2 ? 2 : slots <= 4 ? 4 : slots <= 8 ? 8 : 16;
 }
 
-template <bool ZP, int WAVES, int GW, int STAGE, bool PAIR, int GPC>
+template <bool ZP, int WAVES, int GW, int STAGE, bool PAIR, int GPC, bool BF16>
 hipError_t launch_small_t(const uint16_t* a, int lda, int m, const uint32_t* b,
                           const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                           int splits, float* partials, hipStream_t stream) {
@@ -293,28 +296,27 @@ hipError_t launch_small_t(const uint16_t* a, int lda, int m, const uint32_t* b,
   // The activation slice of this instance (its size is fixed by STAGE and WAVES).
   constexpr size_t lds = (size_t)STAGE * WAVES * 64 * sizeof(f16x8);
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC>),
+      reinterpret_cast<const void*>(&gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
   const dim3 grid(n / (PAIR ? 32 : 16), splits);
-  hipLaunchKernelGGL((gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC>), grid,
+  hipLaunchKernelGGL((gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16>), grid,
                      dim3(WAVES * 64), lds, stream, reinterpret_cast<const f16*>(a), lda, m,
-                     reinterpret_cast<const u32x4*>(b), reinterpret_cast<const f16*>(s),
-                     reinterpret_cast<const u32x2*>(z), reinterpret_cast<f16*>(c), n, groups,
-                     splits, partials);
+                     reinterpret_cast<const u32x4*>(b), s, reinterpret_cast<const u32x2*>(z), c,
+                     n, groups, splits, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  return launch_reduce_splits(partials, c, m, n, splits, stream);
+  return launch_reduce_splits(partials, c, m, n, splits, BF16, stream);
 }
 
-template <bool ZP, int WAVES, int GW, bool PAIR, int GPC>
+template <bool ZP, int WAVES, int GW, bool PAIR, int GPC, bool BF16>
 hipError_t launch_small_stage(const uint16_t* a, int lda, int m, const uint32_t* b,
                               const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                               const SmallPlan& plan, float* partials, hipStream_t stream) {
   const int span = (k / kGroup + plan.splits - 1) / plan.splits;
 #define WQ_SMALL(ST)                                                                         \
-  launch_small_t<ZP, WAVES, GW, ST, PAIR, GPC>(a, lda, m, b, s, z, c, n, k, plan.splits,     \
-                                               partials, stream)
+  launch_small_t<ZP, WAVES, GW, ST, PAIR, GPC, BF16>(a, lda, m, b, s, z, c, n, k,            \
+                                                     plan.splits, partials, stream)
   switch (round_slots(stage_slots(m, span, WAVES))) {
     case 1: return WQ_SMALL(1);
     case 2: return WQ_SMALL(2);
@@ -325,13 +327,13 @@ hipError_t launch_small_stage(const uint16_t* a, int lda, int m, const uint32_t*
 #undef WQ_SMALL
 }
 
-template <bool ZP, int WAVES, bool PAIR, int GPC>
+template <bool ZP, int WAVES, bool PAIR, int GPC, bool BF16>
 hipError_t launch_small_gw(const uint16_t* a, int lda, int m, const uint32_t* b,
                            const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                            const SmallPlan& plan, float* partials, hipStream_t stream) {
 #define WQ_SMALL(GWV)                                                                          \
-  launch_small_stage<ZP, WAVES, GWV, PAIR, GPC>(a, lda, m, b, s, z, c, n, k, plan, partials, \
-                                                stream)
+  launch_small_stage<ZP, WAVES, GWV, PAIR, GPC, BF16>(a, lda, m, b, s, z, c, n, k, plan,     \
+                                                      partials, stream)
   switch (plan.depth) {
     case 1: return WQ_SMALL(1);
     case 2: return WQ_SMALL(2);
@@ -341,32 +343,34 @@ hipError_t launch_small_gw(const uint16_t* a, int lda, int m, const uint32_t* b,
 #undef WQ_SMALL
 }
 
-template <bool ZP, int GPC>
+template <bool ZP, int GPC, bool BF16>
 hipError_t launch_small_waves(const uint16_t* a, int lda, int m, const uint32_t* b,
                               const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                               const SmallPlan& plan, float* partials, hipStream_t stream) {
   if (plan.pair) {
     if (plan.waves == 16)
-      return launch_small_gw<ZP, 16, true, GPC>(a, lda, m, b, s, z, c, n, k, plan, partials,
+      return launch_small_gw<ZP, 16, true, GPC, BF16>(a, lda, m, b, s, z, c, n, k, plan, partials,
                                                 stream);
-    return launch_small_gw<ZP, 8, true, GPC>(a, lda, m, b, s, z, c, n, k, plan, partials,
+    return launch_small_gw<ZP, 8, true, GPC, BF16>(a, lda, m, b, s, z, c, n, k, plan, partials,
                                              stream);
   }
   if (plan.waves == 8)
-    return launch_small_gw<ZP, 8, false, GPC>(a, lda, m, b, s, z, c, n, k, plan, partials,
+    return launch_small_gw<ZP, 8, false, GPC, BF16>(a, lda, m, b, s, z, c, n, k, plan, partials,
                                               stream);
-  return launch_small_gw<ZP, 4, false, GPC>(a, lda, m, b, s, z, c, n, k, plan, partials,
+  return launch_small_gw<ZP, 4, false, GPC, BF16>(a, lda, m, b, s, z, c, n, k, plan, partials,
                                             stream);
 }
 
-// Entry of one GPC: the plan has been checked by small_plan_fits.
-template <int GPC>
+// Entry of one GPC and activation type: the plan has been checked by small_plan_fits.
+template <int GPC, bool BF16>
 hipError_t launch_small_gpc(const uint16_t* a, int lda, int m, const uint32_t* b,
                             const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                             const SmallPlan& plan, float* partials, hipStream_t stream) {
   if (z != nullptr)
-    return launch_small_waves<true, GPC>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
-  return launch_small_waves<false, GPC>(a, lda, m, b, s, z, c, n, k, plan, partials, stream);
+    return launch_small_waves<true, GPC, BF16>(a, lda, m, b, s, z, c, n, k, plan, partials,
+                                               stream);
+  return launch_small_waves<false, GPC, BF16>(a, lda, m, b, s, z, c, n, k, plan, partials,
+                                              stream);
 }
 
 }  // namespace

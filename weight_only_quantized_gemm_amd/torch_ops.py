@@ -11,8 +11,8 @@ import math
 import numpy as np
 import torch
 
-from . import (WQ_FLAG_ACT_ORDER, WQ_FLAG_FP32_REDUCE, WQ_FLAG_HAS_ZP, WQ_FLAG_MUL_TOPK_WEIGHTS,
-               WQ_FLAG_SWIGLU, wq_act_order_perm, wq_interleave_gate_up,
+from . import (WQ_FLAG_ACT_ORDER, WQ_FLAG_BF16, WQ_FLAG_FP32_REDUCE, WQ_FLAG_HAS_ZP,
+               WQ_FLAG_MUL_TOPK_WEIGHTS, WQ_FLAG_SWIGLU, wq_act_order_perm, wq_interleave_gate_up,
                wq_gemm, wq_gemm_workspace_bytes, wq_grouped_gemm, wq_repack_b,
                wq_repack_scales, wq_repack_zeros)
 
@@ -20,23 +20,35 @@ GROUP = 128
 
 
 def to_device(x: np.ndarray, device) -> torch.Tensor:
-    """Upload a numpy array (a tensor is moved as it is); uint32 words travel as int32."""
+    """Upload a numpy array (a tensor is moved as it is); uint32 words travel as int32 and
+    uint16 arrays, which hold bf16 bit patterns (numpy has no bf16), arrive as bfloat16."""
     if isinstance(x, torch.Tensor):
         return x.to(device)
     x = np.ascontiguousarray(x)
     if x.dtype == np.uint32:
         x = x.view(np.int32)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).to(device).view(torch.bfloat16)
     return torch.from_numpy(x).to(device)
 
 
+def act_dtype(bf16: bool) -> torch.dtype:
+    """Element type of activations, scales and outputs."""
+    return torch.bfloat16 if bf16 else torch.float16
+
+
 class PackedWeight:
-    """One weight matrix in the library layout (B, scales, optional zero points, perm)."""
+    """One weight matrix in the library layout (B, scales, optional zero points, perm).
+    bf16: the scales (numpy uint16 bit patterns or a bfloat16 tensor) and the activations
+    and outputs of its products are bf16."""
 
     def __init__(self, qweight: np.ndarray, scales: np.ndarray, zeros: np.ndarray | None = None,
-                 g_idx: np.ndarray | None = None, device="cuda", group_size: int = GROUP):
+                 g_idx: np.ndarray | None = None, device="cuda", group_size: int = GROUP,
+                 bf16: bool = False):
         self.k = qweight.shape[0] * 8
         self.n = qweight.shape[1]
         self.group_size = group_size
+        self.bf16 = bf16
         self.swiglu = False
         self.device = torch.device(device)
         self.perm = None
@@ -47,9 +59,10 @@ class PackedWeight:
         self.b = torch.empty(self.k * self.n // 8, dtype=torch.int32, device=self.device)
         wq_repack_b(qw, self.b, self.k, self.n, perm=self.perm)
         sc = to_device(scales if isinstance(scales, torch.Tensor)
-                       else np.asarray(scales, dtype=np.float16), self.device)
+                       else np.asarray(scales, dtype=np.uint16 if bf16 else np.float16),
+                       self.device)
         unit = math.gcd(group_size, GROUP) if group_size > 0 else GROUP  # rows per scale row
-        self.s = torch.empty((self.k // unit) * self.n, dtype=torch.float16, device=self.device)
+        self.s = torch.empty((self.k // unit) * self.n, dtype=act_dtype(bf16), device=self.device)
         wq_repack_scales(sc, self.s, self.k, self.n, group_size)
         self.z = None
         if zeros is not None:
@@ -61,7 +74,7 @@ class PackedWeight:
 
     @classmethod
     def gate_up(cls, gate: dict, up: dict, device="cuda", group_size: int = GROUP,
-                g_idx: np.ndarray | None = None) -> "PackedWeight":
+                g_idx: np.ndarray | None = None, bf16: bool = False) -> "PackedWeight":
         """One weight of 2*I columns for the SwiGLU epilogue: the gate and up projections'
         qweight, scales and zero points paired in 16-column blocks on the device
         (wq_interleave_gate_up), then repacked like any weight."""
@@ -76,7 +89,7 @@ class PackedWeight:
 
         zeros = pair("zeros", 4) if gate.get("zeros") is not None else None
         w = cls(pair("qweight", 32), pair("scales", 16), zeros, g_idx, device=dev,
-                group_size=group_size)
+                group_size=group_size, bf16=bf16)
         w.swiglu = True
         return w
 
@@ -99,6 +112,8 @@ class PackedWeight:
             f |= WQ_FLAG_FP32_REDUCE
         if self.swiglu:
             f |= WQ_FLAG_SWIGLU
+        if self.bf16:
+            f |= WQ_FLAG_BF16
         return f
 
 
@@ -107,7 +122,7 @@ class GemmBuffers:
 
     def __init__(self, w: PackedWeight, m: int, fp32_reduce: bool):
         self.flags = w.flags(fp32_reduce)
-        self.a_tmp = (torch.empty((m, w.k), dtype=torch.float16, device=w.device)
+        self.a_tmp = (torch.empty((m, w.k), dtype=act_dtype(w.bf16), device=w.device)
                       if w.perm is not None else None)
         nbytes = wq_gemm_workspace_bytes(m, w.n, w.k, self.flags)
         self.workspace = (torch.zeros(nbytes, dtype=torch.uint8, device=w.device)
@@ -120,9 +135,11 @@ def gemm(a: torch.Tensor, w: PackedWeight, out: torch.Tensor | None = None, *,
     """C = A @ dequant(B) through wq_gemm (A fp16 [m][k], row stride a.stride(0)); for a
     gate/up weight, the [m][n/2] SwiGLU activation."""
     m = a.shape[0]
+    if a.dtype != act_dtype(w.bf16):
+        raise TypeError(f"activations are {a.dtype}, the weight expects {act_dtype(w.bf16)}")
     if out is None:
         cols = w.n // 2 if w.swiglu else w.n
-        out = torch.empty((m, cols), dtype=torch.float16, device=a.device)
+        out = torch.empty((m, cols), dtype=act_dtype(w.bf16), device=a.device)
     if buffers is None:
         buffers = GemmBuffers(w, m, fp32_reduce)
     wq_gemm(a, w.b, out, w.s, m=m, n=w.n, k=w.k, zero_points=w.z, perm=w.perm,
@@ -134,18 +151,20 @@ def gemm(a: torch.Tensor, w: PackedWeight, out: torch.Tensor | None = None, *,
 class ExpertBank:
     """Repacked weights of several experts stored back to back (one stride per tensor)."""
 
-    def __init__(self, experts: list[dict], device="cuda"):
+    def __init__(self, experts: list[dict], device="cuda", bf16: bool = False):
         """Each expert is a weight dict (qweight, scales, optional zeros and group_size), or
         {"gate": ..., "up": ...} for a fused gate/up projection with the SwiGLU epilogue."""
         def pack(e):
             gs = e.get("group_size", GROUP)
             if "gate" in e:
-                return PackedWeight.gate_up(e["gate"], e["up"], device=device, group_size=gs)
+                return PackedWeight.gate_up(e["gate"], e["up"], device=device, group_size=gs,
+                                            bf16=bf16)
             return PackedWeight(e["qweight"], e["scales"], e.get("zeros"), device=device,
-                                group_size=gs)
+                                group_size=gs, bf16=bf16)
         self.packed = [pack(e) for e in experts]
         p0 = self.packed[0]
         self.k, self.n, self.group_size, self.swiglu = p0.k, p0.n, p0.group_size, p0.swiglu
+        self.bf16 = bf16
         self.b = torch.stack([p.b for p in self.packed])
         self.s = torch.stack([p.s for p in self.packed])
         self.z = torch.stack([p.z for p in self.packed]) if p0.z is not None else None
@@ -167,7 +186,7 @@ def grouped_gemm(a: torch.Tensor, bank: ExpertBank, csr: dict, out: torch.Tensor
     n_pairs = len(csr["ex_pairs"])
     if out is None:
         cols = bank.n // 2 if bank.swiglu else bank.n
-        out = torch.empty((n_pairs, cols), dtype=torch.float16, device=a.device)
+        out = torch.empty((n_pairs, cols), dtype=act_dtype(bank.bf16), device=a.device)
     wq_grouped_gemm(a, bank.b, bank.b_stride, bank.s, bank.s_stride, device_csr["ex_ids"],
                     device_csr["ex_off"], device_csr["ex_pairs"], device_csr["pair_tok"], out,
                     n_expert=bank.n_expert, n_active=len(csr["ex_ids"]), n_pairs=n_pairs,
@@ -176,6 +195,7 @@ def grouped_gemm(a: torch.Tensor, bank: ExpertBank, csr: dict, out: torch.Tensor
                     group_size=bank.group_size,
                     flags=(WQ_FLAG_HAS_ZP if bank.z is not None else 0)
                     | (WQ_FLAG_MUL_TOPK_WEIGHTS if topk_weights is not None else 0)
-                    | (WQ_FLAG_SWIGLU if bank.swiglu else 0),
+                    | (WQ_FLAG_SWIGLU if bank.swiglu else 0)
+                    | (WQ_FLAG_BF16 if bank.bf16 else 0),
                     stream=stream)
     return out

@@ -126,6 +126,25 @@ __device__ __forceinline__ bf16x8 dequant8_bf(uint32_t w, ZeroOffsetsBf zo, Magi
   return out;
 }
 
+// Biased bf16 dequant for kernels with MFMA to spare: one layout word -> the eight values
+// 128 + q of its rows (row order as above), each nibble OR-ed into the mantissa of 128.0
+// (bf16 0x4300, whose ulp is 1).  A product with these operands is corrected afterwards
+// by subtracting (128 + z) times the product with all-ones operands, the activation sums.
+__device__ __forceinline__ bf16x8 dequant8_bf_biased(uint32_t w, uint32_t m128) {
+  u32x4 d;
+  d[0] = (w & 0x000F000Fu) | m128;
+  d[1] = ((w >> 4) & 0x000F000Fu) | m128;
+  d[2] = ((w >> 8) & 0x000F000Fu) | m128;
+  d[3] = ((w >> 12) & 0x000F000Fu) | m128;
+  return __builtin_bit_cast(bf16x8, d);
+}
+
+__device__ __forceinline__ uint32_t magic_reg_bf128() {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(r));
+  return r;
+}
+
 // The two activation types behind one interface.  A, scales and outputs are 16-bit values
 // of type T; activations travel as raw 16-byte granules (f16x8) until the MFMA.
 template <bool BF16>

@@ -168,7 +168,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   //    group scales are read up front and each chunk's activation operands are read from
   //    LDS while the previous chunk's MFMAs run, so that no LDS round trip sits between a
   //    weight chunk's arrival and its products.
-  const auto mr = A::magic();
+  // fp16: the magic-number registers of the exact dequant; bf16: the 128.0 pattern of the
+  // biased one (see below).
+  const auto mr = [] {
+    if constexpr (BF16)
+      return magic_reg_bf128();
+    else
+      return A::magic();
+  }();
   const int arow = (col < m ? col : m - 1) * per_row;
   const uint16_t* s_half = reinterpret_cast<const uint16_t*>(s_lds);
   int gl[GW];  // chunk of step i inside the staged range (clamped for the masked steps)
@@ -201,7 +208,58 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     // With eight groups per wave, pin the prefetch ahead of this group's work (measured
     // faster for the decode shape, slower for shallower pipelines).
     if constexpr (GW >= 8) __builtin_amdgcn_sched_barrier(0);
-    if constexpr (GPC <= 4) {
+    if constexpr (BF16) {
+      // bf16 has no packed add, and the exact dequant costs 21 VALU per word, which this
+      // weight-stream-bound kernel cannot hide.  The weights enter the MFMA biased, as
+      // 128 + q (7 VALU per word), and the same activations meet an all-ones operand: r is
+      // the activation sum of each row, and p - (128 + z) * r the exact-weight partial,
+      // formed in fp32 by one fma (the cancellation costs about 2^-19 relative).
+      const bf16x8 ones = __builtin_bit_cast(
+          bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+      const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (GPC <= 4) {
+#pragma unroll
+        for (int t = 0; t < GPC; ++t) {
+          const int zc = ZP ? zero_code(z_lds[(half * span + gl[i]) * GPC + t], col) : 8;
+          const float off = (float)(128 + zc);
+          f32x4 p = zero4, r = zero4;
+#pragma unroll
+          for (int jj = 0; jj < JQ; ++jj) {
+            const int j = t * JQ + jj;
+            p = A::mfma16(ac[j], dequant8_bf_biased(bw[i][j], mr), p);
+            r = A::mfma16(ac[j], ones, r);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[e] = __builtin_fmaf(sc[i][t], __builtin_fmaf(-off, r[e], p[e]), acc[e]);
+        }
+      } else {
+        // 16-row units: as on the fp16 path, each MFMA sees one unit's half of the step.
+        const int hi = qd >> 1;
+        const int ubase = (half * span + gl[i]) * 8;
+        const bf16x8 zero8{};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x8 w = dequant8_bf_biased(bw[i][j], mr);
+          const f32x4 p0 = A::mfma16(ac[j], hi ? zero8 : w, zero4);
+          const f32x4 p1 = A::mfma16(ac[j], hi ? w : zero8, zero4);
+          const f32x4 r0 = A::mfma16(ac[j], hi ? zero8 : ones, zero4);
+          const f32x4 r1 = A::mfma16(ac[j], hi ? ones : zero8, zero4);
+          const int z0 = ZP ? zero_code(z_lds[ubase + 2 * j], col) : 8;
+          const int z1 = ZP ? zero_code(z_lds[ubase + 2 * j + 1], col) : 8;
+          const float v0 = A::value(s_half[(ubase + 2 * j) * 16 + col]);
+          const float v1 = A::value(s_half[(ubase + 2 * j + 1) * 16 + col]);
+          const float s0 = i < gw ? v0 : 0.f;
+          const float s1 = i < gw ? v1 : 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[e] = __builtin_fmaf(s0, __builtin_fmaf(-(float)(128 + z0), r0[e], p0[e]), acc[e]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[e] = __builtin_fmaf(s1, __builtin_fmaf(-(float)(128 + z1), r1[e], p1[e]), acc[e]);
+        }
+      }
+    } else if constexpr (GPC <= 4) {
 #pragma unroll
       for (int t = 0; t < GPC; ++t) {
         const auto zo = A::zero(ZP ? zero_code(z_lds[(half * span + gl[i]) * GPC + t], col) : 8);

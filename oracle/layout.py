@@ -76,6 +76,46 @@ def unrepack_b(words: np.ndarray, k_total: int, n_total: int) -> np.ndarray:
     return codes.transpose(1, 4, 2, 5, 0, 3).reshape(k_total, n_total)
 
 
+def repack_fp8_loops(codes: np.ndarray) -> np.ndarray:
+    """Library layout of E4M3 weights from codes uint8 [K][N] (nested loops, small shapes).
+
+    Per 16-column block nb, 128-row group g and half h (rows 64h..64h+63 of the group), each
+    lane l = c + 16*qd (column 16*nb + c) holds four words; word d covers rows
+    128g + 32(2h + d//2) + 8qd + 4(d%2) + i in byte i.  The lane's eight rows of each 32-row
+    step are thus two words, the B operand of one 16x16x32 MFMA after conversion.
+    Flat word index: (((nb * G + g) * 2 + h) * 64 + l) * 4 + d.
+    """
+    k_total, n_total = codes.shape
+    groups = k_total // 128
+    out = np.zeros(k_total * n_total // 4, dtype=np.uint32)
+    for nb in range(n_total // 16):
+        for g in range(groups):
+            for h in range(2):
+                for lane in range(64):
+                    c, qd = lane % 16, lane // 16
+                    for d in range(4):
+                        word = 0
+                        for i in range(4):
+                            row = 128 * g + 32 * (2 * h + d // 2) + 8 * qd + 4 * (d % 2) + i
+                            word |= int(codes[row, 16 * nb + c]) << (8 * i)
+                        out[(((nb * groups + g) * 2 + h) * 64 + lane) * 4 + d] = word
+    return out
+
+
+def unrepack_fp8(words: np.ndarray, k_total: int, n_total: int) -> np.ndarray:
+    """Inverse of repack_fp8_loops (vectorized): library words -> codes uint8 [K][N]."""
+    groups = k_total // 128
+    w = np.asarray(words, dtype=np.uint32).reshape(n_total // 16, groups, 2, 4, 16, 2, 2)
+    # axes: nb, g, h, qd, c, jj (= d // 2), half (= d % 2)
+    out = np.empty((k_total, n_total), dtype=np.uint8)
+    for i in range(4):
+        b = ((w >> np.uint32(8 * i)) & np.uint32(0xFF)).astype(np.uint8)
+        # row = 128g + 64h + 32jj + 8qd + 4half + i; column = 16nb + c
+        t = b.transpose(1, 2, 5, 3, 6, 0, 4)  # g, h, jj, qd, half, nb, c
+        out[i::4, :] = t.reshape(k_total // 4, n_total)
+    return out
+
+
 def interleave_gate_up(gate: np.ndarray, up: np.ndarray, cols_per_elem: int = 1) -> np.ndarray:
     """Pair the columns of two row-major tensors in 16-column blocks: out column block 2t is
     block t of `gate`, block 2t+1 block t of `up` (a fused gate/up projection's weights).

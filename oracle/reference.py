@@ -17,6 +17,9 @@ tests; this is the plain definition they describe):
   `repack_gptq_qzeros_to_marlin`: zero points are the actual codes (0..15).
 * ferrum-kernels marlin.rs, `MarlinWeight.perm` doc: act_order; each row k belongs to group
   g_idx[k]; the permutation is argsort(g_idx).
+* ferrum-kernels vllm_marlin.rs, `ferrum_vllm_marlin_moe_fp8_f16` and
+  `vllm_fp8_marlin_repack_raw_bits`: W8A16 with E4M3 weights (K-major words of four bytes),
+  fp16 scales channelwise or per 128 rows, no zero points.
 * ferrum-kernels vllm_marlin.rs, `ferrum_vllm_marlin_moe_mxfp4_bf16`: the pages' bf16
   activation and output type.  Read here with the same 4-bit integer weights: with bf16,
   activations and scales arrive as bf16 bit patterns (the upper half of a binary32).
@@ -171,6 +174,61 @@ def w4a16_gemm(a, qweight, scales, *, zeros=None, g_idx=None, group_size=128,
 
 
 # ---------------------------------------------------------------------------------------
+# W8A16: FP8 E4M3 weights (vllm_marlin.rs `ferrum_vllm_marlin_moe_fp8_f16`, the E4M3 weight
+# type: fp16 activations and scales, scales channelwise (group_size -1) or per 128 rows of
+# K, no zero points; weights arrive as K-major words of four E4M3 bytes per output channel,
+# `vllm_fp8_marlin_repack_raw_bits`)
+# ---------------------------------------------------------------------------------------
+
+FP8_GROUP_SIZES = (-1, 128)
+
+
+def e4m3_value(codes) -> np.ndarray:
+    """fp64 values of E4M3 (the "fn" variant the pages name, FE4M3FN) bytes: sign bit, 4
+    exponent bits with bias 7, 3 mantissa bits; exponent 0 is subnormal (2^-6 * m/8);
+    0x7F and 0xFF are NaN; there are no infinities."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def unpack_fp8_words(words: np.ndarray) -> np.ndarray:
+    """uint32 [K/4][N] -> uint8 codes [K][N]: byte i (bits 8i..8i+7) of word (r, n) is row
+    4r + i of column n (little-endian, K-major)."""
+    w = np.asarray(words, dtype=np.uint32)
+    r, n = w.shape
+    out = np.empty((4 * r, n), dtype=np.uint8)
+    for i in range(4):
+        out[i::4, :] = (w >> np.uint32(8 * i)) & np.uint32(0xFF)
+    return out
+
+
+def w8a16_weights(words, scales, *, group_size=128, columns=None, bf16=False) -> np.ndarray:
+    """Exact fp64 weights W[k, n] = e4m3(code[k, n]) * s[g(k), n]."""
+    if group_size not in FP8_GROUP_SIZES:
+        raise ValueError(f"E4M3 group size must be -1 or 128, got {group_size}")
+    words = np.asarray(words, dtype=np.uint32)
+    scales = np.asarray(scales)
+    k = words.shape[0] * 4
+    num_groups(k, group_size)
+    if columns is not None:
+        cols = np.asarray(columns, dtype=np.int64)
+        words, scales = words[:, cols], scales[:, cols]
+    group = group_of_rows(k, group_size)
+    return e4m3_value(unpack_fp8_words(words)) * values16(scales, bf16)[group, :]
+
+
+def w8a16_gemm(a, words, scales, *, group_size=128, columns=None, bf16=False) -> np.ndarray:
+    """Reference C = A @ W for E4M3 weights, fp64 and unrounded."""
+    return matmul_fp64(a, w8a16_weights(words, scales, group_size=group_size, columns=columns,
+                                        bf16=bf16), bf16)
+
+
+# ---------------------------------------------------------------------------------------
 # act_order
 # ---------------------------------------------------------------------------------------
 
@@ -283,7 +341,7 @@ def validate_csr(csr: dict) -> None:
 
 
 def grouped_w4a16_gemm(a, experts, csr, *, group_size=128, columns=None,
-                       pairs=None, topk_weights=None, bf16=False) -> np.ndarray:
+                       pairs=None, topk_weights=None, bf16=False, fp8=False) -> np.ndarray:
     """Pair-major reference y[p] = A[pair_tok[p]] @ dequant(B_e) for the expert e owning p.
 
     Walks the expert-major CSR: segment i covers positions ex_off[i]..ex_off[i+1] of
@@ -293,7 +351,8 @@ def grouped_w4a16_gemm(a, experts, csr, *, group_size=128, columns=None,
 
     With `topk_weights` (one fp32 routing weight per pair, pair-major: the vllm_marlin.rs
     MoE launch's `topk_weights` under `mul_topk_weights`), row p is multiplied by
-    topk_weights[p], in fp64.  With bf16, A and the scales are bf16 bit patterns.
+    topk_weights[p], in fp64.  With bf16, A and the scales are bf16 bit patterns; with fp8,
+    each expert's qweight holds E4M3 words ([K/4][N]) instead of 4-bit codes.
     """
     a = np.asarray(a)
     n_pairs = len(csr["ex_pairs"])
@@ -307,8 +366,12 @@ def grouped_w4a16_gemm(a, experts, csr, *, group_size=128, columns=None,
         if not rows:
             continue
         ex = experts[e]
-        w = w4a16_weights(ex["qweight"], ex["scales"], zeros=ex.get("zeros"),
-                          group_size=group_size, columns=columns, bf16=bf16)
+        if fp8:
+            w = w8a16_weights(ex["qweight"], ex["scales"], group_size=group_size,
+                              columns=columns, bf16=bf16)
+        else:
+            w = w4a16_weights(ex["qweight"], ex["scales"], zeros=ex.get("zeros"),
+                              group_size=group_size, columns=columns, bf16=bf16)
         toks = [csr["pair_tok"][p] for p in rows]
         y[rows, :] = matmul_fp64(a[toks, :], w, bf16)
         if topk_weights is not None:

@@ -134,6 +134,19 @@ def scales(seed: int, groups: int, n: int, lo: float = 0.005, hi: float = 0.02) 
     return (lo + (hi - lo) * uniform01(seed, groups * n)).astype(np.float16).reshape(groups, n)
 
 
+FP8_CODES = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint32)  # no NaN
+
+
+def fp8_words(seed: int, k: int, n: int) -> np.ndarray:
+    """E4M3 weight codes, uniform over the 254 non-NaN bytes, packed K-major four to a
+    word (byte i of word (r, n) is row 4r + i): uint32 [k/4][n]."""
+    codes = FP8_CODES[below(seed, k * n, FP8_CODES.size)].reshape(k // 4, 4, n)
+    words = np.zeros((k // 4, n), dtype=np.uint32)
+    for i in range(4):
+        words |= codes[:, i, :] << np.uint32(8 * i)
+    return words
+
+
 def zero_point_words(seed: int, groups: int, n: int) -> np.ndarray:
     """Uniform 4-bit zero-point codes 0..15 packed 8 per word: uint32 [groups][n/8]."""
     return words_u32(seed, groups * (n // 8)).reshape(groups, n // 8)
@@ -205,6 +218,17 @@ def dense_case(m: int, k: int, n: int, *, zp: bool = False, act_order: bool = Fa
                                k if group_size == -1 else group_size) if act_order else None),
     )
     return case
+
+
+def fp8_case(m: int, k: int, n: int, *, group_size: int = GROUP_SIZE, seed: int = ROOT_SEED,
+             bf16: bool = False) -> dict:
+    """One dense W8A16 problem: A, E4M3 words [k/4][n] and scales (group_size -1 or 128)."""
+    groups = 1 if group_size == -1 else k // group_size
+    act, sc = (activations_bf16, scales_bf16) if bf16 else (activations, scales)
+    return dict(m=m, k=k, n=n, group_size=group_size, bf16=bf16, fp8=True,
+                a=act(stream_seed(seed, TAG_ACT), m, k),
+                qweight=fp8_words(stream_seed(seed, TAG_WEIGHT), k, n),
+                scales=sc(stream_seed(seed, TAG_SCALE), groups, n))
 
 
 def config_case(name: str, seed: int | None = None) -> dict:

@@ -378,6 +378,72 @@ def test_bf16_product_matches_bruteforce():
     np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
 
 
+def test_e4m3_values_of_known_codes():
+    """E4M3 (fn): bias 7, subnormals below exponent 1, 0x7F / 0xFF NaN, no infinities."""
+    cases = {0x00: 0.0, 0x38: 1.0, 0xB8: -1.0, 0x3C: 1.5, 0x40: 2.0, 0x7E: 448.0,
+             0xFE: -448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9,
+             0x30: 0.5, 0x77: 240.0, 0x57: 15.0, 0x5F: 30.0}
+    got = ref.e4m3_value(np.array(list(cases), dtype=np.uint8))
+    assert got.tolist() == list(cases.values())
+    assert np.isnan(ref.e4m3_value(np.array([0x7F, 0xFF], dtype=np.uint8))).all()
+    assert np.signbit(ref.e4m3_value(np.array([0x80], dtype=np.uint8)))[0]
+
+
+def test_e4m3_values_match_torch_for_every_code():
+    """Every byte against torch's float8_e4m3fn decode (a library routine the oracle does
+    not use)."""
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    got = ref.e4m3_value(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+
+
+def test_fp8_words_are_k_major_little_endian():
+    w = np.array([[0x04030201, 0xA0B0C0D0]], dtype=np.uint32)
+    assert ref.unpack_fp8_words(w).tolist() == [[1, 0xD0], [2, 0xC0], [3, 0xB0], [4, 0xA0]]
+
+
+def test_w8a16_product_matches_bruteforce():
+    m, k, n = 2, 256, 16
+    for gs, bf16 in ((128, False), (-1, False), (128, True)):
+        a = (synthetic.activations_bf16 if bf16 else synthetic.activations)(30, m, k)
+        words = synthetic.fp8_words(31, k, n)
+        groups = 1 if gs == -1 else k // gs
+        s = (synthetic.scales_bf16 if bf16 else synthetic.scales)(32, groups, n)
+        codes = ref.unpack_fp8_words(words)
+        av = ref.bf16_value(a) if bf16 else a.astype(np.float64)
+        sv = ref.bf16_value(s) if bf16 else s.astype(np.float64)
+        want = np.zeros((m, n))
+        for mi in range(m):
+            for c in range(n):
+                acc = 0.0
+                for kk in range(k):
+                    g = 0 if gs == -1 else kk // gs
+                    acc += float(av[mi, kk]) * float(ref.e4m3_value(codes[kk, c])) * sv[g, c]
+                want[mi, c] = acc
+        got = ref.w8a16_gemm(a, words, s, group_size=gs, bf16=bf16)
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12, err_msg=str((gs, bf16)))
+    with pytest.raises(ValueError):
+        ref.w8a16_weights(words, s, group_size=64)
+
+
+def test_fp8_layout_loops_and_inverse_agree():
+    codes = np.random.default_rng(33).integers(0, 256, size=(256, 32)).astype(np.uint8)
+    words = layout.repack_fp8_loops(codes)
+    assert words.size * 4 == codes.size          # a permutation of the bytes
+    assert np.array_equal(layout.unrepack_fp8(words, 256, 32), codes)
+    # word d of lane l = c + 16*qd in block 0, group 0, half 0: rows 32*(d//2) + 8qd + 4(d%2)
+    for lane in (0, 17, 63):
+        c, qd = lane % 16, lane // 16
+        for d in range(4):
+            rows = [32 * (d // 2) + 8 * qd + 4 * (d % 2) + i for i in range(4)]
+            word = int(words[lane * 4 + d])
+            assert [(word >> (8 * i)) & 0xFF for i in range(4)] == [codes[r, c] for r in rows]
+
+
 def test_act_order_with_256_row_groups_equals_plain_product():
     k, n, m, gs = 1024, 32, 4, 256
     a = synthetic.activations(70, m, k)

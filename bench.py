@@ -156,8 +156,8 @@ def bench_extended(torch, torch_ops, steps, warmup):
         del ws
     # group 128 at decode shape is the control: the same kernel timed in the same context
     # (bf16 rows: bf16 activations, scales and outputs, with the headline's flags)
-    for name, gs, bf16 in (("decode", 128, False), ("decode", 64, False),
-                           ("decode", 32, False), ("decode", 16, False), ("decode", -1, False),
+    for name, gs, bf16 in (("decode", 128, False), ("decode", -1, False), ("decode", 64, False),
+                           ("decode", 32, False), ("decode", 16, False),
                            ("prefill", 32, False), ("prefill", 16, False),
                            ("decode", 128, True), ("prefill", 128, True)):
         cfg = synthetic.CONFIGS[name]
@@ -184,6 +184,28 @@ def bench_extended(torch, torch_ops, steps, warmup):
                         + (" bf16 activations" if bf16 else ""),
             "us": round(sec * 1e6, 2), "tflops": round(flops / sec / 1e12, 2),
             "weight_tbs": round(cfg["k"] * cfg["n"] / 2 / sec / 1e12, 4)}
+        del ws
+    # W8A16 (E4M3 weights, one byte each): decode and prefill shapes, group 128
+    for name in ("decode", "prefill"):
+        cfg = synthetic.CONFIGS[name]
+        case = synthetic.fp8_case(cfg["m"], cfg["k"], cfg["n"], seed=19)
+        w = torch_ops.PackedWeight(case["qweight"], case["scales"], device="cuda", fp8=True)
+        copies = 12 if name == "decode" else 1
+        ws = [w] + [w.clone() for _ in range(copies - 1)]
+        a = torch_ops.to_device(case["a"], "cuda")
+        c = torch.empty((cfg["m"], cfg["n"]), dtype=torch.float16, device="cuda")
+        fp32 = cfg["fp32_reduce"]
+        bufs = torch_ops.GemmBuffers(w, cfg["m"], fp32)
+
+        def step(i, ws=ws, a=a, c=c, bufs=bufs, copies=copies, fp32=fp32):
+            torch_ops.gemm(a, ws[i % copies], c, fp32_reduce=fp32, buffers=bufs)
+        sec = timed_loop(torch, step, steps if name == "decode" else max(5, steps // 8), warmup)
+        out[f"{name}_fp8"] = {
+            "workload": f"{name} shape M={cfg['m']} K={cfg['k']} N={cfg['n']} E4M3 weights "
+                        "group_size 128",
+            "us": round(sec * 1e6, 2),
+            "tflops": round(2.0 * cfg["m"] * cfg["n"] * cfg["k"] / sec / 1e12, 2),
+            "weight_tbs": round(cfg["k"] * cfg["n"] / sec / 1e12, 4)}
         del ws
     moe = synthetic.moe_case()
     bank = torch_ops.ExpertBank(moe["experts"], device="cuda")

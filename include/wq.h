@@ -72,6 +72,12 @@ extern "C" {
  * fp16; codes and zero points are unchanged.  Products are accumulated in fp32 and rounded
  * once to bf16 (round to nearest even).  Scales are repacked bit for bit either way. */
 #define WQ_FLAG_BF16 (1u << 8)
+/* W8A16: B holds FP8 E4M3 weights (the "fn" variant: bias 7, no infinities, 0x7F/0xFF NaN)
+ * in the FP8 library layout (wq_repack_fp8), one byte per weight: the pages' E4M3 weight
+ * type (vllm_marlin.rs `ferrum_vllm_marlin_moe_fp8_f16`).  W[k][n] = e4m3(code) * s.
+ * As the pages require: group_size -1 or 128, no zero points; here also fp16 activations
+ * only, no act_order and no SwiGLU epilogue (WQ_ERR_FLAGS / WQ_ERR_SHAPE otherwise). */
+#define WQ_FLAG_FP8 (1u << 9)
 
 enum wq_stage {
   WQ_STAGE_ARGS = 1,
@@ -123,6 +129,18 @@ int wq_repack_b(const uint32_t* qweight, const int32_t* perm, void* b_out, int k
  */
 int wq_repack_scales(const void* scales, void* s_out, int k, int n, int group_size,
                      void* stream);
+
+/*
+ * E4M3 weights for WQ_FLAG_FP8: K-major words [k/4][n] uint32, byte i (bits 8i..8i+7) of
+ * word (r, col) holding row 4r + i of column col (vllm_marlin.rs
+ * `vllm_fp8_marlin_repack_raw_bits`; a row-major [n][k] checkpoint must be transposed and
+ * packed this way first) -> FP8 library layout, k*n bytes: for 16-column block nb,
+ * 128-row group g and half h (rows 64h..64h+63), lane l = c + 16*qd holds 16 bytes whose
+ * word d covers rows 128g + 32(2h + d/2) + 8qd + 4(d%2) .. +3 of column 16nb + c, at word
+ * (((nb * k/128 + g) * 2 + h) * 64 + l) * 4 + d.  A word permutation, nothing decoded.
+ *   words: device, 4-byte aligned; b_out: device, k*n bytes, 16-byte aligned, no overlap.
+ */
+int wq_repack_fp8(const uint32_t* words, void* b_out, int k, int n, void* stream);
 
 /*
  * Zero points uint32 [k/group_size][n/8] (actual codes 0..15, column 8j+i in bits 4i of
@@ -194,8 +212,9 @@ int wq_gemm(const wq_gemm_args* args);
 /*
  * Dequant export for bit-exact tests: reads library-layout B, scales and optional zero
  * points and writes w[k][n] = rne((q - z) * s) (fp16, or bf16 with WQ_FLAG_BF16; row-major,
- * rows in the stored order, i.e. sorted order for act_order weights).  flags: HAS_ZP and
- * BF16 are read, ACT_ORDER and IS_K_FULL accepted; any other bit fails with WQ_ERR_FLAGS.
+ * rows in the stored order, i.e. sorted order for act_order weights).  flags: HAS_ZP, BF16
+ * and FP8 are read (FP8: b in the FP8 layout, w = fp16_rne(e4m3 * s)), ACT_ORDER and
+ * IS_K_FULL accepted; any other bit fails with WQ_ERR_FLAGS.
  */
 int wq_dequant(const void* b, const void* b_scales, const void* zero_points, int k, int n,
                int group_size, uint32_t flags, void* w_out, void* stream);

@@ -99,7 +99,7 @@ def call_gemm(L, **over):
     (dict(zero_points=0x5000), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
     (dict(flags=wq.WQ_FLAG_HAS_ZP, zero_points=0x5008), status(STAGE_ARGS, wq.WQ_ERR_ALIGN)),
     (dict(flags=wq.WQ_FLAG_ATOMIC_ADD), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
-    (dict(flags=1 << 9), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
+    (dict(flags=1 << 10), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
     (dict(flags=wq.WQ_FLAG_ACT_ORDER), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
     (dict(perm=0x6000), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
     (dict(flags=wq.WQ_FLAG_ACT_ORDER, perm=0x6000), status(STAGE_ARGS, wq.WQ_ERR_NULL)),
@@ -146,11 +146,35 @@ def test_repack_and_dequant_validation(L):
                                                                           wq.WQ_ERR_NULL)
     assert L.wq_dequant(0x1000, 0x2000, None, 1024, 256, 128, wq.WQ_FLAG_HAS_ZP, 0x3000,
                         None) == status(STAGE_ARGS, wq.WQ_ERR_FLAGS)
-    # unknown flag bits (beyond HAS_ZP, ACT_ORDER, IS_K_FULL and BF16) are rejected
-    assert L.wq_dequant(0x1000, 0x2000, None, 1024, 256, 128, 1 << 9, 0x3000,
+    # unknown flag bits (beyond HAS_ZP, ACT_ORDER, IS_K_FULL, BF16 and FP8) are rejected
+    assert L.wq_dequant(0x1000, 0x2000, None, 1024, 256, 128, 1 << 10, 0x3000,
                         None) == status(STAGE_ARGS, wq.WQ_ERR_FLAGS)
     assert L.wq_dequant(0x1000, 0x2000, None, 1024, 256, 128, wq.WQ_FLAG_SWIGLU, 0x3000,
                         None) == status(STAGE_ARGS, wq.WQ_ERR_FLAGS)
+
+
+def test_fp8_validation_before_launch(L):
+    FP8 = wq.WQ_FLAG_FP8
+    # the pages' E4M3 rules: group_size -1 or 128, no zero points; and fp16 only, no
+    # act_order or SwiGLU epilogue here
+    assert call_gemm(L, flags=FP8, group_size=64) == status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)
+    assert call_gemm(L, flags=FP8, group_size=256) == status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)
+    assert call_gemm(L, flags=FP8 | wq.WQ_FLAG_HAS_ZP, zero_points=0x5000) == status(
+        STAGE_ARGS, wq.WQ_ERR_FLAGS)
+    assert call_gemm(L, flags=FP8 | wq.WQ_FLAG_BF16) == status(STAGE_ARGS, wq.WQ_ERR_FLAGS)
+    assert call_gemm(L, flags=FP8 | wq.WQ_FLAG_SWIGLU) == status(STAGE_ARGS, wq.WQ_ERR_FLAGS)
+    assert call_gemm(L, flags=FP8 | wq.WQ_FLAG_ACT_ORDER, perm=0x6000,
+                     a_tmp=0x6100) == status(STAGE_ARGS, wq.WQ_ERR_FLAGS)
+    assert L.wq_dequant(0x1000, 0x2000, None, 1024, 256, 64, FP8, 0x3000,
+                        None) == status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)
+    assert L.wq_dequant(0x1000, 0x2000, 0x4000, 1024, 256, 128, FP8 | wq.WQ_FLAG_HAS_ZP,
+                        0x3000, None) == status(STAGE_ARGS, wq.WQ_ERR_FLAGS)
+    assert L.wq_repack_fp8(None, 0x2000, 1024, 256, None) == status(STAGE_ARGS,
+                                                                   wq.WQ_ERR_NULL)
+    assert L.wq_repack_fp8(0x1000, 0x2008, 1024, 256, None) == status(STAGE_ARGS,
+                                                                     wq.WQ_ERR_ALIGN)
+    assert L.wq_repack_fp8(0x1000, 0x2000, 1000, 256, None) == status(STAGE_SHAPE,
+                                                                     wq.WQ_ERR_SHAPE)
 
 
 def test_flag_values_match_the_header():
@@ -289,7 +313,14 @@ def grouped_args(**over):
     # the SwiGLU activation takes no routing weight
     (dict(topk_weights=0x8000, flags=wq.WQ_FLAG_MUL_TOPK_WEIGHTS | wq.WQ_FLAG_SWIGLU),
      status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
-    (dict(flags=1 << 9), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
+    (dict(flags=1 << 10), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
+    # E4M3 banks: one byte per weight, so a 4-bit bank stride is too short; the pages'
+    # group sizes (-1, 128) and no zero points
+    (dict(flags=wq.WQ_FLAG_FP8), status(STAGE_ARGS, wq.WQ_ERR_SHAPE)),
+    (dict(flags=wq.WQ_FLAG_FP8, group_size=64, b_stride_bytes=1024 * 256),
+     status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)),
+    (dict(flags=wq.WQ_FLAG_FP8 | wq.WQ_FLAG_HAS_ZP, zp_bank=0x9000, zp_stride_bytes=4096,
+          b_stride_bytes=1024 * 256), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
 ])
 def test_grouped_rejects_bad_arguments_before_launch(L, over, expect):
     assert L.wq_grouped_gemm(ctypes.byref(grouped_args(**over))) == expect

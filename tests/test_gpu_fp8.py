@@ -1,0 +1,154 @@
+"""Parity of the W8A16 path (WQ_FLAG_FP8: E4M3 weights) with the CPU oracle, on an MI355X.
+
+The repack and the dequant export must match bit for bit; the export of every E4M3 code
+with unit scales pins the hardware conversion (OCP E4M3 "fn": bias 7, 0x7F / 0xFF NaN).
+GEMM outputs are fp16 and must satisfy |C - ref| <= 2^-11 * |ref| + 2e-3 * rms(ref) + 1e-3
+per element (2^-11: the output's own rounding, as E4M3 magnitudes span 2^-9 .. 448 and
+leave large elements far above the rms) and ||C - ref||_F / ||ref||_F <= 1e-3.
+"""
+
+import numpy as np
+import pytest
+
+import synthetic
+from oracle import layout
+from oracle import reference as ref
+
+torch = pytest.importorskip("torch")
+wq = pytest.importorskip("weight_only_quantized_gemm_amd")
+from weight_only_quantized_gemm_amd import torch_ops  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+FP8_TOL = dict(rel_elem=2.0 ** -11)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def say(*args):
+    print(*args, flush=True)
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def assert_parity(c, want, label):
+    res = ref.check(c, want, **FP8_TOL)
+    say(f"{label}: max_err={res['max_err']:.3e} tol={res['tol']:.3e} "
+        f"rel_frob={res['rel_frob']:.3e} nonfinite={res['nonfinite']}")
+    assert res["ok"], (label, res)
+
+
+def words_of(codes: np.ndarray) -> np.ndarray:
+    """uint8 codes [K][N] -> K-major words [K/4][N], byte i = row 4r + i."""
+    c = codes.astype(np.uint32).reshape(codes.shape[0] // 4, 4, codes.shape[1])
+    return c[:, 0] | (c[:, 1] << 8) | (c[:, 2] << 16) | (c[:, 3] << 24)
+
+
+def test_fp8_repack_matches_layout_bitwise(dev):
+    k, n = 384, 256
+    say(f"fp8 repack k={k} n={n}")
+    codes = np.random.default_rng(6000).integers(0, 256, size=(k, n)).astype(np.uint8)
+    out = torch.empty(k * n // 4, dtype=torch.int32, device=dev)
+    wq.wq_repack_fp8(torch_ops.to_device(words_of(codes), dev), out, k, n)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out).view(np.uint32), layout.repack_fp8_loops(codes))
+
+
+@pytest.mark.parametrize("unit_scales,gs", [(True, 128), (False, 128), (False, -1)])
+def test_fp8_dequant_of_every_code(dev, unit_scales, gs):
+    """Every byte value appears (codes (row + 3 col) mod 256); with unit scales the export
+    is the conversion itself, exact in fp16."""
+    k, n = 512, 256
+    say(f"fp8 dequant of every code unit_scales={unit_scales} group_size={gs}")
+    rows, cols = np.meshgrid(np.arange(k), np.arange(n), indexing="ij")
+    codes = ((rows + 3 * cols) % 256).astype(np.uint8)
+    groups = 1 if gs == -1 else k // 128
+    s = (np.ones((groups, n), np.float16) if unit_scales
+         else synthetic.scales(6001, groups, n))
+    w = torch_ops.PackedWeight(words_of(codes), s, device=dev, group_size=gs, fp8=True)
+    out = torch.empty((k, n), dtype=torch.float16, device=dev)
+    wq.wq_dequant(w.b, w.s, None, out, k=k, n=n, flags=wq.WQ_FLAG_FP8, group_size=gs)
+    torch.cuda.synchronize()
+    want = ref.dequantize_fp16(ref.w8a16_weights(words_of(codes), s, group_size=gs))
+    got = host(out)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok].view(np.uint16), want[ok].view(np.uint16))
+
+
+FP8_SHAPES = [
+    # m, k, n, group_size, fp32_reduce, split_k
+    (1, 4096, 512, 128, False, 0),
+    (1, 2048, 256, -1, True, 3),
+    (5, 1024, 512, 128, True, 0),
+    (16, 2048, 256, -1, False, 0),
+    (3, 8192, 256, 128, False, 0),
+    (17, 1024, 256, 128, False, 0),
+    (300, 1024, 512, 128, False, 0),
+    (257, 384, 256, -1, False, 0),
+    (513, 2048, 768, 128, False, 0),
+]
+
+
+@pytest.mark.parametrize("m,k,n,gs,fp32,split", FP8_SHAPES)
+def test_fp8_gemm_matches_oracle(dev, m, k, n, gs, fp32, split):
+    label = f"fp8 gemm m={m} k={k} n={n} group_size={gs} fp32={fp32} split={split}"
+    say(label)
+    case = synthetic.fp8_case(m, k, n, group_size=gs, seed=6100 + m + k)
+    w = torch_ops.PackedWeight(case["qweight"], case["scales"], device=dev, group_size=gs,
+                               fp8=True)
+    c = host(torch_ops.gemm(torch_ops.to_device(case["a"], dev), w, fp32_reduce=fp32,
+                            split_k=split))
+    torch.cuda.synchronize()
+    want = ref.w8a16_gemm(case["a"], case["qweight"], case["scales"], group_size=gs)
+    assert_parity(c, want, label)
+
+
+def test_fp8_decode_config_in_full(dev):
+    m, k, n = 1, 4096, 14336
+    say("fp8 decode shape M=1 K=4096 N=14336 g128 (full)")
+    case = synthetic.fp8_case(m, k, n, seed=6200)
+    w = torch_ops.PackedWeight(case["qweight"], case["scales"], device=dev, fp8=True)
+    c = host(torch_ops.gemm(torch_ops.to_device(case["a"], dev), w, fp32_reduce=True))
+    torch.cuda.synchronize()
+    assert_parity(c, ref.w8a16_gemm(case["a"], case["qweight"], case["scales"]), "fp8 decode")
+
+
+def test_fp8_prefill_shape_on_sampled_columns(dev):
+    m, k, n = 2048, 4096, 14336
+    say("fp8 prefill shape M=2048 K=4096 N=14336 g128 (sampled columns)")
+    case = synthetic.fp8_case(m, k, n, seed=6300)
+    w = torch_ops.PackedWeight(case["qweight"], case["scales"], device=dev, fp8=True)
+    c = host(torch_ops.gemm(torch_ops.to_device(case["a"], dev), w))
+    torch.cuda.synchronize()
+    cols = np.random.default_rng(6301).choice(n, 96, replace=False)
+    want = ref.w8a16_gemm(case["a"], case["qweight"], case["scales"], columns=cols)
+    assert_parity(c[:, cols], want, "fp8 prefill sampled")
+
+
+@pytest.mark.parametrize("tokens,experts,k,n,weighted", [(40, 4, 256, 256, False),
+                                                         (300, 3, 512, 512, True),
+                                                         (700, 2, 256, 256, False)])
+def test_fp8_grouped_matches_oracle(dev, tokens, experts, k, n, weighted):
+    label = f"fp8 grouped tokens={tokens} experts={experts} k={k} n={n} weighted={weighted}"
+    say(label)
+    moe = synthetic.moe_case(tokens, experts, k, n, seed=6400 + tokens)
+    ex = [dict(qweight=synthetic.fp8_words(6500 + e, k, n), scales=x["scales"])
+          for e, x in enumerate(moe["experts"])]
+    bank = torch_ops.ExpertBank(ex, device=dev, fp8=True)
+    csr = wq.wq_csr_from_routes(moe["routes"], moe["n_tokens"], moe["top_k"], moe["n_expert"])
+    wts = synthetic.routing_weights(6600 + tokens, tokens, 2) if weighted else None
+    y = host(torch_ops.grouped_gemm(torch_ops.to_device(moe["a"], dev), bank, csr,
+                                    topk_weights=None if wts is None
+                                    else torch_ops.to_device(wts, dev)))
+    torch.cuda.synchronize()
+    ocsr = ref.csr_from_token_routes(moe["n_expert"], moe["n_tokens"], moe["top_k"],
+                                     moe["routes"])
+    want = ref.grouped_w4a16_gemm(moe["a"], ex, ocsr, topk_weights=wts, fp8=True)
+    assert_parity(y, want, label)

@@ -25,6 +25,7 @@ WQ_FLAG_FP32_REDUCE = 1 << 5
 WQ_FLAG_MUL_TOPK_WEIGHTS = 1 << 6
 WQ_FLAG_SWIGLU = 1 << 7
 WQ_FLAG_BF16 = 1 << 8
+WQ_FLAG_FP8 = 1 << 9
 
 WQ_STAGE_ARGS, WQ_STAGE_SHAPE, WQ_STAGE_DEVICE = 1, 2, 3
 WQ_STAGE_LAUNCH_CONFIG, WQ_STAGE_FUNC_ATTR, WQ_STAGE_LAUNCH = 4, 5, 6
@@ -35,7 +36,7 @@ EXPORTED = (
     "wq_abi_version", "wq_status_str", "wq_repack_b", "wq_repack_scales", "wq_repack_zeros",
     "wq_act_order_perm", "wq_gemm_workspace_bytes", "wq_gemm", "wq_dequant",
     "wq_csr_from_routes", "wq_grouped_workspace_bytes", "wq_grouped_gemm",
-    "wq_stream_read_sink_words", "wq_stream_read", "wq_interleave_gate_up",
+    "wq_stream_read_sink_words", "wq_stream_read", "wq_interleave_gate_up", "wq_repack_fp8",
 )
 
 
@@ -96,6 +97,7 @@ def lib() -> ctypes.CDLL:
             "wq_abi_version": (u32, []),
             "wq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
             "wq_repack_b": (ctypes.c_int, [vp, vp, vp, i32, i32, vp]),
+            "wq_repack_fp8": (ctypes.c_int, [vp, vp, i32, i32, vp]),
             "wq_repack_scales": (ctypes.c_int, [vp, vp, i32, i32, i32, vp]),
             "wq_repack_zeros": (ctypes.c_int, [vp, vp, i32, i32, i32, vp]),
             "wq_act_order_perm": (ctypes.c_int, [vp, i32, i32, vp, vp]),
@@ -156,6 +158,11 @@ def wq_status_str(status: int) -> str:
 def wq_repack_b(qweight, b_out, k: int, n: int, perm=None, stream=None) -> None:
     _check(lib().wq_repack_b(_ptr(qweight), _ptr(perm), _ptr(b_out), k, n,
                              _stream(stream, b_out)))
+
+
+def wq_repack_fp8(words, b_out, k: int, n: int, stream=None) -> None:
+    """E4M3 words [k/4][n] (K-major, four bytes per word) -> the FP8 library layout."""
+    _check(lib().wq_repack_fp8(_ptr(words), _ptr(b_out), k, n, _stream(stream, b_out)))
 
 
 def wq_repack_scales(scales, s_out, k: int, n: int, group_size: int = 128, stream=None) -> None:

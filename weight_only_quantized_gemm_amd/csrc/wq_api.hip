@@ -42,6 +42,16 @@ bool chunk_group_size(int k, int group_size) {
 // Scale units per 128 rows of K (units of gcd(group_size, 128) rows: 1, 2, 4 or 8).
 int subgroups(int k, int group_size) { return kGroupSize / wq::scale_unit_rows(k, group_size); }
 
+// WQ_FLAG_FP8 (E4M3 weights): group_size -1 or 128, fp16, no zero points, act_order or
+// SwiGLU epilogue.
+int check_fp8(uint32_t flags, int group_size) {
+  if (!(flags & WQ_FLAG_FP8)) return 0;
+  if (group_size != -1 && group_size != kGroupSize) return fail(WQ_STAGE_SHAPE, WQ_ERR_SHAPE);
+  if (flags & (WQ_FLAG_HAS_ZP | WQ_FLAG_ACT_ORDER | WQ_FLAG_BF16 | WQ_FLAG_SWIGLU))
+    return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
+  return 0;
+}
+
 // k % 128 == 0, n % 256 == 0, a supported group_size, and byte extents that fit.
 int check_kn(int k, int n, int group_size) {
   if (k <= 0 || n <= 0 || k % kGroupSize != 0 || n % 256 != 0)
@@ -187,6 +197,16 @@ int wq_repack_b(const uint32_t* qweight, const int32_t* perm, void* b_out, int k
   return e == hipSuccess ? 0 : hip_fail(e);
 }
 
+int wq_repack_fp8(const uint32_t* words, void* b_out, int k, int n, void* stream) {
+  int st = check_kn(k, n, kGroupSize);
+  if (st) return st;
+  if ((st = check_ptr(words, 4))) return st;
+  if ((st = check_ptr(b_out, 16))) return st;
+  const hipError_t e =
+      wq::launch_repack_fp8(words, static_cast<uint32_t*>(b_out), k, n, as_stream(stream));
+  return e == hipSuccess ? 0 : hip_fail(e);
+}
+
 int wq_repack_scales(const void* scales, void* s_out, int k, int n, int group_size,
                      void* stream) {
   int st = check_kn(k, n, group_size);
@@ -251,11 +271,12 @@ int wq_gemm(const wq_gemm_args* args) {
   const wq_gemm_args& p = *args;
   const uint32_t known = WQ_FLAG_ACT_ORDER | WQ_FLAG_IS_K_FULL | WQ_FLAG_HAS_ZP |
                          WQ_FLAG_ATOMIC_ADD | WQ_FLAG_FP32_REDUCE | WQ_FLAG_SWIGLU |
-                         WQ_FLAG_BF16;
+                         WQ_FLAG_BF16 | WQ_FLAG_FP8;
   if ((p.flags & ~known) || (p.flags & WQ_FLAG_ATOMIC_ADD))
     return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
   int st = check_kn(p.k, p.n, p.group_size);
   if (st) return st;
+  if ((st = check_fp8(p.flags, p.group_size))) return st;
   if (p.m <= 0 || p.lda < p.k || p.lda % 8 != 0) return fail(WQ_STAGE_SHAPE, WQ_ERR_SHAPE);
   if ((long long)p.m * p.lda > (long long)std::numeric_limits<int64_t>::max() / 4 ||
       (long long)(p.m + 255) / 256 > 65535)
@@ -276,6 +297,7 @@ int wq_gemm(const wq_gemm_args* args) {
   if (p.split_k > 1 && !(p.flags & WQ_FLAG_FP32_REDUCE)) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
   const bool swiglu = (p.flags & WQ_FLAG_SWIGLU) != 0;
   const bool bf16 = (p.flags & WQ_FLAG_BF16) != 0;
+  const bool fp8 = (p.flags & WQ_FLAG_FP8) != 0;
 
   // Plan, and check the workspace the plan needs, before anything is enqueued.
   const int gpc = subgroups(p.k, p.group_size);
@@ -309,11 +331,12 @@ int wq_gemm(const wq_gemm_args* args) {
 
   if (small) {
     const hipError_t e =
-        wq::launch_gemm_small(a, lda, p.m, b, s, z, c, p.n, p.k, plan, partials, bf16, stream);
+        wq::launch_gemm_small(a, lda, p.m, b, s, z, c, p.n, p.k, plan, partials, bf16, fp8,
+                              stream);
     return e == hipSuccess ? 0 : hip_fail(e);
   }
   const hipError_t e =
-      wq::launch_gemm_tile(a, lda, p.m, b, s, z, c, p.n, p.k, swiglu, gpc, bf16, stream);
+      wq::launch_gemm_tile(a, lda, p.m, b, s, z, c, p.n, p.k, swiglu, gpc, bf16, fp8, stream);
   return e == hipSuccess ? 0 : hip_fail(e);
 }
 
@@ -323,8 +346,17 @@ int wq_dequant(const void* b, const void* b_scales, const void* zero_points, int
   if (st) return st;
   if ((st = check_ptr(b, 16)) || (st = check_ptr(b_scales, 16)) || (st = check_ptr(w_out, 16)))
     return st;
-  if (flags & ~(uint32_t)(WQ_FLAG_HAS_ZP | WQ_FLAG_ACT_ORDER | WQ_FLAG_IS_K_FULL | WQ_FLAG_BF16))
+  if (flags & ~(uint32_t)(WQ_FLAG_HAS_ZP | WQ_FLAG_ACT_ORDER | WQ_FLAG_IS_K_FULL | WQ_FLAG_BF16 |
+                          WQ_FLAG_FP8))
     return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
+  if ((st = check_fp8(flags & ~(uint32_t)WQ_FLAG_ACT_ORDER, group_size))) return st;
+  if (flags & WQ_FLAG_FP8) {
+    if (zero_points != nullptr) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
+    const hipError_t e = wq::launch_dequant_fp8(
+        static_cast<const uint32_t*>(b), static_cast<const uint16_t*>(b_scales), k, n,
+        static_cast<uint16_t*>(w_out), as_stream(stream));
+    return e == hipSuccess ? 0 : hip_fail(e);
+  }
   const bool has_zp = (flags & WQ_FLAG_HAS_ZP) != 0;
   if (has_zp != (zero_points != nullptr)) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
   if (has_zp && (st = check_ptr(zero_points, 16))) return st;
@@ -386,7 +418,7 @@ int wq_grouped_gemm(const wq_grouped_args* args) {
     return fail(WQ_STAGE_ARGS, WQ_ERR_ABI);
   const wq_grouped_args& p = *args;
   if (p.flags & ~(uint32_t)(WQ_FLAG_HAS_ZP | WQ_FLAG_IS_K_FULL | WQ_FLAG_MUL_TOPK_WEIGHTS |
-                            WQ_FLAG_SWIGLU | WQ_FLAG_BF16))
+                            WQ_FLAG_SWIGLU | WQ_FLAG_BF16 | WQ_FLAG_FP8))
     return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
   // The routing weight scales an expert's output, i.e. the down projection; the SwiGLU
   // activation of the gate/up projection takes none.
@@ -394,6 +426,8 @@ int wq_grouped_gemm(const wq_grouped_args* args) {
     return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
   int st = check_kn(p.k, p.n, p.group_size);
   if (st) return st;
+  if ((st = check_fp8(p.flags, p.group_size))) return st;
+  const bool fp8 = (p.flags & WQ_FLAG_FP8) != 0;
   if (p.n_expert <= 0 || p.n_active <= 0 || p.n_active > p.n_expert || p.n_pairs <= 0 ||
       p.n_tokens <= 0 || p.n_active > p.n_pairs)
     return fail(WQ_STAGE_ARGS, WQ_ERR_CSR);
@@ -410,7 +444,7 @@ int wq_grouped_gemm(const wq_grouped_args* args) {
   if (mul_w != (p.topk_weights != nullptr)) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
   if (mul_w && !aligned(p.topk_weights, 4)) return fail(WQ_STAGE_ARGS, WQ_ERR_ALIGN);
   const size_t groups = (size_t)(p.k / wq::scale_unit_rows(p.k, p.group_size));  // scale rows
-  const size_t b_bytes = (size_t)p.k * p.n / 2;
+  const size_t b_bytes = fp8 ? (size_t)p.k * p.n : (size_t)p.k * p.n / 2;
   const size_t s_bytes = groups * p.n * 2;
   const size_t z_bytes = groups * p.n / 2;
   if (p.b_stride_bytes < b_bytes || p.b_stride_bytes % 16 || p.s_stride_bytes < s_bytes ||
@@ -444,6 +478,7 @@ int wq_grouped_gemm(const wq_grouped_args* args) {
   g.n = p.n;
   g.swiglu = (p.flags & WQ_FLAG_SWIGLU) != 0;
   g.bf16 = (p.flags & WQ_FLAG_BF16) != 0;
+  g.fp8 = fp8;
   g.gpc = subgroups(p.k, p.group_size);
   const hipError_t e = wq::launch_grouped_tile(g, as_stream(p.stream));
   return e == hipSuccess ? 0 : hip_fail(e);

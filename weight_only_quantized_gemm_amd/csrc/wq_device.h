@@ -126,6 +126,18 @@ __device__ __forceinline__ bf16x8 dequant8_bf(uint32_t w, ZeroOffsetsBf zo, Magi
   return out;
 }
 
+// ---- FP8 (E4M3) weights ------------------------------------------------------------------
+// Two layout words (rows 0-3 and 4-7 of a lane's 8-row slice, one byte per row) -> the
+// eight weights as fp16, in row order.  gfx950 converts two E4M3 bytes to two fp16 values
+// per instruction (scale 1.0); every E4M3 value is exact in fp16.
+__device__ __forceinline__ f16x8 dequant8_fp8(uint32_t lo, uint32_t hi) {
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+  return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 // Biased bf16 dequant for kernels with MFMA to spare: one layout word -> the eight values
 // 128 + q of its rows (row order as above), each nibble OR-ed into the mantissa of 128.0
 // (bf16 0x4300, whose ulp is 1).  A product with these operands is corrected afterwards

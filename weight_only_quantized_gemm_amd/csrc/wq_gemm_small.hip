@@ -84,9 +84,13 @@ bool small_plan_fits(int m, int k, const SmallPlan& plan) {
 
 hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* b,
                              const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
-                             const SmallPlan& plan, float* partials, bool bf16,
+                             const SmallPlan& plan, float* partials, bool bf16, bool fp8,
                              hipStream_t stream) {
   if (!small_plan_fits(m, k, plan)) return hipErrorInvalidConfiguration;
+  if (fp8) {
+    if (bf16 || z != nullptr) return hipErrorInvalidValue;
+    return launch_small_fp8(a, lda, m, b, s, c, n, k, plan, partials, stream);
+  }
   if (bf16) {
     switch (plan.gpc) {
       case 2: return launch_small_bf16_g2(a, lda, m, b, s, z, c, n, k, plan, partials, stream);

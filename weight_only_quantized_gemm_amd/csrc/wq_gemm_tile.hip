@@ -11,7 +11,7 @@ hipError_t launch_tile_f16(const TileArgs& p, bool grouped, bool swiglu, bool zp
 
 hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b,
                             const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
-                            bool swiglu, int gpc, bool bf16, hipStream_t stream) {
+                            bool swiglu, int gpc, bool bf16, bool fp8, hipStream_t stream) {
   TileArgs p{};
   p.a = a;
   p.lda = lda;
@@ -24,6 +24,10 @@ hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b
   p.k = k;
   p.ldc = swiglu ? n / 2 : n;
   p.tiles = (n / TN) * ((m + TM - 1) / TM);
+  if (fp8) {
+    if (bf16 || swiglu || z != nullptr || gpc != 1) return hipErrorInvalidValue;
+    return launch_tile_fp8(p, false, stream);
+  }
   return bf16 ? launch_tile_bf16(p, false, swiglu, z != nullptr, gpc, stream)
               : launch_tile_f16(p, false, swiglu, z != nullptr, gpc, stream);
 }
@@ -62,6 +66,10 @@ hipError_t launch_grouped_tile(const GroupedProblem& g, hipStream_t stream) {
   if (tiles > 0x7fffffffL) return hipErrorInvalidConfiguration;
   p.tiles = (int)tiles;
   p.ldc = g.swiglu ? g.n / 2 : g.n;
+  if (g.fp8) {
+    if (g.bf16 || g.swiglu || g.z_bank != nullptr || g.gpc != 1) return hipErrorInvalidValue;
+    return launch_tile_fp8(p, true, stream);
+  }
   return g.bf16 ? launch_tile_bf16(p, true, g.swiglu, g.z_bank != nullptr, g.gpc, stream)
                 : launch_tile_f16(p, true, g.swiglu, g.z_bank != nullptr, g.gpc, stream);
 }

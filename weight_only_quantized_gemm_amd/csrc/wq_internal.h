@@ -21,6 +21,12 @@ hipError_t launch_repack_zeros(const uint32_t* z, uint32_t* out, int k, int n, i
 // Gate/up column pairing for the SwiGLU epilogue (bits_per_column 32, 16 or 4).
 hipError_t launch_interleave_gate_up(const void* gate, const void* up, void* out, int rows,
                                      int cols, int bits_per_column, hipStream_t stream);
+// E4M3 weights: K-major words [k/4][n] -> the FP8 layout (k % 128 == 0, n % 16 == 0), and
+// the dequant export of that layout with fp16 scales (one unit per 128 rows).
+hipError_t launch_repack_fp8(const uint32_t* words, uint32_t* out, int k, int n,
+                             hipStream_t stream);
+hipError_t launch_dequant_fp8(const uint32_t* b, const uint16_t* s, int k, int n, uint16_t* w,
+                              hipStream_t stream);
 // bf16: s and w hold bf16 values (else fp16).
 hipError_t launch_dequant(const uint32_t* b, const uint16_t* s, const uint32_t* z, int k, int n,
                           int unit, bool bf16, uint16_t* w, hipStream_t stream);
@@ -39,11 +45,16 @@ struct SmallPlan {
   int gpc;         // scale units per 128-row chunk: 1, 2, 4 or 8 (units of 128/gpc rows)
 };
 bool small_plan_fits(int m, int k, const SmallPlan& plan);
-// bf16: A, s and c hold bf16 values (else fp16).
+// bf16: A, s and c hold bf16 values (else fp16).  fp8: b holds E4M3 weights in the FP8
+// layout (fp16 only, no zero points, 128-row scale units).
 hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* b,
                              const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
-                             const SmallPlan& plan, float* partials, bool bf16,
+                             const SmallPlan& plan, float* partials, bool bf16, bool fp8,
                              hipStream_t stream);
+// The E4M3 instances (wq_gemm_small_fp8.hip).
+hipError_t launch_small_fp8(const uint16_t* a, int lda, int m, const uint32_t* b,
+                            const uint16_t* s, uint16_t* c, int n, int k, const SmallPlan& plan,
+                            float* partials, hipStream_t stream);
 // The instances of each scale-unit count and activation type (wq_gemm_small.hip, _g2.hip,
 // _g4.hip, _g8.hip; wq_gemm_small_bf16.hip, _bf16_g2.hip, _bf16_g4.hip, _bf16_g8.hip).
 #define WQ_SMALL_GPC_DECL(NAME)                                                             \
@@ -69,9 +80,10 @@ constexpr int kTileM = 256;
 constexpr int kTileN = 256;
 // swiglu: B pairs gate/up 16-column blocks and c is the [m][n/2] activation.  gpc: scale
 // units per 128 rows of K (1, 2, 4 or 8).  bf16: A, s and c hold bf16 values (else fp16).
+// fp8: b holds E4M3 weights in the FP8 layout (fp16, gpc 1, no zero points, no swiglu).
 hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b,
                             const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
-                            bool swiglu, int gpc, bool bf16, hipStream_t stream);
+                            bool swiglu, int gpc, bool bf16, bool fp8, hipStream_t stream);
 
 struct GroupedProblem {
   const uint16_t* a;
@@ -91,6 +103,7 @@ struct GroupedProblem {
   bool swiglu;            // SwiGLU epilogue: y is [n_pairs][n/2]
   int gpc;                // scale units per 128 rows of K (1, 2, 4 or 8)
   bool bf16;              // a, scales and y hold bf16 values (else fp16)
+  bool fp8;               // the banks hold E4M3 weights in the FP8 layout
 };
 hipError_t launch_grouped_tile(const GroupedProblem& p, hipStream_t stream);
 

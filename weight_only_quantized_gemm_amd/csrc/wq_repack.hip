@@ -88,6 +88,57 @@ __global__ __launch_bounds__(256) void repack_zeros_kernel(const uint32_t* __res
   }
 }
 
+// E4M3 weights: words [k/4][n] (byte i of word (r, col) is row 4r + i) -> the FP8 layout.
+// Word d of lane l = c + 16*qd in (block nb, group g, half h) covers rows
+// 128g + 32(2h + d/2) + 8qd + 4(d%2) .. +3 of column 16nb + c: one input word, moved whole.
+__global__ __launch_bounds__(256) void repack_fp8_kernel(const uint32_t* __restrict__ words,
+                                                         uint32_t* __restrict__ out, int k,
+                                                         int n) {
+  const long total = (long)k * n / 4;
+  const int groups = k / kGroup;
+  for (long o = (long)blockIdx.x * blockDim.x + threadIdx.x; o < total;
+       o += (long)gridDim.x * blockDim.x) {
+    const int d = (int)(o & 3);
+    const int lane = (int)((o >> 2) & 63);
+    const int h = (int)((o >> 8) & 1);
+    const long rest = o >> 9;
+    const int g = (int)(rest % groups);
+    const long nb = rest / groups;
+    const int col = (int)(nb * 16 + (lane & 15));
+    const int row0 = g * kGroup + 32 * (2 * h + (d >> 1)) + 8 * (lane >> 4) + 4 * (d & 1);
+    out[o] = words[(long)(row0 >> 2) * n + col];
+  }
+}
+
+// E4M3 dequant export: w[row][col] = fp16_rne(e4m3 * s), the product exact in fp32.
+__global__ __launch_bounds__(256) void dequant_fp8_kernel(const u32x4* __restrict__ b,
+                                                          const uint16_t* __restrict__ s,
+                                                          int k, int n,
+                                                          uint16_t* __restrict__ w) {
+  const long total = (long)k * n / 16;  // one u32x4 (16 weights) per item
+  const int groups = k / kGroup;
+  for (long o = (long)blockIdx.x * blockDim.x + threadIdx.x; o < total;
+       o += (long)gridDim.x * blockDim.x) {
+    const int lane = (int)(o & 63);
+    const int h = (int)((o >> 6) & 1);
+    const long rest = o >> 7;
+    const int g = (int)(rest % groups);
+    const long nb = rest / groups;
+    const int c = lane & 15;
+    const long col = nb * 16 + c;
+    const float scale = Act<false>::value(s[(nb * groups + g) * 16 + c]);
+    const u32x4 v = b[o];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const f16x8 x = dequant8_fp8(v[2 * jj], v[2 * jj + 1]);
+      const int row0 = g * kGroup + 32 * (2 * h + jj) + 8 * (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        w[(long)(row0 + i) * n + col] = Act<false>::round((float)x[i] * scale);
+    }
+  }
+}
+
 // w[row][col] = rne((q - z) * s) in the scale's type (fp16, or bf16): the product is exact
 // in fp32 (a 5-bit integer times a 16-bit float), so the one conversion is the only rounding.
 template <bool BF16>
@@ -240,6 +291,20 @@ hipError_t launch_repack_b(const uint32_t* qweight, const int32_t* perm, uint32_
                            int n, hipStream_t stream) {
   hipLaunchKernelGGL(repack_b_kernel, dim3(grid_for((long)k * n / 8)), dim3(256), 0, stream,
                      qweight, perm, out, k, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_repack_fp8(const uint32_t* words, uint32_t* out, int k, int n,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL(repack_fp8_kernel, dim3(grid_for((long)k * n / 4)), dim3(256), 0, stream,
+                     words, out, k, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_fp8(const uint32_t* b, const uint16_t* s, int k, int n, uint16_t* w,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(dequant_fp8_kernel, dim3(grid_for((long)k * n / 16)), dim3(256), 0, stream,
+                     reinterpret_cast<const u32x4*>(b), s, k, n, w);
   return hipGetLastError();
 }
 

@@ -18,7 +18,9 @@
 // each step runs twice, once with the other half's weight lanes set to zero.
 //
 // BF16 selects bf16 activations, scales and outputs (bf16 MFMAs and dequant); the
-// arithmetic is otherwise the same.
+// arithmetic is otherwise the same.  W8 selects E4M3 weights (fp16 activations, one scale
+// unit per 128 rows, no zero points): a lane's group is then two 16-byte vectors (rows
+// 0-63 and 64-127 of the group), converted to fp16 two bytes per instruction.
 //
 // This header holds the kernel template and its launch chain; each translation unit that
 // includes it instantiates one GPC and activation type, so that the instances compile in
@@ -62,12 +64,14 @@ constexpr long small_static_lds(int waves, bool pair, int gpc) {
 // (2t, 2t+1, as wq_interleave_gate_up pairs them); its first half of waves streams the gate
 // block, the second half the up block, both over the same K range and staged activations,
 // and the reduction writes fp16(silu(g) * u) to column 16t + c of the [m][n/2] activation.
-template <bool ZP, int WAVES, int GW, int STAGE, bool PAIR, int GPC, bool BF16>
+template <bool ZP, int WAVES, int GW, int STAGE, bool PAIR, int GPC, bool BF16, bool W8>
 __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     const f16* __restrict__ a, int lda, int m, const u32x4* __restrict__ b,
     const uint16_t* __restrict__ s, const u32x2* __restrict__ z, uint16_t* __restrict__ c,
     int n, int groups, int splits, float* __restrict__ partials) {
   using A = Act<BF16>;
+  static_assert(!W8 || (!ZP && !PAIR && !BF16 && GPC == 1), "E4M3: fp16, no zero points");
+  constexpr int NV = W8 ? 2 : 1;  // 16-byte weight vectors per lane and group
   constexpr int T = WAVES * 64;
   constexpr int NB = PAIR ? 2 : 1;            // column blocks of the work-group
   constexpr int KW = WAVES / NB;              // waves splitting K for one block
@@ -145,11 +149,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   }
 
   // 3. The wave's weight chunks, all in flight before any arithmetic.
-  u32x4 bw[GW];
+  u32x4 bw[GW][NV];
 #pragma unroll
   for (int i = 0; i < GW; ++i) {
     const int g = g0 + (i < gw ? i : gw - 1);
-    bw[i] = __builtin_nontemporal_load(&b[((long)nb * groups + g) * 64 + lane]);
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+      bw[i][v] = __builtin_nontemporal_load(&b[(((long)nb * groups + g) * NV + v) * 64 + lane]);
   }
 
   // 4. Stage into LDS (waits for the activations and scales only), then sync.
@@ -208,7 +214,16 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     // With eight groups per wave, pin the prefetch ahead of this group's work (measured
     // faster for the decode shape, slower for shallower pipelines).
     if constexpr (GW >= 8) __builtin_amdgcn_sched_barrier(0);
-    if constexpr (BF16) {
+    if constexpr (W8) {
+      // 32-row step j: vector j / 2, words 2(j % 2) and 2(j % 2) + 1 (rows 0-3 and 4-7).
+      f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        p = mfma16x16x32(ac[j], dequant8_fp8(bw[i][j >> 1][2 * (j & 1)],
+                                             bw[i][j >> 1][2 * (j & 1) + 1]), p);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sc[i][0], p[e], acc[e]);
+    } else if constexpr (BF16) {
       // bf16 has no packed add, and the exact dequant costs 21 VALU per word, which this
       // weight-stream-bound kernel cannot hide.  The weights enter the MFMA biased, as
       // 128 + q (7 VALU per word), and the same activations meet an all-ones operand: r is
@@ -226,7 +241,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
           for (int jj = 0; jj < JQ; ++jj) {
             const int j = t * JQ + jj;
-            p = A::mfma16(ac[j], dequant8_bf_biased(bw[i][j], mr), p);
+            p = A::mfma16(ac[j], dequant8_bf_biased(bw[i][0][j], mr), p);
             r = A::mfma16(ac[j], ones, r);
           }
 #pragma unroll
@@ -240,7 +255,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
         const bf16x8 zero8{};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const bf16x8 w = dequant8_bf_biased(bw[i][j], mr);
+          const bf16x8 w = dequant8_bf_biased(bw[i][0][j], mr);
           const f32x4 p0 = A::mfma16(ac[j], hi ? zero8 : w, zero4);
           const f32x4 p1 = A::mfma16(ac[j], hi ? w : zero8, zero4);
           const f32x4 r0 = A::mfma16(ac[j], hi ? zero8 : ones, zero4);
@@ -267,7 +282,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
         for (int jj = 0; jj < JQ; ++jj) {
           const int j = t * JQ + jj;
-          p = A::mfma16(ac[j], A::dequant(bw[i][j], zo, mr), p);
+          p = A::mfma16(ac[j], A::dequant(bw[i][0][j], zo, mr), p);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sc[i][t], p[e], acc[e]);
@@ -281,7 +296,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const auto zo = A::zero(ZP ? zero_code(z_lds[ubase + 2 * j + hi], col) : 8);
-        const typename A::W8 w = A::dequant(bw[i][j], zo, mr);
+        const typename A::W8 w = A::dequant(bw[i][0][j], zo, mr);
         const f32x4 p0 = A::mfma16(ac[j], hi ? zero8 : w, f32x4{0.f, 0.f, 0.f, 0.f});
         const f32x4 p1 = A::mfma16(ac[j], hi ? w : zero8, f32x4{0.f, 0.f, 0.f, 0.f});
         // (the reads are unconditional, in bounds through the clamped chunk; a masked step
@@ -346,7 +361,7 @@ inline int round_slots(int slots) {
   return slots <= 1 ? 1 : slots <= 2 ? 2 : slots <= 4 ? 4 : slots <= 8 ? 8 : 16;
 }
 
-template <bool ZP, int WAVES, int GW, int STAGE, bool PAIR, int GPC, bool BF16>
+template <bool ZP, int WAVES, int GW, int STAGE, bool PAIR, int GPC, bool BF16, bool W8>
 hipError_t launch_small_t(const uint16_t* a, int lda, int m, const uint32_t* b,
                           const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                           int splits, float* partials, hipStream_t stream) {
@@ -354,11 +369,12 @@ hipError_t launch_small_t(const uint16_t* a, int lda, int m, const uint32_t* b,
   // The activation slice of this instance (its size is fixed by STAGE and WAVES).
   constexpr size_t lds = (size_t)STAGE * WAVES * 64 * sizeof(f16x8);
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16>),
+      reinterpret_cast<const void*>(
+          &gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16, W8>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
   const dim3 grid(n / (PAIR ? 32 : 16), splits);
-  hipLaunchKernelGGL((gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16>), grid,
+  hipLaunchKernelGGL((gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16, W8>), grid,
                      dim3(WAVES * 64), lds, stream, reinterpret_cast<const f16*>(a), lda, m,
                      reinterpret_cast<const u32x4*>(b), s, reinterpret_cast<const u32x2*>(z), c,
                      n, groups, splits, partials);
@@ -367,14 +383,14 @@ hipError_t launch_small_t(const uint16_t* a, int lda, int m, const uint32_t* b,
   return launch_reduce_splits(partials, c, m, n, splits, BF16, stream);
 }
 
-template <bool ZP, int WAVES, int GW, bool PAIR, int GPC, bool BF16>
+template <bool ZP, int WAVES, int GW, bool PAIR, int GPC, bool BF16, bool W8>
 hipError_t launch_small_stage(const uint16_t* a, int lda, int m, const uint32_t* b,
                               const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                               const SmallPlan& plan, float* partials, hipStream_t stream) {
   const int span = (k / kGroup + plan.splits - 1) / plan.splits;
 #define WQ_SMALL(ST)                                                                         \
-  launch_small_t<ZP, WAVES, GW, ST, PAIR, GPC, BF16>(a, lda, m, b, s, z, c, n, k,            \
-                                                     plan.splits, partials, stream)
+  launch_small_t<ZP, WAVES, GW, ST, PAIR, GPC, BF16, W8>(a, lda, m, b, s, z, c, n, k,        \
+                                                         plan.splits, partials, stream)
   switch (round_slots(stage_slots(m, span, WAVES))) {
     case 1: return WQ_SMALL(1);
     case 2: return WQ_SMALL(2);
@@ -385,13 +401,13 @@ hipError_t launch_small_stage(const uint16_t* a, int lda, int m, const uint32_t*
 #undef WQ_SMALL
 }
 
-template <bool ZP, int WAVES, bool PAIR, int GPC, bool BF16>
+template <bool ZP, int WAVES, bool PAIR, int GPC, bool BF16, bool W8>
 hipError_t launch_small_gw(const uint16_t* a, int lda, int m, const uint32_t* b,
                            const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                            const SmallPlan& plan, float* partials, hipStream_t stream) {
 #define WQ_SMALL(GWV)                                                                          \
-  launch_small_stage<ZP, WAVES, GWV, PAIR, GPC, BF16>(a, lda, m, b, s, z, c, n, k, plan,     \
-                                                      partials, stream)
+  launch_small_stage<ZP, WAVES, GWV, PAIR, GPC, BF16, W8>(a, lda, m, b, s, z, c, n, k, plan, \
+                                                          partials, stream)
   switch (plan.depth) {
     case 1: return WQ_SMALL(1);
     case 2: return WQ_SMALL(2);
@@ -407,16 +423,28 @@ hipError_t launch_small_waves(const uint16_t* a, int lda, int m, const uint32_t*
                               const SmallPlan& plan, float* partials, hipStream_t stream) {
   if (plan.pair) {
     if (plan.waves == 16)
-      return launch_small_gw<ZP, 16, true, GPC, BF16>(a, lda, m, b, s, z, c, n, k, plan, partials,
+      return launch_small_gw<ZP, 16, true, GPC, BF16, false>(a, lda, m, b, s, z, c, n, k, plan, partials,
                                                 stream);
-    return launch_small_gw<ZP, 8, true, GPC, BF16>(a, lda, m, b, s, z, c, n, k, plan, partials,
+    return launch_small_gw<ZP, 8, true, GPC, BF16, false>(a, lda, m, b, s, z, c, n, k, plan, partials,
                                              stream);
   }
   if (plan.waves == 8)
-    return launch_small_gw<ZP, 8, false, GPC, BF16>(a, lda, m, b, s, z, c, n, k, plan, partials,
+    return launch_small_gw<ZP, 8, false, GPC, BF16, false>(a, lda, m, b, s, z, c, n, k, plan, partials,
                                               stream);
-  return launch_small_gw<ZP, 4, false, GPC, BF16>(a, lda, m, b, s, z, c, n, k, plan, partials,
+  return launch_small_gw<ZP, 4, false, GPC, BF16, false>(a, lda, m, b, s, z, c, n, k, plan, partials,
                                             stream);
+}
+
+// E4M3 weights (fp16 activations, 128-row scale units, no zero points, no pair).
+inline hipError_t launch_small_w8(const uint16_t* a, int lda, int m, const uint32_t* b,
+                                  const uint16_t* s, uint16_t* c, int n, int k,
+                                  const SmallPlan& plan, float* partials, hipStream_t stream) {
+  if (plan.pair || plan.gpc != 1) return hipErrorInvalidValue;
+  if (plan.waves == 8)
+    return launch_small_gw<false, 8, false, 1, false, true>(a, lda, m, b, s, nullptr, c, n, k,
+                                                            plan, partials, stream);
+  return launch_small_gw<false, 4, false, 1, false, true>(a, lda, m, b, s, nullptr, c, n, k,
+                                                          plan, partials, stream);
 }
 
 // Entry of one GPC and activation type: the plan has been checked by small_plan_fits.

@@ -142,10 +142,14 @@ __device__ __forceinline__ float sigma_of(uint16_t bits) {
   return f == 0.f ? 0x1p-60f : f;
 }
 
+// FP8: E4M3 weights are twice the bytes of a 4-bit group, so B is staged per 64-row chunk
+// in a ring beside A's (3 x 16 KiB), and with one scale unit per 128 rows two SZ slots of
+// one load per wave suffice: 96 + 48 + 4 KiB.
+template <bool FP8>
 struct Smem {
-  f16x8 a[NS][TM * KC / 8];     // 3 x 32 KiB
-  u32x4 b[2][kBlocks * 64];     // 2 x 16 KiB: 16 column blocks x 64 lanes x 16 B
-  uint32_t sz[3][kSzSlotWords];  // scale / zero-point slots (see SzPlan)
+  f16x8 a[NS][TM * KC / 8];                   // 3 x 32 KiB
+  u32x4 b[FP8 ? NS : 2][kBlocks * 64];        // 16 column blocks x 64 lanes x 16 B per slot
+  uint32_t sz[FP8 ? 2 : 3][FP8 ? kThreads : kSzSlotWords];  // scale / zero-point slots
   int row_a[TM];
   int row_c[TM];
   float row_w[TM];  // grouped: routing weight of each output row (1 without the multiply)
@@ -158,12 +162,13 @@ struct Smem {
 // row.  The two lanes exchange their scaled sums (a lane swizzle, xor 16) and the gate lane
 // writes fp16(silu(g) * u) to column j of the [rows][n/2] activation: the gate and up
 // products never leave the registers.
-template <bool ZP, bool GROUPED, bool SWIGLU, int GPC, bool BF16>
+template <bool ZP, bool GROUPED, bool SWIGLU, int GPC, bool BF16, bool FP8>
 __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
   using A = Act<BF16>;
   using Zo = typename A::Zo;
   using W8 = typename A::W8;
-  __shared__ Smem sm;
+  static_assert(!FP8 || (!ZP && GPC == 1 && !BF16), "E4M3: fp16, 128-row units, no zero points");
+  __shared__ Smem<FP8> sm;
   using SZ = SzPlan<GPC>;
   constexpr int kDmaS = SZ::kDmaS;
   constexpr int kWaitOdd = SZ::kWaitOdd;
@@ -318,6 +323,10 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
   const u32x4* bsrc0 =
       reinterpret_cast<const u32x4*>(bptr) + ((long)(nb0 + 2 * wave) * groups) * 64 + lane;
   const u32x4* bsrc1 = bsrc0 + (long)groups * 64;
+  // FP8 layout: 64-row chunk c of block nb is the 64 lanes' vectors at (nb * groups * 2 + c).
+  const u32x4* b8src0 =
+      reinterpret_cast<const u32x4*>(bptr) + ((long)(nb0 + 2 * wave) * groups * 2) * 64 + lane;
+  const u32x4* b8src1 = b8src0 + (long)groups * 2 * 64;
   // SZ: load u of this lane fills slot dword d = u*512 + wave*64 + lane.  Dwords below
   // 128*GPC are scales (block d / (8 GPC), dword d % (8 GPC) of that block's GPC sub-groups),
   // the next 32*GPC zero-point words (block e / (2 GPC), word e % (2 GPC)); the rest re-read
@@ -356,6 +365,12 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
     u32x4* bdst = &sm.b[g & 1][2 * wave * 64];
     __builtin_amdgcn_global_load_lds(bsrc0 + (long)gg * 64, bdst, 16, 0, 0);
     __builtin_amdgcn_global_load_lds(bsrc1 + (long)gg * 64, bdst + 64, 16, 0, 0);
+  };
+  auto issue_b8 = [&](int c) {
+    const int cc = c < nchunks ? c : nchunks - 1;
+    u32x4* bdst = &sm.b[c % NS][2 * wave * 64];
+    __builtin_amdgcn_global_load_lds(b8src0 + (long)cc * 64, bdst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(b8src1 + (long)cc * 64, bdst + 64, 16, 0, 0);
   };
   auto issue_sz = [&](int g) {
     const int gg = g < groups ? g : groups - 1;
@@ -403,9 +418,9 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
       zg[cb] = A::zero(zc);
     }
   };
-  // The lane's weight vectors of group g (slot g & 1).
+  // The lane's weight vectors of group g (slot g & 1), or for FP8 of chunk g (slot g % NS).
   auto read_b = [&](int g) {
-    const u32x4* bslot = sm.b[g & 1];
+    const u32x4* bslot = sm.b[FP8 ? g % NS : g & 1];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       const int base = bblk[cb] * 64 + c16 + 16 * hh;
@@ -414,17 +429,35 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
     }
   };
 
-  // Prologue (see the issue order above), then group 0's scales and weights.
-  issue_sz(0);
-  issue_b(0);
-  issue_sz(1);
-  issue_a(0);
-  issue_a(1);
-  issue_b(1);
-  wait_vmcnt<kWaitPrologue>();
-  __builtin_amdgcn_s_barrier();
-  read_sz(0, 0, sigma, zo);
-  read_b(0);
+  // Prologue (see the issue order above), then group 0's scales and weights.  FP8 issues
+  //   prologue: SZ(0) SZ(1) A(0) B8(0) A(1) B8(1); chunk 2g: SZ(g+2) A(c+2) B8(c+2);
+  //   chunk 2g+1: A(c+2) B8(c+2)
+  // so that chunk c waits for A(c) and B8(c): 6 loads (A, B8 of chunk c+1) may stay in
+  // flight at an even chunk, 7 (also SZ(g+2)) at an odd one.
+  constexpr int kWait8Even = kDmaA + 2;
+  constexpr int kWait8Odd = kDmaS + kDmaA + 2;
+  if constexpr (FP8) {
+    issue_sz(0);
+    issue_sz(1);
+    issue_a(0);
+    issue_b8(0);
+    issue_a(1);
+    issue_b8(1);
+    wait_vmcnt<kWait8Even>();
+    __builtin_amdgcn_s_barrier();
+    read_sz(0, 0, sigma, zo);
+  } else {
+    issue_sz(0);
+    issue_b(0);
+    issue_sz(1);
+    issue_a(0);
+    issue_a(1);
+    issue_b(1);
+    wait_vmcnt<kWaitPrologue>();
+    __builtin_amdgcn_s_barrier();
+    read_sz(0, 0, sigma, zo);
+    read_b(0);
+  }
 
   // One iteration per group: its even chunk and its odd chunk, so that the chunk parity,
   // and with it the weight dwords each step reads, is static.  NRB is the number of the
@@ -434,15 +467,23 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
     constexpr int h2 = decltype(h2c)::value;
     constexpr int NRB = decltype(nrbc)::value;
     const int g = c >> 1;
-    wait_vmcnt<h2 == 0 ? kWaitEven : kWaitOdd>();
+    if constexpr (FP8)
+      wait_vmcnt<h2 == 0 ? kWait8Even : kWait8Odd>();
+    else
+      wait_vmcnt<h2 == 0 ? kWaitEven : kWaitOdd>();
     __builtin_amdgcn_s_barrier();
     if (h2 == 0) {
       issue_sz(g + 2);
       issue_a(c + 2);
+      if constexpr (FP8) issue_b8(c + 2);
     } else {
       issue_a(c + 2);
-      issue_b(g + 2);
+      if constexpr (FP8)
+        issue_b8(c + 2);
+      else
+        issue_b(g + 2);
     }
+    if constexpr (FP8) read_b(c);  // this chunk's weights: step s in vector s % 2
 
     // Odd chunk: the next group's first scales, for the factor sigma / sigma_next applied
     // to the running sums after this group's last MFMAs (1 after the last group).  The
@@ -471,7 +512,12 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
       for (int rb = 0; rb < NRB; ++rb) aop[rb] = arow[rb * 256 + aswz[0]];
       // Weights of 16-row step (4*h2 + s) of the group: dword (2*h2 + s/2) of vector s%2.
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) bop[cb] = A::dequant(bw[cb][0][2 * h2], zo[cb], mr);
+      for (int cb = 0; cb < 2; ++cb) {
+        if constexpr (FP8)
+          bop[cb] = dequant8_fp8(bw[cb][0][0], bw[cb][0][1]);
+        else
+          bop[cb] = A::dequant(bw[cb][0][2 * h2], zo[cb], mr);
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -506,11 +552,19 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) anext[rb] = arow[rb * 256 + aswz[s + 1]];
           }
+          if constexpr (FP8) {
+            // FP8 step s: vector s % 2, words 2(s / 2) and 2(s / 2) + 1
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb)
-            bnext[cb] = A::dequant(bw[cb][(s + 1) & 1][2 * h2 + ((s + 1) >> 1)],
-                                   inner ? zn[cb] : zo[cb], mr);
-        } else if (h2 == 1) {
+            for (int cb = 0; cb < 2; ++cb)
+              bnext[cb] = dequant8_fp8(bw[cb][(s + 1) & 1][2 * ((s + 1) >> 1)],
+                                       bw[cb][(s + 1) & 1][2 * ((s + 1) >> 1) + 1]);
+          } else {
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+              bnext[cb] = A::dequant(bw[cb][(s + 1) & 1][2 * h2 + ((s + 1) >> 1)],
+                                     inner ? zn[cb] : zo[cb], mr);
+          }
+        } else if (!FP8 && h2 == 1) {
           read_b(g + 1);  // the current weights are dead after step 2's dequant
         }
 #pragma unroll
@@ -639,10 +693,10 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
 template <bool GROUPED, bool SWIGLU, int GPC, bool BF16>
 hipError_t launch_tile_g(const TileArgs& p, bool zp, hipStream_t stream) {
   if (zp)
-    hipLaunchKernelGGL((gemm_tile_kernel<true, GROUPED, SWIGLU, GPC, BF16>),
+    hipLaunchKernelGGL((gemm_tile_kernel<true, GROUPED, SWIGLU, GPC, BF16, false>),
                        dim3((unsigned)p.tiles), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm_tile_kernel<false, GROUPED, SWIGLU, GPC, BF16>),
+    hipLaunchKernelGGL((gemm_tile_kernel<false, GROUPED, SWIGLU, GPC, BF16, false>),
                        dim3((unsigned)p.tiles), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
@@ -670,13 +724,26 @@ hipError_t launch_tile_type(const TileArgs& p, bool grouped, bool swiglu, bool z
                 : launch_tile_t<false, false, BF16>(p, zp, gpc, stream);
 }
 
+// E4M3 weights: fp16 activations, 128-row scale units, no zero points.
+inline hipError_t launch_tile_fp8_any(const TileArgs& p, bool grouped, hipStream_t stream) {
+  if (grouped)
+    hipLaunchKernelGGL((gemm_tile_kernel<false, true, false, 1, false, true>),
+                       dim3((unsigned)p.tiles), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((gemm_tile_kernel<false, false, false, 1, false, true>),
+                       dim3((unsigned)p.tiles), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-// The instances of each type (wq_gemm_tile.hip: fp16; wq_gemm_tile_bf16.hip: bf16).
+// The instances of each type (wq_gemm_tile.hip: fp16; wq_gemm_tile_bf16.hip: bf16;
+// wq_gemm_tile_fp8.hip: E4M3 weights).
 hipError_t launch_tile_f16(const TileArgs& p, bool grouped, bool swiglu, bool zp, int gpc,
                            hipStream_t stream);
 hipError_t launch_tile_bf16(const TileArgs& p, bool grouped, bool swiglu, bool zp, int gpc,
                             hipStream_t stream);
+hipError_t launch_tile_fp8(const TileArgs& p, bool grouped, hipStream_t stream);
 
 }  // namespace wq
 

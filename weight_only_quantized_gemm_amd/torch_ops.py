@@ -11,8 +11,9 @@ import math
 import numpy as np
 import torch
 
-from . import (WQ_FLAG_ACT_ORDER, WQ_FLAG_BF16, WQ_FLAG_FP32_REDUCE, WQ_FLAG_HAS_ZP,
-               WQ_FLAG_MUL_TOPK_WEIGHTS, WQ_FLAG_SWIGLU, wq_act_order_perm, wq_interleave_gate_up,
+from . import (WQ_FLAG_ACT_ORDER, WQ_FLAG_BF16, WQ_FLAG_FP8, WQ_FLAG_FP32_REDUCE,
+               WQ_FLAG_HAS_ZP, WQ_FLAG_MUL_TOPK_WEIGHTS, WQ_FLAG_SWIGLU, wq_act_order_perm,
+               wq_repack_fp8, wq_interleave_gate_up,
                wq_gemm, wq_gemm_workspace_bytes, wq_grouped_gemm, wq_repack_b,
                wq_repack_scales, wq_repack_zeros)
 
@@ -40,15 +41,17 @@ def act_dtype(bf16: bool) -> torch.dtype:
 class PackedWeight:
     """One weight matrix in the library layout (B, scales, optional zero points, perm).
     bf16: the scales (numpy uint16 bit patterns or a bfloat16 tensor) and the activations
-    and outputs of its products are bf16."""
+    and outputs of its products are bf16.  fp8: qweight holds E4M3 words [K/4][N] (four
+    K-consecutive bytes per word), repacked with wq_repack_fp8."""
 
     def __init__(self, qweight: np.ndarray, scales: np.ndarray, zeros: np.ndarray | None = None,
                  g_idx: np.ndarray | None = None, device="cuda", group_size: int = GROUP,
-                 bf16: bool = False):
-        self.k = qweight.shape[0] * 8
+                 bf16: bool = False, fp8: bool = False):
+        self.k = qweight.shape[0] * (4 if fp8 else 8)
         self.n = qweight.shape[1]
         self.group_size = group_size
         self.bf16 = bf16
+        self.fp8 = fp8
         self.swiglu = False
         self.device = torch.device(device)
         self.perm = None
@@ -56,8 +59,12 @@ class PackedWeight:
             perm, _ = wq_act_order_perm(g_idx, group_size)
             self.perm = to_device(perm, self.device)
         qw = to_device(qweight, self.device)
-        self.b = torch.empty(self.k * self.n // 8, dtype=torch.int32, device=self.device)
-        wq_repack_b(qw, self.b, self.k, self.n, perm=self.perm)
+        if fp8:
+            self.b = torch.empty(self.k * self.n // 4, dtype=torch.int32, device=self.device)
+            wq_repack_fp8(qw, self.b, self.k, self.n)
+        else:
+            self.b = torch.empty(self.k * self.n // 8, dtype=torch.int32, device=self.device)
+            wq_repack_b(qw, self.b, self.k, self.n, perm=self.perm)
         sc = to_device(scales if isinstance(scales, torch.Tensor)
                        else np.asarray(scales, dtype=np.uint16 if bf16 else np.float16),
                        self.device)
@@ -114,6 +121,8 @@ class PackedWeight:
             f |= WQ_FLAG_SWIGLU
         if self.bf16:
             f |= WQ_FLAG_BF16
+        if self.fp8:
+            f |= WQ_FLAG_FP8
         return f
 
 
@@ -151,7 +160,8 @@ def gemm(a: torch.Tensor, w: PackedWeight, out: torch.Tensor | None = None, *,
 class ExpertBank:
     """Repacked weights of several experts stored back to back (one stride per tensor)."""
 
-    def __init__(self, experts: list[dict], device="cuda", bf16: bool = False):
+    def __init__(self, experts: list[dict], device="cuda", bf16: bool = False,
+                 fp8: bool = False):
         """Each expert is a weight dict (qweight, scales, optional zeros and group_size), or
         {"gate": ..., "up": ...} for a fused gate/up projection with the SwiGLU epilogue."""
         def pack(e):
@@ -160,11 +170,12 @@ class ExpertBank:
                 return PackedWeight.gate_up(e["gate"], e["up"], device=device, group_size=gs,
                                             bf16=bf16)
             return PackedWeight(e["qweight"], e["scales"], e.get("zeros"), device=device,
-                                group_size=gs, bf16=bf16)
+                                group_size=gs, bf16=bf16, fp8=fp8)
         self.packed = [pack(e) for e in experts]
         p0 = self.packed[0]
         self.k, self.n, self.group_size, self.swiglu = p0.k, p0.n, p0.group_size, p0.swiglu
         self.bf16 = bf16
+        self.fp8 = fp8
         self.b = torch.stack([p.b for p in self.packed])
         self.s = torch.stack([p.s for p in self.packed])
         self.z = torch.stack([p.z for p in self.packed]) if p0.z is not None else None
@@ -196,6 +207,7 @@ def grouped_gemm(a: torch.Tensor, bank: ExpertBank, csr: dict, out: torch.Tensor
                     flags=(WQ_FLAG_HAS_ZP if bank.z is not None else 0)
                     | (WQ_FLAG_MUL_TOPK_WEIGHTS if topk_weights is not None else 0)
                     | (WQ_FLAG_SWIGLU if bank.swiglu else 0)
-                    | (WQ_FLAG_BF16 if bank.bf16 else 0),
+                    | (WQ_FLAG_BF16 if bank.bf16 else 0)
+                    | (WQ_FLAG_FP8 if bank.fp8 else 0),
                     stream=stream)
     return out

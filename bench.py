@@ -27,11 +27,15 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
 
 
+TIMED_LOOPS = 5  # timed replays of each captured loop; the median is reported
+
+
 def timed_loop(torch, fn, steps: int, warmup: int) -> float:
-    """Seconds per step over `steps` calls after `warmup` eager calls.
+    """Seconds per step: the median over TIMED_LOOPS timed loops of `steps` calls, after
+    `warmup` eager calls.
 
     The timed calls are captured once into a HIP graph and replayed, so that host-side
-    launch overhead (Python, ctypes) does not hide the kernels' own time; the replay is
+    launch overhead (Python, ctypes) does not hide the kernels' own time; each replay is
     bracketed by HIP events on the stream the kernels run on.
     """
     side = torch.cuda.Stream()
@@ -47,13 +51,16 @@ def timed_loop(torch, fn, steps: int, warmup: int) -> float:
             fn(i)
     graph.replay()                      # one untimed replay
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    start.record()
-    graph.replay()
-    stop.record()
-    torch.cuda.synchronize()
-    return start.elapsed_time(stop) / 1e3 / steps
+    times = []
+    for _ in range(TIMED_LOOPS):
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record()
+        graph.replay()
+        stop.record()
+        torch.cuda.synchronize()
+        times.append(start.elapsed_time(stop) / 1e3 / steps)
+    return sorted(times)[len(times) // 2]
 
 
 def dense_setup(torch, torch_ops, name: str, copies: int):

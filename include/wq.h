@@ -143,6 +143,20 @@ int wq_repack_scales(const void* scales, void* s_out, int k, int n, int group_si
 int wq_repack_fp8(const uint32_t* words, void* b_out, int k, int n, void* stream);
 
 /*
+ * Block-FP8 checkpoints (vllm_marlin.rs `launch_block_fp8_group128_repack` and
+ * `launch_block_fp8_group128_scales`: E4M3 weights row-major [n][k] with one bf16 inverse
+ * scale per 128 x 128 block), load time:
+ *  - wq_repack_fp8_rows: E4M3 bytes [n][k] (row per output channel, 4-byte aligned) ->
+ *    the FP8 layout of wq_repack_fp8 (k*n bytes, 16-byte aligned, no overlap);
+ *  - wq_fp8_block_scales: bf16 [n/128][k/128] -> fp16 scales in the library scale layout
+ *    for group_size 128 ([n/16][k/128][16], 16-byte aligned): column c of group g takes
+ *    block (c/128, g), rounded to nearest even (exact for values in fp16's normal range).
+ * k % 128 == 0, n % 256 == 0; device pointers; enqueued on `stream`.
+ */
+int wq_repack_fp8_rows(const void* w_nk, void* b_out, int k, int n, void* stream);
+int wq_fp8_block_scales(const void* inv_scales, void* s_out, int k, int n, void* stream);
+
+/*
  * Zero points uint32 [k/group_size][n/8] (actual codes 0..15, column 8j+i in bits 4i of
  * word j: vllm_marlin.rs `repack_gptq_qzeros_to_marlin`; [1][n/8] for group_size -1) ->
  * library layout [n/16][k/U][2], unit u taking the codes of the group holding its rows.

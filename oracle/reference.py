@@ -222,6 +222,25 @@ def w8a16_weights(words, scales, *, group_size=128, columns=None, bf16=False) ->
     return e4m3_value(unpack_fp8_words(words)) * values16(scales, bf16)[group, :]
 
 
+def fp8_rows_to_words(w_nk: np.ndarray) -> np.ndarray:
+    """Block-FP8 checkpoint weights, E4M3 bytes row-major [N][K] (one row per output
+    channel), -> the K-major input words [K/4][N] (vllm_marlin.rs block-FP8 repack: the
+    checkpoint matrix transposed and packed four K-consecutive bytes per word)."""
+    w = np.asarray(w_nk, dtype=np.uint8)
+    n, k = w.shape
+    b = w.T.astype(np.uint32).reshape(k // 4, 4, n)
+    return b[:, 0] | (b[:, 1] << np.uint32(8)) | (b[:, 2] << np.uint32(16)) | (b[:, 3] << np.uint32(24))
+
+
+def fp8_block_scales(inv_scales_bf16: np.ndarray) -> np.ndarray:
+    """Block-FP8 inverse scales, bf16 bit patterns [N/128][K/128] (one per 128 x 128 block of
+    the [N][K] weight), -> per-group fp16 scales [K/128][N]: column n of group g takes the
+    scale of block (n // 128, g), rounded to fp16 (nearest even; exact for bf16 values in
+    fp16's normal range)."""
+    v = bf16_value(inv_scales_bf16)                 # [N/128][G]
+    return np.repeat(v, 128, axis=0).T.astype(np.float16)
+
+
 def w8a16_gemm(a, words, scales, *, group_size=128, columns=None, bf16=False) -> np.ndarray:
     """Reference C = A @ W for E4M3 weights, fp64 and unrounded."""
     return matmul_fp64(a, w8a16_weights(words, scales, group_size=group_size, columns=columns,

@@ -175,6 +175,12 @@ def test_fp8_validation_before_launch(L):
                                                                      wq.WQ_ERR_ALIGN)
     assert L.wq_repack_fp8(0x1000, 0x2000, 1000, 256, None) == status(STAGE_SHAPE,
                                                                      wq.WQ_ERR_SHAPE)
+    for fn in (L.wq_repack_fp8_rows, L.wq_fp8_block_scales):
+        assert fn(None, 0x2000, 1024, 256, None) == status(STAGE_ARGS, wq.WQ_ERR_NULL)
+        assert fn(0x1000, 0x2008, 1024, 256, None) == status(STAGE_ARGS, wq.WQ_ERR_ALIGN)
+        assert fn(0x1000, 0x2000, 1024, 320, None) == status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)
+    assert L.wq_repack_fp8_rows(0x1002, 0x2000, 1024, 256, None) == status(STAGE_ARGS,
+                                                                          wq.WQ_ERR_ALIGN)
 
 
 def test_flag_values_match_the_header():

@@ -152,3 +152,25 @@ def test_fp8_grouped_matches_oracle(dev, tokens, experts, k, n, weighted):
                                      moe["routes"])
     want = ref.grouped_w4a16_gemm(moe["a"], ex, ocsr, topk_weights=wts, fp8=True)
     assert_parity(y, want, label)
+
+
+@pytest.mark.parametrize("m", [5, 300])
+def test_fp8_from_block_checkpoint(dev, m):
+    """Row-major E4M3 weights with one bf16 inverse scale per 128 x 128 block (the pages'
+    block-FP8 checkpoint): the device transforms match the layout and scale oracles bit for
+    bit, and the product matches the oracle."""
+    n, k = 512, 768
+    say(f"fp8 block checkpoint m={m} n={n} k={k}")
+    rng = np.random.default_rng(6700 + m)
+    w_nk = synthetic.FP8_CODES[rng.integers(0, 254, size=(n, k))].astype(np.uint8)
+    inv = (0x3B80 + 0x20 * rng.integers(0, 5, size=(n // 128, k // 128))).astype(np.uint16)
+    w = torch_ops.PackedWeight.from_fp8_blocks(w_nk, inv, device=dev)
+    assert np.array_equal(host(w.b).view(np.uint32), layout.repack_fp8_loops(w_nk.T.copy()))
+    scales = ref.fp8_block_scales(inv)
+    assert np.array_equal(host(w.s).view(np.uint16),
+                          layout.repack_scales(scales).view(np.uint16))
+    a = synthetic.activations(6800 + m, m, k)
+    c = host(torch_ops.gemm(torch_ops.to_device(a, dev), w))
+    torch.cuda.synchronize()
+    assert_parity(c, ref.w8a16_gemm(a, ref.fp8_rows_to_words(w_nk), scales),
+                  f"fp8 block checkpoint m={m}")

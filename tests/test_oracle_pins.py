@@ -430,6 +430,28 @@ def test_w8a16_product_matches_bruteforce():
         ref.w8a16_weights(words, s, group_size=64)
 
 
+def test_block_fp8_checkpoint_product_matches_bruteforce():
+    """The pages' block-FP8 reference: decoded weight = e4m3(w[n][k]) * inv[n/128][k/128],
+    with the pages' inverse-scale values (bf16 0x3b80 + 0x20 r, r < 5)."""
+    n, k, m = 256, 256, 2
+    rng = np.random.default_rng(40)
+    w_nk = synthetic.FP8_CODES[rng.integers(0, 254, size=(n, k))].astype(np.uint8)
+    inv = (0x3B80 + 0x20 * rng.integers(0, 5, size=(n // 128, k // 128))).astype(np.uint16)
+    a = synthetic.activations(41, m, k)
+    want = np.zeros((m, n))
+    for mi in range(m):
+        for o in range(n):
+            acc = 0.0
+            for kk in range(k):
+                wv = float(ref.e4m3_value(w_nk[o, kk])) * float(ref.bf16_value(inv[o // 128, kk // 128]))
+                acc += float(a[mi, kk]) * wv
+            want[mi, o] = acc
+    got = ref.w8a16_gemm(a, ref.fp8_rows_to_words(w_nk), ref.fp8_block_scales(inv))
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+    # the words are the transposed rows, four K-consecutive bytes each
+    assert np.array_equal(ref.unpack_fp8_words(ref.fp8_rows_to_words(w_nk)), w_nk.T)
+
+
 def test_fp8_layout_loops_and_inverse_agree():
     codes = np.random.default_rng(33).integers(0, 256, size=(256, 32)).astype(np.uint8)
     words = layout.repack_fp8_loops(codes)

@@ -37,6 +37,7 @@ EXPORTED = (
     "wq_act_order_perm", "wq_gemm_workspace_bytes", "wq_gemm", "wq_dequant",
     "wq_csr_from_routes", "wq_grouped_workspace_bytes", "wq_grouped_gemm",
     "wq_stream_read_sink_words", "wq_stream_read", "wq_interleave_gate_up", "wq_repack_fp8",
+    "wq_repack_fp8_rows", "wq_fp8_block_scales",
 )
 
 
@@ -98,6 +99,8 @@ def lib() -> ctypes.CDLL:
             "wq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
             "wq_repack_b": (ctypes.c_int, [vp, vp, vp, i32, i32, vp]),
             "wq_repack_fp8": (ctypes.c_int, [vp, vp, i32, i32, vp]),
+            "wq_repack_fp8_rows": (ctypes.c_int, [vp, vp, i32, i32, vp]),
+            "wq_fp8_block_scales": (ctypes.c_int, [vp, vp, i32, i32, vp]),
             "wq_repack_scales": (ctypes.c_int, [vp, vp, i32, i32, i32, vp]),
             "wq_repack_zeros": (ctypes.c_int, [vp, vp, i32, i32, i32, vp]),
             "wq_act_order_perm": (ctypes.c_int, [vp, i32, i32, vp, vp]),
@@ -163,6 +166,17 @@ def wq_repack_b(qweight, b_out, k: int, n: int, perm=None, stream=None) -> None:
 def wq_repack_fp8(words, b_out, k: int, n: int, stream=None) -> None:
     """E4M3 words [k/4][n] (K-major, four bytes per word) -> the FP8 library layout."""
     _check(lib().wq_repack_fp8(_ptr(words), _ptr(b_out), k, n, _stream(stream, b_out)))
+
+
+def wq_repack_fp8_rows(w_nk, b_out, k: int, n: int, stream=None) -> None:
+    """Block-FP8 checkpoint weights, E4M3 bytes [n][k], -> the FP8 library layout."""
+    _check(lib().wq_repack_fp8_rows(_ptr(w_nk), _ptr(b_out), k, n, _stream(stream, b_out)))
+
+
+def wq_fp8_block_scales(inv_scales, s_out, k: int, n: int, stream=None) -> None:
+    """Block-FP8 bf16 inverse scales [n/128][k/128] -> fp16 scales in the library layout."""
+    _check(lib().wq_fp8_block_scales(_ptr(inv_scales), _ptr(s_out), k, n,
+                                     _stream(stream, s_out)))
 
 
 def wq_repack_scales(scales, s_out, k: int, n: int, group_size: int = 128, stream=None) -> None:

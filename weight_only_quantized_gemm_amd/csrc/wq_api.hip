@@ -207,6 +207,28 @@ int wq_repack_fp8(const uint32_t* words, void* b_out, int k, int n, void* stream
   return e == hipSuccess ? 0 : hip_fail(e);
 }
 
+int wq_repack_fp8_rows(const void* w_nk, void* b_out, int k, int n, void* stream) {
+  int st = check_kn(k, n, kGroupSize);
+  if (st) return st;
+  if ((st = check_ptr(w_nk, 4))) return st;
+  if ((st = check_ptr(b_out, 16))) return st;
+  const hipError_t e = wq::launch_repack_fp8_rows(static_cast<const uint8_t*>(w_nk),
+                                                  static_cast<uint32_t*>(b_out), k, n,
+                                                  as_stream(stream));
+  return e == hipSuccess ? 0 : hip_fail(e);
+}
+
+int wq_fp8_block_scales(const void* inv_scales, void* s_out, int k, int n, void* stream) {
+  int st = check_kn(k, n, kGroupSize);
+  if (st) return st;
+  if ((st = check_ptr(inv_scales, 2))) return st;
+  if ((st = check_ptr(s_out, 16))) return st;
+  const hipError_t e = wq::launch_fp8_block_scales(static_cast<const uint16_t*>(inv_scales),
+                                                   static_cast<uint16_t*>(s_out), k, n,
+                                                   as_stream(stream));
+  return e == hipSuccess ? 0 : hip_fail(e);
+}
+
 int wq_repack_scales(const void* scales, void* s_out, int k, int n, int group_size,
                      void* stream) {
   int st = check_kn(k, n, group_size);

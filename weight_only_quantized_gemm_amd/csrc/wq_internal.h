@@ -27,6 +27,12 @@ hipError_t launch_repack_fp8(const uint32_t* words, uint32_t* out, int k, int n,
                              hipStream_t stream);
 hipError_t launch_dequant_fp8(const uint32_t* b, const uint16_t* s, int k, int n, uint16_t* w,
                               hipStream_t stream);
+// Block-FP8 checkpoints: E4M3 bytes row-major [n][k] -> the FP8 layout; bf16 inverse scales
+// [n/128][k/128] -> fp16 scales in the library layout.
+hipError_t launch_repack_fp8_rows(const uint8_t* w_nk, uint32_t* out, int k, int n,
+                                  hipStream_t stream);
+hipError_t launch_fp8_block_scales(const uint16_t* inv, uint16_t* out, int k, int n,
+                                   hipStream_t stream);
 // bf16: s and w hold bf16 values (else fp16).
 hipError_t launch_dequant(const uint32_t* b, const uint16_t* s, const uint32_t* z, int k, int n,
                           int unit, bool bf16, uint16_t* w, hipStream_t stream);

@@ -110,6 +110,44 @@ __global__ __launch_bounds__(256) void repack_fp8_kernel(const uint32_t* __restr
   }
 }
 
+// Block-FP8 checkpoint weights, E4M3 bytes row-major [n][k], -> the FP8 layout: a layout
+// word's four rows are K-consecutive bytes of one checkpoint row, one aligned 32-bit read.
+__global__ __launch_bounds__(256) void repack_fp8_rows_kernel(const uint8_t* __restrict__ w_nk,
+                                                              uint32_t* __restrict__ out, int k,
+                                                              int n) {
+  const long total = (long)k * n / 4;
+  const int groups = k / kGroup;
+  for (long o = (long)blockIdx.x * blockDim.x + threadIdx.x; o < total;
+       o += (long)gridDim.x * blockDim.x) {
+    const int d = (int)(o & 3);
+    const int lane = (int)((o >> 2) & 63);
+    const int h = (int)((o >> 8) & 1);
+    const long rest = o >> 9;
+    const int g = (int)(rest % groups);
+    const long nb = rest / groups;
+    const long col = nb * 16 + (lane & 15);
+    const int row0 = g * kGroup + 32 * (2 * h + (d >> 1)) + 8 * (lane >> 4) + 4 * (d & 1);
+    out[o] = *reinterpret_cast<const uint32_t*>(w_nk + col * k + row0);
+  }
+}
+
+// Block-FP8 inverse scales, bf16 [n/128][k/128], -> fp16 scales in the library layout
+// [n/16][k/128][16]: column col of group g takes block (col / 128, g), rounded to fp16.
+__global__ __launch_bounds__(256) void fp8_block_scales_kernel(const uint16_t* __restrict__ inv,
+                                                               uint16_t* __restrict__ out, int k,
+                                                               int n) {
+  const int groups = k / kGroup;
+  const long total = (long)groups * n;
+  for (long o = (long)blockIdx.x * blockDim.x + threadIdx.x; o < total;
+       o += (long)gridDim.x * blockDim.x) {
+    const int c = (int)(o & 15);
+    const long rest = o >> 4;
+    const int g = (int)(rest % groups);
+    const long col = (rest / groups) * 16 + c;
+    out[o] = Act<false>::round(Act<true>::value(inv[(col / kGroup) * groups + g]));
+  }
+}
+
 // E4M3 dequant export: w[row][col] = fp16_rne(e4m3 * s), the product exact in fp32.
 __global__ __launch_bounds__(256) void dequant_fp8_kernel(const u32x4* __restrict__ b,
                                                           const uint16_t* __restrict__ s,
@@ -298,6 +336,20 @@ hipError_t launch_repack_fp8(const uint32_t* words, uint32_t* out, int k, int n,
                              hipStream_t stream) {
   hipLaunchKernelGGL(repack_fp8_kernel, dim3(grid_for((long)k * n / 4)), dim3(256), 0, stream,
                      words, out, k, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_repack_fp8_rows(const uint8_t* w_nk, uint32_t* out, int k, int n,
+                                  hipStream_t stream) {
+  hipLaunchKernelGGL(repack_fp8_rows_kernel, dim3(grid_for((long)k * n / 4)), dim3(256), 0,
+                     stream, w_nk, out, k, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_block_scales(const uint16_t* inv, uint16_t* out, int k, int n,
+                                   hipStream_t stream) {
+  hipLaunchKernelGGL(fp8_block_scales_kernel, dim3(grid_for((long)(k / kGroup) * n)), dim3(256),
+                     0, stream, inv, out, k, n);
   return hipGetLastError();
 }
 

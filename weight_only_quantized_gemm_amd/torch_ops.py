@@ -13,7 +13,7 @@ import torch
 
 from . import (WQ_FLAG_ACT_ORDER, WQ_FLAG_BF16, WQ_FLAG_FP8, WQ_FLAG_FP32_REDUCE,
                WQ_FLAG_HAS_ZP, WQ_FLAG_MUL_TOPK_WEIGHTS, WQ_FLAG_SWIGLU, wq_act_order_perm,
-               wq_repack_fp8, wq_interleave_gate_up,
+               wq_fp8_block_scales, wq_repack_fp8, wq_repack_fp8_rows, wq_interleave_gate_up,
                wq_gemm, wq_gemm_workspace_bytes, wq_grouped_gemm, wq_repack_b,
                wq_repack_scales, wq_repack_zeros)
 
@@ -98,6 +98,25 @@ class PackedWeight:
         w = cls(pair("qweight", 32), pair("scales", 16), zeros, g_idx, device=dev,
                 group_size=group_size, bf16=bf16)
         w.swiglu = True
+        return w
+
+    @classmethod
+    def from_fp8_blocks(cls, w_nk: np.ndarray, inv_scales: np.ndarray,
+                        device="cuda") -> "PackedWeight":
+        """A block-FP8 checkpoint weight: E4M3 bytes row-major [N][K] and bf16 inverse scales
+        [N/128][K/128] (numpy uint16 bit patterns), converted on the device."""
+        dev = torch.device(device)
+        n, k = w_nk.shape
+        w = object.__new__(cls)
+        w.k, w.n, w.group_size, w.bf16, w.fp8, w.swiglu = k, n, GROUP, False, True, False
+        w.device, w.perm, w.z = dev, None, None
+        src = torch.from_numpy(np.ascontiguousarray(w_nk, dtype=np.uint8)).to(dev)
+        w.b = torch.empty(k * n // 4, dtype=torch.int32, device=dev)
+        wq_repack_fp8_rows(src, w.b, k, n)
+        inv = to_device(np.ascontiguousarray(inv_scales, dtype=np.uint16), dev)
+        w.s = torch.empty((k // GROUP) * n, dtype=torch.float16, device=dev)
+        wq_fp8_block_scales(inv, w.s, k, n)
+        torch.cuda.synchronize(dev)
         return w
 
     def clone(self) -> "PackedWeight":

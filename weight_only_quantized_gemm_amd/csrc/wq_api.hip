@@ -95,6 +95,8 @@ bool plan_small_pair(int m, int k, int gpc, wq::SmallPlan* plan) {
   return false;
 }
 
+constexpr int kDirectRows = 9;
+
 bool plan_small(int m, int n, int k, uint32_t flags, int requested, int gpc,
                 wq::SmallPlan* plan) {
   const int groups = k / kGroupSize;
@@ -111,17 +113,22 @@ bool plan_small(int m, int n, int k, uint32_t flags, int requested, int gpc,
   for (; s <= groups && s <= kMaxSplits; ++s) {
     if (s > 1 && !fp32) return false;
     const int span = (groups + s - 1) / s;
-    for (int waves = 4; waves <= 8; waves *= 2) {
-      const int per_wave = (span + waves - 1) / waves;
-      if (per_wave > 8) continue;
-      wq::SmallPlan p{};
-      p.waves = waves;
-      p.splits = s;
-      p.depth = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 8;
-      p.gpc = gpc;
-      if (wq::small_plan_fits(m, k, p)) {
-        *plan = p;
-        return true;
+    // From kDirectRows rows on, the activation slice through LDS costs more than each wave
+    // reading its own operands, so direct plans (at most 4 groups per wave) come first.
+    for (int pass = m >= kDirectRows ? 0 : 1; pass < 2; ++pass) {
+      for (int waves = 4; waves <= 8; waves *= 2) {
+        const int per_wave = (span + waves - 1) / waves;
+        if (per_wave > 8) continue;
+        wq::SmallPlan p{};
+        p.waves = waves;
+        p.splits = s;
+        p.depth = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 8;
+        p.gpc = gpc;
+        p.direct = pass == 0;
+        if (wq::small_plan_fits(m, k, p)) {
+          *plan = p;
+          return true;
+        }
       }
     }
   }

@@ -76,6 +76,9 @@ bool small_plan_fits(int m, int k, const SmallPlan& plan) {
   const int kw = plan.pair ? plan.waves / 2 : plan.waves;  // waves along K per block
   if (span > kMaxSpan || min_span < kw) return false;   // every wave has a group
   if ((span + kw - 1) / kw > plan.depth || plan.depth > 8) return false;
+  if (plan.direct)  // no activation slice; the operands of at most 4 groups in registers
+    return plan.depth <= 4 && !plan.pair &&
+           small_static_lds(plan.waves, plan.pair, plan.gpc) <= kLdsBytes;
   const int slots = stage_slots(m, span, plan.waves);
   const long dynamic = (long)round_slots(slots) * plan.waves * 64 * (long)sizeof(f16x8);
   return slots <= 16 &&

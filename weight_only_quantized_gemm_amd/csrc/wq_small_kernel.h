@@ -72,6 +72,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   using A = Act<BF16>;
   static_assert(!W8 || (!ZP && !PAIR && !BF16 && GPC == 1), "E4M3: fp16, no zero points");
   constexpr int NV = W8 ? 2 : 1;  // 16-byte weight vectors per lane and group
+  // STAGE 0: no activation slice in LDS; each wave loads its own A operands (16 contiguous
+  // bytes per lane and 32-row step) into registers beside its weights.  For several rows
+  // this avoids streaming the whole slice through LDS, write and read, behind a barrier.
+  constexpr bool DA = STAGE == 0;
+  static_assert(!DA || (GW <= 4 && !PAIR), "direct activations: at most 4 groups, no pair");
   constexpr int T = WAVES * 64;
   constexpr int NB = PAIR ? 2 : 1;            // column blocks of the work-group
   constexpr int KW = WAVES / NB;              // waves splitting K for one block
@@ -110,16 +115,18 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   int r = tid / per_row;
   int q = tid - r * per_row;
   const f16* a_base = a + (long)gs0 * kGroup;
-  f16x8 stage[STAGE];
+  f16x8 stage[DA ? 1 : STAGE];
+  if constexpr (!DA) {
 #pragma unroll
-  for (int u = 0; u < STAGE; ++u) {
-    const int rr = r < m ? r : m - 1;
-    stage[u] = *reinterpret_cast<const f16x8*>(a_base + (long)rr * lda + 8 * q);
-    q += dq;
-    r += dr;
-    const bool wrap = q >= per_row;
-    q = wrap ? q - per_row : q;
-    r = wrap ? r + 1 : r;
+    for (int u = 0; u < STAGE; ++u) {
+      const int rr = r < m ? r : m - 1;
+      stage[u] = *reinterpret_cast<const f16x8*>(a_base + (long)rr * lda + 8 * q);
+      q += dq;
+      r += dr;
+      const bool wrap = q >= per_row;
+      q = wrap ? q - per_row : q;
+      r = wrap ? r + 1 : r;
+    }
   }
   // 2. Scales (8 dwords of fp16 pairs per unit row) and zero points of the range, for each
   //    of the work-group's blocks ([block][unit] in LDS).  A block holds groups*GPC units.
@@ -150,17 +157,26 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 
   // 3. The wave's weight chunks, all in flight before any arithmetic.
   u32x4 bw[GW][NV];
+  f16x8 ag[DA ? GW : 1][4];  // STAGE 0: the lane's activation operands of each group
+  const f16* a_row = a + (long)(col < m ? col : m - 1) * lda + 8 * qd;
 #pragma unroll
   for (int i = 0; i < GW; ++i) {
     const int g = g0 + (i < gw ? i : gw - 1);
 #pragma unroll
     for (int v = 0; v < NV; ++v)
       bw[i][v] = __builtin_nontemporal_load(&b[(((long)nb * groups + g) * NV + v) * 64 + lane]);
+    if constexpr (DA) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        ag[i][j] = *reinterpret_cast<const f16x8*>(a_row + (long)g * kGroup + 32 * j);
+    }
   }
 
   // 4. Stage into LDS (waits for the activations and scales only), then sync.
+  if constexpr (!DA) {
 #pragma unroll
-  for (int u = 0; u < STAGE; ++u) a_lds[tid + u * T] = stage[u];
+    for (int u = 0; u < STAGE; ++u) a_lds[tid + u * T] = stage[u];
+  }
 #pragma unroll
   for (int u = 0; u < SU; ++u) s_lds[tid + u * T] = s_stage[u];
   if constexpr (ZP) {
@@ -199,15 +215,17 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     }
   }
   f16x8 an[4];
+  if constexpr (!DA) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) an[j] = a_lds[arow + gl[0] * 16 + 4 * j + qd];
+    for (int j = 0; j < 4; ++j) an[j] = a_lds[arow + gl[0] * 16 + 4 * j + qd];
+  }
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < GW; ++i) {
     f16x8 ac[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ac[j] = an[j];
-    if (i + 1 < GW) {
+    for (int j = 0; j < 4; ++j) ac[j] = DA ? ag[i][j] : an[j];
+    if (!DA && i + 1 < GW) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) an[j] = a_lds[arow + gl[i + 1] * 16 + 4 * j + qd];
     }
@@ -388,6 +406,13 @@ hipError_t launch_small_stage(const uint16_t* a, int lda, int m, const uint32_t*
                               const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                               const SmallPlan& plan, float* partials, hipStream_t stream) {
   const int span = (k / kGroup + plan.splits - 1) / plan.splits;
+  if (plan.direct) {
+    if constexpr (GW <= 4 && !PAIR)
+      return launch_small_t<ZP, WAVES, GW, 0, PAIR, GPC, BF16, W8>(a, lda, m, b, s, z, c, n, k,
+                                                                   plan.splits, partials,
+                                                                   stream);
+    return hipErrorInvalidValue;
+  }
 #define WQ_SMALL(ST)                                                                         \
   launch_small_t<ZP, WAVES, GW, ST, PAIR, GPC, BF16, W8>(a, lda, m, b, s, z, c, n, k,        \
                                                          plan.splits, partials, stream)

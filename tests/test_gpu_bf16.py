@@ -78,6 +78,9 @@ BF16_SHAPES = [
     (64, 1024, 256, 32, True, False, False, 0),
     (130, 1536, 512, 16, False, False, False, 0),
     (40, 1024, 256, -1, True, False, False, 0),
+    # 9..16 rows with activation operands in registers
+    (9, 2048, 256, 128, True, False, False, 0),
+    (13, 1024, 512, 16, False, False, True, 2),
 ]
 
 

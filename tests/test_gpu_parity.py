@@ -222,6 +222,29 @@ def test_small_m_group_sizes_match_oracle(dev, m, k, n, gs, zp, act_order, fp32,
     assert_parity(c, oracle_gemm(case), label)
 
 
+# 9..16 rows: the small-M kernel loads each wave's activation operands straight into
+# registers (no LDS slice) when a wave holds at most 4 groups.
+DIRECT_SHAPES = [
+    # m, k, n, group_size, zp, act_order, fp32_reduce, split_k
+    (9, 4096, 256, 16, True, False, False, 0),
+    (11, 1024, 512, 128, False, True, True, 0),
+    (13, 2048, 256, 64, True, False, True, 2),
+    (16, 512, 256, -1, False, False, False, 0),
+    (10, 4096, 512, 32, False, False, True, 4),
+]
+
+
+@pytest.mark.parametrize("m,k,n,gs,zp,act_order,fp32,split", DIRECT_SHAPES)
+def test_direct_activation_rows_match_oracle(dev, m, k, n, gs, zp, act_order, fp32, split):
+    label = (f"direct rows m={m} k={k} n={n} group_size={gs} zp={zp} act_order={act_order} "
+             f"fp32={fp32} split={split}")
+    say(label)
+    case = synthetic.dense_case(m, k, n, zp=zp, act_order=act_order, group_size=gs,
+                                seed=3700 + m + k)
+    c = gpu_gemm(case, dev, fp32_reduce=fp32, split_k=split)
+    assert_parity(c, oracle_gemm(case), label)
+
+
 @pytest.mark.parametrize("gs,k", [(-1, 1024), (32, 1024), (64, 1024), (256, 1024), (1024, 1024),
                                   (16, 1024), (48, 768), (80, 1280), (96, 1152)])
 def test_group_size_repack_and_dequant_bitwise(dev, gs, k):

@@ -75,8 +75,10 @@ extern "C" {
 /* W8A16: B holds FP8 E4M3 weights (the "fn" variant: bias 7, no infinities, 0x7F/0xFF NaN)
  * in the FP8 library layout (wq_repack_fp8), one byte per weight: the pages' E4M3 weight
  * type (vllm_marlin.rs `ferrum_vllm_marlin_moe_fp8_f16`).  W[k][n] = e4m3(code) * s.
- * As the pages require: group_size -1 or 128, no zero points; here also fp16 activations
- * only, no act_order and no SwiGLU epilogue (WQ_ERR_FLAGS / WQ_ERR_SHAPE otherwise). */
+ * As the pages require: group_size -1 or 128, no zero points; here also no act_order
+ * (WQ_ERR_FLAGS / WQ_ERR_SHAPE otherwise).  fp16 activations as on the pages, or bf16
+ * (WQ_FLAG_BF16: the weights are converted to bf16 instead); the SwiGLU epilogue works as
+ * for 4-bit weights. */
 #define WQ_FLAG_FP8 (1u << 9)
 
 enum wq_stage {

@@ -412,11 +412,18 @@ def silu(x: np.ndarray) -> np.ndarray:
 
 
 def swiglu_activation(a, gate: dict, up: dict, *, group_size=128, columns=None,
-                      bf16=False) -> np.ndarray:
+                      bf16=False, fp8=False) -> np.ndarray:
     """act = silu(A @ W_gate) * (A @ W_up), fp64 and unrounded ([M][I], or a column subset).
 
-    `gate` and `up` hold qweight, scales and optional zeros of the two projections.
+    `gate` and `up` hold qweight, scales and optional zeros of the two projections (E4M3
+    words and scales with fp8).
     """
+    if fp8:
+        g = w8a16_gemm(a, gate["qweight"], gate["scales"], group_size=group_size,
+                       columns=columns, bf16=bf16)
+        u = w8a16_gemm(a, up["qweight"], up["scales"], group_size=group_size,
+                       columns=columns, bf16=bf16)
+        return silu(g) * u
     g = w4a16_gemm(a, gate["qweight"], gate["scales"], zeros=gate.get("zeros"),
                    group_size=group_size, columns=columns, bf16=bf16)
     u = w4a16_gemm(a, up["qweight"], up["scales"], zeros=up.get("zeros"),

@@ -155,14 +155,16 @@ def test_repack_and_dequant_validation(L):
 
 def test_fp8_validation_before_launch(L):
     FP8 = wq.WQ_FLAG_FP8
-    # the pages' E4M3 rules: group_size -1 or 128, no zero points; and fp16 only, no
-    # act_order or SwiGLU epilogue here
+    # the pages' E4M3 rules: group_size -1 or 128, no zero points; and no act_order here
+    # (bf16 activations and the SwiGLU epilogue are valid, so no fake-pointer call uses them)
     assert call_gemm(L, flags=FP8, group_size=64) == status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)
     assert call_gemm(L, flags=FP8, group_size=256) == status(STAGE_SHAPE, wq.WQ_ERR_SHAPE)
     assert call_gemm(L, flags=FP8 | wq.WQ_FLAG_HAS_ZP, zero_points=0x5000) == status(
         STAGE_ARGS, wq.WQ_ERR_FLAGS)
-    assert call_gemm(L, flags=FP8 | wq.WQ_FLAG_BF16) == status(STAGE_ARGS, wq.WQ_ERR_FLAGS)
-    assert call_gemm(L, flags=FP8 | wq.WQ_FLAG_SWIGLU) == status(STAGE_ARGS, wq.WQ_ERR_FLAGS)
+    assert call_gemm(L, flags=FP8 | wq.WQ_FLAG_BF16, group_size=32) == status(
+        STAGE_SHAPE, wq.WQ_ERR_SHAPE)
+    assert call_gemm(L, flags=FP8 | wq.WQ_FLAG_SWIGLU | wq.WQ_FLAG_HAS_ZP,
+                     zero_points=0x5000) == status(STAGE_ARGS, wq.WQ_ERR_FLAGS)
     assert call_gemm(L, flags=FP8 | wq.WQ_FLAG_ACT_ORDER, perm=0x6000,
                      a_tmp=0x6100) == status(STAGE_ARGS, wq.WQ_ERR_FLAGS)
     assert L.wq_dequant(0x1000, 0x2000, None, 1024, 256, 64, FP8, 0x3000,

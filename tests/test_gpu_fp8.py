@@ -176,3 +176,70 @@ def test_fp8_from_block_checkpoint(dev, m):
     torch.cuda.synchronize()
     assert_parity(c, ref.w8a16_gemm(a, ref.fp8_rows_to_words(w_nk), scales),
                   f"fp8 block checkpoint m={m}")
+
+
+BF16_TOL = dict(rel_elem=2.0 ** -8, rel_frob=4e-3)  # bf16 outputs (see test_gpu_bf16.py)
+
+
+@pytest.mark.parametrize("m,k,n,gs", [(1, 4096, 512, 128), (11, 2048, 256, -1),
+                                      (300, 1024, 512, 128), (17, 768, 256, -1)])
+def test_fp8_with_bf16_activations(dev, m, k, n, gs):
+    label = f"fp8 bf16 gemm m={m} k={k} n={n} group_size={gs}"
+    say(label)
+    case = synthetic.fp8_case(m, k, n, group_size=gs, seed=6900 + m, bf16=True)
+    w = torch_ops.PackedWeight(case["qweight"], case["scales"], device=dev, group_size=gs,
+                               bf16=True, fp8=True)
+    c = torch_ops.gemm(torch_ops.to_device(case["a"], dev), w)
+    torch.cuda.synchronize()
+    assert c.dtype == torch.bfloat16
+    want = ref.w8a16_gemm(case["a"], case["qweight"], case["scales"], group_size=gs, bf16=True)
+    res = ref.check(c.float().cpu().numpy(), want, **BF16_TOL)
+    say(f"{label}: max_err={res['max_err']:.3e} tol={res['tol']:.3e} rel_frob={res['rel_frob']:.3e}")
+    assert res["ok"], (label, res)
+
+
+def fp8_proj(seed, k, cols, bf16=False):
+    sc = synthetic.scales_bf16 if bf16 else synthetic.scales
+    return dict(qweight=synthetic.fp8_words(seed, k, cols), scales=sc(seed + 1, k // 128, cols))
+
+
+@pytest.mark.parametrize("m,k,i,bf16", [(1, 4096, 512, False), (4, 2048, 256, True),
+                                        (300, 1024, 256, False), (130, 768, 256, True)])
+def test_fp8_swiglu_activation(dev, m, k, i, bf16):
+    """The SwiGLU epilogue over E4M3 gate/up weights (paired small-M kernel and tiled)."""
+    label = f"fp8 swiglu m={m} k={k} i={i} bf16={bf16}"
+    say(label)
+    gate, up = fp8_proj(7000 + m, k, i, bf16), fp8_proj(7010 + m, k, i, bf16)
+    a = (synthetic.activations_bf16 if bf16 else synthetic.activations)(7020 + m, m, k)
+    w = torch_ops.PackedWeight.gate_up(gate, up, device=dev, bf16=bf16, fp8=True)
+    act = torch_ops.gemm(torch_ops.to_device(a, dev), w)
+    torch.cuda.synchronize()
+    assert act.shape == (m, i)
+    want = ref.swiglu_activation(a, gate, up, bf16=bf16, fp8=True)
+    tol = BF16_TOL if bf16 else dict(rel_elem=2.0 ** -10)  # the activation's heavy tails
+    res = ref.check(act.float().cpu().numpy(), want, **tol)
+    say(f"{label}: max_err={res['max_err']:.3e} tol={res['tol']:.3e} rel_frob={res['rel_frob']:.3e}")
+    assert res["ok"], (label, res)
+
+
+def test_fp8_grouped_swiglu(dev):
+    """MoE gate/up with E4M3 weights: grouped SwiGLU over pair rows."""
+    tokens, experts, k, i = 200, 3, 512, 256
+    say(f"fp8 grouped swiglu tokens={tokens} experts={experts} k={k} i={i}")
+    moe = synthetic.moe_case(tokens, experts, k, 2 * i, seed=7100)
+    ex = [dict(gate=fp8_proj(7200 + e, k, i), up=fp8_proj(7300 + e, k, i))
+          for e in range(experts)]
+    bank = torch_ops.ExpertBank(ex, device=dev, fp8=True)
+    csr = wq.wq_csr_from_routes(moe["routes"], tokens, 2, experts)
+    y = host(torch_ops.grouped_gemm(torch_ops.to_device(moe["a"], dev), bank, csr))
+    torch.cuda.synchronize()
+    ocsr = ref.csr_from_token_routes(experts, tokens, 2, moe["routes"])
+    want = np.full((len(ocsr["ex_pairs"]), i), np.nan)
+    for s_i, e in enumerate(ocsr["ex_ids"]):
+        rows = [ocsr["ex_pairs"][j] for j in range(ocsr["ex_off"][s_i], ocsr["ex_off"][s_i + 1])]
+        toks = [ocsr["pair_tok"][p] for p in rows]
+        want[rows, :] = ref.swiglu_activation(moe["a"][toks, :], ex[e]["gate"], ex[e]["up"],
+                                              fp8=True)
+    res = ref.check(y, want, rel_elem=2.0 ** -10)
+    say(f"fp8 grouped swiglu: max_err={res['max_err']:.3e} tol={res['tol']:.3e}")
+    assert res["ok"], res

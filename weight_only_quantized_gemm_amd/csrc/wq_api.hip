@@ -42,13 +42,11 @@ bool chunk_group_size(int k, int group_size) {
 // Scale units per 128 rows of K (units of gcd(group_size, 128) rows: 1, 2, 4 or 8).
 int subgroups(int k, int group_size) { return kGroupSize / wq::scale_unit_rows(k, group_size); }
 
-// WQ_FLAG_FP8 (E4M3 weights): group_size -1 or 128, fp16, no zero points, act_order or
-// SwiGLU epilogue.
+// WQ_FLAG_FP8 (E4M3 weights): group_size -1 or 128, no zero points, no act_order.
 int check_fp8(uint32_t flags, int group_size) {
   if (!(flags & WQ_FLAG_FP8)) return 0;
   if (group_size != -1 && group_size != kGroupSize) return fail(WQ_STAGE_SHAPE, WQ_ERR_SHAPE);
-  if (flags & (WQ_FLAG_HAS_ZP | WQ_FLAG_ACT_ORDER | WQ_FLAG_BF16 | WQ_FLAG_SWIGLU))
-    return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
+  if (flags & (WQ_FLAG_HAS_ZP | WQ_FLAG_ACT_ORDER)) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
   return 0;
 }
 

@@ -138,6 +138,17 @@ __device__ __forceinline__ f16x8 dequant8_fp8(uint32_t lo, uint32_t hi) {
   return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// The same for bf16 activations: two E4M3 bytes to two bf16 values per instruction (exact:
+// E4M3 magnitudes need 4 significant bits and lie inside bf16's range).
+__device__ __forceinline__ bf16x8 dequant8_fp8_bf(uint32_t lo, uint32_t hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 // Biased bf16 dequant for kernels with MFMA to spare: one layout word -> the eight values
 // 128 + q of its rows (row order as above), each nibble OR-ed into the mantissa of 128.0
 // (bf16 0x4300, whose ulp is 1).  A product with these operands is corrected afterwards
@@ -170,6 +181,7 @@ struct Act<false> {
   __device__ static Zo zero(int z) { return zero_offsets(z); }
   __device__ static Mr magic() { return magic_regs(); }
   __device__ static W8 dequant(uint32_t w, Zo zo, Mr mr) { return dequant8(w, zo, mr); }
+  __device__ static W8 fp8(uint32_t lo, uint32_t hi) { return dequant8_fp8(lo, hi); }
   __device__ static f32x4 mfma16(f16x8 a, W8 b, f32x4 c) { return mfma16x16x32(a, b, c); }
   __device__ static f32x16 mfma32(f16x8 a, W8 b, f32x16 c) { return mfma32x32x16(a, b, c); }
   __device__ static float value(uint16_t bits) {
@@ -186,6 +198,7 @@ struct Act<true> {
   __device__ static Zo zero(int z) { return zero_offsets_bf(z); }
   __device__ static Mr magic() { return magic_regs_bf(); }
   __device__ static W8 dequant(uint32_t w, Zo zo, Mr mr) { return dequant8_bf(w, zo, mr); }
+  __device__ static W8 fp8(uint32_t lo, uint32_t hi) { return dequant8_fp8_bf(lo, hi); }
   __device__ static f32x4 mfma16(f16x8 a, W8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0,
                                                    0);

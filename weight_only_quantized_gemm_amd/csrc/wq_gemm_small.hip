@@ -91,8 +91,9 @@ hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* 
                              hipStream_t stream) {
   if (!small_plan_fits(m, k, plan)) return hipErrorInvalidConfiguration;
   if (fp8) {
-    if (bf16 || z != nullptr) return hipErrorInvalidValue;
-    return launch_small_fp8(a, lda, m, b, s, c, n, k, plan, partials, stream);
+    if (z != nullptr) return hipErrorInvalidValue;
+    return bf16 ? launch_small_fp8_bf16(a, lda, m, b, s, c, n, k, plan, partials, stream)
+                : launch_small_fp8(a, lda, m, b, s, c, n, k, plan, partials, stream);
   }
   if (bf16) {
     switch (plan.gpc) {

@@ -6,7 +6,7 @@ namespace wq {
 hipError_t launch_small_fp8(const uint16_t* a, int lda, int m, const uint32_t* b,
                             const uint16_t* s, uint16_t* c, int n, int k, const SmallPlan& plan,
                             float* partials, hipStream_t stream) {
-  return launch_small_w8(a, lda, m, b, s, c, n, k, plan, partials, stream);
+  return launch_small_w8<false>(a, lda, m, b, s, c, n, k, plan, partials, stream);
 }
 
 }  // namespace wq

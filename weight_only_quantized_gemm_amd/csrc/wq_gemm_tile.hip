@@ -25,8 +25,8 @@ hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b
   p.ldc = swiglu ? n / 2 : n;
   p.tiles = (n / TN) * ((m + TM - 1) / TM);
   if (fp8) {
-    if (bf16 || swiglu || z != nullptr || gpc != 1) return hipErrorInvalidValue;
-    return launch_tile_fp8(p, false, stream);
+    if (z != nullptr || gpc != 1) return hipErrorInvalidValue;
+    return launch_tile_fp8(p, false, swiglu, bf16, stream);
   }
   return bf16 ? launch_tile_bf16(p, false, swiglu, z != nullptr, gpc, stream)
               : launch_tile_f16(p, false, swiglu, z != nullptr, gpc, stream);
@@ -67,8 +67,8 @@ hipError_t launch_grouped_tile(const GroupedProblem& g, hipStream_t stream) {
   p.tiles = (int)tiles;
   p.ldc = g.swiglu ? g.n / 2 : g.n;
   if (g.fp8) {
-    if (g.bf16 || g.swiglu || g.z_bank != nullptr || g.gpc != 1) return hipErrorInvalidValue;
-    return launch_tile_fp8(p, true, stream);
+    if (g.z_bank != nullptr || g.gpc != 1) return hipErrorInvalidValue;
+    return launch_tile_fp8(p, true, g.swiglu, g.bf16, stream);
   }
   return g.bf16 ? launch_tile_bf16(p, true, g.swiglu, g.z_bank != nullptr, g.gpc, stream)
                 : launch_tile_f16(p, true, g.swiglu, g.z_bank != nullptr, g.gpc, stream);

@@ -54,15 +54,18 @@ struct SmallPlan {
 };
 bool small_plan_fits(int m, int k, const SmallPlan& plan);
 // bf16: A, s and c hold bf16 values (else fp16).  fp8: b holds E4M3 weights in the FP8
-// layout (fp16 only, no zero points, 128-row scale units).
+// layout (no zero points, 128-row scale units).
 hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* b,
                              const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                              const SmallPlan& plan, float* partials, bool bf16, bool fp8,
                              hipStream_t stream);
-// The E4M3 instances (wq_gemm_small_fp8.hip).
+// The E4M3 instances (wq_gemm_small_fp8.hip: fp16; wq_gemm_small_fp8_bf16.hip: bf16).
 hipError_t launch_small_fp8(const uint16_t* a, int lda, int m, const uint32_t* b,
                             const uint16_t* s, uint16_t* c, int n, int k, const SmallPlan& plan,
                             float* partials, hipStream_t stream);
+hipError_t launch_small_fp8_bf16(const uint16_t* a, int lda, int m, const uint32_t* b,
+                                 const uint16_t* s, uint16_t* c, int n, int k,
+                                 const SmallPlan& plan, float* partials, hipStream_t stream);
 // The instances of each scale-unit count and activation type (wq_gemm_small.hip, _g2.hip,
 // _g4.hip, _g8.hip; wq_gemm_small_bf16.hip, _bf16_g2.hip, _bf16_g4.hip, _bf16_g8.hip).
 #define WQ_SMALL_GPC_DECL(NAME)                                                             \
@@ -88,7 +91,7 @@ constexpr int kTileM = 256;
 constexpr int kTileN = 256;
 // swiglu: B pairs gate/up 16-column blocks and c is the [m][n/2] activation.  gpc: scale
 // units per 128 rows of K (1, 2, 4 or 8).  bf16: A, s and c hold bf16 values (else fp16).
-// fp8: b holds E4M3 weights in the FP8 layout (fp16, gpc 1, no zero points, no swiglu).
+// fp8: b holds E4M3 weights in the FP8 layout (gpc 1, no zero points).
 hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b,
                             const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                             bool swiglu, int gpc, bool bf16, bool fp8, hipStream_t stream);

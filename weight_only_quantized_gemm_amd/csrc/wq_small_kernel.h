@@ -18,9 +18,9 @@
 // each step runs twice, once with the other half's weight lanes set to zero.
 //
 // BF16 selects bf16 activations, scales and outputs (bf16 MFMAs and dequant); the
-// arithmetic is otherwise the same.  W8 selects E4M3 weights (fp16 activations, one scale
-// unit per 128 rows, no zero points): a lane's group is then two 16-byte vectors (rows
-// 0-63 and 64-127 of the group), converted to fp16 two bytes per instruction.
+// arithmetic is otherwise the same.  W8 selects E4M3 weights (one scale unit per 128 rows,
+// no zero points): a lane's group is then two 16-byte vectors (rows 0-63 and 64-127 of the
+// group), converted to the activation type two bytes per instruction.
 //
 // This header holds the kernel template and its launch chain; each translation unit that
 // includes it instantiates one GPC and activation type, so that the instances compile in
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     const uint16_t* __restrict__ s, const u32x2* __restrict__ z, uint16_t* __restrict__ c,
     int n, int groups, int splits, float* __restrict__ partials) {
   using A = Act<BF16>;
-  static_assert(!W8 || (!ZP && !PAIR && !BF16 && GPC == 1), "E4M3: fp16, no zero points");
+  static_assert(!W8 || (!ZP && GPC == 1), "E4M3: 128-row scale units, no zero points");
   constexpr int NV = W8 ? 2 : 1;  // 16-byte weight vectors per lane and group
   // STAGE 0: no activation slice in LDS; each wave loads its own A operands (16 contiguous
   // bytes per lane and 32-row step) into registers beside its weights.  For several rows
@@ -237,8 +237,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
       f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        p = mfma16x16x32(ac[j], dequant8_fp8(bw[i][j >> 1][2 * (j & 1)],
-                                             bw[i][j >> 1][2 * (j & 1) + 1]), p);
+        p = A::mfma16(ac[j], A::fp8(bw[i][j >> 1][2 * (j & 1)], bw[i][j >> 1][2 * (j & 1) + 1]),
+                      p);
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sc[i][0], p[e], acc[e]);
     } else if constexpr (BF16) {
@@ -460,16 +460,25 @@ hipError_t launch_small_waves(const uint16_t* a, int lda, int m, const uint32_t*
                                             stream);
 }
 
-// E4M3 weights (fp16 activations, 128-row scale units, no zero points, no pair).
-inline hipError_t launch_small_w8(const uint16_t* a, int lda, int m, const uint32_t* b,
-                                  const uint16_t* s, uint16_t* c, int n, int k,
-                                  const SmallPlan& plan, float* partials, hipStream_t stream) {
-  if (plan.pair || plan.gpc != 1) return hipErrorInvalidValue;
-  if (plan.waves == 8)
-    return launch_small_gw<false, 8, false, 1, false, true>(a, lda, m, b, s, nullptr, c, n, k,
-                                                            plan, partials, stream);
-  return launch_small_gw<false, 4, false, 1, false, true>(a, lda, m, b, s, nullptr, c, n, k,
+// E4M3 weights (128-row scale units, no zero points), either activation type, with or
+// without the SwiGLU pair.
+template <bool BF16>
+hipError_t launch_small_w8(const uint16_t* a, int lda, int m, const uint32_t* b,
+                           const uint16_t* s, uint16_t* c, int n, int k, const SmallPlan& plan,
+                           float* partials, hipStream_t stream) {
+  if (plan.gpc != 1) return hipErrorInvalidValue;
+  if (plan.pair) {
+    if (plan.waves == 16)
+      return launch_small_gw<false, 16, true, 1, BF16, true>(a, lda, m, b, s, nullptr, c, n, k,
+                                                             plan, partials, stream);
+    return launch_small_gw<false, 8, true, 1, BF16, true>(a, lda, m, b, s, nullptr, c, n, k,
                                                           plan, partials, stream);
+  }
+  if (plan.waves == 8)
+    return launch_small_gw<false, 8, false, 1, BF16, true>(a, lda, m, b, s, nullptr, c, n, k,
+                                                           plan, partials, stream);
+  return launch_small_gw<false, 4, false, 1, BF16, true>(a, lda, m, b, s, nullptr, c, n, k,
+                                                         plan, partials, stream);
 }
 
 // Entry of one GPC and activation type: the plan has been checked by small_plan_fits.

@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
   using A = Act<BF16>;
   using Zo = typename A::Zo;
   using W8 = typename A::W8;
-  static_assert(!FP8 || (!ZP && GPC == 1 && !BF16), "E4M3: fp16, 128-row units, no zero points");
+  static_assert(!FP8 || (!ZP && GPC == 1), "E4M3: 128-row scale units, no zero points");
   __shared__ Smem<FP8> sm;
   using SZ = SzPlan<GPC>;
   constexpr int kDmaS = SZ::kDmaS;
@@ -514,7 +514,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         if constexpr (FP8)
-          bop[cb] = dequant8_fp8(bw[cb][0][0], bw[cb][0][1]);
+          bop[cb] = A::fp8(bw[cb][0][0], bw[cb][0][1]);
         else
           bop[cb] = A::dequant(bw[cb][0][2 * h2], zo[cb], mr);
       }
@@ -556,8 +556,8 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
             // FP8 step s: vector s % 2, words 2(s / 2) and 2(s / 2) + 1
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb)
-              bnext[cb] = dequant8_fp8(bw[cb][(s + 1) & 1][2 * ((s + 1) >> 1)],
-                                       bw[cb][(s + 1) & 1][2 * ((s + 1) >> 1) + 1]);
+              bnext[cb] = A::fp8(bw[cb][(s + 1) & 1][2 * ((s + 1) >> 1)],
+                                 bw[cb][(s + 1) & 1][2 * ((s + 1) >> 1) + 1]);
           } else {
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb)
@@ -724,14 +724,25 @@ hipError_t launch_tile_type(const TileArgs& p, bool grouped, bool swiglu, bool z
                 : launch_tile_t<false, false, BF16>(p, zp, gpc, stream);
 }
 
-// E4M3 weights: fp16 activations, 128-row scale units, no zero points.
-inline hipError_t launch_tile_fp8_any(const TileArgs& p, bool grouped, hipStream_t stream) {
-  if (grouped)
-    hipLaunchKernelGGL((gemm_tile_kernel<false, true, false, 1, false, true>),
-                       dim3((unsigned)p.tiles), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((gemm_tile_kernel<false, false, false, 1, false, true>),
-                       dim3((unsigned)p.tiles), dim3(kThreads), 0, stream, p);
+// E4M3 weights: 128-row scale units, no zero points; every layout of one activation type.
+template <bool BF16>
+hipError_t launch_tile_fp8_type(const TileArgs& p, bool grouped, bool swiglu,
+                                hipStream_t stream) {
+#define WQ_TILE_FP8(G, S)                                                                  \
+  hipLaunchKernelGGL((gemm_tile_kernel<false, G, S, 1, BF16, true>), dim3((unsigned)p.tiles), \
+                     dim3(kThreads), 0, stream, p)
+  if (grouped) {
+    if (swiglu)
+      WQ_TILE_FP8(true, true);
+    else
+      WQ_TILE_FP8(true, false);
+  } else {
+    if (swiglu)
+      WQ_TILE_FP8(false, true);
+    else
+      WQ_TILE_FP8(false, false);
+  }
+#undef WQ_TILE_FP8
   return hipGetLastError();
 }
 
@@ -743,7 +754,8 @@ hipError_t launch_tile_f16(const TileArgs& p, bool grouped, bool swiglu, bool zp
                            hipStream_t stream);
 hipError_t launch_tile_bf16(const TileArgs& p, bool grouped, bool swiglu, bool zp, int gpc,
                             hipStream_t stream);
-hipError_t launch_tile_fp8(const TileArgs& p, bool grouped, hipStream_t stream);
+hipError_t launch_tile_fp8(const TileArgs& p, bool grouped, bool swiglu, bool bf16,
+                           hipStream_t stream);
 
 }  // namespace wq
 

@@ -81,7 +81,8 @@ class PackedWeight:
 
     @classmethod
     def gate_up(cls, gate: dict, up: dict, device="cuda", group_size: int = GROUP,
-                g_idx: np.ndarray | None = None, bf16: bool = False) -> "PackedWeight":
+                g_idx: np.ndarray | None = None, bf16: bool = False,
+                fp8: bool = False) -> "PackedWeight":
         """One weight of 2*I columns for the SwiGLU epilogue: the gate and up projections'
         qweight, scales and zero points paired in 16-column blocks on the device
         (wq_interleave_gate_up), then repacked like any weight."""
@@ -96,7 +97,7 @@ class PackedWeight:
 
         zeros = pair("zeros", 4) if gate.get("zeros") is not None else None
         w = cls(pair("qweight", 32), pair("scales", 16), zeros, g_idx, device=dev,
-                group_size=group_size, bf16=bf16)
+                group_size=group_size, bf16=bf16, fp8=fp8)
         w.swiglu = True
         return w
 
@@ -187,7 +188,7 @@ class ExpertBank:
             gs = e.get("group_size", GROUP)
             if "gate" in e:
                 return PackedWeight.gate_up(e["gate"], e["up"], device=device, group_size=gs,
-                                            bf16=bf16)
+                                            bf16=bf16, fp8=fp8)
             return PackedWeight(e["qweight"], e["scales"], e.get("zeros"), device=device,
                                 group_size=gs, bf16=bf16, fp8=fp8)
         self.packed = [pack(e) for e in experts]

@@ -289,12 +289,63 @@ def test_prefill_config_matches_oracle_on_sampled_columns(dev):
 
 # --------------------------------------------------------------------------- pins
 
+# One-row fp16 products take the biased dequant: codes enter the MFMA as 1024 + q or 64 + q
+# and each scale unit's product has the activations' bias excess (computed apart from the
+# MFMA) subtracted before its scale.  Both are fp32 sums of terms up to 1039 |a| over the
+# unit, so the unrounded result is off by at most a few fp32 roundings of 1039 * sum |a| |s|:
+# 24 roundings bound a four-step MFMA chain, the excess's eight-term dot products and
+# butterfly, the subtraction and the scaled accumulation.
+ONE_ROW_ROUNDINGS = 24
+
+
+def one_row_bias_bound(case):
+    a = np.abs(case["a"].astype(np.float64))[0]
+    k = a.size
+    gs = case.get("group_size", 128)
+    gs = k if gs == -1 else gs
+    s_rows = np.abs(case["scales"].astype(np.float64))[np.arange(k) // gs]
+    return ONE_ROW_ROUNDINGS * 2.0 ** -24 * 1039.0 * (a @ s_rows)
+
+
 def test_all_eight_codes_give_exact_zero(dev):
-    for m in (1, 16, 300):
+    for m in (16, 300):
         case = synthetic.dense_case(m, 512, 256, seed=3)
         case["qweight"][:] = 0x88888888
         c = gpu_gemm(case, dev, fp32_reduce=True)
         assert np.all(c.astype(np.float64) == 0.0), m
+    # one row: the biased products and their excess cancel up to the bound above
+    case = synthetic.dense_case(1, 512, 256, seed=3)
+    case["qweight"][:] = 0x88888888
+    c = gpu_gemm(case, dev, fp32_reduce=True)[0].astype(np.float64)
+    bound = one_row_bias_bound(case)
+    assert np.all(np.abs(c) <= bound * (1 + 2.0 ** -10) + 2.0 ** -24)
+
+
+ONE_ROW_SHAPES = [
+    # k, n, group_size, zp, all-positive activations, split_k
+    (4096, 512, 128, False, True, 0),
+    (4096, 512, 128, True, True, 0),
+    (4096, 512, 16, True, True, 0),
+    (2048, 512, 32, False, True, 0),
+    (1024, 512, 64, True, False, 0),
+    (1024, 768, -1, True, True, 0),
+    (4096, 256, 128, True, True, 3),
+]
+
+
+@pytest.mark.parametrize("k,n,gs,zp,positive,split", ONE_ROW_SHAPES)
+def test_one_row_biased_dequant_within_its_bound(dev, k, n, gs, zp, positive, split):
+    label = f"one row k={k} n={n} group_size={gs} zp={zp} positive={positive} split={split}"
+    say(label)
+    case = synthetic.dense_case(1, k, n, zp=zp, group_size=gs, seed=3900 + k + n + gs)
+    if positive:  # every activation of one sign: the largest bias sums for the result's size
+        case["a"] = np.abs(case["a"])
+    c = gpu_gemm(case, dev, fp32_reduce=True, split_k=split)
+    want = oracle_gemm(case)
+    assert_parity(c, want, label)
+    err = np.abs(c[0].astype(np.float64) - want[0])
+    allowed = 2.0 ** -11 * np.abs(want[0]) + one_row_bias_bound(case) * (1 + 2.0 ** -11) + 2.0 ** -25
+    assert np.all(err <= allowed), (label, float(np.max(err - allowed)))
 
 
 def test_unit_scales_integer_products_are_bit_exact(dev):

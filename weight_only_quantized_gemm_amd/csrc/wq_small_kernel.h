@@ -22,6 +22,17 @@
 // no zero points): a lane's group is then two 16-byte vectors (rows 0-63 and 64-127 of the
 // group), converted to the activation type two bytes per instruction.
 //
+// R1 (one activation row, fp16, 4-bit weights) takes the biased dequant: each word's rows
+// enter the MFMA as 1024 + q or 64 + q (one OR each, no subtraction), which saves four of
+// the nine VALU operations per word in this VALU-bound loop.  The excess this leaves in a
+// unit's product, the activations weighted by those biases plus z times their sum, depends
+// on the activations alone: the staging threads form it for every unit of the slice while
+// the weights are in flight, and each unit's product has it subtracted before its scale is
+// applied.  Only the real output row is scaled and accumulated.  Both the product and the
+// excess are fp32 sums of terms up to 1039 |a|, so a unit's difference carries an absolute
+// error of a few fp32 roundings of 1039 * sum(|a|) over the unit: about a tenth of the fp16
+// rounding of the result for signed activations, comparable to it when all are positive.
+//
 // This header holds the kernel template and its launch chain; each translation unit that
 // includes it instantiates one GPC and activation type, so that the instances compile in
 // parallel.
@@ -49,10 +60,11 @@ constexpr int small_zero_slots(int waves, bool pair, int gpc) {
              ? (pair ? 2 : 1) * kMaxSpan * gpc / (waves * 64) : 1;
 }
 // Static LDS of an instance (see the kernel's __shared__ arrays), an upper bound over ZP.
-constexpr long small_static_lds(int waves, bool pair, int gpc) {
+constexpr long small_static_lds(int waves, bool pair, int gpc, bool r1) {
   return (long)small_scale_slots(waves, pair, gpc) * waves * 64 * 4    // s_lds
          + (long)small_zero_slots(waves, pair, gpc) * waves * 64 * 8   // z_lds
-         + (long)waves * 64 * 16;                                      // red
+         + (long)waves * 64 * 16                                       // red
+         + (r1 ? (long)kMaxSpan * gpc * 2 * 4 : 0);                    // corr_lds, rsum_lds
 }
 
 // The kernel body is branch-free up to the arithmetic: every load is issued
@@ -64,7 +76,8 @@ constexpr long small_static_lds(int waves, bool pair, int gpc) {
 // (2t, 2t+1, as wq_interleave_gate_up pairs them); its first half of waves streams the gate
 // block, the second half the up block, both over the same K range and staged activations,
 // and the reduction writes fp16(silu(g) * u) to column 16t + c of the [m][n/2] activation.
-template <bool ZP, int WAVES, int GW, int STAGE, bool PAIR, int GPC, bool BF16, bool W8>
+template <bool ZP, int WAVES, int GW, int STAGE, bool PAIR, int GPC, bool BF16, bool W8,
+          bool R1>
 __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     const f16* __restrict__ a, int lda, int m, const u32x4* __restrict__ b,
     const uint16_t* __restrict__ s, const u32x2* __restrict__ z, uint16_t* __restrict__ c,
@@ -77,6 +90,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   // this avoids streaming the whole slice through LDS, write and read, behind a barrier.
   constexpr bool DA = STAGE == 0;
   static_assert(!DA || (GW <= 4 && !PAIR), "direct activations: at most 4 groups, no pair");
+  static_assert(!R1 || (!DA && !BF16 && !W8), "biased dequant: staged fp16 activations, 4-bit");
   constexpr int T = WAVES * 64;
   constexpr int NB = PAIR ? 2 : 1;            // column blocks of the work-group
   constexpr int KW = WAVES / NB;              // waves splitting K for one block
@@ -89,6 +103,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   __shared__ uint32_t s_lds[SU * T];          // scales, [block][chunk][unit][col] as fp16
   __shared__ u32x2 z_lds[ZP ? ZU * T : 1];    // zero points, [block][chunk][unit]
   __shared__ f32x4 red[WAVES][64];
+  // R1: per scale unit of the slice, the activations weighted by the operand biases (plus
+  // 8 of each without zero points) and, with zero points, their plain sum.
+  __shared__ float corr_lds[R1 ? kMaxSpan * GPC : 1];
+  __shared__ float rsum_lds[R1 && ZP ? kMaxSpan * GPC : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -116,10 +134,16 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   int q = tid - r * per_row;
   const f16* a_base = a + (long)gs0 * kGroup;
   f16x8 stage[DA ? 1 : STAGE];
+  int stage_q[R1 ? STAGE : 1];        // R1: granule column of each slot
+  bool stage_real[R1 ? STAGE : 1];    // R1: the slot lies inside the slice
   if constexpr (!DA) {
 #pragma unroll
     for (int u = 0; u < STAGE; ++u) {
       const int rr = r < m ? r : m - 1;
+      if constexpr (R1) {
+        stage_q[u] = q;
+        stage_real[u] = r < m;
+      }
       stage[u] = *reinterpret_cast<const f16x8*>(a_base + (long)rr * lda + 8 * q);
       q += dq;
       r += dr;
@@ -183,6 +207,41 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
     for (int u = 0; u < ZU; ++u) z_lds[tid + u * T] = z_stage[u];
   }
+  if constexpr (R1) {
+    // A unit of the slice is GR consecutive granules, held by GR consecutive lanes of one
+    // slot (aligned, since T and the row length are multiples of 16): each lane weights its
+    // eight activations by the biases of their rows (1024 for rows 0, 1, 4, 5 of the eight,
+    // 64 for rows 2, 3, 6, 7), a butterfly adds the unit's lanes, and its first lane stores.
+    constexpr int GR = 16 / GPC;
+    const f16x2 b_hi = ZP ? f16x2{1024, 1024} : f16x2{1032, 1032};  // + 8 for u4b8
+    const f16x2 b_lo = ZP ? f16x2{64, 64} : f16x2{72, 72};
+    const f16x2 ones = f16x2{1, 1};
+#pragma unroll
+    for (int u = 0; u < STAGE; ++u) {
+      const f16x8 v = stage[u];
+      const f16x2 v01{v[0], v[1]}, v23{v[2], v[3]}, v45{v[4], v[5]}, v67{v[6], v[7]};
+      float cb = __builtin_amdgcn_fdot2(v01, b_hi, 0.f, false);
+      cb = __builtin_amdgcn_fdot2(v23, b_lo, cb, false);
+      cb = __builtin_amdgcn_fdot2(v45, b_hi, cb, false);
+      cb = __builtin_amdgcn_fdot2(v67, b_lo, cb, false);
+      float rs = 0.f;
+      if constexpr (ZP) {
+        rs = __builtin_amdgcn_fdot2(v01, ones, rs, false);
+        rs = __builtin_amdgcn_fdot2(v23, ones, rs, false);
+        rs = __builtin_amdgcn_fdot2(v45, ones, rs, false);
+        rs = __builtin_amdgcn_fdot2(v67, ones, rs, false);
+      }
+#pragma unroll
+      for (int d = 1; d < GR; d *= 2) {
+        cb += __shfl_xor(cb, d);
+        if constexpr (ZP) rs += __shfl_xor(rs, d);
+      }
+      if (stage_real[u] && (tid & (GR - 1)) == 0) {
+        corr_lds[stage_q[u] / GR] = cb;
+        if constexpr (ZP) rsum_lds[stage_q[u] / GR] = rs;
+      }
+    }
+  }
   __syncthreads();
 
   // 5. Arithmetic.  MFMA rows >= m are never stored, and a row of the product depends on
@@ -212,6 +271,22 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
         const float v = A::value(s_half[((half * span + gl[i]) * GPC + t) * 16 + col]);
         sc[i][t] = i < gw ? v : 0.f;
       }
+    }
+  }
+  // R1: the bias excess of unit t of step i, for this lane's column.
+  const auto excess = [&](int i, int t) -> float {
+    const int unit = gl[i] * GPC + t;
+    if constexpr (ZP)
+      return __builtin_fmaf((float)zero_code(z_lds[(half * span + gl[i]) * GPC + t], col),
+                            rsum_lds[unit], corr_lds[unit]);
+    return corr_lds[unit];
+  };
+  float ex[R1 ? GW : 1][R1 ? HS : 1];  // hoisted with the scales (GPC <= 4)
+  if constexpr (R1 && GPC <= 4) {
+#pragma unroll
+    for (int i = 0; i < GW; ++i) {
+#pragma unroll
+      for (int t = 0; t < GPC; ++t) ex[i][t] = excess(i, t);
     }
   }
   f16x8 an[4];
@@ -290,6 +365,35 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             acc[e] = __builtin_fmaf(s1, __builtin_fmaf(-(float)(128 + z1), r1[e], p1[e]), acc[e]);
+        }
+      }
+    } else if constexpr (R1) {
+      // Biased operands; only row 0 of the product is real.
+      const auto biased = [&](uint32_t w) { return dequant8_biased(w, mr); };
+      if constexpr (GPC <= 4) {
+#pragma unroll
+        for (int t = 0; t < GPC; ++t) {
+          f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int jj = 0; jj < JQ; ++jj) {
+            const int j = t * JQ + jj;
+            p = A::mfma16(ac[j], biased(bw[i][0][j]), p);
+          }
+          acc[0] = __builtin_fmaf(sc[i][t], p[0] - ex[i][t], acc[0]);
+        }
+      } else {
+        const int hi = qd >> 1;
+        const int ubase = (half * span + gl[i]) * 8;
+        const f16x8 zero8{};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f16x8 w = biased(bw[i][0][j]);
+          const f32x4 p0 = A::mfma16(ac[j], hi ? zero8 : w, f32x4{0.f, 0.f, 0.f, 0.f});
+          const f32x4 p1 = A::mfma16(ac[j], hi ? w : zero8, f32x4{0.f, 0.f, 0.f, 0.f});
+          const float v0 = A::value(s_half[(ubase + 2 * j) * 16 + col]);
+          const float v1 = A::value(s_half[(ubase + 2 * j + 1) * 16 + col]);
+          acc[0] = __builtin_fmaf(i < gw ? v0 : 0.f, p0[0] - excess(i, 2 * j), acc[0]);
+          acc[0] = __builtin_fmaf(i < gw ? v1 : 0.f, p1[0] - excess(i, 2 * j + 1), acc[0]);
         }
       }
     } else if constexpr (GPC <= 4) {
@@ -379,7 +483,8 @@ inline int round_slots(int slots) {
   return slots <= 1 ? 1 : slots <= 2 ? 2 : slots <= 4 ? 4 : slots <= 8 ? 8 : 16;
 }
 
-template <bool ZP, int WAVES, int GW, int STAGE, bool PAIR, int GPC, bool BF16, bool W8>
+template <bool ZP, int WAVES, int GW, int STAGE, bool PAIR, int GPC, bool BF16, bool W8,
+          bool R1>
 hipError_t launch_small_t(const uint16_t* a, int lda, int m, const uint32_t* b,
                           const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                           int splits, float* partials, hipStream_t stream) {
@@ -388,11 +493,11 @@ hipError_t launch_small_t(const uint16_t* a, int lda, int m, const uint32_t* b,
   constexpr size_t lds = (size_t)STAGE * WAVES * 64 * sizeof(f16x8);
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(
-          &gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16, W8>),
+          &gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16, W8, R1>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
   const dim3 grid(n / (PAIR ? 32 : 16), splits);
-  hipLaunchKernelGGL((gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16, W8>), grid,
+  hipLaunchKernelGGL((gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16, W8, R1>), grid,
                      dim3(WAVES * 64), lds, stream, reinterpret_cast<const f16*>(a), lda, m,
                      reinterpret_cast<const u32x4*>(b), s, reinterpret_cast<const u32x2*>(z), c,
                      n, groups, splits, partials);
@@ -408,14 +513,28 @@ hipError_t launch_small_stage(const uint16_t* a, int lda, int m, const uint32_t*
   const int span = (k / kGroup + plan.splits - 1) / plan.splits;
   if (plan.direct) {
     if constexpr (GW <= 4 && !PAIR)
-      return launch_small_t<ZP, WAVES, GW, 0, PAIR, GPC, BF16, W8>(a, lda, m, b, s, z, c, n, k,
-                                                                   plan.splits, partials,
-                                                                   stream);
+      return launch_small_t<ZP, WAVES, GW, 0, PAIR, GPC, BF16, W8, false>(
+          a, lda, m, b, s, z, c, n, k, plan.splits, partials, stream);
     return hipErrorInvalidValue;
   }
+  if constexpr (!BF16 && !W8) {
+    // One row (at most 64 groups: at most four slots per thread).
+    if (m == 1) {
+#define WQ_SMALL1(ST)                                                                        \
+  launch_small_t<ZP, WAVES, GW, ST, PAIR, GPC, BF16, W8, true>(a, lda, m, b, s, z, c, n, k,  \
+                                                               plan.splits, partials, stream)
+      switch (round_slots(stage_slots(m, span, WAVES))) {
+        case 1: return WQ_SMALL1(1);
+        case 2: return WQ_SMALL1(2);
+        case 4: return WQ_SMALL1(4);
+        default: return hipErrorInvalidValue;
+      }
+#undef WQ_SMALL1
+    }
+  }
 #define WQ_SMALL(ST)                                                                         \
-  launch_small_t<ZP, WAVES, GW, ST, PAIR, GPC, BF16, W8>(a, lda, m, b, s, z, c, n, k,        \
-                                                         plan.splits, partials, stream)
+  launch_small_t<ZP, WAVES, GW, ST, PAIR, GPC, BF16, W8, false>(a, lda, m, b, s, z, c, n, k, \
+                                                                plan.splits, partials, stream)
   switch (round_slots(stage_slots(m, span, WAVES))) {
     case 1: return WQ_SMALL(1);
     case 2: return WQ_SMALL(2);

@@ -290,11 +290,11 @@ def test_prefill_config_matches_oracle_on_sampled_columns(dev):
 # --------------------------------------------------------------------------- pins
 
 # One-row fp16 products take the biased dequant: codes enter the MFMA as 1024 + q or 64 + q
-# and each scale unit's product has the activations' bias excess (computed apart from the
-# MFMA) subtracted before its scale.  Both are fp32 sums of terms up to 1039 |a| over the
-# unit, so the unrounded result is off by at most a few fp32 roundings of 1039 * sum |a| |s|:
-# 24 roundings bound a four-step MFMA chain, the excess's eight-term dot products and
-# butterfly, the subtraction and the scaled accumulation.
+# and each lane's share of a scale unit has the activations' bias excess (computed apart
+# from the MFMA) subtracted before its scale.  Both are fp32 sums of terms up to 1039 |a|, so
+# the unrounded result is off by at most a few fp32 roundings of 1039 * sum |a| |s|: 24
+# roundings bound an eight-product MFMA chain, the excess's dot products and butterfly, the
+# subtraction, the scaled accumulation and the final adds over lanes and waves.
 ONE_ROW_ROUNDINGS = 24
 
 

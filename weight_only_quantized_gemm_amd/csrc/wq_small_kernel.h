@@ -22,16 +22,23 @@
 // no zero points): a lane's group is then two 16-byte vectors (rows 0-63 and 64-127 of the
 // group), converted to the activation type two bytes per instruction.
 //
-// R1 (one activation row, fp16, 4-bit weights) takes the biased dequant: each word's rows
-// enter the MFMA as 1024 + q or 64 + q (one OR each, no subtraction), which saves four of
-// the nine VALU operations per word in this VALU-bound loop.  The excess this leaves in a
-// unit's product, the activations weighted by those biases plus z times their sum, depends
-// on the activations alone: the staging threads form it for every unit of the slice while
-// the weights are in flight, and each unit's product has it subtracted before its scale is
-// applied.  Only the real output row is scaled and accumulated.  Both the product and the
-// excess are fp32 sums of terms up to 1039 |a|, so a unit's difference carries an absolute
-// error of a few fp32 roundings of 1039 * sum(|a|) over the unit: about a tenth of the fp16
-// rounding of the result for signed activations, comparable to it when all are positive.
+// R1 (one activation row, fp16, 4-bit weights) is a leaner loop for the decode case:
+//  - Biased dequant: each word's rows enter the MFMA as 1024 + q or 64 + q (one OR each, no
+//    subtraction), four of the nine VALU operations per word saved.
+//  - 4x4x4 MFMAs (16 blocks): with one real row the 16x16x32 product wastes 15 of its 16
+//    rows, and two 4x4x4 products carry the same 512 weights in less MFMA time.  Block b of
+//    a lane pair (col, qd) holds columns 4(b % 4).. and the lane's eight rows of the step, so
+//    each lane keeps its own column's sum over its row class qd (rows 8qd..8qd+7 of every
+//    32-row step); two shuffles add the four classes at the end.  A 16-row unit is then the
+//    lane's own, and the masked double product of GPC = 8 is not needed.
+//  - The excess the biases leave, the activations weighted by them plus z times their sum,
+//    depends on the activations alone: the staging threads form it per unit and row class
+//    while the weights are in flight, and each lane subtracts its own before the unit's
+//    scale.  Only the real output row is scaled and accumulated.
+// Both the biased product and the excess are fp32 sums of terms up to 1039 |a| over the
+// lane's rows of a unit, so their difference carries a few fp32 roundings of that size: a
+// small fraction of the fp16 rounding of the result for signed activations, less than it
+// when all are positive.
 //
 // This header holds the kernel template and its launch chain; each translation unit that
 // includes it instantiates one GPC and activation type, so that the instances compile in
@@ -64,7 +71,7 @@ constexpr long small_static_lds(int waves, bool pair, int gpc, bool r1) {
   return (long)small_scale_slots(waves, pair, gpc) * waves * 64 * 4    // s_lds
          + (long)small_zero_slots(waves, pair, gpc) * waves * 64 * 8   // z_lds
          + (long)waves * 64 * 16                                       // red
-         + (r1 ? (long)kMaxSpan * gpc * 2 * 4 : 0);                    // corr_lds, rsum_lds
+         + (r1 ? (long)kMaxSpan * 16 * 2 * 4 : 0);                     // corr_lds, rsum_lds
 }
 
 // The kernel body is branch-free up to the arithmetic: every load is issued
@@ -105,8 +112,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   __shared__ f32x4 red[WAVES][64];
   // R1: per scale unit of the slice, the activations weighted by the operand biases (plus
   // 8 of each without zero points) and, with zero points, their plain sum.
-  __shared__ float corr_lds[R1 ? kMaxSpan * GPC : 1];
-  __shared__ float rsum_lds[R1 && ZP ? kMaxSpan * GPC : 1];
+  constexpr int EX = GPC == 8 ? 2 : 4;  // excess slots per scale unit: one per row class
+  __shared__ float corr_lds[R1 ? kMaxSpan * GPC * EX : 1];
+  __shared__ float rsum_lds[R1 && ZP ? kMaxSpan * GPC * EX : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -209,9 +217,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   }
   if constexpr (R1) {
     // A unit of the slice is GR consecutive granules, held by GR consecutive lanes of one
-    // slot (aligned, since T and the row length are multiples of 16): each lane weights its
-    // eight activations by the biases of their rows (1024 for rows 0, 1, 4, 5 of the eight,
-    // 64 for rows 2, 3, 6, 7), a butterfly adds the unit's lanes, and its first lane stores.
+    // slot (aligned, since T and the row length are multiples of 16); granule q of a chunk
+    // is row class q % 4 of step q / 4.  Each lane weights its eight activations by the
+    // biases of their rows (1024 for rows 0, 1, 4, 5 of the eight, 64 for rows 2, 3, 6, 7),
+    // a butterfly adds the lanes of one class (or, for 16-row units, none), and the first
+    // EX lanes of the unit store per class (per granule) at unit * EX + class.
     constexpr int GR = 16 / GPC;
     const f16x2 b_hi = ZP ? f16x2{1024, 1024} : f16x2{1032, 1032};  // + 8 for u4b8
     const f16x2 b_lo = ZP ? f16x2{64, 64} : f16x2{72, 72};
@@ -232,13 +242,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
         rs = __builtin_amdgcn_fdot2(v67, ones, rs, false);
       }
 #pragma unroll
-      for (int d = 1; d < GR; d *= 2) {
+      for (int d = EX; d < GR; d *= 2) {
         cb += __shfl_xor(cb, d);
         if constexpr (ZP) rs += __shfl_xor(rs, d);
       }
-      if (stage_real[u] && (tid & (GR - 1)) == 0) {
-        corr_lds[stage_q[u] / GR] = cb;
-        if constexpr (ZP) rsum_lds[stage_q[u] / GR] = rs;
+      if (stage_real[u] && (tid & (GR - 1)) < EX) {
+        const int slot = stage_q[u] / GR * EX + stage_q[u] % EX;
+        corr_lds[slot] = cb;
+        if constexpr (ZP) rsum_lds[slot] = rs;
       }
     }
   }
@@ -273,36 +284,62 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
       }
     }
   }
-  // R1: the bias excess of unit t of step i, for this lane's column.
+  // R1: the bias excess of unit t of step i, for this lane's column and row class.
   const auto excess = [&](int i, int t) -> float {
     const int unit = gl[i] * GPC + t;
+    const int slot = GPC == 8 ? unit * 2 + (qd & 1) : unit * 4 + qd;
     if constexpr (ZP)
       return __builtin_fmaf((float)zero_code(z_lds[(half * span + gl[i]) * GPC + t], col),
-                            rsum_lds[unit], corr_lds[unit]);
-    return corr_lds[unit];
+                            rsum_lds[slot], corr_lds[slot]);
+    return corr_lds[slot];
   };
-  float ex[R1 ? GW : 1][R1 ? HS : 1];  // hoisted with the scales (GPC <= 4)
-  if constexpr (R1 && GPC <= 4) {
+  // Hoisted with the scales for up to two units per chunk; with more, the registers would
+  // cost a wave of occupancy, so the excess is read in place.
+  constexpr bool HX = GPC <= 2;
+  float ex[R1 && HX ? GW : 1][R1 && HX ? HS : 1];
+  if constexpr (R1 && HX) {
 #pragma unroll
     for (int i = 0; i < GW; ++i) {
 #pragma unroll
       for (int t = 0; t < GPC; ++t) ex[i][t] = excess(i, t);
     }
   }
-  f16x8 an[4];
-  if constexpr (!DA) {
+  // R1: the 4x4x4 products broadcast one block's activation operand to the four blocks of
+  // a row class (lanes 16qd..16qd+15), from the block ABID names.  Product p = 0..7 of a
+  // chunk (step p / 2, half p % 2) takes it from lane 16qd + 4(p % 4), register pair p / 4,
+  // so a lane holds two 4-row activation pieces per chunk instead of the sixteen rows of
+  // all four steps: a quarter of the LDS reads.
+  const u32x2* a_lds2 = reinterpret_cast<const u32x2*>(a_lds);
+  const auto r1_operands = [&](int chunk, u32x2* r) {
+    const int x = col >> 2;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      r[h] = a_lds2[2 * (chunk * 16 + 4 * (2 * h + (x >> 1)) + qd) + (x & 1)];
+  };
+  f16x8 an[R1 ? 1 : 4];
+  u32x2 an1[2];
+  if constexpr (R1) {
+    r1_operands(gl[0], an1);
+  } else if constexpr (!DA) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) an[j] = a_lds[arow + gl[0] * 16 + 4 * j + qd];
   }
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < GW; ++i) {
-    f16x8 ac[4];
+    f16x8 ac[R1 ? 1 : 4];
+    u32x2 ar[2];
+    if constexpr (R1) {
+      ar[0] = an1[0];
+      ar[1] = an1[1];
+      if (i + 1 < GW) r1_operands(gl[i + 1], an1);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ac[j] = DA ? ag[i][j] : an[j];
-    if (!DA && i + 1 < GW) {
+      for (int j = 0; j < 4; ++j) ac[j] = DA ? ag[i][j] : an[j];
+      if (!DA && i + 1 < GW) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) an[j] = a_lds[arow + gl[i + 1] * 16 + 4 * j + qd];
+        for (int j = 0; j < 4; ++j) an[j] = a_lds[arow + gl[i + 1] * 16 + 4 * j + qd];
+      }
     }
     // With eight groups per wave, pin the prefetch ahead of this group's work (measured
     // faster for the decode shape, slower for shallower pipelines).
@@ -370,6 +407,23 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     } else if constexpr (R1) {
       // Biased operands; only row 0 of the product is real.
       const auto biased = [&](uint32_t w) { return dequant8_biased(w, mr); };
+      typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+      // step j's two products (rows 0-3 and 4-7 of the lane's eight), operands broadcast
+      // from products 2j and 2j + 1 of the chunk
+      const auto mfma4 = [&](int j, f16x8 b8, f32x4 cc) {
+        const h4 b0 = __builtin_shufflevector(b8, b8, 0, 1, 2, 3);
+        const h4 b1 = __builtin_shufflevector(b8, b8, 4, 5, 6, 7);
+        const h4 a0 = __builtin_bit_cast(h4, ar[j >> 1]);
+        const h4 a1 = a0;
+        switch (j & 1) {  // ABID is an immediate: products 2j % 4 and 2j % 4 + 1
+          case 0:
+            cc = __builtin_amdgcn_mfma_f32_4x4x4f16(a0, b0, cc, 2, 0, 0);
+            return __builtin_amdgcn_mfma_f32_4x4x4f16(a1, b1, cc, 2, 1, 0);
+          default:
+            cc = __builtin_amdgcn_mfma_f32_4x4x4f16(a0, b0, cc, 2, 2, 0);
+            return __builtin_amdgcn_mfma_f32_4x4x4f16(a1, b1, cc, 2, 3, 0);
+        }
+      };
       if constexpr (GPC <= 4) {
 #pragma unroll
         for (int t = 0; t < GPC; ++t) {
@@ -377,23 +431,24 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
           for (int jj = 0; jj < JQ; ++jj) {
             const int j = t * JQ + jj;
-            p = A::mfma16(ac[j], biased(bw[i][0][j]), p);
+            p = mfma4(j, biased(bw[i][0][j]), p);
           }
-          acc[0] = __builtin_fmaf(sc[i][t], p[0] - ex[i][t], acc[0]);
+          float e;
+          if constexpr (HX)
+            e = ex[i][t];
+          else
+            e = excess(i, t);
+          acc[0] = __builtin_fmaf(sc[i][t], p[0] - e, acc[0]);
         }
       } else {
-        const int hi = qd >> 1;
+        // 16-row units: the lane's eight rows of step j lie in unit 2j + (qd >> 1).
         const int ubase = (half * span + gl[i]) * 8;
-        const f16x8 zero8{};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const f16x8 w = biased(bw[i][0][j]);
-          const f32x4 p0 = A::mfma16(ac[j], hi ? zero8 : w, f32x4{0.f, 0.f, 0.f, 0.f});
-          const f32x4 p1 = A::mfma16(ac[j], hi ? w : zero8, f32x4{0.f, 0.f, 0.f, 0.f});
-          const float v0 = A::value(s_half[(ubase + 2 * j) * 16 + col]);
-          const float v1 = A::value(s_half[(ubase + 2 * j + 1) * 16 + col]);
-          acc[0] = __builtin_fmaf(i < gw ? v0 : 0.f, p0[0] - excess(i, 2 * j), acc[0]);
-          acc[0] = __builtin_fmaf(i < gw ? v1 : 0.f, p1[0] - excess(i, 2 * j + 1), acc[0]);
+          const f32x4 p = mfma4(j, biased(bw[i][0][j]), f32x4{0.f, 0.f, 0.f, 0.f});
+          const int t = 2 * j + (qd >> 1);
+          const float v = A::value(s_half[(ubase + t) * 16 + col]);
+          acc[0] = __builtin_fmaf(i < gw ? v : 0.f, p[0] - excess(i, t), acc[0]);
         }
       }
     } else if constexpr (GPC <= 4) {
@@ -436,6 +491,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     if constexpr (GW >= 8) __builtin_amdgcn_sched_barrier(0);
   }
 
+  if constexpr (R1) {
+    // each lane holds its column's sum over one of the four row classes of every step
+    acc[0] += __shfl_xor(acc[0], 16);
+    acc[0] += __shfl_xor(acc[0], 32);
+  }
   // Work-group reduce over the waves, in wave order.
   red[wave][lane] = acc;
   __syncthreads();

@@ -78,6 +78,11 @@ BF16_SHAPES = [
     (64, 1024, 256, 32, True, False, False, 0),
     (130, 1536, 512, 16, False, False, False, 0),
     (40, 1024, 256, -1, True, False, False, 0),
+    # one row: biased operands on 4x4x4 products, every unit size
+    (1, 2048, 512, 16, True, False, True, 0),
+    (1, 1024, 768, 32, False, False, False, 0),
+    (1, 2048, 256, 64, True, False, False, 0),
+    (1, 1024, 256, -1, True, False, True, 0),
     # 9..16 rows with activation operands in registers
     (9, 2048, 256, 128, True, False, False, 0),
     (13, 1024, 512, 16, False, False, True, 2),

@@ -22,17 +22,18 @@
 // no zero points): a lane's group is then two 16-byte vectors (rows 0-63 and 64-127 of the
 // group), converted to the activation type two bytes per instruction.
 //
-// R1 (one activation row, fp16, 4-bit weights) is a leaner loop for the decode case:
+// R1 (one activation row, 4-bit weights) is a leaner loop for the decode case:
 //  - Biased dequant: each word's rows enter the MFMA as 1024 + q or 64 + q (one OR each, no
-//    subtraction), four of the nine VALU operations per word saved.
+//    subtraction), four of the nine VALU operations per word saved.  bf16 activations take
+//    128 + q for every row (as on their general path).
 //  - 4x4x4 MFMAs (16 blocks): with one real row the 16x16x32 product wastes 15 of its 16
 //    rows, and two 4x4x4 products carry the same 512 weights in less MFMA time.  Block b of
 //    a lane pair (col, qd) holds columns 4(b % 4).. and the lane's eight rows of the step, so
 //    each lane keeps its own column's sum over its row class qd (rows 8qd..8qd+7 of every
 //    32-row step); two shuffles add the four classes at the end.  A 16-row unit is then the
 //    lane's own, and the masked double product of GPC = 8 is not needed.
-//  - The excess the biases leave, the activations weighted by them plus z times their sum,
-//    depends on the activations alone: the staging threads form it per unit and row class
+//  - The excess the biases leave, the activations weighted by them plus z times their sum
+//    ((128 + z) times the sum for bf16), depends on the activations alone: the staging threads form it per unit and row class
 //    while the weights are in flight, and each lane subtracts its own before the unit's
 //    scale.  Only the real output row is scaled and accumulated.
 // Both the biased product and the excess are fp32 sums of terms up to 1039 |a| over the
@@ -46,6 +47,8 @@
 #pragma once
 #include "wq_device.h"
 #include "wq_internal.h"
+
+#include <type_traits>
 
 namespace wq {
 namespace {
@@ -97,7 +100,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   // this avoids streaming the whole slice through LDS, write and read, behind a barrier.
   constexpr bool DA = STAGE == 0;
   static_assert(!DA || (GW <= 4 && !PAIR), "direct activations: at most 4 groups, no pair");
-  static_assert(!R1 || (!DA && !BF16 && !W8), "biased dequant: staged fp16 activations, 4-bit");
+  static_assert(!R1 || (!DA && !W8), "biased dequant: staged activations, 4-bit weights");
   constexpr int T = WAVES * 64;
   constexpr int NB = PAIR ? 2 : 1;            // column blocks of the work-group
   constexpr int KW = WAVES / NB;              // waves splitting K for one block
@@ -113,8 +116,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   // R1: per scale unit of the slice, the activations weighted by the operand biases (plus
   // 8 of each without zero points) and, with zero points, their plain sum.
   constexpr int EX = GPC == 8 ? 2 : 4;  // excess slots per scale unit: one per row class
-  __shared__ float corr_lds[R1 ? kMaxSpan * GPC * EX : 1];
-  __shared__ float rsum_lds[R1 && ZP ? kMaxSpan * GPC * EX : 1];
+  __shared__ float corr_lds[R1 && !BF16 ? kMaxSpan * GPC * EX : 1];
+  __shared__ float rsum_lds[R1 && (ZP || BF16) ? kMaxSpan * GPC * EX : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -223,33 +226,46 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     // a butterfly adds the lanes of one class (or, for 16-row units, none), and the first
     // EX lanes of the unit store per class (per granule) at unit * EX + class.
     constexpr int GR = 16 / GPC;
+    constexpr bool WSUM = !BF16;       // bias-weighted sum (fp16's two biases)
+    constexpr bool PSUM = ZP || BF16;  // plain sum
     const f16x2 b_hi = ZP ? f16x2{1024, 1024} : f16x2{1032, 1032};  // + 8 for u4b8
     const f16x2 b_lo = ZP ? f16x2{64, 64} : f16x2{72, 72};
     const f16x2 ones = f16x2{1, 1};
 #pragma unroll
     for (int u = 0; u < STAGE; ++u) {
       const f16x8 v = stage[u];
-      const f16x2 v01{v[0], v[1]}, v23{v[2], v[3]}, v45{v[4], v[5]}, v67{v[6], v[7]};
-      float cb = __builtin_amdgcn_fdot2(v01, b_hi, 0.f, false);
-      cb = __builtin_amdgcn_fdot2(v23, b_lo, cb, false);
-      cb = __builtin_amdgcn_fdot2(v45, b_hi, cb, false);
-      cb = __builtin_amdgcn_fdot2(v67, b_lo, cb, false);
-      float rs = 0.f;
-      if constexpr (ZP) {
-        rs = __builtin_amdgcn_fdot2(v01, ones, rs, false);
-        rs = __builtin_amdgcn_fdot2(v23, ones, rs, false);
-        rs = __builtin_amdgcn_fdot2(v45, ones, rs, false);
-        rs = __builtin_amdgcn_fdot2(v67, ones, rs, false);
+      float cb = 0.f, rs = 0.f;
+      if constexpr (BF16) {
+        // each bf16 is the upper half of a binary32 (the bf16 dot-product builtin on words
+        // reinterpreted as bf16 pairs is miscompiled by this toolchain: it reads word 0 four
+        // times)
+        const u32x4 w = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          rs += __builtin_bit_cast(float, w[h] << 16) +
+                __builtin_bit_cast(float, w[h] & 0xFFFF0000u);
+      } else {
+        const f16x2 v01{v[0], v[1]}, v23{v[2], v[3]}, v45{v[4], v[5]}, v67{v[6], v[7]};
+        cb = __builtin_amdgcn_fdot2(v01, b_hi, cb, false);
+        cb = __builtin_amdgcn_fdot2(v23, b_lo, cb, false);
+        cb = __builtin_amdgcn_fdot2(v45, b_hi, cb, false);
+        cb = __builtin_amdgcn_fdot2(v67, b_lo, cb, false);
+        if constexpr (ZP) {
+          rs = __builtin_amdgcn_fdot2(v01, ones, rs, false);
+          rs = __builtin_amdgcn_fdot2(v23, ones, rs, false);
+          rs = __builtin_amdgcn_fdot2(v45, ones, rs, false);
+          rs = __builtin_amdgcn_fdot2(v67, ones, rs, false);
+        }
       }
 #pragma unroll
       for (int d = EX; d < GR; d *= 2) {
-        cb += __shfl_xor(cb, d);
-        if constexpr (ZP) rs += __shfl_xor(rs, d);
+        if constexpr (WSUM) cb += __shfl_xor(cb, d);
+        if constexpr (PSUM) rs += __shfl_xor(rs, d);
       }
       if (stage_real[u] && (tid & (GR - 1)) < EX) {
         const int slot = stage_q[u] / GR * EX + stage_q[u] % EX;
-        corr_lds[slot] = cb;
-        if constexpr (ZP) rsum_lds[slot] = rs;
+        if constexpr (WSUM) corr_lds[slot] = cb;
+        if constexpr (PSUM) rsum_lds[slot] = rs;
       }
     }
   }
@@ -288,9 +304,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   const auto excess = [&](int i, int t) -> float {
     const int unit = gl[i] * GPC + t;
     const int slot = GPC == 8 ? unit * 2 + (qd & 1) : unit * 4 + qd;
-    if constexpr (ZP)
-      return __builtin_fmaf((float)zero_code(z_lds[(half * span + gl[i]) * GPC + t], col),
-                            rsum_lds[slot], corr_lds[slot]);
+    const float zf = ZP ? (float)zero_code(z_lds[(half * span + gl[i]) * GPC + t], col) : 8.f;
+    if constexpr (BF16) return (128.f + zf) * rsum_lds[slot];
+    if constexpr (ZP) return __builtin_fmaf(zf, rsum_lds[slot], corr_lds[slot]);
     return corr_lds[slot];
   };
   // Hoisted with the scales for up to two units per chunk; with more, the registers would
@@ -353,6 +369,65 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
                       p);
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sc[i][0], p[e], acc[e]);
+    } else if constexpr (R1) {
+      // Biased operands; only row 0 of the product is real.
+      const auto biased = [&](uint32_t w) {
+        if constexpr (BF16)
+          return __builtin_bit_cast(u32x4, dequant8_bf_biased(w, mr));
+        else
+          return __builtin_bit_cast(u32x4, dequant8_biased(w, mr));
+      };
+      // one 4x4x4 product (16 blocks) on four rows; the operand broadcast ID is an immediate
+      const auto mfma1 = [](u32x2 a2, u32x2 b2, f32x4 cc, auto abid) {
+        constexpr int ID = decltype(abid)::value;
+        if constexpr (BF16) {
+          typedef short s4 __attribute__((ext_vector_type(4)));
+          return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s4, a2),
+                                                        __builtin_bit_cast(s4, b2), cc, 2, ID, 0);
+        } else {
+          typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+          return __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(h4, a2),
+                                                    __builtin_bit_cast(h4, b2), cc, 2, ID, 0);
+        }
+      };
+      // step j's two products (rows 0-3 and 4-7 of the lane's eight), operands broadcast
+      // from products 2j and 2j + 1 of the chunk (ABID 2j % 4 and 2j % 4 + 1)
+      const auto mfma4 = [&](int j, u32x4 b, f32x4 cc) {
+        const u32x2 b0 = u32x2{b[0], b[1]}, b1 = u32x2{b[2], b[3]};
+        if (j & 1) {
+          cc = mfma1(ar[j >> 1], b0, cc, std::integral_constant<int, 2>{});
+          return mfma1(ar[j >> 1], b1, cc, std::integral_constant<int, 3>{});
+        }
+        cc = mfma1(ar[j >> 1], b0, cc, std::integral_constant<int, 0>{});
+        return mfma1(ar[j >> 1], b1, cc, std::integral_constant<int, 1>{});
+      };
+      if constexpr (GPC <= 4) {
+#pragma unroll
+        for (int t = 0; t < GPC; ++t) {
+          f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int jj = 0; jj < JQ; ++jj) {
+            const int j = t * JQ + jj;
+            p = mfma4(j, biased(bw[i][0][j]), p);
+          }
+          float e;
+          if constexpr (HX)
+            e = ex[i][t];
+          else
+            e = excess(i, t);
+          acc[0] = __builtin_fmaf(sc[i][t], p[0] - e, acc[0]);
+        }
+      } else {
+        // 16-row units: the lane's eight rows of step j lie in unit 2j + (qd >> 1).
+        const int ubase = (half * span + gl[i]) * 8;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 p = mfma4(j, biased(bw[i][0][j]), f32x4{0.f, 0.f, 0.f, 0.f});
+          const int t = 2 * j + (qd >> 1);
+          const float v = A::value(s_half[(ubase + t) * 16 + col]);
+          acc[0] = __builtin_fmaf(i < gw ? v : 0.f, p[0] - excess(i, t), acc[0]);
+        }
+      }
     } else if constexpr (BF16) {
       // bf16 has no packed add, and the exact dequant costs 21 VALU per word, which this
       // weight-stream-bound kernel cannot hide.  The weights enter the MFMA biased, as
@@ -402,53 +477,6 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             acc[e] = __builtin_fmaf(s1, __builtin_fmaf(-(float)(128 + z1), r1[e], p1[e]), acc[e]);
-        }
-      }
-    } else if constexpr (R1) {
-      // Biased operands; only row 0 of the product is real.
-      const auto biased = [&](uint32_t w) { return dequant8_biased(w, mr); };
-      typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-      // step j's two products (rows 0-3 and 4-7 of the lane's eight), operands broadcast
-      // from products 2j and 2j + 1 of the chunk
-      const auto mfma4 = [&](int j, f16x8 b8, f32x4 cc) {
-        const h4 b0 = __builtin_shufflevector(b8, b8, 0, 1, 2, 3);
-        const h4 b1 = __builtin_shufflevector(b8, b8, 4, 5, 6, 7);
-        const h4 a0 = __builtin_bit_cast(h4, ar[j >> 1]);
-        const h4 a1 = a0;
-        switch (j & 1) {  // ABID is an immediate: products 2j % 4 and 2j % 4 + 1
-          case 0:
-            cc = __builtin_amdgcn_mfma_f32_4x4x4f16(a0, b0, cc, 2, 0, 0);
-            return __builtin_amdgcn_mfma_f32_4x4x4f16(a1, b1, cc, 2, 1, 0);
-          default:
-            cc = __builtin_amdgcn_mfma_f32_4x4x4f16(a0, b0, cc, 2, 2, 0);
-            return __builtin_amdgcn_mfma_f32_4x4x4f16(a1, b1, cc, 2, 3, 0);
-        }
-      };
-      if constexpr (GPC <= 4) {
-#pragma unroll
-        for (int t = 0; t < GPC; ++t) {
-          f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int jj = 0; jj < JQ; ++jj) {
-            const int j = t * JQ + jj;
-            p = mfma4(j, biased(bw[i][0][j]), p);
-          }
-          float e;
-          if constexpr (HX)
-            e = ex[i][t];
-          else
-            e = excess(i, t);
-          acc[0] = __builtin_fmaf(sc[i][t], p[0] - e, acc[0]);
-        }
-      } else {
-        // 16-row units: the lane's eight rows of step j lie in unit 2j + (qd >> 1).
-        const int ubase = (half * span + gl[i]) * 8;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4 p = mfma4(j, biased(bw[i][0][j]), f32x4{0.f, 0.f, 0.f, 0.f});
-          const int t = 2 * j + (qd >> 1);
-          const float v = A::value(s_half[(ubase + t) * 16 + col]);
-          acc[0] = __builtin_fmaf(i < gw ? v : 0.f, p[0] - excess(i, t), acc[0]);
         }
       }
     } else if constexpr (GPC <= 4) {
@@ -577,7 +605,7 @@ hipError_t launch_small_stage(const uint16_t* a, int lda, int m, const uint32_t*
           a, lda, m, b, s, z, c, n, k, plan.splits, partials, stream);
     return hipErrorInvalidValue;
   }
-  if constexpr (!BF16 && !W8) {
+  if constexpr (!W8) {
     // One row (at most 64 groups: at most four slots per thread).
     if (m == 1) {
 #define WQ_SMALL1(ST)                                                                        \

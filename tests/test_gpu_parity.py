@@ -289,36 +289,27 @@ def test_prefill_config_matches_oracle_on_sampled_columns(dev):
 
 # --------------------------------------------------------------------------- pins
 
-# One-row fp16 products take the biased dequant: codes enter the MFMA as 1024 + q or 64 + q
-# and each lane's share of a scale unit has the activations' bias excess (computed apart
-# from the MFMA) subtracted before its scale.  Both are fp32 sums of terms up to 1039 |a|, so
-# the unrounded result is off by at most a few fp32 roundings of 1039 * sum |a| |s|: 24
-# roundings bound an eight-product MFMA chain, the excess's dot products and butterfly, the
-# subtraction, the scaled accumulation and the final adds over lanes and waves.
-ONE_ROW_ROUNDINGS = 24
-
-
-def one_row_bias_bound(case):
-    a = np.abs(case["a"].astype(np.float64))[0]
-    k = a.size
-    gs = case.get("group_size", 128)
-    gs = k if gs == -1 else gs
-    s_rows = np.abs(case["scales"].astype(np.float64))[np.arange(k) // gs]
-    return ONE_ROW_ROUNDINGS * 2.0 ** -24 * 1039.0 * (a @ s_rows)
-
-
 def test_all_eight_codes_give_exact_zero(dev):
-    for m in (16, 300):
+    for m in (1, 16, 300):
         case = synthetic.dense_case(m, 512, 256, seed=3)
         case["qweight"][:] = 0x88888888
         c = gpu_gemm(case, dev, fp32_reduce=True)
         assert np.all(c.astype(np.float64) == 0.0), m
-    # one row: the biased products and their excess cancel up to the bound above
-    case = synthetic.dense_case(1, 512, 256, seed=3)
-    case["qweight"][:] = 0x88888888
-    c = gpu_gemm(case, dev, fp32_reduce=True)[0].astype(np.float64)
-    bound = one_row_bias_bound(case)
-    assert np.all(np.abs(c) <= bound * (1 + 2.0 ** -10) + 2.0 ** -24)
+
+
+# One-row products run on 4x4x4 MFMAs, each lane summing its column over one row class of
+# every step, with the classes added by lane shuffles at the end.  With exact integer
+# weights the only errors are fp32 additions: every partial is a sum of at most
+# K exact products, added along a tree of depth below 64 (the 32-term chains of a unit, the
+# scaled fold over units, the shuffles and the four-wave reduction), so the unrounded
+# result is within 64 * 2^-24 * sum |a| |w| of the exact one.
+ACCUMULATION_ROUNDINGS = 64
+
+
+def accumulation_bound(case):
+    w = ref.w4a16_weights(case["qweight"], case["scales"], zeros=case.get("zeros"),
+                          group_size=case.get("group_size", 128))
+    return ACCUMULATION_ROUNDINGS * 2.0 ** -24 * (np.abs(case["a"].astype(np.float64)) @ np.abs(w))
 
 
 ONE_ROW_SHAPES = [
@@ -334,17 +325,18 @@ ONE_ROW_SHAPES = [
 
 
 @pytest.mark.parametrize("k,n,gs,zp,positive,split", ONE_ROW_SHAPES)
-def test_one_row_biased_dequant_within_its_bound(dev, k, n, gs, zp, positive, split):
+def test_one_row_within_rounding_of_the_exact_product(dev, k, n, gs, zp, positive, split):
     label = f"one row k={k} n={n} group_size={gs} zp={zp} positive={positive} split={split}"
     say(label)
     case = synthetic.dense_case(1, k, n, zp=zp, group_size=gs, seed=3900 + k + n + gs)
-    if positive:  # every activation of one sign: the largest bias sums for the result's size
+    if positive:  # every activation of one sign: the largest partial sums for the result
         case["a"] = np.abs(case["a"])
     c = gpu_gemm(case, dev, fp32_reduce=True, split_k=split)
     want = oracle_gemm(case)
     assert_parity(c, want, label)
     err = np.abs(c[0].astype(np.float64) - want[0])
-    allowed = 2.0 ** -11 * np.abs(want[0]) + one_row_bias_bound(case) * (1 + 2.0 ** -11) + 2.0 ** -25
+    allowed = (2.0 ** -11 * np.abs(want[0]) + accumulation_bound(case)[0] * (1 + 2.0 ** -11)
+               + 2.0 ** -25)
     assert np.all(err <= allowed), (label, float(np.max(err - allowed)))
 
 

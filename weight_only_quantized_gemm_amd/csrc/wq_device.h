@@ -62,18 +62,6 @@ __device__ __forceinline__ f16x8 dequant8(uint32_t w, ZeroOffsets zo, MagicRegs 
   return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// Biased fp16 dequant: the same OR as dequant8 without the subtraction, so a word's eight
-// rows enter the MFMA as 1024 + q (rows 0, 1, 4, 5 of the eight) and 64 + q (rows 2, 3, 6,
-// 7).  A product over such operands exceeds the exact one by the activations weighted with
-// these biases plus z times the activation sum, a term that does not depend on the weights
-// and is subtracted once per scale unit.
-__device__ __forceinline__ f16x8 dequant8_biased(uint32_t w, MagicRegs mr) {
-  const uint32_t w8 = w >> 8;
-  return __builtin_bit_cast(f16x8, u32x4{(w & 0x000F000Fu) | mr.m1024, (w & 0x00F000F0u) | mr.m64,
-                                         (w8 & 0x000F000Fu) | mr.m1024,
-                                         (w8 & 0x00F000F0u) | mr.m64});
-}
-
 // Zero-point code of column c (0..15) of a 16-column block: two words, 8 codes each.
 __device__ __forceinline__ int zero_code(u32x2 zw, int c) {
   const uint32_t w = (c < 8) ? zw[0] : zw[1];

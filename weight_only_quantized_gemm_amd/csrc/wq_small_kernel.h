@@ -23,23 +23,20 @@
 // group), converted to the activation type two bytes per instruction.
 //
 // R1 (one activation row, 4-bit weights) is a leaner loop for the decode case:
-//  - Biased dequant: each word's rows enter the MFMA as 1024 + q or 64 + q (one OR each, no
-//    subtraction), four of the nine VALU operations per word saved.  bf16 activations take
-//    128 + q for every row (as on their general path).
 //  - 4x4x4 MFMAs (16 blocks): with one real row the 16x16x32 product wastes 15 of its 16
 //    rows, and two 4x4x4 products carry the same 512 weights in less MFMA time.  Block b of
 //    a lane pair (col, qd) holds columns 4(b % 4).. and the lane's eight rows of the step, so
 //    each lane keeps its own column's sum over its row class qd (rows 8qd..8qd+7 of every
-//    32-row step); two shuffles add the four classes at the end.  A 16-row unit is then the
-//    lane's own, and the masked double product of GPC = 8 is not needed.
-//  - The excess the biases leave, the activations weighted by them plus z times their sum
-//    ((128 + z) times the sum for bf16), depends on the activations alone: the staging threads form it per unit and row class
-//    while the weights are in flight, and each lane subtracts its own before the unit's
-//    scale.  Only the real output row is scaled and accumulated.
-// Both the biased product and the excess are fp32 sums of terms up to 1039 |a| over the
-// lane's rows of a unit, so their difference carries a few fp32 roundings of that size: a
-// small fraction of the fp16 rounding of the result for signed activations, less than it
-// when all are positive.
+//    32-row step); two shuffles add the four classes at the end.  A 16-row unit then lies in
+//    the lane's own rows, and the masked double product of GPC = 8 is not needed.
+//  - Activation broadcast: one block's A operand serves the four blocks of a row class, so
+//    a lane reads two 4-row activation pieces per chunk instead of sixteen rows.
+//  - Only the real output row is scaled and accumulated.
+// fp16 keeps the exact dequant, so results are as exact as on the general path (all-zero
+// weights give exactly zero).  bf16, which has no packed add, takes 128 + q for every row as
+// on its general path; the excess (128 + z) times the activations' sum over the lane's rows
+// of a unit depends on the activations alone, and the staging threads form the sums per
+// unit and row class from the slice while the weights are in flight.
 //
 // This header holds the kernel template and its launch chain; each translation unit that
 // includes it instantiates one GPC and activation type, so that the instances compile in
@@ -74,7 +71,7 @@ constexpr long small_static_lds(int waves, bool pair, int gpc, bool r1) {
   return (long)small_scale_slots(waves, pair, gpc) * waves * 64 * 4    // s_lds
          + (long)small_zero_slots(waves, pair, gpc) * waves * 64 * 8   // z_lds
          + (long)waves * 64 * 16                                       // red
-         + (r1 ? (long)kMaxSpan * 16 * 2 * 4 : 0);                     // corr_lds, rsum_lds
+         + (r1 ? (long)kMaxSpan * 16 * 4 : 0);                         // rsum_lds
 }
 
 // The kernel body is branch-free up to the arithmetic: every load is issued
@@ -115,9 +112,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   __shared__ f32x4 red[WAVES][64];
   // R1: per scale unit of the slice, the activations weighted by the operand biases (plus
   // 8 of each without zero points) and, with zero points, their plain sum.
-  constexpr int EX = GPC == 8 ? 2 : 4;  // excess slots per scale unit: one per row class
-  __shared__ float corr_lds[R1 && !BF16 ? kMaxSpan * GPC * EX : 1];
-  __shared__ float rsum_lds[R1 && (ZP || BF16) ? kMaxSpan * GPC * EX : 1];
+  constexpr int EX = GPC == 8 ? 2 : 4;  // activation sums per scale unit: one per row class
+  constexpr bool R1B = R1 && BF16;      // one row with biased bf16 operands
+  __shared__ float rsum_lds[R1B ? kMaxSpan * GPC * EX : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -145,13 +142,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   int q = tid - r * per_row;
   const f16* a_base = a + (long)gs0 * kGroup;
   f16x8 stage[DA ? 1 : STAGE];
-  int stage_q[R1 ? STAGE : 1];        // R1: granule column of each slot
-  bool stage_real[R1 ? STAGE : 1];    // R1: the slot lies inside the slice
+  int stage_q[R1B ? STAGE : 1];        // granule column of each slot
+  bool stage_real[R1B ? STAGE : 1];    // the slot lies inside the slice
   if constexpr (!DA) {
 #pragma unroll
     for (int u = 0; u < STAGE; ++u) {
       const int rr = r < m ? r : m - 1;
-      if constexpr (R1) {
+      if constexpr (R1B) {
         stage_q[u] = q;
         stage_real[u] = r < m;
       }
@@ -218,55 +215,27 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
     for (int u = 0; u < ZU; ++u) z_lds[tid + u * T] = z_stage[u];
   }
-  if constexpr (R1) {
+  if constexpr (R1B) {
     // A unit of the slice is GR consecutive granules, held by GR consecutive lanes of one
     // slot (aligned, since T and the row length are multiples of 16); granule q of a chunk
-    // is row class q % 4 of step q / 4.  Each lane weights its eight activations by the
-    // biases of their rows (1024 for rows 0, 1, 4, 5 of the eight, 64 for rows 2, 3, 6, 7),
-    // a butterfly adds the lanes of one class (or, for 16-row units, none), and the first
-    // EX lanes of the unit store per class (per granule) at unit * EX + class.
+    // is row class q % 4 of step q / 4.  Each lane adds its eight activations, a butterfly
+    // adds the lanes of one class (none for 16-row units), and the first EX lanes of the
+    // unit store per class (per granule) at unit * EX + class.
     constexpr int GR = 16 / GPC;
-    constexpr bool WSUM = !BF16;       // bias-weighted sum (fp16's two biases)
-    constexpr bool PSUM = ZP || BF16;  // plain sum
-    const f16x2 b_hi = ZP ? f16x2{1024, 1024} : f16x2{1032, 1032};  // + 8 for u4b8
-    const f16x2 b_lo = ZP ? f16x2{64, 64} : f16x2{72, 72};
-    const f16x2 ones = f16x2{1, 1};
 #pragma unroll
     for (int u = 0; u < STAGE; ++u) {
-      const f16x8 v = stage[u];
-      float cb = 0.f, rs = 0.f;
-      if constexpr (BF16) {
-        // each bf16 is the upper half of a binary32 (the bf16 dot-product builtin on words
-        // reinterpreted as bf16 pairs is miscompiled by this toolchain: it reads word 0 four
-        // times)
-        const u32x4 w = __builtin_bit_cast(u32x4, v);
+      // each bf16 is the upper half of a binary32 (the bf16 dot-product builtin on words
+      // reinterpreted as bf16 pairs is miscompiled by this toolchain: it reads word 0 four
+      // times)
+      const u32x4 w = __builtin_bit_cast(u32x4, stage[u]);
+      float rs = 0.f;
 #pragma unroll
-        for (int h = 0; h < 4; ++h)
-          rs += __builtin_bit_cast(float, w[h] << 16) +
-                __builtin_bit_cast(float, w[h] & 0xFFFF0000u);
-      } else {
-        const f16x2 v01{v[0], v[1]}, v23{v[2], v[3]}, v45{v[4], v[5]}, v67{v[6], v[7]};
-        cb = __builtin_amdgcn_fdot2(v01, b_hi, cb, false);
-        cb = __builtin_amdgcn_fdot2(v23, b_lo, cb, false);
-        cb = __builtin_amdgcn_fdot2(v45, b_hi, cb, false);
-        cb = __builtin_amdgcn_fdot2(v67, b_lo, cb, false);
-        if constexpr (ZP) {
-          rs = __builtin_amdgcn_fdot2(v01, ones, rs, false);
-          rs = __builtin_amdgcn_fdot2(v23, ones, rs, false);
-          rs = __builtin_amdgcn_fdot2(v45, ones, rs, false);
-          rs = __builtin_amdgcn_fdot2(v67, ones, rs, false);
-        }
-      }
+      for (int h = 0; h < 4; ++h)
+        rs += __builtin_bit_cast(float, w[h] << 16) + __builtin_bit_cast(float, w[h] & 0xFFFF0000u);
 #pragma unroll
-      for (int d = EX; d < GR; d *= 2) {
-        if constexpr (WSUM) cb += __shfl_xor(cb, d);
-        if constexpr (PSUM) rs += __shfl_xor(rs, d);
-      }
-      if (stage_real[u] && (tid & (GR - 1)) < EX) {
-        const int slot = stage_q[u] / GR * EX + stage_q[u] % EX;
-        if constexpr (WSUM) corr_lds[slot] = cb;
-        if constexpr (PSUM) rsum_lds[slot] = rs;
-      }
+      for (int d = EX; d < GR; d *= 2) rs += __shfl_xor(rs, d);
+      if (stage_real[u] && (tid & (GR - 1)) < EX)
+        rsum_lds[stage_q[u] / GR * EX + stage_q[u] % EX] = rs;
     }
   }
   __syncthreads();
@@ -300,20 +269,21 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
       }
     }
   }
-  // R1: the bias excess of unit t of step i, for this lane's column and row class.
+  // unit t of step i: its zero point for this lane's column
+  const auto zero_of = [&](int i, int t) {
+    return ZP ? zero_code(z_lds[(half * span + gl[i]) * GPC + t], col) : 8;
+  };
+  // R1 bf16: the bias excess of unit t of step i, for this lane's column and row class.
   const auto excess = [&](int i, int t) -> float {
     const int unit = gl[i] * GPC + t;
     const int slot = GPC == 8 ? unit * 2 + (qd & 1) : unit * 4 + qd;
-    const float zf = ZP ? (float)zero_code(z_lds[(half * span + gl[i]) * GPC + t], col) : 8.f;
-    if constexpr (BF16) return (128.f + zf) * rsum_lds[slot];
-    if constexpr (ZP) return __builtin_fmaf(zf, rsum_lds[slot], corr_lds[slot]);
-    return corr_lds[slot];
+    return (128.f + (float)zero_of(i, t)) * rsum_lds[slot];
   };
   // Hoisted with the scales for up to two units per chunk; with more, the registers would
   // cost a wave of occupancy, so the excess is read in place.
   constexpr bool HX = GPC <= 2;
-  float ex[R1 && HX ? GW : 1][R1 && HX ? HS : 1];
-  if constexpr (R1 && HX) {
+  float ex[R1B && HX ? GW : 1][R1B && HX ? HS : 1];
+  if constexpr (R1B && HX) {
 #pragma unroll
     for (int i = 0; i < GW; ++i) {
 #pragma unroll
@@ -370,12 +340,22 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sc[i][0], p[e], acc[e]);
     } else if constexpr (R1) {
-      // Biased operands; only row 0 of the product is real.
-      const auto biased = [&](uint32_t w) {
+      // Only row 0 of the product is real.  Operands of unit t: exact (q - z) for fp16,
+      // biased 128 + q for bf16.
+      const auto operand = [&](uint32_t w, int t) {
         if constexpr (BF16)
           return __builtin_bit_cast(u32x4, dequant8_bf_biased(w, mr));
         else
-          return __builtin_bit_cast(u32x4, dequant8_biased(w, mr));
+          return __builtin_bit_cast(u32x4, dequant8(w, zero_offsets(zero_of(i, t)), mr));
+      };
+      // the bias excess to remove from unit t's product (none for fp16)
+      const auto unit_excess = [&](int t) -> float {
+        if constexpr (!BF16)
+          return 0.f;
+        else if constexpr (HX)
+          return ex[i][t];
+        else
+          return excess(i, t);
       };
       // one 4x4x4 product (16 blocks) on four rows; the operand broadcast ID is an immediate
       const auto mfma1 = [](u32x2 a2, u32x2 b2, f32x4 cc, auto abid) {
@@ -408,24 +388,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
           for (int jj = 0; jj < JQ; ++jj) {
             const int j = t * JQ + jj;
-            p = mfma4(j, biased(bw[i][0][j]), p);
+            p = mfma4(j, operand(bw[i][0][j], t), p);
           }
-          float e;
-          if constexpr (HX)
-            e = ex[i][t];
-          else
-            e = excess(i, t);
-          acc[0] = __builtin_fmaf(sc[i][t], p[0] - e, acc[0]);
+          acc[0] = __builtin_fmaf(sc[i][t], BF16 ? p[0] - unit_excess(t) : p[0], acc[0]);
         }
       } else {
         // 16-row units: the lane's eight rows of step j lie in unit 2j + (qd >> 1).
         const int ubase = (half * span + gl[i]) * 8;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const f32x4 p = mfma4(j, biased(bw[i][0][j]), f32x4{0.f, 0.f, 0.f, 0.f});
           const int t = 2 * j + (qd >> 1);
+          const f32x4 p = mfma4(j, operand(bw[i][0][j], t), f32x4{0.f, 0.f, 0.f, 0.f});
           const float v = A::value(s_half[(ubase + t) * 16 + col]);
-          acc[0] = __builtin_fmaf(i < gw ? v : 0.f, p[0] - excess(i, t), acc[0]);
+          acc[0] = __builtin_fmaf(i < gw ? v : 0.f, BF16 ? p[0] - excess(i, t) : p[0], acc[0]);
         }
       }
     } else if constexpr (BF16) {

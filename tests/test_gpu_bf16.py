@@ -86,6 +86,9 @@ BF16_SHAPES = [
     # 9..16 rows with activation operands in registers
     (9, 2048, 256, 128, True, False, False, 0),
     (13, 1024, 512, 16, False, False, True, 2),
+    # two column blocks per wave
+    (16, 1024, 8192, 128, True, False, False, 0),
+    (10, 2048, 8192, 16, False, False, True, 0),
 ]
 
 

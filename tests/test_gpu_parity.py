@@ -223,7 +223,8 @@ def test_small_m_group_sizes_match_oracle(dev, m, k, n, gs, zp, act_order, fp32,
 
 
 # 9..16 rows: the small-M kernel loads each wave's activation operands straight into
-# registers (no LDS slice) when a wave holds at most 4 groups.
+# registers (no LDS slice) when a wave holds at most 4 groups; with enough column blocks
+# each wave applies them to two blocks.
 DIRECT_SHAPES = [
     # m, k, n, group_size, zp, act_order, fp32_reduce, split_k
     (9, 4096, 256, 16, True, False, False, 0),
@@ -231,6 +232,12 @@ DIRECT_SHAPES = [
     (13, 2048, 256, 64, True, False, True, 2),
     (16, 512, 256, -1, False, False, False, 0),
     (10, 4096, 512, 32, False, False, True, 4),
+    # two column blocks per wave (at least 256 work-groups of two blocks)
+    (16, 1024, 8192, 128, True, False, True, 0),
+    (9, 2048, 8192, 16, True, False, False, 0),
+    (12, 4096, 1024, 64, False, True, True, 8),
+    (11, 1024, 8192, 32, False, False, False, 0),
+    (14, 768, 8192, -1, True, False, False, 0),
 ]
 
 

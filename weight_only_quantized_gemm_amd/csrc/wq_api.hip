@@ -94,6 +94,11 @@ bool plan_small_pair(int m, int k, int gpc, wq::SmallPlan* plan) {
 }
 
 constexpr int kDirectRows = 9;
+// Two column blocks per wave halve the activation reads of the direct form but halve its
+// work-groups too.  Measured on MI355X at M=16, K=4096 with zero points: N=4096 (128
+// paired work-groups) 8.1 against 6.4 us; N=8192 (256) 9.0 against 10.6 us; N=14336 (448)
+// 13.6 against 18.1 us.
+constexpr int kDualMinGroups = 256;
 
 bool plan_small(int m, int n, int k, uint32_t flags, int requested, int gpc,
                 wq::SmallPlan* plan) {
@@ -123,6 +128,10 @@ bool plan_small(int m, int n, int k, uint32_t flags, int requested, int gpc,
         p.depth = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 8;
         p.gpc = gpc;
         p.direct = pass == 0;
+        // Direct activations are read by every work-group in full; pairing two column
+        // blocks per wave halves those reads while at least kDualMinGroups work-groups
+        // remain (E4M3 weights excepted).
+        p.dual = p.direct && !(flags & WQ_FLAG_FP8) && (n / 32) * s >= kDualMinGroups;
         if (wq::small_plan_fits(m, k, p)) {
           *plan = p;
           return true;

@@ -76,13 +76,14 @@ bool small_plan_fits(int m, int k, const SmallPlan& plan) {
   const int kw = plan.pair ? plan.waves / 2 : plan.waves;  // waves along K per block
   if (span > kMaxSpan || min_span < kw) return false;   // every wave has a group
   if ((span + kw - 1) / kw > plan.depth || plan.depth > 8) return false;
+  if (plan.dual && !plan.direct) return false;
   if (plan.direct)  // no activation slice; the operands of at most 4 groups in registers
     return plan.depth <= 4 && !plan.pair &&
-           small_static_lds(plan.waves, plan.pair, plan.gpc, false) <= kLdsBytes;
+           small_static_lds(plan.waves, plan.pair, plan.gpc, false, plan.dual) <= kLdsBytes;
   const int slots = stage_slots(m, span, plan.waves);
   const long dynamic = (long)round_slots(slots) * plan.waves * 64 * (long)sizeof(f16x8);
   return slots <= 16 &&
-         dynamic + small_static_lds(plan.waves, plan.pair, plan.gpc, m == 1) <= kLdsBytes;
+         dynamic + small_static_lds(plan.waves, plan.pair, plan.gpc, m == 1, false) <= kLdsBytes;
 }
 
 hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* b,

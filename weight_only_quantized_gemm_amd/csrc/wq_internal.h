@@ -51,6 +51,8 @@ struct SmallPlan {
   int gpc;         // scale units per 128-row chunk: 1, 2, 4 or 8 (units of 128/gpc rows)
   bool direct;     // activation operands loaded straight into registers, no LDS slice
                    // (depth <= 4, not with pair)
+  bool dual;       // direct only: each wave covers two adjacent column blocks, reading the
+                   // activations once for both (4-bit weights)
 };
 bool small_plan_fits(int m, int k, const SmallPlan& plan);
 // bf16: A, s and c hold bf16 values (else fp16).  fp8: b holds E4M3 weights in the FP8

@@ -67,11 +67,12 @@ constexpr int small_zero_slots(int waves, bool pair, int gpc) {
              ? (pair ? 2 : 1) * kMaxSpan * gpc / (waves * 64) : 1;
 }
 // Static LDS of an instance (see the kernel's __shared__ arrays), an upper bound over ZP.
-constexpr long small_static_lds(int waves, bool pair, int gpc, bool r1) {
-  return (long)small_scale_slots(waves, pair, gpc) * waves * 64 * 4    // s_lds
-         + (long)small_zero_slots(waves, pair, gpc) * waves * 64 * 8   // z_lds
-         + (long)waves * 64 * 16                                       // red
-         + (r1 ? (long)kMaxSpan * 16 * 4 : 0);                         // rsum_lds
+// (pair: two column blocks split between the waves; dual: two column blocks per wave)
+constexpr long small_static_lds(int waves, bool pair, int gpc, bool r1, bool dual) {
+  return (long)small_scale_slots(waves, pair || dual, gpc) * waves * 64 * 4    // s_lds
+         + (long)small_zero_slots(waves, pair || dual, gpc) * waves * 64 * 8   // z_lds
+         + (long)(dual ? 2 : 1) * waves * 64 * 16                              // red
+         + (r1 ? (long)kMaxSpan * 16 * 4 : 0);                                 // rsum_lds
 }
 
 // The kernel body is branch-free up to the arithmetic: every load is issued
@@ -84,7 +85,7 @@ constexpr long small_static_lds(int waves, bool pair, int gpc, bool r1) {
 // block, the second half the up block, both over the same K range and staged activations,
 // and the reduction writes fp16(silu(g) * u) to column 16t + c of the [m][n/2] activation.
 template <bool ZP, int WAVES, int GW, int STAGE, bool PAIR, int GPC, bool BF16, bool W8,
-          bool R1>
+          bool R1, bool DUAL>
 __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     const f16* __restrict__ a, int lda, int m, const u32x4* __restrict__ b,
     const uint16_t* __restrict__ s, const u32x2* __restrict__ z, uint16_t* __restrict__ c,
@@ -98,18 +99,22 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   constexpr bool DA = STAGE == 0;
   static_assert(!DA || (GW <= 4 && !PAIR), "direct activations: at most 4 groups, no pair");
   static_assert(!R1 || (!DA && !W8), "biased dequant: staged activations, 4-bit weights");
+  // DUAL: each wave applies its activation operands to two adjacent column blocks, so the
+  // activations are read once per two blocks (direct activations, 4-bit weights).
+  static_assert(!DUAL || (DA && !PAIR && !W8 && !R1), "dual blocks: direct activations");
   constexpr int T = WAVES * 64;
-  constexpr int NB = PAIR ? 2 : 1;            // column blocks of the work-group
-  constexpr int KW = WAVES / NB;              // waves splitting K for one block
-  constexpr int SU = small_scale_slots(WAVES, PAIR, GPC);  // staged scale dwords per thread
-  constexpr int ZU = small_zero_slots(WAVES, PAIR, GPC);   // staged zero points per thread
+  constexpr int NB = (PAIR || DUAL) ? 2 : 1;  // column blocks of the work-group
+  constexpr int NBV = DUAL ? 2 : 1;           // column blocks of each wave
+  constexpr int KW = PAIR ? WAVES / 2 : WAVES;  // waves splitting K for one block
+  constexpr int SU = small_scale_slots(WAVES, PAIR || DUAL, GPC);  // staged scale dwords
+  constexpr int ZU = small_zero_slots(WAVES, PAIR || DUAL, GPC);   // staged zero points
   constexpr int JQ = GPC <= 4 ? 4 / GPC : 1;  // 32-row MFMA steps per scale unit (GPC <= 4)
   static_assert(SU >= 1 && SU * T == NB * kMaxSpan * 8 * GPC, "scale slots cover the range");
   static_assert(ZU * T >= NB * kMaxSpan * GPC, "zero-point slots cover the range");
   extern __shared__ f16x8 a_lds[];            // [m][span*16] granules (+ padding)
   __shared__ uint32_t s_lds[SU * T];          // scales, [block][chunk][unit][col] as fp16
   __shared__ u32x2 z_lds[ZP ? ZU * T : 1];    // zero points, [block][chunk][unit]
-  __shared__ f32x4 red[WAVES][64];
+  __shared__ f32x4 red[NBV][WAVES][64];
   // R1: per scale unit of the slice, the activations weighted by the operand biases (plus
   // 8 of each without zero points) and, with zero points, their plain sum.
   constexpr int EX = GPC == 8 ? 2 : 4;  // activation sums per scale unit: one per row class
@@ -171,7 +176,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   for (int u = 0; u < SU; ++u) {
     int i = tid + u * T;
     i = i < NB * s_words ? i : NB * s_words - 1;
-    const int h = PAIR && i >= s_words ? 1 : 0;  // block of the pair holding dword i
+    const int h = NB == 2 && i >= s_words ? 1 : 0;  // block of the pair holding dword i
     s_stage[u] = s32[(pair0 + h * units) * 8 + (i - h * s_words)];
   }
   u32x2 z_stage[ZU];
@@ -182,21 +187,22 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
       const int z_words = span * GPC;
       int i = tid + u * T;
       i = i < NB * z_words ? i : NB * z_words - 1;
-      const int h = PAIR && i >= z_words ? 1 : 0;
+      const int h = NB == 2 && i >= z_words ? 1 : 0;
       z_stage[u] = z[pair0 + h * units + (i - h * z_words)];
     }
   }
 
   // 3. The wave's weight chunks, all in flight before any arithmetic.
-  u32x4 bw[GW][NV];
+  u32x4 bw[GW][NV * NBV];  // E4M3: the group's two vectors; DUAL: the two blocks' chunks
   f16x8 ag[DA ? GW : 1][4];  // STAGE 0: the lane's activation operands of each group
   const f16* a_row = a + (long)(col < m ? col : m - 1) * lda + 8 * qd;
 #pragma unroll
   for (int i = 0; i < GW; ++i) {
     const int g = g0 + (i < gw ? i : gw - 1);
 #pragma unroll
-    for (int v = 0; v < NV; ++v)
-      bw[i][v] = __builtin_nontemporal_load(&b[(((long)nb * groups + g) * NV + v) * 64 + lane]);
+    for (int v = 0; v < NV * NBV; ++v)
+      bw[i][v] = __builtin_nontemporal_load(
+          &b[(DUAL ? (long)(nb + v) * groups + g : ((long)nb * groups + g) * NV + v) * 64 + lane]);
     if constexpr (DA) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -257,18 +263,23 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   const uint16_t* s_half = reinterpret_cast<const uint16_t*>(s_lds);
   int gl[GW];  // chunk of step i inside the staged range (clamped for the masked steps)
   constexpr int HS = GPC <= 4 ? GPC : 1;  // scales hoisted per chunk (read in place for 8)
-  float sc[GW][HS];
+  float scs[NBV][GW][HS];                   // per column block of the wave
 #pragma unroll
   for (int i = 0; i < GW; ++i) {
     gl[i] = g0 - gs0 + (i < gw ? i : gw - 1);
     if constexpr (GPC <= 4) {
 #pragma unroll
-      for (int t = 0; t < GPC; ++t) {
-        const float v = A::value(s_half[((half * span + gl[i]) * GPC + t) * 16 + col]);
-        sc[i][t] = i < gw ? v : 0.f;
+      for (int v = 0; v < NBV; ++v) {
+        const int hv = DUAL ? v : half;
+#pragma unroll
+        for (int t = 0; t < GPC; ++t) {
+          const float x = A::value(s_half[((hv * span + gl[i]) * GPC + t) * 16 + col]);
+          scs[v][i][t] = i < gw ? x : 0.f;
+        }
       }
     }
   }
+  auto& sc = scs[0];  // the scales of the wave's only (or first) block
   // unit t of step i: its zero point for this lane's column
   const auto zero_of = [&](int i, int t) {
     return ZP ? zero_code(z_lds[(half * span + gl[i]) * GPC + t], col) : 8;
@@ -310,7 +321,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) an[j] = a_lds[arow + gl[0] * 16 + 4 * j + qd];
   }
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 accs[NBV];
+#pragma unroll
+  for (int v = 0; v < NBV; ++v) accs[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int half0 = half;
 #pragma unroll
   for (int i = 0; i < GW; ++i) {
     f16x8 ac[R1 ? 1 : 4];
@@ -330,6 +344,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     // With eight groups per wave, pin the prefetch ahead of this group's work (measured
     // faster for the decode shape, slower for shallower pipelines).
     if constexpr (GW >= 8) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int v = 0; v < NBV; ++v) {
+    // the wave's block v: its place in the staged scales and zero points, its weights and sums
+    const int half = DUAL ? v : half0;
+    const int bv = DUAL ? v : 0;
+    f32x4& acc = accs[v];
+    auto& sc = scs[v];
     if constexpr (W8) {
       // 32-row step j: vector j / 2, words 2(j % 2) and 2(j % 2) + 1 (rows 0-3 and 4-7).
       f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -388,7 +409,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
           for (int jj = 0; jj < JQ; ++jj) {
             const int j = t * JQ + jj;
-            p = mfma4(j, operand(bw[i][0][j], t), p);
+            p = mfma4(j, operand(bw[i][bv][j], t), p);
           }
           acc[0] = __builtin_fmaf(sc[i][t], BF16 ? p[0] - unit_excess(t) : p[0], acc[0]);
         }
@@ -398,7 +419,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int t = 2 * j + (qd >> 1);
-          const f32x4 p = mfma4(j, operand(bw[i][0][j], t), f32x4{0.f, 0.f, 0.f, 0.f});
+          const f32x4 p = mfma4(j, operand(bw[i][bv][j], t), f32x4{0.f, 0.f, 0.f, 0.f});
           const float v = A::value(s_half[(ubase + t) * 16 + col]);
           acc[0] = __builtin_fmaf(i < gw ? v : 0.f, BF16 ? p[0] - excess(i, t) : p[0], acc[0]);
         }
@@ -421,7 +442,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
           for (int jj = 0; jj < JQ; ++jj) {
             const int j = t * JQ + jj;
-            p = A::mfma16(ac[j], dequant8_bf_biased(bw[i][0][j], mr), p);
+            p = A::mfma16(ac[j], dequant8_bf_biased(bw[i][bv][j], mr), p);
             r = A::mfma16(ac[j], ones, r);
           }
 #pragma unroll
@@ -435,7 +456,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
         const bf16x8 zero8{};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const bf16x8 w = dequant8_bf_biased(bw[i][0][j], mr);
+          const bf16x8 w = dequant8_bf_biased(bw[i][bv][j], mr);
           const f32x4 p0 = A::mfma16(ac[j], hi ? zero8 : w, zero4);
           const f32x4 p1 = A::mfma16(ac[j], hi ? w : zero8, zero4);
           const f32x4 r0 = A::mfma16(ac[j], hi ? zero8 : ones, zero4);
@@ -462,7 +483,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
         for (int jj = 0; jj < JQ; ++jj) {
           const int j = t * JQ + jj;
-          p = A::mfma16(ac[j], A::dequant(bw[i][0][j], zo, mr), p);
+          p = A::mfma16(ac[j], A::dequant(bw[i][bv][j], zo, mr), p);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sc[i][t], p[e], acc[e]);
@@ -476,7 +497,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const auto zo = A::zero(ZP ? zero_code(z_lds[ubase + 2 * j + hi], col) : 8);
-        const typename A::W8 w = A::dequant(bw[i][0][j], zo, mr);
+        const typename A::W8 w = A::dequant(bw[i][bv][j], zo, mr);
         const f32x4 p0 = A::mfma16(ac[j], hi ? zero8 : w, f32x4{0.f, 0.f, 0.f, 0.f});
         const f32x4 p1 = A::mfma16(ac[j], hi ? w : zero8, f32x4{0.f, 0.f, 0.f, 0.f});
         // (the reads are unconditional, in bounds through the clamped chunk; a masked step
@@ -491,24 +512,26 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
         for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(s1, p1[e], acc[e]);
       }
     }
+    }  // blocks of the wave
     if constexpr (GW >= 8) __builtin_amdgcn_sched_barrier(0);
   }
 
   if constexpr (R1) {
     // each lane holds its column's sum over one of the four row classes of every step
-    acc[0] += __shfl_xor(acc[0], 16);
-    acc[0] += __shfl_xor(acc[0], 32);
+    accs[0][0] += __shfl_xor(accs[0][0], 16);
+    accs[0][0] += __shfl_xor(accs[0][0], 32);
   }
   // Work-group reduce over the waves, in wave order.
-  red[wave][lane] = acc;
+#pragma unroll
+  for (int v = 0; v < NBV; ++v) red[v][wave][lane] = accs[v];
   __syncthreads();
   if (wave != 0) return;
   if constexpr (PAIR) {
-    f32x4 gs = red[0][lane], us = red[KW][lane];
+    f32x4 gs = red[0][0][lane], us = red[0][KW][lane];
 #pragma unroll
     for (int w = 1; w < KW; ++w) {
-      gs += red[w][lane];
-      us += red[KW + w][lane];
+      gs += red[0][w][lane];
+      us += red[0][KW + w][lane];
     }
     const long colj = (long)blockIdx.x * 16 + col;  // column of the [m][n/2] activation
 #pragma unroll
@@ -518,20 +541,23 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     }
     return;
   }
-  f32x4 tot = red[0][lane];
 #pragma unroll
-  for (int w = 1; w < WAVES; ++w) tot += red[w][lane];
+  for (int v = 0; v < NBV; ++v) {
+    f32x4 tot = red[v][0][lane];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) tot += red[v][w][lane];
 
-  // Output layout of the 16x16 block: lane holds rows 4*qd + e of column `col`.
-  const long colx = (long)nb * 16 + col;
+    // Output layout of the 16x16 block: lane holds rows 4*qd + e of column `col`.
+    const long colx = (long)(nb + v) * 16 + col;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int row = 4 * qd + e;
-    if (row >= m) continue;
-    if (splits == 1)
-      c[(long)row * n + colx] = A::round(tot[e]);
-    else
-      partials[((long)split * m + row) * n + colx] = tot[e];
+    for (int e = 0; e < 4; ++e) {
+      const int row = 4 * qd + e;
+      if (row >= m) continue;
+      if (splits == 1)
+        c[(long)row * n + colx] = A::round(tot[e]);
+      else
+        partials[((long)split * m + row) * n + colx] = tot[e];
+    }
   }
 }
 
@@ -547,7 +573,7 @@ inline int round_slots(int slots) {
 }
 
 template <bool ZP, int WAVES, int GW, int STAGE, bool PAIR, int GPC, bool BF16, bool W8,
-          bool R1>
+          bool R1, bool DUAL>
 hipError_t launch_small_t(const uint16_t* a, int lda, int m, const uint32_t* b,
                           const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                           int splits, float* partials, hipStream_t stream) {
@@ -556,11 +582,11 @@ hipError_t launch_small_t(const uint16_t* a, int lda, int m, const uint32_t* b,
   constexpr size_t lds = (size_t)STAGE * WAVES * 64 * sizeof(f16x8);
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(
-          &gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16, W8, R1>),
+          &gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16, W8, R1, DUAL>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
-  const dim3 grid(n / (PAIR ? 32 : 16), splits);
-  hipLaunchKernelGGL((gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16, W8, R1>), grid,
+  const dim3 grid(n / (PAIR || DUAL ? 32 : 16), splits);
+  hipLaunchKernelGGL((gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16, W8, R1, DUAL>), grid,
                      dim3(WAVES * 64), lds, stream, reinterpret_cast<const f16*>(a), lda, m,
                      reinterpret_cast<const u32x4*>(b), s, reinterpret_cast<const u32x2*>(z), c,
                      n, groups, splits, partials);
@@ -575,17 +601,23 @@ hipError_t launch_small_stage(const uint16_t* a, int lda, int m, const uint32_t*
                               const SmallPlan& plan, float* partials, hipStream_t stream) {
   const int span = (k / kGroup + plan.splits - 1) / plan.splits;
   if (plan.direct) {
-    if constexpr (GW <= 4 && !PAIR)
-      return launch_small_t<ZP, WAVES, GW, 0, PAIR, GPC, BF16, W8, false>(
+    if constexpr (GW <= 4 && !PAIR) {
+      if constexpr (!W8) {
+        if (plan.dual)
+          return launch_small_t<ZP, WAVES, GW, 0, PAIR, GPC, BF16, W8, false, true>(
+              a, lda, m, b, s, z, c, n, k, plan.splits, partials, stream);
+      }
+      return launch_small_t<ZP, WAVES, GW, 0, PAIR, GPC, BF16, W8, false, false>(
           a, lda, m, b, s, z, c, n, k, plan.splits, partials, stream);
+    }
     return hipErrorInvalidValue;
   }
   if constexpr (!W8) {
     // One row (at most 64 groups: at most four slots per thread).
     if (m == 1) {
 #define WQ_SMALL1(ST)                                                                        \
-  launch_small_t<ZP, WAVES, GW, ST, PAIR, GPC, BF16, W8, true>(a, lda, m, b, s, z, c, n, k,  \
-                                                               plan.splits, partials, stream)
+  launch_small_t<ZP, WAVES, GW, ST, PAIR, GPC, BF16, W8, true, false>(                        \
+      a, lda, m, b, s, z, c, n, k, plan.splits, partials, stream)
       switch (round_slots(stage_slots(m, span, WAVES))) {
         case 1: return WQ_SMALL1(1);
         case 2: return WQ_SMALL1(2);
@@ -596,8 +628,8 @@ hipError_t launch_small_stage(const uint16_t* a, int lda, int m, const uint32_t*
     }
   }
 #define WQ_SMALL(ST)                                                                         \
-  launch_small_t<ZP, WAVES, GW, ST, PAIR, GPC, BF16, W8, false>(a, lda, m, b, s, z, c, n, k, \
-                                                                plan.splits, partials, stream)
+  launch_small_t<ZP, WAVES, GW, ST, PAIR, GPC, BF16, W8, false, false>(                       \
+      a, lda, m, b, s, z, c, n, k, plan.splits, partials, stream)
   switch (round_slots(stage_slots(m, span, WAVES))) {
     case 1: return WQ_SMALL(1);
     case 2: return WQ_SMALL(2);

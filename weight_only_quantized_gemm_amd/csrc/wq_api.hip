@@ -486,10 +486,10 @@ int wq_grouped_gemm(const wq_grouped_args* args) {
   if (p.b_stride_bytes < b_bytes || p.b_stride_bytes % 16 || p.s_stride_bytes < s_bytes ||
       p.s_stride_bytes % 16 || (has_zp && (p.zp_stride_bytes < z_bytes || p.zp_stride_bytes % 16)))
     return fail(WQ_STAGE_ARGS, WQ_ERR_SHAPE);
-  // The launch's work-group count: per-XCD shares of at most n_pairs/256 + n_active row
+  // The launch's work-group count: per-XCD shares of at most n_pairs/128 + n_active row
   // tiles and n_active tail tiles, each times n/256 column tiles.
   const long long ntn = p.n / wq::kTileN;
-  const long long tiles = ((long long)p.n_pairs / wq::kTileM + 2LL * p.n_active) * ntn + 16;
+  const long long tiles = ((long long)p.n_pairs / wq::kTileMinM + 2LL * p.n_active) * ntn + 16;
   if (tiles > std::numeric_limits<int32_t>::max()) return fail(WQ_STAGE_SHAPE, WQ_ERR_OVERFLOW);
 
   wq::GroupedProblem g{};

@@ -5,8 +5,8 @@
 namespace wq {
 
 hipError_t launch_tile_f16(const TileArgs& p, bool grouped, bool swiglu, bool zp, int gpc,
-                           hipStream_t stream) {
-  return launch_tile_type<false>(p, grouped, swiglu, zp, gpc, stream);
+                           bool tall, hipStream_t stream) {
+  return launch_tile_type<false>(p, grouped, swiglu, zp, gpc, tall, stream);
 }
 
 hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b,
@@ -23,13 +23,15 @@ hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b
   p.n = n;
   p.k = k;
   p.ldc = swiglu ? n / 2 : n;
-  p.tiles = (n / TN) * ((m + TM - 1) / TM);
+  const bool tall = tile_tall(false, m, gpc, fp8);
+  const int tm = tile_rows(tall);
+  p.tiles = (n / TN) * ((m + tm - 1) / tm);
   if (fp8) {
     if (z != nullptr || gpc != 1) return hipErrorInvalidValue;
     return launch_tile_fp8(p, false, swiglu, bf16, stream);
   }
-  return bf16 ? launch_tile_bf16(p, false, swiglu, z != nullptr, gpc, stream)
-              : launch_tile_f16(p, false, swiglu, z != nullptr, gpc, stream);
+  return bf16 ? launch_tile_bf16(p, false, swiglu, z != nullptr, gpc, tall, stream)
+              : launch_tile_f16(p, false, swiglu, z != nullptr, gpc, tall, stream);
 }
 
 hipError_t launch_grouped_tile(const GroupedProblem& g, hipStream_t stream) {
@@ -55,11 +57,12 @@ hipError_t launch_grouped_tile(const GroupedProblem& g, hipStream_t stream) {
   p.n_active = g.n_active;
   p.n_pairs = g.n_pairs;
   p.n_tokens = g.n_tokens;
-  // Per XCD: an upper bound on its share of big tiles (at most n_pairs / 256 full row tiles
+  // Per XCD: an upper bound on its share of big tiles (at most n_pairs / tm full row tiles
   // plus one partial tile per segment) and of small tiles (one per segment); the kernel
   // derives the exact shares from the CSR, and work-groups without a tile exit at once.
+  const bool tall = tile_tall(true, 0, g.gpc, g.fp8);
   const long ntn = g.n / TN;
-  const long big = ((long)g.n_pairs / TM + g.n_active) * ntn;
+  const long big = ((long)g.n_pairs / tile_rows(tall) + g.n_active) * ntn;
   const long small = (long)g.n_active * ntn;
   const long tiles = kXcds * ((big + kXcds - 1) / kXcds + (small + kXcds - 1) / kXcds);
   if (tiles <= 0) return hipSuccess;
@@ -70,8 +73,8 @@ hipError_t launch_grouped_tile(const GroupedProblem& g, hipStream_t stream) {
     if (g.z_bank != nullptr || g.gpc != 1) return hipErrorInvalidValue;
     return launch_tile_fp8(p, true, g.swiglu, g.bf16, stream);
   }
-  return g.bf16 ? launch_tile_bf16(p, true, g.swiglu, g.z_bank != nullptr, g.gpc, stream)
-                : launch_tile_f16(p, true, g.swiglu, g.z_bank != nullptr, g.gpc, stream);
+  return g.bf16 ? launch_tile_bf16(p, true, g.swiglu, g.z_bank != nullptr, g.gpc, tall, stream)
+                : launch_tile_f16(p, true, g.swiglu, g.z_bank != nullptr, g.gpc, tall, stream);
 }
 
 }  // namespace wq

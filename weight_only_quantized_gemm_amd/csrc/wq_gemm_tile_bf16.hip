@@ -4,8 +4,8 @@
 namespace wq {
 
 hipError_t launch_tile_bf16(const TileArgs& p, bool grouped, bool swiglu, bool zp, int gpc,
-                            hipStream_t stream) {
-  return launch_tile_type<true>(p, grouped, swiglu, zp, gpc, stream);
+                            bool tall, hipStream_t stream) {
+  return launch_tile_type<true>(p, grouped, swiglu, zp, gpc, tall, stream);
 }
 
 }  // namespace wq

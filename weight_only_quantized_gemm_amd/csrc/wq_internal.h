@@ -88,8 +88,9 @@ hipError_t launch_reduce_splits(const float* partials, uint16_t* c, int m, int n
                                 bool bf16, hipStream_t stream);
 
 // Tiled kernel (wq_tile_kernel.h, wq_gemm_tile*.hip): 256 x 256 output tiles on 8 waves
-// of 128 x 64.
-constexpr int kTileM = 256;
+// of 128 x 64, or 128 x 256 tiles on 4 waves (kTileMinM rows: grouped products and ragged
+// row counts).
+constexpr int kTileMinM = 128;
 constexpr int kTileN = 256;
 // swiglu: B pairs gate/up 16-column blocks and c is the [m][n/2] activation.  gpc: scale
 // units per 128 rows of K (1, 2, 4 or 8).  bf16: A, s and c hold bf16 values (else fp16).

@@ -83,27 +83,41 @@ struct TileArgs {
 
 namespace {
 
-constexpr int TM = kTileM;   // 256
 constexpr int TN = kTileN;   // 256
 constexpr int KC = 64;       // K rows per A chunk (half a group)
-constexpr int NS = 3;        // A ring stages
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
 constexpr int kBlocks = TN / 16;  // 16-column blocks per tile
 constexpr int kXcds = 8;
-constexpr int kTailRows = TM / 2;  // grouped tiles with at most this many rows are "small"
 
-// Direct-to-LDS loads each wave issues: 4 per A chunk, 2 per B group, kDmaS per scale /
-// zero-point group ("SZ").  Issue order (one group = 128 rows = chunks 2g, 2g+1):
-//   prologue:   SZ(0) B(0) SZ(1) A(0) A(1) B(1)
-//   chunk 2g:   SZ(g+2) A(2g+2)
-//   chunk 2g+1: A(2g+3) B(g+2)
-// Chunk 2g needs A(2g) (followed by A(2g+1), B(g+1)); chunk 2g+1 needs A(2g+1) and, for
-// the next group's weights read in its last step, B(g+1) (followed by SZ(g+2), A(2g+2)).
-constexpr int kDmaA = TM * KC / 8 / kThreads;
-constexpr int kDmaB = 2;
-constexpr int kWaitEven = kDmaA + kDmaB;
-static_assert(kDmaA == 4 && 2 * kWaves == kBlocks, "load split assumes 8 waves, 256 x 256");
+// Two tile geometries share the kernel.  Both give each wave 128 rows x 64 columns.
+//  * 256 x 256 on eight waves (2 x 4), one work-group per CU: a 3-stage A ring (96 KiB).
+//  * TALL: 128 x 256 on four waves (1 x 4), two work-groups per CU: a 2-stage A ring
+//    (32 KiB), about 70 KiB of LDS per work-group.  The two waves sharing a SIMD then come
+//    from different work-groups, and ragged row counts (expert segments, m % 256) leave
+//    less padding.  It serves 128- and 64-row scale units of 4-bit weights.
+//
+// Direct-to-LDS loads each wave issues: 4 per A chunk, kDmaB (2 or 4) per B group, kDmaS
+// per scale / zero-point group ("SZ").  Issue order (one group = 128 rows = chunks 2g, 2g+1):
+//   256 x 256:  prologue SZ(0) B(0) SZ(1) A(0) A(1) B(1); chunk 2g: SZ(g+2) A(2g+2);
+//               chunk 2g+1: A(2g+3) B(g+2).
+//     Chunk 2g needs A(2g) (followed by A(2g+1), B(g+1)); chunk 2g+1 needs A(2g+1) and,
+//     for the next group's weights read in its last step, B(g+1) (followed by SZ(g+2),
+//     A(2g+2)).
+//   TALL:       prologue SZ(0) B(0) A(0) SZ(1) B(1); chunk 2g: A(2g+1) SZ(g+2) B(g+2);
+//               chunk 2g+1: A(2g+2).
+//     With two ring stages a chunk can only be loaded once every wave has left the chunk
+//     before it, one chunk ahead: chunk 2g needs A(2g), the last load issued; chunk 2g+1
+//     needs A(2g+1) (followed by SZ(g+2), B(g+2)), B(g+1) and SZ(g+1).
+template <bool TALL>
+struct Geo {
+  static constexpr int TM = TALL ? 128 : 256;  // tile rows
+  static constexpr int NS = TALL ? 2 : 3;      // A ring stages
+  static constexpr int kWaves = TALL ? 4 : 8;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kTailRows = TM / 2;     // grouped tiles of at most this many rows are "small"
+  static constexpr int kDmaA = TM * KC / 8 / kThreads;
+  static constexpr int kDmaB = kBlocks / kWaves;
+  static_assert(kDmaA == 4 && kDmaB * kWaves == kBlocks, "load split");
+};
 
 // Scale units smaller than 128 rows: scales and zero points are stored per unit of
 // gcd(group_size, 128) rows, GPC = 1, 2, 4 or 8 sub-groups per 128-row group.  A group's SZ
@@ -111,18 +125,18 @@ static_assert(kDmaA == 4 && 2 * kWaves == kBlocks, "load split assumes 8 waves, 
 // words of zero points, loaded 4 bytes per lane (kDmaS loads per wave).  With one sub-group its scales are read once, a group ahead, so two LDS slots
 // suffice; with several, a group reads its own slot while the scales of two groups ahead
 // arrive, hence three.
-template <int GPC>
+template <int GPC, bool TALL>
 struct SzPlan {
-  static constexpr int kDmaS = GPC == 8 ? 3 : GPC == 4 ? 2 : 1;
+  using G = Geo<TALL>;
+  static constexpr int kDmaS = (160 * GPC + G::kThreads - 1) / G::kThreads;
   static constexpr int kSlots = GPC == 1 ? 2 : 3;
+  static constexpr int kSlotWords = kDmaS * G::kThreads;
   static constexpr int kScaleWords = 128 * GPC;
-  static constexpr int kWaitOdd = kDmaS + kDmaA;
-  static constexpr int kWaitPrologue = kDmaS + 2 * kDmaA + kDmaB;  // SZ(0) and B(0) landed
+  static constexpr int kWaitOdd = kDmaS + G::kDmaA;
+  static constexpr int kWaitPrologue = kDmaS + 2 * G::kDmaA + G::kDmaB;  // SZ(0), B(0) landed
   static_assert(kWaitPrologue < 64, "vmcnt holds 6 bits");
-  static_assert(160 * GPC <= kDmaS * kThreads, "SZ data fits the loads");
+  static_assert(160 * GPC <= kDmaS * G::kThreads, "SZ data fits the loads");
 };
-constexpr int kSzSlotWords = 3 * kThreads;  // room for three loads per wave
-static_assert(SzPlan<8>::kDmaS * kThreads <= kSzSlotWords, "SZ loads fit a slot");
 
 // Scheduling-group masks (instruction classes of the AMDGPU scheduler hints).
 constexpr int kSchedVALU = 0x002;
@@ -144,15 +158,19 @@ __device__ __forceinline__ float sigma_of(uint16_t bits) {
 
 // FP8: E4M3 weights are twice the bytes of a 4-bit group, so B is staged per 64-row chunk
 // in a ring beside A's (3 x 16 KiB), and with one scale unit per 128 rows two SZ slots of
-// one load per wave suffice: 96 + 48 + 4 KiB.
-template <bool FP8>
+// one load per wave suffice: 96 + 48 + 4 KiB (256 x 256 only).
+template <bool FP8, int GPC, bool TALL>
 struct Smem {
-  f16x8 a[NS][TM * KC / 8];                   // 3 x 32 KiB
-  u32x4 b[FP8 ? NS : 2][kBlocks * 64];        // 16 column blocks x 64 lanes x 16 B per slot
-  uint32_t sz[FP8 ? 2 : 3][FP8 ? kThreads : kSzSlotWords];  // scale / zero-point slots
-  int row_a[TM];
-  int row_c[TM];
-  float row_w[TM];  // grouped: routing weight of each output row (1 without the multiply)
+  using G = Geo<TALL>;
+  using SZ = SzPlan<GPC, TALL>;
+  f16x8 a[G::NS][G::TM * KC / 8];             // 3 x 32 KiB, or TALL 2 x 16 KiB
+  u32x4 b[FP8 ? G::NS : 2][kBlocks * 64];     // 16 column blocks x 64 lanes x 16 B per slot
+  // scale / zero-point slots: TALL sized to its unit count; 256 x 256 room for three loads
+  // per wave whatever the unit count
+  uint32_t sz[TALL ? SZ::kSlots : FP8 ? 2 : 3][TALL ? SZ::kSlotWords : FP8 ? 512 : 1536];
+  int row_a[G::TM];
+  int row_c[G::TM];
+  float row_w[G::TM];  // grouped: routing weight of each output row (1 without the multiply)
   int info[5];
 };
 
@@ -162,14 +180,16 @@ struct Smem {
 // row.  The two lanes exchange their scaled sums (a lane swizzle, xor 16) and the gate lane
 // writes fp16(silu(g) * u) to column j of the [rows][n/2] activation: the gate and up
 // products never leave the registers.
-template <bool ZP, bool GROUPED, bool SWIGLU, int GPC, bool BF16, bool FP8>
-__global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
+template <bool ZP, bool GROUPED, bool SWIGLU, int GPC, bool BF16, bool FP8, bool TALL>
+__device__ __forceinline__ void gemm_tile_body(TileArgs p) {
   using A = Act<BF16>;
   using Zo = typename A::Zo;
   using W8 = typename A::W8;
+  using G = Geo<TALL>;  // geometry constants are used as G:: members throughout
   static_assert(!FP8 || (!ZP && GPC == 1), "E4M3: 128-row scale units, no zero points");
-  __shared__ Smem<FP8> sm;
-  using SZ = SzPlan<GPC>;
+  static_assert(!TALL || (!FP8 && GPC <= 2), "TALL: 4-bit weights, 128- or 64-row units");
+  __shared__ Smem<FP8, GPC, TALL> sm;
+  using SZ = SzPlan<GPC, TALL>;
   constexpr int kDmaS = SZ::kDmaS;
   constexpr int kWaitOdd = SZ::kWaitOdd;
   constexpr int kWaitPrologue = SZ::kWaitPrologue;
@@ -182,8 +202,8 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
-  const int wm = wave >> 2;   // wave's 128-row half of the tile
-  const int wn = wave & 3;    // wave's 64-column quarter of the tile
+  const int wm = TALL ? 0 : wave >> 2;    // wave's 128-row half of the tile
+  const int wn = TALL ? wave : wave & 3;  // wave's 64-column quarter of the tile
   const int groups = p.k / kGroup;
   const int ntiles_n = p.n / TN;
 
@@ -199,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
   if constexpr (GROUPED) {
     if (tid == 0) {
       // Tiles in longest-first order.  A segment's row tiles are its full 256-row tiles
-      // plus a partial last one; a partial tile of at most kTailRows rows only busies the
+      // plus a partial last one; a partial tile of at most G::kTailRows rows only busies the
       // first half of the waves and is "small", every other tile is "big".  Each XCD takes
       // a contiguous share of the big tiles (column tile fastest, so consecutive tiles
       // reuse the same activation rows) followed by a share of the small ones, and work-
@@ -210,9 +230,9 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
         int a0 = p.ex_off[i], a1 = p.ex_off[i + 1];
         a0 = a0 < 0 ? 0 : (a0 > p.n_pairs ? p.n_pairs : a0);
         a1 = a1 < a0 ? a0 : (a1 > p.n_pairs ? p.n_pairs : a1);
-        const int r = a1 - a0, full = r / TM, rem = r - full * TM;
-        nbig += full + (rem > kTailRows ? 1 : 0);
-        nsmall += (rem > 0 && rem <= kTailRows) ? 1 : 0;
+        const int r = a1 - a0, full = r / G::TM, rem = r - full * G::TM;
+        nbig += full + (rem > G::kTailRows ? 1 : 0);
+        nsmall += (rem > 0 && rem <= G::kTailRows) ? 1 : 0;
       }
       nbig *= ntiles_n;
       nsmall *= ntiles_n;
@@ -231,9 +251,9 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
         int a0 = p.ex_off[i], a1 = p.ex_off[i + 1];
         a0 = a0 < 0 ? 0 : (a0 > p.n_pairs ? p.n_pairs : a0);
         a1 = a1 < a0 ? a0 : (a1 > p.n_pairs ? p.n_pairs : a1);
-        const int r = a1 - a0, full = r / TM, rem = r - full * TM;
-        const int cnt = kind == 1 ? ((rem > 0 && rem <= kTailRows) ? 1 : 0)
-                                  : full + (rem > kTailRows ? 1 : 0);
+        const int r = a1 - a0, full = r / G::TM, rem = r - full * G::TM;
+        const int cnt = kind == 1 ? ((rem > 0 && rem <= G::kTailRows) ? 1 : 0)
+                                  : full + (rem > G::kTailRows ? 1 : 0);
         const int tiles = cnt * ntiles_n;
         if (idx < tiles) {
           seg = i;
@@ -250,8 +270,8 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
       if (e < 0 || e >= p.n_expert) seg = -1;
       sm.info[0] = seg;
       sm.info[1] = e;
-      sm.info[2] = lo + mt * TM;    // first CSR position of the tile
-      sm.info[3] = rows - mt * TM;  // CSR positions left in the segment from there
+      sm.info[2] = lo + mt * G::TM;    // first CSR position of the tile
+      sm.info[3] = rows - mt * G::TM;  // CSR positions left in the segment from there
       sm.info[4] = nt;
     }
     __syncthreads();
@@ -261,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
     const int pos0 = sm.info[2];
     const int left = sm.info[3];
     const int nt = sm.info[4];
-    valid_rows = left < TM ? left : TM;
+    valid_rows = left < G::TM ? left : G::TM;
     n0 = nt * TN;
     // Row maps: CSR position -> (activation row, output row); rows without a valid pair
     // read activation row 0 (finite data, never stored) and are not written.
@@ -278,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
         }
       }
     }
-    if (tid < TM) {
+    if (tid < G::TM) {
       sm.row_a[tid] = ra;
       sm.row_c[tid] = rc;
       sm.row_w[tid] = rw;
@@ -290,11 +310,11 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
     const int mt = t / ntiles_n;
     const int nt = t - mt * ntiles_n;
     n0 = nt * TN;
-    const int m0 = mt * TM;
-    valid_rows = p.m - m0 < TM ? p.m - m0 : TM;
+    const int m0 = mt * G::TM;
+    valid_rows = p.m - m0 < G::TM ? p.m - m0 : G::TM;
     // Rows past m read the last row (finite, never stored).
     const int r = m0 + tid;
-    if (tid < TM) {
+    if (tid < G::TM) {
       sm.row_a[tid] = r < p.m ? r : p.m - 1;
       sm.row_c[tid] = r < p.m ? r : -1;
     }
@@ -311,18 +331,18 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
   // ---- load sources -------------------------------------------------------------------
   // A: slot u of this lane fills ring granule (u*8 + wave)*64 + lane = row 8*(u*8+wave) +
   // lane/8, physical granule lane%8, i.e. logical granule (lane%8) ^ ((row >> 1) & 7).
-  const f16* asrc[kDmaA];
+  const f16* asrc[G::kDmaA];
 #pragma unroll
-  for (int u = 0; u < kDmaA; ++u) {
-    const int row = 8 * (u * kWaves + wave) + (lane >> 3);
+  for (int u = 0; u < G::kDmaA; ++u) {
+    const int row = 8 * (u * G::kWaves + wave) + (lane >> 3);
     const int gi = (lane & 7) ^ ((row >> 1) & 7);
     asrc[u] = reinterpret_cast<const f16*>(p.a) + (long)sm.row_a[row] * p.lda + 8 * gi;
   }
-  // B: wave w fills column blocks 2w and 2w+1 of the tile (1 KiB each per group).
+  // B: wave w fills column blocks G::kDmaB*w .. G::kDmaB*w + G::kDmaB-1 of the tile (1 KiB each per
+  // group).
   const int nb0 = n0 / 16;
   const u32x4* bsrc0 =
-      reinterpret_cast<const u32x4*>(bptr) + ((long)(nb0 + 2 * wave) * groups) * 64 + lane;
-  const u32x4* bsrc1 = bsrc0 + (long)groups * 64;
+      reinterpret_cast<const u32x4*>(bptr) + ((long)(nb0 + G::kDmaB * wave) * groups) * 64 + lane;
   // FP8 layout: 64-row chunk c of block nb is the 64 lanes' vectors at (nb * groups * 2 + c).
   const u32x4* b8src0 =
       reinterpret_cast<const u32x4*>(bptr) + ((long)(nb0 + 2 * wave) * groups * 2) * 64 + lane;
@@ -336,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
   long szstride[kDmaS];  // dwords per 128-row group
 #pragma unroll
   for (int u = 0; u < kDmaS; ++u) {
-    const int d = u * kThreads + wave * 64 + lane;
+    const int d = u * G::kThreads + wave * 64 + lane;
     const long sub_rows = (long)groups * GPC;
     if (d < SZ::kScaleWords) {
       szsrc[u] = reinterpret_cast<const uint32_t*>(sptr) +
@@ -355,20 +375,22 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
   const int nchunks = p.k / KC;
   auto issue_a = [&](int c) {
     const int cc = c < nchunks ? c : nchunks - 1;
-    f16x8* dst = &sm.a[c % NS][wave * 64];
+    f16x8* dst = &sm.a[c % G::NS][wave * 64];
 #pragma unroll
-    for (int u = 0; u < kDmaA; ++u)
-      __builtin_amdgcn_global_load_lds(asrc[u] + (long)cc * KC, dst + u * kThreads, 16, 0, 0);
+    for (int u = 0; u < G::kDmaA; ++u)
+      __builtin_amdgcn_global_load_lds(asrc[u] + (long)cc * KC, dst + u * G::kThreads, 16, 0, 0);
   };
   auto issue_b = [&](int g) {
     const int gg = g < groups ? g : groups - 1;
-    u32x4* bdst = &sm.b[g & 1][2 * wave * 64];
-    __builtin_amdgcn_global_load_lds(bsrc0 + (long)gg * 64, bdst, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(bsrc1 + (long)gg * 64, bdst + 64, 16, 0, 0);
+    u32x4* bdst = &sm.b[g & 1][G::kDmaB * wave * 64];
+#pragma unroll
+    for (int j = 0; j < G::kDmaB; ++j)
+      __builtin_amdgcn_global_load_lds(bsrc0 + (long)(j * groups + gg) * 64, bdst + j * 64, 16,
+                                       0, 0);
   };
   auto issue_b8 = [&](int c) {
     const int cc = c < nchunks ? c : nchunks - 1;
-    u32x4* bdst = &sm.b[c % NS][2 * wave * 64];
+    u32x4* bdst = &sm.b[c % G::NS][2 * wave * 64];
     __builtin_amdgcn_global_load_lds(b8src0 + (long)cc * 64, bdst, 16, 0, 0);
     __builtin_amdgcn_global_load_lds(b8src1 + (long)cc * 64, bdst + 64, 16, 0, 0);
   };
@@ -377,7 +399,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
 #pragma unroll
     for (int u = 0; u < kDmaS; ++u)
       __builtin_amdgcn_global_load_lds(szsrc[u] + (long)gg * szstride[u],
-                                       &sm.sz[slot_of(g)][u * kThreads + wave * 64], 4, 0, 0);
+                                       &sm.sz[slot_of(g)][u * G::kThreads + wave * 64], 4, 0, 0);
   };
 
   // ---- per-lane compute geometry ---------------------------------------------------------
@@ -418,9 +440,9 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
       zg[cb] = A::zero(zc);
     }
   };
-  // The lane's weight vectors of group g (slot g & 1), or for FP8 of chunk g (slot g % NS).
+  // The lane's weight vectors of group g (slot g & 1), or for FP8 of chunk g (slot g % G::NS).
   auto read_b = [&](int g) {
-    const u32x4* bslot = sm.b[FP8 ? g % NS : g & 1];
+    const u32x4* bslot = sm.b[FP8 ? g % G::NS : g & 1];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       const int base = bblk[cb] * 64 + c16 + 16 * hh;
@@ -434,8 +456,8 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
   //   chunk 2g+1: A(c+2) B8(c+2)
   // so that chunk c waits for A(c) and B8(c): 6 loads (A, B8 of chunk c+1) may stay in
   // flight at an even chunk, 7 (also SZ(g+2)) at an odd one.
-  constexpr int kWait8Even = kDmaA + 2;
-  constexpr int kWait8Odd = kDmaS + kDmaA + 2;
+  constexpr int kWait8Even = G::kDmaA + 2;
+  constexpr int kWait8Odd = kDmaS + G::kDmaA + 2;
   if constexpr (FP8) {
     issue_sz(0);
     issue_sz(1);
@@ -446,6 +468,16 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
     wait_vmcnt<kWait8Even>();
     __builtin_amdgcn_s_barrier();
     read_sz(0, 0, sigma, zo);
+  } else if constexpr (TALL) {
+    issue_sz(0);
+    issue_b(0);
+    issue_a(0);
+    issue_sz(1);
+    issue_b(1);
+    wait_vmcnt<SZ::kDmaS + G::kDmaB>();  // SZ(0), B(0) and A(0) landed
+    __builtin_amdgcn_s_barrier();
+    read_sz(0, 0, sigma, zo);
+    read_b(0);
   } else {
     issue_sz(0);
     issue_b(0);
@@ -469,10 +501,19 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
     const int g = c >> 1;
     if constexpr (FP8)
       wait_vmcnt<h2 == 0 ? kWait8Even : kWait8Odd>();
+    else if constexpr (TALL)
+      wait_vmcnt<h2 == 0 ? 0 : SZ::kDmaS + G::kDmaB>();
     else
-      wait_vmcnt<h2 == 0 ? kWaitEven : kWaitOdd>();
+      wait_vmcnt<h2 == 0 ? (G::kDmaA + G::kDmaB) : kWaitOdd>();
     __builtin_amdgcn_s_barrier();
-    if (h2 == 0) {
+    if constexpr (TALL) {
+      // the stage chunk c + 1 refills was last read in chunk c - 1
+      issue_a(c + 1);
+      if (h2 == 0) {
+        issue_sz(g + 2);
+        issue_b(g + 2);
+      }
+    } else if (h2 == 0) {
       issue_sz(g + 2);
       issue_a(c + 2);
       if constexpr (FP8) issue_b8(c + 2);
@@ -505,7 +546,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
     if constexpr (NRB > 0) {
       // Row 128*wm + 32*rb + c32 of the stage; its swizzle (row >> 1) & 7 = (c32 >> 1) & 7
       // does not depend on rb, so a step's reads share one address plus offsets.
-      const f16x8* arow = sm.a[c % NS] + (128 * wm + c32) * 8;
+      const f16x8* arow = sm.a[c % G::NS] + (128 * wm + c32) * 8;
       f16x8 aop[NRB];
       W8 bop[2];
 #pragma unroll
@@ -690,25 +731,56 @@ __global__ __launch_bounds__(kThreads) void gemm_tile_kernel(TileArgs p) {
   }
 }
 
-template <bool GROUPED, bool SWIGLU, int GPC, bool BF16>
+// The kernels of each instance, one per geometry.  (The body is a device function: with
+// the geometry as a template parameter, this toolchain's host pass dropped the launch stubs
+// of a kernel that held the body itself.)  Both run two waves per SIMD, at most 256 VGPRs
+// per wave: eight-wave work-groups one per CU, four-wave work-groups two per CU.
+template <bool ZP, bool GROUPED, bool SWIGLU, int GPC, bool BF16, bool FP8>
+__global__ __launch_bounds__(512) void gemm_tile_kernel(TileArgs p) {
+  gemm_tile_body<ZP, GROUPED, SWIGLU, GPC, BF16, FP8, false>(p);
+}
+
+template <bool ZP, bool GROUPED, bool SWIGLU, int GPC, bool BF16>
+__global__ __launch_bounds__(256, 2) void gemm_tile_kernel_tall(TileArgs p) {
+  gemm_tile_body<ZP, GROUPED, SWIGLU, GPC, BF16, false, true>(p);
+}
+
+template <bool GROUPED, bool SWIGLU, int GPC, bool BF16, bool TALL>
 hipError_t launch_tile_g(const TileArgs& p, bool zp, hipStream_t stream) {
-  if (zp)
-    hipLaunchKernelGGL((gemm_tile_kernel<true, GROUPED, SWIGLU, GPC, BF16, false>),
-                       dim3((unsigned)p.tiles), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((gemm_tile_kernel<false, GROUPED, SWIGLU, GPC, BF16, false>),
-                       dim3((unsigned)p.tiles), dim3(kThreads), 0, stream, p);
+  const dim3 grid((unsigned)p.tiles), block(Geo<TALL>::kThreads);
+  if constexpr (TALL) {
+    if (zp)
+      hipLaunchKernelGGL((gemm_tile_kernel_tall<true, GROUPED, SWIGLU, GPC, BF16>), grid, block,
+                         0, stream, p);
+    else
+      hipLaunchKernelGGL((gemm_tile_kernel_tall<false, GROUPED, SWIGLU, GPC, BF16>), grid, block,
+                         0, stream, p);
+  } else {
+    if (zp)
+      hipLaunchKernelGGL((gemm_tile_kernel<true, GROUPED, SWIGLU, GPC, BF16, false>), grid, block,
+                         0, stream, p);
+    else
+      hipLaunchKernelGGL((gemm_tile_kernel<false, GROUPED, SWIGLU, GPC, BF16, false>), grid,
+                         block, 0, stream, p);
+  }
   return hipGetLastError();
 }
 
-// gpc: scale units per 128 rows of K (1, 2, 4 or 8).
+// gpc: scale units per 128 rows of K (1, 2, 4 or 8); tall: the 128 x 256 geometry (gpc 1
+// or 2).
 template <bool GROUPED, bool SWIGLU, bool BF16>
-hipError_t launch_tile_t(const TileArgs& p, bool zp, int gpc, hipStream_t stream) {
+hipError_t launch_tile_t(const TileArgs& p, bool zp, int gpc, bool tall, hipStream_t stream) {
   switch (gpc) {
-    case 1: return launch_tile_g<GROUPED, SWIGLU, 1, BF16>(p, zp, stream);
-    case 2: return launch_tile_g<GROUPED, SWIGLU, 2, BF16>(p, zp, stream);
-    case 4: return launch_tile_g<GROUPED, SWIGLU, 4, BF16>(p, zp, stream);
-    case 8: return launch_tile_g<GROUPED, SWIGLU, 8, BF16>(p, zp, stream);
+    case 1:
+      return tall ? launch_tile_g<GROUPED, SWIGLU, 1, BF16, true>(p, zp, stream)
+                  : launch_tile_g<GROUPED, SWIGLU, 1, BF16, false>(p, zp, stream);
+    case 2:
+      return tall ? launch_tile_g<GROUPED, SWIGLU, 2, BF16, true>(p, zp, stream)
+                  : launch_tile_g<GROUPED, SWIGLU, 2, BF16, false>(p, zp, stream);
+    case 4:
+      return tall ? hipErrorInvalidValue : launch_tile_g<GROUPED, SWIGLU, 4, BF16, false>(p, zp, stream);
+    case 8:
+      return tall ? hipErrorInvalidValue : launch_tile_g<GROUPED, SWIGLU, 8, BF16, false>(p, zp, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -716,21 +788,22 @@ hipError_t launch_tile_t(const TileArgs& p, bool zp, int gpc, hipStream_t stream
 // Every instance of one activation type.
 template <bool BF16>
 hipError_t launch_tile_type(const TileArgs& p, bool grouped, bool swiglu, bool zp, int gpc,
-                            hipStream_t stream) {
+                            bool tall, hipStream_t stream) {
   if (grouped)
-    return swiglu ? launch_tile_t<true, true, BF16>(p, zp, gpc, stream)
-                  : launch_tile_t<true, false, BF16>(p, zp, gpc, stream);
-  return swiglu ? launch_tile_t<false, true, BF16>(p, zp, gpc, stream)
-                : launch_tile_t<false, false, BF16>(p, zp, gpc, stream);
+    return swiglu ? launch_tile_t<true, true, BF16>(p, zp, gpc, tall, stream)
+                  : launch_tile_t<true, false, BF16>(p, zp, gpc, tall, stream);
+  return swiglu ? launch_tile_t<false, true, BF16>(p, zp, gpc, tall, stream)
+                : launch_tile_t<false, false, BF16>(p, zp, gpc, tall, stream);
 }
 
-// E4M3 weights: 128-row scale units, no zero points; every layout of one activation type.
+// E4M3 weights: 128-row scale units, no zero points, the 256 x 256 geometry; every layout
+// of one activation type.
 template <bool BF16>
 hipError_t launch_tile_fp8_type(const TileArgs& p, bool grouped, bool swiglu,
                                 hipStream_t stream) {
 #define WQ_TILE_FP8(G, S)                                                                  \
-  hipLaunchKernelGGL((gemm_tile_kernel<false, G, S, 1, BF16, true>), dim3((unsigned)p.tiles), \
-                     dim3(kThreads), 0, stream, p)
+  hipLaunchKernelGGL((gemm_tile_kernel<false, G, S, 1, BF16, true>),                      \
+                     dim3((unsigned)p.tiles), dim3(Geo<false>::kThreads), 0, stream, p)
   if (grouped) {
     if (swiglu)
       WQ_TILE_FP8(true, true);
@@ -746,14 +819,24 @@ hipError_t launch_tile_fp8_type(const TileArgs& p, bool grouped, bool swiglu,
   return hipGetLastError();
 }
 
+// Geometry of a tiled product: 128-row tiles for grouped products (expert segments leave
+// partial tiles) and for dense ones that 128-row tiles cover with fewer padding rows, for
+// 4-bit weights with 128- or 64-row scale units; 256 x 256 otherwise.
+inline bool tile_tall(bool grouped, int m, int gpc, bool fp8) {
+  if (fp8 || gpc > 2) return false;
+  return grouped || (m + 127) / 128 * 128 < (m + 255) / 256 * 256;
+}
+
+inline int tile_rows(bool tall) { return tall ? Geo<true>::TM : Geo<false>::TM; }
+
 }  // namespace
 
 // The instances of each type (wq_gemm_tile.hip: fp16; wq_gemm_tile_bf16.hip: bf16;
 // wq_gemm_tile_fp8.hip: E4M3 weights).
 hipError_t launch_tile_f16(const TileArgs& p, bool grouped, bool swiglu, bool zp, int gpc,
-                           hipStream_t stream);
+                           bool tall, hipStream_t stream);
 hipError_t launch_tile_bf16(const TileArgs& p, bool grouped, bool swiglu, bool zp, int gpc,
-                            hipStream_t stream);
+                            bool tall, hipStream_t stream);
 hipError_t launch_tile_fp8(const TileArgs& p, bool grouped, bool swiglu, bool bf16,
                            hipStream_t stream);
 

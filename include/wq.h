@@ -189,9 +189,12 @@ int wq_act_order_perm(const int32_t* g_idx, int k, int group_size, int32_t* perm
                       int32_t* sorted_gidx_out);
 
 /* Workspace bytes wq_gemm needs for (m, n, k, flags): room for the fp32 split-K partials
- * of the largest split the library may choose (0 when it never splits: m > 16 or no
- * WQ_FLAG_FP32_REDUCE).  Contents need no initialization; calls that share one workspace
- * must not run concurrently. */
+ * [splits][m][n] of the largest split the library may choose (0 when it never splits: no
+ * WQ_FLAG_FP32_REDUCE, or m > 16 with enough output tiles to occupy every CU).  For
+ * m > 16 the tiled kernel splits K when its 256-column tiles are fewer than the CUs, the
+ * pages' fp32 global reduce (marlin.rs MoE entry point: use_fp32_reduce with c_tmp).
+ * Contents need no initialization; calls that share one workspace must not run
+ * concurrently. */
 int wq_gemm_workspace_bytes(int m, int n, int k, uint32_t flags, size_t* bytes_out);
 
 typedef struct wq_gemm_args {
@@ -213,7 +216,8 @@ typedef struct wq_gemm_args {
   uint32_t flags;           /* WQ_FLAG_*; HAS_ZP iff zero_points != NULL; ACT_ORDER iff perm */
   int32_t split_k;          /* 0 = library's choice; 1 = no split; s > 1 requests s splits
                                along K for m <= 16 (needs WQ_FLAG_FP32_REDUCE; clamped to
-                               k/128 and 16); partials are added in split order          */
+                               k/128 and 16); partials are added in split order.  For
+                               m > 16 the split is always the library's choice          */
   int32_t reserved;         /* must be 0                                                */
 } wq_gemm_args;
 

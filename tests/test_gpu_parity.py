@@ -135,6 +135,33 @@ def test_gemm_matches_oracle_small(dev, m, k, n, zp, act_order, fp32, split):
     assert_parity(c, oracle_gemm(case), label)
 
 
+# Split-K on the tiled kernel (m > 16 with the fp32 reduce, when the output tiles are fewer
+# than the CUs): both tile geometries, every scale-unit class it serves, splits that do not
+# divide the groups, act_order and zero points.
+MID_SHAPES = [
+    # m, k, n, zp, act_order, group_size
+    (17, 4096, 2048, False, False, 128),    # 128-row tiles: 8 tiles, 16 splits
+    (64, 2048, 512, True, False, 128),      # 2 tiles, 8 splits
+    (128, 4096, 14336, False, False, 128),  # 56 tiles, 5 splits
+    (300, 1024, 768, False, True, 128),     # 9 tiles, 4 splits
+    (256, 1152, 512, True, False, 64),      # 256-row tile, 9 groups over 4 splits
+    (40, 1024, 256, False, False, 32),      # 32-row units on the 256-row geometry
+    (1100, 4096, 2048, False, False, 128),  # 72 tiles, 4 splits
+]
+
+
+@pytest.mark.parametrize("m,k,n,zp,act_order,gs", MID_SHAPES)
+def test_tiled_split_k_matches_oracle(dev, m, k, n, zp, act_order, gs):
+    label = f"tiled split-K m={m} k={k} n={n} zp={zp} act_order={act_order} gs={gs}"
+    say(label)
+    case = synthetic.dense_case(m, k, n, zp=zp, act_order=act_order, group_size=gs,
+                                seed=2000 + m + k + n)
+    c = gpu_gemm(case, dev, fp32_reduce=True)
+    assert_parity(c, oracle_gemm(case), label)
+    again = gpu_gemm(case, dev, fp32_reduce=True)
+    assert np.array_equal(c.view(np.uint16), again.view(np.uint16)), label
+
+
 # act_order gathers: every LDS staging width of the row gather (K/8 granules over 256
 # threads: 1, 2, 4, 8 per thread), its global-memory fallback beyond K = 16384, and more
 # rows than the gather's 1024 work-groups, so that work-groups loop over rows.

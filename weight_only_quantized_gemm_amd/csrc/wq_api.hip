@@ -142,9 +142,18 @@ bool plan_small(int m, int n, int k, uint32_t flags, int requested, int gpc,
   return false;
 }
 
-// fp32 partials [splits][m][n] for the largest split the small-M path may use.
+// fp32 partials [splits][m][n] for the largest split the small-M path may use, or for
+// m > 16 the split the tiled path chooses (the larger of its two geometries' choices, since
+// the group size is not known here).
 size_t gemm_workspace_bytes(int m, int n, int k, uint32_t flags) {
-  if (m > 16 || !(flags & WQ_FLAG_FP32_REDUCE)) return 0;
+  if (!(flags & WQ_FLAG_FP32_REDUCE)) return 0;
+  if (m > 16) {
+    const bool fp8 = (flags & WQ_FLAG_FP8) != 0, swiglu = (flags & WQ_FLAG_SWIGLU) != 0;
+    int s = wq::tile_splits(m, n, k, 1, fp8, swiglu);
+    const int s4 = wq::tile_splits(m, n, k, 4, fp8, swiglu);
+    if (s4 > s) s = s4;
+    return s > 1 ? (size_t)s * m * n * sizeof(float) : 0;
+  }
   int smax = k / kGroupSize;
   if (smax > kMaxSplits) smax = kMaxSplits;
   if (smax <= 1) return 0;
@@ -341,9 +350,14 @@ int wq_gemm(const wq_gemm_args* args) {
   const bool small = p.m <= 16 &&
                      (swiglu ? plan_small_pair(p.m, p.k, gpc, &plan)
                              : plan_small(p.m, p.n, p.k, p.flags, p.split_k, gpc, &plan));
+  // Without a small-M plan the tiled kernel computes the product, split along K (with the
+  // fp32 reduce) when its output tiles would leave CUs idle.
+  const int tile_split = !small && (p.flags & WQ_FLAG_FP32_REDUCE)
+                             ? wq::tile_splits(p.m, p.n, p.k, gpc, fp8, swiglu) : 1;
   float* partials = nullptr;
-  if (small && plan.splits > 1) {
-    const size_t need = (size_t)plan.splits * p.m * p.n * sizeof(float);
+  if ((small && plan.splits > 1) || tile_split > 1) {
+    const size_t need =
+        (size_t)(small ? plan.splits : tile_split) * p.m * p.n * sizeof(float);
     if (p.workspace == nullptr || p.workspace_bytes < need)
       return fail(WQ_STAGE_ARGS, WQ_ERR_WORKSPACE);
     if (!aligned(p.workspace, 16)) return fail(WQ_STAGE_ARGS, WQ_ERR_ALIGN);
@@ -371,8 +385,8 @@ int wq_gemm(const wq_gemm_args* args) {
                               stream);
     return e == hipSuccess ? 0 : hip_fail(e);
   }
-  const hipError_t e =
-      wq::launch_gemm_tile(a, lda, p.m, b, s, z, c, p.n, p.k, swiglu, gpc, bf16, fp8, stream);
+  const hipError_t e = wq::launch_gemm_tile(a, lda, p.m, b, s, z, c, p.n, p.k, swiglu, gpc, bf16,
+                                             fp8, tile_split, partials, stream);
   return e == hipSuccess ? 0 : hip_fail(e);
 }
 

@@ -9,9 +9,26 @@ hipError_t launch_tile_f16(const TileArgs& p, bool grouped, bool swiglu, bool zp
   return launch_tile_type<false>(p, grouped, swiglu, zp, gpc, tall, stream);
 }
 
+constexpr int kCus = 256;
+
+int tile_splits(int m, int n, int k, int gpc, bool fp8, bool swiglu) {
+  if (swiglu || fp8) return 1;
+  const int tm = tile_rows(tile_tall(false, m, gpc, fp8));
+  const long tiles = (long)(n / TN) * ((m + tm - 1) / tm);
+  if (tiles >= kCus) return 1;
+  int splits = (int)((kCus + tiles - 1) / tiles);
+  int max_splits = k / kGroup / 2;
+  if (max_splits > 16) max_splits = 16;
+  if (splits > max_splits) splits = max_splits;
+  return splits < 1 ? 1 : splits;
+}
+
 hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b,
                             const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
-                            bool swiglu, int gpc, bool bf16, bool fp8, hipStream_t stream) {
+                            bool swiglu, int gpc, bool bf16, bool fp8, int splits,
+                            float* partials, hipStream_t stream) {
+  if (splits < 1 || (splits > 1 && (partials == nullptr || swiglu || fp8)))
+    return hipErrorInvalidValue;
   TileArgs p{};
   p.a = a;
   p.lda = lda;
@@ -23,15 +40,21 @@ hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b
   p.n = n;
   p.k = k;
   p.ldc = swiglu ? n / 2 : n;
+  p.splits = splits;
+  p.partials = partials;
   const bool tall = tile_tall(false, m, gpc, fp8);
   const int tm = tile_rows(tall);
-  p.tiles = (n / TN) * ((m + tm - 1) / tm);
+  p.tiles = (n / TN) * ((m + tm - 1) / tm) * splits;
+  hipError_t e;
   if (fp8) {
     if (z != nullptr || gpc != 1) return hipErrorInvalidValue;
-    return launch_tile_fp8(p, false, swiglu, bf16, stream);
+    e = launch_tile_fp8(p, false, swiglu, bf16, stream);
+  } else {
+    e = bf16 ? launch_tile_bf16(p, false, swiglu, z != nullptr, gpc, tall, stream)
+             : launch_tile_f16(p, false, swiglu, z != nullptr, gpc, tall, stream);
   }
-  return bf16 ? launch_tile_bf16(p, false, swiglu, z != nullptr, gpc, tall, stream)
-              : launch_tile_f16(p, false, swiglu, z != nullptr, gpc, tall, stream);
+  if (e != hipSuccess || splits == 1) return e;
+  return launch_reduce_splits(partials, c, m, n, splits, bf16, stream);
 }
 
 hipError_t launch_grouped_tile(const GroupedProblem& g, hipStream_t stream) {
@@ -57,6 +80,7 @@ hipError_t launch_grouped_tile(const GroupedProblem& g, hipStream_t stream) {
   p.n_active = g.n_active;
   p.n_pairs = g.n_pairs;
   p.n_tokens = g.n_tokens;
+  p.splits = 1;
   // Per XCD: an upper bound on its share of big tiles (at most n_pairs / tm full row tiles
   // plus one partial tile per segment) and of small tiles (one per segment); the kernel
   // derives the exact shares from the CSR, and work-groups without a tile exit at once.

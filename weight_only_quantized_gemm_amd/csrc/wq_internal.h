@@ -95,9 +95,16 @@ constexpr int kTileN = 256;
 // swiglu: B pairs gate/up 16-column blocks and c is the [m][n/2] activation.  gpc: scale
 // units per 128 rows of K (1, 2, 4 or 8).  bf16: A, s and c hold bf16 values (else fp16).
 // fp8: b holds E4M3 weights in the FP8 layout (gpc 1, no zero points).
+// splits > 1 (from tile_splits): work-groups along K per output tile, fp32 partials
+// [splits][m][n] in `partials`, added in split order by launch_reduce_splits.
 hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b,
                             const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
-                            bool swiglu, int gpc, bool bf16, bool fp8, hipStream_t stream);
+                            bool swiglu, int gpc, bool bf16, bool fp8, int splits,
+                            float* partials, hipStream_t stream);
+// Splits along K of a dense tiled product with the fp32 reduce: when its output tiles are
+// fewer than the CUs, enough splits to give every CU a work-group (at least two groups of
+// K each, at most 16); 1 for SwiGLU, E4M3 weights or enough tiles.
+int tile_splits(int m, int n, int k, int gpc, bool fp8, bool swiglu);
 
 struct GroupedProblem {
   const uint16_t* a;

@@ -65,7 +65,9 @@ struct TileArgs {
   int n;
   int k;
   int ldc;    // output row stride: n, or n / 2 for the SwiGLU epilogue
-  int tiles;  // work-groups launched
+  int tiles;  // work-groups launched (dense: output tiles x splits)
+  int splits;        // dense: work-groups along K per output tile (1: c written directly)
+  float* partials;   // dense, splits > 1: fp32 partial sums [splits][m][n]
   // grouped
   const uint8_t* b_bank;
   size_t b_stride;
@@ -102,11 +104,13 @@ constexpr int kXcds = 8;
 //     Chunk 2g needs A(2g) (followed by A(2g+1), B(g+1)); chunk 2g+1 needs A(2g+1) and,
 //     for the next group's weights read in its last step, B(g+1) (followed by SZ(g+2),
 //     A(2g+2)).
-//   TALL:       prologue SZ(0) B(0) A(0) SZ(1) B(1); chunk 2g: A(2g+1) SZ(g+2) B(g+2);
-//               chunk 2g+1: A(2g+2).
+//   TALL:       prologue SZ(0) B(0) A(0) SZ(1) B(1); chunk 2g: A(2g+1) SZ(g+2);
+//               chunk 2g+1: A(2g+2) B(g+2).
 //     With two ring stages a chunk can only be loaded once every wave has left the chunk
-//     before it, one chunk ahead: chunk 2g needs A(2g), the last load issued; chunk 2g+1
-//     needs A(2g+1) (followed by SZ(g+2), B(g+2)), B(g+1) and SZ(g+1).
+//     before it, one chunk ahead: chunk 2g needs A(2g) (followed by B(g+1)); chunk 2g+1
+//     needs A(2g+1) (followed by SZ(g+2)), B(g+1) and SZ(g+1).  B(g+2) goes to the slot
+//     of B(g), whose LDS reads (the last step of chunk 2g-1) lie two barriers back; a
+//     barrier does not wait for a wave's LDS reads still in flight.
 template <bool TALL>
 struct Geo {
   static constexpr int TM = TALL ? 128 : 256;  // tile rows
@@ -147,6 +151,11 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   // s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, expcnt 6:4 (7 = none), lgkmcnt 11:8.
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// All of this wave's LDS reads have returned (vmcnt and expcnt not waited for).
+__device__ __forceinline__ void wait_lds_reads() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
 }
 
 
@@ -204,12 +213,19 @@ __device__ __forceinline__ void gemm_tile_body(TileArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int wm = TALL ? 0 : wave >> 2;    // wave's 128-row half of the tile
   const int wn = TALL ? wave : wave & 3;  // wave's 64-column quarter of the tile
-  const int groups = p.k / kGroup;
+  const int groups_all = p.k / kGroup;  // groups of K in the weights
   const int ntiles_n = p.n / TN;
 
   // XCD-aware tile id: work-group i runs on XCD i % 8; give each XCD a contiguous range.
   int t = blockIdx.x;
   if (!GROUPED && p.tiles % kXcds == 0) t = (t % kXcds) * (p.tiles / kXcds) + t / kXcds;
+  // Dense split-K: the splits of one tile are consecutive, and split s covers groups
+  // [groups_all * s / S, groups_all * (s + 1) / S) of K.
+  const int split = GROUPED ? 0 : t % p.splits;
+  if (!GROUPED) t /= p.splits;
+  const int gs0 = GROUPED ? 0 : (int)((long)groups_all * split / p.splits);
+  const int groups =
+      GROUPED ? groups_all : (int)((long)groups_all * (split + 1) / p.splits) - gs0;
 
   int n0, valid_rows;
   const uint32_t* bptr;
@@ -336,17 +352,18 @@ __device__ __forceinline__ void gemm_tile_body(TileArgs p) {
   for (int u = 0; u < G::kDmaA; ++u) {
     const int row = 8 * (u * G::kWaves + wave) + (lane >> 3);
     const int gi = (lane & 7) ^ ((row >> 1) & 7);
-    asrc[u] = reinterpret_cast<const f16*>(p.a) + (long)sm.row_a[row] * p.lda + 8 * gi;
+    asrc[u] = reinterpret_cast<const f16*>(p.a) + (long)sm.row_a[row] * p.lda +
+              (long)gs0 * kGroup + 8 * gi;
   }
-  // B: wave w fills column blocks G::kDmaB*w .. G::kDmaB*w + G::kDmaB-1 of the tile (1 KiB each per
-  // group).
+  // B: wave w fills column blocks kDmaB * w .. kDmaB * w + kDmaB - 1 of the tile (1 KiB each
+  // per group), from the work-group's first group on.
   const int nb0 = n0 / 16;
-  const u32x4* bsrc0 =
-      reinterpret_cast<const u32x4*>(bptr) + ((long)(nb0 + G::kDmaB * wave) * groups) * 64 + lane;
+  const u32x4* bsrc0 = reinterpret_cast<const u32x4*>(bptr) +
+                       ((long)(nb0 + G::kDmaB * wave) * groups_all + gs0) * 64 + lane;
   // FP8 layout: 64-row chunk c of block nb is the 64 lanes' vectors at (nb * groups * 2 + c).
-  const u32x4* b8src0 =
-      reinterpret_cast<const u32x4*>(bptr) + ((long)(nb0 + 2 * wave) * groups * 2) * 64 + lane;
-  const u32x4* b8src1 = b8src0 + (long)groups * 2 * 64;
+  const u32x4* b8src0 = reinterpret_cast<const u32x4*>(bptr) +
+                        ((long)(nb0 + 2 * wave) * groups_all * 2 + 2 * gs0) * 64 + lane;
+  const u32x4* b8src1 = b8src0 + (long)groups_all * 2 * 64;
   // SZ: load u of this lane fills slot dword d = u*512 + wave*64 + lane.  Dwords below
   // 128*GPC are scales (block d / (8 GPC), dword d % (8 GPC) of that block's GPC sub-groups),
   // the next 32*GPC zero-point words (block e / (2 GPC), word e % (2 GPC)); the rest re-read
@@ -357,7 +374,7 @@ __device__ __forceinline__ void gemm_tile_body(TileArgs p) {
 #pragma unroll
   for (int u = 0; u < kDmaS; ++u) {
     const int d = u * G::kThreads + wave * 64 + lane;
-    const long sub_rows = (long)groups * GPC;
+    const long sub_rows = (long)groups_all * GPC;
     if (d < SZ::kScaleWords) {
       szsrc[u] = reinterpret_cast<const uint32_t*>(sptr) +
                  ((long)(nb0 + d / (8 * GPC)) * sub_rows) * 8 + d % (8 * GPC);
@@ -370,9 +387,10 @@ __device__ __forceinline__ void gemm_tile_body(TileArgs p) {
       szsrc[u] = reinterpret_cast<const uint32_t*>(sptr) + (long)nb0 * sub_rows * 8;
       szstride[u] = 8 * GPC;
     }
+    szsrc[u] += gs0 * szstride[u];  // the work-group's first group
   }
 
-  const int nchunks = p.k / KC;
+  const int nchunks = 2 * groups;
   auto issue_a = [&](int c) {
     const int cc = c < nchunks ? c : nchunks - 1;
     f16x8* dst = &sm.a[c % G::NS][wave * 64];
@@ -385,8 +403,8 @@ __device__ __forceinline__ void gemm_tile_body(TileArgs p) {
     u32x4* bdst = &sm.b[g & 1][G::kDmaB * wave * 64];
 #pragma unroll
     for (int j = 0; j < G::kDmaB; ++j)
-      __builtin_amdgcn_global_load_lds(bsrc0 + (long)(j * groups + gg) * 64, bdst + j * 64, 16,
-                                       0, 0);
+      __builtin_amdgcn_global_load_lds(bsrc0 + ((long)j * groups_all + gg) * 64, bdst + j * 64,
+                                       16, 0, 0);
   };
   auto issue_b8 = [&](int c) {
     const int cc = c < nchunks ? c : nchunks - 1;
@@ -490,6 +508,9 @@ __device__ __forceinline__ void gemm_tile_body(TileArgs p) {
     read_sz(0, 0, sigma, zo);
     read_b(0);
   }
+  // Group 0's scales are first used after chunk 0's barrier, behind which SZ(2) refills
+  // their slot (one group ahead of two slots): their reads must have returned before it.
+  wait_lds_reads();
 
   // One iteration per group: its even chunk and its odd chunk, so that the chunk parity,
   // and with it the weight dwords each step reads, is static.  NRB is the number of the
@@ -502,17 +523,17 @@ __device__ __forceinline__ void gemm_tile_body(TileArgs p) {
     if constexpr (FP8)
       wait_vmcnt<h2 == 0 ? kWait8Even : kWait8Odd>();
     else if constexpr (TALL)
-      wait_vmcnt<h2 == 0 ? 0 : SZ::kDmaS + G::kDmaB>();
+      wait_vmcnt<h2 == 0 ? G::kDmaB : SZ::kDmaS>();
     else
       wait_vmcnt<h2 == 0 ? (G::kDmaA + G::kDmaB) : kWaitOdd>();
     __builtin_amdgcn_s_barrier();
     if constexpr (TALL) {
       // the stage chunk c + 1 refills was last read in chunk c - 1
       issue_a(c + 1);
-      if (h2 == 0) {
+      if (h2 == 0)
         issue_sz(g + 2);
+      else
         issue_b(g + 2);
-      }
     } else if (h2 == 0) {
       issue_sz(g + 2);
       issue_a(c + 2);
@@ -706,6 +727,27 @@ __device__ __forceinline__ void gemm_tile_body(TileArgs p) {
           const int orow = sm.row_c[row];
           if (c32 < 16 && orow >= 0)
             p.c[(long)orow * p.ldc + j] = A::round(silu_times(mine, other));
+        }
+      }
+    }
+    return;
+  }
+  if (!GROUPED && p.splits > 1) {
+    // Split K: this split's fp32 sums; a second kernel adds the splits in order and rounds.
+    // (A loop of its own, so that the rounding below stays one rounding of the exact
+    // product rather than of its fp32 value.)
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      if (rb >= nrb) continue;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const long col = n0 + 64 * wn + 32 * cb + c32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 128 * wm + 32 * rb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const int orow = sm.row_c[row];
+          if (orow >= 0)
+            p.partials[((long)split * p.m + orow) * p.n + col] = acc[rb][cb][r] * sigma[cb];
         }
       }
     }

@@ -135,7 +135,8 @@ def bench_moe(torch, torch_ops, steps, warmup):
 def bench_extended(torch, torch_ops, steps, warmup):
     """Timings of the widened features on the same workload shapes (one object per row):
     the SwiGLU gate/up projection with its fused activation at decode (M=1) and prefill
-    (M=2048) shape, 32-row and channelwise scale groups, and MoE with routing weights."""
+    (M=2048) shape, other scale-group sizes, bf16 activations, E4M3 weights, mid-size
+    batches with the split-K fp32 reduce, and MoE with routing weights."""
     import synthetic
     import weight_only_quantized_gemm_amd as wq
     out = {}
@@ -214,6 +215,27 @@ def bench_extended(torch, torch_ops, steps, warmup):
             "tflops": round(2.0 * cfg["m"] * cfg["n"] * cfg["k"] / sec / 1e12, 2),
             "weight_tbs": round(cfg["k"] * cfg["n"] / sec / 1e12, 4)}
         del ws
+    # Mid-size batches on the decode weights with the fp32 reduce: the tiled kernel splits K
+    # when its 256-column tiles would leave CUs idle.
+    cfg = synthetic.CONFIGS["decode"]
+    case = synthetic.dense_case(1, cfg["k"], cfg["n"], seed=21)
+    w = torch_ops.PackedWeight(case["qweight"], case["scales"], device="cuda")
+    ws = [w] + [w.clone() for _ in range(11)]
+    for m in (64, 256):
+        a = torch_ops.to_device(synthetic.activations(23, m, cfg["k"]), "cuda")
+        c = torch.empty((m, cfg["n"]), dtype=torch.float16, device="cuda")
+        bufs = torch_ops.GemmBuffers(w, m, True)
+
+        def step(i, a=a, c=c, bufs=bufs):
+            torch_ops.gemm(a, ws[i % 12], c, fp32_reduce=True, buffers=bufs)
+        sec = timed_loop(torch, step, max(5, steps // 4), warmup)
+        out[f"batch_m{m}_fp32_reduce"] = {
+            "workload": f"M={m} K={cfg['k']} N={cfg['n']} u4b8 g128, fp32 reduce (split K), "
+                        "12 rotating weight copies",
+            "us": round(sec * 1e6, 2),
+            "tflops": round(2.0 * m * cfg["n"] * cfg["k"] / sec / 1e12, 2),
+            "weight_tbs": round(cfg["k"] * cfg["n"] / 2 / sec / 1e12, 4)}
+    del ws
     moe = synthetic.moe_case()
     bank = torch_ops.ExpertBank(moe["experts"], device="cuda")
     csr = wq.wq_csr_from_routes(moe["routes"], moe["n_tokens"], moe["top_k"], moe["n_expert"])

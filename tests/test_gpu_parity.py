@@ -136,8 +136,8 @@ def test_gemm_matches_oracle_small(dev, m, k, n, zp, act_order, fp32, split):
 
 
 # Split-K on the tiled kernel (m > 16 with the fp32 reduce, when the output tiles are fewer
-# than the CUs): both tile geometries, every scale-unit class it serves, splits that do not
-# divide the groups, act_order and zero points.
+# than the CUs): both tile geometries, 128- and 64-row scale units (and 32-row units, which
+# are not split), splits that do not divide the groups, act_order and zero points.
 MID_SHAPES = [
     # m, k, n, zp, act_order, group_size
     (17, 4096, 2048, False, False, 128),    # 128-row tiles: 8 tiles, 16 splits
@@ -145,7 +145,7 @@ MID_SHAPES = [
     (128, 4096, 14336, False, False, 128),  # 56 tiles, 5 splits
     (300, 1024, 768, False, True, 128),     # 9 tiles, 4 splits
     (256, 1152, 512, True, False, 64),      # 256-row tile, 9 groups over 4 splits
-    (40, 1024, 256, False, False, 32),      # 32-row units on the 256-row geometry
+    (40, 1024, 256, False, False, 32),      # 32-row units: the flag is taken, K not split
     (1100, 4096, 2048, False, False, 128),  # 72 tiles, 4 splits
 ]
 

@@ -12,7 +12,7 @@ hipError_t launch_tile_f16(const TileArgs& p, bool grouped, bool swiglu, bool zp
 constexpr int kCus = 256;
 
 int tile_splits(int m, int n, int k, int gpc, bool fp8, bool swiglu) {
-  if (swiglu || fp8) return 1;
+  if (swiglu || fp8 || gpc > 2) return 1;
   const int tm = tile_rows(tile_tall(false, m, gpc, fp8));
   const long tiles = (long)(n / TN) * ((m + tm - 1) / tm);
   if (tiles >= kCus) return 1;
@@ -27,7 +27,7 @@ hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b
                             const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                             bool swiglu, int gpc, bool bf16, bool fp8, int splits,
                             float* partials, hipStream_t stream) {
-  if (splits < 1 || (splits > 1 && (partials == nullptr || swiglu || fp8)))
+  if (splits < 1 || (splits > 1 && (partials == nullptr || swiglu || fp8 || gpc > 2)))
     return hipErrorInvalidValue;
   TileArgs p{};
   p.a = a;

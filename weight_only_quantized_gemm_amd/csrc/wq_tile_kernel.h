@@ -219,13 +219,15 @@ __device__ __forceinline__ void gemm_tile_body(TileArgs p) {
   // XCD-aware tile id: work-group i runs on XCD i % 8; give each XCD a contiguous range.
   int t = blockIdx.x;
   if (!GROUPED && p.tiles % kXcds == 0) t = (t % kXcds) * (p.tiles / kXcds) + t / kXcds;
-  // Dense split-K: the splits of one tile are consecutive, and split s covers groups
-  // [groups_all * s / S, groups_all * (s + 1) / S) of K.
-  const int split = GROUPED ? 0 : t % p.splits;
-  if (!GROUPED) t /= p.splits;
-  const int gs0 = GROUPED ? 0 : (int)((long)groups_all * split / p.splits);
+  // Dense split-K (128- and 64-row scale units; the instances for smaller units, already
+  // short of registers, are built without it): the splits of one tile are consecutive, and
+  // split s covers groups [groups_all * s / S, groups_all * (s + 1) / S) of K.
+  constexpr bool kSplitK = !GROUPED && GPC <= 2;
+  const int split = kSplitK ? t % p.splits : 0;
+  if (kSplitK) t /= p.splits;
+  const int gs0 = kSplitK ? (int)((long)groups_all * split / p.splits) : 0;
   const int groups =
-      GROUPED ? groups_all : (int)((long)groups_all * (split + 1) / p.splits) - gs0;
+      kSplitK ? (int)((long)groups_all * (split + 1) / p.splits) - gs0 : groups_all;
 
   int n0, valid_rows;
   const uint32_t* bptr;
@@ -732,7 +734,7 @@ __device__ __forceinline__ void gemm_tile_body(TileArgs p) {
     }
     return;
   }
-  if (!GROUPED && p.splits > 1) {
+  if (kSplitK && p.splits > 1) {
     // Split K: this split's fp32 sums; a second kernel adds the splits in order and rounds.
     // (A loop of its own, so that the rounding below stays one rounding of the exact
     // product rather than of its fp32 value.)

@@ -539,7 +539,7 @@ def test_moe_config_matches_oracle_on_sampled_columns(dev, weighted):
 
 # --------------------------------------------------------------------------- graph replay
 
-@pytest.mark.parametrize("m,fp32", [(1, True), (16, True), (300, False)])
+@pytest.mark.parametrize("m,fp32", [(1, True), (16, True), (300, False), (64, True)])
 def test_graph_replays_match_eager(dev, m, fp32):
     """Captured calls replay bit-identically, with eager work between replays."""
     case = synthetic.dense_case(m, 2048, 512, zp=(m == 16), act_order=(m == 300), seed=31)

@@ -128,8 +128,8 @@ def test_workspace_sizes():
     ws = wq.wq_gemm_workspace_bytes(1, 14336, 4096, fp32)
     assert ws == 16 * 1 * 14336 * 4          # fp32 partials of up to 16 splits
     assert wq.wq_gemm_workspace_bytes(16, 4096, 4096, fp32) >= 16 * 16 * 4096 * 4
-    # m > 16: the tiled kernel's split, ceil(256 CUs / 56 tiles) = 5 at n = 14336
-    assert wq.wq_gemm_workspace_bytes(128, 14336, 4096, fp32) == 5 * 128 * 14336 * 4
+    # m > 16: the tiled kernel's split, ceil(256 CUs / (2 x 56 tiles)) = 3 at n = 14336
+    assert wq.wq_gemm_workspace_bytes(128, 14336, 4096, fp32) == 3 * 128 * 14336 * 4
     assert wq.wq_gemm_workspace_bytes(128, 14336, 4096, 0) == 0
     # at most two groups of K per split: k = 512 allows 2
     assert wq.wq_gemm_workspace_bytes(100, 256, 512, fp32) == 2 * 100 * 256 * 4

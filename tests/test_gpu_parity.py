@@ -142,11 +142,11 @@ MID_SHAPES = [
     # m, k, n, zp, act_order, group_size
     (17, 4096, 2048, False, False, 128),    # 128-row tiles: 8 tiles, 16 splits
     (64, 2048, 512, True, False, 128),      # 2 tiles, 8 splits
-    (128, 4096, 14336, False, False, 128),  # 56 tiles, 5 splits
+    (128, 4096, 14336, False, False, 128),  # 56 tiles, 3 splits
     (300, 1024, 768, False, True, 128),     # 9 tiles, 4 splits
-    (256, 1152, 512, True, False, 64),      # 256-row tile, 9 groups over 4 splits
-    (40, 1024, 256, False, False, 32),      # 32-row units: the flag is taken, K not split
-    (1100, 4096, 2048, False, False, 128),  # 72 tiles, 4 splits
+    (256, 1152, 512, True, False, 64),      # 64-row units, 9 groups over 4 splits
+    (40, 1024, 256, False, False, 32),      # 32-row units (256-row tiles): K not split
+    (1100, 4096, 2048, False, False, 128),  # 72 tiles, 2 splits
 ]
 
 
@@ -403,14 +403,17 @@ def test_one_hot_rows_give_dequantized_rows_bitwise(dev):
 
 @pytest.mark.parametrize("gs,zp", [(128, True), (64, False)])
 def test_tile_geometries_agree_bitwise(dev, gs, zp):
-    """512 rows run on 256 x 256 tiles and 384 rows on 128 x 256 tiles; every output is the
-    same sum in the same order either way, so the shared rows agree bit for bit."""
-    k, n = 1024, 512
-    case = synthetic.dense_case(512, k, n, zp=zp, group_size=gs, seed=41)
+    """1024 rows by 16384 columns run on 256 x 256 tiles (256 of them) and 896 rows on
+    128 x 256 tiles; every output is the same sum in the same order either way, so the
+    shared rows agree bit for bit."""
+    k, n = 256, 16384
+    case = synthetic.dense_case(1024, k, n, zp=zp, group_size=gs, seed=41)
     c_full = gpu_gemm(case, dev)
-    c_part = gpu_gemm(case, dev, a=np.ascontiguousarray(case["a"][:384]))
-    assert np.array_equal(c_full[:384].view(np.uint16), c_part.view(np.uint16))
-    assert_parity(c_part, oracle_gemm(dict(case, a=case["a"][:384])), f"384 rows gs={gs}")
+    c_part = gpu_gemm(case, dev, a=np.ascontiguousarray(case["a"][:896]))
+    assert np.array_equal(c_full[:896].view(np.uint16), c_part.view(np.uint16))
+    cols = sample_columns(n, 4, 64)
+    assert_parity(c_part[:, cols], oracle_gemm(dict(case, a=case["a"][:896]), columns=cols),
+                  f"896 rows gs={gs}")
 
 
 def test_results_are_deterministic_and_split_independent(dev):

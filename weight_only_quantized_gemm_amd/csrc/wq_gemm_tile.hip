@@ -13,10 +13,12 @@ constexpr int kCus = 256;
 
 int tile_splits(int m, int n, int k, int gpc, bool fp8, bool swiglu) {
   if (swiglu || fp8 || gpc > 2) return 1;
-  const int tm = tile_rows(tile_tall(false, m, gpc, fp8));
+  const int tm = tile_rows(tile_tall(false, m, gpc, fp8, n));
   const long tiles = (long)(n / TN) * ((m + tm - 1) / tm);
-  if (tiles >= kCus) return 1;
-  int splits = (int)((kCus + tiles - 1) / tiles);
+  // Measured at K = 4096, N = 14336: splits for about half as many work-groups as CUs beat
+  // one work-group per CU (the partials' round trip grows with the split count) and a
+  // quarter (M=64: 24.0 against 27.3 and 28.3 us; M=256: 46.4 against 73.6 and 63.6 us).
+  int splits = (int)((kCus + 2 * tiles - 1) / (2 * tiles));
   int max_splits = k / kGroup / 2;
   if (max_splits > 16) max_splits = 16;
   if (splits > max_splits) splits = max_splits;
@@ -42,7 +44,7 @@ hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b
   p.ldc = swiglu ? n / 2 : n;
   p.splits = splits;
   p.partials = partials;
-  const bool tall = tile_tall(false, m, gpc, fp8);
+  const bool tall = tile_tall(false, m, gpc, fp8, n);
   const int tm = tile_rows(tall);
   p.tiles = (n / TN) * ((m + tm - 1) / tm) * splits;
   hipError_t e;
@@ -84,7 +86,7 @@ hipError_t launch_grouped_tile(const GroupedProblem& g, hipStream_t stream) {
   // Per XCD: an upper bound on its share of big tiles (at most n_pairs / tm full row tiles
   // plus one partial tile per segment) and of small tiles (one per segment); the kernel
   // derives the exact shares from the CSR, and work-groups without a tile exit at once.
-  const bool tall = tile_tall(true, 0, g.gpc, g.fp8);
+  const bool tall = tile_tall(true, 0, g.gpc, g.fp8, g.n);
   const long ntn = g.n / TN;
   const long big = ((long)g.n_pairs / tile_rows(tall) + g.n_active) * ntn;
   const long small = (long)g.n_active * ntn;

@@ -102,9 +102,9 @@ hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b
                             bool swiglu, int gpc, bool bf16, bool fp8, int splits,
                             float* partials, hipStream_t stream);
 // Splits along K of a dense tiled product with the fp32 reduce: when its output tiles are
-// fewer than the CUs, enough splits to give every CU a work-group (at least two groups of
-// K each, at most 16); 1 for SwiGLU, E4M3 weights, 32- or 16-row scale units (gpc > 2) or
-// enough tiles.
+// fewer than half the CUs, about 128 work-groups' worth (at least two groups of K each, at
+// most 16); 1 for SwiGLU, E4M3 weights, 32- or 16-row scale units (gpc > 2) or enough
+// tiles.
 int tile_splits(int m, int n, int k, int gpc, bool fp8, bool swiglu);
 
 struct GroupedProblem {

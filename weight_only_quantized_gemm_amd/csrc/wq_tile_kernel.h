@@ -864,11 +864,13 @@ hipError_t launch_tile_fp8_type(const TileArgs& p, bool grouped, bool swiglu,
 }
 
 // Geometry of a tiled product: 128-row tiles for grouped products (expert segments leave
-// partial tiles) and for dense ones that 128-row tiles cover with fewer padding rows, for
-// 4-bit weights with 128- or 64-row scale units; 256 x 256 otherwise.
-inline bool tile_tall(bool grouped, int m, int gpc, bool fp8) {
+// partial tiles), for dense ones that 128-row tiles cover with fewer padding rows, and for
+// dense ones whose 256 x 256 tiles would be fewer than the CUs (n columns); 4-bit weights
+// with 128- or 64-row scale units only.  256 x 256 otherwise.
+inline bool tile_tall(bool grouped, int m, int gpc, bool fp8, int n) {
   if (fp8 || gpc > 2) return false;
-  return grouped || (m + 127) / 128 * 128 < (m + 255) / 256 * 256;
+  return grouped || (m + 127) / 128 * 128 < (m + 255) / 256 * 256 ||
+         (long)(n / TN) * ((m + 255) / 256) < 256;
 }
 
 inline int tile_rows(bool tall) { return tall ? Geo<true>::TM : Geo<false>::TM; }

@@ -89,6 +89,9 @@ BF16_SHAPES = [
     # two column blocks per wave
     (16, 1024, 8192, 128, True, False, False, 0),
     (10, 2048, 8192, 16, False, False, True, 0),
+    # tiled kernel split along K with the fp32 reduce (128-row tiles)
+    (64, 2048, 512, 128, True, False, True, 0),
+    (300, 1024, 768, 64, False, True, True, 0),
 ]
 
 

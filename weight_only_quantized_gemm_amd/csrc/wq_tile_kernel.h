@@ -1,12 +1,14 @@
 // Tiled W4A16 GEMM for larger M (prefill) and the expert-major grouped (MoE) variant.
 //
-// A work-group computes a 256 x 256 tile of C with eight waves (2 x 4) of 128 x 64, each
-// a 4 x 2 grid of 32x32x16 fp16 MFMA blocks with fp32 accumulators held in VGPRs.  Two
-// waves share each SIMD, so one wave's MFMAs cover the other's LDS waits and barrier.
+// Each wave computes 128 x 64 of C, a 4 x 2 grid of 32x32x16 fp16 MFMA blocks with fp32
+// accumulators held in VGPRs.  A work-group is a 256 x 256 tile on eight waves (2 x 4), one
+// per CU, or a 128 x 256 tile on four waves (1 x 4), two per CU (the TALL geometry below).
+// Two waves share each SIMD, so one wave's MFMAs cover the other's LDS waits and barrier.
 //
 // Data movement is all direct-to-LDS loads (global_load_lds), issued at a fixed count per
 // wave so that the in-order load counter tells exactly when a stage has landed:
-//  * A (16-bit) in 256 x 64 chunks through a 3-stage ring (96 KiB), two chunks ahead;
+//  * A (16-bit) in 256 x 64 chunks through a 3-stage ring (96 KiB), two chunks ahead (TALL:
+//    128 x 64 chunks, a 2-stage ring, one chunk ahead);
 //    each wave load writes 8 rows x 128 B, and the source granule of every lane is chosen
 //    so that the ring holds the 16-byte granules of a row XOR-swizzled by ((row >> 1) & 7):
 //    reads of one granule column by 32 consecutive rows are then free of bank conflicts.
@@ -36,6 +38,10 @@
 // Tiles are assigned XCD-aware: work-groups are dealt to the 8 XCDs round-robin, so tile
 // ids are remapped to give each XCD a contiguous range (for a 2048-row problem, one
 // 256-row A panel per XCD, which then stays in that XCD's L2).
+//
+// Dense split-K (fp32 reduce, few output tiles): the splits of a tile are consecutive work-
+// groups, each over its own range of K groups; they store fp32 sums and a second kernel adds
+// them in split order.
 //
 // Grouped variant (memra-engine mmq_ffi.rs, `ExpertCsr` and the grouped projection call):
 // a tile's rows are CSR positions of one expert, A rows come from pair_tok[ex_pairs[j]]

@@ -443,15 +443,17 @@ def test_act_order_equals_plain_product_on_permuted_operands(dev):
         assert_parity(c_act, c_plain.astype(np.float64), f"act_order vs plain m={m}")
 
 
-def test_strided_activations(dev):
-    m, k, n = 20, 512, 256
+@pytest.mark.parametrize("m,fp32", [(20, False), (20, True), (5, True), (12, True)])
+def test_strided_activations(dev, m, fp32):
+    """lda > k on the tiled kernel (unsplit and split along K) and the small-M kernel."""
+    k, n = 512, 256
     case = synthetic.dense_case(m, k, n, seed=12)
     w = torch_ops.PackedWeight(case["qweight"], case["scales"], device=dev)
     wide = torch.zeros((m, k + 64), dtype=torch.float16, device=dev)
     wide[:, :k] = torch_ops.to_device(case["a"], dev)
-    c = torch_ops.gemm(wide[:, :k], w)
+    c = torch_ops.gemm(wide[:, :k], w, fp32_reduce=fp32)
     torch.cuda.synchronize()
-    assert_parity(host(c), oracle_gemm(case), "lda > k")
+    assert_parity(host(c), oracle_gemm(case), f"lda > k m={m} fp32={fp32}")
 
 
 # --------------------------------------------------------------------------- grouped (MoE)

@@ -112,11 +112,15 @@ def bf16_value(bits) -> np.ndarray:
 
 
 def round_bf16(x) -> np.ndarray:
-    """Round fp64 values to the nearest bf16 value (8 significant bits), ties to even, as
-    fp64 (normal range; no overflow or subnormal handling is needed here)."""
+    """Round fp64 values to the nearest bf16 value, ties to even, as fp64.
+
+    bf16 is the upper half of a binary32, so it keeps 8 significant bits down to 2^-126
+    and below that a fixed spacing of 2^-133 (its subnormals).  No overflow handling is
+    needed here (|x| stays far below 2^127)."""
     x = np.asarray(x, dtype=np.float64)
-    mant, exp = np.frexp(x)                 # x = mant * 2**exp, 0.5 <= |mant| < 1
-    return np.ldexp(np.round(mant * 256.0) / 256.0, exp)  # np.round: half to even
+    _, exp = np.frexp(x)                    # x = mant * 2**exp, 0.5 <= |mant| < 1
+    quantum = np.ldexp(1.0, np.maximum(exp, -125) - 8)
+    return np.round(x / quantum) * quantum  # np.round: half to even
 
 
 def values16(x, bf16: bool = False) -> np.ndarray:
@@ -281,82 +285,69 @@ class CsrError(ValueError):
 
 
 def csr_from_pair_rows(n_expert: int, n_tokens: int, selected, pair_tok) -> dict:
-    """Expert-major CSR from one expert choice and one activation row per output pair.
+    """Expert-major CSR of routed pairs, from each pair's expert and activation row.
 
-    mmq_ffi.rs, `ExpertCsr::from_pair_rows`: count pairs per expert, prefix-sum, list the
-    non-empty experts in ascending order with their segment starts (plus the final pair
-    count), then place pairs into their expert's segment in ascending pair order.
+    mmq_ffi.rs, `ExpertCsr` (the grouped projection's contract): the pair ids listed in
+    order of their expert, experts ascending and pair ids ascending within an expert
+    (ex_pairs); the experts that own at least one pair, ascending (ex_ids); where each
+    expert's run starts in that list, followed by the pair count (ex_off); and the
+    activation row of every pair, indexed by pair id (pair_tok).  Written here as a stable
+    sort of the pairs by expert.
     """
-    selected = [int(x) for x in selected]
-    pair_tok = [int(x) for x in pair_tok]
-    if n_expert <= 0 or n_tokens <= 0 or not selected:
-        raise CsrError("CSR requires non-empty experts, tokens and pairs")
-    if len(pair_tok) != len(selected):
-        raise CsrError("one activation row per pair is required")
-    counts = [0] * n_expert
-    for e in selected:
-        if not 0 <= e < n_expert:
-            raise CsrError(f"expert {e} outside 0..{n_expert}")
-        counts[e] += 1
-    for t in pair_tok:
-        if not 0 <= t < n_tokens:
-            raise CsrError(f"token {t} outside 0..{n_tokens}")
-    start = [0] * (n_expert + 1)
-    for e in range(n_expert):
-        start[e + 1] = start[e] + counts[e]
-    ex_ids = [e for e in range(n_expert) if counts[e]]
-    ex_off = [start[e] for e in ex_ids] + [len(selected)]
-    cursor = start[:n_expert]
-    ex_pairs = [0] * len(selected)
-    for p, e in enumerate(selected):
-        ex_pairs[cursor[e]] = p
-        cursor[e] += 1
-    csr = dict(ex_ids=ex_ids, ex_off=ex_off, ex_pairs=ex_pairs, pair_tok=pair_tok,
-               n_expert=n_expert, n_tokens=n_tokens)
+    sel = np.asarray(selected, dtype=np.int64).reshape(-1)
+    tok = np.asarray(pair_tok, dtype=np.int64).reshape(-1)
+    if n_expert <= 0 or n_tokens <= 0 or sel.size == 0:
+        raise CsrError("an expert CSR needs at least one expert, one token and one pair")
+    if tok.size != sel.size:
+        raise CsrError(f"{sel.size} expert choices but {tok.size} activation rows")
+    if sel.min() < 0 or sel.max() >= n_expert:
+        raise CsrError(f"an expert choice lies outside 0..{n_expert - 1}")
+    if tok.min() < 0 or tok.max() >= n_tokens:
+        raise CsrError(f"an activation row lies outside 0..{n_tokens - 1}")
+    order = np.argsort(sel, kind="stable")            # by expert; pair order kept within one
+    experts, first = np.unique(sel[order], return_index=True)
+    csr = dict(ex_ids=experts.tolist(), ex_off=first.tolist() + [int(sel.size)],
+               ex_pairs=order.tolist(), pair_tok=tok.tolist(), n_expert=n_expert,
+               n_tokens=n_tokens)
     validate_csr(csr)
     return csr
 
 
 def csr_from_token_routes(n_expert: int, n_tokens: int, top_k: int, selected) -> dict:
-    """CSR from token-major top-k routes; pair p reads activation row p // top_k.
-
-    mmq_ffi.rs, `ExpertCsr::from_token_routes`.
-    """
+    """CSR from token-major top-k routes: route j of token t is pair t * top_k + j, which
+    reads activation row t (mmq_ffi.rs, `ExpertCsr::from_token_routes`)."""
     if top_k <= 0:
-        raise CsrError("experts per token must be nonzero")
-    selected = [int(x) for x in np.asarray(selected).reshape(-1)]
-    if len(selected) != n_tokens * top_k:
-        raise CsrError("route count must equal tokens x top_k")
-    return csr_from_pair_rows(n_expert, n_tokens, selected,
-                              [p // top_k for p in range(len(selected))])
+        raise CsrError("each token needs at least one route")
+    sel = np.asarray(selected, dtype=np.int64).reshape(-1)
+    if sel.size != n_tokens * top_k:
+        raise CsrError(f"{sel.size} routes for {n_tokens} tokens of {top_k} routes each")
+    return csr_from_pair_rows(n_expert, n_tokens, sel, np.arange(sel.size) // top_k)
 
 
 def validate_csr(csr: dict) -> None:
-    """The CSR invariants of mmq_ffi.rs `ExpertCsr::from_parts`."""
-    ex_ids, ex_off = csr["ex_ids"], csr["ex_off"]
-    ex_pairs, pair_tok = csr["ex_pairs"], csr["pair_tok"]
+    """Raise CsrError unless `csr` is a well-formed expert-major CSR (the invariants the
+    mmq_ffi.rs grouped call relies on): non-empty; ex_off starts at 0, ends at the pair
+    count and rises strictly (no empty segment); expert ids rise strictly inside
+    0..n_expert-1; ex_pairs lists every pair id once; every activation row is in range."""
+    ids = np.asarray(csr["ex_ids"], dtype=np.int64)
+    off = np.asarray(csr["ex_off"], dtype=np.int64)
+    pairs = np.asarray(csr["ex_pairs"], dtype=np.int64)
+    tok = np.asarray(csr["pair_tok"], dtype=np.int64)
     n_expert, n_tokens = csr["n_expert"], csr["n_tokens"]
-    if n_expert <= 0 or n_tokens <= 0 or not ex_ids or not ex_pairs:
-        raise CsrError("CSR requires non-empty experts, tokens and pairs")
-    if len(ex_off) != len(ex_ids) + 1 or ex_off[0] != 0:
-        raise CsrError("offsets must be active experts + 1 long and start at zero")
-    if len(pair_tok) != len(ex_pairs) or ex_off[-1] != len(ex_pairs):
-        raise CsrError("offsets must end at the pair count")
-    if any(a >= b for a, b in zip(ex_ids, ex_ids[1:])):
-        raise CsrError("expert ids must be strictly increasing")
-    if any(not 0 <= e < n_expert for e in ex_ids):
-        raise CsrError("expert id out of range")
-    seen = [False] * len(ex_pairs)
-    for p in ex_pairs:
-        if not 0 <= p < len(ex_pairs):
-            raise CsrError(f"pair {p} out of range")
-        if seen[p]:
-            raise CsrError(f"pair {p} appears more than once")
-        seen[p] = True
-        if not 0 <= pair_tok[p] < n_tokens:
-            raise CsrError("token out of range")
-    if any(a >= b for a, b in zip(ex_off, ex_off[1:])):
-        raise CsrError("segments must be non-empty and increasing")
+    if n_expert <= 0 or n_tokens <= 0 or ids.size == 0 or pairs.size == 0:
+        raise CsrError("an expert CSR needs at least one expert, one token and one pair")
+    if off.size != ids.size + 1 or off[0] != 0 or off[-1] != pairs.size:
+        raise CsrError("ex_off must hold one start per listed expert plus the pair count")
+    if np.any(np.diff(off) <= 0):
+        raise CsrError("every listed expert must own at least one pair")
+    if np.any(np.diff(ids) <= 0) or ids.min() < 0 or ids.max() >= n_expert:
+        raise CsrError(f"expert ids must rise strictly inside 0..{n_expert - 1}")
+    if tok.size != pairs.size:
+        raise CsrError("pair_tok must hold one activation row per pair")
+    if not np.array_equal(np.sort(pairs), np.arange(pairs.size)):
+        raise CsrError("ex_pairs must list every pair id exactly once")
+    if tok.min() < 0 or tok.max() >= n_tokens:
+        raise CsrError(f"an activation row lies outside 0..{n_tokens - 1}")
 
 
 def grouped_w4a16_gemm(a, experts, csr, *, group_size=128, columns=None,

@@ -28,11 +28,11 @@ MUTATIONS = {
     "u4b8 offset": ("ref", "U4B8_ZERO = 8", "U4B8_ZERO = 7"),
     "act_order rows": ("ref", "        return g\n", "        return np.sort(g)\n"),
     "scale indexing": ("ref", "* s[group, :]", "* s[group % s.shape[0], ::-1]"),
-    "CSR order": ("ref", "ex_ids = [e for e in range(n_expert) if counts[e]]",
-                  "ex_ids = [e for e in reversed(range(n_expert)) if counts[e]]"),
+    "CSR order": ("ref", "order = np.argsort(sel, kind=\"stable\")",
+                  "order = np.argsort(-sel, kind=\"stable\")"),
     "bf16 decode": ("ref", "<< np.uint32(16)", "<< np.uint32(15)"),
-    "bf16 rounding width": ("ref", "np.round(mant * 256.0) / 256.0",
-                            "np.round(mant * 128.0) / 128.0"),
+    "bf16 rounding width": ("ref", "np.maximum(exp, -125) - 8)", "np.maximum(exp, -125) - 7)"),
+    "bf16 subnormal spacing": ("ref", "np.maximum(exp, -125) - 8)", "exp - 8)"),
     "E4M3 bias": ("ref", "np.ldexp(1.0 + m / 8.0, e - 7)", "np.ldexp(1.0 + m / 8.0, e - 8)"),
     "E4M3 subnormals": ("ref", "np.ldexp(m / 8.0, -6)", "np.ldexp(m / 8.0, -7)"),
     "E4M3 word byte order": ("ref", "out[i::4, :] = (w >> np.uint32(8 * i))",
@@ -40,6 +40,18 @@ MUTATIONS = {
     "block scale mapping": ("ref", "np.repeat(v, 128, axis=0).T",
                             "np.tile(v.T, (1, 128))"),
     "silu sign": ("ref", "x / (1.0 + np.exp(-x))", "x / (1.0 + np.exp(x))"),
+    "SwiGLU fp16 activation unrounded": (
+        "ref", "act16 = dequantize_fp16(swiglu_activation(a, gate, up, group_size=group_size))",
+        "act16 = swiglu_activation(a, gate, up, group_size=group_size)"),
+    "SwiGLU down projection zeros dropped": (
+        "ref", "out = w4a16_gemm(act16, down[\"qweight\"], down[\"scales\"], zeros=down.get(\"zeros\"),",
+        "out = w4a16_gemm(act16, down[\"qweight\"], down[\"scales\"], zeros=None,"),
+    "SwiGLU bf16 activation unrounded": (
+        "ref", "act = round_bf16(swiglu_activation(a, gate, up, group_size=group_size, bf16=True))",
+        "act = swiglu_activation(a, gate, up, group_size=group_size, bf16=True)"),
+    "SwiGLU bf16 down zeros dropped": (
+        "ref", "w = w4a16_weights(down[\"qweight\"], down[\"scales\"], zeros=down.get(\"zeros\"),",
+        "w = w4a16_weights(down[\"qweight\"], down[\"scales\"], zeros=None,"),
     "routing weight row": ("ref", "[rows].astype(np.float64)", "[rows[::-1]].astype(np.float64)"),
     "scale unit": ("layout", "        unit //= 2\n", "        unit //= 4\n"),
     "FP8 layout rows": ("layout", "+ 8 * qd + 4 * (d % 2) + i", "+ 4 * qd + 8 * (d % 2) + i"),

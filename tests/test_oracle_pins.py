@@ -348,12 +348,14 @@ def test_bf16_values_of_known_bit_patterns():
 def test_bf16_rounding_is_nearest_even_by_brute_force():
     """round_bf16 against a search over every finite positive bf16 value: the nearest one,
     and on a tie the one with an even last mantissa bit."""
-    table_bits = np.arange(0x0080, 0x7F80, dtype=np.uint16)   # positive normal bf16 values
+    table_bits = np.arange(0x0000, 0x7F80, dtype=np.uint16)   # zero, subnormals, normals
     table = ref.bf16_value(table_bits)
     rng = np.random.default_rng(7)
     xs = np.concatenate([rng.uniform(2.0 ** -20, 2.0 ** 20, 300),
-                         # exact midpoints between neighbours: ties
+                         rng.uniform(2.0 ** -134, 2.0 ** -124, 100),  # around the subnormals
+                         # exact midpoints between neighbours: ties (normal, then subnormal)
                          (table[1000:1100] + table[1001:1101]) / 2,
+                         (table[5:60] + table[6:61]) / 2,
                          table[2000:2050]])
     got = ref.round_bf16(xs)
     for x, g in zip(xs, got):
@@ -528,6 +530,96 @@ def test_gate_up_interleave_and_mlp_chain_shapes():
                                 scales=synthetic.scales(s + 1, kk // 128, nn))
     act16, out = ref.swiglu_mlp(a, mk(85, k, i), mk(87, k, i), mk(89, i, h))
     assert act16.dtype == np.float16 and act16.shape == (m, i) and out.shape == (m, h)
+
+
+def fp16_nearest(x):
+    """Nearest fp16 value, ties to even, by Python's own half-precision packing."""
+    return struct.unpack("<e", struct.pack("<e", float(x)))[0]
+
+
+BF16_ALL = np.array([struct.unpack("<f", struct.pack("<I", b << 16))[0] for b in range(0x8000)
+                     if (b & 0x7F80) != 0x7F80])  # every finite non-negative bf16 value
+
+
+def bf16_nearest(x):
+    """Nearest bf16 value, ties to the even bit pattern, by searching every finite bf16
+    value (decoded through struct, not the oracle)."""
+    mag = abs(float(x))
+    d = np.abs(BF16_ALL - mag)
+    best = np.flatnonzero(d == d.min())
+    pick = best[0] if best.size == 1 else [b for b in best if b % 2 == 0][0]
+    return float(np.copysign(BF16_ALL[pick], x))
+
+
+def chain_bruteforce(a_vals, gq, uq, dq, d_scales, d_zeros, round16):
+    """The SwiGLU chain by plain loops: gate and up sums of unit-scale codes read from hex
+    digits, act = round16(silu(g) * u), then the down projection of act with per-group
+    scales and zero-point codes (also from hex digits), all exact in fp64."""
+    m, k = len(a_vals), len(a_vals[0])
+    i = gq.shape[1]
+    h = dq.shape[1]
+    act = [[0.0] * i for _ in range(m)]
+    for r in range(m):
+        for j in range(i):
+            g = u = 0.0
+            for kk in range(k):
+                g += a_vals[r][kk] * (hex_nibbles(gq[kk // 8, j])[kk % 8] - 8)
+                u += a_vals[r][kk] * (hex_nibbles(uq[kk // 8, j])[kk % 8] - 8)
+            act[r][j] = round16(g / (1.0 + math.exp(-g)) * u)
+    out = [[0.0] * h for _ in range(m)]
+    for r in range(m):
+        for c in range(h):
+            acc = 0.0
+            for j in range(i):
+                grp = j // 128
+                w = (hex_nibbles(dq[j // 8, c])[j % 8] - hex_nibbles(d_zeros[grp, c // 8])[c % 8])
+                acc += act[r][j] * (w * d_scales[grp][c])
+            out[r][c] = acc
+    return np.array(act), np.array(out)
+
+
+def test_swiglu_mlp_chain_by_brute_force():
+    """swiglu_mlp: the fp16-rounded activation and the down projection with zero points,
+    against plain loops (ternary A and unit gate/up scales keep the sums exact integers,
+    so the activation's fp16 rounding is the only rounding; the down scales are not 1)."""
+    k, i, h, m = 128, 256, 16, 2
+    tern = synthetic.below(90, m * k, 3).reshape(m, k).astype(np.float64) - 1.0
+    a = tern.astype(np.float16)
+    gq, uq = synthetic.qweight_words(91, k, i), synthetic.qweight_words(92, k, i)
+    dq = synthetic.qweight_words(93, i, h)
+    ds = synthetic.scales(94, i // 128, h)
+    dz = synthetic.zero_point_words(95, i // 128, h)
+    ones = np.ones((1, i), np.float16)
+    act16, out = ref.swiglu_mlp(a, dict(qweight=gq, scales=ones), dict(qweight=uq, scales=ones),
+                                dict(qweight=dq, scales=ds, zeros=dz))
+    want_act, want_out = chain_bruteforce(tern.tolist(), gq, uq, dq, ds.astype(np.float64).tolist(),
+                                          dz, fp16_nearest)
+    assert act16.dtype == np.float16
+    assert act16.astype(np.float64).tolist() == want_act.tolist()
+    assert np.any(want_act != np.round(want_act))   # the rounding is visible in the sums
+    assert np.allclose(out, want_out, rtol=1e-12, atol=1e-9)
+
+
+def test_swiglu_mlp_bf16_chain_by_brute_force():
+    """swiglu_mlp_bf16: activations and scales as bf16 bit patterns; the activation is
+    rounded to bf16 (nearest even, by searching every bf16 value) before the down
+    projection with zero points."""
+    k, i, h, m = 128, 128, 16, 2
+    tern = synthetic.below(96, m * k, 3).reshape(m, k).astype(np.float64) - 1.0
+    a_bits = np.where(tern > 0, 0x3F80, np.where(tern < 0, 0xBF80, 0)).astype(np.uint16)
+    gq, uq = synthetic.qweight_words(97, k, i), synthetic.qweight_words(98, k, i)
+    dq = synthetic.qweight_words(99, i, h)
+    ds = synthetic.scales_bf16(100, i // 128, h)
+    dz = synthetic.zero_point_words(101, i // 128, h)
+    ones = np.full((1, i), 0x3F80, np.uint16)
+    act, out = ref.swiglu_mlp_bf16(a_bits, dict(qweight=gq, scales=ones),
+                                   dict(qweight=uq, scales=ones),
+                                   dict(qweight=dq, scales=ds, zeros=dz))
+    ds_vals = [[struct.unpack("<f", struct.pack("<I", int(b) << 16))[0] for b in row] for row in ds]
+    want_act, want_out = chain_bruteforce(tern.tolist(), gq, uq, dq, ds_vals, dz, bf16_nearest)
+    assert np.asarray(act).tolist() == want_act.tolist()
+    assert np.any(want_act != np.round(want_act))
+    assert np.allclose(out, want_out, rtol=1e-12, atol=1e-9)
 
 
 def test_routing_weights_scale_each_pair_row():

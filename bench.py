@@ -1,11 +1,12 @@
 """Benchmark of the W4A16 GEMM on one MI355X; prints one JSON line.
 
 Headline (value): packed-weight TB/s of the decode GEMM, M=1 K=4096 N=14336, u4b8, group
-128, split-K with the fp32 workspace reduce.  Each step is one wq_gemm call; steps rotate
-over enough weight copies that the weights stream from HBM rather than from the 256 MB
-Infinity Cache.  The same line carries the prefill (M=2048, act_order) TFLOP/s with its
-MFMA roofline, the batched-decode and grouped-MoE figures, and the oracle timed on the
-host cores as the CPU baseline.
+128, with the fp32-reduce flag set (the planner keeps K unsplit at this shape; the line's
+workload text says what runs).  Each step is one wq_gemm call; steps rotate over enough
+weight copies that the weights stream from HBM rather than from the 256 MB Infinity Cache.
+The same line carries the prefill (M=2048, act_order) TFLOP/s with its MFMA roofline, the
+batched-decode, tiny and grouped-MoE figures, the measured HBM-read and MFMA ceilings, and
+the oracle timed on the host cores for every workload as the CPU baseline.
 """
 
 from __future__ import annotations
@@ -255,6 +256,32 @@ def bench_extended(torch, torch_ops, steps, warmup):
     return out
 
 
+MFMA_ITERS = 512  # K steps of the register-only MFMA loop per launch (about 0.1-0.2 ms)
+
+
+def bench_mfma(torch, steps, warmup):
+    """Practical fp16 matrix rate (wq_mfma_rate): the tiled GEMM's per-wave products from
+    registers on every CU, with this method's operand data (A ~ N(0,1) in fp16, B integer
+    codes q - 8 in -8..7) and with all-zero operands (the least switching activity)."""
+    import synthetic
+    import weight_only_quantized_gemm_amd as wq
+    a = synthetic.activations(31, 4 * 64, 8).reshape(4, 64, 8)
+    b = (synthetic.below(32, 2 * 64 * 8, 16).astype(np.float16) - 8).reshape(2, 64, 8)
+    data = {"method_operands": np.concatenate([a, b]).astype(np.float16),
+            "zeros": np.zeros((6, 64, 8), np.float16)}
+    sink = torch.empty(256 * 512, dtype=torch.float32, device="cuda")
+    out = {}
+    for key, ops_h in data.items():
+        ops = torch.from_numpy(ops_h).cuda()
+        flops = [0.0]
+
+        def step(i, ops=ops):
+            flops[0] = wq.wq_mfma_rate(ops, MFMA_ITERS, sink, sink.numel())
+        sec = timed_loop(torch, step, steps, warmup)
+        out[key] = {"us": round(sec * 1e6, 2), "tflops": round(flops[0] / sec / 1e12, 1)}
+    return out
+
+
 COPY_BYTES = 1 << 30  # plain device copy used to calibrate the HBM byte counters
 
 
@@ -300,29 +327,82 @@ def measured_traffic() -> float | None:
         return None
 
 
-def cpu_baseline(budget_s: float) -> dict:
-    """The oracle (fp64 numpy) on the decode workload, repeated for about `budget_s`."""
-    import synthetic
-    from oracle import reference as ref
+def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
     except Exception:  # pragma: no cover - threadpoolctl is optional
-        blas = 1
-    case = synthetic.config_case("decode")
+        return 1
+
+
+def _time_repeated(fn, budget_s: float) -> tuple[float, int]:
+    """Seconds per call of fn, repeated until about budget_s has passed (at least once)."""
     runs, t0 = 0, time.perf_counter()
     while True:
-        ref.w4a16_gemm(case["a"], case["qweight"], case["scales"])
+        fn()
         runs += 1
         if time.perf_counter() - t0 >= budget_s:
             break
-    sec = (time.perf_counter() - t0) / runs
-    weight_bytes = case["k"] * case["n"] // 2
-    return {"value": weight_bytes / sec / 1e12, "unit": "TB/s", "cores": int(blas),
-            "kind": "oracle",
-            "sample": f"full decode problem M=1 K=4096 N=14336 (unpack, exact dequant, fp64 "
-                      f"matmul), {runs} runs in {sec * runs:.1f} s; {sec * 1e3:.0f} ms per run; "
-                      f"elementwise numpy on 1 thread, BLAS on {blas}"}
+    return (time.perf_counter() - t0) / runs, runs
+
+
+def cpu_baseline(budget_s: float, gpu_us: dict) -> dict:
+    """The oracle (fp64 numpy: unpack, exact dequant, fp64 matmul) timed on the host cores
+    for every workload, beside the GPU time of the same workload.  The headline fields are
+    the decode workload's, in the line's unit; `configs` holds each workload's oracle time
+    (the MoE workload on a sample of its columns, scaled to all of them)."""
+    import synthetic
+    from oracle import reference as ref
+    blas = _blas_threads()
+    per = {}
+    share = budget_s / 6.0
+
+    def dense(name, frac=1.0):
+        case = synthetic.config_case(name)
+        cols = None if frac >= 1.0 else np.arange(int(case["n"] * frac))
+        sec, runs = _time_repeated(lambda: ref.w4a16_gemm(
+            case["a"], case["qweight"], case["scales"], zeros=case["zeros"],
+            g_idx=case["g_idx"], columns=cols), share)
+        scale = case["n"] / (case["n"] if cols is None else len(cols))
+        return case, sec * scale, runs, cols
+
+    for name in ("tiny", "decode", "batched", "prefill"):
+        case, sec, runs, _ = dense(name)
+        per[name] = {"oracle_s": round(sec, 5), "runs": runs,
+                     "sample": f"full problem M={case['m']} K={case['k']} N={case['n']}",
+                     "gpu_us": gpu_us.get(name),
+                     "gpu_speedup": round(sec / (gpu_us[name] * 1e-6), 1) if gpu_us.get(name)
+                     else None}
+    moe = synthetic.moe_case()
+    csr = ref.csr_from_token_routes(moe["n_expert"], moe["n_tokens"], moe["top_k"],
+                                    moe["routes"])
+    cols = np.arange(moe["n"] // 7)             # 2048 of the 14336 columns
+    sec, runs = _time_repeated(lambda: ref.grouped_w4a16_gemm(moe["a"], moe["experts"], csr,
+                                                              columns=cols), share)
+    sec *= moe["n"] / len(cols)
+    per["moe"] = {"oracle_s": round(sec, 4), "runs": runs,
+                  "sample": f"columns 0..{len(cols) - 1} of {moe['n']} (all 2048 pairs, all 8 "
+                            "experts), time scaled by 7",
+                  "gpu_us": gpu_us.get("moe"),
+                  "gpu_speedup": round(sec / (gpu_us["moe"] * 1e-6), 1) if gpu_us.get("moe")
+                  else None}
+    dec = per["decode"]
+    weight_bytes = 4096 * 14336 // 2
+    return {"value": round(weight_bytes / dec["oracle_s"] / 1e12, 8), "unit": "TB/s",
+            "cores": blas, "host_cores": os.cpu_count(), "kind": "oracle",
+            "sample": f"full decode problem M=1 K=4096 N=14336, {dec['runs']} runs, "
+                      f"{dec['oracle_s'] * 1e3:.0f} ms per run; numpy elementwise work on 1 "
+                      f"thread, BLAS (the fp64 matmul) on {blas} of {os.cpu_count()} host "
+                      "cores; every workload under `configs`",
+            "configs": per}
+
+
+def plan_text(m, n, k, flags) -> str:
+    """What the library runs for a problem, from its own planner (wq_gemm_plan)."""
+    import weight_only_quantized_gemm_amd as wq
+    kernel, splits = wq.wq_gemm_plan(m, n, k, flags=flags)
+    split = "K not split" if splits == 1 else f"K split {splits} ways, fp32 partials reduced"
+    return f"{wq.KERNEL_NAMES[kernel]} kernel, {split}"
 
 
 def main() -> int:
@@ -330,12 +410,12 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extended", action="store_true",
                     help="skip the timings of the widened features")
     ap.add_argument("--only", choices=["decode", "batched", "prefill", "moe", "tiny", "copy",
-                                       "ceiling"],
+                                       "ceiling", "mfma"],
                     default=None, help="time one workload (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -344,6 +424,7 @@ def main() -> int:
         return 2
 
     import torch
+    import weight_only_quantized_gemm_amd as wq
     from weight_only_quantized_gemm_amd import torch_ops
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -360,6 +441,9 @@ def main() -> int:
             c = bench_stream_read(torch, r["weights"], args.steps, args.warmup)
             print(json.dumps({"only": "ceiling", "bytes": c["bytes"], "us": c["sec"] * 1e6,
                               "TBs": c["bytes"] / c["sec"] / 1e12}), flush=True)
+        elif args.only == "mfma":
+            print(json.dumps({"only": "mfma", **bench_mfma(torch, args.steps, args.warmup)}),
+                  flush=True)
         elif args.only == "moe":
             r = bench_moe(torch, torch_ops, args.steps, args.warmup)
             print(json.dumps({"only": "moe", "us": r["sec"] * 1e6,
@@ -372,25 +456,40 @@ def main() -> int:
                               "tflops": r["flops"] / r["sec"] / 1e12}), flush=True)
         return 0
 
+    def log(text):
+        print(text, file=sys.stderr, flush=True)
+
     dec = bench_dense(torch, torch_ops, "decode", 12, args.steps, args.warmup)
-    print(f"decode: {dec['sec'] * 1e6:.2f} us/call", file=sys.stderr, flush=True)
+    log(f"decode: {dec['sec'] * 1e6:.2f} us/call")
     ceil = bench_stream_read(torch, dec.pop("weights"), args.steps, args.warmup)
     ceil_tbs = ceil["bytes"] / ceil["sec"] / 1e12
-    print(f"streaming read of the same bytes: {ceil['sec'] * 1e6:.2f} us ({ceil_tbs:.3f} TB/s)",
-          file=sys.stderr, flush=True)
+    log(f"streaming read of the decode weights: {ceil['sec'] * 1e6:.2f} us ({ceil_tbs:.3f} TB/s)")
     bat = bench_dense(torch, torch_ops, "batched", 40, args.steps, args.warmup)
-    bat.pop("weights")
-    print(f"batched: {bat['sec'] * 1e6:.2f} us/call", file=sys.stderr, flush=True)
+    bceil = bench_stream_read(torch, bat.pop("weights"), args.steps, args.warmup)
+    log(f"batched: {bat['sec'] * 1e6:.2f} us/call; streaming read of its weights: "
+        f"{bceil['sec'] * 1e6:.2f} us")
+    tiny = bench_dense(torch, torch_ops, "tiny", 1, args.steps, args.warmup)
+    tiny.pop("weights")
+    log(f"tiny: {tiny['sec'] * 1e6:.2f} us/call")
     pre_steps = max(10, args.steps // 4)
     pre = bench_dense(torch, torch_ops, "prefill", 1, pre_steps, max(3, args.warmup // 4))
     pre.pop("weights")
-    print(f"prefill: {pre['sec'] * 1e6:.1f} us/call", file=sys.stderr, flush=True)
+    log(f"prefill: {pre['sec'] * 1e6:.1f} us/call")
     moe = bench_moe(torch, torch_ops, pre_steps, max(3, args.warmup // 4))
-    print(f"moe: {moe['sec'] * 1e6:.1f} us/call", file=sys.stderr, flush=True)
+    log(f"moe: {moe['sec'] * 1e6:.1f} us/call")
+    mfma = bench_mfma(torch, max(10, args.steps // 10), 3)
+    log("mfma register-only rate: " + ", ".join(f"{k} {v['tflops']} TFLOP/s"
+                                                 for k, v in mfma.items()))
 
+    fp32 = wq.WQ_FLAG_FP32_REDUCE
     tbs = dec["weight_bytes"] / dec["sec"] / 1e12
-    achieved = dec["alg_bytes"] / dec["sec"] / 1e9
+    achieved = dec["weight_bytes"] / dec["sec"] / 1e9          # packed-weight bytes
+    achieved_all = dec["alg_bytes"] / dec["sec"] / 1e9         # weights, scales, A and C
     pre_tflops = pre["flops"] / pre["sec"] / 1e12
+    moe_tflops = moe["flops"] / moe["sec"] / 1e12
+    bat_tbs = bat["weight_bytes"] / bat["sec"] / 1e12
+    bceil_tbs = bceil["bytes"] / bceil["sec"] / 1e12
+    real_mfma = mfma["method_operands"]["tflops"]
     line = {
         "metric": METRIC,
         "value": round(tbs, 4),
@@ -404,38 +503,61 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "fp16",
         "data": "synthetic",
-        "config": {"workload": "decode GEMM M=1 K=4096 N=14336 u4b8 group128 split-K fp32 "
-                               "reduce, 12 rotating weight copies",
+        "config": {"workload": "decode GEMM M=1 K=4096 N=14336 u4b8 group 128, fp32-reduce "
+                               "flag set; " + plan_text(1, 14336, 4096, fp32)
+                               + "; 12 rotating weight copies",
                    "m": 1, "k": 4096, "n": 14336, "weight_bytes": dec["weight_bytes"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic()},
+                     "traffic": measured_traffic(),
+                     "basis": "packed-weight bytes K*N/2 per launch",
+                     "achieved_all_operands": round(achieved_all, 1),
+                     "frac_all_operands": round(achieved_all / HBM_PEAK_GBS, 4)},
         "hbm_read_ceiling": {"kernel": "wq_stream_read (plain 16-byte non-temporal streaming "
                                        "read of the same 12 rotating weight buffers)",
                              "bytes": ceil["bytes"], "us": round(ceil["sec"] * 1e6, 3),
                              "TBs": round(ceil_tbs, 4),
                              "frac_of_peak": round(ceil_tbs * 1e3 / HBM_PEAK_GBS, 4),
                              "decode_frac_of_ceiling": round(tbs / ceil_tbs, 4)},
-        "prefill": {"workload": "M=2048 K=4096 N=14336 u4b8 group128 act_order (gather + GEMM)",
+        "prefill": {"workload": "M=2048 K=4096 N=14336 u4b8 group 128 act_order (gather + GEMM); "
+                                + plan_text(2048, 14336, 4096, wq.WQ_FLAG_ACT_ORDER),
                     "tflops": round(pre_tflops, 2), "us": round(pre["sec"] * 1e6, 2),
                     "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2),
                                  "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                 "frac": round(pre_tflops / MFMA_FP16_PEAK_TFLOPS, 4)}},
-        "batched": {"workload": "M=16 K=4096 N=4096 u4+zp group128 fp32 reduce, 40 copies",
-                    "us": round(bat["sec"] * 1e6, 3),
-                    "weight_tbs": round(bat["weight_bytes"] / bat["sec"] / 1e12, 4),
-                    "hbm_frac": round(bat["alg_bytes"] / bat["sec"] / 1e9 / HBM_PEAK_GBS, 4)},
-        "moe": {"workload": "1024 tokens top-2 of 8 experts K=4096 N=14336 u4b8 group128",
-                "us": round(moe["sec"] * 1e6, 2),
-                "tflops": round(moe["flops"] / moe["sec"] / 1e12, 2),
-                "mfma_frac": round(moe["flops"] / moe["sec"] / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4)},
+                                 "frac": round(pre_tflops / MFMA_FP16_PEAK_TFLOPS, 4)},
+                    "frac_of_mfma_ceiling": round(pre_tflops / real_mfma, 4)},
+        "batched": {"workload": "M=16 K=4096 N=4096 u4 + zero points group 128, fp32-reduce "
+                                "flag set; " + plan_text(16, 4096, 4096, fp32 | wq.WQ_FLAG_HAS_ZP)
+                                + "; 40 rotating weight copies",
+                    "us": round(bat["sec"] * 1e6, 3), "weight_tbs": round(bat_tbs, 4),
+                    "hbm_frac": round(bat_tbs * 1e3 / HBM_PEAK_GBS, 4),
+                    "hbm_frac_all_operands": round(
+                        bat["alg_bytes"] / bat["sec"] / 1e9 / HBM_PEAK_GBS, 4),
+                    "read_ceiling_us": round(bceil["sec"] * 1e6, 3),
+                    "read_ceiling_tbs": round(bceil_tbs, 4),
+                    "frac_of_read_ceiling": round(bat_tbs / bceil_tbs, 4)},
+        "tiny": {"workload": "M=16 K=1024 N=256 u4b8 group 128 (one 131 KB weight, cache "
+                             "resident); " + plan_text(16, 256, 1024, 0),
+                 "us": round(tiny["sec"] * 1e6, 3)},
+        "moe": {"workload": "1024 tokens top-2 of 8 experts K=4096 N=14336 u4b8 group 128, "
+                            "grouped tiled kernel (128 x 256 tiles)",
+                "us": round(moe["sec"] * 1e6, 2), "tflops": round(moe_tflops, 2),
+                "mfma_frac": round(moe_tflops / MFMA_FP16_PEAK_TFLOPS, 4),
+                "frac_of_mfma_ceiling": round(moe_tflops / real_mfma, 4)},
+        "mfma_ceiling": {"kernel": "wq_mfma_rate (register-only v_mfma_f32_32x32x16_f16 loop, "
+                                   "the tiled GEMM's 128 x 64 wave tile, 2 waves per SIMD on "
+                                   "every CU)", **mfma,
+                         "frac_of_peak": {k: round(v["tflops"] / MFMA_FP16_PEAK_TFLOPS, 4)
+                                          for k, v in mfma.items()}},
     }
     if not args.no_extended:
         line["extended"] = bench_extended(torch, torch_ops, args.steps, max(3, args.warmup // 4))
-        print("extended: " + ", ".join(f"{k} {v['us']} us" for k, v in line["extended"].items()),
-              file=sys.stderr, flush=True)
+        log("extended: " + ", ".join(f"{k} {v['us']} us" for k, v in line["extended"].items()))
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args.cpu_budget)
+        gpu_us = {"tiny": tiny["sec"] * 1e6, "decode": dec["sec"] * 1e6,
+                  "batched": bat["sec"] * 1e6, "prefill": pre["sec"] * 1e6,
+                  "moe": moe["sec"] * 1e6}
+        line["cpu_baseline"] = cpu_baseline(args.cpu_budget, gpu_us)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -36,7 +36,7 @@
  *  - scales: fp16 [n/16][k/U][16]; zero points: uint32 [n/16][k/U][2] (16 codes per pair,
  *    column c of the block in bits 4*(c%8) of word c/8).
  *  - act_order: B rows are stored in sorted order (row position i holds original row
- *    perm[i]); sorted position i belongs to group i / 128 (see wq_act_order_perm).
+ *    perm[i]); sorted position i belongs to group i / group_size (see wq_act_order_perm).
  */
 #ifndef WQ_H
 #define WQ_H
@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define WQ_ABI_VERSION 2u
+#define WQ_ABI_VERSION 3u
 
 /* Flag bits: the bit positions of the vllm_marlin.rs launch flags. */
 #define WQ_FLAG_ACT_ORDER   (1u << 1) /* gather A by perm before the product              */
@@ -197,6 +197,18 @@ int wq_act_order_perm(const int32_t* g_idx, int k, int group_size, int32_t* perm
  * concurrently. */
 int wq_gemm_workspace_bytes(int m, int n, int k, uint32_t flags, size_t* bytes_out);
 
+/* Which kernel wq_gemm runs for a problem, and how many splits along K it uses (host,
+ * no device access): the planner's own choice for (m, n, k, group_size, flags, split_k),
+ * the same arguments as in wq_gemm_args.  kernel_out: WQ_KERNEL_SMALL_M (m <= 16: 16-column
+ * blocks, weights streamed once), WQ_KERNEL_TILE_256 or WQ_KERNEL_TILE_128 (MFMA tiles of
+ * 256 or 128 rows by 256 columns); splits_out: 1 = K not split, s > 1 = s fp32 partials
+ * added by a second kernel in split order.  Shape errors as in wq_gemm. */
+#define WQ_KERNEL_SMALL_M 1
+#define WQ_KERNEL_TILE_256 2
+#define WQ_KERNEL_TILE_128 3
+int wq_gemm_plan(int m, int n, int k, int group_size, uint32_t flags, int split_k,
+                 int32_t* kernel_out, int32_t* splits_out);
+
 typedef struct wq_gemm_args {
   uint32_t abi_version;     /* WQ_ABI_VERSION                                          */
   uint32_t struct_size;     /* sizeof(wq_gemm_args)                                   */
@@ -206,6 +218,13 @@ typedef struct wq_gemm_args {
   const void* b_scales;     /* device, library scale layout (wq_repack_scales)          */
   const void* zero_points;  /* device, library zero-point layout, or NULL (u4b8)        */
   const int32_t* perm;      /* device int32 [k] with WQ_FLAG_ACT_ORDER, else NULL       */
+  const int32_t* group_index; /* device int32 [k] or NULL (act_order only): the group of
+                               each sorted row position, g_idx[perm[i]] (the sorted_gidx_out
+                               of wq_act_order_perm).  The library layout puts sorted
+                               position i in group i / group_size (k for -1), so this is a
+                               check, not an input: positions whose entry differs make the
+                               act_order gather write NaN into that activation column, and
+                               every output of the call is then NaN                      */
   void* a_tmp;              /* device [m][k] 16-bit gather scratch with act_order, or NULL */
   void* workspace;          /* device scratch (wq_gemm_workspace_bytes), may be NULL if 0 */
   size_t workspace_bytes;
@@ -222,7 +241,10 @@ typedef struct wq_gemm_args {
 } wq_gemm_args;
 
 /*
- * C = A @ dequant(B) (all of it enqueued on args->stream).  With WQ_FLAG_SWIGLU, c is the
+ * C = A @ dequant(B) (all of it enqueued on args->stream).  (ferrum-kernels vllm_marlin.rs,
+ * `FerrumMarlinLaunch`: a, b, c, scales, zero points, group_index and permutation, the
+ * scratch buffers, the sizes, the group size and the flag word.)  A group_index without
+ * WQ_FLAG_ACT_ORDER fails with WQ_ERR_FLAGS, a misaligned one with WQ_ERR_ALIGN.  With WQ_FLAG_SWIGLU, c is the
  * [m][n/2] activation silu(A Wg) * (A Wu) of paired gate/up weights (any m; for m <= 16
  * and k <= 8192 the small-M kernel computes both sums of a pair in one work-group, with
  * no split along K).
@@ -307,6 +329,19 @@ int wq_grouped_gemm(const wq_grouped_args* args);
 int wq_stream_read_sink_words(size_t bytes, size_t* words_out);
 int wq_stream_read(const void* src, size_t bytes, void* sink, size_t sink_words,
                    void* stream);
+
+/*
+ * Measurement helper, not a step of the method: the practical fp16 matrix rate.  One work-
+ * group per CU (256), two waves per SIMD; every wave keeps the tiled GEMM's 128 x 64 wave
+ * tile in registers (four A operands, two B operands: `operands` is device f16 [6][64][8],
+ * 16-byte aligned, A first) and runs `iters` (1 .. 2^20) steps of its eight
+ * v_mfma_f32_32x32x16_f16 products.  No memory is touched between the operand loads and
+ * one fp32 store per thread into `sink` (device, at least 256 * 512 floats).  The chip's
+ * clock falls with the operands' switching activity, so the rate depends on the data.
+ * *flops_out receives the launch's floating-point operation count.  Enqueues on `stream`.
+ */
+int wq_mfma_rate(const void* operands, int iters, float* sink, size_t sink_floats,
+                 double* flops_out, void* stream);
 
 #ifdef __cplusplus
 }

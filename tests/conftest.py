@@ -12,6 +12,14 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
 
 
+def by_column_chunks(fn, n, chunk=2048):
+    """An oracle result over all n columns, built chunk by chunk to bound host memory:
+    fn(columns) returns the rows for that column subset."""
+    import numpy as np
+    parts = [fn(np.arange(c0, min(c0 + chunk, n))) for c0 in range(0, n, chunk)]
+    return np.concatenate(parts, axis=1)
+
+
 def read_golden(name):
     """Lines of a golden fixture without comments or blanks."""
     path = os.path.join(ROOT, "tests", "golden", name)

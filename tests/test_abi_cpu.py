@@ -49,7 +49,7 @@ def test_library_exports_every_declared_function(L):
 
 
 def test_abi_version(L):
-    assert wq.wq_abi_version() == wq.WQ_ABI_VERSION == 2
+    assert wq.wq_abi_version() == wq.WQ_ABI_VERSION == 3
 
 
 def test_status_strings_decode_stage_and_code(L):
@@ -63,7 +63,8 @@ def test_status_strings_decode_stage_and_code(L):
 def gemm_args(**over):
     base = dict(abi_version=wq.WQ_ABI_VERSION, struct_size=ctypes.sizeof(wq.wq_gemm_args),
                 a=0x1000, b=0x2000,
-                c=0x3000, b_scales=0x4000, zero_points=None, perm=None, a_tmp=None,
+                c=0x3000, b_scales=0x4000, zero_points=None, perm=None, group_index=None,
+                a_tmp=None,
                 workspace=None, workspace_bytes=0, stream=None, m=16, n=256, k=1024, lda=1024,
                 group_size=128, flags=0, split_k=0, reserved=0)
     base.update(over)
@@ -103,6 +104,12 @@ def call_gemm(L, **over):
     (dict(flags=wq.WQ_FLAG_ACT_ORDER), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
     (dict(perm=0x6000), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
     (dict(flags=wq.WQ_FLAG_ACT_ORDER, perm=0x6000), status(STAGE_ARGS, wq.WQ_ERR_NULL)),
+    # group_index: only with act_order (it checks the act_order layout's groups), 4-byte aligned
+    (dict(group_index=0x6800), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
+    (dict(flags=wq.WQ_FLAG_ACT_ORDER, perm=0x6000, a_tmp=0x7000, group_index=0x6802),
+     status(STAGE_ARGS, wq.WQ_ERR_ALIGN)),
+    (dict(flags=wq.WQ_FLAG_ACT_ORDER, perm=0x6000, a_tmp=0x7000, group_index=0x6800, a=None),
+     status(STAGE_ARGS, wq.WQ_ERR_NULL)),
     (dict(split_k=2), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
     (dict(split_k=-1), status(STAGE_ARGS, wq.WQ_ERR_FLAGS)),
     (dict(flags=wq.WQ_FLAG_FP32_REDUCE, split_k=2), status(STAGE_ARGS, wq.WQ_ERR_WORKSPACE)),
@@ -344,3 +351,28 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(wq, "LIB_PATH", "/nonexistent/libwq.so")
     with pytest.raises(RuntimeError):
         wq.wq_abi_version()
+
+
+def test_gemm_plan_names_the_kernel_and_split():
+    """The planner's choice for the benchmarked shapes (host only, no device access)."""
+    fp32, zp, act = wq.WQ_FLAG_FP32_REDUCE, wq.WQ_FLAG_HAS_ZP, wq.WQ_FLAG_ACT_ORDER
+    small, t256, t128 = wq.WQ_KERNEL_SMALL_M, wq.WQ_KERNEL_TILE_256, wq.WQ_KERNEL_TILE_128
+    # decode: 896 column blocks fill the CUs, so the fp32 reduce flag leads to no split
+    assert wq.wq_gemm_plan(1, 14336, 4096, flags=fp32) == (small, 1)
+    assert wq.wq_gemm_plan(16, 4096, 4096, flags=fp32 | zp) == (small, 1)
+    assert wq.wq_gemm_plan(2048, 14336, 4096, flags=act) == (t256, 1)
+    # few column blocks: split along K (at most a quarter of the groups, one per wave)
+    assert wq.wq_gemm_plan(1, 256, 1024, flags=fp32) == (small, 2)
+    assert wq.wq_gemm_plan(1, 256, 4096, flags=fp32, split_k=3) == (small, 3)
+    assert wq.wq_gemm_plan(1, 256, 1024) == (small, 1)
+    # mid-size m: 128-row tiles, split when they are fewer than half the CUs
+    assert wq.wq_gemm_plan(64, 14336, 4096, flags=fp32) == (t128, 3)
+    assert wq.wq_gemm_plan(256, 14336, 4096, flags=fp32) == (t128, 2)
+    assert wq.wq_gemm_plan(256, 14336, 4096) == (t128, 1)
+    # the planner's split always fits the workspace the library asks for
+    for m, n in ((1, 256), (64, 14336), (256, 14336), (16, 512)):
+        _, s = wq.wq_gemm_plan(m, n, 1024 if n == 256 else 4096, flags=fp32)
+        need = wq.wq_gemm_workspace_bytes(m, n, 1024 if n == 256 else 4096, fp32)
+        assert s == 1 or need >= s * m * n * 4
+    with pytest.raises(wq.WQError):
+        wq.wq_gemm_plan(1, 100, 4096)

@@ -17,6 +17,7 @@ import numpy as np
 import pytest
 
 import synthetic
+from conftest import by_column_chunks
 from oracle import reference as ref
 
 torch = pytest.importorskip("torch")
@@ -155,15 +156,15 @@ def test_bf16_decode_config_in_full(dev):
     assert_parity(host(c), oracle_gemm(case), "bf16 decode config")
 
 
-def test_bf16_prefill_config_on_sampled_columns(dev):
+def test_bf16_prefill_config_in_full(dev):
     m, k, n = 2048, 4096, 14336
-    say("bf16 prefill config M=2048 K=4096 N=14336 g128 act_order (sampled columns)")
+    say("bf16 prefill config M=2048 K=4096 N=14336 g128 act_order (every output)")
     case = synthetic.dense_case(m, k, n, act_order=True, seed=5400, bf16=True)
     w = packed(case, dev)
     c = host(torch_ops.gemm(torch_ops.to_device(case["a"], dev), w))
     torch.cuda.synchronize()
-    cols = np.random.default_rng(5401).choice(n, 96, replace=False)
-    assert_parity(c[:, cols], oracle_gemm(case, columns=cols), "bf16 prefill sampled")
+    want = by_column_chunks(lambda cols: oracle_gemm(case, columns=cols), n)
+    assert_parity(c, want, "bf16 prefill")
 
 
 @pytest.mark.parametrize("tokens,experts,k,n,zp,weighted", [(40, 4, 256, 256, False, False),

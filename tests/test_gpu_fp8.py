@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 import synthetic
+from conftest import by_column_chunks
 from oracle import layout
 from oracle import reference as ref
 
@@ -122,16 +123,16 @@ def test_fp8_decode_config_in_full(dev):
     assert_parity(c, ref.w8a16_gemm(case["a"], case["qweight"], case["scales"]), "fp8 decode")
 
 
-def test_fp8_prefill_shape_on_sampled_columns(dev):
+def test_fp8_prefill_shape_in_full(dev):
     m, k, n = 2048, 4096, 14336
-    say("fp8 prefill shape M=2048 K=4096 N=14336 g128 (sampled columns)")
+    say("fp8 prefill shape M=2048 K=4096 N=14336 g128 (every output)")
     case = synthetic.fp8_case(m, k, n, seed=6300)
     w = torch_ops.PackedWeight(case["qweight"], case["scales"], device=dev, fp8=True)
     c = host(torch_ops.gemm(torch_ops.to_device(case["a"], dev), w))
     torch.cuda.synchronize()
-    cols = np.random.default_rng(6301).choice(n, 96, replace=False)
-    want = ref.w8a16_gemm(case["a"], case["qweight"], case["scales"], columns=cols)
-    assert_parity(c[:, cols], want, "fp8 prefill sampled")
+    want = by_column_chunks(
+        lambda cols: ref.w8a16_gemm(case["a"], case["qweight"], case["scales"], columns=cols), n)
+    assert_parity(c, want, "fp8 prefill")
 
 
 @pytest.mark.parametrize("tokens,experts,k,n,weighted", [(40, 4, 256, 256, False),

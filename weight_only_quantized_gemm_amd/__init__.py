@@ -16,7 +16,7 @@ import numpy as np
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libwq.so")
 
-WQ_ABI_VERSION = 2
+WQ_ABI_VERSION = 3
 WQ_FLAG_ACT_ORDER = 1 << 1
 WQ_FLAG_IS_K_FULL = 1 << 2
 WQ_FLAG_HAS_ZP = 1 << 3
@@ -37,8 +37,12 @@ EXPORTED = (
     "wq_act_order_perm", "wq_gemm_workspace_bytes", "wq_gemm", "wq_dequant",
     "wq_csr_from_routes", "wq_grouped_workspace_bytes", "wq_grouped_gemm",
     "wq_stream_read_sink_words", "wq_stream_read", "wq_interleave_gate_up", "wq_repack_fp8",
-    "wq_repack_fp8_rows", "wq_fp8_block_scales",
+    "wq_repack_fp8_rows", "wq_fp8_block_scales", "wq_mfma_rate", "wq_gemm_plan",
 )
+
+WQ_KERNEL_SMALL_M, WQ_KERNEL_TILE_256, WQ_KERNEL_TILE_128 = 1, 2, 3
+KERNEL_NAMES = {WQ_KERNEL_SMALL_M: "small-M (16-column blocks)",
+                WQ_KERNEL_TILE_256: "tiled 256 x 256", WQ_KERNEL_TILE_128: "tiled 128 x 256"}
 
 
 class WQError(RuntimeError):
@@ -54,7 +58,8 @@ class wq_gemm_args(ctypes.Structure):
         ("abi_version", ctypes.c_uint32), ("struct_size", ctypes.c_uint32),
         ("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("c", ctypes.c_void_p),
         ("b_scales", ctypes.c_void_p), ("zero_points", ctypes.c_void_p),
-        ("perm", ctypes.c_void_p), ("a_tmp", ctypes.c_void_p),
+        ("perm", ctypes.c_void_p), ("group_index", ctypes.c_void_p),
+        ("a_tmp", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
         ("m", ctypes.c_int32), ("n", ctypes.c_int32), ("k", ctypes.c_int32),
@@ -106,6 +111,8 @@ def lib() -> ctypes.CDLL:
             "wq_act_order_perm": (ctypes.c_int, [vp, i32, i32, vp, vp]),
             "wq_gemm_workspace_bytes": (ctypes.c_int, [i32, i32, i32, u32, ctypes.POINTER(sz)]),
             "wq_gemm": (ctypes.c_int, [ctypes.POINTER(wq_gemm_args)]),
+            "wq_gemm_plan": (ctypes.c_int, [i32, i32, i32, i32, u32, i32, ctypes.POINTER(i32),
+                                            ctypes.POINTER(i32)]),
             "wq_dequant": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, u32, vp, vp]),
             "wq_csr_from_routes": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp,
                                                   ctypes.POINTER(i32)]),
@@ -114,6 +121,8 @@ def lib() -> ctypes.CDLL:
             "wq_grouped_gemm": (ctypes.c_int, [ctypes.POINTER(wq_grouped_args)]),
             "wq_stream_read_sink_words": (ctypes.c_int, [sz, ctypes.POINTER(sz)]),
             "wq_stream_read": (ctypes.c_int, [vp, sz, vp, sz, vp]),
+            "wq_mfma_rate": (ctypes.c_int, [vp, i32, vp, sz, ctypes.POINTER(ctypes.c_double),
+                                            vp]),
             "wq_interleave_gate_up": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp]),
         }
         for name, (res, args) in sig.items():
@@ -205,7 +214,7 @@ def wq_gemm_workspace_bytes(m: int, n: int, k: int, flags: int = 0) -> int:
 
 
 def wq_gemm(a, b, c, b_scales, *, m: int, n: int, k: int, zero_points=None, perm=None,
-            a_tmp=None, workspace=None, workspace_bytes: int | None = None, flags: int = 0,
+            group_index=None, a_tmp=None, workspace=None, workspace_bytes: int | None = None, flags: int = 0,
             split_k: int = 0, lda: int | None = None, group_size: int = 128,
             stream=None) -> None:
     if workspace_bytes is None:
@@ -214,11 +223,21 @@ def wq_gemm(a, b, c, b_scales, *, m: int, n: int, k: int, zero_points=None, perm
     args = wq_gemm_args(
         abi_version=WQ_ABI_VERSION, struct_size=ctypes.sizeof(wq_gemm_args),
         a=_ptr(a), b=_ptr(b), c=_ptr(c), b_scales=_ptr(b_scales),
-        zero_points=_ptr(zero_points), perm=_ptr(perm), a_tmp=_ptr(a_tmp),
+        zero_points=_ptr(zero_points), perm=_ptr(perm), group_index=_ptr(group_index),
+        a_tmp=_ptr(a_tmp),
         workspace=_ptr(workspace), workspace_bytes=workspace_bytes,
         stream=_stream(stream, c), m=m, n=n, k=k, lda=k if lda is None else lda,
         group_size=group_size, flags=flags, split_k=split_k, reserved=0)
     _check(lib().wq_gemm(ctypes.byref(args)))
+
+
+def wq_gemm_plan(m: int, n: int, k: int, *, group_size: int = 128, flags: int = 0,
+                 split_k: int = 0) -> tuple[int, int]:
+    """(kernel, splits) the library picks for this problem (see include/wq.h)."""
+    kernel, splits = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib().wq_gemm_plan(m, n, k, group_size, flags, split_k, ctypes.byref(kernel),
+                              ctypes.byref(splits)))
+    return int(kernel.value), int(splits.value)
 
 
 def wq_dequant(b, b_scales, zero_points, w_out, *, k: int, n: int, flags: int = 0,
@@ -283,6 +302,15 @@ def wq_stream_read(src, nbytes: int, sink, sink_words: int, stream=None) -> None
     """Measurement helper: one streaming read of `nbytes` at `src` (see include/wq.h)."""
     _check(lib().wq_stream_read(_ptr(src), nbytes, _ptr(sink), sink_words,
                                 _stream(stream, src)))
+
+
+def wq_mfma_rate(operands, iters: int, sink, sink_floats: int, stream=None) -> float:
+    """Measurement helper: one register-only MFMA loop launch (see include/wq.h); returns
+    the launch's floating-point operation count."""
+    flops = ctypes.c_double(0.0)
+    _check(lib().wq_mfma_rate(_ptr(operands), iters, _ptr(sink), sink_floats,
+                              ctypes.byref(flops), _stream(stream, sink)))
+    return float(flops.value)
 
 
 def wq_interleave_gate_up(gate, up, out, rows: int, cols: int, bits_per_column: int,

@@ -30,10 +30,9 @@ int check_ptr(const void* p, size_t align) {
 }
 
 // Supported group sizes: -1 (one group over K, channelwise, as transformer.rs
-// `marlin_num_groups` maps it to one group), 32 and 64 (2 or 4 scale sub-groups per 128
-// rows, tiled kernel), or a multiple of 128 dividing K (its scales repeated for each
-// 128-row chunk it covers).  The pages also allow the other positive multiples of 16
-// dividing K; those are rejected here.
+// `marlin_num_groups` maps it to one group) and every positive multiple of 16 dividing K
+// (the pages' rule).  Scales and zero points are stored per unit of gcd(group_size, 128)
+// rows, so a group is repeated for each unit it covers.
 bool chunk_group_size(int k, int group_size) {
   if (group_size == -1) return true;
   return group_size > 0 && group_size % 16 == 0 && k % group_size == 0;
@@ -143,15 +142,13 @@ bool plan_small(int m, int n, int k, uint32_t flags, int requested, int gpc,
 }
 
 // fp32 partials [splits][m][n] for the largest split the small-M path may use, or for
-// m > 16 the split the tiled path chooses (the larger of its two geometries' choices, since
-// the group size is not known here).
+// m > 16 the split the tiled path chooses (the same for 128- and 64-row scale units; the
+// smaller units never split).
 size_t gemm_workspace_bytes(int m, int n, int k, uint32_t flags) {
   if (!(flags & WQ_FLAG_FP32_REDUCE)) return 0;
   if (m > 16) {
     const bool fp8 = (flags & WQ_FLAG_FP8) != 0, swiglu = (flags & WQ_FLAG_SWIGLU) != 0;
-    int s = wq::tile_splits(m, n, k, 1, fp8, swiglu);
-    const int s4 = wq::tile_splits(m, n, k, 4, fp8, swiglu);
-    if (s4 > s) s = s4;
+    const int s = wq::tile_splits(m, n, k, 1, fp8, swiglu);
     return s > 1 ? (size_t)s * m * n * sizeof(float) : 0;
   }
   int smax = k / kGroupSize;
@@ -338,6 +335,10 @@ int wq_gemm(const wq_gemm_args* args) {
     if ((st = check_ptr(p.perm, 16))) return st;
     if ((st = check_ptr(p.a_tmp, 16))) return st;
   }
+  // group_index only checks the act_order layout's groups (include/wq.h).
+  if (p.group_index != nullptr && !act_order) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
+  if (p.group_index != nullptr && !aligned(p.group_index, 4))
+    return fail(WQ_STAGE_ARGS, WQ_ERR_ALIGN);
   if (p.split_k < 0) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
   if (p.split_k > 1 && !(p.flags & WQ_FLAG_FP32_REDUCE)) return fail(WQ_STAGE_ARGS, WQ_ERR_FLAGS);
   const bool swiglu = (p.flags & WQ_FLAG_SWIGLU) != 0;
@@ -368,8 +369,9 @@ int wq_gemm(const wq_gemm_args* args) {
   const uint16_t* a = static_cast<const uint16_t*>(p.a);
   int lda = p.lda;
   if (act_order) {
-    const hipError_t e = wq::launch_gather_columns(a, lda, p.perm, static_cast<uint16_t*>(p.a_tmp),
-                                                   p.m, p.k, stream);
+    const hipError_t e =
+        wq::launch_gather_columns(a, lda, p.perm, p.group_index, p.group_size,
+                                  static_cast<uint16_t*>(p.a_tmp), p.m, p.k, stream);
     if (e != hipSuccess) return hip_fail(e);
     a = static_cast<const uint16_t*>(p.a_tmp);
     lda = p.k;
@@ -388,6 +390,28 @@ int wq_gemm(const wq_gemm_args* args) {
   const hipError_t e = wq::launch_gemm_tile(a, lda, p.m, b, s, z, c, p.n, p.k, swiglu, gpc, bf16,
                                              fp8, tile_split, partials, stream);
   return e == hipSuccess ? 0 : hip_fail(e);
+}
+
+int wq_gemm_plan(int m, int n, int k, int group_size, uint32_t flags, int split_k,
+                 int32_t* kernel_out, int32_t* splits_out) {
+  if (kernel_out == nullptr || splits_out == nullptr) return fail(WQ_STAGE_ARGS, WQ_ERR_NULL);
+  int st = check_kn(k, n, group_size);
+  if (st) return st;
+  if ((st = check_fp8(flags, group_size))) return st;
+  if (m <= 0 || split_k < 0) return fail(WQ_STAGE_SHAPE, WQ_ERR_SHAPE);
+  const bool swiglu = (flags & WQ_FLAG_SWIGLU) != 0, fp8 = (flags & WQ_FLAG_FP8) != 0;
+  const int gpc = subgroups(k, group_size);
+  wq::SmallPlan plan{};
+  const bool small = m <= 16 && (swiglu ? plan_small_pair(m, k, gpc, &plan)
+                                        : plan_small(m, n, k, flags, split_k, gpc, &plan));
+  if (small) {
+    *kernel_out = WQ_KERNEL_SMALL_M;
+    *splits_out = plan.splits;
+    return 0;
+  }
+  *kernel_out = wq::tile_is_tall(m, n, gpc, fp8) ? WQ_KERNEL_TILE_128 : WQ_KERNEL_TILE_256;
+  *splits_out = (flags & WQ_FLAG_FP32_REDUCE) ? wq::tile_splits(m, n, k, gpc, fp8, swiglu) : 1;
+  return 0;
 }
 
 int wq_dequant(const void* b, const void* b_scales, const void* zero_points, int k, int n,
@@ -546,6 +570,20 @@ int wq_interleave_gate_up(const void* gate, const void* up, void* out, int rows,
     return st;
   const hipError_t e = wq::launch_interleave_gate_up(gate, up, out, rows, cols,
                                                      bits_per_column, as_stream(stream));
+  return e == hipSuccess ? 0 : hip_fail(e);
+}
+
+int wq_mfma_rate(const void* operands, int iters, float* sink, size_t sink_floats,
+                 double* flops_out, void* stream) {
+  if (operands == nullptr || sink == nullptr || flops_out == nullptr)
+    return fail(WQ_STAGE_ARGS, WQ_ERR_NULL);
+  if (!aligned(operands, 16) || !aligned(sink, 4)) return fail(WQ_STAGE_ARGS, WQ_ERR_ALIGN);
+  if (iters <= 0 || iters > (1 << 20)) return fail(WQ_STAGE_SHAPE, WQ_ERR_SHAPE);
+  if (sink_floats < (size_t)wq::kMfmaBlocks * wq::kMfmaThreads)
+    return fail(WQ_STAGE_ARGS, WQ_ERR_WORKSPACE);
+  // waves x iterations x 8 products x 2 * 32 * 32 * 16 flops
+  *flops_out = (double)wq::kMfmaBlocks * (wq::kMfmaThreads / 64) * iters * 8 * 32768.0;
+  const hipError_t e = wq::launch_mfma_loop(operands, iters, sink, as_stream(stream));
   return e == hipSuccess ? 0 : hip_fail(e);
 }
 

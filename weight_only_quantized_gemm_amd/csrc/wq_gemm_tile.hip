@@ -11,6 +11,8 @@ hipError_t launch_tile_f16(const TileArgs& p, bool grouped, bool swiglu, bool zp
 
 constexpr int kCus = 256;
 
+bool tile_is_tall(int m, int n, int gpc, bool fp8) { return tile_tall(false, m, gpc, fp8, n); }
+
 int tile_splits(int m, int n, int k, int gpc, bool fp8, bool swiglu) {
   if (swiglu || fp8 || gpc > 2) return 1;
   const int tm = tile_rows(tile_tall(false, m, gpc, fp8, n));
@@ -45,6 +47,7 @@ hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b
   p.splits = splits;
   p.partials = partials;
   const bool tall = tile_tall(false, m, gpc, fp8, n);
+  if (splits > 1 && !tall) return hipErrorInvalidValue;  // only 128-row tiles split K
   const int tm = tile_rows(tall);
   p.tiles = (n / TN) * ((m + tm - 1) / tm) * splits;
   hipError_t e;

@@ -36,7 +36,10 @@ hipError_t launch_fp8_block_scales(const uint16_t* inv, uint16_t* out, int k, in
 // bf16: s and w hold bf16 values (else fp16).
 hipError_t launch_dequant(const uint32_t* b, const uint16_t* s, const uint32_t* z, int k, int n,
                           int unit, bool bf16, uint16_t* w, hipStream_t stream);
-hipError_t launch_gather_columns(const uint16_t* a, int lda, const int32_t* perm, uint16_t* out,
+// out[r][i] = a[r][perm[i]]; with group_index, columns whose entry is not i / group_size
+// (k for -1) are written as NaN.
+hipError_t launch_gather_columns(const uint16_t* a, int lda, const int32_t* perm,
+                                 const int32_t* group_index, int group_size, uint16_t* out,
                                  int m, int k, hipStream_t stream);
 
 // Small-M kernel (wq_gemm_small.hip): m <= 16, one 16-row MFMA block; with `splits` > 1
@@ -106,6 +109,8 @@ hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b
 // most 16); 1 for SwiGLU, E4M3 weights, 32- or 16-row scale units (gpc > 2) or enough
 // tiles.
 int tile_splits(int m, int n, int k, int gpc, bool fp8, bool swiglu);
+// Whether a dense tiled product takes 128 x 256 tiles (else 256 x 256).
+bool tile_is_tall(int m, int n, int gpc, bool fp8);
 
 struct GroupedProblem {
   const uint16_t* a;
@@ -128,6 +133,14 @@ struct GroupedProblem {
   bool fp8;               // the banks hold E4M3 weights in the FP8 layout
 };
 hipError_t launch_grouped_tile(const GroupedProblem& p, hipStream_t stream);
+
+// Register-only MFMA measurement helper (wq_measure.hip): kMfmaBlocks work-groups of
+// kMfmaThreads threads, each thread running `iters` steps of eight 32x32x16 fp16 MFMAs on
+// operands ops[6][64] (f16x8: four A operands, then two B operands) and storing one float.
+constexpr int kMfmaBlocks = 256;
+constexpr int kMfmaThreads = 512;
+constexpr int kMfmaLds = 96 * 1024;  // two work-groups never share a CU
+hipError_t launch_mfma_loop(const void* ops, int iters, float* sink, hipStream_t stream);
 
 // Streaming-read measurement helper (wq_measure.hip).
 long stream_read_sink_words(size_t bytes);

@@ -1,8 +1,12 @@
-// Measurement helper: a plain streaming read of a device buffer, the practical HBM read
-// ceiling that the weight-streaming GEMM is compared against.  It reads every byte once
-// with the same 16-byte non-temporal loads (eight per lane, all issued before any use) and
-// work-group shape (four waves) as the small-M GEMM, and keeps the data live through a
-// data-dependent store that practically never happens.
+// Measurement helpers, not steps of the method:
+//  - a plain streaming read of a device buffer, the practical HBM read ceiling that the
+//    weight-streaming GEMM is compared against.  It reads every byte once with the same
+//    16-byte non-temporal loads (eight per lane, all issued before any use) and work-group
+//    shape (four waves) as the small-M GEMM, and keeps the data live through a
+//    data-dependent store that practically never happens;
+//  - a register-only loop of the tiled GEMM's fp16 MFMAs on every CU, the practical matrix
+//    rate (the chip lowers its clock with the operands' switching activity, so the rate
+//    depends on the data the caller supplies).
 #include "wq_device.h"
 #include "wq_internal.h"
 
@@ -29,7 +33,53 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
   if (x == 0x9E3779B9u) sink[wave] = x;
 }
 
+// One work-group per CU (the dynamic LDS the launch requests keeps a second one away), two
+// waves per SIMD: each wave holds the A operands of four 32-row blocks and the B operands of
+// two 32-column blocks, the tiled GEMM's 128 x 64 wave tile, and runs `iters` steps of the
+// eight 32x32x16 products into eight fp32 accumulators.  Every thread stores its sum.
+__global__ __launch_bounds__(kMfmaThreads) void mfma_loop_kernel(const f16x8* __restrict__ ops,
+                                                                 int iters,
+                                                                 float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  f16x8 a[4], b[2];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) a[rb] = ops[rb * 64 + lane];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) b[cb] = ops[(4 + cb) * 64 + lane];
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma32x32x16(a[rb], b[cb], acc[rb][cb]);
+  }
+  float x = 0.f;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x += acc[rb][cb][r];
+  sink[(long)blockIdx.x * kMfmaThreads + threadIdx.x] = x;
+}
+
 }  // namespace
+
+hipError_t launch_mfma_loop(const void* ops, int iters, float* sink, hipStream_t stream) {
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_loop_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaLds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(mfma_loop_kernel, dim3(kMfmaBlocks), dim3(kMfmaThreads), kMfmaLds, stream,
+                     static_cast<const f16x8*>(ops), iters, sink);
+  return hipGetLastError();
+}
 
 long stream_read_sink_words(size_t bytes) {
   const long granules = (long)(bytes / 16);

@@ -212,10 +212,20 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
   }
 }
 
+// The act_order gather also checks an optional group_index against the layout's groups
+// (sorted position i in group i / gsz): a column whose entry differs is written as NaN
+// (0xFFFF is a NaN in both fp16 and bf16), so that every output of the product is NaN.
+__device__ __forceinline__ bool group_mismatch(const int32_t* gidx, int i, int gsz) {
+  return gidx != nullptr && gidx[i] != i / gsz;
+}
+constexpr uint16_t kNaN16 = 0xFFFF;
+
 // out[r][i] = a[r][perm[i]] for the act_order gather (eight columns per thread).
 __global__ __launch_bounds__(256) void gather_columns_kernel(const uint16_t* __restrict__ a,
                                                              int lda,
                                                              const int32_t* __restrict__ perm,
+                                                             const int32_t* __restrict__ gidx,
+                                                             int gsz,
                                                              uint16_t* __restrict__ out, int m,
                                                              int k) {
   const int per_row = k / 8;
@@ -232,7 +242,7 @@ __global__ __launch_bounds__(256) void gather_columns_kernel(const uint16_t* __r
     for (int j = 0; j < 8; ++j) {
       int c = j < 4 ? p0[j] : p1[j - 4];
       c = c < 0 ? 0 : (c >= k ? k - 1 : c);
-      v[j] = row[c];
+      v[j] = group_mismatch(gidx, i0 + j, gsz) ? kNaN16 : row[c];
     }
     u32x4 packed;
 #pragma unroll
@@ -244,12 +254,14 @@ __global__ __launch_bounds__(256) void gather_columns_kernel(const uint16_t* __r
 // Row-staged gather for K up to 8 * 256 * G: a work-group copies whole activation rows into
 // LDS with coalesced 16-byte loads (the next row's loads issued before the current row is
 // gathered), then each thread assembles its G output granules of 8 columns from LDS through
-// the permutation, which it holds in registers for all its rows.  Reading permuted columns
-// straight from global memory instead touches a different cache line per lane and load.
+// the permutation it holds in registers.  Reading permuted columns straight from global
+// memory touches a different cache line per lane and element.
 template <int G>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ a,
                                                           int lda,
                                                           const int32_t* __restrict__ perm,
+                                                          const int32_t* __restrict__ gidx,
+                                                          int gsz,
                                                           uint16_t* __restrict__ out, int m,
                                                           int k) {
   extern __shared__ u32x4 row_lds[];  // one row, k / 8 granules
@@ -257,14 +269,17 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
   const int t = threadIdx.x;
   const int granules = k / 8;
   int src[G][8];  // permuted source column of each output column (clamped into the row)
+  uint32_t bad[G];  // bit e: output column 8g + e fails the group_index check
 #pragma unroll
   for (int j = 0; j < G; ++j) {
     const int g = t + 256 * j;
     const int gg = g < granules ? g : granules - 1;
+    bad[j] = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int c = perm[8 * gg + e];
       src[j][e] = c < 0 ? 0 : (c >= k ? k - 1 : c);
+      bad[j] |= group_mismatch(gidx, 8 * gg + e, gsz) ? 1u << e : 0u;
     }
   }
   int r = blockIdx.x;
@@ -294,8 +309,11 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
       if (g >= granules) break;
       u32x4 packed;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        packed[e] = (uint32_t)row16[src[j][2 * e]] | ((uint32_t)row16[src[j][2 * e + 1]] << 16);
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = (bad[j] >> (2 * e)) & 1 ? kNaN16 : row16[src[j][2 * e]];
+        const uint32_t hi = (bad[j] >> (2 * e + 1)) & 1 ? kNaN16 : row16[src[j][2 * e + 1]];
+        packed[e] = lo | (hi << 16);
+      }
       *reinterpret_cast<u32x4*>(out + (long)r * k + 8 * g) = packed;
     }
   }
@@ -410,24 +428,27 @@ hipError_t launch_dequant(const uint32_t* b, const uint16_t* s, const uint32_t* 
 }
 
 template <int G>
-hipError_t launch_gather_rows(const uint16_t* a, int lda, const int32_t* perm, uint16_t* out,
-                              int m, int k, hipStream_t stream) {
+hipError_t launch_gather_rows(const uint16_t* a, int lda, const int32_t* perm,
+                              const int32_t* gidx, int gsz, uint16_t* out, int m, int k,
+                              hipStream_t stream) {
   // Up to 1024 work-groups (four per CU); larger m loops, amortizing the permutation loads.
   const int blocks = m < 1024 ? m : 1024;
   hipLaunchKernelGGL((gather_rows_kernel<G>), dim3(blocks), dim3(256), (size_t)k * 2, stream, a,
-                     lda, perm, out, m, k);
+                     lda, perm, gidx, gsz, out, m, k);
   return hipGetLastError();
 }
 
-hipError_t launch_gather_columns(const uint16_t* a, int lda, const int32_t* perm, uint16_t* out,
+hipError_t launch_gather_columns(const uint16_t* a, int lda, const int32_t* perm,
+                                 const int32_t* group_index, int group_size, uint16_t* out,
                                  int m, int k, hipStream_t stream) {
+  const int gsz = group_size == -1 ? k : group_size;
   const int granules = k / 8;
-  if (granules <= 256) return launch_gather_rows<1>(a, lda, perm, out, m, k, stream);
-  if (granules <= 512) return launch_gather_rows<2>(a, lda, perm, out, m, k, stream);
-  if (granules <= 1024) return launch_gather_rows<4>(a, lda, perm, out, m, k, stream);
-  if (granules <= 2048) return launch_gather_rows<8>(a, lda, perm, out, m, k, stream);
+  if (granules <= 256) return launch_gather_rows<1>(a, lda, perm, group_index, gsz, out, m, k, stream);
+  if (granules <= 512) return launch_gather_rows<2>(a, lda, perm, group_index, gsz, out, m, k, stream);
+  if (granules <= 1024) return launch_gather_rows<4>(a, lda, perm, group_index, gsz, out, m, k, stream);
+  if (granules <= 2048) return launch_gather_rows<8>(a, lda, perm, group_index, gsz, out, m, k, stream);
   hipLaunchKernelGGL(gather_columns_kernel, dim3(grid_for((long)m * (k / 8))), dim3(256), 0,
-                     stream, a, lda, perm, out, m, k);
+                     stream, a, lda, perm, group_index, gsz, out, m, k);
   return hipGetLastError();
 }
 

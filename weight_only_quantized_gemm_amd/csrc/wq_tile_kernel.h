@@ -31,9 +31,10 @@
 // running sums are multiplied by sigma_g / sigma_{g+1} (interleaved with those MFMAs), and
 // the result is multiplied by sigma_last at the end, so C = sum_g sigma_g * P_g with P_g
 // the exact-integer-weight partial of group g.  sigma is the 16-bit scale widened to fp32,
-// with an exact zero replaced by 2^-60 (its contribution then vanishes after rounding to
-// the output type; for bf16 a column whose every scale is zero comes out near 2^-60
-// times its partial sums instead of exactly zero).
+// with an exact zero replaced by 2^-60 so that the ratios stay finite: a zero-scale group
+// then adds 2^-60-relative noise to the other groups' sum, which no output rounding keeps.
+// A column whose every scale (in the work-group's range of K) is zero is written as
+// exactly zero: a flag per column records whether any nonzero scale was read.
 //
 // Tiles are assigned XCD-aware: work-groups are dealt to the 8 XCDs round-robin, so tile
 // ids are remapped to give each XCD a contiguous range (for a 2048-row problem, one
@@ -225,10 +226,11 @@ __device__ __forceinline__ void gemm_tile_body(TileArgs p) {
   // XCD-aware tile id: work-group i runs on XCD i % 8; give each XCD a contiguous range.
   int t = blockIdx.x;
   if (!GROUPED && p.tiles % kXcds == 0) t = (t % kXcds) * (p.tiles / kXcds) + t / kXcds;
-  // Dense split-K (128- and 64-row scale units; the instances for smaller units, already
-  // short of registers, are built without it): the splits of one tile are consecutive, and
-  // split s covers groups [groups_all * s / S, groups_all * (s + 1) / S) of K.
-  constexpr bool kSplitK = !GROUPED && GPC <= 2;
+  // Dense split-K (128-row tiles with 128- or 64-row scale units: the planner only splits
+  // products whose 256 x 256 tiles would be fewer than the CUs, and those take 128-row
+  // tiles): the splits of one tile are consecutive, and split s covers groups
+  // [groups_all * s / S, groups_all * (s + 1) / S) of K.
+  constexpr bool kSplitK = !GROUPED && TALL && GPC <= 2;
   const int split = kSplitK ? t % p.splits : 0;
   if (kSplitK) t /= p.splits;
   const int gs0 = kSplitK ? (int)((long)groups_all * split / p.splits) : 0;
@@ -447,6 +449,7 @@ __device__ __forceinline__ void gemm_tile_body(TileArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
   float sigma[2];
+  bool scaled[2] = {false, false};  // a nonzero scale of the lane's column has been read
   u32x4 bw[2][2];  // [cb][r]: vector r of the lane's column, rows 16*r + 8*h + ... per step
   Zo zo[2];
   const auto mr = A::magic();
@@ -457,7 +460,9 @@ __device__ __forceinline__ void gemm_tile_body(TileArgs p) {
     const uint16_t* sl = reinterpret_cast<const uint16_t*>(slot);
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      sg[cb] = sigma_of<BF16>(sl[bblk[cb] * 16 * GPC + 16 * q + c16]);
+      const uint16_t bits = sl[bblk[cb] * 16 * GPC + 16 * q + c16];
+      sg[cb] = sigma_of<BF16>(bits);
+      scaled[cb] = scaled[cb] || (bits & 0x7FFF) != 0;
       int zc = 8;
       if constexpr (ZP) {
         const uint32_t* zl = slot + SZ::kScaleWords + bblk[cb] * 2 * GPC + 2 * q;
@@ -728,7 +733,7 @@ __device__ __forceinline__ void gemm_tile_body(TileArgs p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = 128 * wm + 32 * rb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const float mine = acc[rb][cb][r] * sigma[cb];
+          const float mine = scaled[cb] ? acc[rb][cb][r] * sigma[cb] : 0.f;
           // ds_swizzle bit mode: and 0x1f, or 0, xor 0x10 (lanes l and l ^ 16 swap)
           const float other = __builtin_bit_cast(
               float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, mine), 0x401F));
@@ -755,7 +760,8 @@ __device__ __forceinline__ void gemm_tile_body(TileArgs p) {
           const int row = 128 * wm + 32 * rb + 8 * (r >> 2) + 4 * hh + (r & 3);
           const int orow = sm.row_c[row];
           if (orow >= 0)
-            p.partials[((long)split * p.m + orow) * p.n + col] = acc[rb][cb][r] * sigma[cb];
+            p.partials[((long)split * p.m + orow) * p.n + col] =
+                scaled[cb] ? acc[rb][cb][r] * sigma[cb] : 0.f;
         }
       }
     }
@@ -773,7 +779,8 @@ __device__ __forceinline__ void gemm_tile_body(TileArgs p) {
         const int orow = sm.row_c[row];
         // The routing weight (1 without the multiply) joins the scale, so that the output
         // is one rounding of acc * factor, as on the dense path.
-        const float factor = GROUPED ? sigma[cb] * sm.row_w[row] : sigma[cb];
+        const float sig = scaled[cb] ? sigma[cb] : 0.f;
+        const float factor = GROUPED ? sig * sm.row_w[row] : sig;
         if (orow >= 0)
           p.c[(long)orow * p.ldc + col] = A::round(acc[rb][cb][r] * factor);
       }

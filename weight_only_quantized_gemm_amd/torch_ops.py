@@ -55,9 +55,11 @@ class PackedWeight:
         self.swiglu = False
         self.device = torch.device(device)
         self.perm = None
+        self.group_index = None  # sorted per-position groups, checked by every act_order call
         if g_idx is not None:
-            perm, _ = wq_act_order_perm(g_idx, group_size)
+            perm, sorted_g = wq_act_order_perm(g_idx, group_size)
             self.perm = to_device(perm, self.device)
+            self.group_index = to_device(sorted_g, self.device)
         qw = to_device(qweight, self.device)
         if fp8:
             self.b = torch.empty(self.k * self.n // 4, dtype=torch.int32, device=self.device)
@@ -110,7 +112,7 @@ class PackedWeight:
         n, k = w_nk.shape
         w = object.__new__(cls)
         w.k, w.n, w.group_size, w.bf16, w.fp8, w.swiglu = k, n, GROUP, False, True, False
-        w.device, w.perm, w.z = dev, None, None
+        w.device, w.perm, w.group_index, w.z = dev, None, None, None
         src = torch.from_numpy(np.ascontiguousarray(w_nk, dtype=np.uint8)).to(dev)
         w.b = torch.empty(k * n // 4, dtype=torch.int32, device=dev)
         wq_repack_fp8_rows(src, w.b, k, n)
@@ -172,7 +174,7 @@ def gemm(a: torch.Tensor, w: PackedWeight, out: torch.Tensor | None = None, *,
     if buffers is None:
         buffers = GemmBuffers(w, m, fp32_reduce)
     wq_gemm(a, w.b, out, w.s, m=m, n=w.n, k=w.k, zero_points=w.z, perm=w.perm,
-            a_tmp=buffers.a_tmp, workspace=buffers.workspace, flags=buffers.flags,
+            group_index=w.group_index, a_tmp=buffers.a_tmp, workspace=buffers.workspace, flags=buffers.flags,
             split_k=split_k, lda=a.stride(0), group_size=w.group_size, stream=stream)
     return out
 

@@ -538,7 +538,10 @@ def test_moe_config_matches_oracle_in_full(dev, weighted):
     y, ex, ocsr = run_grouped(moe, dev, weights=w)
     want = by_column_chunks(lambda cols: ref.grouped_w4a16_gemm(
         moe["a"], ex, ocsr, columns=cols, topk_weights=w), moe["n"])
-    assert_parity(y, want, "moe")
+    # Routing weights shrink rms(ref) while the largest outputs keep |y| near 20, where the
+    # fp16 output's own rounding (half an ulp, at most 2^-11 |y|) exceeds 2e-3 rms + 1e-3:
+    # the weighted check adds that rounding bound per element.
+    assert_parity(y, want, "moe", rel_elem=2.0 ** -11 if weighted else 0.0)
 
 
 # --------------------------------------------------------------------------- graph replay

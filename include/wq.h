@@ -252,6 +252,22 @@ typedef struct wq_gemm_args {
 int wq_gemm(const wq_gemm_args* args);
 
 /*
+ * wq_gemm without caller scratch, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments and result as wq_gemm, except that workspace, workspace_bytes and a_tmp must be
+ * NULL / 0 (else WQ_ERR_WORKSPACE): the act_order gather buffer (m*k 16-bit values, rounded
+ * up to 256 bytes) and the split-K fp32 partials (splits*m*n floats, splits as
+ * wq_gemm_plan reports) come from one static device array of WQ_NOALLOC_SCRATCH_BYTES per
+ * GPU, reserved when the library is first used on that GPU and held until the process
+ * ends.  A problem whose scratch exceeds it fails with WQ_ERR_WORKSPACE before anything is
+ * enqueued.  It allocates and frees nothing.  All calls on one GPU share that array: calls
+ * that may overlap on one GPU (other streams, other threads) race and must be serialized by
+ * the caller.  The calling thread's current device must be the device of args->stream.
+ */
+#define WQ_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int wq_gemm_noalloc(const wq_gemm_args* args);
+
+/*
  * Dequant export for bit-exact tests: reads library-layout B, scales and optional zero
  * points and writes w[k][n] = rne((q - z) * s) (fp16, or bf16 with WQ_FLAG_BF16; row-major,
  * rows in the stored order, i.e. sorted order for act_order weights).  flags: HAS_ZP, BF16

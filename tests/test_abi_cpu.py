@@ -376,3 +376,16 @@ def test_gemm_plan_names_the_kernel_and_split():
         assert s == 1 or need >= s * m * n * 4
     with pytest.raises(wq.WQError):
         wq.wq_gemm_plan(1, 100, 4096)
+
+
+def test_noalloc_rejects_caller_scratch_and_oversize(L):
+    """wq_gemm_noalloc takes no caller scratch, and refuses problems whose scratch would
+    exceed its static array, before touching any device."""
+    ws = status(STAGE_ARGS, wq.WQ_ERR_WORKSPACE)
+    assert L.wq_gemm_noalloc(ctypes.byref(gemm_args(workspace=0x7000, workspace_bytes=64))) == ws
+    assert L.wq_gemm_noalloc(ctypes.byref(gemm_args(a_tmp=0x7000))) == ws
+    big = gemm_args(m=8192, k=4096, lda=4096, flags=wq.WQ_FLAG_ACT_ORDER, perm=0x6000)
+    assert L.wq_gemm_noalloc(ctypes.byref(big)) == ws
+    assert L.wq_gemm_noalloc(None) == status(STAGE_ARGS, wq.WQ_ERR_NULL)
+    assert L.wq_gemm_noalloc(ctypes.byref(gemm_args(abi_version=2))) == status(STAGE_ARGS,
+                                                                               wq.WQ_ERR_ABI)

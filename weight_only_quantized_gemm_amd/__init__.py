@@ -38,7 +38,9 @@ EXPORTED = (
     "wq_csr_from_routes", "wq_grouped_workspace_bytes", "wq_grouped_gemm",
     "wq_stream_read_sink_words", "wq_stream_read", "wq_interleave_gate_up", "wq_repack_fp8",
     "wq_repack_fp8_rows", "wq_fp8_block_scales", "wq_mfma_rate", "wq_gemm_plan",
+    "wq_gemm_noalloc",
 )
+WQ_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 WQ_KERNEL_SMALL_M, WQ_KERNEL_TILE_256, WQ_KERNEL_TILE_128 = 1, 2, 3
 KERNEL_NAMES = {WQ_KERNEL_SMALL_M: "small-M (16-column blocks)",
@@ -111,6 +113,7 @@ def lib() -> ctypes.CDLL:
             "wq_act_order_perm": (ctypes.c_int, [vp, i32, i32, vp, vp]),
             "wq_gemm_workspace_bytes": (ctypes.c_int, [i32, i32, i32, u32, ctypes.POINTER(sz)]),
             "wq_gemm": (ctypes.c_int, [ctypes.POINTER(wq_gemm_args)]),
+            "wq_gemm_noalloc": (ctypes.c_int, [ctypes.POINTER(wq_gemm_args)]),
             "wq_gemm_plan": (ctypes.c_int, [i32, i32, i32, i32, u32, i32, ctypes.POINTER(i32),
                                             ctypes.POINTER(i32)]),
             "wq_dequant": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, u32, vp, vp]),
@@ -229,6 +232,20 @@ def wq_gemm(a, b, c, b_scales, *, m: int, n: int, k: int, zero_points=None, perm
         stream=_stream(stream, c), m=m, n=n, k=k, lda=k if lda is None else lda,
         group_size=group_size, flags=flags, split_k=split_k, reserved=0)
     _check(lib().wq_gemm(ctypes.byref(args)))
+
+
+def wq_gemm_noalloc(a, b, c, b_scales, *, m: int, n: int, k: int, zero_points=None,
+                    perm=None, group_index=None, flags: int = 0, split_k: int = 0,
+                    lda: int | None = None, group_size: int = 128, stream=None) -> None:
+    """wq_gemm with the library's own static scratch (no workspace or a_tmp argument)."""
+    args = wq_gemm_args(
+        abi_version=WQ_ABI_VERSION, struct_size=ctypes.sizeof(wq_gemm_args),
+        a=_ptr(a), b=_ptr(b), c=_ptr(c), b_scales=_ptr(b_scales),
+        zero_points=_ptr(zero_points), perm=_ptr(perm), group_index=_ptr(group_index),
+        a_tmp=None, workspace=None, workspace_bytes=0,
+        stream=_stream(stream, c), m=m, n=n, k=k, lda=k if lda is None else lda,
+        group_size=group_size, flags=flags, split_k=split_k, reserved=0)
+    _check(lib().wq_gemm_noalloc(ctypes.byref(args)))
 
 
 def wq_gemm_plan(m: int, n: int, k: int, *, group_size: int = 128, flags: int = 0,

@@ -323,27 +323,40 @@ def test_prefill_config_matches_oracle_in_full(dev):
 
 # --------------------------------------------------------------------------- pins
 
-def test_all_eight_codes_give_exact_zero(dev):
-    for m in (1, 16, 300):
-        case = synthetic.dense_case(m, 512, 256, seed=3)
-        case["qweight"][:] = 0x88888888
-        c = gpu_gemm(case, dev, fp32_reduce=True)
-        assert np.all(c.astype(np.float64) == 0.0), m
-
-
 # One-row products run on 4x4x4 MFMAs, each lane summing its column over one row class of
-# every step, with the classes added by lane shuffles at the end.  With exact integer
-# weights the only errors are fp32 additions: every partial is a sum of at most
-# K exact products, added along a tree of depth below 64 (the 32-term chains of a unit, the
-# scaled fold over units, the shuffles and the four-wave reduction), so the unrounded
-# result is within 64 * 2^-24 * sum |a| |w| of the exact one.
+# every step, with the classes added by lane shuffles at the end.  The fp16 operands are
+# the codes q themselves (fp16 subnormals, exact) and the zero point enters once per scale
+# unit as z times the activations' sum over the lane's rows of the unit, so every partial
+# is an fp32 sum of exact terms whose magnitudes add up to at most sum |a| (q + z) s,
+# added along a tree of depth below 64 (the 32-term chains of a unit, the zero-point term,
+# the scaled fold over units, the shuffles and the four-wave reduction): the unrounded
+# result is within 64 * 2^-24 * sum |a| (q + z) s of the exact one.
 ACCUMULATION_ROUNDINGS = 64
 
 
 def accumulation_bound(case):
-    w = ref.w4a16_weights(case["qweight"], case["scales"], zeros=case.get("zeros"),
-                          group_size=case.get("group_size", 128))
-    return ACCUMULATION_ROUNDINGS * 2.0 ** -24 * (np.abs(case["a"].astype(np.float64)) @ np.abs(w))
+    k = case["qweight"].shape[0] * 8
+    gs = case.get("group_size", 128)
+    group = ref.group_of_rows(k, gs)
+    q = ref.unpack_qweight(case["qweight"]).astype(np.float64)
+    z = (8.0 if case.get("zeros") is None
+         else ref.unpack_zero_points(case["zeros"]).astype(np.float64)[group, :])
+    mag = (q + z) * ref.values16(case["scales"])[group, :]
+    return ACCUMULATION_ROUNDINGS * 2.0 ** -24 * (np.abs(case["a"].astype(np.float64)) @ mag)
+
+
+def test_all_eight_codes_give_zero(dev):
+    """Codes equal to the zero point give zero: exactly on the tiled kernel and the
+    small-M kernel's general path (the weights enter the products as exact zeros); within
+    the accumulation bound on the one-row path, where q * a and z * a are summed apart."""
+    for m in (1, 16, 300):
+        case = synthetic.dense_case(m, 512, 256, seed=3)
+        case["qweight"][:] = 0x88888888
+        c = gpu_gemm(case, dev, fp32_reduce=True).astype(np.float64)
+        if m == 1:
+            assert np.all(np.abs(c[0]) <= accumulation_bound(case)[0]), m
+        else:
+            assert np.all(c == 0.0), m
 
 
 ONE_ROW_SHAPES = [

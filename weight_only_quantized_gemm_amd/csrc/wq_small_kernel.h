@@ -32,11 +32,18 @@
 //  - Activation broadcast: one block's A operand serves the four blocks of a row class, so
 //    a lane reads two 4-row activation pieces per chunk instead of sixteen rows.
 //  - Only the real output row is scaled and accumulated.
-// fp16 keeps the exact dequant, so results are as exact as on the general path (all-zero
-// weights give exactly zero).  bf16, which has no packed add, takes 128 + q for every row as
-// on its general path; the excess (128 + z) times the activations' sum over the lane's rows
-// of a unit depends on the activations alone, and the staging threads form the sums per
-// unit and row class from the slice while the weights are in flight.
+//  - The zero point is applied once per scale unit, not per weight.  fp16 operands are the
+//    raw nibble bits read as fp16 subnormals: masking a word with 0x000F000F gives the
+//    pair (q * 2^-24, q' * 2^-24) and with 0x00F000F0 the pair (q * 2^-20, q' * 2^-20),
+//    both exact, so a word costs one shift and four ANDs instead of the general path's
+//    nine operations.  The two scales go to separate products (rows 0, 1, 4, 5 of the
+//    lane's eight at 2^-24, rows 2, 3, 6, 7 at 2^-20; the staged activations are stored
+//    with their middle dwords swapped to match), and a unit's exact-weight partial is
+//    2^24 p24 + 2^20 p20 - z S, S the activations' sum over the lane's rows of the unit.
+//    bf16, which has no packed add, takes 128 + q for every row as on its general path
+//    and subtracts (128 + z) S.  The staging threads form S per unit and row class from
+//    the slice while the weights are in flight.  The products are exact; only the fp32
+//    sums round, at magnitudes a few times those of the exact-weight sums.
 //
 // This header holds the kernel template and its launch chain; each translation unit that
 // includes it instantiates one GPC and activation type, so that the instances compile in
@@ -98,7 +105,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   // this avoids streaming the whole slice through LDS, write and read, behind a barrier.
   constexpr bool DA = STAGE == 0;
   static_assert(!DA || (GW <= 4 && !PAIR), "direct activations: at most 4 groups, no pair");
-  static_assert(!R1 || (!DA && !W8), "biased dequant: staged activations, 4-bit weights");
+  static_assert(!R1 || (!DA && !W8), "one-row path: staged activations, 4-bit weights");
   // DUAL: each wave applies its activation operands to two adjacent column blocks, so the
   // activations are read once per two blocks (direct activations, 4-bit weights).
   static_assert(!DUAL || (DA && !PAIR && !W8 && !R1), "dual blocks: direct activations");
@@ -115,15 +122,16 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   __shared__ uint32_t s_lds[SU * T];          // scales, [block][chunk][unit][col] as fp16
   __shared__ u32x2 z_lds[ZP ? ZU * T : 1];    // zero points, [block][chunk][unit]
   __shared__ f32x4 red[NBV][WAVES][64];
-  // R1: per scale unit of the slice, the activations weighted by the operand biases (plus
-  // 8 of each without zero points) and, with zero points, their plain sum.
+  // R1: per scale unit of the slice and row class, the activations' sum (the zero-point
+  // term of the unit's partial).
   constexpr int EX = GPC == 8 ? 2 : 4;  // activation sums per scale unit: one per row class
-  constexpr bool R1B = R1 && BF16;      // one row with biased bf16 operands
+  constexpr bool R1B = R1;              // one row: activation sums staged
   __shared__ float rsum_lds[R1B ? kMaxSpan * GPC * EX : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave-uniform: every per-wave index below is formed once, on the scalar unit
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15;  // column inside the 16-column block; also the A row of the lane
   const int qd = lane >> 4;   // which 8 rows of each 32-row MFMA step the lane carries
   const int half = PAIR ? wave / KW : 0;       // the wave's block of the pair
@@ -131,8 +139,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   const int nb = NB * blockIdx.x + half;
   const int split = blockIdx.y;
 
-  const int gs0 = (int)((long)groups * split / splits);
-  const int gs1 = (int)((long)groups * (split + 1) / splits);
+  // The work-group's range of K groups (groups * splits stays far below 2^31); a single
+  // split, the common case, needs no division.
+  int gs0 = 0, gs1 = groups;
+  if (splits > 1) {
+    gs0 = (int)((unsigned)(groups * split) / (unsigned)splits);
+    gs1 = (int)((unsigned)(groups * (split + 1)) / (unsigned)splits);
+  }
   const int span = gs1 - gs0;
   const int g0 = gs0 + span * kwave / KW;
   const int g1 = gs0 + span * (kwave + 1) / KW;
@@ -141,9 +154,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   // 1. Activation granules: slot u of this thread is granule tid + u*T of the slice, at row
   //    r and granule column q; (r, q) advance by a fixed (dr, dq) per slot.
   const int per_row = span * (kGroup / 8);
-  const int dr = T / per_row;
+  int dr = 0, r = 0;  // a row at least as long as a staging round needs no division
+  if (per_row < T) {
+    dr = T / per_row;
+    r = tid / per_row;
+  }
   const int dq = T - dr * per_row;
-  int r = tid / per_row;
   int q = tid - r * per_row;
   const f16* a_base = a + (long)gs0 * kGroup;
   f16x8 stage[DA ? 1 : STAGE];
@@ -213,7 +229,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   // 4. Stage into LDS (waits for the activations and scales only), then sync.
   if constexpr (!DA) {
 #pragma unroll
-    for (int u = 0; u < STAGE; ++u) a_lds[tid + u * T] = stage[u];
+    for (int u = 0; u < STAGE; ++u) {
+      // one row, fp16: rows 0, 1, 4, 5 of the granule first, then 2, 3, 6, 7 (the order of
+      // the subnormal operands' two products)
+      const u32x4 w = __builtin_bit_cast(u32x4, stage[u]);
+      a_lds[tid + u * T] = R1 && !BF16 ? __builtin_bit_cast(f16x8, u32x4{w[0], w[2], w[1], w[3]})
+                                       : stage[u];
+    }
   }
 #pragma unroll
   for (int u = 0; u < SU; ++u) s_lds[tid + u * T] = s_stage[u];
@@ -230,14 +252,21 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     constexpr int GR = 16 / GPC;
 #pragma unroll
     for (int u = 0; u < STAGE; ++u) {
-      // each bf16 is the upper half of a binary32 (the bf16 dot-product builtin on words
-      // reinterpreted as bf16 pairs is miscompiled by this toolchain: it reads word 0 four
-      // times)
+      // fp16: a dot product of each pair with ones (exact products, fp32 sums).  bf16: each
+      // value is the upper half of a binary32 (words reinterpreted as bf16 pairs for the dot
+      // builtin are miscompiled by this toolchain inside this loop: it reads word 0 four
+      // times).
       const u32x4 w = __builtin_bit_cast(u32x4, stage[u]);
       float rs = 0.f;
 #pragma unroll
-      for (int h = 0; h < 4; ++h)
-        rs += __builtin_bit_cast(float, w[h] << 16) + __builtin_bit_cast(float, w[h] & 0xFFFF0000u);
+      for (int h = 0; h < 4; ++h) {
+        if constexpr (BF16) {
+          rs += __builtin_bit_cast(float, w[h] << 16) + __builtin_bit_cast(float, w[h] & 0xFFFF0000u);
+        } else {
+          rs = __builtin_amdgcn_fdot2(f16x2{stage[u][2 * h], stage[u][2 * h + 1]},
+                                      f16x2{(f16)1.f, (f16)1.f}, rs, false);
+        }
+      }
 #pragma unroll
       for (int d = EX; d < GR; d *= 2) rs += __shfl_xor(rs, d);
       if (stage_real[u] && (tid & (GR - 1)) < EX)
@@ -284,11 +313,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   const auto zero_of = [&](int i, int t) {
     return ZP ? zero_code(z_lds[(half * span + gl[i]) * GPC + t], col) : 8;
   };
-  // R1 bf16: the bias excess of unit t of step i, for this lane's column and row class.
+  // R1: the zero-point term of unit t of step i, for this lane's column and row class:
+  // (bias + z) S, the bias 128 of the bf16 operands (none for the fp16 subnormals).
   const auto excess = [&](int i, int t) -> float {
     const int unit = gl[i] * GPC + t;
     const int slot = GPC == 8 ? unit * 2 + (qd & 1) : unit * 4 + qd;
-    return (128.f + (float)zero_of(i, t)) * rsum_lds[slot];
+    return ((BF16 ? 128.f : 0.f) + (float)zero_of(i, t)) * rsum_lds[slot];
   };
   // Hoisted with the scales for up to two units per chunk; with more, the registers would
   // cost a wave of occupancy, so the excess is read in place.
@@ -361,19 +391,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sc[i][0], p[e], acc[e]);
     } else if constexpr (R1) {
-      // Only row 0 of the product is real.  Operands of unit t: exact (q - z) for fp16,
-      // biased 128 + q for bf16.
-      const auto operand = [&](uint32_t w, int t) {
-        if constexpr (BF16)
-          return __builtin_bit_cast(u32x4, dequant8_bf_biased(w, mr));
-        else
-          return __builtin_bit_cast(u32x4, dequant8(w, zero_offsets(zero_of(i, t)), mr));
-      };
-      // the bias excess to remove from unit t's product (none for fp16)
+      // Only row 0 of the product is real.  Operands: the fp16 subnormal nibbles, or biased
+      // 128 + q for bf16 (see the header comment).
+      // the zero-point term to remove from unit t's product
       const auto unit_excess = [&](int t) -> float {
-        if constexpr (!BF16)
-          return 0.f;
-        else if constexpr (HX)
+        if constexpr (HX)
           return ex[i][t];
         else
           return excess(i, t);
@@ -391,27 +413,49 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
                                                     __builtin_bit_cast(h4, b2), cc, 2, ID, 0);
         }
       };
-      // step j's two products (rows 0-3 and 4-7 of the lane's eight), operands broadcast
-      // from products 2j and 2j + 1 of the chunk (ABID 2j % 4 and 2j % 4 + 1)
-      const auto mfma4 = [&](int j, u32x4 b, f32x4 cc) {
-        const u32x2 b0 = u32x2{b[0], b[1]}, b1 = u32x2{b[2], b[3]};
-        if (j & 1) {
-          cc = mfma1(ar[j >> 1], b0, cc, std::integral_constant<int, 2>{});
-          return mfma1(ar[j >> 1], b1, cc, std::integral_constant<int, 3>{});
+      // Step j's two products, operands broadcast from products 2j and 2j + 1 of the chunk
+      // (ABID 2j % 4 and 2j % 4 + 1).  bf16: rows 0-3 and 4-7 into one sum c24.  fp16:
+      // rows 0, 1, 4, 5 (nibbles at 2^-24) into c24, rows 2, 3, 6, 7 (at 2^-20) into c20,
+      // each against the matching half of the reordered activation granule.
+      const auto step = [&](int j, uint32_t w, f32x4& c24, f32x4& c20) {
+        u32x2 b0, b1;
+        if constexpr (BF16) {
+          const u32x4 b = __builtin_bit_cast(u32x4, dequant8_bf_biased(w, mr));
+          b0 = u32x2{b[0], b[1]};
+          b1 = u32x2{b[2], b[3]};
+        } else {
+          const uint32_t w8 = w >> 8;
+          b0 = u32x2{w & 0x000F000Fu, w8 & 0x000F000Fu};
+          b1 = u32x2{w & 0x00F000F0u, w8 & 0x00F000F0u};
         }
-        cc = mfma1(ar[j >> 1], b0, cc, std::integral_constant<int, 0>{});
-        return mfma1(ar[j >> 1], b1, cc, std::integral_constant<int, 1>{});
+        f32x4& second = BF16 ? c24 : c20;
+        if (j & 1) {
+          c24 = mfma1(ar[j >> 1], b0, c24, std::integral_constant<int, 2>{});
+          second = mfma1(ar[j >> 1], b1, second, std::integral_constant<int, 3>{});
+        } else {
+          c24 = mfma1(ar[j >> 1], b0, c24, std::integral_constant<int, 0>{});
+          second = mfma1(ar[j >> 1], b1, second, std::integral_constant<int, 1>{});
+        }
       };
+      // a unit's exact-weight partial: 2^24 c24 + 2^20 c20 - z S (fp16), c24 - (128 + z) S
+      // (bf16)
+      const auto unit_sum = [](f32x4 c24, f32x4 c20, float exv) -> float {
+        if constexpr (BF16)
+          return c24[0] - exv;
+        else
+          return __builtin_fmaf(__builtin_fmaf(c20[0], 0x1p-4f, c24[0]), 0x1p24f, -exv);
+      };
+      const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (GPC <= 4) {
 #pragma unroll
         for (int t = 0; t < GPC; ++t) {
-          f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
+          f32x4 c24 = zero4, c20 = zero4;
 #pragma unroll
           for (int jj = 0; jj < JQ; ++jj) {
             const int j = t * JQ + jj;
-            p = mfma4(j, operand(bw[i][bv][j], t), p);
+            step(j, bw[i][bv][j], c24, c20);
           }
-          acc[0] = __builtin_fmaf(sc[i][t], BF16 ? p[0] - unit_excess(t) : p[0], acc[0]);
+          acc[0] = __builtin_fmaf(sc[i][t], unit_sum(c24, c20, unit_excess(t)), acc[0]);
         }
       } else {
         // 16-row units: the lane's eight rows of step j lie in unit 2j + (qd >> 1).
@@ -419,9 +463,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int t = 2 * j + (qd >> 1);
-          const f32x4 p = mfma4(j, operand(bw[i][bv][j], t), f32x4{0.f, 0.f, 0.f, 0.f});
+          f32x4 c24 = zero4, c20 = zero4;
+          step(j, bw[i][bv][j], c24, c20);
           const float v = A::value(s_half[(ubase + t) * 16 + col]);
-          acc[0] = __builtin_fmaf(i < gw ? v : 0.f, BF16 ? p[0] - excess(i, t) : p[0], acc[0]);
+          acc[0] = __builtin_fmaf(i < gw ? v : 0.f, unit_sum(c24, c20, excess(i, t)), acc[0]);
         }
       }
     } else if constexpr (BF16) {

@@ -253,6 +253,27 @@ def bench_extended(torch, torch_ops, steps, warmup):
         "workload": "MoE config with a per-pair fp32 routing-weight multiply",
         "us": round(sec * 1e6, 2),
         "tflops": round(2.0 * csr["n_pairs"] * moe["n"] * moe["k"] / sec / 1e12, 2)}
+    del bank
+    # Many experts: 1024 tokens, top-2 of 64 experts (about 32 rows per expert), the same
+    # K and N; every expert holds the same synthetic weights (the time does not depend on
+    # the values), 64 x 29.4 MB of banks.
+    one = synthetic.moe_case(1024, 1, seed=41)
+    bank = torch_ops.ExpertBank(one["experts"] * 64, device="cuda")
+    routes = synthetic.top2_routes(43, 1024, 64)
+    csr = wq.wq_csr_from_routes(routes, 1024, 2, 64)
+    dcsr = {key: torch_ops.to_device(np.asarray(csr[key], np.int32), "cuda")
+            for key in ("ex_ids", "ex_off", "ex_pairs", "pair_tok")}
+    a = torch_ops.to_device(one["a"], "cuda")
+
+    def moe64_step(i):
+        torch_ops.grouped_gemm(a, bank, csr, y, device_csr=dcsr)
+    sec = timed_loop(torch, moe64_step, max(5, steps // 8), warmup)
+    out["moe_64_experts"] = {
+        "workload": "1024 tokens top-2 of 64 experts K=4096 N=14336 u4b8 group 128 "
+                    f"({csr['n_active']} active experts)",
+        "us": round(sec * 1e6, 2),
+        "tflops": round(2.0 * csr["n_pairs"] * one["n"] * one["k"] / sec / 1e12, 2),
+        "weight_tbs": round(csr["n_active"] * one["k"] * one["n"] / 2 / sec / 1e12, 4)}
     return out
 
 

@@ -732,3 +732,25 @@ def test_moe_swiglu_chain_matches_oracle(dev):
     oid["pair_tok"] = list(range(n_pairs))
     want = ref.grouped_w4a16_gemm(act16, [d for _, _, d in mats], oid, topk_weights=wts)
     assert_parity(out, want, "moe swiglu chain output", rel_elem=ACT_REL)
+
+
+@pytest.mark.parametrize("tokens,experts,k,n,gs,skew", [(600, 64, 512, 256, 128, False),
+                                                       (700, 300, 256, 256, 128, False),
+                                                       (900, 64, 512, 256, 128, True),
+                                                       (700, 300, 256, 256, 32, False)])
+def test_grouped_many_experts(dev, tokens, experts, k, n, gs, skew):
+    """Many experts: the tile lookup scans the segments in parallel (several rounds of the
+    work-group's threads beyond 256 or 512 segments); skewed routes mix full, partial and
+    tail tiles; 32-row scale units take the 256 x 256 geometry (512 threads)."""
+    label = f"grouped experts={experts} tokens={tokens} k={k} n={n} gs={gs} skew={skew}"
+    say(label)
+    moe = synthetic.moe_case(tokens, experts, k, n, group_size=gs, seed=500 + experts + tokens)
+    if skew:  # most first choices on three experts: segments of hundreds of rows and of few
+        r = moe["routes"]
+        r[: 2 * tokens // 3, 0] = np.arange(2 * tokens // 3) % 3
+        r[:, 1] = np.where(r[:, 1] == r[:, 0], (r[:, 0] + 7) % experts, r[:, 1])
+    for e in moe["experts"]:
+        e["group_size"] = gs
+    y, ex, ocsr = run_grouped(moe, dev)
+    assert len(ocsr["ex_ids"]) > 50
+    assert_parity(y, ref.grouped_w4a16_gemm(moe["a"], ex, ocsr, group_size=gs), label)

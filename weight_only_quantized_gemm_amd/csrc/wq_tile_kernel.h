@@ -188,6 +188,7 @@ struct Smem {
   int row_c[G::TM];
   float row_w[G::TM];  // grouped: routing weight of each output row (1 without the multiply)
   int info[5];
+  int wsum[2][16];  // grouped tile lookup: per-wave sums of the big and small tile counts
 };
 
 // The SwiGLU epilogue: B holds a gate and an up projection with their 16-column blocks
@@ -243,62 +244,104 @@ __device__ __forceinline__ void gemm_tile_body(TileArgs p) {
   const uint32_t* zptr;
 
   if constexpr (GROUPED) {
-    if (tid == 0) {
-      // Tiles in longest-first order.  A segment's row tiles are its full 256-row tiles
-      // plus a partial last one; a partial tile of at most G::kTailRows rows only busies the
-      // first half of the waves and is "small", every other tile is "big".  Each XCD takes
-      // a contiguous share of the big tiles (column tile fastest, so consecutive tiles
-      // reuse the same activation rows) followed by a share of the small ones, and work-
-      // groups are dispatched in order, so the small tiles fill the CUs that the last
-      // round of big tiles leaves idle.
-      int nbig = 0, nsmall = 0;
-      for (int i = 0; i < p.n_active; ++i) {
-        int a0 = p.ex_off[i], a1 = p.ex_off[i + 1];
+    // Tiles in longest-first order.  A segment's row tiles are its full TM-row tiles plus a
+    // partial last one; a partial tile of at most G::kTailRows rows only busies the first
+    // half of the waves and is "small", every other tile is "big".  Each XCD takes a
+    // contiguous share of the big tiles (column tile fastest, so consecutive tiles reuse the
+    // same activation rows) followed by a share of the small ones, and work-groups are
+    // dispatched in order, so the small tiles fill the CUs that the last round of big tiles
+    // leaves idle.  The lookup is parallel over segments (one per thread, in rounds of
+    // kThreads): a block-wide sum of the tile counts, then a block-wide prefix sum that the
+    // thread owning the work-group's tile index reads its tile from.
+    const int wv = tid >> 6;
+    // this thread's segment of round `base`: its big and small tile counts, and the segment
+    auto seg_tiles = [&](int base, int* big, int* small, int* lo, int* rows) {
+      const int i = base + tid;
+      int a0 = 0, a1 = 0;
+      if (i < p.n_active) {
+        a0 = p.ex_off[i];
+        a1 = p.ex_off[i + 1];
         a0 = a0 < 0 ? 0 : (a0 > p.n_pairs ? p.n_pairs : a0);
         a1 = a1 < a0 ? a0 : (a1 > p.n_pairs ? p.n_pairs : a1);
-        const int r = a1 - a0, full = r / G::TM, rem = r - full * G::TM;
-        nbig += full + (rem > G::kTailRows ? 1 : 0);
-        nsmall += (rem > 0 && rem <= G::kTailRows) ? 1 : 0;
       }
-      nbig *= ntiles_n;
-      nsmall *= ntiles_n;
-      const int b8 = (nbig + kXcds - 1) / kXcds, s8 = (nsmall + kXcds - 1) / kXcds;
-      const int x = (int)(blockIdx.x % kXcds), l = (int)(blockIdx.x / kXcds);
-      int kind = -1, idx = 0;  // 0 big, 1 small
-      if (l < b8) {
-        idx = x * b8 + l;
-        kind = idx < nbig ? 0 : -1;
-      } else if (l < b8 + s8) {
-        idx = x * s8 + (l - b8);
-        kind = idx < nsmall ? 1 : -1;
-      }
-      int seg = -1, lo = 0, rows = 0, mt = 0, nt = 0;
-      for (int i = 0; kind >= 0 && i < p.n_active; ++i) {
-        int a0 = p.ex_off[i], a1 = p.ex_off[i + 1];
-        a0 = a0 < 0 ? 0 : (a0 > p.n_pairs ? p.n_pairs : a0);
-        a1 = a1 < a0 ? a0 : (a1 > p.n_pairs ? p.n_pairs : a1);
-        const int r = a1 - a0, full = r / G::TM, rem = r - full * G::TM;
-        const int cnt = kind == 1 ? ((rem > 0 && rem <= G::kTailRows) ? 1 : 0)
-                                  : full + (rem > G::kTailRows ? 1 : 0);
-        const int tiles = cnt * ntiles_n;
-        if (idx < tiles) {
-          seg = i;
-          lo = a0;
-          rows = r;
-          mt = kind == 1 ? full : idx / ntiles_n;
-          nt = kind == 1 ? idx : idx - (idx / ntiles_n) * ntiles_n;
-          break;
+      const int r = a1 - a0, full = r / G::TM, rem = r - full * G::TM;
+      *big = (full + (rem > G::kTailRows ? 1 : 0)) * ntiles_n;
+      *small = (rem > 0 && rem <= G::kTailRows) ? ntiles_n : 0;
+      *lo = a0;
+      *rows = r;
+    };
+    // block-wide inclusive prefix sums of (x, y) over the threads, and their totals
+    auto block_scan = [&](int* x, int* y, int* tx, int* ty) {
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int ux = __shfl_up(*x, d), uy = __shfl_up(*y, d);
+        if (lane >= d) {
+          *x += ux;
+          *y += uy;
         }
-        idx -= tiles;
       }
-      int e = seg;
-      if (seg >= 0 && p.ex_ids != nullptr) e = p.ex_ids[seg];
-      if (e < 0 || e >= p.n_expert) seg = -1;
-      sm.info[0] = seg;
-      sm.info[1] = e;
-      sm.info[2] = lo + mt * G::TM;    // first CSR position of the tile
-      sm.info[3] = rows - mt * G::TM;  // CSR positions left in the segment from there
-      sm.info[4] = nt;
+      __syncthreads();  // the previous round's readers of wsum are done
+      if (lane == 63) {
+        sm.wsum[0][wv] = *x;
+        sm.wsum[1][wv] = *y;
+      }
+      __syncthreads();
+      int px = 0, py = 0, sx = 0, sy = 0;
+#pragma unroll
+      for (int w = 0; w < G::kWaves; ++w) {
+        const int vx = sm.wsum[0][w], vy = sm.wsum[1][w];
+        px += w < wv ? vx : 0;
+        py += w < wv ? vy : 0;
+        sx += vx;
+        sy += vy;
+      }
+      *x += px;
+      *y += py;
+      *tx = sx;
+      *ty = sy;
+    };
+    int nbig = 0, nsmall = 0;
+    for (int base = 0; base < p.n_active; base += G::kThreads) {
+      int b, sml, lo, rows, tb, ts;
+      seg_tiles(base, &b, &sml, &lo, &rows);
+      block_scan(&b, &sml, &tb, &ts);
+      nbig += tb;
+      nsmall += ts;
+    }
+    const int b8 = (nbig + kXcds - 1) / kXcds, s8 = (nsmall + kXcds - 1) / kXcds;
+    const int x = (int)(blockIdx.x % kXcds), l = (int)(blockIdx.x / kXcds);
+    int kind = -1, idx = 0;  // 0 big, 1 small
+    if (l < b8) {
+      idx = x * b8 + l;
+      kind = idx < nbig ? 0 : -1;
+    } else if (l < b8 + s8) {
+      idx = x * s8 + (l - b8);
+      kind = idx < nsmall ? 1 : -1;
+    }
+    if (tid == 0) sm.info[0] = -1;  // no tile unless a thread finds one below
+    int done_b = 0, done_s = 0;     // tiles of the earlier rounds
+    for (int base = 0; kind >= 0 && base < p.n_active; base += G::kThreads) {
+      int b, sml, lo, rows, tb, ts;
+      seg_tiles(base, &b, &sml, &lo, &rows);
+      const int cnt = kind == 1 ? sml : b;
+      int ib = b, is = sml;
+      block_scan(&ib, &is, &tb, &ts);
+      const int end = done_b * (kind == 0) + done_s * (kind == 1) + (kind == 1 ? is : ib);
+      const int start = end - cnt;
+      if (cnt > 0 && idx >= start && idx < end) {  // exactly one thread of the block
+        const int seg = base + tid, j = idx - start;
+        const int full = rows / G::TM;
+        const int mt = kind == 1 ? full : j / ntiles_n;
+        int e = seg;
+        if (p.ex_ids != nullptr) e = p.ex_ids[seg];
+        sm.info[0] = (e < 0 || e >= p.n_expert) ? -1 : seg;
+        sm.info[1] = e;
+        sm.info[2] = lo + mt * G::TM;    // first CSR position of the tile
+        sm.info[3] = rows - mt * G::TM;  // CSR positions left in the segment from there
+        sm.info[4] = kind == 1 ? j : j - (j / ntiles_n) * ntiles_n;
+      }
+      done_b += tb;
+      done_s += ts;
     }
     __syncthreads();
     const int seg = sm.info[0];

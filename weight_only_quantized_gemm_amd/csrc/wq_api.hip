@@ -94,9 +94,9 @@ bool plan_small_pair(int m, int k, int gpc, wq::SmallPlan* plan) {
 
 constexpr int kDirectRows = 9;
 // Two column blocks per wave halve the activation reads of the direct form but halve its
-// work-groups too.  Measured on MI355X at M=16, K=4096 with zero points: N=4096 (128
-// paired work-groups) 8.1 against 6.4 us; N=8192 (256) 9.0 against 10.6 us; N=14336 (448)
-// 13.6 against 18.1 us.
+// work-groups too.  Measured on MI355X at M=16, K=4096 with zero points (single blocks on
+// 8 waves of 4 groups, paired blocks on 4 waves of 8): N=4096 (128 paired work-groups)
+// 5.9 against 4.9 us; N=8192 (256) 7.0 against 8.8 us; N=14336 (448) 11.7 against 15.5 us.
 constexpr int kDualMinGroups = 256;
 
 bool plan_small(int m, int n, int k, uint32_t flags, int requested, int gpc,
@@ -115,10 +115,16 @@ bool plan_small(int m, int n, int k, uint32_t flags, int requested, int gpc,
   for (; s <= groups && s <= kMaxSplits; ++s) {
     if (s > 1 && !fp32) return false;
     const int span = (groups + s - 1) / s;
-    // From kDirectRows rows on, the activation slice through LDS costs more than each wave
-    // reading its own operands, so direct plans (at most 4 groups per wave) come first.
+    // From kDirectRows rows on, the activation slice shared through LDS costs more than
+    // each wave fetching its own groups' tiles, so direct plans come first.
     for (int pass = m >= kDirectRows ? 0 : 1; pass < 2; ++pass) {
-      for (int waves = 4; waves <= 8; waves *= 2) {
+      // Direct activations are read by every work-group in full; pairing two column blocks
+      // per wave halves those reads while at least kDualMinGroups work-groups remain (E4M3
+      // weights excepted).  Direct single blocks try 8 waves first, paired ones 4 (the
+      // faster of the two on MI355X at M=16, K=4096); staged plans 4 waves first.
+      const bool dual = pass == 0 && !(flags & WQ_FLAG_FP8) && (n / 32) * s >= kDualMinGroups;
+      for (int wi = 0; wi < 2; ++wi) {
+        const int waves = (pass == 0 && !dual) == (wi == 0) ? 8 : 4;
         const int per_wave = (span + waves - 1) / waves;
         if (per_wave > 8) continue;
         wq::SmallPlan p{};
@@ -127,10 +133,7 @@ bool plan_small(int m, int n, int k, uint32_t flags, int requested, int gpc,
         p.depth = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 8;
         p.gpc = gpc;
         p.direct = pass == 0;
-        // Direct activations are read by every work-group in full; pairing two column
-        // blocks per wave halves those reads while at least kDualMinGroups work-groups
-        // remain (E4M3 weights excepted).
-        p.dual = p.direct && !(flags & WQ_FLAG_FP8) && (n / 32) * s >= kDualMinGroups;
+        p.dual = dual;
         if (wq::small_plan_fits(m, k, p)) {
           *plan = p;
           return true;

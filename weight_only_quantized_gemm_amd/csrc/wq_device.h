@@ -62,6 +62,16 @@ __device__ __forceinline__ f16x8 dequant8(uint32_t w, ZeroOffsets zo, MagicRegs 
   return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// Wait until at most N of this wave's vector-memory operations are outstanding; they
+// complete in issue order, so this is the wait for everything issued before the last N.
+// Direct-to-LDS loads count here too, and the compiler does not wait for them by itself.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
+  // s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, expcnt 6:4 (7 = none), lgkmcnt 11:8.
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Zero-point code of column c (0..15) of a 16-column block: two words, 8 codes each.
 __device__ __forceinline__ int zero_code(u32x2 zw, int c) {
   const uint32_t w = (c < 8) ? zw[0] : zw[1];

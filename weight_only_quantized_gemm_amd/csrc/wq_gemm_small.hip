@@ -77,9 +77,11 @@ bool small_plan_fits(int m, int k, const SmallPlan& plan) {
   if (span > kMaxSpan || min_span < kw) return false;   // every wave has a group
   if ((span + kw - 1) / kw > plan.depth || plan.depth > 8) return false;
   if (plan.dual && !plan.direct) return false;
-  if (plan.direct)  // no activation slice; the operands of at most 4 groups in registers
-    return plan.depth <= 4 && !plan.pair &&
-           small_static_lds(plan.waves, plan.pair, plan.gpc, false, plan.dual) <= kLdsBytes;
+  if (plan.direct)  // per-wave LDS regions of `depth` activation tiles and scale words
+    return !plan.pair &&
+           small_static_lds(plan.waves, false, plan.gpc, false, plan.dual, true) +
+                   small_direct_lds(plan.waves, plan.depth, plan.gpc, true, plan.dual) <=
+               kLdsBytes;
   const int slots = stage_slots(m, span, plan.waves);
   const long dynamic = (long)round_slots(slots) * plan.waves * 64 * (long)sizeof(f16x8);
   return slots <= 16 &&

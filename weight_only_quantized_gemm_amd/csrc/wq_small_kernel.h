@@ -74,12 +74,27 @@ constexpr int small_zero_slots(int waves, bool pair, int gpc) {
              ? (pair ? 2 : 1) * kMaxSpan * gpc / (waves * 64) : 1;
 }
 // Static LDS of an instance (see the kernel's __shared__ arrays), an upper bound over ZP.
-// (pair: two column blocks split between the waves; dual: two column blocks per wave)
-constexpr long small_static_lds(int waves, bool pair, int gpc, bool r1, bool dual) {
+// (pair: two column blocks split between the waves; dual: two column blocks per wave;
+// direct: per-wave regions in the dynamic LDS instead, see small_direct_lds)
+constexpr long small_static_lds(int waves, bool pair, int gpc, bool r1, bool dual,
+                                bool direct = false) {
+  if (direct) return 4 + 8 + 16 + 4;
   return (long)small_scale_slots(waves, pair || dual, gpc) * waves * 64 * 4    // s_lds
          + (long)small_zero_slots(waves, pair || dual, gpc) * waves * 64 * 8   // z_lds
          + (long)(dual ? 2 : 1) * waves * 64 * 16                              // red
          + (r1 ? (long)kMaxSpan * 16 * 4 : 0);                                 // rsum_lds
+}
+
+// Direct activations: each wave owns an LDS region holding, for each of its GW groups, the
+// 16-row activation tile of the group (16 x 128 fp16, 4 KiB), and after all waves' tiles,
+// the scale (8 dwords per unit) and zero-point (2 per unit) words of its groups for each
+// of its column blocks, fetched 64 dwords per direct load.
+constexpr int kDirectTile = 16 * kGroup * 2;
+constexpr int direct_sz_loads(int gw, int gpc, bool zp) {
+  return (gw * gpc * (zp ? 10 : 8) + 63) / 64;
+}
+constexpr long small_direct_lds(int waves, int gw, int gpc, bool zp, bool dual) {
+  return (long)waves * ((long)gw * kDirectTile + (dual ? 2 : 1) * direct_sz_loads(gw, gpc, zp) * 256L);
 }
 
 // The kernel body is branch-free up to the arithmetic: every load is issued
@@ -100,11 +115,17 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   using A = Act<BF16>;
   static_assert(!W8 || (!ZP && GPC == 1), "E4M3: 128-row scale units, no zero points");
   constexpr int NV = W8 ? 2 : 1;  // 16-byte weight vectors per lane and group
-  // STAGE 0: no activation slice in LDS; each wave loads its own A operands (16 contiguous
-  // bytes per lane and 32-row step) into registers beside its weights.  For several rows
-  // this avoids streaming the whole slice through LDS, write and read, behind a barrier.
+  // STAGE 0 (direct activations): no shared slice; each wave fetches the activation tiles
+  // of its own groups, and the scales and zero points of its own groups and blocks, into
+  // its own LDS region with direct-to-LDS loads, so no barrier stands between the loads and
+  // the arithmetic.  An MFMA operand holds 16 rows of 16 bytes per 32-row step, so loading
+  // it straight into registers reads 16 rows x 64 bytes per instruction; the direct loads
+  // instead read four whole 256-byte row pieces per instruction (measured on MI355X at
+  // M=16, K=N=4096: 4.9 against 6.4 us).  A tile's 16 granules of row r are stored in the
+  // order (granule ^ r), so that the operand reads of 8 or 16 consecutive lanes (rows)
+  // fall in distinct banks.
   constexpr bool DA = STAGE == 0;
-  static_assert(!DA || (GW <= 4 && !PAIR), "direct activations: at most 4 groups, no pair");
+  static_assert(!DA || (GW <= 8 && !PAIR), "direct activations: at most 8 groups, no pair");
   static_assert(!R1 || (!DA && !W8), "one-row path: staged activations, 4-bit weights");
   // DUAL: each wave applies its activation operands to two adjacent column blocks, so the
   // activations are read once per two blocks (direct activations, 4-bit weights).
@@ -118,10 +139,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   constexpr int JQ = GPC <= 4 ? 4 / GPC : 1;  // 32-row MFMA steps per scale unit (GPC <= 4)
   static_assert(SU >= 1 && SU * T == NB * kMaxSpan * 8 * GPC, "scale slots cover the range");
   static_assert(ZU * T >= NB * kMaxSpan * GPC, "zero-point slots cover the range");
-  extern __shared__ f16x8 a_lds[];            // [m][span*16] granules (+ padding)
-  __shared__ uint32_t s_lds[SU * T];          // scales, [block][chunk][unit][col] as fp16
-  __shared__ u32x2 z_lds[ZP ? ZU * T : 1];    // zero points, [block][chunk][unit]
-  __shared__ f32x4 red[NBV][WAVES][64];
+  extern __shared__ f16x8 a_lds[];            // [m][span*16] granules (+ padding), or direct
+  __shared__ uint32_t s_lds[DA ? 1 : SU * T];          // scales, [block][chunk][unit][col]
+  __shared__ u32x2 z_lds[ZP && !DA ? ZU * T : 1];      // zero points, [block][chunk][unit]
+  __shared__ f32x4 red[DA ? 1 : NBV][DA ? 1 : WAVES][64];
   // R1: per scale unit of the slice and row class, the activations' sum (the zero-point
   // term of the unit's partial).
   constexpr int EX = GPC == 8 ? 2 : 4;  // activation sums per scale unit: one per row class
@@ -187,17 +208,17 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   const long pair0 = (long)NB * blockIdx.x * units + (long)gs0 * GPC;  // first block's range
   const uint32_t* s32 = reinterpret_cast<const uint32_t*>(s);
   const int s_words = span * GPC * 8;
-  uint32_t s_stage[SU];
+  uint32_t s_stage[DA ? 1 : SU];
 #pragma unroll
-  for (int u = 0; u < SU; ++u) {
+  for (int u = 0; u < (DA ? 0 : SU); ++u) {
     int i = tid + u * T;
     i = i < NB * s_words ? i : NB * s_words - 1;
     const int h = NB == 2 && i >= s_words ? 1 : 0;  // block of the pair holding dword i
     s_stage[u] = s32[(pair0 + h * units) * 8 + (i - h * s_words)];
   }
-  u32x2 z_stage[ZU];
+  u32x2 z_stage[DA ? 1 : ZU];
 #pragma unroll
-  for (int u = 0; u < ZU; ++u) {
+  for (int u = 0; u < (DA ? 0 : ZU); ++u) {
     z_stage[u] = u32x2{0u, 0u};
     if constexpr (ZP) {
       const int z_words = span * GPC;
@@ -210,20 +231,68 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 
   // 3. The wave's weight chunks, all in flight before any arithmetic.
   u32x4 bw[GW][NV * NBV];  // E4M3: the group's two vectors; DUAL: the two blocks' chunks
-  f16x8 ag[DA ? GW : 1][4];  // STAGE 0: the lane's activation operands of each group
-  const f16* a_row = a + (long)(col < m ? col : m - 1) * lda + 8 * qd;
-#pragma unroll
-  for (int i = 0; i < GW; ++i) {
+  const auto load_b = [&](int i) {
     const int g = g0 + (i < gw ? i : gw - 1);
 #pragma unroll
     for (int v = 0; v < NV * NBV; ++v)
       bw[i][v] = __builtin_nontemporal_load(
           &b[(DUAL ? (long)(nb + v) * groups + g : ((long)nb * groups + g) * NV + v) * 64 + lane]);
-    if constexpr (DA) {
+  };
+  // Direct activations: the wave's region (tiles of its GW groups) and its scale words.
+  constexpr int SZN = direct_sz_loads(GW, GPC, ZP);
+  constexpr int SZS = GW * GPC * 8;  // scale dwords per block; the zero-point words follow
+  f16x8* const a_own = a_lds + wave * GW * (kDirectTile / 16);
+  uint32_t* const sz_own =
+      reinterpret_cast<uint32_t*>(a_lds + WAVES * GW * (kDirectTile / 16)) + wave * NBV * SZN * 64;
+  if constexpr (DA) {
+    // Issue order: scale words, group 0's weights, every activation tile, the remaining
+    // weights; the scheduling barriers keep it, so the single wait below (for all loads but
+    // the trailing weights) covers the LDS data, and each group's weights are waited for
+    // in order as they are consumed.
+    const long unit0 = (long)g0 * GPC;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        ag[i][j] = *reinterpret_cast<const f16x8*>(a_row + (long)g * kGroup + 32 * j);
+    for (int v = 0; v < NBV; ++v) {
+      const long units0 = (long)(nb + v) * units + unit0;  // the block's first unit of the wave
+#pragma unroll
+      for (int u = 0; u < SZN; ++u) {
+        // dword d: scale dword d (d < SZS), else zero-point word d - SZS, clamped into the
+        // wave's gw groups (the trailing padding repeats the last word)
+        const int d = lane + 64 * u;
+        const uint32_t* src;
+        if (!ZP || d < SZS) {
+          const int e = d < gw * GPC * 8 ? d : gw * GPC * 8 - 1;
+          src = reinterpret_cast<const uint32_t*>(s) + units0 * 8 + e;
+        } else {
+          const int e = d - SZS < gw * GPC * 2 ? d - SZS : gw * GPC * 2 - 1;
+          src = reinterpret_cast<const uint32_t*>(z) + units0 * 2 + e;
+        }
+        __builtin_amdgcn_global_load_lds(src, sz_own + (v * SZN + u) * 64, 4, 0, 0);
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < GW; ++i) {
+      // tile load t: rows 4t .. 4t + 3 (clamped to m - 1), lane granule (lane & 15) ^ row
+      const int g = g0 + (i < gw ? i : gw - 1);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int r = 4 * t + (lane >> 4);
+        const int rr = r < m ? r : m - 1;
+        __builtin_amdgcn_global_load_lds(
+            a + (long)rr * lda + (long)g * kGroup + 8 * ((lane & 15) ^ r),
+            a_own + (i * 4 + t) * 64, 16, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 1; i < GW; ++i) load_b(i);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<(GW - 1) * NV * NBV>();
+  } else {
+#pragma unroll
+    for (int i = 0; i < GW; ++i) load_b(i);
   }
 
   // 4. Stage into LDS (waits for the activations and scales only), then sync.
@@ -237,11 +306,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
                                        : stage[u];
     }
   }
+  if constexpr (!DA) {
 #pragma unroll
-  for (int u = 0; u < SU; ++u) s_lds[tid + u * T] = s_stage[u];
-  if constexpr (ZP) {
+    for (int u = 0; u < SU; ++u) s_lds[tid + u * T] = s_stage[u];
+    if constexpr (ZP) {
 #pragma unroll
-    for (int u = 0; u < ZU; ++u) z_lds[tid + u * T] = z_stage[u];
+      for (int u = 0; u < ZU; ++u) z_lds[tid + u * T] = z_stage[u];
+    }
   }
   if constexpr (R1B) {
     // A unit of the slice is GR consecutive granules, held by GR consecutive lanes of one
@@ -273,7 +344,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
         rsum_lds[stage_q[u] / GR * EX + stage_q[u] % EX] = rs;
     }
   }
-  __syncthreads();
+  if constexpr (!DA) __syncthreads();
 
   // 5. Arithmetic.  MFMA rows >= m are never stored, and a row of the product depends on
   //    its own A row only, so those lanes read row m - 1 instead of selecting zeros.  The
@@ -291,6 +362,22 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   const int arow = (col < m ? col : m - 1) * per_row;
   const uint16_t* s_half = reinterpret_cast<const uint16_t*>(s_lds);
   int gl[GW];  // chunk of step i inside the staged range (clamped for the masked steps)
+  // Scale bits of unit t of step i for this lane's column, and the zero-point words of that
+  // unit, for block hb of the work-group (staged) or of the wave (direct).
+  const auto scale_bits = [&](int hb, int i, int t) -> uint16_t {
+    if constexpr (DA)
+      return reinterpret_cast<const uint16_t*>(sz_own + hb * SZN * 64)[(i * GPC + t) * 16 + col];
+    else
+      return s_half[((hb * span + gl[i]) * GPC + t) * 16 + col];
+  };
+  const auto zero_word = [&](int hb, int i, int t) -> u32x2 {
+    if constexpr (DA) {
+      const uint32_t* zw = sz_own + hb * SZN * 64 + SZS + 2 * (i * GPC + t);
+      return u32x2{zw[0], zw[1]};
+    } else {
+      return z_lds[(hb * span + gl[i]) * GPC + t];
+    }
+  };
   constexpr int HS = GPC <= 4 ? GPC : 1;  // scales hoisted per chunk (read in place for 8)
   float scs[NBV][GW][HS];                   // per column block of the wave
 #pragma unroll
@@ -302,7 +389,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
         const int hv = DUAL ? v : half;
 #pragma unroll
         for (int t = 0; t < GPC; ++t) {
-          const float x = A::value(s_half[((hv * span + gl[i]) * GPC + t) * 16 + col]);
+          const float x = A::value(scale_bits(hv, i, t));
           scs[v][i][t] = i < gw ? x : 0.f;
         }
       }
@@ -311,7 +398,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   auto& sc = scs[0];  // the scales of the wave's only (or first) block
   // unit t of step i: its zero point for this lane's column
   const auto zero_of = [&](int i, int t) {
-    return ZP ? zero_code(z_lds[(half * span + gl[i]) * GPC + t], col) : 8;
+    return ZP ? zero_code(zero_word(half, i, t), col) : 8;
   };
   // R1: the zero-point term of unit t of step i, for this lane's column and row class:
   // (bias + z) S, the bias 128 of the bf16 operands (none for the fp16 subnormals).
@@ -364,8 +451,15 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
       ar[1] = an1[1];
       if (i + 1 < GW) r1_operands(gl[i + 1], an1);
     } else {
+      if constexpr (DA) {
+        // lane (row col, class qd) of step j: granule 4j + qd of row col, in tile load col / 4
 #pragma unroll
-      for (int j = 0; j < 4; ++j) ac[j] = DA ? ag[i][j] : an[j];
+        for (int j = 0; j < 4; ++j)
+          ac[j] = a_own[(i * 4 + (col >> 2)) * 64 + 16 * (col & 3) + ((4 * j + qd) ^ col)];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ac[j] = an[j];
+      }
       if (!DA && i + 1 < GW) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) an[j] = a_lds[arow + gl[i + 1] * 16 + 4 * j + qd];
@@ -459,13 +553,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
         }
       } else {
         // 16-row units: the lane's eight rows of step j lie in unit 2j + (qd >> 1).
-        const int ubase = (half * span + gl[i]) * 8;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int t = 2 * j + (qd >> 1);
           f32x4 c24 = zero4, c20 = zero4;
           step(j, bw[i][bv][j], c24, c20);
-          const float v = A::value(s_half[(ubase + t) * 16 + col]);
+          const float v = A::value(scale_bits(half, i, t));
           acc[0] = __builtin_fmaf(i < gw ? v : 0.f, unit_sum(c24, c20, excess(i, t)), acc[0]);
         }
       }
@@ -481,7 +574,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
       if constexpr (GPC <= 4) {
 #pragma unroll
         for (int t = 0; t < GPC; ++t) {
-          const int zc = ZP ? zero_code(z_lds[(half * span + gl[i]) * GPC + t], col) : 8;
+          const int zc = ZP ? zero_code(zero_word(half, i, t), col) : 8;
           const float off = (float)(128 + zc);
           f32x4 p = zero4, r = zero4;
 #pragma unroll
@@ -497,7 +590,6 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
       } else {
         // 16-row units: as on the fp16 path, each MFMA sees one unit's half of the step.
         const int hi = qd >> 1;
-        const int ubase = (half * span + gl[i]) * 8;
         const bf16x8 zero8{};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -506,10 +598,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
           const f32x4 p1 = A::mfma16(ac[j], hi ? w : zero8, zero4);
           const f32x4 r0 = A::mfma16(ac[j], hi ? zero8 : ones, zero4);
           const f32x4 r1 = A::mfma16(ac[j], hi ? ones : zero8, zero4);
-          const int z0 = ZP ? zero_code(z_lds[ubase + 2 * j], col) : 8;
-          const int z1 = ZP ? zero_code(z_lds[ubase + 2 * j + 1], col) : 8;
-          const float v0 = A::value(s_half[(ubase + 2 * j) * 16 + col]);
-          const float v1 = A::value(s_half[(ubase + 2 * j + 1) * 16 + col]);
+          const int z0 = ZP ? zero_code(zero_word(half, i, 2 * j), col) : 8;
+          const int z1 = ZP ? zero_code(zero_word(half, i, 2 * j + 1), col) : 8;
+          const float v0 = A::value(scale_bits(half, i, 2 * j));
+          const float v1 = A::value(scale_bits(half, i, 2 * j + 1));
           const float s0 = i < gw ? v0 : 0.f;
           const float s1 = i < gw ? v1 : 0.f;
 #pragma unroll
@@ -523,7 +615,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     } else if constexpr (GPC <= 4) {
 #pragma unroll
       for (int t = 0; t < GPC; ++t) {
-        const auto zo = A::zero(ZP ? zero_code(z_lds[(half * span + gl[i]) * GPC + t], col) : 8);
+        const auto zo = A::zero(ZP ? zero_code(zero_word(half, i, t), col) : 8);
         f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int jj = 0; jj < JQ; ++jj) {
@@ -537,18 +629,17 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
       // 16-row units: the lane's 8 rows of step j lie in unit 2j + hi.  Its weights enter
       // the MFMA of that unit and zeros the other's, so each product sums one unit only.
       const int hi = qd >> 1;
-      const int ubase = (half * span + gl[i]) * 8;
       const typename A::W8 zero8{};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const auto zo = A::zero(ZP ? zero_code(z_lds[ubase + 2 * j + hi], col) : 8);
+        const auto zo = A::zero(ZP ? zero_code(zero_word(half, i, 2 * j + hi), col) : 8);
         const typename A::W8 w = A::dequant(bw[i][bv][j], zo, mr);
         const f32x4 p0 = A::mfma16(ac[j], hi ? zero8 : w, f32x4{0.f, 0.f, 0.f, 0.f});
         const f32x4 p1 = A::mfma16(ac[j], hi ? w : zero8, f32x4{0.f, 0.f, 0.f, 0.f});
         // (the reads are unconditional, in bounds through the clamped chunk; a masked step
         // selects zero scales)
-        const float v0 = A::value(s_half[(ubase + 2 * j) * 16 + col]);
-        const float v1 = A::value(s_half[(ubase + 2 * j + 1) * 16 + col]);
+        const float v0 = A::value(scale_bits(half, i, 2 * j));
+        const float v1 = A::value(scale_bits(half, i, 2 * j + 1));
         const float s0 = i < gw ? v0 : 0.f;
         const float s1 = i < gw ? v1 : 0.f;
 #pragma unroll
@@ -566,17 +657,25 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     accs[0][0] += __shfl_xor(accs[0][0], 16);
     accs[0][0] += __shfl_xor(accs[0][0], 32);
   }
-  // Work-group reduce over the waves, in wave order.
+  // Work-group reduce over the waves, in wave order.  Direct plans put each wave's sums at
+  // the start of its own region (its operand reads precede the writes in the wave's LDS
+  // order, and no other wave reads that region).
+  const auto red_at = [&](int v, int w) -> f32x4* {
+    if constexpr (DA)
+      return reinterpret_cast<f32x4*>(a_lds + w * GW * (kDirectTile / 16)) + v * 64;
+    else
+      return red[v][w];
+  };
 #pragma unroll
-  for (int v = 0; v < NBV; ++v) red[v][wave][lane] = accs[v];
+  for (int v = 0; v < NBV; ++v) red_at(v, wave)[lane] = accs[v];
   __syncthreads();
   if (wave != 0) return;
   if constexpr (PAIR) {
-    f32x4 gs = red[0][0][lane], us = red[0][KW][lane];
+    f32x4 gs = red_at(0, 0)[lane], us = red_at(0, KW)[lane];
 #pragma unroll
     for (int w = 1; w < KW; ++w) {
-      gs += red[0][w][lane];
-      us += red[0][KW + w][lane];
+      gs += red_at(0, w)[lane];
+      us += red_at(0, KW + w)[lane];
     }
     const long colj = (long)blockIdx.x * 16 + col;  // column of the [m][n/2] activation
 #pragma unroll
@@ -588,9 +687,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   }
 #pragma unroll
   for (int v = 0; v < NBV; ++v) {
-    f32x4 tot = red[v][0][lane];
+    f32x4 tot = red_at(v, 0)[lane];
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) tot += red[v][w][lane];
+    for (int w = 1; w < WAVES; ++w) tot += red_at(v, w)[lane];
 
     // Output layout of the 16x16 block: lane holds rows 4*qd + e of column `col`.
     const long colx = (long)(nb + v) * 16 + col;
@@ -623,8 +722,10 @@ hipError_t launch_small_t(const uint16_t* a, int lda, int m, const uint32_t* b,
                           const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                           int splits, float* partials, hipStream_t stream) {
   const int groups = k / kGroup;
-  // The activation slice of this instance (its size is fixed by STAGE and WAVES).
-  constexpr size_t lds = (size_t)STAGE * WAVES * 64 * sizeof(f16x8);
+  // The activation slice of this instance (its size is fixed by STAGE and WAVES), or the
+  // waves' direct regions.
+  constexpr size_t lds = STAGE == 0 ? (size_t)small_direct_lds(WAVES, GW, GPC, ZP, DUAL)
+                                    : (size_t)STAGE * WAVES * 64 * sizeof(f16x8);
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(
           &gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16, W8, R1, DUAL>),
@@ -646,7 +747,7 @@ hipError_t launch_small_stage(const uint16_t* a, int lda, int m, const uint32_t*
                               const SmallPlan& plan, float* partials, hipStream_t stream) {
   const int span = (k / kGroup + plan.splits - 1) / plan.splits;
   if (plan.direct) {
-    if constexpr (GW <= 4 && !PAIR) {
+    if constexpr (!PAIR) {
       if constexpr (!W8) {
         if (plan.dual)
           return launch_small_t<ZP, WAVES, GW, 0, PAIR, GPC, BF16, W8, false, true>(

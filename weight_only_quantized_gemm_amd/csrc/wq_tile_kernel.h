@@ -154,12 +154,6 @@ constexpr int kSchedVALU = 0x002;
 constexpr int kSchedMFMA = 0x008;
 constexpr int kSchedDSRead = 0x100;
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  // s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, expcnt 6:4 (7 = none), lgkmcnt 11:8.
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // All of this wave's LDS reads have returned (vmcnt and expcnt not waited for).
 __device__ __forceinline__ void wait_lds_reads() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));

@@ -1,16 +1,17 @@
 // Small-M W4A16 GEMM (m <= 16): decode and small batches, bound by the weight stream.
 //
-// One 16x16x32 fp16 MFMA block covers all m rows (rows >= m repeat row m - 1 and are never
-// stored), so the packed weights are read exactly once.  A work-group owns one 16-column block and a range of K
-// groups; its WAVES waves split that range, each streaming one 1 KiB layout chunk per
-// 128-row group with a single non-temporal 16-byte load per lane.  All of a wave's weight
-// loads are issued before any arithmetic and consumed in issue order, so the weight
-// stream is never stalled behind compute.  Activations, scales and zero points reach LDS
-// one of two ways: staged once for the work-group's range by all its threads (few rows), or
-// fetched by each wave for its own groups with direct-to-LDS loads (9 rows and more, the
-// "direct" form below).  Codes become exact fp16 integers (q - z) in
-// registers; each scale group's MFMA partial is scaled by its fp16 group scale in fp32 and
-// accumulated in fp32; the waves' sums are added in wave order.
+// One 16x16x32 fp16 MFMA block covers all m rows (rows >= m repeat row m - 1 and are
+// never stored), so the packed weights are read exactly once.  A work-group owns one
+// 16-column block and a range of K groups; its WAVES waves split that range, each
+// streaming one 1 KiB layout chunk per 128-row group with a single non-temporal 16-byte
+// load per lane.  All of a wave's weight loads are issued before any arithmetic and
+// consumed in issue order, so the weight stream is never stalled behind compute.
+// Activations, scales and zero points reach LDS one of two ways: staged once for the
+// work-group's range by all its threads (few rows), or fetched by each wave for its own
+// groups with direct-to-LDS loads (9 rows and more; the "direct" form below).  Codes become
+// exact fp16 integers (q - z) in registers; each scale group's MFMA partial is scaled by
+// its fp16 group scale in fp32 and accumulated in fp32; the waves' sums are added in wave
+// order.
 //
 // GPC is the number of scale units per 128-row chunk: scales and zero points are stored
 // per unit of gcd(group_size, 128) rows (128, 64, 32 or 16), so a chunk owns GPC = 1, 2, 4
@@ -96,7 +97,8 @@ constexpr int direct_sz_loads(int gw, int gpc, bool zp) {
   return (gw * gpc * (zp ? 10 : 8) + 63) / 64;
 }
 constexpr long small_direct_lds(int waves, int gw, int gpc, bool zp, bool dual) {
-  return (long)waves * ((long)gw * kDirectTile + (dual ? 2 : 1) * direct_sz_loads(gw, gpc, zp) * 256L);
+  return (long)waves *
+         ((long)gw * kDirectTile + (dual ? 2 : 1) * direct_sz_loads(gw, gpc, zp) * 256L);
 }
 
 // The kernel body is branch-free up to the arithmetic: every load is issued

@@ -100,11 +100,12 @@ def test_zero_scales_grouped(dev, bf16):
     check(yh, ref.grouped_w4a16_gemm(moe["a"], ex, ocsr, bf16=bf16), label, bf16)
 
 
-@pytest.mark.parametrize("m", [5, 300])
-def test_group_index_is_checked(dev, m):
+@pytest.mark.parametrize("m,k", [(5, 1024), (300, 1024), (3, 16512)])
+def test_group_index_is_checked(dev, m, k):
     """The sorted per-position groups change no bit; a group_index that disagrees with the
-    layout's groups turns every output into NaN."""
-    k, n = 1024, 512
+    layout's groups turns every output into NaN.  K = 16512 takes the per-column gather
+    (rows longer than the row-staged gather holds)."""
+    n = 512
     case = synthetic.dense_case(m, k, n, act_order=True, seed=960 + m)
     w = torch_ops.PackedWeight(case["qweight"], case["scales"], None, case["g_idx"], device=dev)
     a = torch_ops.to_device(case["a"], dev)
@@ -115,7 +116,7 @@ def test_group_index_is_checked(dev, m):
     without = host(torch_ops.gemm(a, w, buffers=bufs))
     assert np.array_equal(with_gi.view(np.uint16), without.view(np.uint16))
     want = ref.w4a16_gemm(case["a"], case["qweight"], case["scales"], g_idx=case["g_idx"])
-    check(with_gi, want, f"group_index m={m}", False)
+    check(with_gi, want, f"group_index m={m} k={k}", False)
     bad = saved.clone()
     bad[200] += 1                      # one position claims the next group
     w.group_index = bad

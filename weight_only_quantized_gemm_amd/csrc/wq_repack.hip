@@ -213,14 +213,14 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
 }
 
 // The act_order gather also checks an optional group_index against the layout's groups
-// (sorted position i in group i / gsz): a column whose entry differs is written as NaN
-// (0xFFFF is a NaN in both fp16 and bf16), so that every output of the product is NaN.
-__device__ __forceinline__ bool group_mismatch(const int32_t* gidx, int i, int gsz) {
-  return gidx != nullptr && gidx[i] != i / gsz;
-}
+// (sorted position i in group i / gsz; CHECK instances): a column whose entry differs is
+// written as NaN (0xFFFF is a NaN in both fp16 and bf16), so that every output of the
+// product is NaN.  Positions 8g .. 8g + 7 lie in group q = 8g / gsz, or q + 1 from the
+// position where 8g - q gsz + e reaches gsz (gsz >= 16: at most two groups).
 constexpr uint16_t kNaN16 = 0xFFFF;
 
 // out[r][i] = a[r][perm[i]] for the act_order gather (eight columns per thread).
+template <bool CHECK>
 __global__ __launch_bounds__(256) void gather_columns_kernel(const uint16_t* __restrict__ a,
                                                              int lda,
                                                              const int32_t* __restrict__ perm,
@@ -237,12 +237,18 @@ __global__ __launch_bounds__(256) void gather_columns_kernel(const uint16_t* __r
     const i32x4 p0 = *reinterpret_cast<const i32x4*>(perm + i0);
     const i32x4 p1 = *reinterpret_cast<const i32x4*>(perm + i0 + 4);
     const uint16_t* row = a + r * lda;
+    int q = 0, rem = 0;
+    if constexpr (CHECK) {
+      q = i0 / gsz;
+      rem = i0 - q * gsz;
+    }
     uint16_t v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       int c = j < 4 ? p0[j] : p1[j - 4];
       c = c < 0 ? 0 : (c >= k ? k - 1 : c);
-      v[j] = group_mismatch(gidx, i0 + j, gsz) ? kNaN16 : row[c];
+      v[j] = row[c];
+      if constexpr (CHECK) v[j] = gidx[i0 + j] != q + (rem + j >= gsz ? 1 : 0) ? kNaN16 : v[j];
     }
     u32x4 packed;
 #pragma unroll
@@ -255,8 +261,12 @@ __global__ __launch_bounds__(256) void gather_columns_kernel(const uint16_t* __r
 // LDS with coalesced 16-byte loads (the next row's loads issued before the current row is
 // gathered), then each thread assembles its G output granules of 8 columns from LDS through
 // the permutation it holds in registers.  Reading permuted columns straight from global
-// memory touches a different cache line per lane and element.
-template <int G>
+// memory touches a different cache line per lane and element.  CHECK: a column that fails
+// the group_index check gathers from a NaN slot past the row's end instead, so the gather
+// itself carries no per-element test.  The check is a template parameter so that both
+// prologues are straight-line code: a branch per element would end a basic block after
+// every load and serialize the loads (measured 2-3x slower at M=2048, K=4096).
+template <int G, bool CHECK>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ a,
                                                           int lda,
                                                           const int32_t* __restrict__ perm,
@@ -264,22 +274,31 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
                                                           int gsz,
                                                           uint16_t* __restrict__ out, int m,
                                                           int k) {
-  extern __shared__ u32x4 row_lds[];  // one row, k / 8 granules
+  extern __shared__ u32x4 row_lds[];  // one row, k / 8 granules, then one granule of NaNs
   const uint16_t* row16 = reinterpret_cast<const uint16_t*>(row_lds);
   const int t = threadIdx.x;
   const int granules = k / 8;
-  int src[G][8];  // permuted source column of each output column (clamped into the row)
-  uint32_t bad[G];  // bit e: output column 8g + e fails the group_index check
+  if (t == 0) row_lds[granules] = u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+  // Permuted source column of each output column (clamped into the row), or k (the NaN
+  // slot) where group_index disagrees with the layout's group of the sorted position.
+  int src[G][8];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
     const int g = t + 256 * j;
     const int gg = g < granules ? g : granules - 1;
-    bad[j] = 0;
+    // sorted position 8gg + e lies in group q, or q + 1 once rem + e reaches gsz (gsz >= 16,
+    // so a granule's eight positions span at most two groups)
+    int q = 0, rem = 0;
+    if constexpr (CHECK) {
+      q = 8 * gg / gsz;
+      rem = 8 * gg - q * gsz;
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int c = perm[8 * gg + e];
-      src[j][e] = c < 0 ? 0 : (c >= k ? k - 1 : c);
-      bad[j] |= group_mismatch(gidx, 8 * gg + e, gsz) ? 1u << e : 0u;
+      int sc = c < 0 ? 0 : (c >= k ? k - 1 : c);
+      if constexpr (CHECK) sc = gidx[8 * gg + e] != q + (rem + e >= gsz ? 1 : 0) ? k : sc;
+      src[j][e] = sc;
     }
   }
   int r = blockIdx.x;
@@ -309,11 +328,8 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
       if (g >= granules) break;
       u32x4 packed;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = (bad[j] >> (2 * e)) & 1 ? kNaN16 : row16[src[j][2 * e]];
-        const uint32_t hi = (bad[j] >> (2 * e + 1)) & 1 ? kNaN16 : row16[src[j][2 * e + 1]];
-        packed[e] = lo | (hi << 16);
-      }
+      for (int e = 0; e < 4; ++e)
+        packed[e] = (uint32_t)row16[src[j][2 * e]] | ((uint32_t)row16[src[j][2 * e + 1]] << 16);
       *reinterpret_cast<u32x4*>(out + (long)r * k + 8 * g) = packed;
     }
   }
@@ -433,8 +449,12 @@ hipError_t launch_gather_rows(const uint16_t* a, int lda, const int32_t* perm,
                               hipStream_t stream) {
   // Up to 1024 work-groups (four per CU); larger m loops, amortizing the permutation loads.
   const int blocks = m < 1024 ? m : 1024;
-  hipLaunchKernelGGL((gather_rows_kernel<G>), dim3(blocks), dim3(256), (size_t)k * 2, stream, a,
-                     lda, perm, gidx, gsz, out, m, k);
+  if (gidx != nullptr)
+    hipLaunchKernelGGL((gather_rows_kernel<G, true>), dim3(blocks), dim3(256), (size_t)k * 2 + 16,
+                       stream, a, lda, perm, gidx, gsz, out, m, k);
+  else
+    hipLaunchKernelGGL((gather_rows_kernel<G, false>), dim3(blocks), dim3(256),
+                       (size_t)k * 2 + 16, stream, a, lda, perm, gidx, gsz, out, m, k);
   return hipGetLastError();
 }
 
@@ -447,8 +467,12 @@ hipError_t launch_gather_columns(const uint16_t* a, int lda, const int32_t* perm
   if (granules <= 512) return launch_gather_rows<2>(a, lda, perm, group_index, gsz, out, m, k, stream);
   if (granules <= 1024) return launch_gather_rows<4>(a, lda, perm, group_index, gsz, out, m, k, stream);
   if (granules <= 2048) return launch_gather_rows<8>(a, lda, perm, group_index, gsz, out, m, k, stream);
-  hipLaunchKernelGGL(gather_columns_kernel, dim3(grid_for((long)m * (k / 8))), dim3(256), 0,
-                     stream, a, lda, perm, group_index, gsz, out, m, k);
+  if (group_index != nullptr)
+    hipLaunchKernelGGL(gather_columns_kernel<true>, dim3(grid_for((long)m * (k / 8))), dim3(256),
+                       0, stream, a, lda, perm, group_index, gsz, out, m, k);
+  else
+    hipLaunchKernelGGL(gather_columns_kernel<false>, dim3(grid_for((long)m * (k / 8))),
+                       dim3(256), 0, stream, a, lda, perm, group_index, gsz, out, m, k);
   return hipGetLastError();
 }
 

@@ -79,6 +79,9 @@ BF16_SHAPES = [
     (64, 1024, 256, 32, True, False, False, 0),
     (130, 1536, 512, 16, False, False, False, 0),
     (40, 1024, 256, -1, True, False, False, 0),
+    # direct activation tiles: 8 waves x 4 groups (one block), 4 waves x 8 (two blocks)
+    (12, 4096, 4096, 64, True, False, False, 0),
+    (16, 4096, 8192, 128, True, False, True, 0),
     # one row: biased operands on 4x4x4 products, every unit size
     (1, 2048, 512, 16, True, False, True, 0),
     (1, 1024, 768, 32, False, False, False, 0),

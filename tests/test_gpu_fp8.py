@@ -94,7 +94,8 @@ FP8_SHAPES = [
     (300, 1024, 512, 128, False, 0),
     (257, 384, 256, -1, False, 0),
     (513, 2048, 768, 128, False, 0),
-    (11, 2048, 256, 128, False, 0),   # activation operands in registers
+    (11, 2048, 256, 128, False, 0),   # direct activation tiles
+    (16, 4096, 4096, 128, False, 0),  # direct, 8 waves x 4 groups of two vectors each
     (14, 4096, 256, -1, True, 2),
 ]
 

@@ -250,9 +250,9 @@ def test_small_m_group_sizes_match_oracle(dev, m, k, n, gs, zp, act_order, fp32,
     assert_parity(c, oracle_gemm(case), label)
 
 
-# 9..16 rows: the small-M kernel loads each wave's activation operands straight into
-# registers (no LDS slice) when a wave holds at most 4 groups; with enough column blocks
-# each wave applies them to two blocks.
+# 9..16 rows: each wave of the small-M kernel fetches its own groups' activation tiles,
+# scales and zero points into its own LDS region (no shared slice, no barrier before the
+# arithmetic); with enough column blocks each wave applies them to two blocks.
 DIRECT_SHAPES = [
     # m, k, n, group_size, zp, act_order, fp32_reduce, split_k
     (9, 4096, 256, 16, True, False, False, 0),
@@ -266,6 +266,12 @@ DIRECT_SHAPES = [
     (12, 4096, 1024, 64, False, True, True, 8),
     (11, 1024, 8192, 32, False, False, False, 0),
     (14, 768, 8192, -1, True, False, False, 0),
+    # 4 waves of 8 groups over two blocks; with 16-row units ten scale loads per block
+    (16, 4096, 8192, 128, True, False, False, 0),
+    (9, 4096, 8192, 16, True, False, False, 0),
+    # 8 waves of 4 groups over one block, 16-row units (five scale loads)
+    (16, 4096, 4096, 16, True, False, False, 0),
+    (15, 3072, 4096, 48, False, True, True, 0),
 ]
 
 

@@ -1,0 +1,113 @@
+"""A seeded sweep of dense products over both kernels and every plan form (staged and
+direct small-M, paired blocks, the one-row path, 128- and 256-row tiles, split K), every
+activation and weight type, group sizes, zero points, act_order and strided activations,
+each compared with the CPU oracle on every output.
+
+The shapes come from a fixed-seed generator, so the sweep is the same on every run; each
+case prints its parameters before it runs.
+"""
+
+import numpy as np
+import pytest
+
+import synthetic
+from oracle import reference as ref
+
+torch = pytest.importorskip("torch")
+wq = pytest.importorskip("weight_only_quantized_gemm_amd")
+from weight_only_quantized_gemm_amd import torch_ops  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+# Tolerances: fp16 outputs use the GEMM criterion; bf16 outputs add their own rounding
+# (2^-8 |ref| per element, Frobenius 4e-3); E4M3 weights add the fp16 output's rounding per
+# element (their magnitudes span 2^-9 .. 448, far beyond the rms).
+FP16_TOL = {}
+BF16_TOL = dict(rel_elem=2.0 ** -8, rel_frob=4e-3)
+FP8_TOL = dict(rel_elem=2.0 ** -11)
+
+M_CHOICES = [1, 2, 3, 5, 8, 9, 12, 16, 17, 33, 64, 100, 129, 256, 300]
+K_CHOICES = [128, 256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096]
+N_CHOICES = [256, 512, 768, 1024, 2048, 4096, 8192]
+GS_CHOICES = [-1, 16, 32, 48, 64, 80, 96, 128, 256, 512, 1024]
+
+
+def sweep_cases(count=160, seed=20261203):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        kind = ["u4b8", "u4zp", "bf16", "fp8"][int(rng.integers(4))]
+        m = int(rng.choice(M_CHOICES))
+        k = int(rng.choice(K_CHOICES))
+        n = int(rng.choice(N_CHOICES))
+        if m * k * n > 1_500_000_000 or (m > 16 and n > 4096):
+            continue  # keeps each oracle product well under a second
+        if kind == "fp8":
+            gs = int(rng.choice([-1, 128]))
+        else:
+            gs = int(rng.choice([g for g in GS_CHOICES if g == -1 or (g <= k and k % g == 0)]))
+        zp = kind == "u4zp" or (kind == "bf16" and bool(rng.integers(2)))
+        act_order = kind != "fp8" and rng.random() < 0.3
+        fp32 = bool(rng.integers(2))
+        split = int(rng.choice([0, 0, 2, 3, 5])) if fp32 else 0
+        lda_pad = int(rng.choice([0, 0, 0, 8, 64]))
+        bf16_act = kind == "bf16" or (kind == "fp8" and rng.random() < 0.25)
+        cases.append((kind, m, k, n, gs, zp, act_order, fp32, split, lda_pad, bf16_act))
+    return cases
+
+
+CASES = sweep_cases()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def to_host(t):
+    return t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+def strided(a, pad, dev, bf16):
+    """The activations on the device with row stride k + pad (pad columns hold NaNs that no
+    product may read)."""
+    m, k = a.shape
+    dt = torch.bfloat16 if bf16 else torch.float16
+    base = torch_ops.to_device(a, dev)
+    if pad == 0:
+        return base
+    wide = torch.full((m, k + pad), float("nan"), dtype=dt, device=dev)
+    wide[:, :k] = base
+    return wide[:, :k]
+
+
+@pytest.mark.parametrize("kind,m,k,n,gs,zp,act_order,fp32,split,lda_pad,bf16_act", CASES)
+def test_sweep_matches_oracle(dev, kind, m, k, n, gs, zp, act_order, fp32, split, lda_pad,
+                              bf16_act):
+    label = (f"sweep {kind} m={m} k={k} n={n} group_size={gs} zp={zp} act_order={act_order} "
+             f"fp32={fp32} split={split} lda=k+{lda_pad} bf16={bf16_act}")
+    print(label, flush=True)
+    seed = 7000 + m * 31 + k * 7 + n + gs
+    if kind == "fp8":
+        case = synthetic.fp8_case(m, k, n, group_size=gs, seed=seed, bf16=bf16_act)
+        w = torch_ops.PackedWeight(case["qweight"], case["scales"], device=dev, group_size=gs,
+                                   bf16=bf16_act, fp8=True)
+        want = ref.w8a16_gemm(case["a"], case["qweight"], case["scales"], group_size=gs,
+                              bf16=bf16_act)
+        tol = BF16_TOL if bf16_act else FP8_TOL
+    else:
+        case = synthetic.dense_case(m, k, n, zp=zp, act_order=act_order, group_size=gs,
+                                    seed=seed, bf16=bf16_act)
+        w = torch_ops.PackedWeight(case["qweight"], case["scales"], case["zeros"],
+                                   case["g_idx"], device=dev, group_size=gs, bf16=bf16_act)
+        want = ref.w4a16_gemm(case["a"], case["qweight"], case["scales"], zeros=case["zeros"],
+                              g_idx=case["g_idx"], group_size=gs, bf16=bf16_act)
+        tol = BF16_TOL if bf16_act else FP16_TOL
+    a = strided(case["a"], lda_pad, dev, bf16_act)
+    c = torch_ops.gemm(a, w, fp32_reduce=fp32, split_k=split)
+    torch.cuda.synchronize()
+    res = ref.check(to_host(c), want, **tol)
+    print(f"{label}: max_err={res['max_err']:.3e} tol={res['tol']:.3e} "
+          f"rel_frob={res['rel_frob']:.3e} nonfinite={res['nonfinite']}", flush=True)
+    assert res["ok"], (label, res)

@@ -1,7 +1,8 @@
 """A seeded sweep of dense products over both kernels and every plan form (staged and
 direct small-M, paired blocks, the one-row path, 128- and 256-row tiles, split K), every
 activation and weight type, group sizes, zero points, act_order and strided activations,
-each compared with the CPU oracle on every output.
+and of grouped (MoE) products over token and expert counts, types, group sizes, zero
+points and routing weights, each compared with the CPU oracle on every output.
 
 The shapes come from a fixed-seed generator, so the sweep is the same on every run; each
 case prints its parameters before it runs.
@@ -108,6 +109,58 @@ def test_sweep_matches_oracle(dev, kind, m, k, n, gs, zp, act_order, fp32, split
     c = torch_ops.gemm(a, w, fp32_reduce=fp32, split_k=split)
     torch.cuda.synchronize()
     res = ref.check(to_host(c), want, **tol)
+    print(f"{label}: max_err={res['max_err']:.3e} tol={res['tol']:.3e} "
+          f"rel_frob={res['rel_frob']:.3e} nonfinite={res['nonfinite']}", flush=True)
+    assert res["ok"], (label, res)
+
+
+def grouped_cases(count=48, seed=20261204):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        kind = ["fp16", "bf16", "fp8"][int(rng.integers(3))]
+        tokens = int(rng.choice([1, 3, 40, 129, 300, 700]))
+        experts = int(rng.choice([1, 2, 3, 8, 17]))
+        k = int(rng.choice([128, 256, 512, 1024]))
+        n = int(rng.choice([256, 512, 768]))
+        gs = 128 if kind == "fp8" else int(rng.choice([g for g in (16, 32, 64, 128) if k % g == 0]))
+        zp = kind != "fp8" and bool(rng.integers(2))
+        weighted = bool(rng.integers(2))
+        cases.append((kind, tokens, experts, k, n, gs, zp, weighted))
+    return cases
+
+
+@pytest.mark.parametrize("kind,tokens,experts,k,n,gs,zp,weighted", grouped_cases())
+def test_grouped_sweep_matches_oracle(dev, kind, tokens, experts, k, n, gs, zp, weighted):
+    label = (f"grouped sweep {kind} tokens={tokens} experts={experts} k={k} n={n} "
+             f"group_size={gs} zp={zp} weighted={weighted}")
+    print(label, flush=True)
+    seed = 9000 + tokens * 13 + experts * 101 + k + n + gs
+    bf16 = kind == "bf16"
+    fp8 = kind == "fp8"
+    moe = synthetic.moe_case(tokens, experts, k, n, group_size=gs, seed=seed, bf16=bf16)
+    ex = []
+    for i, e in enumerate(moe["experts"]):
+        d = dict(e, group_size=gs)
+        if fp8:
+            d["qweight"] = synthetic.fp8_words(seed + 50 + i, k, n)
+        if zp:
+            d["zeros"] = synthetic.zero_point_words(seed + 100 + i, k // gs, n)
+        ex.append(d)
+    bank = torch_ops.ExpertBank(ex, device=dev, bf16=bf16, fp8=fp8)
+    csr = wq.wq_csr_from_routes(moe["routes"], moe["n_tokens"], moe["top_k"], moe["n_expert"])
+    wts = synthetic.routing_weights(seed + 200, tokens, 2) if weighted else None
+    y = torch_ops.grouped_gemm(torch_ops.to_device(moe["a"], dev), bank, csr,
+                               topk_weights=None if wts is None else torch_ops.to_device(wts, dev))
+    torch.cuda.synchronize()
+    ocsr = ref.csr_from_token_routes(moe["n_expert"], moe["n_tokens"], moe["top_k"],
+                                     moe["routes"])
+    want = ref.grouped_w4a16_gemm(moe["a"], ex, ocsr, group_size=gs, topk_weights=wts,
+                                  bf16=bf16, fp8=fp8)
+    # fp16 outputs with routing weights, and E4M3 weights, add the fp16 output's own
+    # rounding per element (see the dense tolerances above)
+    tol = BF16_TOL if bf16 else (FP8_TOL if fp8 or weighted else FP16_TOL)
+    res = ref.check(to_host(y), want, **tol)
     print(f"{label}: max_err={res['max_err']:.3e} tol={res['tol']:.3e} "
           f"rel_frob={res['rel_frob']:.3e} nonfinite={res['nonfinite']}", flush=True)
     assert res["ok"], (label, res)

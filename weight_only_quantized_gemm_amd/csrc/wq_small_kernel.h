@@ -294,6 +294,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     for (int i = 1; i < GW; ++i) load_b(i);
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<(GW - 1) * NV * NBV>();
+    __builtin_amdgcn_sched_barrier(0);  // no LDS read of the region moves above the wait
   } else {
 #pragma unroll
     for (int i = 0; i < GW; ++i) load_b(i);

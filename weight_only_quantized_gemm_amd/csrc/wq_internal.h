@@ -52,8 +52,8 @@ struct SmallPlan {
   bool pair;       // SwiGLU epilogue: a gate/up pair of blocks per work-group, half the
                    // waves on each (n counts both; c is [m][n/2]; splits must be 1)
   int gpc;         // scale units per 128-row chunk: 1, 2, 4 or 8 (units of 128/gpc rows)
-  bool direct;     // activation operands loaded straight into registers, no LDS slice
-                   // (depth <= 4, not with pair)
+  bool direct;     // each wave fetches its own groups' activation tiles, scales and zero
+                   // points into its own LDS region (no shared slice; not with pair)
   bool dual;       // direct only: each wave covers two adjacent column blocks, reading the
                    // activations once for both (4-bit weights)
 };

@@ -400,7 +400,6 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
       }
     }
   }
-  auto& sc = scs[0];  // the scales of the wave's only (or first) block
   // unit t of step i: its zero point for this lane's column
   const auto zero_of = [&](int i, int t) {
     return ZP ? zero_code(zero_word(half, i, t), col) : 8;

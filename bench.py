@@ -274,6 +274,32 @@ def bench_extended(torch, torch_ops, steps, warmup):
         "us": round(sec * 1e6, 2),
         "tflops": round(2.0 * csr["n_pairs"] * one["n"] * one["k"] / sec / 1e12, 2),
         "weight_tbs": round(csr["n_active"] * one["k"] * one["n"] / 2 / sec / 1e12, 4)}
+    del bank
+    # MoE decode: a few tokens, top-2 of 8 experts, the same K and N (segments of at most four
+    # rows run on the small-M kernel).  Three banks of eight experts rotate with sixteen
+    # routings, so that the experts read by one step are not those of the step before.
+    one = synthetic.moe_case(4, 1, seed=45)
+    banks = [torch_ops.ExpertBank(one["experts"] * 8, device="cuda") for _ in range(3)]
+    for tokens in (1, 4):
+        csrs, dcsrs = [], []
+        for r in range(16):
+            routes = synthetic.top2_routes(47 + 16 * tokens + r, tokens, 8)
+            csr = wq.wq_csr_from_routes(routes, tokens, 2, 8)
+            csrs.append(csr)
+            dcsrs.append({key: torch_ops.to_device(np.asarray(csr[key], np.int32), "cuda")
+                          for key in ("ex_ids", "ex_off", "ex_pairs", "pair_tok")})
+        a = torch_ops.to_device(synthetic.activations(49, tokens, one["k"]), "cuda")
+        y = torch.empty((2 * tokens, one["n"]), dtype=torch.float16, device="cuda")
+
+        def decode_step(i, a=a, y=y, csrs=csrs, dcsrs=dcsrs):
+            torch_ops.grouped_gemm(a, banks[i % 3], csrs[i % 16], y, device_csr=dcsrs[i % 16])
+        sec = timed_loop(torch, decode_step, 48, warmup)
+        active = float(np.mean([c["n_active"] for c in csrs]))
+        out[f"moe_decode_{tokens}_tokens"] = {
+            "workload": f"{tokens} token(s) top-2 of 8 experts K=4096 N=14336 u4b8 group 128 "
+                        f"({active:.2f} active experts on average), 3 rotating banks",
+            "us": round(sec * 1e6, 2),
+            "weight_tbs": round(active * one["k"] * one["n"] / 2 / sec / 1e12, 4)}
     return out
 
 

@@ -329,7 +329,10 @@ int wq_grouped_workspace_bytes(int n_pairs, int n_active, int n, int k, uint32_t
  * `mul_topk_weights` with its fp32 `topk_weights`, one per routed pair).  The device CSR is
  * not re-validated (that would need a host sync): build it with wq_csr_from_routes;
  * entries out of range are skipped by the kernel (never read or written out of bounds),
- * leaving those output rows unwritten.
+ * leaving those output rows unwritten.  Segments must be non-empty: when n_pairs -
+ * n_active + 1 <= 4 (every segment then holds at most four rows; decode-sized batches)
+ * 4-bit products without the SwiGLU epilogue run on the small-M kernel, one work-group per
+ * 16-column block and segment, which computes at most that many rows of a segment.
  */
 int wq_grouped_gemm(const wq_grouped_args* args);
 

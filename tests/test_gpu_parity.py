@@ -286,6 +286,36 @@ def test_direct_activation_rows_match_oracle(dev, m, k, n, gs, zp, act_order, fp
     assert_parity(c, oracle_gemm(case), label)
 
 
+# 2..4 rows on the small-M kernel's staged general path: slices of one to eight slots per
+# thread (four or eight waves), every scale unit size and channelwise scales, zero points,
+# act_order and requested splits.
+FEW_ROW_SHAPES = [
+    # m, k, n, group_size, zp, act_order, fp32_reduce, split_k
+    (2, 128, 256, 128, False, False, False, 0),
+    (3, 1024, 512, 128, True, False, True, 0),
+    (4, 4096, 512, 128, False, False, False, 0),
+    (4, 4096, 768, 128, True, False, True, 3),
+    (2, 8192, 256, 128, False, True, False, 0),
+    (3, 2048, 768, 64, True, False, False, 0),
+    (4, 2048, 512, 32, False, False, True, 0),
+    (2, 1024, 512, 16, True, False, False, 0),
+    (4, 1024, 256, -1, True, False, False, 0),
+    (3, 1536, 256, 48, False, True, False, 0),
+    (4, 6144, 256, 16, True, False, True, 2),
+]
+
+
+@pytest.mark.parametrize("m,k,n,gs,zp,act_order,fp32,split", FEW_ROW_SHAPES)
+def test_few_rows_match_oracle(dev, m, k, n, gs, zp, act_order, fp32, split):
+    label = (f"few rows m={m} k={k} n={n} group_size={gs} zp={zp} act_order={act_order} "
+             f"fp32={fp32} split={split}")
+    say(label)
+    case = synthetic.dense_case(m, k, n, zp=zp, act_order=act_order, group_size=gs,
+                                seed=3800 + m + k + gs)
+    c = gpu_gemm(case, dev, fp32_reduce=fp32, split_k=split)
+    assert_parity(c, oracle_gemm(case), label)
+
+
 @pytest.mark.parametrize("gs,k", [(-1, 1024), (32, 1024), (64, 1024), (256, 1024), (1024, 1024),
                                   (16, 1024), (48, 768), (80, 1280), (96, 1152)])
 def test_group_size_repack_and_dequant_bitwise(dev, gs, k):
@@ -355,7 +385,7 @@ def test_all_eight_codes_give_zero(dev):
     """Codes equal to the zero point give zero: exactly on the tiled kernel and the
     small-M kernel's general path (the weights enter the products as exact zeros); within
     the accumulation bound on the one-row path, where q * a and z * a are summed apart."""
-    for m in (1, 16, 300):
+    for m in (1, 3, 16, 300):
         case = synthetic.dense_case(m, 512, 256, seed=3)
         case["qweight"][:] = 0x88888888
         c = gpu_gemm(case, dev, fp32_reduce=True).astype(np.float64)
@@ -366,35 +396,36 @@ def test_all_eight_codes_give_zero(dev):
 
 
 ONE_ROW_SHAPES = [
-    # k, n, group_size, zp, all-positive activations, split_k
-    (4096, 512, 128, False, True, 0),
-    (4096, 512, 128, True, True, 0),
-    (4096, 512, 16, True, True, 0),
-    (2048, 512, 32, False, True, 0),
-    (1024, 512, 64, True, False, 0),
-    (1024, 768, -1, True, True, 0),
-    (4096, 256, 128, True, True, 3),
+    # m, k, n, group_size, zp, all-positive activations, split_k
+    (1, 4096, 512, 128, False, True, 0),
+    (1, 4096, 512, 128, True, True, 0),
+    (1, 4096, 512, 16, True, True, 0),
+    (1, 2048, 512, 32, False, True, 0),
+    (1, 1024, 512, 64, True, False, 0),
+    (1, 1024, 768, -1, True, True, 0),
+    (1, 4096, 256, 128, True, True, 3),
 ]
 
 
-@pytest.mark.parametrize("k,n,gs,zp,positive,split", ONE_ROW_SHAPES)
-def test_one_row_within_rounding_of_the_exact_product(dev, k, n, gs, zp, positive, split):
-    label = f"one row k={k} n={n} group_size={gs} zp={zp} positive={positive} split={split}"
+@pytest.mark.parametrize("m,k,n,gs,zp,positive,split", ONE_ROW_SHAPES)
+def test_one_row_within_rounding_of_the_exact_product(dev, m, k, n, gs, zp, positive, split):
+    label = (f"one row m={m} k={k} n={n} group_size={gs} zp={zp} positive={positive} "
+             f"split={split}")
     say(label)
-    case = synthetic.dense_case(1, k, n, zp=zp, group_size=gs, seed=3900 + k + n + gs)
+    case = synthetic.dense_case(m, k, n, zp=zp, group_size=gs, seed=3900 + k + n + gs + m)
     if positive:  # every activation of one sign: the largest partial sums for the result
         case["a"] = np.abs(case["a"])
     c = gpu_gemm(case, dev, fp32_reduce=True, split_k=split)
     want = oracle_gemm(case)
     assert_parity(c, want, label)
-    err = np.abs(c[0].astype(np.float64) - want[0])
-    allowed = (2.0 ** -11 * np.abs(want[0]) + accumulation_bound(case)[0] * (1 + 2.0 ** -11)
+    err = np.abs(c.astype(np.float64) - want)
+    allowed = (2.0 ** -11 * np.abs(want) + accumulation_bound(case) * (1 + 2.0 ** -11)
                + 2.0 ** -25)
     assert np.all(err <= allowed), (label, float(np.max(err - allowed)))
 
 
 def test_unit_scales_integer_products_are_bit_exact(dev):
-    for m in (1, 16, 40):
+    for m in (1, 3, 16, 40):
         k, n = 1024, 256
         case = synthetic.dense_case(m, k, n, seed=4)
         case["a"] = (synthetic.below(5, m * k, 3) - 1).reshape(m, k).astype(np.float16)
@@ -405,9 +436,9 @@ def test_unit_scales_integer_products_are_bit_exact(dev):
         assert np.array_equal(c.astype(np.float64), want), m
 
 
-def test_one_hot_rows_give_dequantized_rows_bitwise(dev):
+@pytest.mark.parametrize("rows", [[0, 1, 127, 128, 500, 1023], [0, 500, 1023], [129]])
+def test_one_hot_rows_give_dequantized_rows_bitwise(dev, rows):
     k, n = 1024, 512
-    rows = [0, 1, 127, 128, 500, 1023]
     for zp in (False, True):
         case = synthetic.dense_case(len(rows), k, n, zp=zp, seed=6)
         a = np.zeros((len(rows), k), dtype=np.float16)
@@ -546,6 +577,82 @@ def test_grouped_single_expert_equals_dense(dev):
     dense = gpu_gemm(dict(a=moe["a"], qweight=moe["experts"][0]["qweight"],
                           scales=moe["experts"][0]["scales"]), dev)
     assert np.array_equal(y.view(np.uint16), dense.view(np.uint16))
+
+
+# Segments of at most four rows (n_pairs - n_active + 1 <= 4) run on the small-M kernel, one
+# work-group per 16-column block and segment: one-row segments on its one-row path, up to
+# four rows on its general path; four waves of 1..8 groups or eight waves of 8 (K = 8192).
+FEW_ROW_GROUPED = [
+    # tokens, experts, k, n, group_size, zp, weighted, bf16
+    (1, 8, 4096, 512, 128, False, False, False),
+    (1, 8, 1024, 768, 128, True, True, False),
+    (1, 1, 2048, 256, 128, False, False, False),      # both slots on one expert: two rows
+    (2, 8, 2048, 512, 64, True, False, False),
+    (3, 8, 8192, 256, 128, False, True, False),
+    (2, 3, 1024, 512, 32, False, True, False),
+    (1, 4, 4096, 256, 16, True, False, False),
+    (3, 6, 768, 256, 256, False, False, False),
+    (1, 8, 2048, 512, 128, False, True, True),
+    (2, 8, 1024, 256, 64, True, False, True),
+    (3, 5, 512, 512, 16, False, True, True),
+    (4, 8, 1024, 256, 128, True, True, False),
+    (5, 8, 1024, 512, 128, False, False, True),
+]
+
+
+@pytest.mark.parametrize("tokens,experts,k,n,gs,zp,weighted,bf16", FEW_ROW_GROUPED)
+def test_grouped_few_rows_match_oracle(dev, tokens, experts, k, n, gs, zp, weighted, bf16):
+    label = (f"grouped few rows tokens={tokens} experts={experts} k={k} n={n} group_size={gs} "
+             f"zp={zp} weighted={weighted} bf16={bf16}")
+    say(label)
+    seed = 5100 + tokens * 7 + experts + k + gs
+    moe = synthetic.moe_case(tokens, experts, k, n, group_size=gs, seed=seed, bf16=bf16)
+    groups = k // gs
+    ex = []
+    for i, e in enumerate(moe["experts"]):
+        d = dict(e, group_size=gs)
+        if zp:
+            d["zeros"] = synthetic.zero_point_words(seed + 100 + i, groups, n)
+        ex.append(d)
+    bank = torch_ops.ExpertBank(ex, device=dev, bf16=bf16)
+    csr = wq.wq_csr_from_routes(moe["routes"], tokens, 2, experts)
+    assert csr["n_pairs"] - csr["n_active"] + 1 <= 4, "not a few-row product"
+    wts = synthetic.routing_weights(seed + 200, tokens, 2) if weighted else None
+    y = torch_ops.grouped_gemm(torch_ops.to_device(moe["a"], dev), bank, csr,
+                               topk_weights=None if wts is None else torch_ops.to_device(wts, dev))
+    torch.cuda.synchronize()
+    ocsr = ref.csr_from_token_routes(experts, tokens, 2, moe["routes"])
+    want = ref.grouped_w4a16_gemm(moe["a"], ex, ocsr, group_size=gs, topk_weights=wts,
+                                  bf16=bf16)
+    got = y.float().cpu().numpy() if bf16 else host(y)
+    # bf16 outputs, and fp16 outputs scaled by routing weights, add their own rounding per
+    # element (as the dense bf16 and the weighted MoE checks do)
+    res = ref.check(got, want, rel_elem=(2.0 ** -8 if bf16 else 2.0 ** -11 if weighted else 0.0),
+                    rel_frob=4e-3 if bf16 else 1e-3)
+    say(f"{label}: max_err={res['max_err']:.3e} tol={res['tol']:.3e} "
+        f"rel_frob={res['rel_frob']:.3e} nonfinite={res['nonfinite']}")
+    assert res["ok"], (label, res)
+
+
+@pytest.mark.parametrize("tokens,experts", [(1, 8), (1, 1), (2, 8)])
+def test_grouped_few_rows_equal_dense_rows_bitwise(dev, tokens, experts):
+    """A segment's rows give the same bits as the dense small-M product of its expert on
+    those activation rows (the same plan: four waves, no split)."""
+    k, n = 2048, 512
+    moe = synthetic.moe_case(tokens, experts, k, n, seed=5200 + tokens + experts)
+    bank = torch_ops.ExpertBank(moe["experts"], device=dev)
+    csr = wq.wq_csr_from_routes(moe["routes"], tokens, 2, experts)
+    y = host(torch_ops.grouped_gemm(torch_ops.to_device(moe["a"], dev), bank, csr))
+    bound = csr["n_pairs"] - csr["n_active"] + 1
+    for i, e in enumerate(csr["ex_ids"]):
+        pairs = [int(p) for p in csr["ex_pairs"][csr["ex_off"][i]:csr["ex_off"][i + 1]]]
+        rows = [int(csr["pair_tok"][p]) for p in pairs]
+        # the instance is chosen by the bound: a shorter segment repeats its last row
+        rows_b = rows + [rows[-1]] * (bound - len(rows))
+        dense = gpu_gemm(dict(a=moe["a"][rows_b], qweight=moe["experts"][e]["qweight"],
+                              scales=moe["experts"][e]["scales"]), dev)
+        assert np.array_equal(y[pairs].view(np.uint16), dense[:len(rows)].view(np.uint16)), \
+            (tokens, experts, e)
 
 
 @pytest.mark.parametrize("weighted", [False, True])

@@ -557,7 +557,16 @@ int wq_grouped_gemm(const wq_grouped_args* args) {
   g.bf16 = (p.flags & WQ_FLAG_BF16) != 0;
   g.fp8 = fp8;
   g.gpc = subgroups(p.k, p.group_size);
-  const hipError_t e = wq::launch_grouped_tile(g, as_stream(p.stream));
+  // Few rows in every segment (decode-sized batches): the small-M kernel, one work-group per
+  // 16-column block and segment, streams each active expert's weights on far more
+  // work-groups than its row tiles would give.  Non-empty segments hold at most
+  // n_pairs - n_active + 1 rows each.
+  const long long seg_rows = (long long)p.n_pairs - p.n_active + 1;
+  wq::SmallPlan sp{};
+  const hipError_t e =
+      seg_rows <= wq::kSegRows && wq::grouped_small_plan(g, (int)seg_rows, &sp)
+          ? wq::launch_grouped_small(g, (int)seg_rows, sp, as_stream(p.stream))
+          : wq::launch_grouped_tile(g, as_stream(p.stream));
   return e == hipSuccess ? 0 : hip_fail(e);
 }
 

@@ -88,6 +88,50 @@ bool small_plan_fits(int m, int k, const SmallPlan& plan) {
          dynamic + small_static_lds(plan.waves, plan.pair, plan.gpc, m == 1, false) <= kLdsBytes;
 }
 
+bool grouped_small_plan(const GroupedProblem& p, int rows, SmallPlan* plan) {
+  if (p.fp8 || p.swiglu || rows < 1 || rows > kSegRows) return false;
+  if (p.n_active > 65535) return false;                     // segments along grid y
+  if ((long long)p.n_tokens * p.k > 0x7fffffffLL) return false;  // 32-bit row offsets
+  const int groups = p.k / kGroup;
+  for (int waves = 4; waves <= 8; waves *= 2) {
+    const int per_wave = (groups + waves - 1) / waves;
+    if (per_wave > 8) continue;
+    SmallPlan q{};
+    q.waves = waves;
+    q.splits = 1;
+    q.depth = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 8;
+    q.gpc = p.gpc;
+    if (waves == 8 && q.depth != 8) continue;  // the instances of eight waves
+    if (small_plan_fits(rows, p.k, q)) {
+      *plan = q;
+      return true;
+    }
+  }
+  return false;
+}
+
+hipError_t launch_grouped_small(const GroupedProblem& p, int rows, const SmallPlan& plan,
+                                hipStream_t stream) {
+  SmallPlan check{};
+  if (!grouped_small_plan(p, rows, &check) || check.waves != plan.waves ||
+      check.depth != plan.depth)
+    return hipErrorInvalidConfiguration;
+  if (p.bf16) {
+    switch (p.gpc) {
+      case 2: return launch_seg_bf16_g2(p, rows, plan, stream);
+      case 4: return launch_seg_bf16_g4(p, rows, plan, stream);
+      case 8: return launch_seg_bf16_g8(p, rows, plan, stream);
+      default: return launch_seg_bf16_g1(p, rows, plan, stream);
+    }
+  }
+  switch (p.gpc) {
+    case 2: return launch_seg_g2(p, rows, plan, stream);
+    case 4: return launch_seg_g4(p, rows, plan, stream);
+    case 8: return launch_seg_g8(p, rows, plan, stream);
+    default: return launch_seg_g1(p, rows, plan, stream);
+  }
+}
+
 hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* b,
                              const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                              const SmallPlan& plan, float* partials, bool bf16, bool fp8,

@@ -1,0 +1,12 @@
+// Grouped small-M instances (segments of few rows) for fp16 activations
+// (128-row scale units, 1 per 128-row chunk).
+#include "wq_small_kernel.h"
+
+namespace wq {
+
+hipError_t launch_seg_g1(const GroupedProblem& p, int rows, const SmallPlan& plan,
+                         hipStream_t stream) {
+  return launch_seg_gpc<1, false>(p, rows, plan, stream);
+}
+
+}  // namespace wq

@@ -133,6 +133,27 @@ struct GroupedProblem {
   bool fp8;               // the banks hold E4M3 weights in the FP8 layout
 };
 hipError_t launch_grouped_tile(const GroupedProblem& p, hipStream_t stream);
+// Grouped products whose segments all hold few rows run on the small-M kernel instead (4-bit
+// weights, no SwiGLU epilogue): one work-group per 16-column block and segment, its
+// activation rows gathered through pair_tok and its outputs scattered to the pair rows.
+// `rows` bounds every segment's row count (n_pairs - n_active + 1 for a CSR of non-empty
+// segments) and is 1 or at most kSegRows; `plan` is a single-split staged plan for m = rows
+// (four waves, or eight with GW 8).
+constexpr int kSegRows = 4;
+bool grouped_small_plan(const GroupedProblem& p, int rows, SmallPlan* plan);
+hipError_t launch_grouped_small(const GroupedProblem& p, int rows, const SmallPlan& plan,
+                                hipStream_t stream);
+#define WQ_SEG_GPC_DECL(NAME)                                                               \
+  hipError_t NAME(const GroupedProblem& p, int rows, const SmallPlan& plan, hipStream_t stream);
+WQ_SEG_GPC_DECL(launch_seg_g1)
+WQ_SEG_GPC_DECL(launch_seg_g2)
+WQ_SEG_GPC_DECL(launch_seg_g4)
+WQ_SEG_GPC_DECL(launch_seg_g8)
+WQ_SEG_GPC_DECL(launch_seg_bf16_g1)
+WQ_SEG_GPC_DECL(launch_seg_bf16_g2)
+WQ_SEG_GPC_DECL(launch_seg_bf16_g4)
+WQ_SEG_GPC_DECL(launch_seg_bf16_g8)
+#undef WQ_SEG_GPC_DECL
 
 // Register-only MFMA measurement helper (wq_measure.hip): kMfmaBlocks work-groups of
 // kMfmaThreads threads, each thread running `iters` steps of eight 32x32x16 fp16 MFMAs on

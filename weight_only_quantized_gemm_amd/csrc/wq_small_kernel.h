@@ -110,12 +110,27 @@ constexpr long small_direct_lds(int waves, int gw, int gpc, bool zp, bool dual) 
 // (2t, 2t+1, as wq_interleave_gate_up pairs them); its first half of waves streams the gate
 // block, the second half the up block, both over the same K range and staged activations,
 // and the reduction writes fp16(silu(g) * u) to column 16t + c of the [m][n/2] activation.
+// SEG (grouped products with few rows per expert): blockIdx.y is a segment of the
+// expert-major CSR (ex_ids, ex_off, ex_pairs, pair_tok), whose rows, at most kSegRows of
+// them (one on the one-row path), all use one expert's weights, scales and zero points (b,
+// s and z plus the expert times b_stride, s_stride and z_stride elements).  Segment row j
+// reads activation row pair_tok[p] (p = ex_pairs[ex_off[seg] + j]) and writes output row p,
+// times topk_w[p] when given.  As on the tiled path, CSR entries out of range are never
+// followed: a segment with an expert outside [0, n_expert) is skipped, its range is
+// clamped into [0, n_pairs], and a row whose pair or token is out of range reads a clamped
+// activation row and is not written.  The expert's weights for the first groups are
+// requested before the row indices, so that the weight stream starts while the index loads
+// resolve.
 template <bool ZP, int WAVES, int GW, int STAGE, bool PAIR, int GPC, bool BF16, bool W8,
-          bool R1, bool DUAL>
+          bool R1, bool DUAL, bool SEG = false>
 __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     const f16* __restrict__ a, int lda, int m, const u32x4* __restrict__ b,
     const uint16_t* __restrict__ s, const u32x2* __restrict__ z, uint16_t* __restrict__ c,
-    int n, int groups, int splits, float* __restrict__ partials) {
+    int n, int groups, int splits, float* __restrict__ partials,
+    const int32_t* __restrict__ ex_ids, const int32_t* __restrict__ ex_off,
+    const int32_t* __restrict__ ex_pairs, const int32_t* __restrict__ pair_tok,
+    const float* __restrict__ topk_w, long b_stride, long s_stride, long z_stride,
+    int n_expert, int n_pairs, int n_tokens) {
   using A = Act<BF16>;
   static_assert(!W8 || (!ZP && GPC == 1), "E4M3: 128-row scale units, no zero points");
   constexpr int NV = W8 ? 2 : 1;  // 16-byte weight vectors per lane and group
@@ -134,6 +149,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   // DUAL: each wave applies its activation operands to two adjacent column blocks, so the
   // activations are read once per two blocks (direct activations, 4-bit weights).
   static_assert(!DUAL || (DA && !PAIR && !W8 && !R1), "dual blocks: direct activations");
+  static_assert(!SEG || (!DA && !PAIR && !W8 && !DUAL), "segments: staged, 4-bit, one block");
+  constexpr int SR = R1 ? 1 : kSegRows;  // rows of a segment (SEG)
   constexpr int T = WAVES * 64;
   constexpr int NB = (PAIR || DUAL) ? 2 : 1;  // column blocks of the work-group
   constexpr int NBV = DUAL ? 2 : 1;           // column blocks of each wave
@@ -162,7 +179,61 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   const int half = PAIR ? wave / KW : 0;       // the wave's block of the pair
   const int kwave = wave - half * KW;          // the wave's index along K
   const int nb = NB * blockIdx.x + half;
-  const int split = blockIdx.y;
+  const int split = SEG ? 0 : blockIdx.y;
+
+  // SEG: the segment's expert and rows (wave-uniform, scalar loads).
+  int seg_p0 = 0;
+  if constexpr (SEG) {
+    const int sgi = blockIdx.y;
+    const int ex = ex_ids != nullptr ? ex_ids[sgi] : sgi;
+    if (ex < 0 || ex >= n_expert) return;
+    int a0 = ex_off[sgi], a1 = ex_off[sgi + 1];
+    a0 = a0 < 0 ? 0 : (a0 > n_pairs ? n_pairs : a0);
+    a1 = a1 < a0 ? a0 : (a1 > n_pairs ? n_pairs : a1);
+    seg_p0 = a0;
+    const int rows = a1 - a0;  // at most SR by the launch's bound for a valid CSR
+    if (rows <= 0) return;
+    m = rows < SR ? rows : SR;
+    b += (long)ex * b_stride;
+    s += (long)ex * s_stride;
+    if constexpr (ZP) z += (long)ex * z_stride;
+  }
+  // SEG: output row (pair, or -1: not written) and activation row offset of segment row j
+  // (rows past the last repeat it); filled once the first weight loads are in flight.
+  i32x4 seg_pair = {0, 0, 0, 0};
+  i32x4 seg_aoff = {0, 0, 0, 0};
+  f32x4 seg_w = {1.f, 1.f, 1.f, 1.f};  // routing weights of the rows (with topk_w)
+  static_assert(SR <= 4, "segment rows held in one register vector");
+  const auto seg_rows = [&] {
+#pragma unroll
+    for (int j = 0; j < SR; ++j) seg_pair[j] = ex_pairs[seg_p0 + (j < m ? j : m - 1)];
+    __builtin_amdgcn_sched_barrier(0);  // all row loads in flight before the first use
+    i32x4 tok;
+#pragma unroll
+    for (int j = 0; j < SR; ++j) tok[j] = pair_tok[max(0, min(seg_pair[j], n_pairs - 1))];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < SR; ++j) {
+      // a row with a pair or token out of range reads a clamped row and is not written
+      const int pr = seg_pair[j];
+      seg_aoff[j] = max(0, min(tok[j], n_tokens - 1)) * lda;
+      const bool ok = ((unsigned)pr < (unsigned)n_pairs) & ((unsigned)tok[j] < (unsigned)n_tokens);
+      seg_pair[j] = ok ? pr : -1;
+    }
+  };
+  const auto seg_weights = [&] {
+    if (topk_w != nullptr) {
+#pragma unroll
+      for (int j = 0; j < SR; ++j) seg_w[j] = topk_w[max(0, seg_pair[j])];
+    }
+  };
+  // segment row rr (per lane) -> its entry of v
+  const auto seg_select = [&](i32x4 v, int rr) {
+    int x = v[0];
+#pragma unroll
+    for (int j = 1; j < SR; ++j) x = rr == j ? v[j] : x;
+    return x;
+  };
 
   // The work-group's range of K groups (groups * splits stays far below 2^31); a single
   // split, the common case, needs no division.
@@ -190,7 +261,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   f16x8 stage[DA ? 1 : STAGE];
   int stage_q[R1B ? STAGE : 1];        // granule column of each slot
   bool stage_real[R1B ? STAGE : 1];    // the slot lies inside the slice
-  if constexpr (!DA) {
+  const auto load_stage = [&] {
 #pragma unroll
     for (int u = 0; u < STAGE; ++u) {
       const int rr = r < m ? r : m - 1;
@@ -198,14 +269,16 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
         stage_q[u] = q;
         stage_real[u] = r < m;
       }
-      stage[u] = *reinterpret_cast<const f16x8*>(a_base + (long)rr * lda + 8 * q);
+      const long row_off = SEG ? (long)seg_select(seg_aoff, rr) : (long)rr * lda;
+      stage[u] = *reinterpret_cast<const f16x8*>(a_base + row_off + 8 * q);
       q += dq;
       r += dr;
       const bool wrap = q >= per_row;
       q = wrap ? q - per_row : q;
       r = wrap ? r + 1 : r;
     }
-  }
+  };
+  if constexpr (!DA && !SEG) load_stage();
   // 2. Scales (8 dwords of fp16 pairs per unit row) and zero points of the range, for each
   //    of the work-group's blocks ([block][unit] in LDS).  A block holds groups*GPC units.
   const long units = (long)groups * GPC;
@@ -295,6 +368,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<(GW - 1) * NV * NBV>();
     __builtin_amdgcn_sched_barrier(0);  // no LDS read of the region moves above the wait
+  } else if constexpr (SEG) {
+    // the first groups' weights, then the row indices and the activation slice, then the
+    // rest of the weights: the slice's LDS writes wait for the first groups' weights only
+    constexpr int EARLY = GW >= 4 ? 2 : 1;
+#pragma unroll
+    for (int i = 0; i < EARLY; ++i) load_b(i);
+    __builtin_amdgcn_sched_barrier(0);
+    seg_rows();
+    load_stage();
+    __builtin_amdgcn_sched_barrier(0);
+    seg_weights();
+#pragma unroll
+    for (int i = EARLY; i < GW; ++i) load_b(i);
   } else {
 #pragma unroll
     for (int i = 0; i < GW; ++i) load_b(i);
@@ -701,10 +787,18 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     for (int e = 0; e < 4; ++e) {
       const int row = 4 * qd + e;
       if (row >= m) continue;
-      if (splits == 1)
+      if constexpr (SEG) {
+        // the pair's output row, times its routing weight in fp32 before the rounding
+        const int pr = seg_select(seg_pair, row);
+        float wr = seg_w[0];
+#pragma unroll
+        for (int j = 1; j < SR; ++j) wr = row == j ? seg_w[j] : wr;
+        if (pr >= 0) c[(long)pr * n + colx] = A::round(topk_w != nullptr ? tot[e] * wr : tot[e]);
+      } else if (splits == 1) {
         c[(long)row * n + colx] = A::round(tot[e]);
-      else
+      } else {
         partials[((long)split * m + row) * n + colx] = tot[e];
+      }
     }
   }
 }
@@ -739,10 +833,72 @@ hipError_t launch_small_t(const uint16_t* a, int lda, int m, const uint32_t* b,
   hipLaunchKernelGGL((gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16, W8, R1, DUAL>), grid,
                      dim3(WAVES * 64), lds, stream, reinterpret_cast<const f16*>(a), lda, m,
                      reinterpret_cast<const u32x4*>(b), s, reinterpret_cast<const u32x2*>(z), c,
-                     n, groups, splits, partials);
+                     n, groups, splits, partials, nullptr, nullptr, nullptr, nullptr, nullptr,
+                     0L, 0L, 0L, 0, 0, 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   return launch_reduce_splits(partials, c, m, n, splits, BF16, stream);
+}
+
+// Grouped products with few rows per segment: grid (n / 16, n_active), one split.
+template <bool ZP, int WAVES, int GW, int STAGE, int GPC, bool BF16, bool R1>
+hipError_t launch_seg_t(const GroupedProblem& p, int rows, hipStream_t stream) {
+  constexpr size_t lds = (size_t)STAGE * WAVES * 64 * sizeof(f16x8);
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(
+          &gemm_small_kernel<ZP, WAVES, GW, STAGE, false, GPC, BF16, false, R1, false, true>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
+  const dim3 grid(p.n / 16, p.n_active);
+  hipLaunchKernelGGL(
+      (gemm_small_kernel<ZP, WAVES, GW, STAGE, false, GPC, BF16, false, R1, false, true>), grid,
+      dim3(WAVES * 64), lds, stream, reinterpret_cast<const f16*>(p.a), p.k, rows,
+      reinterpret_cast<const u32x4*>(p.b_bank), reinterpret_cast<const uint16_t*>(p.s_bank),
+      reinterpret_cast<const u32x2*>(p.z_bank), p.y, p.n, p.k / kGroup, 1, nullptr, p.ex_ids,
+      p.ex_off, p.ex_pairs, p.pair_tok, p.topk_w, (long)(p.b_stride / 16),
+      (long)(p.s_stride / 2), (long)(p.z_stride / 8), p.n_expert, p.n_pairs, p.n_tokens);
+  return hipGetLastError();
+}
+
+template <bool ZP, int WAVES, int GW, int GPC, bool BF16>
+hipError_t launch_seg_stage(const GroupedProblem& p, int rows, hipStream_t stream) {
+  const int slots = round_slots(stage_slots(rows, p.k / kGroup, WAVES));
+  if (rows == 1) {
+    switch (slots) {
+      case 1: return launch_seg_t<ZP, WAVES, GW, 1, GPC, BF16, true>(p, rows, stream);
+      case 2: return launch_seg_t<ZP, WAVES, GW, 2, GPC, BF16, true>(p, rows, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (slots) {
+    case 1: return launch_seg_t<ZP, WAVES, GW, 1, GPC, BF16, false>(p, rows, stream);
+    case 2: return launch_seg_t<ZP, WAVES, GW, 2, GPC, BF16, false>(p, rows, stream);
+    case 4: return launch_seg_t<ZP, WAVES, GW, 4, GPC, BF16, false>(p, rows, stream);
+    case 8: return launch_seg_t<ZP, WAVES, GW, 8, GPC, BF16, false>(p, rows, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Four waves of 1, 2, 4 or 8 groups (K up to 32 groups), or eight waves of 8 (up to 64).
+template <bool ZP, int GPC, bool BF16>
+hipError_t launch_seg_zp(const GroupedProblem& p, int rows, const SmallPlan& plan,
+                         hipStream_t stream) {
+  if (plan.waves == 8)
+    return plan.depth == 8 ? launch_seg_stage<ZP, 8, 8, GPC, BF16>(p, rows, stream)
+                           : hipErrorInvalidValue;
+  switch (plan.depth) {
+    case 1: return launch_seg_stage<ZP, 4, 1, GPC, BF16>(p, rows, stream);
+    case 2: return launch_seg_stage<ZP, 4, 2, GPC, BF16>(p, rows, stream);
+    case 4: return launch_seg_stage<ZP, 4, 4, GPC, BF16>(p, rows, stream);
+    default: return launch_seg_stage<ZP, 4, 8, GPC, BF16>(p, rows, stream);
+  }
+}
+
+template <int GPC, bool BF16>
+hipError_t launch_seg_gpc(const GroupedProblem& p, int rows, const SmallPlan& plan,
+                          hipStream_t stream) {
+  if (p.z_bank != nullptr) return launch_seg_zp<true, GPC, BF16>(p, rows, plan, stream);
+  return launch_seg_zp<false, GPC, BF16>(p, rows, plan, stream);
 }
 
 template <bool ZP, int WAVES, int GW, bool PAIR, int GPC, bool BF16, bool W8>

@@ -369,6 +369,12 @@ def test_gemm_plan_names_the_kernel_and_split():
     assert wq.wq_gemm_plan(64, 14336, 4096, flags=fp32) == (t128, 3)
     assert wq.wq_gemm_plan(256, 14336, 4096, flags=fp32) == (t128, 2)
     assert wq.wq_gemm_plan(256, 14336, 4096) == (t128, 1)
+    # 17..64 rows without the fp32 reduce flag: the small-M kernel in 16-row chunks, unsplit
+    for m in (17, 32, 48, 64):
+        assert wq.wq_gemm_plan(m, 14336, 4096) == (small, 1), m
+        assert wq.wq_gemm_plan(m, 14336, 4096, flags=fp32)[0] == t128, m
+    assert wq.wq_gemm_plan(65, 14336, 4096) == (t128, 1)
+    assert wq.wq_gemm_plan(32, 14336, 4096, flags=wq.WQ_FLAG_SWIGLU)[0] != small
     # the planner's split always fits the workspace the library asks for
     for m, n in ((1, 256), (64, 14336), (256, 14336), (16, 512)):
         _, s = wq.wq_gemm_plan(m, n, 1024 if n == 256 else 4096, flags=fp32)

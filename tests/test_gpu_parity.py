@@ -305,6 +305,33 @@ FEW_ROW_SHAPES = [
 ]
 
 
+# 17..64 rows without the fp32 reduce flag: the small-M kernel's direct form in 16-row
+# chunks along grid z (single and paired column blocks, ragged last chunks, group sizes,
+# zero points, act_order).
+CHUNK_SHAPES = [
+    # m, k, n, group_size, zp, act_order
+    (17, 1024, 512, 128, False, False),
+    (24, 4096, 256, 128, True, False),
+    (32, 2048, 8192, 128, False, False),
+    (33, 1024, 256, 64, True, False),
+    (48, 768, 512, 16, False, False),
+    (64, 4096, 1024, 128, False, True),
+    (50, 1536, 256, 48, True, False),
+    (61, 2048, 8192, 32, True, True),
+]
+
+
+@pytest.mark.parametrize("m,k,n,gs,zp,act_order", CHUNK_SHAPES)
+def test_row_chunks_match_oracle(dev, m, k, n, gs, zp, act_order):
+    label = f"row chunks m={m} k={k} n={n} group_size={gs} zp={zp} act_order={act_order}"
+    say(label)
+    assert wq.wq_gemm_plan(m, n, k, group_size=gs)[0] == wq.WQ_KERNEL_SMALL_M
+    case = synthetic.dense_case(m, k, n, zp=zp, act_order=act_order, group_size=gs,
+                                seed=4100 + m + k + gs)
+    c = gpu_gemm(case, dev)
+    assert_parity(c, oracle_gemm(case), label)
+
+
 @pytest.mark.parametrize("m,k,n,gs,zp,act_order,fp32,split", FEW_ROW_SHAPES)
 def test_few_rows_match_oracle(dev, m, k, n, gs, zp, act_order, fp32, split):
     label = (f"few rows m={m} k={k} n={n} group_size={gs} zp={zp} act_order={act_order} "

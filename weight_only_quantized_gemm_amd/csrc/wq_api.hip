@@ -144,6 +144,23 @@ bool plan_small(int m, int n, int k, uint32_t flags, int requested, int gpc,
   return false;
 }
 
+// The small-M plan of a dense product, if it takes one: m <= 16, or, without the fp32
+// reduce flag, up to kChunkMaxM rows as 16-row chunks (grid z) on the direct form, which
+// reads the weights once per chunk.  Measured on MI355X at K=4096, N=14336 (12 rotating
+// weight copies): chunks 20.5-21.5 us for 17-32 rows, 30.2-30.5 for 33-48, 36.6 for 64,
+// against 35.2-35.9, 41.3-41.7 and 42.0 for the unsplit row tiles; with the flag the tiles'
+// split K is faster (19.4-20.4, 23.0-23.3, 24.3), so it keeps them.  Beyond that, with a
+// requested split or with the SwiGLU epilogue, the tiled kernel.
+bool plan_small_any(int m, int n, int k, uint32_t flags, int requested, int gpc, bool swiglu,
+                    wq::SmallPlan* plan) {
+  if (m <= 16)
+    return swiglu ? plan_small_pair(m, k, gpc, plan)
+                  : plan_small(m, n, k, flags, requested, gpc, plan);
+  if (m > wq::kChunkMaxM || swiglu || requested > 1 || (flags & WQ_FLAG_FP32_REDUCE))
+    return false;
+  return plan_small(16, n, k, flags, 0, gpc, plan) && plan->direct && plan->splits == 1;
+}
+
 // fp32 partials [splits][m][n] for the largest split the small-M path may use, or for
 // m > 16 the split the tiled path chooses (the same for 128- and 64-row scale units; the
 // smaller units never split).
@@ -351,9 +368,7 @@ int wq_gemm(const wq_gemm_args* args) {
   // Plan, and check the workspace the plan needs, before anything is enqueued.
   const int gpc = subgroups(p.k, p.group_size);
   wq::SmallPlan plan{};
-  const bool small = p.m <= 16 &&
-                     (swiglu ? plan_small_pair(p.m, p.k, gpc, &plan)
-                             : plan_small(p.m, p.n, p.k, p.flags, p.split_k, gpc, &plan));
+  const bool small = plan_small_any(p.m, p.n, p.k, p.flags, p.split_k, gpc, swiglu, &plan);
   // Without a small-M plan the tiled kernel computes the product, split along K (with the
   // fp32 reduce) when its output tiles would leave CUs idle.
   const int tile_split = !small && (p.flags & WQ_FLAG_FP32_REDUCE)
@@ -405,8 +420,7 @@ int wq_gemm_plan(int m, int n, int k, int group_size, uint32_t flags, int split_
   const bool swiglu = (flags & WQ_FLAG_SWIGLU) != 0, fp8 = (flags & WQ_FLAG_FP8) != 0;
   const int gpc = subgroups(k, group_size);
   wq::SmallPlan plan{};
-  const bool small = m <= 16 && (swiglu ? plan_small_pair(m, k, gpc, &plan)
-                                        : plan_small(m, n, k, flags, split_k, gpc, &plan));
+  const bool small = plan_small_any(m, n, k, flags, split_k, gpc, swiglu, &plan);
   if (small) {
     *kernel_out = WQ_KERNEL_SMALL_M;
     *splits_out = plan.splits;

@@ -58,6 +58,9 @@ struct SmallPlan {
                    // activations once for both (4-bit weights)
 };
 bool small_plan_fits(int m, int k, const SmallPlan& plan);
+// Dense products of 17..kChunkMaxM rows without the fp32 reduce flag run on the small-M
+// kernel's direct form in 16-row chunks (grid z), one split.
+constexpr int kChunkMaxM = 64;
 // bf16: A, s and c hold bf16 values (else fp16).  fp8: b holds E4M3 weights in the FP8
 // layout (no zero points, 128-row scale units).
 hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* b,

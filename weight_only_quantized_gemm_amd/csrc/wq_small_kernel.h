@@ -180,6 +180,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   const int kwave = wave - half * KW;          // the wave's index along K
   const int nb = NB * blockIdx.x + half;
   const int split = SEG ? 0 : blockIdx.y;
+  // Row chunks (grid z, one split): the work-group's 16 rows of a product taller than 16.
+  if (!SEG && gridDim.z > 1) {
+    const int r0 = 16 * blockIdx.z;
+    a += (long)r0 * lda;
+    c += (long)r0 * (PAIR ? n / 2 : n);
+    m = m - r0 < 16 ? m - r0 : 16;
+  }
 
   // SEG: the segment's expert and rows (wave-uniform, scalar loads).
   int seg_p0 = 0;
@@ -829,7 +836,10 @@ hipError_t launch_small_t(const uint16_t* a, int lda, int m, const uint32_t* b,
           &gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16, W8, R1, DUAL>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
-  const dim3 grid(n / (PAIR || DUAL ? 32 : 16), splits);
+  // more than 16 rows: 16-row chunks along grid z (single split only)
+  const int chunks = (m + 15) / 16;
+  if (chunks > 1 && splits != 1) return hipErrorInvalidValue;
+  const dim3 grid(n / (PAIR || DUAL ? 32 : 16), splits, chunks);
   hipLaunchKernelGGL((gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16, W8, R1, DUAL>), grid,
                      dim3(WAVES * 64), lds, stream, reinterpret_cast<const f16*>(a), lda, m,
                      reinterpret_cast<const u32x4*>(b), s, reinterpret_cast<const u32x2*>(z), c,

@@ -300,6 +300,30 @@ def bench_extended(torch, torch_ops, steps, warmup):
                         f"({active:.2f} active experts on average), 3 rotating banks",
             "us": round(sec * 1e6, 2),
             "weight_tbs": round(active * one["k"] * one["n"] / 2 / sec / 1e12, 4)}
+    del banks
+    # The matching down projection at one token: K=14336, N=4096 per expert.
+    down = synthetic.moe_case(1, 1, 14336, 4096, seed=51)
+    banks = [torch_ops.ExpertBank(down["experts"] * 8, device="cuda") for _ in range(3)]
+    csrs, dcsrs = [], []
+    for r in range(16):
+        csr = wq.wq_csr_from_routes(synthetic.top2_routes(53 + r, 1, 8), 1, 2, 8)
+        csrs.append(csr)
+        dcsrs.append({key: torch_ops.to_device(np.asarray(csr[key], np.int32), "cuda")
+                      for key in ("ex_ids", "ex_off", "ex_pairs", "pair_tok")})
+    a = torch_ops.to_device(synthetic.activations(55, 2, 14336), "cuda")
+    y = torch.empty((2, 4096), dtype=torch.float16, device="cuda")
+    ident = [dict(c, pair_tok=[0, 1]) for c in csrs]
+    dident = [dict(d, pair_tok=torch_ops.to_device(np.arange(2, dtype=np.int32), "cuda"))
+              for d in dcsrs]
+
+    def down_step(i):
+        torch_ops.grouped_gemm(a, banks[i % 3], ident[i % 16], y, device_csr=dident[i % 16])
+    sec = timed_loop(torch, down_step, 48, warmup)
+    out["moe_decode_1_token_down"] = {
+        "workload": "1 token top-2 of 8 experts, down projection K=14336 N=4096 u4b8 group 128 "
+                    "over the pair rows (2 active experts), 3 rotating banks",
+        "us": round(sec * 1e6, 2),
+        "weight_tbs": round(2 * 14336 * 4096 / 2 / sec / 1e12, 4)}
     return out
 
 

@@ -305,6 +305,55 @@ FEW_ROW_SHAPES = [
 ]
 
 
+# K beyond 64 groups on one work-group per column block: sixteen waves of eight groups over
+# a staged slice (up to four rows at K = 14336), with and without the fp32 reduce flag.
+LONG_K_SHAPES = [
+    # m, k, n, group_size, zp, act_order, fp32
+    (1, 14336, 512, 128, False, False, False),
+    (1, 11008, 2048, 128, True, False, True),
+    (4, 14336, 256, 128, False, False, False),
+    (3, 16384, 512, 64, True, False, False),
+    (2, 12288, 256, 32, False, True, False),
+    (1, 8320, 256, 16, True, False, False),
+    (4, 9216, 2048, -1, False, False, True),
+]
+
+
+@pytest.mark.parametrize("m,k,n,gs,zp,act_order,fp32", LONG_K_SHAPES)
+def test_long_k_sixteen_waves_match_oracle(dev, m, k, n, gs, zp, act_order, fp32):
+    label = (f"long K m={m} k={k} n={n} group_size={gs} zp={zp} act_order={act_order} "
+             f"fp32={fp32}")
+    say(label)
+    flags = wq.WQ_FLAG_FP32_REDUCE if fp32 else 0
+    assert wq.wq_gemm_plan(m, n, k, group_size=gs, flags=flags) == (wq.WQ_KERNEL_SMALL_M, 1)
+    case = synthetic.dense_case(m, k, n, zp=zp, act_order=act_order, group_size=gs,
+                                seed=4300 + m + k + gs)
+    c = gpu_gemm(case, dev, fp32_reduce=fp32)
+    assert_parity(c, oracle_gemm(case), label)
+
+
+# More rows than one staged work-group holds at long K, without the fp32 reduce flag: row
+# chunks of 8, 4 (or fewer) rows along grid z on sixteen waves.
+LONG_K_CHUNK_SHAPES = [
+    # m, k, n, group_size, zp
+    (8, 14336, 256, 128, False),
+    (16, 11008, 512, 128, True),
+    (11, 12288, 256, 64, False),
+    (24, 8192, 512, 128, True),
+    (6, 16384, 256, 32, False),
+]
+
+
+@pytest.mark.parametrize("m,k,n,gs,zp", LONG_K_CHUNK_SHAPES)
+def test_long_k_row_chunks_match_oracle(dev, m, k, n, gs, zp):
+    label = f"long K row chunks m={m} k={k} n={n} group_size={gs} zp={zp}"
+    say(label)
+    assert wq.wq_gemm_plan(m, n, k, group_size=gs) == (wq.WQ_KERNEL_SMALL_M, 1)
+    case = synthetic.dense_case(m, k, n, zp=zp, group_size=gs, seed=4400 + m + k + gs)
+    c = gpu_gemm(case, dev)
+    assert_parity(c, oracle_gemm(case), label)
+
+
 # 17..64 rows without the fp32 reduce flag: the small-M kernel's direct form in 16-row
 # chunks along grid z (single and paired column blocks, ragged last chunks, group sizes,
 # zero points, act_order).
@@ -608,7 +657,8 @@ def test_grouped_single_expert_equals_dense(dev):
 
 # Segments of at most four rows (n_pairs - n_active + 1 <= 4) run on the small-M kernel, one
 # work-group per 16-column block and segment: one-row segments on its one-row path, up to
-# four rows on its general path; four waves of 1..8 groups or eight waves of 8 (K = 8192).
+# four rows on its general path; four waves of 1..8 groups, eight waves of 8 (K = 8192)
+# or sixteen of 8 (K beyond 64 groups).
 FEW_ROW_GROUPED = [
     # tokens, experts, k, n, group_size, zp, weighted, bf16
     (1, 8, 4096, 512, 128, False, False, False),
@@ -624,6 +674,9 @@ FEW_ROW_GROUPED = [
     (3, 5, 512, 512, 16, False, True, True),
     (4, 8, 1024, 256, 128, True, True, False),
     (5, 8, 1024, 512, 128, False, False, True),
+    # a down projection's K (sixteen waves of eight groups)
+    (1, 8, 14336, 256, 128, False, True, False),
+    (2, 8, 11008, 256, 64, True, False, False),
 ]
 
 
@@ -843,10 +896,13 @@ def test_swiglu_mlp_chain_matches_oracle(dev):
     assert_parity(out, want, "chain output", rel_elem=ACT_REL)
 
 
-def test_moe_swiglu_chain_matches_oracle(dev):
-    tokens, experts, h, i = 300, 4, 512, 256
+# 300 tokens: row tiles; 1..3 tokens (every segment at most four rows): the small-M kernel,
+# its SwiGLU pair for the gate/up projection and single blocks for the down projection.
+@pytest.mark.parametrize("tokens,experts,h,i", [(300, 4, 512, 256), (1, 8, 1024, 512),
+                                                (2, 8, 512, 256), (3, 4, 512, 256)])
+def test_moe_swiglu_chain_matches_oracle(dev, tokens, experts, h, i):
     say(f"moe swiglu chain tokens={tokens} experts={experts} hidden={h} intermediate={i}")
-    moe = synthetic.moe_case(tokens, experts, h, i, seed=610)
+    moe = synthetic.moe_case(tokens, experts, h, i, seed=610 + tokens)
     mats = [mlp_weights(620 + 30 * e, h, i, h) for e in range(experts)]
     gu_bank = torch_ops.ExpertBank([dict(gate=g, up=u) for g, u, _ in mats], device=dev)
     dn_bank = torch_ops.ExpertBank([d for _, _, d in mats], device=dev)

@@ -123,8 +123,10 @@ bool plan_small(int m, int n, int k, uint32_t flags, int requested, int gpc,
       // weights excepted).  Direct single blocks try 8 waves first, paired ones 4 (the
       // faster of the two on MI355X at M=16, K=4096); staged plans 4 waves first.
       const bool dual = pass == 0 && !(flags & WQ_FLAG_FP8) && (n / 32) * s >= kDualMinGroups;
-      for (int wi = 0; wi < 2; ++wi) {
-        const int waves = (pass == 0 && !dual) == (wi == 0) ? 8 : 4;
+      // staged 4-bit plans may take sixteen waves of eight groups (K up to 128 groups)
+      const int tries = pass == 1 && !(flags & WQ_FLAG_FP8) ? 3 : 2;
+      for (int wi = 0; wi < tries; ++wi) {
+        const int waves = wi == 2 ? 16 : (pass == 0 && !dual) == (wi == 0) ? 8 : 4;
         const int per_wave = (span + waves - 1) / waves;
         if (per_wave > 8) continue;
         wq::SmallPlan p{};
@@ -145,20 +147,34 @@ bool plan_small(int m, int n, int k, uint32_t flags, int requested, int gpc,
 }
 
 // The small-M plan of a dense product, if it takes one: m <= 16, or, without the fp32
-// reduce flag, up to kChunkMaxM rows as 16-row chunks (grid z) on the direct form, which
-// reads the weights once per chunk.  Measured on MI355X at K=4096, N=14336 (12 rotating
-// weight copies): chunks 20.5-21.5 us for 17-32 rows, 30.2-30.5 for 33-48, 36.6 for 64,
-// against 35.2-35.9, 41.3-41.7 and 42.0 for the unsplit row tiles; with the flag the tiles'
-// split K is faster (19.4-20.4, 23.0-23.3, 24.3), so it keeps them.  Beyond that, with a
-// requested split or with the SwiGLU epilogue, the tiled kernel.
+// reduce flag, up to kChunkMaxM rows as row chunks (grid z), each reading the weights.
+// Measured on MI355X at K=4096, N=14336 (12 rotating weight copies): 16-row chunks
+// 20.5-21.5 us for 17-32 rows, 30.2-30.5 for 33-48, 36.6 for 64, against 35.2-35.9,
+// 41.3-41.7 and 42.0 for the unsplit row tiles; with the flag the tiles' split K is faster
+// (19.4-20.4, 23.0-23.3, 24.3), so it keeps them.  Beyond that, with a requested split or
+// with the SwiGLU epilogue, the tiled kernel.
 bool plan_small_any(int m, int n, int k, uint32_t flags, int requested, int gpc, bool swiglu,
                     wq::SmallPlan* plan) {
-  if (m <= 16)
-    return swiglu ? plan_small_pair(m, k, gpc, plan)
-                  : plan_small(m, n, k, flags, requested, gpc, plan);
+  if (m <= 16) {
+    if (swiglu) return plan_small_pair(m, k, gpc, plan);
+    if (plan_small(m, n, k, flags, requested, gpc, plan)) return true;
+  }
   if (m > wq::kChunkMaxM || swiglu || requested > 1 || (flags & WQ_FLAG_FP32_REDUCE))
     return false;
-  return plan_small(16, n, k, flags, 0, gpc, plan) && plan->direct && plan->splits == 1;
+  // Row chunks, at most four: 16 rows on the direct form, or, where K is too long for it
+  // (beyond 64 groups), a staged slice of 8, 4, 2 or 1 rows (the row tiles that would take
+  // such a product unsplit are as few as N / 256 work-groups).
+  for (int rows = 16; rows >= 1; rows /= 2) {
+    if ((m + rows - 1) / rows > 4) break;
+    if (rows >= m) continue;
+    wq::SmallPlan q{};
+    if (plan_small(rows, n, k, flags, 0, gpc, &q) && q.splits == 1 && (q.direct || rows < 9)) {
+      q.rows = rows;
+      *plan = q;
+      return true;
+    }
+  }
+  return false;
 }
 
 // fp32 partials [splits][m][n] for the largest split the small-M path may use, or for

@@ -71,10 +71,14 @@ bool small_plan_fits(int m, int k, const SmallPlan& plan) {
   if (plan.pair && plan.splits != 1) return false;  // the SwiGLU epilogue needs whole sums
   const int span = (groups + plan.splits - 1) / plan.splits;
   const int min_span = groups / plan.splits;  // every split holds at least this many groups
-  if (plan.pair ? (plan.waves != 8 && plan.waves != 16) : (plan.waves != 4 && plan.waves != 8))
+  if (plan.pair ? (plan.waves != 8 && plan.waves != 16)
+                : (plan.waves != 4 && plan.waves != 8 && plan.waves != 16))
     return false;
+  // sixteen waves without the pair: staged activations and eight groups per wave only
+  if (!plan.pair && plan.waves == 16 && (plan.direct || plan.depth != 8)) return false;
   const int kw = plan.pair ? plan.waves / 2 : plan.waves;  // waves along K per block
-  if (span > kMaxSpan || min_span < kw) return false;   // every wave has a group
+  if (span > small_max_span(plan.waves, plan.pair) || min_span < kw)
+    return false;  // at most eight groups and at least one per wave
   if ((span + kw - 1) / kw > plan.depth || plan.depth > 8) return false;
   if (plan.dual && !plan.direct) return false;
   if (plan.direct)  // per-wave LDS regions of `depth` activation tiles and scale words
@@ -89,19 +93,22 @@ bool small_plan_fits(int m, int k, const SmallPlan& plan) {
 }
 
 bool grouped_small_plan(const GroupedProblem& p, int rows, SmallPlan* plan) {
-  if (p.fp8 || p.swiglu || rows < 1 || rows > kSegRows) return false;
+  if (p.fp8 || rows < 1 || rows > kSegRows) return false;
   if (p.n_active > 65535) return false;                     // segments along grid y
   if ((long long)p.n_tokens * p.k > 0x7fffffffLL) return false;  // 32-bit row offsets
   const int groups = p.k / kGroup;
-  for (int waves = 4; waves <= 8; waves *= 2) {
-    const int per_wave = (groups + waves - 1) / waves;
+  // waves along K per block: 4, 8 or 16 (twice that with the SwiGLU pair, half on each
+  // block, at most 16 waves in all)
+  for (int kw = 4; kw <= (p.swiglu ? 8 : 16); kw *= 2) {
+    const int per_wave = (groups + kw - 1) / kw;
     if (per_wave > 8) continue;
     SmallPlan q{};
-    q.waves = waves;
+    q.waves = p.swiglu ? 2 * kw : kw;
     q.splits = 1;
     q.depth = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 8;
+    q.pair = p.swiglu;
     q.gpc = p.gpc;
-    if (waves == 8 && q.depth != 8) continue;  // the instances of eight waves
+    if (kw >= 8 && q.depth != 8) continue;  // the instances of 8 or 16 waves per block
     if (small_plan_fits(rows, p.k, q)) {
       *plan = q;
       return true;
@@ -114,7 +121,7 @@ hipError_t launch_grouped_small(const GroupedProblem& p, int rows, const SmallPl
                                 hipStream_t stream) {
   SmallPlan check{};
   if (!grouped_small_plan(p, rows, &check) || check.waves != plan.waves ||
-      check.depth != plan.depth)
+      check.depth != plan.depth || check.pair != plan.pair)
     return hipErrorInvalidConfiguration;
   if (p.bf16) {
     switch (p.gpc) {
@@ -136,7 +143,8 @@ hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* 
                              const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                              const SmallPlan& plan, float* partials, bool bf16, bool fp8,
                              hipStream_t stream) {
-  if (!small_plan_fits(m, k, plan)) return hipErrorInvalidConfiguration;
+  if (!small_plan_fits(plan.rows > 0 && plan.rows < m ? plan.rows : m, k, plan))
+    return hipErrorInvalidConfiguration;
   if (fp8) {
     if (z != nullptr) return hipErrorInvalidValue;
     return bf16 ? launch_small_fp8_bf16(a, lda, m, b, s, c, n, k, plan, partials, stream)

@@ -56,10 +56,13 @@ struct SmallPlan {
                    // points into its own LDS region (no shared slice; not with pair)
   bool dual;       // direct only: each wave covers two adjacent column blocks, reading the
                    // activations once for both (4-bit weights)
+  int rows;        // rows per work-group when the product is split into row chunks along
+                   // grid z (one split), else 0 (every work-group takes all m rows)
 };
 bool small_plan_fits(int m, int k, const SmallPlan& plan);
-// Dense products of 17..kChunkMaxM rows without the fp32 reduce flag run on the small-M
-// kernel's direct form in 16-row chunks (grid z), one split.
+// Dense products of up to kChunkMaxM rows without the fp32 reduce flag that one small-M
+// work-group cannot take (more than 16 rows, or a staged slice too long for LDS) run on it in
+// at most four row chunks along grid z (SmallPlan::rows), one split.
 constexpr int kChunkMaxM = 64;
 // bf16: A, s and c hold bf16 values (else fp16).  fp8: b holds E4M3 weights in the FP8
 // layout (no zero points, 128-row scale units).
@@ -137,11 +140,12 @@ struct GroupedProblem {
 };
 hipError_t launch_grouped_tile(const GroupedProblem& p, hipStream_t stream);
 // Grouped products whose segments all hold few rows run on the small-M kernel instead (4-bit
-// weights, no SwiGLU epilogue): one work-group per 16-column block and segment, its
-// activation rows gathered through pair_tok and its outputs scattered to the pair rows.
-// `rows` bounds every segment's row count (n_pairs - n_active + 1 for a CSR of non-empty
-// segments) and is 1 or at most kSegRows; `plan` is a single-split staged plan for m = rows
-// (four waves, or eight with GW 8).
+// weights): one work-group per 16-column block (a gate/up pair of blocks with the SwiGLU
+// epilogue) and segment, its activation rows gathered through pair_tok and its outputs
+// scattered to the pair rows.  `rows` bounds every segment's row count (n_pairs - n_active
+// + 1 for a CSR of non-empty segments) and is 1 or at most kSegRows; `plan` is a
+// single-split staged plan for m = rows (four waves per block, or eight or sixteen with
+// GW 8).
 constexpr int kSegRows = 4;
 bool grouped_small_plan(const GroupedProblem& p, int rows, SmallPlan* plan);
 hipError_t launch_grouped_small(const GroupedProblem& p, int rows, const SmallPlan& plan,

@@ -64,17 +64,20 @@ namespace {
 // and reduction buffers and the dynamically sized activation slice (fp16 [m][span*128],
 // padded to a whole number of staging rounds).
 constexpr int kLdsBytes = 160 * 1024;
-constexpr int kMaxSpan = 64;   // groups per work-group covered by the staged scales
 
-// Scale and zero-point staging: the work-group's blocks hold at most NB x kMaxSpan chunks
-// of GPC units, 8 scale dwords and one zero-point pair per unit.  Threads stage whole
-// slots of T entries (T = waves x 64, a multiple of 256, so the scale count divides).
-constexpr int small_scale_slots(int waves, bool pair, int gpc) {
-  return (pair ? 2 : 1) * kMaxSpan * 8 * gpc / (waves * 64);
+// Groups of K a staged work-group covers: a wave takes at most eight, so eight per wave
+// along K (pair: half the waves on each block).
+constexpr int small_max_span(int waves, bool pair) { return 8 * (pair ? waves / 2 : waves); }
+
+// Scale and zero-point staging: the work-group's nb blocks hold at most nb x
+// small_max_span chunks of GPC units, 8 scale dwords and one zero-point pair per unit.
+// Threads stage whole slots of T entries (T = waves x 64).
+constexpr int small_scale_slots(int waves, bool pair, int nb, int gpc) {
+  return nb * small_max_span(waves, pair) * 8 * gpc / (waves * 64);
 }
-constexpr int small_zero_slots(int waves, bool pair, int gpc) {
-  return (pair ? 2 : 1) * kMaxSpan * gpc > waves * 64
-             ? (pair ? 2 : 1) * kMaxSpan * gpc / (waves * 64) : 1;
+constexpr int small_zero_slots(int waves, bool pair, int nb, int gpc) {
+  return nb * small_max_span(waves, pair) * gpc > waves * 64
+             ? nb * small_max_span(waves, pair) * gpc / (waves * 64) : 1;
 }
 // Static LDS of an instance (see the kernel's __shared__ arrays), an upper bound over ZP.
 // (pair: two column blocks split between the waves; dual: two column blocks per wave;
@@ -82,10 +85,11 @@ constexpr int small_zero_slots(int waves, bool pair, int gpc) {
 constexpr long small_static_lds(int waves, bool pair, int gpc, bool r1, bool dual,
                                 bool direct = false) {
   if (direct) return 4 + 8 + 16 + 4;
-  return (long)small_scale_slots(waves, pair || dual, gpc) * waves * 64 * 4    // s_lds
-         + (long)small_zero_slots(waves, pair || dual, gpc) * waves * 64 * 8   // z_lds
-         + (long)(dual ? 2 : 1) * waves * 64 * 16                              // red
-         + (r1 ? (long)kMaxSpan * 16 * 4 : 0);                                 // rsum_lds
+  const int nb = pair || dual ? 2 : 1;
+  return (long)small_scale_slots(waves, pair, nb, gpc) * waves * 64 * 4    // s_lds
+         + (long)small_zero_slots(waves, pair, nb, gpc) * waves * 64 * 8   // z_lds
+         + (long)(dual ? 2 : 1) * waves * 64 * 16                          // red
+         + (r1 ? (long)small_max_span(waves, pair) * 16 * 4 : 0);          // rsum_lds
 }
 
 // Direct activations: each wave owns an LDS region holding, for each of its GW groups, the
@@ -130,7 +134,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     const int32_t* __restrict__ ex_ids, const int32_t* __restrict__ ex_off,
     const int32_t* __restrict__ ex_pairs, const int32_t* __restrict__ pair_tok,
     const float* __restrict__ topk_w, long b_stride, long s_stride, long z_stride,
-    int n_expert, int n_pairs, int n_tokens) {
+    int n_expert, int n_pairs, int n_tokens, int chunk_rows) {
   using A = Act<BF16>;
   static_assert(!W8 || (!ZP && GPC == 1), "E4M3: 128-row scale units, no zero points");
   constexpr int NV = W8 ? 2 : 1;  // 16-byte weight vectors per lane and group
@@ -149,17 +153,18 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   // DUAL: each wave applies its activation operands to two adjacent column blocks, so the
   // activations are read once per two blocks (direct activations, 4-bit weights).
   static_assert(!DUAL || (DA && !PAIR && !W8 && !R1), "dual blocks: direct activations");
-  static_assert(!SEG || (!DA && !PAIR && !W8 && !DUAL), "segments: staged, 4-bit, one block");
+  static_assert(!SEG || (!DA && !W8 && !DUAL), "segments: staged activations, 4-bit weights");
   constexpr int SR = R1 ? 1 : kSegRows;  // rows of a segment (SEG)
   constexpr int T = WAVES * 64;
   constexpr int NB = (PAIR || DUAL) ? 2 : 1;  // column blocks of the work-group
   constexpr int NBV = DUAL ? 2 : 1;           // column blocks of each wave
   constexpr int KW = PAIR ? WAVES / 2 : WAVES;  // waves splitting K for one block
-  constexpr int SU = small_scale_slots(WAVES, PAIR || DUAL, GPC);  // staged scale dwords
-  constexpr int ZU = small_zero_slots(WAVES, PAIR || DUAL, GPC);   // staged zero points
+  constexpr int MS = small_max_span(WAVES, PAIR);  // groups the staged scales cover
+  constexpr int SU = small_scale_slots(WAVES, PAIR, NB, GPC);  // staged scale dwords
+  constexpr int ZU = small_zero_slots(WAVES, PAIR, NB, GPC);   // staged zero points
   constexpr int JQ = GPC <= 4 ? 4 / GPC : 1;  // 32-row MFMA steps per scale unit (GPC <= 4)
-  static_assert(SU >= 1 && SU * T == NB * kMaxSpan * 8 * GPC, "scale slots cover the range");
-  static_assert(ZU * T >= NB * kMaxSpan * GPC, "zero-point slots cover the range");
+  static_assert(SU >= 1 && SU * T == NB * MS * 8 * GPC, "scale slots cover the range");
+  static_assert(ZU * T >= NB * MS * GPC, "zero-point slots cover the range");
   extern __shared__ f16x8 a_lds[];            // [m][span*16] granules (+ padding), or direct
   __shared__ uint32_t s_lds[DA ? 1 : SU * T];          // scales, [block][chunk][unit][col]
   __shared__ u32x2 z_lds[ZP && !DA ? ZU * T : 1];      // zero points, [block][chunk][unit]
@@ -168,7 +173,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   // term of the unit's partial).
   constexpr int EX = GPC == 8 ? 2 : 4;  // activation sums per scale unit: one per row class
   constexpr bool R1B = R1;              // one row: activation sums staged
-  __shared__ float rsum_lds[R1B ? kMaxSpan * GPC * EX : 1];
+  __shared__ float rsum_lds[R1B ? MS * GPC * EX : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -180,12 +185,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   const int kwave = wave - half * KW;          // the wave's index along K
   const int nb = NB * blockIdx.x + half;
   const int split = SEG ? 0 : blockIdx.y;
-  // Row chunks (grid z, one split): the work-group's 16 rows of a product taller than 16.
+  // Row chunks (grid z, one split): the work-group's chunk_rows rows of a taller product.
   if (!SEG && gridDim.z > 1) {
-    const int r0 = 16 * blockIdx.z;
+    const int r0 = chunk_rows * blockIdx.z;
     a += (long)r0 * lda;
     c += (long)r0 * (PAIR ? n / 2 : n);
-    m = m - r0 < 16 ? m - r0 : 16;
+    m = m - r0 < chunk_rows ? m - r0 : chunk_rows;
   }
 
   // SEG: the segment's expert and rows (wave-uniform, scalar loads).
@@ -778,7 +783,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = 4 * qd + e;
-      if (row < m) c[(long)row * (n / 2) + colj] = A::round(silu_times(gs[e], us[e]));
+      if (row >= m) continue;
+      // SEG: the pair's row of the activation (not written for an out-of-range pair)
+      const int pr = SEG ? seg_select(seg_pair, row) : row;
+      if (pr >= 0) c[(long)pr * (n / 2) + colj] = A::round(silu_times(gs[e], us[e]));
     }
     return;
   }
@@ -825,7 +833,7 @@ template <bool ZP, int WAVES, int GW, int STAGE, bool PAIR, int GPC, bool BF16, 
           bool R1, bool DUAL>
 hipError_t launch_small_t(const uint16_t* a, int lda, int m, const uint32_t* b,
                           const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
-                          int splits, float* partials, hipStream_t stream) {
+                          int splits, float* partials, int chunk_rows, hipStream_t stream) {
   const int groups = k / kGroup;
   // The activation slice of this instance (its size is fixed by STAGE and WAVES), or the
   // waves' direct regions.
@@ -836,71 +844,88 @@ hipError_t launch_small_t(const uint16_t* a, int lda, int m, const uint32_t* b,
           &gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16, W8, R1, DUAL>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
-  // more than 16 rows: 16-row chunks along grid z (single split only)
-  const int chunks = (m + 15) / 16;
+  // more rows than a work-group takes: chunks of chunk_rows rows along grid z (one split)
+  if (chunk_rows < 1) return hipErrorInvalidValue;
+  const int chunks = (m + chunk_rows - 1) / chunk_rows;
   if (chunks > 1 && splits != 1) return hipErrorInvalidValue;
   const dim3 grid(n / (PAIR || DUAL ? 32 : 16), splits, chunks);
   hipLaunchKernelGGL((gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16, W8, R1, DUAL>), grid,
                      dim3(WAVES * 64), lds, stream, reinterpret_cast<const f16*>(a), lda, m,
                      reinterpret_cast<const u32x4*>(b), s, reinterpret_cast<const u32x2*>(z), c,
                      n, groups, splits, partials, nullptr, nullptr, nullptr, nullptr, nullptr,
-                     0L, 0L, 0L, 0, 0, 0);
+                     0L, 0L, 0L, 0, 0, 0, chunk_rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   return launch_reduce_splits(partials, c, m, n, splits, BF16, stream);
 }
 
-// Grouped products with few rows per segment: grid (n / 16, n_active), one split.
-template <bool ZP, int WAVES, int GW, int STAGE, int GPC, bool BF16, bool R1>
+// Grouped products with few rows per segment: grid (n / 16, n_active), one split; with the
+// SwiGLU pair, (n / 32, n_active).
+template <bool ZP, int WAVES, int GW, int STAGE, bool PAIR, int GPC, bool BF16, bool R1>
 hipError_t launch_seg_t(const GroupedProblem& p, int rows, hipStream_t stream) {
   constexpr size_t lds = (size_t)STAGE * WAVES * 64 * sizeof(f16x8);
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(
-          &gemm_small_kernel<ZP, WAVES, GW, STAGE, false, GPC, BF16, false, R1, false, true>),
+          &gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16, false, R1, false, true>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
-  const dim3 grid(p.n / 16, p.n_active);
+  const dim3 grid(p.n / (PAIR ? 32 : 16), p.n_active);
   hipLaunchKernelGGL(
-      (gemm_small_kernel<ZP, WAVES, GW, STAGE, false, GPC, BF16, false, R1, false, true>), grid,
+      (gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16, false, R1, false, true>), grid,
       dim3(WAVES * 64), lds, stream, reinterpret_cast<const f16*>(p.a), p.k, rows,
       reinterpret_cast<const u32x4*>(p.b_bank), reinterpret_cast<const uint16_t*>(p.s_bank),
       reinterpret_cast<const u32x2*>(p.z_bank), p.y, p.n, p.k / kGroup, 1, nullptr, p.ex_ids,
       p.ex_off, p.ex_pairs, p.pair_tok, p.topk_w, (long)(p.b_stride / 16),
-      (long)(p.s_stride / 2), (long)(p.z_stride / 8), p.n_expert, p.n_pairs, p.n_tokens);
+      (long)(p.s_stride / 2), (long)(p.z_stride / 8), p.n_expert, p.n_pairs, p.n_tokens, 0);
   return hipGetLastError();
 }
 
-template <bool ZP, int WAVES, int GW, int GPC, bool BF16>
+template <bool ZP, int WAVES, int GW, bool PAIR, int GPC, bool BF16>
 hipError_t launch_seg_stage(const GroupedProblem& p, int rows, hipStream_t stream) {
   const int slots = round_slots(stage_slots(rows, p.k / kGroup, WAVES));
   if (rows == 1) {
     switch (slots) {
-      case 1: return launch_seg_t<ZP, WAVES, GW, 1, GPC, BF16, true>(p, rows, stream);
-      case 2: return launch_seg_t<ZP, WAVES, GW, 2, GPC, BF16, true>(p, rows, stream);
+      case 1: return launch_seg_t<ZP, WAVES, GW, 1, PAIR, GPC, BF16, true>(p, rows, stream);
+      case 2: return launch_seg_t<ZP, WAVES, GW, 2, PAIR, GPC, BF16, true>(p, rows, stream);
       default: return hipErrorInvalidValue;
     }
   }
   switch (slots) {
-    case 1: return launch_seg_t<ZP, WAVES, GW, 1, GPC, BF16, false>(p, rows, stream);
-    case 2: return launch_seg_t<ZP, WAVES, GW, 2, GPC, BF16, false>(p, rows, stream);
-    case 4: return launch_seg_t<ZP, WAVES, GW, 4, GPC, BF16, false>(p, rows, stream);
-    case 8: return launch_seg_t<ZP, WAVES, GW, 8, GPC, BF16, false>(p, rows, stream);
+    case 1: return launch_seg_t<ZP, WAVES, GW, 1, PAIR, GPC, BF16, false>(p, rows, stream);
+    case 2: return launch_seg_t<ZP, WAVES, GW, 2, PAIR, GPC, BF16, false>(p, rows, stream);
+    case 4: return launch_seg_t<ZP, WAVES, GW, 4, PAIR, GPC, BF16, false>(p, rows, stream);
+    case 8: return launch_seg_t<ZP, WAVES, GW, 8, PAIR, GPC, BF16, false>(p, rows, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-// Four waves of 1, 2, 4 or 8 groups (K up to 32 groups), or eight waves of 8 (up to 64).
+// Four waves of 1, 2, 4 or 8 groups (K up to 32 groups), or eight or sixteen waves of 8 (up
+// to 64 or 128); with the SwiGLU pair twice the waves (at most sixteen), half on each block.
 template <bool ZP, int GPC, bool BF16>
 hipError_t launch_seg_zp(const GroupedProblem& p, int rows, const SmallPlan& plan,
                          hipStream_t stream) {
+  if (plan.pair) {
+    if (plan.waves == 16)
+      return plan.depth == 8 ? launch_seg_stage<ZP, 16, 8, true, GPC, BF16>(p, rows, stream)
+                             : hipErrorInvalidValue;
+    switch (plan.depth) {
+      case 1: return launch_seg_stage<ZP, 8, 1, true, GPC, BF16>(p, rows, stream);
+      case 2: return launch_seg_stage<ZP, 8, 2, true, GPC, BF16>(p, rows, stream);
+      case 4: return launch_seg_stage<ZP, 8, 4, true, GPC, BF16>(p, rows, stream);
+      default: return launch_seg_stage<ZP, 8, 8, true, GPC, BF16>(p, rows, stream);
+    }
+  }
+  if (plan.waves == 16)
+    return plan.depth == 8 ? launch_seg_stage<ZP, 16, 8, false, GPC, BF16>(p, rows, stream)
+                           : hipErrorInvalidValue;
   if (plan.waves == 8)
-    return plan.depth == 8 ? launch_seg_stage<ZP, 8, 8, GPC, BF16>(p, rows, stream)
+    return plan.depth == 8 ? launch_seg_stage<ZP, 8, 8, false, GPC, BF16>(p, rows, stream)
                            : hipErrorInvalidValue;
   switch (plan.depth) {
-    case 1: return launch_seg_stage<ZP, 4, 1, GPC, BF16>(p, rows, stream);
-    case 2: return launch_seg_stage<ZP, 4, 2, GPC, BF16>(p, rows, stream);
-    case 4: return launch_seg_stage<ZP, 4, 4, GPC, BF16>(p, rows, stream);
-    default: return launch_seg_stage<ZP, 4, 8, GPC, BF16>(p, rows, stream);
+    case 1: return launch_seg_stage<ZP, 4, 1, false, GPC, BF16>(p, rows, stream);
+    case 2: return launch_seg_stage<ZP, 4, 2, false, GPC, BF16>(p, rows, stream);
+    case 4: return launch_seg_stage<ZP, 4, 4, false, GPC, BF16>(p, rows, stream);
+    default: return launch_seg_stage<ZP, 4, 8, false, GPC, BF16>(p, rows, stream);
   }
 }
 
@@ -916,25 +941,26 @@ hipError_t launch_small_stage(const uint16_t* a, int lda, int m, const uint32_t*
                               const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                               const SmallPlan& plan, float* partials, hipStream_t stream) {
   const int span = (k / kGroup + plan.splits - 1) / plan.splits;
+  const int mw = plan.rows > 0 && plan.rows < m ? plan.rows : m;  // rows per work-group
   if (plan.direct) {
-    if constexpr (!PAIR) {
+    if constexpr (!PAIR && WAVES <= 8) {
       if constexpr (!W8) {
         if (plan.dual)
           return launch_small_t<ZP, WAVES, GW, 0, PAIR, GPC, BF16, W8, false, true>(
-              a, lda, m, b, s, z, c, n, k, plan.splits, partials, stream);
+              a, lda, m, b, s, z, c, n, k, plan.splits, partials, mw, stream);
       }
       return launch_small_t<ZP, WAVES, GW, 0, PAIR, GPC, BF16, W8, false, false>(
-          a, lda, m, b, s, z, c, n, k, plan.splits, partials, stream);
+          a, lda, m, b, s, z, c, n, k, plan.splits, partials, mw, stream);
     }
     return hipErrorInvalidValue;
   }
   if constexpr (!W8) {
-    // One row (at most 64 groups: at most four slots per thread).
-    if (m == 1) {
+    // One row (at most 128 groups: at most four slots per thread).
+    if (mw == 1) {
 #define WQ_SMALL1(ST)                                                                        \
   launch_small_t<ZP, WAVES, GW, ST, PAIR, GPC, BF16, W8, true, false>(                        \
-      a, lda, m, b, s, z, c, n, k, plan.splits, partials, stream)
-      switch (round_slots(stage_slots(m, span, WAVES))) {
+      a, lda, m, b, s, z, c, n, k, plan.splits, partials, mw, stream)
+      switch (round_slots(stage_slots(mw, span, WAVES))) {
         case 1: return WQ_SMALL1(1);
         case 2: return WQ_SMALL1(2);
         case 4: return WQ_SMALL1(4);
@@ -945,8 +971,8 @@ hipError_t launch_small_stage(const uint16_t* a, int lda, int m, const uint32_t*
   }
 #define WQ_SMALL(ST)                                                                         \
   launch_small_t<ZP, WAVES, GW, ST, PAIR, GPC, BF16, W8, false, false>(                       \
-      a, lda, m, b, s, z, c, n, k, plan.splits, partials, stream)
-  switch (round_slots(stage_slots(m, span, WAVES))) {
+      a, lda, m, b, s, z, c, n, k, plan.splits, partials, mw, stream)
+  switch (round_slots(stage_slots(mw, span, WAVES))) {
     case 1: return WQ_SMALL(1);
     case 2: return WQ_SMALL(2);
     case 4: return WQ_SMALL(4);
@@ -983,6 +1009,10 @@ hipError_t launch_small_waves(const uint16_t* a, int lda, int m, const uint32_t*
     return launch_small_gw<ZP, 8, true, GPC, BF16, false>(a, lda, m, b, s, z, c, n, k, plan, partials,
                                              stream);
   }
+  if (plan.waves == 16)  // staged, eight groups per wave (K beyond 64 groups)
+    return plan.depth == 8 ? launch_small_stage<ZP, 16, 8, false, GPC, BF16, false>(
+                                 a, lda, m, b, s, z, c, n, k, plan, partials, stream)
+                           : hipErrorInvalidValue;
   if (plan.waves == 8)
     return launch_small_gw<ZP, 8, false, GPC, BF16, false>(a, lda, m, b, s, z, c, n, k, plan, partials,
                                               stream);

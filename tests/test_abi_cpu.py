@@ -375,6 +375,12 @@ def test_gemm_plan_names_the_kernel_and_split():
         assert wq.wq_gemm_plan(m, 14336, 4096, flags=fp32)[0] == t128, m
     assert wq.wq_gemm_plan(65, 14336, 4096) == (t128, 1)
     assert wq.wq_gemm_plan(32, 14336, 4096, flags=wq.WQ_FLAG_SWIGLU)[0] != small
+    # long K: sixteen waves on one work-group per column block (no flag: never split);
+    # with the flag, beyond 128 groups, splits of at most 64 groups
+    assert wq.wq_gemm_plan(1, 4096, 14336) == (small, 1)
+    assert wq.wq_gemm_plan(1, 8192, 28672) == (small, 1)
+    assert wq.wq_gemm_plan(1, 8192, 28672, flags=fp32) == (small, 4)
+    assert wq.wq_gemm_plan(8, 4096, 14336) == (small, 1)   # two staged 4-row chunks
     # the planner's split always fits the workspace the library asks for
     for m, n in ((1, 256), (64, 14336), (256, 14336), (16, 512)):
         _, s = wq.wq_gemm_plan(m, n, 1024 if n == 256 else 4096, flags=fp32)

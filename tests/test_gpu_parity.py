@@ -305,8 +305,9 @@ FEW_ROW_SHAPES = [
 ]
 
 
-# K beyond 64 groups on one work-group per column block: sixteen waves of eight groups over
-# a staged slice (up to four rows at K = 14336), with and without the fp32 reduce flag.
+# K beyond 64 groups on one work-group per column block: sixteen waves of eight (or, beyond
+# 128 groups, sixteen) groups over a staged slice (up to four rows at K = 14336), with and
+# without the fp32 reduce flag.
 LONG_K_SHAPES = [
     # m, k, n, group_size, zp, act_order, fp32
     (1, 14336, 512, 128, False, False, False),
@@ -316,6 +317,10 @@ LONG_K_SHAPES = [
     (2, 12288, 256, 32, False, True, False),
     (1, 8320, 256, 16, True, False, False),
     (4, 9216, 2048, -1, False, False, True),
+    # beyond 128 groups: sixteen groups per wave
+    (1, 28672, 256, 128, False, False, False),
+    (2, 20480, 512, 128, True, False, False),
+    (1, 24576, 2048, 32, True, False, True),
 ]
 
 
@@ -325,7 +330,9 @@ def test_long_k_sixteen_waves_match_oracle(dev, m, k, n, gs, zp, act_order, fp32
              f"fp32={fp32}")
     say(label)
     flags = wq.WQ_FLAG_FP32_REDUCE if fp32 else 0
-    assert wq.wq_gemm_plan(m, n, k, group_size=gs, flags=flags) == (wq.WQ_KERNEL_SMALL_M, 1)
+    kernel, splits = wq.wq_gemm_plan(m, n, k, group_size=gs, flags=flags)
+    # (with the flag, beyond 128 groups the planner splits K into at most 64 groups)
+    assert kernel == wq.WQ_KERNEL_SMALL_M and (splits == 1 or (fp32 and k // 128 > 128))
     case = synthetic.dense_case(m, k, n, zp=zp, act_order=act_order, group_size=gs,
                                 seed=4300 + m + k + gs)
     c = gpu_gemm(case, dev, fp32_reduce=fp32)
@@ -341,6 +348,8 @@ LONG_K_CHUNK_SHAPES = [
     (11, 12288, 256, 64, False),
     (24, 8192, 512, 128, True),
     (6, 16384, 256, 32, False),
+    (4, 32768, 256, 64, True),
+    (8, 28672, 256, 128, False),
 ]
 
 

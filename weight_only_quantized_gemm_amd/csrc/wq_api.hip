@@ -109,6 +109,10 @@ bool plan_small(int m, int n, int k, uint32_t flags, int requested, int gpc,
   } else if (fp32) {
     const int col_blocks = n / 16;
     s = col_blocks >= 128 ? 1 : (256 + col_blocks - 1) / col_blocks;
+    // Beyond 128 groups a single work-group per column block would need sixteen groups per
+    // wave; splits of at most 64 groups were faster where the flag allows them (MI355X,
+    // K=28672, N=8192: m=1 27.0 against 31.9 us unsplit, m=4 34.8 against 42.2).
+    if (groups > 128 && s < (groups + 63) / 64) s = (groups + 63) / 64;
     const int max_s = groups / 4 > 0 ? groups / 4 : 1;  // keep a group per wave of a split
     if (s > max_s) s = max_s;
   }
@@ -123,16 +127,17 @@ bool plan_small(int m, int n, int k, uint32_t flags, int requested, int gpc,
       // weights excepted).  Direct single blocks try 8 waves first, paired ones 4 (the
       // faster of the two on MI355X at M=16, K=4096); staged plans 4 waves first.
       const bool dual = pass == 0 && !(flags & WQ_FLAG_FP8) && (n / 32) * s >= kDualMinGroups;
-      // staged 4-bit plans may take sixteen waves of eight groups (K up to 128 groups)
+      // staged 4-bit plans may take sixteen waves of eight or sixteen groups (K up to 256
+      // groups)
       const int tries = pass == 1 && !(flags & WQ_FLAG_FP8) ? 3 : 2;
       for (int wi = 0; wi < tries; ++wi) {
         const int waves = wi == 2 ? 16 : (pass == 0 && !dual) == (wi == 0) ? 8 : 4;
         const int per_wave = (span + waves - 1) / waves;
-        if (per_wave > 8) continue;
+        if (per_wave > (waves == 16 ? 16 : 8)) continue;
         wq::SmallPlan p{};
         p.waves = waves;
         p.splits = s;
-        p.depth = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 8;
+        p.depth = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : per_wave <= 8 ? 8 : 16;
         p.gpc = gpc;
         p.direct = pass == 0;
         p.dual = dual;

@@ -74,22 +74,25 @@ bool small_plan_fits(int m, int k, const SmallPlan& plan) {
   if (plan.pair ? (plan.waves != 8 && plan.waves != 16)
                 : (plan.waves != 4 && plan.waves != 8 && plan.waves != 16))
     return false;
-  // sixteen waves without the pair: staged activations and eight groups per wave only
-  if (!plan.pair && plan.waves == 16 && (plan.direct || plan.depth != 8)) return false;
+  // sixteen waves without the pair: staged activations and eight or sixteen groups per
+  // wave only; sixteen groups per wave only there
+  if (!plan.pair && plan.waves == 16 && (plan.direct || plan.depth < 8)) return false;
+  if (plan.depth > (!plan.pair && plan.waves == 16 ? 16 : 8)) return false;
   const int kw = plan.pair ? plan.waves / 2 : plan.waves;  // waves along K per block
-  if (span > small_max_span(plan.waves, plan.pair) || min_span < kw)
-    return false;  // at most eight groups and at least one per wave
-  if ((span + kw - 1) / kw > plan.depth || plan.depth > 8) return false;
+  if (span > small_max_span(plan.waves, plan.pair, plan.depth) || min_span < kw)
+    return false;  // at most `depth` groups and at least one per wave
+  if ((span + kw - 1) / kw > plan.depth) return false;
   if (plan.dual && !plan.direct) return false;
   if (plan.direct)  // per-wave LDS regions of `depth` activation tiles and scale words
     return !plan.pair &&
-           small_static_lds(plan.waves, false, plan.gpc, false, plan.dual, true) +
+           small_static_lds(plan.waves, false, plan.depth, plan.gpc, false, plan.dual, true) +
                    small_direct_lds(plan.waves, plan.depth, plan.gpc, true, plan.dual) <=
                kLdsBytes;
   const int slots = stage_slots(m, span, plan.waves);
   const long dynamic = (long)round_slots(slots) * plan.waves * 64 * (long)sizeof(f16x8);
   return slots <= 16 &&
-         dynamic + small_static_lds(plan.waves, plan.pair, plan.gpc, m == 1, false) <= kLdsBytes;
+         dynamic + small_static_lds(plan.waves, plan.pair, plan.depth, plan.gpc, m == 1,
+                                    false) <= kLdsBytes;
 }
 
 bool grouped_small_plan(const GroupedProblem& p, int rows, SmallPlan* plan) {

@@ -65,31 +65,33 @@ namespace {
 // padded to a whole number of staging rounds).
 constexpr int kLdsBytes = 160 * 1024;
 
-// Groups of K a staged work-group covers: a wave takes at most eight, so eight per wave
-// along K (pair: half the waves on each block).
-constexpr int small_max_span(int waves, bool pair) { return 8 * (pair ? waves / 2 : waves); }
+// Groups of K a staged work-group covers: gw per wave along K (pair: half the waves on
+// each block), sized for at least eight.
+constexpr int small_max_span(int waves, bool pair, int gw) {
+  return (gw > 8 ? gw : 8) * (pair ? waves / 2 : waves);
+}
 
 // Scale and zero-point staging: the work-group's nb blocks hold at most nb x
 // small_max_span chunks of GPC units, 8 scale dwords and one zero-point pair per unit.
 // Threads stage whole slots of T entries (T = waves x 64).
-constexpr int small_scale_slots(int waves, bool pair, int nb, int gpc) {
-  return nb * small_max_span(waves, pair) * 8 * gpc / (waves * 64);
+constexpr int small_scale_slots(int waves, bool pair, int gw, int nb, int gpc) {
+  return nb * small_max_span(waves, pair, gw) * 8 * gpc / (waves * 64);
 }
-constexpr int small_zero_slots(int waves, bool pair, int nb, int gpc) {
-  return nb * small_max_span(waves, pair) * gpc > waves * 64
-             ? nb * small_max_span(waves, pair) * gpc / (waves * 64) : 1;
+constexpr int small_zero_slots(int waves, bool pair, int gw, int nb, int gpc) {
+  return nb * small_max_span(waves, pair, gw) * gpc > waves * 64
+             ? nb * small_max_span(waves, pair, gw) * gpc / (waves * 64) : 1;
 }
 // Static LDS of an instance (see the kernel's __shared__ arrays), an upper bound over ZP.
 // (pair: two column blocks split between the waves; dual: two column blocks per wave;
 // direct: per-wave regions in the dynamic LDS instead, see small_direct_lds)
-constexpr long small_static_lds(int waves, bool pair, int gpc, bool r1, bool dual,
+constexpr long small_static_lds(int waves, bool pair, int gw, int gpc, bool r1, bool dual,
                                 bool direct = false) {
   if (direct) return 4 + 8 + 16 + 4;
   const int nb = pair || dual ? 2 : 1;
-  return (long)small_scale_slots(waves, pair, nb, gpc) * waves * 64 * 4    // s_lds
-         + (long)small_zero_slots(waves, pair, nb, gpc) * waves * 64 * 8   // z_lds
-         + (long)(dual ? 2 : 1) * waves * 64 * 16                          // red
-         + (r1 ? (long)small_max_span(waves, pair) * 16 * 4 : 0);          // rsum_lds
+  return (long)small_scale_slots(waves, pair, gw, nb, gpc) * waves * 64 * 4    // s_lds
+         + (long)small_zero_slots(waves, pair, gw, nb, gpc) * waves * 64 * 8   // z_lds
+         + (long)(dual ? 2 : 1) * waves * 64 * 16                              // red
+         + (r1 ? (long)small_max_span(waves, pair, gw) * 16 * 4 : 0);          // rsum_lds
 }
 
 // Direct activations: each wave owns an LDS region holding, for each of its GW groups, the
@@ -159,9 +161,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   constexpr int NB = (PAIR || DUAL) ? 2 : 1;  // column blocks of the work-group
   constexpr int NBV = DUAL ? 2 : 1;           // column blocks of each wave
   constexpr int KW = PAIR ? WAVES / 2 : WAVES;  // waves splitting K for one block
-  constexpr int MS = small_max_span(WAVES, PAIR);  // groups the staged scales cover
-  constexpr int SU = small_scale_slots(WAVES, PAIR, NB, GPC);  // staged scale dwords
-  constexpr int ZU = small_zero_slots(WAVES, PAIR, NB, GPC);   // staged zero points
+  constexpr int MS = small_max_span(WAVES, PAIR, GW);  // groups the staged scales cover
+  constexpr int SU = small_scale_slots(WAVES, PAIR, GW, NB, GPC);  // staged scale dwords
+  constexpr int ZU = small_zero_slots(WAVES, PAIR, GW, NB, GPC);   // staged zero points
   constexpr int JQ = GPC <= 4 ? 4 / GPC : 1;  // 32-row MFMA steps per scale unit (GPC <= 4)
   static_assert(SU >= 1 && SU * T == NB * MS * 8 * GPC, "scale slots cover the range");
   static_assert(ZU * T >= NB * MS * GPC, "zero-point slots cover the range");
@@ -481,12 +483,15 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
       return z_lds[(hb * span + gl[i]) * GPC + t];
     }
   };
-  constexpr int HS = GPC <= 4 ? GPC : 1;  // scales hoisted per chunk (read in place for 8)
-  float scs[NBV][GW][HS];                   // per column block of the wave
+  // Scales hoisted per chunk, for up to four units and eight groups per wave (read in place
+  // otherwise: the registers of sixteen groups would spill).
+  constexpr bool HSC = GPC <= 4 && GW <= 8;
+  constexpr int HS = GPC <= 4 ? GPC : 1;
+  float scs[NBV][HSC ? GW : 1][HSC ? HS : 1];  // per column block of the wave
 #pragma unroll
   for (int i = 0; i < GW; ++i) {
     gl[i] = g0 - gs0 + (i < gw ? i : gw - 1);
-    if constexpr (GPC <= 4) {
+    if constexpr (HSC) {
 #pragma unroll
       for (int v = 0; v < NBV; ++v) {
         const int hv = DUAL ? v : half;
@@ -511,7 +516,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   };
   // Hoisted with the scales for up to two units per chunk; with more, the registers would
   // cost a wave of occupancy, so the excess is read in place.
-  constexpr bool HX = GPC <= 2;
+  constexpr bool HX = GPC <= 2 && GW <= 8;
   float ex[R1B && HX ? GW : 1][R1B && HX ? HS : 1];
   if constexpr (R1B && HX) {
 #pragma unroll
@@ -576,7 +581,15 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     const int half = DUAL ? v : half0;
     const int bv = DUAL ? v : 0;
     f32x4& acc = accs[v];
-    auto& sc = scs[v];
+    // unit t's scale of this chunk (zero for a masked chunk)
+    const auto scale_at = [&](int t) -> float {
+      if constexpr (HSC) {
+        return scs[v][i][t];
+      } else {
+        const float x = A::value(scale_bits(half, i, t));
+        return i < gw ? x : 0.f;
+      }
+    };
     if constexpr (W8) {
       // 32-row step j: vector j / 2, words 2(j % 2) and 2(j % 2) + 1 (rows 0-3 and 4-7).
       f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -585,7 +598,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
         p = A::mfma16(ac[j], A::fp8(bw[i][j >> 1][2 * (j & 1)], bw[i][j >> 1][2 * (j & 1) + 1]),
                       p);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sc[i][0], p[e], acc[e]);
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(scale_at(0), p[e], acc[e]);
     } else if constexpr (R1) {
       // Only row 0 of the product is real.  Operands: the fp16 subnormal nibbles, or biased
       // 128 + q for bf16 (see the header comment).
@@ -651,7 +664,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
             const int j = t * JQ + jj;
             step(j, bw[i][bv][j], c24, c20);
           }
-          acc[0] = __builtin_fmaf(sc[i][t], unit_sum(c24, c20, unit_excess(t)), acc[0]);
+          acc[0] = __builtin_fmaf(scale_at(t), unit_sum(c24, c20, unit_excess(t)), acc[0]);
         }
       } else {
         // 16-row units: the lane's eight rows of step j lie in unit 2j + (qd >> 1).
@@ -687,7 +700,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
           }
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            acc[e] = __builtin_fmaf(sc[i][t], __builtin_fmaf(-off, r[e], p[e]), acc[e]);
+            acc[e] = __builtin_fmaf(scale_at(t), __builtin_fmaf(-off, r[e], p[e]), acc[e]);
         }
       } else {
         // 16-row units: as on the fp16 path, each MFMA sees one unit's half of the step.
@@ -725,7 +738,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
           p = A::mfma16(ac[j], A::dequant(bw[i][bv][j], zo, mr), p);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sc[i][t], p[e], acc[e]);
+        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(scale_at(t), p[e], acc[e]);
       }
     } else {
       // 16-row units: the lane's 8 rows of step j lie in unit 2j + hi.  Its weights enter
@@ -955,7 +968,7 @@ hipError_t launch_small_stage(const uint16_t* a, int lda, int m, const uint32_t*
     return hipErrorInvalidValue;
   }
   if constexpr (!W8) {
-    // One row (at most 128 groups: at most four slots per thread).
+    // One row (at most 256 groups: at most four slots per thread).
     if (mw == 1) {
 #define WQ_SMALL1(ST)                                                                        \
   launch_small_t<ZP, WAVES, GW, ST, PAIR, GPC, BF16, W8, true, false>(                        \
@@ -1009,10 +1022,14 @@ hipError_t launch_small_waves(const uint16_t* a, int lda, int m, const uint32_t*
     return launch_small_gw<ZP, 8, true, GPC, BF16, false>(a, lda, m, b, s, z, c, n, k, plan, partials,
                                              stream);
   }
-  if (plan.waves == 16)  // staged, eight groups per wave (K beyond 64 groups)
+  if (plan.waves == 16) {  // staged, eight or sixteen groups per wave (K beyond 64 groups)
+    if (plan.depth == 16)
+      return launch_small_stage<ZP, 16, 16, false, GPC, BF16, false>(
+          a, lda, m, b, s, z, c, n, k, plan, partials, stream);
     return plan.depth == 8 ? launch_small_stage<ZP, 16, 8, false, GPC, BF16, false>(
                                  a, lda, m, b, s, z, c, n, k, plan, partials, stream)
                            : hipErrorInvalidValue;
+  }
   if (plan.waves == 8)
     return launch_small_gw<ZP, 8, false, GPC, BF16, false>(a, lda, m, b, s, z, c, n, k, plan, partials,
                                               stream);

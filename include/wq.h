@@ -236,9 +236,11 @@ typedef struct wq_gemm_args {
   int32_t group_size;       /* as repacked: -1 or a multiple of 16 dividing k           */
   uint32_t flags;           /* WQ_FLAG_*; HAS_ZP iff zero_points != NULL; ACT_ORDER iff perm */
   int32_t split_k;          /* 0 = library's choice; 1 = no split; s > 1 requests s splits
-                               along K for m <= 16 (needs WQ_FLAG_FP32_REDUCE; clamped to
-                               k/128 and 16); partials are added in split order.  For
-                               m > 16 the split is always the library's choice          */
+                               along K (needs WQ_FLAG_FP32_REDUCE; clamped to k/128 and 16
+                               for m <= 16, and for m > 16 to what the tiles allow: none
+                               on 256-row tiles, SwiGLU, E4M3 or 32/16-row units, else
+                               k/256 and 16); partials are added in split order.  A split
+                               above the library's choice needs split*m*n*4 workspace bytes */
   int32_t reserved;         /* must be 0                                                */
 } wq_gemm_args;
 
@@ -261,8 +263,10 @@ int wq_gemm(const wq_gemm_args* args);
  * up to 256 bytes) and the split-K fp32 partials (splits*m*n floats, splits as
  * wq_gemm_plan reports) come from one static device array of WQ_NOALLOC_SCRATCH_BYTES per
  * GPU, reserved when the library is first used on that GPU and held until the process
- * ends.  A problem whose scratch exceeds it fails with WQ_ERR_WORKSPACE before anything is
- * enqueued.  It allocates and frees nothing.  All calls on one GPU share that array: calls
+ * ends.  When the library's own split (split_k 0) would not fit beside the gather buffer,
+ * the call takes the largest split that does (none if even two do not), and its result is
+ * then that of wq_gemm with that split_k.  A problem whose scratch still exceeds the array
+ * fails with WQ_ERR_WORKSPACE before anything is enqueued.  It allocates and frees nothing.  All calls on one GPU share that array: calls
  * that may overlap on one GPU (other streams, other threads) race and must be serialized by
  * the caller.  The calling thread's current device must be the device of args->stream.
  */

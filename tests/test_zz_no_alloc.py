@@ -66,6 +66,32 @@ def test_noalloc_matches_caller_scratch(dev, first, second):
     assert all(used), "every case must use the static scratch"
 
 
+def test_noalloc_shrinks_a_split_that_does_not_fit(dev):
+    """A tiled split whose partials exceed the static array (1000 x 4096 outputs, K = 14336:
+    the library's own choice is four splits, 64 MiB) runs with the largest split that fits
+    (two, 31 MiB): the same bits as wq_gemm with split_k = 2, within the oracle's tolerance
+    on sampled columns."""
+    m, k, n = 1000, 14336, 4096
+    fp32 = wq.WQ_FLAG_FP32_REDUCE
+    _, auto = wq.wq_gemm_plan(m, n, k, flags=fp32)
+    assert auto * m * n * 4 > wq.WQ_NOALLOC_SCRATCH_BYTES >= 2 * m * n * 4
+    case = synthetic.dense_case(m, k, n, seed=1333)
+    w = torch_ops.PackedWeight(case["qweight"], case["scales"], device=dev)
+    a = torch_ops.to_device(case["a"], dev)
+    for i in range(2):   # twice: the second call reuses the array's stale partials
+        base = torch_ops.gemm(a, w, fp32_reduce=True, split_k=2)
+        out = torch.full((m, n), float("nan"), dtype=torch.float16, device=dev)
+        wq.wq_gemm_noalloc(a, w.b, out, w.s, m=m, n=n, k=k, flags=w.flags(True))
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert np.array_equal(base.cpu().numpy().view(np.uint16), got.view(np.uint16)), i
+    cols = np.r_[0:64, n - 64:n]
+    want = ref.w4a16_gemm(case["a"], case["qweight"], case["scales"], columns=cols)
+    res = ref.check(got[:, cols], want)
+    print(f"noalloc shrunk split: max_err={res['max_err']:.3e} tol={res['tol']:.3e}", flush=True)
+    assert res["ok"], res
+
+
 def test_noalloc_rejects_oversized_scratch_before_launch(dev):
     """An act_order gather larger than the static array is refused with WQ_ERR_WORKSPACE."""
     m, k, n = 8192, 4096, 256          # 64 MiB of gathered activations

@@ -182,6 +182,18 @@ bool plan_small_any(int m, int n, int k, uint32_t flags, int requested, int gpc,
   return false;
 }
 
+// Splits of a tiled product: none without the fp32 reduce flag; a requested count, within
+// what its tiles allow; else the planner's.
+int tile_split_count(int m, int n, int k, uint32_t flags, int requested, int gpc, bool fp8,
+                     bool swiglu) {
+  if (!(flags & WQ_FLAG_FP32_REDUCE)) return 1;
+  if (requested > 0) {
+    const int most = wq::tile_max_splits(m, n, k, gpc, fp8, swiglu);
+    return requested < most ? requested : most;
+  }
+  return wq::tile_splits(m, n, k, gpc, fp8, swiglu);
+}
+
 // fp32 partials [splits][m][n] for the largest split the small-M path may use, or for
 // m > 16 the split the tiled path chooses (the same for 128- and 64-row scale units; the
 // smaller units never split).
@@ -392,8 +404,8 @@ int wq_gemm(const wq_gemm_args* args) {
   const bool small = plan_small_any(p.m, p.n, p.k, p.flags, p.split_k, gpc, swiglu, &plan);
   // Without a small-M plan the tiled kernel computes the product, split along K (with the
   // fp32 reduce) when its output tiles would leave CUs idle.
-  const int tile_split = !small && (p.flags & WQ_FLAG_FP32_REDUCE)
-                             ? wq::tile_splits(p.m, p.n, p.k, gpc, fp8, swiglu) : 1;
+  const int tile_split =
+      small ? 1 : tile_split_count(p.m, p.n, p.k, p.flags, p.split_k, gpc, fp8, swiglu);
   float* partials = nullptr;
   if ((small && plan.splits > 1) || tile_split > 1) {
     const size_t need =
@@ -448,7 +460,7 @@ int wq_gemm_plan(int m, int n, int k, int group_size, uint32_t flags, int split_
     return 0;
   }
   *kernel_out = wq::tile_is_tall(m, n, gpc, fp8) ? WQ_KERNEL_TILE_128 : WQ_KERNEL_TILE_256;
-  *splits_out = (flags & WQ_FLAG_FP32_REDUCE) ? wq::tile_splits(m, n, k, gpc, fp8, swiglu) : 1;
+  *splits_out = tile_split_count(m, n, k, flags, split_k, gpc, fp8, swiglu);
   return 0;
 }
 

@@ -13,18 +13,28 @@ constexpr int kCus = 256;
 
 bool tile_is_tall(int m, int n, int gpc, bool fp8) { return tile_tall(false, m, gpc, fp8, n); }
 
+int tile_max_splits(int m, int n, int k, int gpc, bool fp8, bool swiglu) {
+  // only 128-row tiles of 4-bit weights with 128- or 64-row units, no SwiGLU, split K, into
+  // ranges of at least two groups, at most 16
+  if (swiglu || fp8 || gpc > 2 || !tile_tall(false, m, gpc, fp8, n)) return 1;
+  const int most = k / kGroup / 2;
+  return most > 16 ? 16 : (most < 1 ? 1 : most);
+}
+
 int tile_splits(int m, int n, int k, int gpc, bool fp8, bool swiglu) {
-  if (swiglu || fp8 || gpc > 2) return 1;
-  const int tm = tile_rows(tile_tall(false, m, gpc, fp8, n));
+  const int most = tile_max_splits(m, n, k, gpc, fp8, swiglu);
+  if (most <= 1) return 1;
+  const int tm = tile_rows(true);
   const long tiles = (long)(n / TN) * ((m + tm - 1) / tm);
   // Measured at K = 4096, N = 14336: splits for about half as many work-groups as CUs beat
   // one work-group per CU (the partials' round trip grows with the split count) and a
   // quarter (M=64: 24.0 against 27.3 and 28.3 us; M=256: 46.4 against 73.6 and 63.6 us).
-  int splits = (int)((kCus + 2 * tiles - 1) / (2 * tiles));
-  int max_splits = k / kGroup / 2;
-  if (max_splits > 16) max_splits = 16;
-  if (splits > max_splits) splits = max_splits;
-  return splits < 1 ? 1 : splits;
+  // A longer K gives each tile proportionally more work against the same partials, so the
+  // target grows with K / 4096 (K = 14336, N = 4096: M=512 111.7 -> 83.0 us, M=1024 200.3 ->
+  // 130.6 us).
+  const long target = (long)kCus * (k > 4096 ? k : 4096) / 4096;
+  const int splits = (int)((target + 2 * tiles - 1) / (2 * tiles));
+  return splits > most ? most : (splits < 1 ? 1 : splits);
 }
 
 hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b,

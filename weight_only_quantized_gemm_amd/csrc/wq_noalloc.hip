@@ -61,12 +61,23 @@ int wq_gemm_noalloc(const wq_gemm_args* args) {
   if (st) return st;
   const bool act_order = (args->flags & WQ_FLAG_ACT_ORDER) != 0;
   const size_t gather = act_order ? round256((size_t)args->m * args->k * 2) : 0;
-  const size_t partials = splits > 1 ? (size_t)splits * args->m * args->n * sizeof(float) : 0;
-  if (gather > kScratchBytes || partials > kScratchBytes - gather)
-    return WQ_STATUS(WQ_STAGE_ARGS, WQ_ERR_WORKSPACE);
+  if (gather > kScratchBytes) return WQ_STATUS(WQ_STAGE_ARGS, WQ_ERR_WORKSPACE);
+  const size_t per_split = (size_t)args->m * args->n * sizeof(float);
+  int32_t split_k = args->split_k;
+  if (splits > 1 && (size_t)splits * per_split > kScratchBytes - gather && split_k == 0) {
+    // the library's own split does not fit: the largest split that does (or none)
+    const size_t fit = (kScratchBytes - gather) / per_split;
+    split_k = fit >= 2 ? (int32_t)(fit < (size_t)splits ? fit : (size_t)splits) : 1;
+    if ((st = wq_gemm_plan(args->m, args->n, args->k, args->group_size, args->flags, split_k,
+                           &kernel, &splits)))
+      return st;
+  }
+  const size_t partials = splits > 1 ? (size_t)splits * per_split : 0;
+  if (partials > kScratchBytes - gather) return WQ_STATUS(WQ_STAGE_ARGS, WQ_ERR_WORKSPACE);
   void* base = nullptr;
   if ((st = scratch_for_current_device(&base))) return st;
   wq_gemm_args p = *args;
+  p.split_k = split_k;
   unsigned char* bytes = static_cast<unsigned char*>(base);
   p.a_tmp = act_order ? bytes : nullptr;
   p.workspace = partials ? bytes + gather : nullptr;

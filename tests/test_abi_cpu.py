@@ -373,7 +373,10 @@ def test_gemm_plan_names_the_kernel_and_split():
     for m in (17, 32, 48, 64):
         assert wq.wq_gemm_plan(m, 14336, 4096) == (small, 1), m
         assert wq.wq_gemm_plan(m, 14336, 4096, flags=fp32)[0] == t128, m
-    assert wq.wq_gemm_plan(65, 14336, 4096) == (t128, 1)
+    assert wq.wq_gemm_plan(80, 14336, 4096) == (small, 1)    # five chunks, 147 MB of reads
+    assert wq.wq_gemm_plan(81, 14336, 4096) == (t128, 1)     # six would pass the budget
+    assert wq.wq_gemm_plan(256, 4096, 4096) == (small, 1)    # sixteen chunks of 8.4 MB
+    assert wq.wq_gemm_plan(24, 28672, 8192) == (t128, 1)     # staged chunks past the budget
     assert wq.wq_gemm_plan(32, 14336, 4096, flags=wq.WQ_FLAG_SWIGLU)[0] != small
     # long K: sixteen waves on one work-group per column block (no flag: never split);
     # with the flag, beyond 128 groups, splits of at most 64 groups

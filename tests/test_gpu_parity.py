@@ -363,7 +363,7 @@ def test_long_k_row_chunks_match_oracle(dev, m, k, n, gs, zp):
     assert_parity(c, oracle_gemm(case), label)
 
 
-# 17..64 rows without the fp32 reduce flag: the small-M kernel's direct form in 16-row
+# More than 16 rows without the fp32 reduce flag: the small-M kernel's direct form in 16-row
 # chunks along grid z (single and paired column blocks, ragged last chunks, group sizes,
 # zero points, act_order).
 CHUNK_SHAPES = [
@@ -376,6 +376,11 @@ CHUNK_SHAPES = [
     (64, 4096, 1024, 128, False, True),
     (50, 1536, 256, 48, True, False),
     (61, 2048, 8192, 32, True, True),
+    # up to sixteen chunks while their weight reads stay within the budget
+    (80, 1024, 2048, 128, False, False),
+    (200, 2048, 1024, 128, True, False),
+    (256, 512, 512, 64, False, False),
+    (130, 4096, 512, 128, False, True),
 ]
 
 

@@ -152,32 +152,40 @@ bool plan_small(int m, int n, int k, uint32_t flags, int requested, int gpc,
 }
 
 // The small-M plan of a dense product, if it takes one: m <= 16, or, without the fp32
-// reduce flag, up to kChunkMaxM rows as row chunks (grid z), each reading the weights.
-// Measured on MI355X at K=4096, N=14336 (12 rotating weight copies): 16-row chunks
-// 20.5-21.5 us for 17-32 rows, 30.2-30.5 for 33-48, 36.6 for 64, against 35.2-35.9,
-// 41.3-41.7 and 42.0 for the unsplit row tiles; with the flag the tiles' split K is faster
-// (19.4-20.4, 23.0-23.3, 24.3), so it keeps them.  Beyond that, with a requested split or
-// with the SwiGLU epilogue, the tiled kernel.
+// reduce flag, row chunks along grid z, each reading the weights (at most sixteen).  The
+// chunks' weight reads are held to a budget proportional to K, since the unsplit row tiles
+// that would take the product otherwise are few and their time grows with K:
+// kChunkDirectBytes per K for 16-row chunks on the direct form, kChunkStagedBytes per K for
+// staged chunks of 8, 4, 2 or 1 rows (slower per weight byte).  Measured on MI355X without
+// the flag (one run each; chunks against tiles): K=N=4096 M=80..256 21-49 against 61-64 us;
+// K=4096, N=8192, M=128 42 against 64; K=2048, N=4096, M=256 22 against 37; K=14336,
+// N=4096, M=16 39 against 115; K=28672, N=8192, M=8 120 against 225; beyond the budgets
+// K=8192, N=28672, M=24 123 against 78, and K=11008, N=4096, M=64 about 180 against 101.
+// With the flag the tiles' split K is faster (K=4096, N=14336: 16-row chunks 20.5-21.5 us
+// for 17-32 rows, 36.6 for 64, split tiles 19.4-20.4 and 24.3), so it keeps them; so does a
+// requested split or the SwiGLU epilogue.
 bool plan_small_any(int m, int n, int k, uint32_t flags, int requested, int gpc, bool swiglu,
                     wq::SmallPlan* plan) {
   if (m <= 16) {
     if (swiglu) return plan_small_pair(m, k, gpc, plan);
     if (plan_small(m, n, k, flags, requested, gpc, plan)) return true;
   }
-  if (m > wq::kChunkMaxM || swiglu || requested > 1 || (flags & WQ_FLAG_FP32_REDUCE))
-    return false;
-  // Row chunks, at most four: 16 rows on the direct form, or, where K is too long for it
-  // (beyond 64 groups), a staged slice of 8, 4, 2 or 1 rows (the row tiles that would take
-  // such a product unsplit are as few as N / 256 work-groups).
+  if (swiglu || requested > 1 || (flags & WQ_FLAG_FP32_REDUCE)) return false;
+  const double weight_bytes = (double)k * n * ((flags & WQ_FLAG_FP8) ? 1.0 : 0.5);
+  // 16 rows on the direct form, or, where K is too long for it (beyond 32 groups), a staged
+  // slice of 8, 4, 2 or 1 rows
   for (int rows = 16; rows >= 1; rows /= 2) {
-    if ((m + rows - 1) / rows > 4) break;
+    const int chunks = (m + rows - 1) / rows;
+    if (chunks > 16) break;
     if (rows >= m) continue;
     wq::SmallPlan q{};
-    if (plan_small(rows, n, k, flags, 0, gpc, &q) && q.splits == 1 && (q.direct || rows < 9)) {
-      q.rows = rows;
-      *plan = q;
-      return true;
-    }
+    if (!plan_small(rows, n, k, flags, 0, gpc, &q) || q.splits != 1 || (!q.direct && rows > 8))
+      continue;
+    const double budget = (q.direct ? wq::kChunkDirectBytes : wq::kChunkStagedBytes) * k;
+    if (chunks * weight_bytes > budget) return false;
+    q.rows = rows;
+    *plan = q;
+    return true;
   }
   return false;
 }

@@ -60,10 +60,13 @@ struct SmallPlan {
                    // grid z (one split), else 0 (every work-group takes all m rows)
 };
 bool small_plan_fits(int m, int k, const SmallPlan& plan);
-// Dense products of up to kChunkMaxM rows without the fp32 reduce flag that one small-M
-// work-group cannot take (more than 16 rows, or a staged slice too long for LDS) run on it in
-// at most four row chunks along grid z (SmallPlan::rows), one split.
-constexpr int kChunkMaxM = 64;
+// Dense products without the fp32 reduce flag that one small-M work-group cannot take (more
+// than 16 rows, or a staged slice too long for LDS) run on it in row chunks along grid z
+// (SmallPlan::rows), one split: at most sixteen chunks, while their weight reads stay within
+// K x kChunkDirectBytes (16-row chunks on the direct form) or K x kChunkStagedBytes (staged
+// chunks of at most 8 rows).
+constexpr double kChunkDirectBytes = 38e3;
+constexpr double kChunkStagedBytes = 20e3;
 // bf16: A, s and c hold bf16 values (else fp16).  fp8: b holds E4M3 weights in the FP8
 // layout (no zero points, 128-row scale units).
 hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* b,

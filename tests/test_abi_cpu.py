@@ -377,6 +377,9 @@ def test_gemm_plan_names_the_kernel_and_split():
     assert wq.wq_gemm_plan(81, 14336, 4096) == (t128, 1)     # six would pass the budget
     assert wq.wq_gemm_plan(256, 4096, 4096) == (small, 1)    # sixteen chunks of 8.4 MB
     assert wq.wq_gemm_plan(24, 28672, 8192) == (t128, 1)     # staged chunks past the budget
+    # with the flag, direct chunks within K x 12 kB of weight reads (else split tiles)
+    assert wq.wq_gemm_plan(64, 4096, 4096, flags=fp32) == (small, 1)
+    assert wq.wq_gemm_plan(96, 4096, 4096, flags=fp32)[0] == t128
     assert wq.wq_gemm_plan(32, 14336, 4096, flags=wq.WQ_FLAG_SWIGLU)[0] != small
     # long K: sixteen waves on one work-group per column block (no flag: never split);
     # with the flag, beyond 128 groups, splits of at most 64 groups

@@ -161,16 +161,19 @@ bool plan_small(int m, int n, int k, uint32_t flags, int requested, int gpc,
 // K=4096, N=8192, M=128 42 against 64; K=2048, N=4096, M=256 22 against 37; K=14336,
 // N=4096, M=16 39 against 115; K=28672, N=8192, M=8 120 against 225; beyond the budgets
 // K=8192, N=28672, M=24 123 against 78, and K=11008, N=4096, M=64 about 180 against 101.
-// With the flag the tiles' split K is faster (K=4096, N=14336: 16-row chunks 20.5-21.5 us
-// for 17-32 rows, 36.6 for 64, split tiles 19.4-20.4 and 24.3), so it keeps them; so does a
-// requested split or the SwiGLU epilogue.
+// With the flag the tiles may split K instead, which is faster from about 50 MB of chunk
+// reads at K = 4096 (K=4096, N=14336: 16-row chunks 20.5-21.5 us for 17-32 rows against
+// split tiles 19.4-20.4; N=4096: chunks 9.3-9.5 against 13.6-14.2 us for 24-32 rows, 16.6
+// against 18.5 for 64): direct chunks then take a budget of kChunkSplitBytes per K.  A
+// requested split or the SwiGLU epilogue keeps the tiles.
 bool plan_small_any(int m, int n, int k, uint32_t flags, int requested, int gpc, bool swiglu,
                     wq::SmallPlan* plan) {
   if (m <= 16) {
     if (swiglu) return plan_small_pair(m, k, gpc, plan);
     if (plan_small(m, n, k, flags, requested, gpc, plan)) return true;
   }
-  if (swiglu || requested > 1 || (flags & WQ_FLAG_FP32_REDUCE)) return false;
+  if (swiglu || requested > 1) return false;
+  const bool fp32 = (flags & WQ_FLAG_FP32_REDUCE) != 0;
   const double weight_bytes = (double)k * n * ((flags & WQ_FLAG_FP8) ? 1.0 : 0.5);
   // 16 rows on the direct form, or, where K is too long for it (beyond 32 groups), a staged
   // slice of 8, 4, 2 or 1 rows
@@ -179,9 +182,12 @@ bool plan_small_any(int m, int n, int k, uint32_t flags, int requested, int gpc,
     if (chunks > 16) break;
     if (rows >= m) continue;
     wq::SmallPlan q{};
-    if (!plan_small(rows, n, k, flags, 0, gpc, &q) || q.splits != 1 || (!q.direct && rows > 8))
+    if (!plan_small(rows, n, k, flags & ~(uint32_t)WQ_FLAG_FP32_REDUCE, 0, gpc, &q) ||
+        q.splits != 1 || (!q.direct && rows > 8) || (fp32 && !q.direct))
       continue;
-    const double budget = (q.direct ? wq::kChunkDirectBytes : wq::kChunkStagedBytes) * k;
+    const double budget =
+        (fp32 ? wq::kChunkSplitBytes
+              : (q.direct ? wq::kChunkDirectBytes : wq::kChunkStagedBytes)) * k;
     if (chunks * weight_bytes > budget) return false;
     q.rows = rows;
     *plan = q;

@@ -67,6 +67,8 @@ bool small_plan_fits(int m, int k, const SmallPlan& plan);
 // chunks of at most 8 rows).
 constexpr double kChunkDirectBytes = 38e3;
 constexpr double kChunkStagedBytes = 20e3;
+// With the fp32 reduce flag (the tiles may split K): direct chunks only, K x kChunkSplitBytes.
+constexpr double kChunkSplitBytes = 12e3;
 // bf16: A, s and c hold bf16 values (else fp16).  fp8: b holds E4M3 weights in the FP8
 // layout (no zero points, 128-row scale units).
 hipError_t launch_gemm_small(const uint16_t* a, int lda, int m, const uint32_t* b,

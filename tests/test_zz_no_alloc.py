@@ -43,7 +43,7 @@ PAIRS = [
     ((1, 2048, 512, False, False, True), (1, 1024, 256, False, False, True)),    # small-M split
     ((7, 2048, 512, True, False, True), (3, 1024, 256, True, False, True)),      # zp, split
     ((300, 1024, 512, False, True, False), (100, 512, 256, False, True, False)),  # act_order
-    ((64, 2048, 1024, False, False, True), (40, 1024, 512, False, False, True)),  # tiled split
+    ((64, 4096, 8192, False, False, True), (24, 2048, 14336, False, False, True)),  # tiled split
     ((16, 1024, 512, False, True, True), (5, 512, 256, False, True, True)),      # both scratches
 ]
 

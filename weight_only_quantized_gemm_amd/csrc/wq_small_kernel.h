@@ -781,6 +781,27 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     else
       return red[v][w];
   };
+  if constexpr (R1 && !PAIR) {
+    // One row: after the shuffles every row class holds the column sums, so each wave hands
+    // over only its 16 column sums, and the first 16 lanes of wave 0 add them in wave order.
+    float* const redf = reinterpret_cast<float*>(&red[0][0][0]);
+    if (lane < 16) redf[wave * 16 + lane] = accs[0][0];
+    __syncthreads();
+    if (wave != 0 || lane >= 16) return;
+    float tot = redf[lane];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) tot += redf[w * 16 + lane];
+    const long colx = (long)nb * 16 + lane;
+    if constexpr (SEG) {
+      if (seg_pair[0] >= 0)
+        c[(long)seg_pair[0] * n + colx] = A::round(topk_w != nullptr ? tot * seg_w[0] : tot);
+    } else if (splits == 1) {
+      c[colx] = A::round(tot);
+    } else {
+      partials[(long)split * n + colx] = tot;
+    }
+    return;
+  }
 #pragma unroll
   for (int v = 0; v < NBV; ++v) red_at(v, wave)[lane] = accs[v];
   __syncthreads();

@@ -135,8 +135,15 @@ def test_workspace_sizes():
     ws = wq.wq_gemm_workspace_bytes(1, 14336, 4096, fp32)
     assert ws == 16 * 1 * 14336 * 4          # fp32 partials of up to 16 splits
     assert wq.wq_gemm_workspace_bytes(16, 4096, 4096, fp32) >= 16 * 16 * 4096 * 4
-    # m > 16: the tiled kernel's split, ceil(256 CUs / (2 x 56 tiles)) = 3 at n = 14336
-    assert wq.wq_gemm_workspace_bytes(128, 14336, 4096, fp32) == 3 * 128 * 14336 * 4
+    # m > 16: the tiled kernel's split, about one work-group per CU: 256 // 56 tiles = 4 at
+    # n = 14336; none once the tiles fill most CUs (224 tiles at m = 512)
+    assert wq.wq_gemm_workspace_bytes(128, 14336, 4096, fp32) == 4 * 128 * 14336 * 4
+    assert wq.wq_gemm_workspace_bytes(512, 14336, 4096, fp32) == 0
+    # from k = 8192, two work-groups per CU once the tiles fill half of them: 512 // 128 at
+    # m = 1024, 512 // 256 at m = 2048; 256 // 64 below that
+    assert wq.wq_gemm_workspace_bytes(1024, 4096, 14336, fp32) == 4 * 1024 * 4096 * 4
+    assert wq.wq_gemm_workspace_bytes(2048, 4096, 14336, fp32) == 2 * 2048 * 4096 * 4
+    assert wq.wq_gemm_workspace_bytes(512, 4096, 14336, fp32) == 4 * 512 * 4096 * 4
     assert wq.wq_gemm_workspace_bytes(128, 14336, 4096, 0) == 0
     # at most two groups of K per split: k = 512 allows 2
     assert wq.wq_gemm_workspace_bytes(100, 256, 512, fp32) == 2 * 100 * 256 * 4
@@ -365,8 +372,8 @@ def test_gemm_plan_names_the_kernel_and_split():
     assert wq.wq_gemm_plan(1, 256, 1024, flags=fp32) == (small, 2)
     assert wq.wq_gemm_plan(1, 256, 4096, flags=fp32, split_k=3) == (small, 3)
     assert wq.wq_gemm_plan(1, 256, 1024) == (small, 1)
-    # mid-size m: 128-row tiles, split when they are fewer than half the CUs
-    assert wq.wq_gemm_plan(64, 14336, 4096, flags=fp32) == (t128, 3)
+    # mid-size m: 128-row tiles, split for about one work-group per CU (256 // 56 tiles)
+    assert wq.wq_gemm_plan(64, 14336, 4096, flags=fp32) == (t128, 4)
     assert wq.wq_gemm_plan(256, 14336, 4096, flags=fp32) == (t128, 2)
     assert wq.wq_gemm_plan(256, 14336, 4096) == (t128, 1)
     # 17..64 rows without the fp32 reduce flag: the small-M kernel in 16-row chunks, unsplit

@@ -26,14 +26,16 @@ int tile_splits(int m, int n, int k, int gpc, bool fp8, bool swiglu) {
   if (most <= 1) return 1;
   const int tm = tile_rows(true);
   const long tiles = (long)(n / TN) * ((m + tm - 1) / tm);
-  // Measured at K = 4096, N = 14336: splits for about half as many work-groups as CUs beat
-  // one work-group per CU (the partials' round trip grows with the split count) and a
-  // quarter (M=64: 24.0 against 27.3 and 28.3 us; M=256: 46.4 against 73.6 and 63.6 us).
-  // A longer K gives each tile proportionally more work against the same partials, so the
-  // target grows with K / 4096 (K = 14336, N = 4096: M=512 111.7 -> 83.0 us, M=1024 200.3 ->
-  // 130.6 us).
-  const long target = (long)kCus * (k > 4096 ? k : 4096) / 4096;
-  const int splits = (int)((target + 2 * tiles - 1) / (2 * tiles));
+  // About one work-group per CU; two from K = 8192 once the tiles alone fill half the CUs
+  // (a longer K gives each tile more work against the same partials).  The best of splits
+  // 1-16 in sweeps on MI355X (us): K=4096: N=4096, M=128/200/300/512/1024 (16-128 tiles) s16
+  // 26.0, s8 26.5, s4 32.9, s4 36.5, s2 51.3 against s1 63.6-66.8; N=8192, M=128/256/512 s8
+  // 28.3, s4 35.5, s2 53.1; N=14336, M=24/64/128 s4 18.8, 23.3, 34.2 against s1 36.8-63.0,
+  // M=256 s2 51.5, M=512 s1 75.3.  K=14336, N=4096: M=128/256/512 s16 34.2, s8 45.9, s4 73.2
+  // against s1 197-199, M=1024 s4 125.0, M=2048 s2 223.0 against s1 233.7; K=28672, N=8192,
+  // M=128/256 s8 73.8, s4 128.9 against s1 384-386.
+  const long target = (long)kCus * (k >= 8192 && 2 * tiles >= kCus ? 2 : 1);
+  const int splits = (int)(target / tiles);
   return splits > most ? most : (splits < 1 ? 1 : splits);
 }
 

@@ -115,8 +115,8 @@ hipError_t launch_gemm_tile(const uint16_t* a, int lda, int m, const uint32_t* b
                             const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                             bool swiglu, int gpc, bool bf16, bool fp8, int splits,
                             float* partials, hipStream_t stream);
-// Splits along K of a dense tiled product with the fp32 reduce: about 128 x K / 4096
-// work-groups' worth when the 128-row tiles are fewer (at least two groups of K each, at
+// Splits along K of a dense tiled product with the fp32 reduce: about one work-group per CU
+// (two from K = 8192 with 128 tiles or more) when the 128-row tiles are fewer (at least two groups of K each, at
 // most 16); 1 for SwiGLU, E4M3 weights, 32- or 16-row scale units (gpc > 2), 256-row tiles
 // or enough tiles.  tile_max_splits: the most a requested split may take (1: none).
 int tile_splits(int m, int n, int k, int gpc, bool fp8, bool swiglu);

@@ -175,6 +175,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   // term of the unit's partial).
   constexpr int EX = GPC == 8 ? 2 : 4;  // activation sums per scale unit: one per row class
   constexpr bool R1B = R1;              // one row: activation sums staged
+  // One row (no SwiGLU pair): each wave stages only its own groups' activation granules,
+  // scale words and zero points, at their places in the shared slice, so that its arithmetic
+  // waits for its own loads only and no work-group barrier precedes it.  Under a full weight
+  // stream the activation loads arrive late (a median 2.4 us after the wave starts at
+  // K=14336, N=4096), and the barrier had waited for the slowest of up to sixteen waves
+  // (MI355X, one run, m=1: K=14336, N=4096 8.4 -> 7.2 us; K=11008 7.7 -> 6.7; K=28672,
+  // N=8192 29 -> 24; K=14336, N=14336 26 -> 22; decode unchanged).
+  constexpr bool PW = R1 && !PAIR;
   __shared__ float rsum_lds[R1B ? MS * GPC * EX : 1];
 
   const int tid = threadIdx.x;
@@ -276,6 +284,20 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   int stage_q[R1B ? STAGE : 1];        // granule column of each slot
   bool stage_real[R1B ? STAGE : 1];    // the slot lies inside the slice
   const auto load_stage = [&] {
+    if constexpr (PW) {
+      // slot u of the lane: granule lane + 64u of the wave's groups (the stage slots cover a
+      // wave's share: STAGE >= ceil(ceil(span / WAVES) / 4))
+#pragma unroll
+      for (int u = 0; u < STAGE; ++u) {
+        const bool real = lane + 64 * u < gw * 16;
+        const int qq = (g0 - gs0) * 16 + (real ? lane + 64 * u : 0);
+        stage_q[u] = qq;
+        stage_real[u] = real;
+        const long row_off = SEG ? (long)seg_select(seg_aoff, 0) : 0;
+        stage[u] = *reinterpret_cast<const f16x8*>(a_base + row_off + 8 * qq);
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < STAGE; ++u) {
       const int rr = r < m ? r : m - 1;
@@ -303,6 +325,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
   for (int u = 0; u < (DA ? 0 : SU); ++u) {
     int i = tid + u * T;
+    if constexpr (PW) {
+      const int e = lane + 64 * u;
+      i = (g0 - gs0) * GPC * 8 + (e < gw * GPC * 8 ? e : 0);
+    }
     i = i < NB * s_words ? i : NB * s_words - 1;
     const int h = NB == 2 && i >= s_words ? 1 : 0;  // block of the pair holding dword i
     s_stage[u] = s32[(pair0 + h * units) * 8 + (i - h * s_words)];
@@ -314,6 +340,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     if constexpr (ZP) {
       const int z_words = span * GPC;
       int i = tid + u * T;
+      if constexpr (PW) {
+        const int e = lane + 64 * u;
+        i = (g0 - gs0) * GPC + (e < gw * GPC ? e : 0);
+      }
       i = i < NB * z_words ? i : NB * z_words - 1;
       const int h = NB == 2 && i >= z_words ? 1 : 0;
       z_stage[u] = z[pair0 + h * units + (i - h * z_words)];
@@ -420,11 +450,29 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
       // one row, fp16: rows 0, 1, 4, 5 of the granule first, then 2, 3, 6, 7 (the order of
       // the subnormal operands' two products)
       const u32x4 w = __builtin_bit_cast(u32x4, stage[u]);
-      a_lds[tid + u * T] = R1 && !BF16 ? __builtin_bit_cast(f16x8, u32x4{w[0], w[2], w[1], w[3]})
-                                       : stage[u];
+      const f16x8 v = R1 && !BF16 ? __builtin_bit_cast(f16x8, u32x4{w[0], w[2], w[1], w[3]})
+                                  : stage[u];
+      if constexpr (PW) {
+        if (stage_real[u]) a_lds[stage_q[u]] = v;
+      } else {
+        a_lds[tid + u * T] = v;
+      }
     }
   }
-  if constexpr (!DA) {
+  if constexpr (PW) {
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+      const int e = lane + 64 * u;
+      if (e < gw * GPC * 8) s_lds[(g0 - gs0) * GPC * 8 + e] = s_stage[u];
+    }
+    if constexpr (ZP) {
+#pragma unroll
+      for (int u = 0; u < ZU; ++u) {
+        const int e = lane + 64 * u;
+        if (e < gw * GPC) z_lds[(g0 - gs0) * GPC + e] = z_stage[u];
+      }
+    }
+  } else if constexpr (!DA) {
 #pragma unroll
     for (int u = 0; u < SU; ++u) s_lds[tid + u * T] = s_stage[u];
     if constexpr (ZP) {
@@ -462,7 +510,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
         rsum_lds[stage_q[u] / GR * EX + stage_q[u] % EX] = rs;
     }
   }
-  if constexpr (!DA) __syncthreads();
+  if constexpr (PW) {
+    // the wave reads only what its own lanes wrote: order its LDS writes before its reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else if constexpr (!DA) {
+    __syncthreads();
+  }
 
   // 5. Arithmetic.  MFMA rows >= m are never stored, and a row of the product depends on
   //    its own A row only, so those lanes read row m - 1 instead of selecting zeros.  The

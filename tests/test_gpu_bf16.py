@@ -96,6 +96,10 @@ BF16_SHAPES = [
     # tiled kernel split along K with the fp32 reduce (128-row tiles)
     (64, 2048, 512, 128, True, False, True, 0),
     (300, 1024, 768, 64, False, True, True, 0),
+    # long K on sixteen waves, each staging its own groups' activations and scales
+    (1, 14336, 512, 128, True, False, False, 0),
+    (4, 12288, 256, 64, False, False, False, 0),
+    (3, 20480, 256, 128, True, False, False, 0),
 ]
 
 

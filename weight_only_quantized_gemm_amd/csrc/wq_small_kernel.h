@@ -175,14 +175,18 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   // term of the unit's partial).
   constexpr int EX = GPC == 8 ? 2 : 4;  // activation sums per scale unit: one per row class
   constexpr bool R1B = R1;              // one row: activation sums staged
-  // One row (no SwiGLU pair): each wave stages only its own groups' activation granules,
-  // scale words and zero points, at their places in the shared slice, so that its arithmetic
-  // waits for its own loads only and no work-group barrier precedes it.  Under a full weight
-  // stream the activation loads arrive late (a median 2.4 us after the wave starts at
-  // K=14336, N=4096), and the barrier had waited for the slowest of up to sixteen waves
-  // (MI355X, one run, m=1: K=14336, N=4096 8.4 -> 7.2 us; K=11008 7.7 -> 6.7; K=28672,
-  // N=8192 29 -> 24; K=14336, N=14336 26 -> 22; decode unchanged).
-  constexpr bool PW = R1 && !PAIR;
+  // Staged, no SwiGLU pair, one row (or a dense product of up to eight rows on sixteen
+  // waves): each wave stages only its own groups' activation granules, scale words and zero
+  // points, at their places in the shared slice, so that its arithmetic waits for its own
+  // loads only and no work-group barrier precedes it.  Under a full weight stream the
+  // activation loads arrive late (a median 2.4 us after the wave starts at K=14336, N=4096),
+  // and the barrier had waited for the slowest of up to sixteen waves (MI355X, one run, m=1:
+  // K=14336, N=4096 8.4 -> 7.2 us; K=11008 7.7 -> 6.7; K=28672, N=8192 29 -> 24; K=14336,
+  // N=14336 26 -> 22; decode unchanged; m=2/4/8 at K=14336, N=4096 9.8/11.4/20.7 ->
+  // 8.4/9.7/17.8).  With four waves and more rows it measured slower (K=N=4096, m=8: 4.3 ->
+  // 5.2 us), so several rows keep the shared slice there.  The stage slots cover a wave's
+  // share (stage_slots).
+  constexpr bool PW = !DA && !PAIR && (R1 || (!SEG && WAVES == 16));
   __shared__ float rsum_lds[R1B ? MS * GPC * EX : 1];
 
   const int tid = threadIdx.x;
@@ -281,12 +285,41 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   int q = tid - r * per_row;
   const f16* a_base = a + (long)gs0 * kGroup;
   f16x8 stage[DA ? 1 : STAGE];
-  int stage_q[R1B ? STAGE : 1];        // granule column of each slot
-  bool stage_real[R1B ? STAGE : 1];    // the slot lies inside the slice
+  int stage_q[R1B ? STAGE : 1];        // granule of each slot in the slice
+  bool stage_real[R1B ? STAGE : 1];    // the slot lies inside the slice (and its share)
+  // The wave's share of the slice (dense, more than one row): m rows of gw * 16 granules;
+  // slot u of the lane holds element lane + 64u of it, at row wr and granule wq of the row's
+  // share, stepped like the shared slice.  f(u, row (clamped), slice column, inside).
+  const auto pw_walk = [&](auto f) {
+    const int per_w = gw * 16;
+    int wr = 0, ddr = 0;
+    if (per_w < 64) {
+      ddr = 64 / per_w;
+      wr = lane / per_w;
+    }
+    const int ddq = 64 - ddr * per_w;
+    int wq = lane - wr * per_w;
+#pragma unroll
+    for (int u = 0; u < STAGE; ++u) {
+      f(u, wr < m ? wr : m - 1, (g0 - gs0) * 16 + wq, wr < m);
+      wq += ddq;
+      wr += ddr;
+      const bool wrap = wq >= per_w;
+      wq = wrap ? wq - per_w : wq;
+      wr = wrap ? wr + 1 : wr;
+    }
+  };
   const auto load_stage = [&] {
+    if constexpr (PW && !R1) {
+      // the wave's share: m rows of gw * 16 granules; slot u of the lane holds element
+      // lane + 64u of it (row wr, granule wq of the row's share), stepped like the slice
+      pw_walk([&](int u, int rr, int col_g, bool) {
+        stage[u] = *reinterpret_cast<const f16x8*>(a_base + (long)rr * lda + 8 * col_g);
+      });
+      return;
+    }
     if constexpr (PW) {
-      // slot u of the lane: granule lane + 64u of the wave's groups (the stage slots cover a
-      // wave's share: STAGE >= ceil(ceil(span / WAVES) / 4))
+      // one row: slot u of the lane holds granule lane + 64u of the wave's groups
 #pragma unroll
       for (int u = 0; u < STAGE; ++u) {
         const bool real = lane + 64 * u < gw * 16;
@@ -452,11 +485,16 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
       const u32x4 w = __builtin_bit_cast(u32x4, stage[u]);
       const f16x8 v = R1 && !BF16 ? __builtin_bit_cast(f16x8, u32x4{w[0], w[2], w[1], w[3]})
                                   : stage[u];
-      if constexpr (PW) {
+      if constexpr (PW && R1) {
         if (stage_real[u]) a_lds[stage_q[u]] = v;
-      } else {
+      } else if constexpr (!PW) {
         a_lds[tid + u * T] = v;
       }
+    }
+    if constexpr (PW && !R1) {
+      pw_walk([&](int u, int rr, int col_g, bool inside) {
+        if (inside) a_lds[rr * per_row + col_g] = stage[u];
+      });
     }
   }
   if constexpr (PW) {
@@ -920,11 +958,16 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   }
 }
 
-// Staging slots per thread for an activation slice of m rows and `span` groups.
+// Staging slots per thread for an activation slice of m rows and `span` groups: enough for
+// the slice shared by all threads, and with sixteen waves (which stage their own groups)
+// for each wave's own share of it: m rows of its ceil(span / waves) groups, 64 granules per
+// slot.  (For one row the two counts agree.)
 inline int stage_slots(int m, int span, int waves) {
   const long granules = (long)m * span * (kGroup / 8);
   const long per_slot = (long)waves * 64;
-  return (int)((granules + per_slot - 1) / per_slot);
+  const long shared = (granules + per_slot - 1) / per_slot;
+  const long own = ((long)m * ((span + waves - 1) / waves) * (kGroup / 8) + 63) / 64;
+  return (int)(waves == 16 && own > shared ? own : shared);
 }
 
 inline int round_slots(int slots) {

@@ -688,9 +688,11 @@ FEW_ROW_GROUPED = [
     (3, 5, 512, 512, 16, False, True, True),
     (4, 8, 1024, 256, 128, True, True, False),
     (5, 8, 1024, 512, 128, False, False, True),
-    # a down projection's K (sixteen waves of eight groups)
+    # a down projection's K (sixteen waves of eight groups, each staging its own share)
     (1, 8, 14336, 256, 128, False, True, False),
     (2, 8, 11008, 256, 64, True, False, False),
+    (3, 4, 14336, 256, 128, False, True, True),
+    (2, 2, 12288, 512, 32, True, True, False),
 ]
 
 

@@ -175,8 +175,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   // term of the unit's partial).
   constexpr int EX = GPC == 8 ? 2 : 4;  // activation sums per scale unit: one per row class
   constexpr bool R1B = R1;              // one row: activation sums staged
-  // Staged, no SwiGLU pair, one row (or a dense product of up to eight rows on sixteen
-  // waves): each wave stages only its own groups' activation granules, scale words and zero
+  // Staged, no SwiGLU pair, one row (or, on sixteen waves, up to eight rows of a dense
+  // product or a grouped segment of up to four rows; MoE down projection K=14336, N=4096,
+  // two and three tokens: 27.6-29.5 -> 25.4 us, 41.7-43.3 -> 36.7-37.2 us): each wave
+  // stages only its own groups' activation granules, scale words and zero
   // points, at their places in the shared slice, so that its arithmetic waits for its own
   // loads only and no work-group barrier precedes it.  Under a full weight stream the
   // activation loads arrive late (a median 2.4 us after the wave starts at K=14336, N=4096),
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   // 8.4/9.7/17.8).  With four waves and more rows it measured slower (K=N=4096, m=8: 4.3 ->
   // 5.2 us), so several rows keep the shared slice there.  The stage slots cover a wave's
   // share (stage_slots).
-  constexpr bool PW = !DA && !PAIR && (R1 || (!SEG && WAVES == 16));
+  constexpr bool PW = !DA && !PAIR && (R1 || WAVES == 16);
   __shared__ float rsum_lds[R1B ? MS * GPC * EX : 1];
 
   const int tid = threadIdx.x;
@@ -314,7 +316,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
       // the wave's share: m rows of gw * 16 granules; slot u of the lane holds element
       // lane + 64u of it (row wr, granule wq of the row's share), stepped like the slice
       pw_walk([&](int u, int rr, int col_g, bool) {
-        stage[u] = *reinterpret_cast<const f16x8*>(a_base + (long)rr * lda + 8 * col_g);
+        const long row_off = SEG ? (long)seg_select(seg_aoff, rr) : (long)rr * lda;
+        stage[u] = *reinterpret_cast<const f16x8*>(a_base + row_off + 8 * col_g);
       });
       return;
     }
@@ -455,8 +458,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     seg_rows();
     load_stage();
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (R1) {
-      // one row: every wave's activations ahead of any wave's remaining weights (as below)
+    if constexpr (PW) {
+      // every wave's activations ahead of any wave's remaining weights (as below)
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
     }

@@ -175,19 +175,18 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   // term of the unit's partial).
   constexpr int EX = GPC == 8 ? 2 : 4;  // activation sums per scale unit: one per row class
   constexpr bool R1B = R1;              // one row: activation sums staged
-  // Staged, no SwiGLU pair, one row (or, on sixteen waves, up to eight rows of a dense
-  // product or a grouped segment of up to four rows; MoE down projection K=14336, N=4096,
-  // two and three tokens: 27.6-29.5 -> 25.4 us, 41.7-43.3 -> 36.7-37.2 us): each wave
-  // stages only its own groups' activation granules, scale words and zero
-  // points, at their places in the shared slice, so that its arithmetic waits for its own
-  // loads only and no work-group barrier precedes it.  Under a full weight stream the
-  // activation loads arrive late (a median 2.4 us after the wave starts at K=14336, N=4096),
-  // and the barrier had waited for the slowest of up to sixteen waves (MI355X, one run, m=1:
-  // K=14336, N=4096 8.4 -> 7.2 us; K=11008 7.7 -> 6.7; K=28672, N=8192 29 -> 24; K=14336,
-  // N=14336 26 -> 22; decode unchanged; m=2/4/8 at K=14336, N=4096 9.8/11.4/20.7 ->
-  // 8.4/9.7/17.8).  With four waves and more rows it measured slower (K=N=4096, m=8: 4.3 ->
-  // 5.2 us), so several rows keep the shared slice there.  The stage slots cover a wave's
-  // share (stage_slots).
+  // Per-wave staging (PW): each wave stages only its own groups' activation granules, scale
+  // words and zero points, at their places in the shared slice, so that its arithmetic
+  // waits for its own loads only and no work-group barrier precedes it.  It serves the one-
+  // row path, and on sixteen waves dense products of up to eight rows and grouped segments
+  // of up to four.  Under a full weight stream the activation loads arrive late (a median
+  // 2.4 us after the wave starts at K=14336, N=4096), and the barrier waited for the slowest
+  // of the waves.  Measured on MI355X (one run each, us): m=1, K=14336, N=4096 8.4 -> 7.2;
+  // K=11008 7.7 -> 6.7; K=28672, N=8192 29 -> 24; K=14336, N=14336 26 -> 22; decode
+  // unchanged; m=2/4/8 at K=14336, N=4096 9.8/11.4/20.7 -> 8.4/9.7/17.8; MoE down projection
+  // (K=14336, N=4096) at two and three tokens 28 -> 25.4 and 42 -> 37.  With four waves and
+  // several rows it was slower (K=N=4096, m=8: 4.3 -> 5.2), so those keep the shared slice.
+  // The stage slots cover a wave's share (stage_slots).
   constexpr bool PW = !DA && !PAIR && (R1 || WAVES == 16);
   __shared__ float rsum_lds[R1B ? MS * GPC * EX : 1];
 

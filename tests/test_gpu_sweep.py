@@ -2,7 +2,9 @@
 direct small-M, paired blocks, the one-row path, 128- and 256-row tiles, split K), every
 activation and weight type, group sizes, zero points, act_order and strided activations,
 and of grouped (MoE) products over token and expert counts, types, group sizes, zero
-points and routing weights, each compared with the CPU oracle on every output.
+points and routing weights, each compared with the CPU oracle on every output.  Two more
+sweeps take long K (8192 to 28672: sixteen-wave small-M plans with per-wave staging, row
+chunks and split tiles, and grouped segments of a few rows).
 
 The shapes come from a fixed-seed generator, so the sweep is the same on every run; each
 case prints its parameters before it runs.
@@ -59,6 +61,33 @@ def sweep_cases(count=160, seed=20261203):
 
 CASES = sweep_cases()
 
+LONG_M = [1, 2, 3, 4, 5, 6, 8, 9, 12, 16, 24]
+LONG_K = [8192, 9216, 11008, 12288, 14336, 16384, 20480, 24576, 28672]
+
+
+def long_k_cases(count=24, seed=20261205):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        kind = ["u4b8", "u4zp", "bf16", "fp8"][int(rng.choice(4, p=[0.35, 0.3, 0.25, 0.1]))]
+        m = int(rng.choice(LONG_M))
+        k = int(rng.choice(LONG_K))
+        n = int(rng.choice([256, 512, 1024]))
+        if m * k * n > 400_000_000:
+            continue
+        if kind == "fp8":
+            gs = int(rng.choice([-1, 128]))
+        else:
+            gs = int(rng.choice([g for g in GS_CHOICES if g == -1 or (g <= k and k % g == 0)]))
+        zp = kind == "u4zp" or (kind == "bf16" and bool(rng.integers(2)))
+        act_order = kind != "fp8" and rng.random() < 0.25
+        fp32 = bool(rng.integers(2))
+        split = int(rng.choice([0, 0, 0, 2, 4])) if fp32 else 0
+        lda_pad = int(rng.choice([0, 0, 8]))
+        bf16_act = kind == "bf16"
+        cases.append((kind, m, k, n, gs, zp, act_order, fp32, split, lda_pad, bf16_act))
+    return cases
+
 
 @pytest.fixture(scope="module")
 def dev():
@@ -86,7 +115,19 @@ def strided(a, pad, dev, bf16):
 @pytest.mark.parametrize("kind,m,k,n,gs,zp,act_order,fp32,split,lda_pad,bf16_act", CASES)
 def test_sweep_matches_oracle(dev, kind, m, k, n, gs, zp, act_order, fp32, split, lda_pad,
                               bf16_act):
-    label = (f"sweep {kind} m={m} k={k} n={n} group_size={gs} zp={zp} act_order={act_order} "
+    run_dense(dev, "sweep", kind, m, k, n, gs, zp, act_order, fp32, split, lda_pad, bf16_act)
+
+
+@pytest.mark.parametrize("kind,m,k,n,gs,zp,act_order,fp32,split,lda_pad,bf16_act",
+                         long_k_cases())
+def test_long_k_sweep_matches_oracle(dev, kind, m, k, n, gs, zp, act_order, fp32, split,
+                                     lda_pad, bf16_act):
+    run_dense(dev, "long-K sweep", kind, m, k, n, gs, zp, act_order, fp32, split, lda_pad,
+              bf16_act)
+
+
+def run_dense(dev, name, kind, m, k, n, gs, zp, act_order, fp32, split, lda_pad, bf16_act):
+    label = (f"{name} {kind} m={m} k={k} n={n} group_size={gs} zp={zp} act_order={act_order} "
              f"fp32={fp32} split={split} lda=k+{lda_pad} bf16={bf16_act}")
     print(label, flush=True)
     seed = 7000 + m * 31 + k * 7 + n + gs
@@ -130,9 +171,35 @@ def grouped_cases(count=48, seed=20261204):
     return cases
 
 
+def grouped_long_k_cases(count=16, seed=20261206):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        kind = ["fp16", "bf16", "fp8"][int(rng.choice(3, p=[0.55, 0.35, 0.1]))]
+        tokens = int(rng.choice([1, 2, 3, 4]))
+        experts = int(rng.choice([2, 3, 8]))
+        k = int(rng.choice([8192, 11008, 14336, 16384]))
+        n = int(rng.choice([256, 512]))
+        gs = 128 if kind == "fp8" else int(rng.choice([g for g in (16, 32, 64, 128) if k % g == 0]))
+        zp = kind != "fp8" and bool(rng.integers(2))
+        weighted = bool(rng.integers(2))
+        cases.append((kind, tokens, experts, k, n, gs, zp, weighted))
+    return cases
+
+
 @pytest.mark.parametrize("kind,tokens,experts,k,n,gs,zp,weighted", grouped_cases())
 def test_grouped_sweep_matches_oracle(dev, kind, tokens, experts, k, n, gs, zp, weighted):
-    label = (f"grouped sweep {kind} tokens={tokens} experts={experts} k={k} n={n} "
+    run_grouped(dev, "grouped sweep", kind, tokens, experts, k, n, gs, zp, weighted)
+
+
+@pytest.mark.parametrize("kind,tokens,experts,k,n,gs,zp,weighted", grouped_long_k_cases())
+def test_grouped_long_k_sweep_matches_oracle(dev, kind, tokens, experts, k, n, gs, zp,
+                                             weighted):
+    run_grouped(dev, "grouped long-K sweep", kind, tokens, experts, k, n, gs, zp, weighted)
+
+
+def run_grouped(dev, name, kind, tokens, experts, k, n, gs, zp, weighted):
+    label = (f"{name} {kind} tokens={tokens} experts={experts} k={k} n={n} "
              f"group_size={gs} zp={zp} weighted={weighted}")
     print(label, flush=True)
     seed = 9000 + tokens * 13 + experts * 101 + k + n + gs

@@ -1059,7 +1059,8 @@ hipError_t launch_seg_zp(const GroupedProblem& p, int rows, const SmallPlan& pla
       case 1: return launch_seg_stage<ZP, 8, 1, true, GPC, BF16>(p, rows, stream);
       case 2: return launch_seg_stage<ZP, 8, 2, true, GPC, BF16>(p, rows, stream);
       case 4: return launch_seg_stage<ZP, 8, 4, true, GPC, BF16>(p, rows, stream);
-      default: return launch_seg_stage<ZP, 8, 8, true, GPC, BF16>(p, rows, stream);
+      case 8: return launch_seg_stage<ZP, 8, 8, true, GPC, BF16>(p, rows, stream);
+      default: return hipErrorInvalidValue;
     }
   }
   if (plan.waves == 16)
@@ -1072,7 +1073,8 @@ hipError_t launch_seg_zp(const GroupedProblem& p, int rows, const SmallPlan& pla
     case 1: return launch_seg_stage<ZP, 4, 1, false, GPC, BF16>(p, rows, stream);
     case 2: return launch_seg_stage<ZP, 4, 2, false, GPC, BF16>(p, rows, stream);
     case 4: return launch_seg_stage<ZP, 4, 4, false, GPC, BF16>(p, rows, stream);
-    default: return launch_seg_stage<ZP, 4, 8, false, GPC, BF16>(p, rows, stream);
+    case 8: return launch_seg_stage<ZP, 4, 8, false, GPC, BF16>(p, rows, stream);
+    default: return hipErrorInvalidValue;
   }
 }
 
@@ -1140,7 +1142,8 @@ hipError_t launch_small_gw(const uint16_t* a, int lda, int m, const uint32_t* b,
     case 1: return WQ_SMALL(1);
     case 2: return WQ_SMALL(2);
     case 4: return WQ_SMALL(4);
-    default: return WQ_SMALL(8);
+    case 8: return WQ_SMALL(8);
+    default: return hipErrorInvalidValue;  // deeper plans only on sixteen waves
   }
 #undef WQ_SMALL
 }

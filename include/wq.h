@@ -337,8 +337,10 @@ int wq_grouped_workspace_bytes(int n_pairs, int n_active, int n, int k, uint32_t
  * entries out of range are skipped by the kernel (never read or written out of bounds),
  * leaving those output rows unwritten.  Segments must be non-empty: when n_pairs -
  * n_active + 1 <= 4 (every segment then holds at most four rows; decode-sized batches)
- * 4-bit products without the SwiGLU epilogue run on the small-M kernel, one work-group per
- * 16-column block and segment, which computes at most that many rows of a segment.
+ * products with 4-bit weights (K up to 128 groups of 128 rows, 64 with WQ_FLAG_SWIGLU) run
+ * on the small-M kernel, one work-group per 16-column block (a gate/up pair of blocks with
+ * the SwiGLU epilogue) and segment, which computes at most that many rows of a segment;
+ * E4M3 weights and longer K take the tiled kernel.
  */
 int wq_grouped_gemm(const wq_grouped_args* args);
 

@@ -200,8 +200,11 @@ int wq_gemm_workspace_bytes(int m, int n, int k, uint32_t flags, size_t* bytes_o
 /* Which kernel wq_gemm runs for a problem, and how many splits along K it uses (host,
  * no device access): the planner's own choice for (m, n, k, group_size, flags, split_k),
  * the same arguments as in wq_gemm_args.  kernel_out: WQ_KERNEL_SMALL_M (16-column blocks:
- * m <= 16, weights streamed once; or, without WQ_FLAG_FP32_REDUCE or SwiGLU, m <= 64 in
- * at most four row chunks that each stream the weights, K not split), WQ_KERNEL_TILE_256 or
+ * m <= 16, weights streamed once; or, without SwiGLU or a requested split, up to sixteen
+ * row chunks of 16 rows, or of 8, 4, 2 or 1 where K is long, each streaming the weights
+ * with K not split, while the chunks' weight reads stay within K x 38 kB (16-row chunks)
+ * or K x 20 kB (shorter chunks); with WQ_FLAG_FP32_REDUCE, 16-row chunks within K x
+ * 12 kB, since the tiles may then split K), WQ_KERNEL_TILE_256 or
  * WQ_KERNEL_TILE_128 (MFMA tiles of 256 or 128 rows by 256 columns); splits_out: 1 = K not
  * split, s > 1 = s fp32 partials added by a second kernel in split order.  Shape errors as
  * in wq_gemm. */

@@ -63,14 +63,6 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 // --- planning of the small-M kernel ------------------------------------------------------
 
-// Plan of the small-M kernel, or false when no plan fits its staging limits (the tiled
-// kernel then computes the product).  Without WQ_FLAG_FP32_REDUCE the product is never
-// split (every output is one work-group's fp32 sum, rounded once).  With it, a requested
-// split count is honoured, raised if the activation slice would not fit in LDS; the
-// library's own choice splits only when the 16-column blocks alone give fewer than 128
-// work-groups (half the CUs), since every split adds an fp32 partial round trip and a
-// reduce launch (measured on MI355X: at N=4096..14336 one split is fastest).  Each split's
-// groups are shared by 4 or 8 waves, at most 8 groups per wave.
 // Plan of the small-M kernel's SwiGLU (paired) form: no split, 8 or 16 waves (4 or 8 per
 // block along K), or false when no plan fits (the tiled kernel then computes it).
 bool plan_small_pair(int m, int k, int gpc, wq::SmallPlan* plan) {
@@ -99,6 +91,15 @@ constexpr int kDirectRows = 9;
 // 5.9 against 4.9 us; N=8192 (256) 7.0 against 8.8 us; N=14336 (448) 11.7 against 15.5 us.
 constexpr int kDualMinGroups = 256;
 
+// Plan of the small-M kernel, or false when no plan fits its staging limits (the tiled
+// kernel then computes the product).  Without WQ_FLAG_FP32_REDUCE the product is never
+// split (every output is one work-group's fp32 sum, rounded once).  With it, a requested
+// split count is honoured, raised if the activation slice would not fit in LDS; the
+// library's own choice splits when the 16-column blocks alone give fewer than 128
+// work-groups (half the CUs), since every split adds an fp32 partial round trip and a
+// reduce launch (measured on MI355X: at N=4096..14336 one split is fastest), and beyond
+// 128 groups into ranges of at most 64.  Each split's groups are shared by 4, 8 or 16
+// waves: at most 8 groups per wave, or 16 with sixteen staged waves.
 bool plan_small(int m, int n, int k, uint32_t flags, int requested, int gpc,
                 wq::SmallPlan* plan) {
   const int groups = k / kGroupSize;

@@ -46,9 +46,11 @@ hipError_t launch_gather_columns(const uint16_t* a, int lda, const int32_t* perm
 // work-groups per column block, fp32 partials go to `partials` [splits][m][n] and a second
 // kernel reduces them in split order.
 struct SmallPlan {
-  int waves;       // waves per work-group (4 or 8; 8 or 16 when pair), splitting K
+  int waves;       // waves per work-group splitting K: 4 or 8, or 16 on the staged form
+                   // (8 or 16 when pair)
   int splits;      // work-groups along K per column block
-  int depth;       // groups of K per wave, all loaded before arithmetic (1, 2, 4 or 8)
+  int depth;       // groups of K per wave, all loaded before arithmetic: 1, 2, 4 or 8, or
+                   // 16 with sixteen staged waves
   bool pair;       // SwiGLU epilogue: a gate/up pair of blocks per work-group, half the
                    // waves on each (n counts both; c is [m][n/2]; splits must be 1)
   int gpc;         // scale units per 128-row chunk: 1, 2, 4 or 8 (units of 128/gpc rows)

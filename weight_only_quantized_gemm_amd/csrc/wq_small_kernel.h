@@ -7,8 +7,12 @@
 // load per lane.  All of a wave's weight loads are issued before any arithmetic and
 // consumed in issue order, so the weight stream is never stalled behind compute.
 // Activations, scales and zero points reach LDS one of two ways: staged once for the
-// work-group's range by all its threads (few rows), or fetched by each wave for its own
-// groups with direct-to-LDS loads (9 rows and more; the "direct" form below).  Codes become
+// work-group's range (up to 8 rows; by all its threads, or, on the one-row path and on
+// sixteen waves, each wave staging its own share with no barrier before its arithmetic),
+// or fetched by each wave for its own groups with direct-to-LDS loads (9 rows and more;
+// the "direct" form below).  On the staged form every wave's activation and scale loads
+// are issued before any wave's weight loads (measured faster: the staging then waits less
+// behind other waves' weights).  Codes become
 // exact fp16 integers (q - z) in registers; each scale group's MFMA partial is scaled by
 // its fp16 group scale in fp32 and accumulated in fp32; the waves' sums are added in wave
 // order.
@@ -466,9 +470,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
     for (int i = EARLY; i < GW; ++i) load_b(i);
   } else {
-    // A bare barrier (no wait) puts every wave's activation and scale loads ahead of any
-    // wave's weight loads in the CU's queue: the slice's LDS writes, and so the arithmetic,
-    // no longer wait for other waves' weights (MI355X, one run: K=8192, N=4096, m=1 5.74 ->
+    // A bare barrier (no wait) issues every wave's activation and scale loads ahead of any
+    // wave's weight loads, so that the slice's LDS writes, and so the arithmetic, wait less
+    // behind other waves' weights (MI355X, one run: K=8192, N=4096, m=1 5.74 ->
     // 5.27 us; K=14336, N=4096, m=4 11.9 -> 11.3; K=4096, N=14336, m=4 9.2 -> 8.9; decode
     // unchanged).
     __builtin_amdgcn_sched_barrier(0);

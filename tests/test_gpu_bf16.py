@@ -96,6 +96,9 @@ BF16_SHAPES = [
     # tiled kernel split along K with the fp32 reduce (128-row tiles)
     (64, 2048, 512, 128, True, False, True, 0),
     (300, 1024, 768, 64, False, True, True, 0),
+    # eight staged waves with two to four rows, each staging its own share
+    (3, 8192, 256, 128, True, False, False, 0),
+    (4, 6144, 512, -1, False, False, False, 0),
     # long K on sixteen waves, each staging its own groups' activations and scales
     (1, 14336, 512, 128, True, False, False, 0),
     (4, 12288, 256, 64, False, False, False, 0),

@@ -339,6 +339,33 @@ def test_long_k_sixteen_waves_match_oracle(dev, m, k, n, gs, zp, act_order, fp32
     assert_parity(c, oracle_gemm(case), label)
 
 
+# Eight staged waves (33 to 64 groups of K) with two to four rows per work-group: each wave
+# stages its own share of the activation slice (the separate per-wave instances); row
+# chunks of up to four rows take them too.
+EIGHT_WAVE_SHAPES = [
+    # m, k, n, group_size, zp, act_order, fp32
+    (2, 8192, 512, 128, False, False, False),
+    (3, 6144, 256, 64, True, False, False),
+    (4, 5120, 768, 32, False, True, False),
+    (4, 8192, 256, 16, True, False, False),
+    (2, 4352, 4096, 128, False, False, True),
+]
+
+
+@pytest.mark.parametrize("m,k,n,gs,zp,act_order,fp32", EIGHT_WAVE_SHAPES)
+def test_eight_wave_per_wave_staging_matches_oracle(dev, m, k, n, gs, zp, act_order, fp32):
+    label = (f"eight waves m={m} k={k} n={n} group_size={gs} zp={zp} act_order={act_order} "
+             f"fp32={fp32}")
+    say(label)
+    flags = wq.WQ_FLAG_FP32_REDUCE if fp32 else 0
+    kernel, splits = wq.wq_gemm_plan(m, n, k, group_size=gs, flags=flags)
+    assert kernel == wq.WQ_KERNEL_SMALL_M and splits == 1
+    case = synthetic.dense_case(m, k, n, zp=zp, act_order=act_order, group_size=gs,
+                                seed=4400 + m + k + gs)
+    c = gpu_gemm(case, dev, fp32_reduce=fp32)
+    assert_parity(c, oracle_gemm(case), label)
+
+
 # More rows than one staged work-group holds at long K, without the fp32 reduce flag: row
 # chunks of 8, 4 (or fewer) rows along grid z on sixteen waves.
 LONG_K_CHUNK_SHAPES = [

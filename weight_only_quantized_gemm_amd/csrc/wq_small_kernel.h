@@ -132,7 +132,7 @@ constexpr long small_direct_lds(int waves, int gw, int gpc, bool zp, bool dual) 
 // requested before the row indices, so that the weight stream starts while the index loads
 // resolve.
 template <bool ZP, int WAVES, int GW, int STAGE, bool PAIR, int GPC, bool BF16, bool W8,
-          bool R1, bool DUAL, bool SEG = false>
+          bool R1, bool DUAL, bool SEG = false, bool PWR = false>
 __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     const f16* __restrict__ a, int lda, int m, const u32x4* __restrict__ b,
     const uint16_t* __restrict__ s, const u32x2* __restrict__ z, uint16_t* __restrict__ c,
@@ -190,8 +190,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   // unchanged; m=2/4/8 at K=14336, N=4096 9.8/11.4/20.7 -> 8.4/9.7/17.8; MoE down projection
   // (K=14336, N=4096) at two and three tokens 28 -> 25.4 and 42 -> 37.  With four waves and
   // several rows it was slower (K=N=4096, m=8: 4.3 -> 5.2), so those keep the shared slice.
-  // The stage slots cover a wave's share (stage_slots).
-  constexpr bool PW = !DA && !PAIR && (R1 || WAVES == 16);
+  // Dense eight-wave plans of up to four rows per work-group launch separate instances
+  // that take it (PWR; K=N=8192, m=2/3/4: 8.9-10.0/10.0-10.3/10.0-10.3 -> 8.6-8.7/9.4/
+  // 9.7-10.0 us; K=N=5120, m=4: 8.6-8.9 -> 8.2-8.4), while more rows keep the shared slice
+  // (m=6/8 measured 2-8% slower with it).  The stage slots cover a wave's share
+  // (stage_slots).
+  static_assert(!PWR || (WAVES == 8 && !SEG && !DA && !PAIR && !R1 && !W8),
+                "per-wave staging on request: dense eight-wave staged plans");
+  constexpr bool PW = !DA && !PAIR && (R1 || WAVES == 16 || PWR);
   __shared__ float rsum_lds[R1B ? MS * GPC * EX : 1];
 
   const int tid = threadIdx.x;
@@ -965,15 +971,16 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 }
 
 // Staging slots per thread for an activation slice of m rows and `span` groups: enough for
-// the slice shared by all threads, and with sixteen waves (which stage their own groups)
-// for each wave's own share of it: m rows of its ceil(span / waves) groups, 64 granules per
-// slot.  (For one row the two counts agree.)
+// the slice shared by all threads, and where the waves stage their own groups (sixteen
+// waves, or eight with at most four rows) for each wave's own share of it: m rows of its
+// ceil(span / waves) groups, 64 granules per slot.  (For one row the two counts agree.)
 inline int stage_slots(int m, int span, int waves) {
   const long granules = (long)m * span * (kGroup / 8);
   const long per_slot = (long)waves * 64;
   const long shared = (granules + per_slot - 1) / per_slot;
   const long own = ((long)m * ((span + waves - 1) / waves) * (kGroup / 8) + 63) / 64;
-  return (int)(waves == 16 && own > shared ? own : shared);
+  const bool per_wave = waves == 16 || (waves == 8 && m <= 4);
+  return (int)(per_wave && own > shared ? own : shared);
 }
 
 inline int round_slots(int slots) {
@@ -981,7 +988,7 @@ inline int round_slots(int slots) {
 }
 
 template <bool ZP, int WAVES, int GW, int STAGE, bool PAIR, int GPC, bool BF16, bool W8,
-          bool R1, bool DUAL>
+          bool R1, bool DUAL, bool PWR = false>
 hipError_t launch_small_t(const uint16_t* a, int lda, int m, const uint32_t* b,
                           const uint16_t* s, const uint32_t* z, uint16_t* c, int n, int k,
                           int splits, float* partials, int chunk_rows, hipStream_t stream) {
@@ -992,7 +999,7 @@ hipError_t launch_small_t(const uint16_t* a, int lda, int m, const uint32_t* b,
                                     : (size_t)STAGE * WAVES * 64 * sizeof(f16x8);
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(
-          &gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16, W8, R1, DUAL>),
+          &gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16, W8, R1, DUAL, false, PWR>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
   // more rows than a work-group takes: chunks of chunk_rows rows along grid z (one split)
@@ -1000,7 +1007,8 @@ hipError_t launch_small_t(const uint16_t* a, int lda, int m, const uint32_t* b,
   const int chunks = (m + chunk_rows - 1) / chunk_rows;
   if (chunks > 1 && splits != 1) return hipErrorInvalidValue;
   const dim3 grid(n / (PAIR || DUAL ? 32 : 16), splits, chunks);
-  hipLaunchKernelGGL((gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16, W8, R1, DUAL>), grid,
+  hipLaunchKernelGGL((gemm_small_kernel<ZP, WAVES, GW, STAGE, PAIR, GPC, BF16, W8, R1, DUAL, false,
+                                       PWR>), grid,
                      dim3(WAVES * 64), lds, stream, reinterpret_cast<const f16*>(a), lda, m,
                      reinterpret_cast<const u32x4*>(b), s, reinterpret_cast<const u32x2*>(z), c,
                      n, groups, splits, partials, nullptr, nullptr, nullptr, nullptr, nullptr,
@@ -1120,6 +1128,22 @@ hipError_t launch_small_stage(const uint16_t* a, int lda, int m, const uint32_t*
         default: return hipErrorInvalidValue;
       }
 #undef WQ_SMALL1
+    }
+  }
+  if constexpr (WAVES == 8 && !PAIR && !W8) {
+    // up to four rows per work-group: the per-wave staging instances (at most 8 slots)
+    if (mw <= 4) {
+#define WQ_SMALLW(ST)                                                                        \
+  launch_small_t<ZP, WAVES, GW, ST, PAIR, GPC, BF16, W8, false, false, true>(                 \
+      a, lda, m, b, s, z, c, n, k, plan.splits, partials, mw, stream)
+      switch (round_slots(stage_slots(mw, span, WAVES))) {
+        case 1: return WQ_SMALLW(1);
+        case 2: return WQ_SMALLW(2);
+        case 4: return WQ_SMALLW(4);
+        case 8: return WQ_SMALLW(8);
+        default: return hipErrorInvalidValue;
+      }
+#undef WQ_SMALLW
     }
   }
 #define WQ_SMALL(ST)                                                                         \

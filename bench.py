@@ -137,7 +137,8 @@ def bench_extended(torch, torch_ops, steps, warmup):
     """Timings of the widened features on the same workload shapes (one object per row):
     the SwiGLU gate/up projection with its fused activation at decode (M=1) and prefill
     (M=2048) shape, other scale-group sizes, bf16 activations, E4M3 weights, mid-size
-    batches with the split-K fp32 reduce, and MoE with routing weights."""
+    batches with the split-K fp32 reduce, a decode down projection (K=14336) at one and four
+    rows, and MoE with routing weights."""
     import synthetic
     import weight_only_quantized_gemm_amd as wq
     out = {}
@@ -236,6 +237,26 @@ def bench_extended(torch, torch_ops, steps, warmup):
             "us": round(sec * 1e6, 2),
             "tflops": round(2.0 * m * cfg["n"] * cfg["k"] / sec / 1e12, 2),
             "weight_tbs": round(cfg["k"] * cfg["n"] / 2 / sec / 1e12, 4)}
+    del ws
+    # A decode down projection (the MLP's second product, K = 14336, N = 4096): one row and a
+    # four-row batch, no flags, on the small-M kernel's sixteen-wave plans.
+    kd, nd = 14336, 4096
+    case = synthetic.dense_case(1, kd, nd, seed=25)
+    w = torch_ops.PackedWeight(case["qweight"], case["scales"], device="cuda")
+    ws = [w] + [w.clone() for _ in range(11)]
+    for m in (1, 4):
+        a = torch_ops.to_device(synthetic.activations(27, m, kd), "cuda")
+        c = torch.empty((m, nd), dtype=torch.float16, device="cuda")
+        bufs = torch_ops.GemmBuffers(w, m, False)
+
+        def step(i, a=a, c=c, bufs=bufs):
+            torch_ops.gemm(a, ws[i % 12], c, buffers=bufs)
+        sec = timed_loop(torch, step, steps, warmup)
+        out[f"down_proj_m{m}"] = {
+            "workload": f"M={m} K={kd} N={nd} u4b8 g128 (a decode down projection), 12 rotating "
+                        "weight copies",
+            "us": round(sec * 1e6, 2),
+            "weight_tbs": round(kd * nd / 2 / sec / 1e12, 4)}
     del ws
     moe = synthetic.moe_case()
     bank = torch_ops.ExpertBank(moe["experts"], device="cuda")

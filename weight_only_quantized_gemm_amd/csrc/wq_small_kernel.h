@@ -923,8 +923,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
   for (int v = 0; v < NBV; ++v) red_at(v, wave)[lane] = accs[v];
   __syncthreads();
-  if (wave != 0) return;
   if constexpr (PAIR) {
+    if (wave != 0) return;
     f32x4 gs = red_at(0, 0)[lane], us = red_at(0, KW)[lane];
 #pragma unroll
     for (int w = 1; w < KW; ++w) {
@@ -942,30 +942,32 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     }
     return;
   }
+  // The 4 x NBV output elements of a lane are summed by different waves (part = wave, wave
+  // + WAVES, ...: block part / 4, element part % 4), each adding the waves' sums in wave
+  // order, so the reduction's tail is spread over the waves.
 #pragma unroll
-  for (int v = 0; v < NBV; ++v) {
-    f32x4 tot = red_at(v, 0)[lane];
+  for (int part = wave; part < 4 * NBV; part += WAVES) {
+    const int v = part / 4;
+    const int e = part % 4;
+    float tot = reinterpret_cast<const float*>(red_at(v, 0) + lane)[e];
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) tot += red_at(v, w)[lane];
+    for (int w = 1; w < WAVES; ++w) tot += reinterpret_cast<const float*>(red_at(v, w) + lane)[e];
 
     // Output layout of the 16x16 block: lane holds rows 4*qd + e of column `col`.
     const long colx = (long)(nb + v) * 16 + col;
+    const int row = 4 * qd + e;
+    if (row >= m) continue;
+    if constexpr (SEG) {
+      // the pair's output row, times its routing weight in fp32 before the rounding
+      const int pr = seg_select(seg_pair, row);
+      float wr = seg_w[0];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 4 * qd + e;
-      if (row >= m) continue;
-      if constexpr (SEG) {
-        // the pair's output row, times its routing weight in fp32 before the rounding
-        const int pr = seg_select(seg_pair, row);
-        float wr = seg_w[0];
-#pragma unroll
-        for (int j = 1; j < SR; ++j) wr = row == j ? seg_w[j] : wr;
-        if (pr >= 0) c[(long)pr * n + colx] = A::round(topk_w != nullptr ? tot[e] * wr : tot[e]);
-      } else if (splits == 1) {
-        c[(long)row * n + colx] = A::round(tot[e]);
-      } else {
-        partials[((long)split * m + row) * n + colx] = tot[e];
-      }
+      for (int j = 1; j < SR; ++j) wr = row == j ? seg_w[j] : wr;
+      if (pr >= 0) c[(long)pr * n + colx] = A::round(topk_w != nullptr ? tot * wr : tot);
+    } else if (splits == 1) {
+      c[(long)row * n + colx] = A::round(tot);
+    } else {
+      partials[((long)split * m + row) * n + colx] = tot;
     }
   }
 }

@@ -924,22 +924,22 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   for (int v = 0; v < NBV; ++v) red_at(v, wave)[lane] = accs[v];
   __syncthreads();
   if constexpr (PAIR) {
-    if (wave != 0) return;
-    f32x4 gs = red_at(0, 0)[lane], us = red_at(0, KW)[lane];
+    // wave e (e < 4) sums element e of the lane's gate and up sums, in wave order
+    if (wave >= 4) return;
+    const int e = wave;
+    const int row = 4 * qd + e;
+    float gs = reinterpret_cast<const float*>(red_at(0, 0) + lane)[e];
+    float us = reinterpret_cast<const float*>(red_at(0, KW) + lane)[e];
 #pragma unroll
     for (int w = 1; w < KW; ++w) {
-      gs += red_at(0, w)[lane];
-      us += red_at(0, KW + w)[lane];
+      gs += reinterpret_cast<const float*>(red_at(0, w) + lane)[e];
+      us += reinterpret_cast<const float*>(red_at(0, KW + w) + lane)[e];
     }
     const long colj = (long)blockIdx.x * 16 + col;  // column of the [m][n/2] activation
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 4 * qd + e;
-      if (row >= m) continue;
-      // SEG: the pair's row of the activation (not written for an out-of-range pair)
-      const int pr = SEG ? seg_select(seg_pair, row) : row;
-      if (pr >= 0) c[(long)pr * (n / 2) + colj] = A::round(silu_times(gs[e], us[e]));
-    }
+    if (row >= m) return;
+    // SEG: the pair's row of the activation (not written for an out-of-range pair)
+    const int pr = SEG ? seg_select(seg_pair, row) : row;
+    if (pr >= 0) c[(long)pr * (n / 2) + colj] = A::round(silu_times(gs, us));
     return;
   }
   // The 4 x NBV output elements of a lane are summed by different waves (part = wave, wave

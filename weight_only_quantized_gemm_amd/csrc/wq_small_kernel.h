@@ -7,8 +7,9 @@
 // load per lane.  All of a wave's weight loads are issued before any arithmetic and
 // consumed in issue order, so the weight stream is never stalled behind compute.
 // Activations, scales and zero points reach LDS one of two ways: staged once for the
-// work-group's range (up to 8 rows; by all its threads, or, on the one-row path and on
-// sixteen waves, each wave staging its own share with no barrier before its arithmetic),
+// work-group's range (up to 8 rows; by all its threads, or, on the one-row path, on
+// sixteen waves and on eight waves with at most four rows, each wave staging its own share
+// with no barrier before its arithmetic),
 // or fetched by each wave for its own groups with direct-to-LDS loads (9 rows and more;
 // the "direct" form below).  On the staged form every wave's activation and scale loads
 // are issued before any wave's weight loads (measured faster: the staging then waits less
@@ -322,8 +323,6 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
   };
   const auto load_stage = [&] {
     if constexpr (PW && !R1) {
-      // the wave's share: m rows of gw * 16 granules; slot u of the lane holds element
-      // lane + 64u of it (row wr, granule wq of the row's share), stepped like the slice
       pw_walk([&](int u, int rr, int col_g, bool) {
         const long row_off = SEG ? (long)seg_select(seg_aoff, rr) : (long)rr * lda;
         stage[u] = *reinterpret_cast<const f16x8*>(a_base + row_off + 8 * col_g);

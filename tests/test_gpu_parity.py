@@ -366,6 +366,33 @@ def test_eight_wave_per_wave_staging_matches_oracle(dev, m, k, n, gs, zp, act_or
     assert_parity(c, oracle_gemm(case), label)
 
 
+# Four to eight rows at long K with the fp32 reduce flag, where the grid exceeds the CUs: the
+# planner splits K into ranges of at most 16 groups (at most 8 splits), with act_order,
+# zero points and 64-row units.
+DEEP_SPLIT_SHAPES = [
+    # m, k, n, group_size, zp, act_order, splits the planner takes
+    (5, 14336, 4096, 128, False, False, 8),
+    (4, 8192, 8192, 128, True, False, 4),
+    (7, 12288, 4608, 64, False, True, 8),
+    (6, 28672, 2048, 128, False, False, 8),
+    (8, 16384, 4352, 64, True, False, 8),
+]
+
+
+@pytest.mark.parametrize("m,k,n,gs,zp,act_order,want", DEEP_SPLIT_SHAPES)
+def test_deep_split_matches_oracle(dev, m, k, n, gs, zp, act_order, want):
+    label = f"deep split m={m} k={k} n={n} group_size={gs} zp={zp} act_order={act_order}"
+    say(label)
+    kernel, splits = wq.wq_gemm_plan(m, n, k, group_size=gs, flags=wq.WQ_FLAG_FP32_REDUCE)
+    assert kernel == wq.WQ_KERNEL_SMALL_M and splits == want
+    case = synthetic.dense_case(m, k, n, zp=zp, act_order=act_order, group_size=gs,
+                                seed=4600 + m + k + gs)
+    c = gpu_gemm(case, dev, fp32_reduce=True)
+    assert_parity(c, oracle_gemm(case), label)
+    again = gpu_gemm(case, dev, fp32_reduce=True)
+    assert np.array_equal(c.view(np.uint16), again.view(np.uint16)), label
+
+
 # More rows than one staged work-group holds at long K, without the fp32 reduce flag: row
 # chunks of 8, 4 (or fewer) rows along grid z on sixteen waves.
 LONG_K_CHUNK_SHAPES = [

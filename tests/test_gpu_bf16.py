@@ -103,9 +103,9 @@ BF16_SHAPES = [
     (1, 14336, 512, 128, True, False, False, 0),
     (4, 12288, 256, 64, False, False, False, 0),
     (3, 20480, 256, 128, True, False, False, 0),
-    # K split into ranges of at most 16 groups (four to eight rows, grid beyond the CUs)
+    # K split into ranges of at most 16 groups (four or more rows, grid beyond the CUs)
     (6, 14336, 4096, 128, True, False, True, 0),
-    (4, 8192, 8192, 64, False, True, True, 0),
+    (4, 11008, 8192, 64, False, True, True, 0),
 ]
 
 

@@ -366,16 +366,19 @@ def test_eight_wave_per_wave_staging_matches_oracle(dev, m, k, n, gs, zp, act_or
     assert_parity(c, oracle_gemm(case), label)
 
 
-# Four to eight rows at long K with the fp32 reduce flag, where the grid exceeds the CUs: the
-# planner splits K into ranges of at most 16 groups (at most 8 splits), with act_order,
-# zero points and 64-row units.
+# Four to sixteen rows at long K with the fp32 reduce flag, where the grid exceeds the CUs:
+# the planner splits K into ceil(groups / 16) ranges of at most 16 groups, on the staged
+# and the direct forms, with act_order, zero points and 64-row units.
 DEEP_SPLIT_SHAPES = [
     # m, k, n, group_size, zp, act_order, splits the planner takes
-    (5, 14336, 4096, 128, False, False, 8),
-    (4, 8192, 8192, 128, True, False, 4),
-    (7, 12288, 4608, 64, False, True, 8),
-    (6, 28672, 2048, 128, False, False, 8),
+    (5, 14336, 4096, 128, False, False, 7),
+    (4, 11008, 8192, 128, True, False, 6),
+    (7, 12288, 4608, 64, False, True, 6),
+    (6, 28672, 2048, 128, False, False, 14),
     (8, 16384, 4352, 64, True, False, 8),
+    (12, 28672, 4096, 128, False, False, 14),
+    (10, 11008, 4096, 128, True, False, 6),
+    (16, 14336, 4352, 64, False, True, 7),
 ]
 
 

@@ -91,26 +91,31 @@ constexpr int kDirectRows = 9;
 // 5.9 against 4.9 us; N=8192 (256) 7.0 against 8.8 us; N=14336 (448) 11.7 against 15.5 us.
 constexpr int kDualMinGroups = 256;
 
-// Own choice with the flag, 4-bit weights, 4 to 8 rows (a staged slice) and K from 64
-// groups: when the grid holds more work-groups than the CUs, K is split into ranges of at
-// most kDeepSplitGroups groups, in at most kDeepSplitMax splits (a power of two).  Measured on
-// MI355X (us, own choice -> deep split, two rounds): K=14336, N=4096, m=8 15.5-15.7 -> 13.5;
-// K=14336, N=14336, m=4 31.5 -> 25.8-27.8, m=8 41.3 -> 32.6-32.9; K=28672, N=8192, m=4
-// 32.5-33.0 -> 29.2, m=8 46.6 -> 39.1-39.9; K=16384, N=8192, m=4 18.4 -> 17.8-17.9, m=8
-// 25.9-26.4 -> 21.2-22.8; K=8192, N=14336, m=4 16.0 -> 15.8-16.3, m=8 22.2-22.6 -> 19.1-19.4;
-// K=11008 and 12288, N=4096, m=6 and 8 about 15 -> 12.6-12.8.  Where one round of work-groups
+// Own choice with the flag, 4-bit weights, 4 to 16 rows and K from 64 groups: when the grid
+// holds more work-groups than the CUs, K is split into ranges of at most kDeepSplitGroups
+// groups, in ceil(groups / kDeepSplitGroups) splits (so that the ranges come out even: 112
+// groups in 7, not 8 ranges of 14, which leave waves idle).  Measured on MI355X (us, two
+// rounds, the previous own choice -> the deep split): K=14336, N=4096, m=8 15.5-15.7 -> 12.4,
+// m=12 24.0 -> 13.6; K=14336, N=14336, m=4 31.5 -> 23.6-23.7, m=8 41.3 -> 28.9-29.0;
+// K=28672, N=8192, m=4 32.5-33.0 -> 25.9-26.2, m=8 46.6 -> 32.4-32.8, m=12 82.0 -> 37.2,
+// m=16 40.8-41.0 -> 38.8-39.1; K=28672, N=4096, m=4 18.4 -> 16.5, m=16 24.3 -> 22.6;
+// K=16384, N=8192, m=4 18.6 -> 17.0-17.4, m=8 26.1 -> 21.3-22.2; K=11008, N=4096, m=8 about
+// 15 -> 11.5; K=12288, N=4096, m=16 13.9 -> 12.4; K=8192, N=14336, m=8 22.2-22.6 ->
+// 19.1-19.4.  Where one round of work-groups
 // covers the grid the unsplit plan stays (K=8192, N=4096, m=8 7.6 against 8.7 with two
-// splits; K=14336, N=4096, m=4 9.6 against 11.3 with four), and with one or two rows
-// splitting was as often slower (K=8192, N=14336, m=1 12.0 against 14.1-14.8 with two).
+// splits; K=14336, N=4096, m=4 9.6 against 11.3 with four), and so does four rows at 64
+// groups (K=8192, N=8192 with zero points 10.7-11.0 against 11.5-11.7 with four); with one
+// to three rows splitting was as often slower (K=8192, N=14336, m=1 12.0 against 14.1-14.8
+// with two).
 constexpr int kDeepSplitGroups = 16;
-constexpr int kDeepSplitMax = 8;
 constexpr int kCus = 256;
 
 int deep_split(int m, int n, int groups, uint32_t flags, int s) {
-  if (m < 4 || m >= kDirectRows || groups < 64 || (flags & WQ_FLAG_FP8) || (n / 16) * s <= kCus)
+  if (m < 4 || groups < 64 || (m == 4 && groups == 64) || (flags & WQ_FLAG_FP8) ||
+      (n / 16) * s <= kCus)
     return s;
-  int want = 1;
-  while (want < kDeepSplitMax && (groups + want - 1) / want > kDeepSplitGroups) want *= 2;
+  int want = (groups + kDeepSplitGroups - 1) / kDeepSplitGroups;
+  if (want > kMaxSplits) want = kMaxSplits;
   return want > s ? want : s;
 }
 
@@ -121,7 +126,7 @@ int deep_split(int m, int n, int groups, uint32_t flags, int s) {
 // library's own choice splits when the 16-column blocks alone give fewer than 128
 // work-groups (half the CUs), since every split adds an fp32 partial round trip and a
 // reduce launch (measured on MI355X: at N=4096..14336 one split is fastest), and beyond
-// 128 groups into ranges of at most 64, and deeper for 4 to 8 rows (deep_split).  Each
+// 128 groups into ranges of at most 64, and deeper from 4 rows (deep_split).  Each
 // split's groups are shared by 4, 8 or 16 waves: at most 8 groups per wave, or 16 with
 // sixteen staged waves.
 bool plan_small(int m, int n, int k, uint32_t flags, int requested, int gpc,

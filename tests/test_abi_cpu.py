@@ -389,10 +389,18 @@ def test_gemm_plan_names_the_kernel_and_split():
     assert wq.wq_gemm_plan(96, 4096, 4096, flags=fp32)[0] == t128
     assert wq.wq_gemm_plan(32, 14336, 4096, flags=wq.WQ_FLAG_SWIGLU)[0] != small
     # long K: sixteen waves on one work-group per column block (no flag: never split);
-    # with the flag, beyond 128 groups, splits of at most 64 groups
+    # with the flag, beyond 128 groups, splits of at most 64 groups, and of at most 32 where
+    # the grid exceeds two work-groups per CU (16 from four rows, beyond one per CU)
     assert wq.wq_gemm_plan(1, 4096, 14336) == (small, 1)
     assert wq.wq_gemm_plan(1, 8192, 28672) == (small, 1)
-    assert wq.wq_gemm_plan(1, 8192, 28672, flags=fp32) == (small, 4)
+    assert wq.wq_gemm_plan(1, 8192, 28672, flags=fp32) == (small, 7)
+    assert wq.wq_gemm_plan(1, 2048, 28672, flags=fp32) == (small, 4)
+    assert wq.wq_gemm_plan(1, 14336, 14336, flags=fp32) == (small, 4)
+    assert wq.wq_gemm_plan(1, 8192, 14336, flags=fp32) == (small, 1)
+    assert wq.wq_gemm_plan(4, 4096, 14336, flags=fp32) == (small, 1)
+    assert wq.wq_gemm_plan(8, 4096, 14336, flags=fp32) == (small, 7)
+    assert wq.wq_gemm_plan(4, 8192, 8192, flags=fp32) == (small, 1)
+    assert wq.wq_gemm_plan(12, 8192, 28672, flags=fp32) == (small, 14)
     assert wq.wq_gemm_plan(8, 4096, 14336) == (small, 1)   # two staged 4-row chunks
     # the planner's split always fits the workspace the library asks for
     for m, n in ((1, 256), (64, 14336), (256, 14336), (16, 512)):

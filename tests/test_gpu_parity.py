@@ -366,9 +366,10 @@ def test_eight_wave_per_wave_staging_matches_oracle(dev, m, k, n, gs, zp, act_or
     assert_parity(c, oracle_gemm(case), label)
 
 
-# Four to sixteen rows at long K with the fp32 reduce flag, where the grid exceeds the CUs:
-# the planner splits K into ceil(groups / 16) ranges of at most 16 groups, on the staged
-# and the direct forms, with act_order, zero points and 64-row units.
+# Long K with the fp32 reduce flag where the grid exceeds the CUs: from four rows the planner
+# splits K into ceil(groups / 16) ranges of at most 16 groups, on the staged and the direct
+# forms; with one to three rows into ranges of at most 32; with act_order, zero points and
+# 64-row units.
 DEEP_SPLIT_SHAPES = [
     # m, k, n, group_size, zp, act_order, splits the planner takes
     (5, 14336, 4096, 128, False, False, 7),
@@ -379,6 +380,10 @@ DEEP_SPLIT_SHAPES = [
     (12, 28672, 4096, 128, False, False, 14),
     (10, 11008, 4096, 128, True, False, 6),
     (16, 14336, 4352, 64, False, True, 7),
+    # one to three rows: ranges of at most 32 groups beyond two work-groups per CU
+    (3, 28672, 4096, 128, True, False, 7),
+    (1, 14336, 8704, 128, False, False, 4),
+    (2, 14336, 8704, 64, False, True, 4),
 ]
 
 

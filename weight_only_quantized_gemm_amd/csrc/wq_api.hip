@@ -104,17 +104,26 @@ constexpr int kDualMinGroups = 256;
 // 19.1-19.4.  Where one round of work-groups
 // covers the grid the unsplit plan stays (K=8192, N=4096, m=8 7.6 against 8.7 with two
 // splits; K=14336, N=4096, m=4 9.6 against 11.3 with four), and so does four rows at 64
-// groups (K=8192, N=8192 with zero points 10.7-11.0 against 11.5-11.7 with four); with one
-// to three rows splitting was as often slower (K=8192, N=14336, m=1 12.0 against 14.1-14.8
-// with two).
+// groups (K=8192, N=8192 with zero points 10.7-11.0 against 11.5-11.7 with four).  One to
+// three rows split only beyond 64 groups and two work-groups per CU, into ranges of at most
+// 32 groups: K=14336, N=14336, m=1 22.2-24.4 -> 20.6-20.8, m=3 29.7 -> 25.0-25.3; K=28672,
+// N=8192 (four splits before), m=1 24.2 -> 22.8-22.9, m=2 28.0 -> 23.6, m=3 31.6-31.9 ->
+// 25.7-26.4; K=28672, N=4096, m=3 18.5-18.7 -> 15.8-16.1.  With fewer work-groups it was
+// as often slower (K=8192, N=14336, m=1 12.0 against 14.1-14.8 with two; K=16384, N=8192,
+// m=1 13.6-13.8 against 14.8-15.3 with four).
 constexpr int kDeepSplitGroups = 16;
 constexpr int kCus = 256;
 
 int deep_split(int m, int n, int groups, uint32_t flags, int s) {
-  if (m < 4 || groups < 64 || (m == 4 && groups == 64) || (flags & WQ_FLAG_FP8) ||
-      (n / 16) * s <= kCus)
+  if (flags & WQ_FLAG_FP8) return s;
+  int range = kDeepSplitGroups;
+  if (m < 4) {
+    if (groups <= 64 || (n / 16) * s <= 2 * kCus) return s;
+    range = 2 * kDeepSplitGroups;
+  } else if (groups < 64 || (m == 4 && groups == 64) || (n / 16) * s <= kCus) {
     return s;
-  int want = (groups + kDeepSplitGroups - 1) / kDeepSplitGroups;
+  }
+  int want = (groups + range - 1) / range;
   if (want > kMaxSplits) want = kMaxSplits;
   return want > s ? want : s;
 }

@@ -6,7 +6,8 @@ workload text says what runs).  Each step is one wq_gemm call; steps rotate over
 weight copies that the weights stream from HBM rather than from the 256 MB Infinity Cache.
 The same line carries the prefill (M=2048, act_order) TFLOP/s with its MFMA roofline, the
 batched-decode, tiny and grouped-MoE figures, the measured HBM-read and MFMA ceilings, and
-the oracle timed on the host cores for every workload as the CPU baseline.
+the oracle timed on the host cores for every workload as the CPU baseline; `extended` adds
+other group sizes, bf16, E4M3, SwiGLU, MoE variants, split-K batches and down projections.
 """
 
 from __future__ import annotations
@@ -257,7 +258,28 @@ def bench_extended(torch, torch_ops, steps, warmup):
                         "weight copies",
             "us": round(sec * 1e6, 2),
             "weight_tbs": round(kd * nd / 2 / sec / 1e12, 4)}
-    del ws
+    # The same down projection for 8- and 16-row batches with the fp32 reduce flag (K split
+    # into seven even 16-group ranges), and a 70B-class one (K = 28672, N = 8192, 117 MB of
+    # weights, four rotating copies) for a four-row batch (fourteen ranges).
+    long_rows = [(m, kd, nd, ws, 12) for m in (8, 16)]
+    case = synthetic.dense_case(1, 28672, 8192, seed=26)
+    w70 = torch_ops.PackedWeight(case["qweight"], case["scales"], device="cuda")
+    long_rows.append((4, 28672, 8192, [w70] + [w70.clone() for _ in range(3)], 4))
+    for m, kl, nl, wl, copies in long_rows:
+        a = torch_ops.to_device(synthetic.activations(28, m, kl), "cuda")
+        c = torch.empty((m, nl), dtype=torch.float16, device="cuda")
+        bufs = torch_ops.GemmBuffers(wl[0], m, True)
+
+        def step(i, a=a, c=c, bufs=bufs, wl=wl, copies=copies):
+            torch_ops.gemm(a, wl[i % copies], c, fp32_reduce=True, buffers=bufs)
+        sec = timed_loop(torch, step, steps, warmup)
+        splits = wq.wq_gemm_plan(m, nl, kl, flags=wq.WQ_FLAG_FP32_REDUCE)[1]
+        out[f"down_proj_{kl}x{nl}_m{m}_fp32_reduce"] = {
+            "workload": f"M={m} K={kl} N={nl} u4b8 g128 (a down projection), fp32 reduce "
+                        f"({splits} splits), {copies} rotating weight copies",
+            "us": round(sec * 1e6, 2),
+            "weight_tbs": round(kl * nl / 2 / sec / 1e12, 4)}
+    del ws, w70, long_rows
     moe = synthetic.moe_case()
     bank = torch_ops.ExpertBank(moe["experts"], device="cuda")
     csr = wq.wq_csr_from_routes(moe["routes"], moe["n_tokens"], moe["top_k"], moe["n_expert"])
